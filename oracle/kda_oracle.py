@@ -1,0 +1,285 @@
+"""fp64 CPU oracle for the Kimi Delta Attention (KDA) gated delta rule.
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the CPU
+baseline leg of the benchmark may import this module.  It shares no code with
+the HIP path (no kernels, headers, helpers or constants) and imports nothing
+from the product package.
+
+Everything here is plain, slow and written to be checked by eye against the
+pages it follows.  Citations name the page by its title and the section:
+
+  [KDA-demo]     "【轻量化复刻大模型 / KIMI K3】KDA 模块交互式演示"
+  [LinAttn-demo] "【轻量化复刻大模型】线性注意力交互式演示"
+  [KDA-layer]    "KDAAttention 层" (notes, sec-05)
+  [Impl-KDA]     "Implémenter KDA"
+
+Layouts follow the pages' tensor statement ([LinAttn-demo] §1.2 "总体公式";
+[KDA-layer] "完整数据流"): q, k, z are [B, T, H, Dk]; v is [B, T, H, Dv];
+beta is [B, T, H]; A_log is [H]; states are [B, H, Dk, Dv].  All arithmetic
+is float64.
+
+Readings taken where the pages are silent or disagree (each also listed in
+the design notes):
+  * decay is applied BEFORE the delta erase ([Impl-KDA] "La forme récurrente
+    de référence" and its first pitfall), although [KDA-demo] §1.3 and
+    [LinAttn-demo] Eq. 1 write the erase against the un-decayed state;
+  * the readout uses the post-update state, o_t = S_t^T q_t, with no 1/sqrt(Dk)
+    scale ([KDA-demo] §1.3; [Impl-KDA] third pitfall);
+  * the gate is g = g_min * sigmoid(exp(A_log[h]) * z) ([LinAttn-demo] Eq. 8,
+    [Impl-KDA] "La décroissance bornée"; the parenthesis in [KDA-demo] §1.4 is
+    garbled);
+  * L2 normalisation divides by sqrt(sum x^2 + eps) with eps = 1e-6 (the
+    pages give no epsilon);
+  * with a switch off ([KDA-layer] "三个 in_kernel 开关") the caller supplies
+    the activated quantity itself: the normalised q/k, beta in (0, 1), or the
+    log-decay g in place of the gate logit z.
+
+Every function below is pinned by tests that do not retype it (closed forms,
+the pages' limit cases, exact rational arithmetic, the KCP identity and the
+chunkwise form); none is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# Switch bits, mirroring the three "in kernel" switches of [KDA-layer].
+QK_L2NORM = 1
+BETA_SIGMOID = 2
+GATE_IN_KERNEL = 4
+FLAGS_DEFAULT = QK_L2NORM | BETA_SIGMOID | GATE_IN_KERNEL
+
+G_MIN_DEFAULT = -5.0  # gate lower bound, [Impl-KDA] "La décroissance bornée"
+L2_EPS = 1e-6
+
+
+# ---------------------------------------------------------------------------
+# Gates and normalisation
+# ---------------------------------------------------------------------------
+
+def sigmoid(x):
+    """Logistic function in float64 ([KDA-layer] switch 2; [Impl-KDA])."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    pos = x >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
+    ex = np.exp(x[~pos])
+    out[~pos] = ex / (1.0 + ex)
+    return out
+
+
+def l2_normalize(x, eps=L2_EPS):
+    """x / sqrt(sum(x^2) + eps) over the last axis ([KDA-demo] §1.3: q and k are
+    L2-normalised; [KDA-layer] switch 1)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
+def bounded_log_decay(z, A_log, g_min=G_MIN_DEFAULT):
+    """Bounded log-decay g = g_min * sigmoid(exp(A_log[h]) * z) per Dk channel.
+
+    [LinAttn-demo] §1.2 Eq. 8 and [Impl-KDA] "La décroissance bornée".
+    z is [..., H, Dk]; A_log is [H].  The result lies in (g_min, 0), so the
+    retention alpha = exp(g) lies in (exp(g_min), 1).
+    """
+    z = np.asarray(z, dtype=np.float64)
+    scale = np.exp(np.asarray(A_log, dtype=np.float64))[:, None]  # [H, 1]
+    return g_min * sigmoid(scale * z)
+
+
+def prepare(q, k, z, beta_raw, A_log, g_min=G_MIN_DEFAULT, flags=FLAGS_DEFAULT):
+    """Apply the switched activations of [KDA-layer] "chunk_kda 内部做了什么":
+    L2-normalise q and k, squash beta by a sigmoid, and turn the gate logit
+    into the bounded log-decay.  Returns (q_hat, k_hat, g, beta)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    beta_raw = np.asarray(beta_raw, dtype=np.float64)
+    if flags & QK_L2NORM:
+        q = l2_normalize(q)
+        k = l2_normalize(k)
+    beta = sigmoid(beta_raw) if flags & BETA_SIGMOID else beta_raw
+    g = bounded_log_decay(z, A_log, g_min) if flags & GATE_IN_KERNEL else z
+    return q, k, g, beta
+
+
+# ---------------------------------------------------------------------------
+# The recurrence (the plain definition)
+# ---------------------------------------------------------------------------
+
+def recurrent(q, k, v, g, beta, S0=None):
+    """Token-by-token KDA recurrence; the definition every other form must meet.
+
+    For each token, per (b, h) ([Impl-KDA] "La forme récurrente de référence",
+    read with its pitfalls):
+        S <- Diag(exp(g_t)) S            forget, channel by channel
+        S <- S - beta_t k_t (k_t^T S)    erase the part aligned with k_t
+        S <- S + beta_t k_t v_t^T        write the new association
+        o_t = S^T q_t                    read the UPDATED state
+    q, k, g: [B, T, H, Dk] (already activated); v: [B, T, H, Dv];
+    beta: [B, T, H]; S0: [B, H, Dk, Dv] or None (zero state).
+    Returns o [B, T, H, Dv] and the final state [B, H, Dk, Dv].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    B, T, H, Dk = k.shape
+    Dv = v.shape[-1]
+    S = np.zeros((B, H, Dk, Dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    o = np.zeros((B, T, H, Dv))
+    for t in range(T):
+        alpha = np.exp(g[:, t])                        # [B, H, Dk]
+        S = alpha[..., None] * S                       # decay first
+        kt = k[:, t]                                   # [B, H, Dk]
+        proj = np.einsum("bhk,bhkv->bhv", kt, S)       # k^T S
+        bt = beta[:, t][..., None]                     # [B, H, 1]
+        S = S - kt[..., None] * (bt * proj)[..., None, :]
+        S = S + kt[..., None] * (bt * v[:, t])[..., None, :]
+        o[:, t] = np.einsum("bhk,bhkv->bhv", q[:, t], S)
+    return o, S
+
+
+def forward(q, k, v, z, beta_raw, A_log, S0=None, g_min=G_MIN_DEFAULT,
+            flags=FLAGS_DEFAULT):
+    """chunk_kda forward as a plain definition: switched activations
+    ([KDA-layer]) followed by the recurrence.  Returns (o, S_final)."""
+    qh, kh, g, beta = prepare(q, k, z, beta_raw, A_log, g_min, flags)
+    return recurrent(qh, kh, v, g, beta, S0)
+
+
+def step(S, q, k, v, z, beta_raw, A_log, g_min=G_MIN_DEFAULT, flags=FLAGS_DEFAULT):
+    """One decode step ([KDA-demo] §1.7 lists kda_step as the single-token
+    form of the core).  q, k, z: [B, H, Dk]; v: [B, H, Dv]; beta_raw: [B, H];
+    S: [B, H, Dk, Dv].  Returns (o [B, H, Dv], S_new)."""
+    o, S_new = forward(np.asarray(q)[:, None], np.asarray(k)[:, None],
+                       np.asarray(v)[:, None], np.asarray(z)[:, None],
+                       np.asarray(beta_raw)[:, None], A_log, S, g_min, flags)
+    return o[:, 0], S_new
+
+
+# ---------------------------------------------------------------------------
+# Affine structure: transitions, segment fragments, composition (KCP)
+# ---------------------------------------------------------------------------
+
+def transition(k, beta, alpha):
+    """Per-token transition M_t = (I - beta k k^T) Diag(alpha)
+    ([Impl-KDA] Test 2, kda_transition).  k, alpha: [..., Dk]; beta: [...]."""
+    k = np.asarray(k, dtype=np.float64)
+    alpha = np.asarray(alpha, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    Dk = k.shape[-1]
+    eye = np.broadcast_to(np.eye(Dk), k.shape[:-1] + (Dk, Dk))
+    proj = eye - beta[..., None, None] * (k[..., :, None] * k[..., None, :])
+    return proj * alpha[..., None, :]          # right-multiply by Diag(alpha)
+
+
+def segment_fragment(k, v, g, beta):
+    """Fragment of one segment from a zero state ([Impl-KDA] Test 3):
+    M = M_T ... M_1 (later tokens on the left) and S_tilde = run(segment, 0).
+    Shapes as in `recurrent`; returns M [B,H,Dk,Dk], S_tilde [B,H,Dk,Dv]."""
+    k = np.asarray(k, dtype=np.float64)
+    B, T, H, Dk = k.shape
+    q_dummy = np.zeros_like(k)
+    _, S_tilde = recurrent(q_dummy, k, v, g, beta, None)
+    M = np.broadcast_to(np.eye(Dk), (B, H, Dk, Dk)).copy()
+    for t in range(T):
+        Mt = transition(k[:, t], beta[:, t], np.exp(np.asarray(g)[:, t]))
+        M = Mt @ M
+    return M, S_tilde
+
+
+def compose(fragments, S_in=None):
+    """Prefix scan over segment fragments ([KDA-demo] §1.6; [Impl-KDA] Test 3):
+    S <- M_s S + S_tilde_s for s = 1..n.  Returns the list of states after each
+    segment.  fragments: sequence of (M, S_tilde) pairs."""
+    out = []
+    S = None
+    for M, St in fragments:
+        if S is None:
+            S = np.zeros_like(St) if S_in is None else np.array(S_in, dtype=np.float64)
+        S = M @ S + St
+        out.append(S)
+    return out
+
+
+def compose_pair(second, first):
+    """Associative composition law ([Impl-KDA] "La loi de composition
+    associative"): (M2, S2) o (M1, S1) = (M2 M1, M2 S1 + S2)."""
+    M2, S2 = second
+    M1, S1 = first
+    return M2 @ M1, M2 @ S1 + S2
+
+
+# ---------------------------------------------------------------------------
+# Chunkwise form (model of the chunk algebra; used only to pin recurrent == chunk)
+# ---------------------------------------------------------------------------
+
+def chunkwise(q, k, v, g, beta, S0=None, chunk=64):
+    """Chunkwise-parallel evaluation ([KDA-demo] §1.5 Eqs. 3-4, generalised to
+    carry decay and the incoming state as in [Impl-KDA] "La forme par blocs",
+    where the intra-chunk value is U - W S).
+
+    Inside a chunk with incoming state S and local cumulative log-decay
+    G_r = sum_{i<=r} g_i:
+        A_kk[i, j] = beta_i sum_d k_id k_jd exp(G_id - G_jd)     (j <  i)
+        A_qk[i, j] =        sum_d q_id k_jd exp(G_id - G_jd)     (j <= i)
+        (I + A_kk) U = Diag(beta) (V - (K * exp(G)) S)           UT solve
+        O = (Q * exp(G)) S + A_qk U
+        S <- Diag(exp(G_C)) S + (K * exp(G_C - G))^T U
+    The decay factors are formed element-wise from differences of G (never as
+    1/gamma), so this model cannot overflow.  Shapes as in `recurrent`.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    B, T, H, Dk = k.shape
+    Dv = v.shape[-1]
+    S = np.zeros((B, H, Dk, Dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    o = np.zeros((B, T, H, Dv))
+    for b in range(B):
+        for h in range(H):
+            Sbh = S[b, h]
+            for c0 in range(0, T, chunk):
+                c1 = min(c0 + chunk, T)
+                Q = q[b, c0:c1, h]
+                K = k[b, c0:c1, h]
+                V = v[b, c0:c1, h]
+                bt = beta[b, c0:c1, h]
+                G = np.cumsum(g[b, c0:c1, h], axis=0)          # [n, Dk]
+                n = c1 - c0
+                diff = G[:, None, :] - G[None, :, :]            # G_i - G_j
+                lower_eq = np.tril(np.ones((n, n), dtype=bool))
+                diff = np.where(lower_eq[..., None], diff, -np.inf)
+                decay = np.exp(diff)                            # 0 above diagonal
+                Akk = bt[:, None] * np.einsum("id,jd,ijd->ij", K, K, decay)
+                Akk = np.tril(Akk, -1)
+                Aqk = np.einsum("id,jd,ijd->ij", Q, K, decay)
+                gam = np.exp(G)
+                rhs = bt[:, None] * (V - (K * gam) @ Sbh)
+                U = np.linalg.solve(np.eye(n) + Akk, rhs)
+                o[b, c0:c1, h] = (Q * gam) @ Sbh + Aqk @ U
+                Kc = K * np.exp(G[-1][None, :] - G)
+                Sbh = np.exp(G[-1])[:, None] * Sbh + Kc.T @ U
+            S[b, h] = Sbh
+    return o, S
+
+
+# ---------------------------------------------------------------------------
+# Chunk-size safety bound
+# ---------------------------------------------------------------------------
+
+def safe_chunk_size(g_min, dtype_max, headroom=2.0 ** 10):
+    """Largest tile n whose factored inverse retention exp(-g_min * n) stays
+    below dtype_max / headroom: floor(ln(dtype_max / headroom) / (-g_min))
+    ([KDA-demo] §1.4 safe_chunk_size; the pages leave the headroom open, 2^10
+    is this project's reading).  g_min must be negative and finite."""
+    if not (math.isfinite(g_min) and g_min < 0):
+        raise ValueError("g_min must be finite and negative")
+    val = math.log(dtype_max / headroom) / (-g_min)
+    return max(0, int(math.floor(val)))

@@ -1,0 +1,384 @@
+"""Pins of the fp64 oracle to facts the pages and mathematics fix.
+
+None of these tests retypes an oracle formula: they use closed forms, limit
+cases the pages state, exact rational arithmetic on a different formulation
+(explicit transition matrices), the affine (KCP) structure, the chunkwise
+reorganisation and numbers printed on the pages (tests/golden).
+"""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import kda_oracle as ora
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_numbers.json")))
+
+BF16_MAX = float((2 - 2 ** -7) * 2 ** 127)
+F32_MAX = float(np.finfo(np.float32).max)
+F16_MAX = 65504.0
+F64_MAX = float(np.finfo(np.float64).max)
+
+
+def rand_problem(rng, B=2, T=37, H=3, Dk=8, Dv=6, s0=True):
+    q = ora.l2_normalize(rng.standard_normal((B, T, H, Dk)))
+    k = ora.l2_normalize(rng.standard_normal((B, T, H, Dk)))
+    v = rng.standard_normal((B, T, H, Dv))
+    g = ora.bounded_log_decay(rng.standard_normal((B, T, H, Dk)), rng.normal(0, 0.5, H))
+    beta = ora.sigmoid(rng.standard_normal((B, T, H)))
+    S0 = rng.normal(0, 0.3, (B, H, Dk, Dv)) if s0 else None
+    return q, k, v, g, beta, S0
+
+
+def rel(a, b):
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# --------------------------------------------------------------------- gates
+
+class TestGate:
+    """Bounded log-decay, [LinAttn-demo] Eq. 8 / [Impl-KDA] 'La décroissance bornée'."""
+
+    def test_zero_logit_gives_half_bound(self):
+        # sigmoid(0) = 1/2 for every head scale: g = g_min / 2 exactly.
+        z = np.zeros((1, 4, 3, 5))
+        for A in ([0.0, 1.0, -2.0], [3.0, 0.3, -0.7]):
+            g = ora.bounded_log_decay(z, np.array(A), -5.0)
+            assert np.all(g == -2.5)
+
+    def test_strict_bounds_and_alpha_range(self):
+        rng = np.random.default_rng(0)
+        z = rng.normal(0, 6, (2, 50, 4, 16))
+        g = ora.bounded_log_decay(z, rng.normal(0, 0.5, 4), -5.0)
+        assert np.all(g < 0) and np.all(g > -5.0)
+        a = np.exp(g)
+        assert np.all(a < 1) and np.all(a > math.exp(-5.0))
+
+    def test_inverse_saturation_monotone(self):
+        # [LinAttn-demo] Tab 2: larger z forgets more (alpha decreases in z).
+        z = np.linspace(-8, 8, 401).reshape(1, -1, 1, 1)
+        a = np.exp(ora.bounded_log_decay(z, np.array([0.4]), -5.0)).ravel()
+        assert np.all(np.diff(a) < 0)
+        # saturation limits: alpha -> 1 as z -> -inf, alpha -> exp(g_min) as z -> +inf
+        ends = np.exp(ora.bounded_log_decay(np.array([[[[-60.0]], [[60.0]]]]), np.array([0.0]), -5.0)).ravel()
+        assert abs(ends[0] - 1.0) < 1e-15 and abs(ends[1] - math.exp(-5.0)) < 1e-15
+
+    def test_head_scale_multiplies_logit(self):
+        # exp(A_log) scales z: A_log = ln 2 at z equals A_log = 0 at 2z.
+        z = np.linspace(-3, 3, 13).reshape(1, -1, 1, 1)
+        g1 = ora.bounded_log_decay(z, np.array([math.log(2.0)]), -5.0)
+        g2 = ora.bounded_log_decay(2 * z, np.array([0.0]), -5.0)
+        assert np.max(np.abs(g1 - g2)) < 1e-15
+
+    def test_gate_derivative_minimum_matches_page(self):
+        # [LinAttn-demo] Tab 3: alpha floor 0.01 (g_min = ln 0.01), A_log = 0:
+        # d alpha / dz has its minimum about -0.29 near z = -1.5.
+        gold = GOLD["gate_v2_dalpha_dz_min"]
+        gmin = math.log(gold["alpha_floor"])
+        z = np.linspace(-6, 6, 120001)
+        h = 1e-5
+        ap = np.exp(ora.bounded_log_decay((z + h).reshape(1, -1, 1, 1), np.array([gold["A_log"]]), gmin)).ravel()
+        am = np.exp(ora.bounded_log_decay((z - h).reshape(1, -1, 1, 1), np.array([gold["A_log"]]), gmin)).ravel()
+        d = (ap - am) / (2 * h)
+        i = int(np.argmin(d))
+        assert abs(d[i] - gold["value"]) <= gold["abs_tol"]
+        assert abs(z[i] - gold["at_z"]) <= gold["z_tol"]
+
+    def test_sigmoid_closed_values(self):
+        x = np.array([0.0, math.log(3.0), -math.log(3.0), 800.0, -800.0])
+        s = ora.sigmoid(x)
+        assert s[0] == 0.5
+        assert abs(s[1] - 0.75) < 1e-16 and abs(s[2] - 0.25) < 1e-16
+        assert s[3] == 1.0 and s[4] == 0.0
+
+
+class TestL2Norm:
+    def test_unit_norm_and_scale_invariance(self):
+        rng = np.random.default_rng(1)
+        x = rng.standard_normal((5, 7, 128))
+        y = ora.l2_normalize(x, eps=0.0)
+        assert np.max(np.abs(np.linalg.norm(y, axis=-1) - 1)) < 1e-14
+        assert np.max(np.abs(ora.l2_normalize(37.5 * x, eps=0.0) - y)) < 1e-15
+
+    def test_epsilon_is_inside_the_root(self):
+        # a vector of squared norm 3e-6 with eps 1e-6 has norm sqrt(3/4) after scaling
+        x = np.full((1, 3), 1e-3)
+        y = ora.l2_normalize(x, eps=1e-6)
+        assert abs(np.linalg.norm(y) - math.sqrt(0.75)) < 1e-12
+
+
+# ------------------------------------------------------------ limit behaviours
+
+class TestLimits:
+    """[Impl-KDA] 'Vérifier votre implémentation', Test 1."""
+
+    def test_beta_zero_is_pure_decay_bitwise(self):
+        rng = np.random.default_rng(2)
+        q, k, v, g, beta, S0 = rand_problem(rng, T=1)
+        _, S1 = ora.recurrent(q, k, v, g, np.zeros_like(beta), S0)
+        expect = np.exp(g[:, 0])[..., None] * S0
+        assert np.array_equal(S1, expect)
+
+    def test_unit_gates_recall_value_exactly(self):
+        rng = np.random.default_rng(3)
+        B, H, Dk, Dv = 2, 3, 16, 9
+        k = ora.l2_normalize(rng.standard_normal((B, 1, H, Dk)), eps=0.0)
+        v = rng.standard_normal((B, 1, H, Dv))
+        _, S1 = ora.recurrent(k, k, v, np.zeros((B, 1, H, Dk)), np.ones((B, 1, H)), None)
+        readout = np.einsum("bhk,bhkv->bhv", k[:, 0], S1)
+        assert np.max(np.abs(readout - v[:, 0])) < 1e-15 * 16
+
+    def test_repeated_key_closed_form(self):
+        # same key written n times with the same value, alpha = 1:
+        # the retrieved value is (1 - (1 - beta)^n) v.
+        rng = np.random.default_rng(4)
+        Dk, Dv, n, b = 8, 5, 9, 0.35
+        kk = ora.l2_normalize(rng.standard_normal(Dk), eps=0.0)
+        vv = rng.standard_normal(Dv)
+        k = np.tile(kk, (1, n, 1, 1))
+        v = np.tile(vv, (1, n, 1, 1))
+        o, S = ora.recurrent(k, k, v, np.zeros((1, n, 1, Dk)), np.full((1, n, 1), b), None)
+        for t in range(n):
+            expect = (1 - (1 - b) ** (t + 1)) * vv
+            assert np.max(np.abs(o[0, t, 0] - expect)) < 1e-14
+
+    def test_latest_value_wins_for_unit_beta(self):
+        # [KDA-demo] §1.3: with the same key and changing values, retrieval
+        # follows the newest value (beta = 1, alpha = 1 overwrites exactly).
+        rng = np.random.default_rng(5)
+        Dk, Dv, n = 6, 4, 7
+        kk = ora.l2_normalize(rng.standard_normal(Dk), eps=0.0)
+        k = np.tile(kk, (1, n, 1, 1))
+        v = rng.standard_normal((1, n, 1, Dv))
+        o, _ = ora.recurrent(k, k, v, np.zeros((1, n, 1, Dk)), np.ones((1, n, 1)), None)
+        assert np.max(np.abs(o - v)) < 1e-14
+
+    def test_orthonormal_keys_textbook_delta_rule(self):
+        # DeltaNet special case (alpha = beta = 1): S = sum_i k_i v_i^T for
+        # orthonormal keys, so key k_j retrieves v_j.
+        rng = np.random.default_rng(6)
+        Dk, Dv = 12, 7
+        Qm, _ = np.linalg.qr(rng.standard_normal((Dk, Dk)))
+        k = Qm.T.reshape(1, Dk, 1, Dk)
+        v = rng.standard_normal((1, Dk, 1, Dv))
+        _, S = ora.recurrent(k, k, v, np.zeros((1, Dk, 1, Dk)), np.ones((1, Dk, 1)), None)
+        assert np.max(np.abs(S[0, 0] - Qm @ v[0, :, 0])) < 1e-14
+        assert np.max(np.abs(Qm.T @ S[0, 0] - v[0, :, 0])) < 1e-14
+
+
+# ------------------------------------------------- exact rational brute force
+
+def _frac_transition_run(ks, vs, qs, alphas, betas, S0):
+    """Exact arithmetic on the transition-matrix form S_t = M_t S_{t-1} + beta k v^T,
+    M_t = (I - beta k k^T) Diag(alpha): a different formulation from the oracle's
+    rank-1 update sequence."""
+    Dk = len(ks[0])
+    Dv = len(vs[0])
+    S = [[Fraction(x) for x in row] for row in S0]
+    outs = []
+    for k, v, q, a, b in zip(ks, vs, qs, alphas, betas):
+        M = [[((1 if i == j else 0) - b * k[i] * k[j]) * a[j] for j in range(Dk)] for i in range(Dk)]
+        S = [[sum(M[i][m] * S[m][c] for m in range(Dk)) + b * k[i] * v[c] for c in range(Dv)]
+             for i in range(Dk)]
+        outs.append([sum(S[i][c] * q[i] for i in range(Dk)) for c in range(Dv)])
+    return outs, S
+
+
+def test_exact_rational_recurrence():
+    F = Fraction
+    ks = [(F(3, 5), F(4, 5)), (F(-4, 5), F(3, 5)), (F(5, 13), F(12, 13)),
+          (F(1), F(0)), (F(8, 17), F(-15, 17))]
+    vs = [(F(1, 2), F(-3)), (F(2), F(1, 7)), (F(-5, 4), F(3, 8)), (F(1, 3), F(1)), (F(0), F(-2))]
+    qs = [(F(1), F(2)), (F(-1, 2), F(1, 4)), (F(3), F(-1)), (F(2, 3), F(5, 6)), (F(1, 9), F(-7, 3))]
+    alphas = [(F(1, 2), F(3, 4)), (F(7, 8), F(1, 4)), (F(1), F(2, 3)), (F(5, 6), F(9, 10)), (F(1, 5), F(1))]
+    betas = [F(1, 3), F(1, 2), F(9, 10), F(1), F(1, 4)]
+    S0 = [(F(1, 2), F(-1)), (F(3, 2), F(2, 5))]
+    o_ex, S_ex = _frac_transition_run(ks, vs, qs, alphas, betas, S0)
+
+    f = lambda rows: np.array([[float(x) for x in r] for r in rows])
+    k = f(ks).reshape(1, 5, 1, 2)
+    v = f(vs).reshape(1, 5, 1, 2)
+    q = f(qs).reshape(1, 5, 1, 2)
+    g = np.log(f(alphas)).reshape(1, 5, 1, 2)
+    beta = np.array([float(b) for b in betas]).reshape(1, 5, 1)
+    o, S = ora.recurrent(q, k, v, g, beta, f(S0).reshape(1, 1, 2, 2))
+    assert np.max(np.abs(o[0, :, 0] - f(o_ex))) < 1e-14
+    assert np.max(np.abs(S[0, 0] - f(S_ex))) < 1e-14
+    # the erase-before-decay reading of the other pages gives a different model
+    S_alt = f(S0)
+    for t in range(5):
+        kt = k[0, t, 0]
+        S_alt = np.exp(g[0, t, 0])[:, None] * S_alt + beta[0, t, 0] * np.outer(kt, v[0, t, 0] - S_alt.T @ kt)
+    assert np.max(np.abs(S_alt - f(S_ex))) > 1e-3
+
+
+# --------------------------------------------------- affine structure (KCP)
+
+class TestAffine:
+    def test_kcp_identity(self):
+        # [Impl-KDA] Test 2: run(S0) = run(0) + (prod M_t) S0.
+        gold = GOLD["kcp_identity_max_err"]
+        rng = np.random.default_rng(7)
+        q, k, v, g, beta, S0 = rand_problem(rng, T=53)
+        _, S_direct = ora.recurrent(q, k, v, g, beta, S0)
+        M, S_tilde = ora.segment_fragment(k, v, g, beta)
+        err = np.max(np.abs(S_direct - (S_tilde + M @ S0)))
+        assert err < min(gold["bar"], 1e-12)
+
+    @pytest.mark.parametrize("nseg", [2, 4, 8])
+    def test_prefix_scan_equals_full_run(self, nseg):
+        # [Impl-KDA] Test 3 with 2, 4 and 8 simulated ranks (uneven cuts).
+        gold = GOLD["prefix_scan_4_ranks_max_err"]
+        rng = np.random.default_rng(8 + nseg)
+        q, k, v, g, beta, _ = rand_problem(rng, T=61, s0=False)
+        cuts = np.sort(rng.choice(np.arange(1, 61), nseg - 1, replace=False))
+        bounds = [0, *cuts.tolist(), 61]
+        frags = [ora.segment_fragment(k[:, a:b], v[:, a:b], g[:, a:b], beta[:, a:b])
+                 for a, b in zip(bounds[:-1], bounds[1:])]
+        states = ora.compose(frags)
+        _, S_full = ora.recurrent(q, k, v, g, beta, None)
+        assert np.max(np.abs(states[-1] - S_full)) < min(gold["bar"], 1e-12)
+        for s, b in enumerate(bounds[1:]):
+            _, S_pref = ora.recurrent(q[:, :b], k[:, :b], v[:, :b], g[:, :b], beta[:, :b], None)
+            assert np.max(np.abs(states[s] - S_pref)) < 1e-12
+
+    def test_composition_is_associative(self):
+        rng = np.random.default_rng(9)
+        q, k, v, g, beta, _ = rand_problem(rng, T=30, s0=False)
+        a, b, c = [ora.segment_fragment(k[:, i:j], v[:, i:j], g[:, i:j], beta[:, i:j])
+                   for i, j in ((0, 9), (9, 20), (20, 30))]
+        left = ora.compose_pair(ora.compose_pair(c, b), a)
+        right = ora.compose_pair(c, ora.compose_pair(b, a))
+        whole = ora.segment_fragment(k, v, g, beta)
+        for x, y, w in zip(left, right, whole):
+            assert np.max(np.abs(x - y)) < 1e-12 and np.max(np.abs(x - w)) < 1e-12
+
+    def test_linear_in_values_and_state(self):
+        # [Impl-KDA] 'Que teste réellement le test 2': the recurrence is affine,
+        # so (o, S_T) is linear in (V, S0) jointly.
+        rng = np.random.default_rng(10)
+        q, k, v1, g, beta, S1 = rand_problem(rng, T=25)
+        v2 = rng.standard_normal(v1.shape)
+        S2 = rng.standard_normal(S1.shape)
+        a, b = 0.7, -1.9
+        o1, T1 = ora.recurrent(q, k, v1, g, beta, S1)
+        o2, T2 = ora.recurrent(q, k, v2, g, beta, S2)
+        o3, T3 = ora.recurrent(q, k, a * v1 + b * v2, g, beta, a * S1 + b * S2)
+        assert rel(o3, a * o1 + b * o2) < 1e-12 and rel(T3, a * T1 + b * T2) < 1e-12
+
+    def test_resume_from_state(self):
+        rng = np.random.default_rng(11)
+        q, k, v, g, beta, S0 = rand_problem(rng, T=40)
+        o, S = ora.recurrent(q, k, v, g, beta, S0)
+        oa, Sa = ora.recurrent(q[:, :17], k[:, :17], v[:, :17], g[:, :17], beta[:, :17], S0)
+        ob, Sb = ora.recurrent(q[:, 17:], k[:, 17:], v[:, 17:], g[:, 17:], beta[:, 17:], Sa)
+        assert rel(np.concatenate([oa, ob], 1), o) < 1e-13 and rel(Sb, S) < 1e-13
+
+    def test_transition_matches_one_token(self):
+        rng = np.random.default_rng(12)
+        q, k, v, g, beta, S0 = rand_problem(rng, T=1)
+        _, S1 = ora.recurrent(q, k, v, g, beta, S0)
+        M = ora.transition(k[:, 0], beta[:, 0], np.exp(g[:, 0]))
+        expect = M @ S0 + beta[:, 0][..., None, None] * np.einsum("bhk,bhv->bhkv", k[:, 0], v[:, 0])
+        assert np.max(np.abs(S1 - expect)) < 1e-14
+
+
+# ----------------------------------------------------------- chunkwise form
+
+@pytest.mark.parametrize("chunk", [8, 16, 32, 64])
+def test_chunkwise_equals_recurrence(chunk):
+    # [KDA-demo] Tab 8: the two forms agree to fp64 precision (bar 1e-10).
+    gold = GOLD["recurrent_vs_chunk_fp64"]
+    rng = np.random.default_rng(20 + chunk)
+    q, k, v, g, beta, S0 = rand_problem(rng, B=2, T=141, H=2, Dk=16, Dv=12)
+    o_r, S_r = ora.recurrent(q, k, v, g, beta, S0)
+    o_c, S_c = ora.chunkwise(q, k, v, g, beta, S0, chunk=chunk)
+    assert rel(o_c, o_r) < min(gold["bar"], 1e-12)
+    assert rel(S_c, S_r) < min(gold["bar"], 1e-12)
+
+
+def test_chunkwise_survives_strongest_decay():
+    # worst-case gate (g = g_min on every token) over a 64-token chunk: the
+    # element-wise factors stay finite and the forms still agree.
+    rng = np.random.default_rng(30)
+    q, k, v, _, beta, S0 = rand_problem(rng, B=1, T=128, H=1, Dk=8, Dv=8)
+    g = np.full(q.shape, -5.0 + 1e-9)
+    o_r, S_r = ora.recurrent(q, k, v, g, beta, S0)
+    o_c, S_c = ora.chunkwise(q, k, v, g, beta, S0, chunk=64)
+    assert np.all(np.isfinite(o_c)) and rel(o_c, o_r) < 1e-12 and rel(S_c, S_r) < 1e-12
+
+
+def test_step_matches_sequence():
+    # [KDA-demo] Tab 13: stepping token by token equals the sequence form.
+    rng = np.random.default_rng(31)
+    B, T, H, Dk, Dv = 2, 9, 3, 8, 5
+    q, k, z = (rng.standard_normal((B, T, H, Dk)) for _ in range(3))
+    v = rng.standard_normal((B, T, H, Dv))
+    br = rng.standard_normal((B, T, H))
+    A = rng.normal(0, 0.5, H)
+    S0 = rng.standard_normal((B, H, Dk, Dv))
+    o, S = ora.forward(q, k, v, z, br, A, S0)
+    St = S0
+    for t in range(T):
+        ot, St = ora.step(St, q[:, t], k[:, t], v[:, t], z[:, t], br[:, t], A)
+        assert np.max(np.abs(ot - o[:, t])) < 1e-13
+    assert np.max(np.abs(St - S)) < 1e-13
+
+
+def test_switches_off_take_activated_inputs():
+    # [KDA-layer] 'three in_kernel switches': with a switch off the caller has
+    # already applied the activation.
+    rng = np.random.default_rng(32)
+    B, T, H, Dk, Dv = 1, 6, 2, 4, 3
+    q, k, z = (rng.standard_normal((B, T, H, Dk)) for _ in range(3))
+    v = rng.standard_normal((B, T, H, Dv))
+    br = rng.standard_normal((B, T, H))
+    A = rng.normal(0, 0.5, H)
+    o_on, S_on = ora.forward(q, k, v, z, br, A, flags=ora.FLAGS_DEFAULT)
+    o_off, S_off = ora.forward(q / np.linalg.norm(q, axis=-1, keepdims=True),
+                               k / np.linalg.norm(k, axis=-1, keepdims=True), v,
+                               -5.0 / (1 + np.exp(-np.exp(A)[:, None] * z)),
+                               1 / (1 + np.exp(-br)), A, flags=0)
+    # eps = 1e-6 inside the root makes the only difference (relative ~1e-7)
+    assert rel(o_off, o_on) < 1e-5 and rel(S_off, S_on) < 1e-5
+
+
+# --------------------------------------------------------- safe chunk size
+
+class TestSafeChunk:
+    """[KDA-demo] §1.4 and Tab 9; [Impl-KDA] 'La décroissance bornée'."""
+
+    def test_page_values(self):
+        s_bf = ora.safe_chunk_size(-5.0, BF16_MAX)
+        s_32 = ora.safe_chunk_size(-5.0, F32_MAX)
+        assert s_bf == GOLD["safe_tile_g_min_5"]["value"] == s_32
+        assert s_bf < GOLD["unsafe_tile_g_min_5"]["value"]
+        assert ora.safe_chunk_size(GOLD["g_min_10_overflows_at_16"]["value"], BF16_MAX) < 16
+        assert ora.safe_chunk_size(-10.0, BF16_MAX) == 8
+        assert ora.safe_chunk_size(-5.0, F16_MAX) == 0
+        assert ora.safe_chunk_size(-5.0, F64_MAX) == 140
+        gold = GOLD["exp80"]
+        assert abs(math.exp(80) - gold["value"]) <= gold["rel_tol"] * gold["value"]
+        assert abs(BF16_MAX - GOLD["bf16_max"]["value"]) <= GOLD["bf16_max"]["rel_tol"] * BF16_MAX
+        assert abs(F32_MAX - GOLD["fp32_max"]["value"]) <= GOLD["fp32_max"]["rel_tol"] * F32_MAX
+
+    def test_bf16_and_fp32_curves_coincide(self):
+        for gm in np.linspace(-12, -0.5, 200):
+            assert ora.safe_chunk_size(gm, BF16_MAX) == ora.safe_chunk_size(gm, F32_MAX)
+
+    def test_fp32_inverse_retention_overflow_edge(self):
+        # worst case alpha = exp(g_min): 1/gamma over n tokens is exp(5 n);
+        # finite in fp32 at 17 tokens, inf at 18 (headroom 1 gives 17).
+        with np.errstate(over="ignore"):
+            assert np.isfinite(np.float32(math.exp(5 * 17)))
+            assert np.isinf(np.float32(math.exp(5 * 18)))
+        assert ora.safe_chunk_size(-5.0, F32_MAX, headroom=1.0) == 17
+
+    def test_rejects_bad_bound(self):
+        for bad in (0.0, 1.0, float("nan"), float("-inf")):
+            with pytest.raises(ValueError):
+                ora.safe_chunk_size(bad, F32_MAX)
