@@ -1,0 +1,150 @@
+// kda_api.cpp - the exported C ABI: host validation, sizing and dispatch.
+//
+// Every entry point validates all arguments before it enqueues anything, and
+// validation itself makes no HIP call, so rejected calls are side-effect free
+// and can be exercised on a machine without a GPU.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+constexpr double kBf16Max = 3.3895313892515355e38;  // (2 - 2^-7) * 2^127
+constexpr double kF32Max = 3.4028234663852886e38;
+constexpr double kHeadroom = 1024.0;
+constexpr int kFactorTile = 16;  // token tile of the factored decay products
+
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dtype_ok(kda_dtype dt) { return dt == KDA_F32 || dt == KDA_BF16; }
+bool flags_ok(unsigned f) { return (f & ~7u) == 0; }
+int elem_bytes(kda_dtype dt) { return dt == KDA_BF16 ? 2 : 4; }
+
+bool gmin_ok(float g_min) { return isfinite(g_min) && g_min < 0.0f; }
+
+// Checks a pointer that must be present; optional ones pass when NULL.
+kda_status need(const void* p) {
+    if (!p) return KDA_ERR_NULL;
+    return aligned16(p) ? KDA_OK : KDA_ERR_ALIGN;
+}
+kda_status maybe(const void* p) { return (!p || aligned16(p)) ? KDA_OK : KDA_ERR_ALIGN; }
+
+#define KDA_TRY(expr)                        \
+    do {                                     \
+        const kda_status st_ = (expr);       \
+        if (st_ != KDA_OK) return st_;       \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int kda_safe_chunk_size(float g_min, kda_dtype dt) {
+    if (!gmin_ok(g_min) || !dtype_ok(dt)) return -1;
+    const double mx = dt == KDA_BF16 ? kBf16Max : kF32Max;
+    const double v = log(mx / kHeadroom) / (-(double)g_min);
+    return v < 0 ? 0 : (int)floor(v);
+}
+
+size_t kda_chunk_fwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype dt) {
+    if (chunk == 0) chunk = 64;
+    if (B < 0 || T < 0 || H < 0 || !dim_ok(Dk) || !dim_ok(Dv) || !dtype_ok(dt)) return 0;
+    if (chunk != 16 && chunk != 32 && chunk != 64) return 0;
+    const size_t nc = (size_t)(T + chunk - 1) / (size_t)chunk;
+    const kda::BlockLayout L = kda::block_layout(elem_bytes(dt), Dk, chunk);
+    return (size_t)B * (size_t)H * nc * L.bytes;
+}
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* z,
+                         const void* beta_raw, const float* A_log, const float* S0,
+                         void* o, float* S_out, float* M_out, void* P_out,
+                         int B, int T, int H, int Dk, int Dv, int chunk,
+                         float g_min, unsigned flags, kda_dtype dt,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!dtype_ok(dt) || !flags_ok(flags)) return KDA_ERR_DTYPE;
+    if (chunk == 0) chunk = 64;
+    if (B < 0 || T < 0 || H < 0 || !dim_ok(Dk) || !dim_ok(Dv)) return KDA_ERR_SHAPE;
+    if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_SHAPE;
+    if (!gmin_ok(g_min) || kda_safe_chunk_size(g_min, dt) < kFactorTile) return KDA_ERR_GATE;
+    if ((size_t)B * (size_t)T * (size_t)H * 128u > ((size_t)1 << 46)) return KDA_ERR_SHAPE;
+    if (B == 0 || H == 0) return KDA_OK;
+    if (T > 0) {
+        KDA_TRY(need(q)); KDA_TRY(need(k)); KDA_TRY(need(v)); KDA_TRY(need(z));
+        KDA_TRY(need(beta_raw)); KDA_TRY(need(o));
+        if (flags & KDA_GATE_IN_KERNEL) KDA_TRY(need(A_log));
+        else KDA_TRY(maybe(A_log));
+    }
+    KDA_TRY(maybe(S0)); KDA_TRY(maybe(S_out)); KDA_TRY(maybe(M_out)); KDA_TRY(maybe(P_out));
+    const size_t ws_need = kda_chunk_fwd_workspace(B, T, H, Dk, Dv, chunk, dt);
+    if (ws_need > 0) {
+        if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+            workspace_bytes < ws_need)
+            return KDA_ERR_WORKSPACE;
+    }
+    kda::ChunkArgs a{};
+    a.q = q; a.k = k; a.v = v; a.z = z; a.beta_raw = beta_raw; a.A_log = A_log; a.S0 = S0;
+    a.o = o; a.S_out = S_out; a.M_out = M_out; a.P_out = P_out; a.ws = workspace;
+    a.B = B; a.T = T; a.H = H; a.Dv = Dv; a.NC = (T + chunk - 1) / chunk;
+    a.g_min = g_min; a.flags = flags;
+    return kda::launch_chunk(dt == KDA_BF16 ? 1 : 0, Dk, chunk, a, stream) == hipSuccess ? KDA_OK
+                                                                                         : KDA_ERR_HIP;
+}
+
+kda_status kda_step(const void* q, const void* k, const void* v, const void* z,
+                    const void* beta_raw, const float* A_log, float* S, void* o,
+                    int B, int H, int Dk, int Dv, float g_min, unsigned flags,
+                    kda_dtype dt, hipStream_t stream) {
+    if (!dtype_ok(dt) || !flags_ok(flags)) return KDA_ERR_DTYPE;
+    if (B < 0 || H < 0 || !dim_ok(Dk) || !dim_ok(Dv)) return KDA_ERR_SHAPE;
+    if (!gmin_ok(g_min)) return KDA_ERR_GATE;
+    if (B == 0 || H == 0) return KDA_OK;
+    KDA_TRY(need(q)); KDA_TRY(need(k)); KDA_TRY(need(v)); KDA_TRY(need(z));
+    KDA_TRY(need(beta_raw)); KDA_TRY(need(S)); KDA_TRY(need(o));
+    if (flags & KDA_GATE_IN_KERNEL) KDA_TRY(need(A_log));
+    else KDA_TRY(maybe(A_log));
+    kda::StepArgs a{q, k, v, z, beta_raw, A_log, S, o, B, H, g_min, flags};
+    return kda::launch_step(dt == KDA_BF16 ? 1 : 0, Dk, Dv, a, stream) == hipSuccess ? KDA_OK
+                                                                                     : KDA_ERR_HIP;
+}
+
+kda_status kda_segment_compose(int n_seg, const float* M, const float* S_tilde,
+                               const float* S_in, float* S_prefix,
+                               int B, int H, int Dk, int Dv, hipStream_t stream) {
+    if (n_seg < 0 || B < 0 || H < 0 || !dim_ok(Dk) || !dim_ok(Dv)) return KDA_ERR_SHAPE;
+    if (n_seg == 0 || B == 0 || H == 0) return KDA_OK;
+    KDA_TRY(need(M)); KDA_TRY(need(S_tilde)); KDA_TRY(need(S_prefix)); KDA_TRY(maybe(S_in));
+    kda::ComposeArgs a{M, S_tilde, S_in, S_prefix, n_seg, B, H, Dv};
+    return kda::launch_compose(Dk, a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_segment_fixup(int n_seg, const void* P, const float* S_in,
+                             const float* S_prefix, void* o, int B, int T_seg,
+                             int H, int Dk, int Dv, kda_dtype dt, hipStream_t stream) {
+    if (!dtype_ok(dt)) return KDA_ERR_DTYPE;
+    if (n_seg < 0 || B < 0 || T_seg < 0 || H < 0 || !dim_ok(Dk) || !dim_ok(Dv)) return KDA_ERR_SHAPE;
+    if (n_seg == 0 || B == 0 || H == 0 || T_seg == 0) return KDA_OK;
+    KDA_TRY(need(P)); KDA_TRY(need(o)); KDA_TRY(maybe(S_in));
+    if (n_seg > 1) KDA_TRY(need(S_prefix));
+    else KDA_TRY(maybe(S_prefix));
+    kda::FixupArgs a{P, S_in, S_prefix, o, n_seg, B, T_seg, H, Dv};
+    return kda::launch_fixup(dt == KDA_BF16 ? 1 : 0, Dk, a, stream) == hipSuccess ? KDA_OK
+                                                                                  : KDA_ERR_HIP;
+}
+
+const char* kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_NULL: return "a required pointer is NULL";
+        case KDA_ERR_SHAPE: return "unsupported or negative size";
+        case KDA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case KDA_ERR_DTYPE: return "unknown dtype or switch bits";
+        case KDA_ERR_GATE: return "g_min is not finite and negative, or the 16-token tile is unsafe for it";
+        case KDA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case KDA_ERR_HIP: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

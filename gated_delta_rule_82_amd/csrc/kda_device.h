@@ -1,0 +1,182 @@
+// kda_device.h - device-side building blocks shared by the gfx950 KDA kernels.
+//
+// Matrix-core convention used throughout (wave64, one 16x16 output tile):
+//
+//   * C layout ("column owner"): lane l holds X[4*(l/16) + i][l % 16], i = 0..3.
+//     This is the accumulator layout of v_mfma_f32_16x16x{32_bf16,4_f32}.
+//   * Operand fragment for one 32-long contraction step: lane l supplies row
+//     (l % 16) of A (or column (l % 16) of B) at 8 contraction slots
+//         slot j < 4  -> index 4*(l/16) + j
+//         slot j >= 4 -> index 16 + 4*(l/16) + (j - 4).
+//     A and B use the same slot map, so the product is exact whatever order the
+//     hardware sums the slots in.  The map is chosen so that two C-layout tiles
+//     stacked along the contraction axis (rows 0..15 and 16..31) ARE the B
+//     fragment of the next product: no data moves across lanes.
+//   * R layout ("row owner"): lane l holds X[l % 16][4*(l/16) + i].  For 16x16
+//     matrices, mm(R(X), C(Y)) = C(X Y) and mm(C(Y), R(X)) = R(X Y).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16_t;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kL2Eps = 1e-6f;
+
+// ---------------------------------------------------------------- scalars
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float sigmoidf_(float x) {
+    // 1 / (1 + e^-x); exp2 of a large positive argument gives +inf -> 0.
+    return 1.0f / (1.0f + exp2f(-x * kLog2e));
+}
+
+template <typename T> __device__ __forceinline__ float to_f(T x);
+template <> __device__ __forceinline__ float to_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float x) { return (bf16_t)x; }
+
+// Load 4 consecutive elements (8-byte aligned for bf16, 16-byte for fp32).
+__device__ __forceinline__ void load4(const float* p, float out[4]) {
+    float4 v = *reinterpret_cast<const float4*>(p);
+    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+}
+__device__ __forceinline__ void load4(const bf16_t* p, float out[4]) {
+    uint2 v = *reinterpret_cast<const uint2*>(p);
+    out[0] = bf16_bits_to_float(v.x & 0xffffu);
+    out[1] = bf16_bits_to_float(v.x >> 16);
+    out[2] = bf16_bits_to_float(v.y & 0xffffu);
+    out[3] = bf16_bits_to_float(v.y >> 16);
+}
+
+// ---------------------------------------------------------------- fragments
+
+__host__ __device__ constexpr int slot_index(int grp, int j) {
+    return j < 4 ? 4 * grp + j : 16 + 4 * grp + (j - 4);
+}
+
+template <typename T> struct Frag;
+template <> struct Frag<bf16_t> {
+    bf16x8 v;
+    __device__ __forceinline__ void set(int j, float x) { v[j] = (bf16_t)x; }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = (bf16_t)0.0f;
+    }
+};
+template <> struct Frag<float> {
+    float v[8];
+    __device__ __forceinline__ void set(int j, float x) { v[j] = x; }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+    }
+};
+
+// acc += A * B over one 32-long contraction step.
+__device__ __forceinline__ floatx4 mma(const Frag<bf16_t>& a, const Frag<bf16_t>& b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mma(const Frag<float>& a, const Frag<float>& b, floatx4 c) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], c, 0, 0, 0);
+    return c;
+}
+
+// Load / store a fragment from a fragment-major tile (64 lanes x 8 elements).
+__device__ __forceinline__ void frag_load(Frag<bf16_t>& f, const bf16_t* tile, int lane) {
+    f.v = *reinterpret_cast<const bf16x8*>(tile + lane * 8);
+}
+__device__ __forceinline__ void frag_load(Frag<float>& f, const float* tile, int lane) {
+    const float4* p = reinterpret_cast<const float4*>(tile + lane * 8);
+    float4 a = p[0], b = p[1];
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+__device__ __forceinline__ void frag_store(const Frag<bf16_t>& f, bf16_t* tile, int lane) {
+    *reinterpret_cast<bf16x8*>(tile + lane * 8) = f.v;
+}
+__device__ __forceinline__ void frag_store(const Frag<float>& f, float* tile, int lane) {
+    float4* p = reinterpret_cast<float4*>(tile + lane * 8);
+    p[0] = make_float4(f.v[0], f.v[1], f.v[2], f.v[3]);
+    p[1] = make_float4(f.v[4], f.v[5], f.v[6], f.v[7]);
+}
+
+// Store 4 values into one half (slots 0..3 or 4..7) of a lane's fragment slot.
+__device__ __forceinline__ void half_store(bf16_t* tile, int lane, int half, const float x[4]) {
+    bf16_t* p = tile + lane * 8 + half * 4;
+    uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (bf16_t)x[0]) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, (bf16_t)x[1]) << 16);
+    uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (bf16_t)x[2]) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, (bf16_t)x[3]) << 16);
+    *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+}
+__device__ __forceinline__ void half_store(float* tile, int lane, int half, const float x[4]) {
+    *reinterpret_cast<float4*>(tile + lane * 8 + half * 4) = make_float4(x[0], x[1], x[2], x[3]);
+}
+
+// B fragment from two C-layout tiles stacked along the contraction axis.
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_from_c(const floatx4& lo, const floatx4& hi) {
+    Frag<T> f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { f.set(i, lo[i]); f.set(4 + i, hi[i]); }
+    return f;
+}
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_from_c_lo(const floatx4& lo) {
+    Frag<T> f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { f.set(i, lo[i]); f.set(4 + i, 0.0f); }
+    return f;
+}
+
+// 16x16x16 fp32 product on the matrix core: acc = X * Y with X given as its
+// 4 contraction slots per lane (R layout of X or C layout of Y^T, see header).
+__device__ __forceinline__ floatx4 mm16(const floatx4& a, const floatx4& b) {
+    floatx4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], c, 0, 0, 0);
+    return c;
+}
+
+// ---------------------------------------------------------------- lane ops
+
+// Inclusive prefix sum over the 16 lanes of each DPP row (lane % 16 order).
+__device__ __forceinline__ float row_scan16(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, true));
+    return x;
+}
+
+// Sum over the four lane groups that share lane % 16.
+__device__ __forceinline__ float group_sum4(float x) {
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
+    return x;
+}
+
+// Map a linear block index so that consecutive logical blocks share an XCD
+// (blocks are dealt round-robin over the 8 XCDs of MI355X).
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+    constexpr int kXcd = 8;
+    if (nblocks % kXcd != 0) return bid;
+    return (bid % kXcd) * (nblocks / kXcd) + bid / kXcd;
+}
+
+}  // namespace kda

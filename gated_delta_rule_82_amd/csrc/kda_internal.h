@@ -1,0 +1,78 @@
+// kda_internal.h - host/device shared sizes and the internal launch interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+enum : unsigned { kQkL2 = 1u, kBetaSig = 2u, kGateIn = 4u };
+
+// Per chunk-head block of intermediates written by the intra kernel and read
+// by the inter kernel.  All matrices are stored as fragment-major tiles of
+// 64 lanes x 8 elements (see kda_device.h), in the operand element type:
+//   Kd  = K_hat * exp(G)           [C x Dk]   tiles (token block, channel step)
+//   Qp  = Q_hat * exp(G)           [C x Dk]   tiles (token block, channel step)
+//   KpT = (K_hat * exp(G_C - G))^T [Dk x C]   tiles (channel block, token step)
+//   Tb  = (I + A_kk)^-1 Diag(beta) [C x C]    tiles (token block, token step)
+//   Aqk = tril(Q K^T with decay)   [C x C]    tiles (token block, token step)
+// followed by gamma = exp(G_C) [Dk] in fp32.
+struct BlockLayout {
+    int nbk, ksd, nbd, ksc;
+    size_t kd, qp, kpt, tb, aqk, end;   // element offsets
+    size_t gamma_byte, bytes;
+};
+
+__host__ __device__ constexpr size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+__host__ __device__ constexpr BlockLayout block_layout(int elem_bytes, int DK, int C) {
+    BlockLayout L{};
+    L.nbk = C / 16;
+    L.ksd = (DK + 31) / 32;
+    L.nbd = DK / 16;
+    L.ksc = (C + 31) / 32;
+    const size_t tile = 512;
+    L.kd = 0;
+    L.qp = L.kd + (size_t)L.nbk * L.ksd * tile;
+    L.kpt = L.qp + (size_t)L.nbk * L.ksd * tile;
+    L.tb = L.kpt + (size_t)L.nbd * L.ksc * tile;
+    L.aqk = L.tb + (size_t)L.nbk * L.ksc * tile;
+    L.end = L.aqk + (size_t)L.nbk * L.ksc * tile;
+    L.gamma_byte = L.end * (size_t)elem_bytes;
+    L.bytes = round_up(L.gamma_byte + (size_t)DK * 4, 256);
+    return L;
+}
+
+struct StepArgs {
+    const void* q; const void* k; const void* v; const void* z; const void* beta_raw;
+    const float* A_log; float* S; void* o;
+    int B, H; float g_min; unsigned flags;
+};
+
+struct ChunkArgs {
+    const void* q; const void* k; const void* v; const void* z; const void* beta_raw;
+    const float* A_log; const float* S0;
+    void* o; float* S_out; float* M_out; void* P_out;
+    void* ws;
+    int B, T, H, Dv, NC;
+    float g_min; unsigned flags;
+};
+
+struct ComposeArgs {
+    const float* M; const float* S_tilde; const float* S_in; float* S_prefix;
+    int n_seg, B, H, Dv;
+};
+
+struct FixupArgs {
+    const void* P; const float* S_in; const float* S_prefix; void* o;
+    int n_seg, B, T_seg, H, Dv;
+};
+
+// dt: 0 = fp32, 1 = bf16.  Return the launch status (hipSuccess on success).
+hipError_t launch_step(int dt, int DK, int DV, const StepArgs& a, hipStream_t s);
+hipError_t launch_chunk(int dt, int DK, int C, const ChunkArgs& a, hipStream_t s);
+hipError_t launch_compose(int DK, const ComposeArgs& a, hipStream_t s);
+hipError_t launch_fixup(int dt, int DK, const FixupArgs& a, hipStream_t s);
+
+}  // namespace kda

@@ -1,0 +1,166 @@
+"""Thin Python binding of libkda.so (the C ABI in include/kda.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  torch supplies device memory and the current
+stream.  There is no fallback: if libkda.so is missing or a call is rejected,
+an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+QK_L2NORM, BETA_SIGMOID, GATE_IN_KERNEL = 1, 2, 4
+FLAGS_DEFAULT = 7
+
+EXPORTS = (
+    "kda_safe_chunk_size", "kda_chunk_fwd_workspace", "kda_chunk_fwd", "kda_step",
+    "kda_segment_compose", "kda_segment_fixup", "kda_status_string",
+)
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libkda.so and declare the prototypes (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m gated_delta_rule_82_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, F, U, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_uint, ctypes.c_size_t
+    L.kda_safe_chunk_size.argtypes = [F, I]
+    L.kda_safe_chunk_size.restype = I
+    L.kda_chunk_fwd_workspace.argtypes = [I, I, I, I, I, I, I]
+    L.kda_chunk_fwd_workspace.restype = S
+    L.kda_chunk_fwd.argtypes = [P] * 11 + [I] * 6 + [F, U, I, P, S, P]
+    L.kda_chunk_fwd.restype = I
+    L.kda_step.argtypes = [P] * 8 + [I] * 4 + [F, U, I, P]
+    L.kda_step.restype = I
+    L.kda_segment_compose.argtypes = [I, P, P, P, P, I, I, I, I, P]
+    L.kda_segment_compose.restype = I
+    L.kda_segment_fixup.argtypes = [I, P, P, P, P, I, I, I, I, I, I, P]
+    L.kda_segment_fixup.restype = I
+    L.kda_status_string.argtypes = [I]
+    L.kda_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return load().kda_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise KDAError(fn, status, status_string(status))
+
+
+def _dt(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return KDA_F32
+    if t == torch.bfloat16:
+        return KDA_BF16
+    raise TypeError(f"unsupported dtype {t}; use float32 or bfloat16")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("tensors must be contiguous device tensors")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def safe_chunk_size(g_min: float = -5.0, dtype: torch.dtype = torch.bfloat16) -> int:
+    return load().kda_safe_chunk_size(g_min, _dt(dtype))
+
+
+def workspace_bytes(B, T, H, Dk, Dv, chunk=64, dtype=torch.bfloat16) -> int:
+    return load().kda_chunk_fwd_workspace(B, T, H, Dk, Dv, chunk, _dt(dtype))
+
+
+def chunk_fwd(q, k, v, z, beta_raw, A_log, S0=None, *, chunk=64, g_min=-5.0,
+              flags=FLAGS_DEFAULT, want_M=False, want_P=False, o=None, S_out=None,
+              M_out=None, P_out=None, workspace=None):
+    """Chunkwise KDA forward.  Returns (o, S_out) plus M and/or P when asked."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    dev = q.device
+    if o is None:
+        o = torch.empty(B, T, H, Dv, dtype=dt, device=dev)
+    if S_out is None:
+        S_out = torch.empty(B, H, Dk, Dv, dtype=torch.float32, device=dev)
+    if want_M and M_out is None:
+        M_out = torch.empty(B, H, Dk, Dk, dtype=torch.float32, device=dev)
+    if want_P and P_out is None:
+        P_out = torch.empty(B, T, H, Dk, dtype=dt, device=dev)
+    need = workspace_bytes(B, T, H, Dk, Dv, chunk, dt)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    st = load().kda_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta_raw), _ptr(A_log), _ptr(S0),
+        _ptr(o), _ptr(S_out), _ptr(M_out), _ptr(P_out),
+        B, T, H, Dk, Dv, chunk, g_min, flags, _dt(dt),
+        _ptr(workspace), workspace.numel(), _stream(dev))
+    _check("kda_chunk_fwd", st)
+    out = [o, S_out]
+    if want_M:
+        out.append(M_out)
+    if want_P:
+        out.append(P_out)
+    return tuple(out)
+
+
+def step(q, k, v, z, beta_raw, A_log, S, *, g_min=-5.0, flags=FLAGS_DEFAULT, o=None):
+    """One decode step; S [B,H,Dk,Dv] fp32 is updated in place.  Returns o."""
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if o is None:
+        o = torch.empty(B, H, Dv, dtype=q.dtype, device=q.device)
+    st = load().kda_step(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta_raw), _ptr(A_log),
+                         _ptr(S), _ptr(o), B, H, Dk, Dv, g_min, flags, _dt(q.dtype),
+                         _stream(q.device))
+    _check("kda_step", st)
+    return o
+
+
+def segment_compose(M, S_tilde, S_in=None, *, S_prefix=None):
+    """Prefix scan S_s = M_s S_{s-1} + S_tilde_s; M [n,B,H,Dk,Dk], S_tilde [n,B,H,Dk,Dv]."""
+    n, B, H, Dk, Dv = S_tilde.shape
+    if S_prefix is None:
+        S_prefix = torch.empty_like(S_tilde)
+    st = load().kda_segment_compose(n, _ptr(M), _ptr(S_tilde), _ptr(S_in), _ptr(S_prefix),
+                                    B, H, Dk, Dv, _stream(S_tilde.device))
+    _check("kda_segment_compose", st)
+    return S_prefix
+
+
+def segment_fixup(P, S_prefix, o, S_in=None):
+    """o[s] += P[s] @ S_prev[s] in place; P [n,B,Tseg,H,Dk], o [n,B,Tseg,H,Dv]."""
+    n, B, Tseg, H, Dk = P.shape
+    Dv = o.shape[-1]
+    st = load().kda_segment_fixup(n, _ptr(P), _ptr(S_in), _ptr(S_prefix), _ptr(o), B, Tseg,
+                                  H, Dk, Dv, _dt(P.dtype), _stream(P.device))
+    _check("kda_segment_fixup", st)
+    return o

@@ -1,0 +1,137 @@
+/*
+ * kda.h - C ABI of the MI355X (gfx950) Kimi Delta Attention core.
+ *
+ * The operation is the gated delta rule with a bounded per-channel decay:
+ *
+ *   g_t  = g_min * sigmoid(exp(A_log[h]) * z_t)      per Dk channel
+ *   S_t  = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T
+ *   o_t  = S_t^T q_t
+ *
+ * with q, k L2-normalised and beta = sigmoid(beta_raw).  Decay is applied before
+ * the delta erase and the readout uses the updated state ("Implémenter KDA",
+ * 'La forme récurrente de référence' and its pitfalls).  The gate is the bounded
+ * one of "线性注意力交互式演示" §1.2 Eq. 8 and "Implémenter KDA" 'La décroissance
+ * bornée'.  The three switches mirror the in-kernel switches of "KDAAttention
+ * 层", 'chunk_kda 内部做了什么'.
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers to contiguous row-major buffers, 16-byte
+ *    aligned.  Layouts: q, k, z [B,T,H,Dk]; v [B,T,H,Dv]; beta_raw [B,T,H];
+ *    A_log [H] fp32; states [B,H,Dk,Dv] fp32; transitions [B,H,Dk,Dk] fp32.
+ *    Decode tensors drop the T axis.  q, k, v, z, beta_raw and o share `dt`.
+ *  - The caller owns every buffer, including the workspace.  The library never
+ *    allocates, frees or synchronises; work is enqueued on `stream` (0 = null
+ *    stream) and is asynchronous.
+ *  - Arguments are validated on the host before anything is enqueued, so a
+ *    rejected call writes nothing and makes no HIP call.  A failed launch
+ *    returns KDA_ERR_HIP.  There is no global mutable state: concurrent calls
+ *    are safe as long as they do not share output buffers or workspace.
+ *  - Supported sizes: Dk, Dv in {16, 32, 64, 128}; chunk in {16, 32, 64}; any
+ *    T >= 0 (a ragged tail chunk is padded with identity transitions).
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,      /* a required pointer is NULL                         */
+    KDA_ERR_SHAPE = 2,     /* unsupported or negative size, or bad chunk         */
+    KDA_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned                   */
+    KDA_ERR_DTYPE = 4,     /* unknown dtype or unknown switch bits               */
+    KDA_ERR_GATE = 5,      /* g_min not finite/negative, or the 16-token factor
+                              tile exceeds kda_safe_chunk_size(g_min, dt)        */
+    KDA_ERR_WORKSPACE = 6, /* workspace NULL, misaligned or too small           */
+    KDA_ERR_HIP = 7        /* a kernel launch failed                             */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Switch bits ("KDAAttention 层", 'three in_kernel switches'; all on by default).
+ * With a bit clear the caller supplies the activated value in the same slot:
+ * the already-normalised q/k, beta itself in place of beta_raw, or the
+ * log-decay g (which must lie in [g_min, 0]) in place of the gate logit z. */
+enum {
+    KDA_QK_L2NORM = 1u,
+    KDA_BETA_SIGMOID = 2u,
+    KDA_GATE_IN_KERNEL = 4u,
+    KDA_FLAGS_DEFAULT = 7u
+};
+
+/* Largest token tile whose factored inverse retention exp(-g_min * n) stays
+ * below dtype_max / 2^10: floor(ln(dtype_max / 2^10) / -g_min)
+ * ("KDA 模块交互式演示" §1.4 safe_chunk_size; Tab 9).  Returns 16 for g_min = -5
+ * with either dtype, 8 for g_min = -10, and -1 for a non-finite or
+ * non-negative g_min or an unknown dtype.  Host only; no HIP call. */
+int kda_safe_chunk_size(float g_min, kda_dtype dt);
+
+/* Bytes of device workspace kda_chunk_fwd needs for these sizes (0 for invalid
+ * sizes).  The workspace holds the per-chunk intermediates of the chunkwise
+ * form; it must be 256-byte aligned.  Host only. */
+size_t kda_chunk_fwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk,
+                               kda_dtype dt);
+
+/* Chunkwise KDA forward ("KDA 模块交互式演示" §1.5 Eqs. 3-4 with the UT transform;
+ * "Implémenter KDA" 'La forme par blocs').  Intra-chunk work is parallel,
+ * the state is carried serially from chunk to chunk in fp32.
+ *   S0     nullable: initial state [B,H,Dk,Dv] fp32; NULL means zero.
+ *   o      [B,T,H,Dv], dtype dt (required when T > 0).
+ *   S_out  nullable: final state [B,H,Dk,Dv] fp32; may alias S0 exactly.
+ *   M_out  nullable: segment transition M = M_T ... M_1 [B,H,Dk,Dk] fp32 of the
+ *          whole call ("Implémenter KDA" Test 2), for segment composition.
+ *   P_out  nullable: correction rows [B,T,H,Dk], dtype dt, with
+ *          o_t(S0) = o_t(0) + P_t S0 ("KDA 模块交互式演示" §1.6; the recurrence is
+ *          affine in S0).  Requesting M_out or P_out doubles the state width.
+ *   chunk  0 selects 64.
+ * Returns KDA_OK or the first validation error. */
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* z,
+                         const void* beta_raw, const float* A_log, const float* S0,
+                         void* o, float* S_out, float* M_out, void* P_out,
+                         int B, int T, int H, int Dk, int Dv, int chunk,
+                         float g_min, unsigned flags, kda_dtype dt,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* One decode step per (b,h), state updated IN PLACE ("KDA 模块交互式演示" §1.7
+ * kda_step; "Implémenter KDA" reference step): decay, erase along k, write,
+ * then read the updated state.  q, k, z [B,H,Dk]; v [B,H,Dv]; beta_raw [B,H];
+ * S [B,H,Dk,Dv] fp32 in/out; o [B,H,Dv] dtype dt. */
+kda_status kda_step(const void* q, const void* k, const void* v, const void* z,
+                    const void* beta_raw, const float* A_log, float* S, void* o,
+                    int B, int H, int Dk, int Dv, float g_min, unsigned flags,
+                    kda_dtype dt, hipStream_t stream);
+
+/* Segment prefix scan ("KDA 模块交互式演示" §1.6 KCP; "Implémenter KDA" Test 3
+ * and 'La loi de composition associative'): for s = 0..n_seg-1,
+ *   S_prefix[s] = M[s] S_prev + S_tilde[s],  S_prev = (s ? S_prefix[s-1] : S_in).
+ *   M [n_seg,B,H,Dk,Dk], S_tilde and S_prefix [n_seg,B,H,Dk,Dv], all fp32;
+ *   S_in nullable [B,H,Dk,Dv] (NULL = zero).  S_prefix must not overlap the
+ *   inputs. */
+kda_status kda_segment_compose(int n_seg, const float* M, const float* S_tilde,
+                               const float* S_in, float* S_prefix,
+                               int B, int H, int Dk, int Dv, hipStream_t stream);
+
+/* Output correction of segments run from a zero state (the affine split of
+ * "Implémenter KDA" Test 2 applied to outputs): for every segment s and token t,
+ *   o[s,b,t,h,:] += P[s,b,t,h,:] S_prev[s,b,h]   with
+ *   S_prev[s] = (s ? S_prefix[s-1] : S_in)   (S_in NULL: segment 0 untouched).
+ * P and o are segment-major [n_seg,B,T_seg,H,Dk] / [n_seg,B,T_seg,H,Dv] in dt
+ * (a B = 1 sequence cut into equal segments already has this layout);
+ * S_prefix [n_seg,B,H,Dk,Dv] fp32 as written by kda_segment_compose. */
+kda_status kda_segment_fixup(int n_seg, const void* P, const float* S_in,
+                             const float* S_prefix, void* o, int B, int T_seg,
+                             int H, int Dk, int Dv, kda_dtype dt, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* kda_status_string(kda_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */
