@@ -1,0 +1,358 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one kda_chunk_fwd call (prep, intra-chunk and inter-chunk kernels)
+over the layer-shaped workload B=4, T=4096, H=16, Dk=Dv=128, chunk 64, bf16
+inputs and fp32 state, with the inputs already resident in HBM.  Four input
+sets (about 1.1 GB) rotate from step to step so the 256 MB Infinity Cache
+cannot serve them.  The JSON line also reports, measured in the same run:
+  * per-kernel times from HIP events recorded by the library between its
+    kernels, and the roofline of the dominant kernel;
+  * MFMA % of the whole call under both flop counts, HBM % on compulsory bytes;
+  * the decode step (B=256, H=32, D=128, fp32 state) and its HBM %;
+  * the long-context segmented flow (B=1, T=65536, H=32, 8 segments);
+  * the fp64 oracle timed on the host cores on a bounded sample.
+Only the JSON line goes to stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "chunk_kda fwd tokens/s (H=16,Dk=Dv=128,T=4096) + % MFMA peak; decode % HBM"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_layer.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ work model
+
+def chunk_flops(B, T, H, Dk, Dv, C):
+    """Algorithmic flops of the chunkwise forward (per chunk-head, triangle
+    exact): C^2 (3 Dk + 2 Dv) + 6 C Dk Dv (+ C^3/3 for the solve); and the
+    count with full C x C tiles: 2 C^2 (3 Dk + 2 Dv) + 6 C Dk Dv."""
+    nch = B * H * ((T + C - 1) // C)
+    tri = C * C * (3 * Dk + 2 * Dv) + 6 * C * Dk * Dv + C ** 3 / 3
+    full = 2 * C * C * (3 * Dk + 2 * Dv) + 6 * C * Dk * Dv
+    return nch * tri, nch * full
+
+
+def chunk_bytes(B, T, H, Dk, Dv, esize=2):
+    """Compulsory HBM bytes of one call: q, k, z, v, beta_raw read once, o and
+    the final fp32 state written once."""
+    rows = B * T * H
+    return rows * (3 * Dk + Dv + 1) * esize + rows * Dv * esize + B * H * Dk * Dv * 4 + H * 4
+
+
+def kernel_bytes(B, T, H, Dk, Dv, C, ws_bytes, esize=2):
+    """Algorithmic bytes per launch of each kernel: what it must read and write."""
+    rows = B * T * H
+    intra = rows * (3 * Dk + 1) * esize + H * 4 + ws_bytes
+    inter = ws_bytes + rows * Dv * esize + rows * Dv * esize + B * H * Dk * Dv * 4
+    return {"kda_intra": intra, "kda_inter": inter}
+
+
+def decode_bytes(B, H, Dk, Dv, esize=2):
+    return 2 * B * H * Dk * Dv * 4 + B * H * (3 * Dk + Dv + 1) * esize + B * H * Dv * esize + H * 4
+
+
+def source_sha():
+    h = hashlib.sha256()
+    for f in ("kda_chunk.hip", "kda_device.h", "kda_internal.h"):
+        with open(os.path.join(ROOT, "gated_delta_rule_82_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel sources changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha") != source_sha():
+        return None
+    val = kv.get(f"{kernel}_hbm_bytes")
+    return float(val) if val else None
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+def _oracle_slice(args):
+    from threadpoolctl import threadpool_limits
+    from oracle import kda_oracle as ora
+    q, k, v, z, br, A = args
+    with threadpool_limits(1):
+        ora.forward(q, k, v, z, br, A, None)
+    return True
+
+
+def cpu_baseline(inp, T_sample):
+    """Time the fp64 oracle on all heads of the layer workload, first T_sample
+    tokens, split over (b, head group) across worker processes."""
+    import multiprocessing as mp
+
+    import numpy as np
+    f = lambda t: t[:, :T_sample].double().numpy()
+    q, k, v, z = (f(inp[n]) for n in ("q", "k", "v", "z"))
+    br = inp["beta_raw"][:, :T_sample].double().numpy()
+    A = inp["A_log"].double().numpy()
+    B, _, H, _ = q.shape
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    per_b = max(1, workers // B)
+    hg = max(1, H // per_b)
+    jobs = [(q[b:b + 1, :, h:h + hg], k[b:b + 1, :, h:h + hg], v[b:b + 1, :, h:h + hg],
+             z[b:b + 1, :, h:h + hg], br[b:b + 1, :, h:h + hg], A[h:h + hg])
+            for b in range(B) for h in range(0, H, hg)]
+    n_proc = min(workers, len(jobs))
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(n_proc) as pool:
+        pool.map(_oracle_slice, jobs)
+    wall = time.perf_counter() - t0
+    return {"value": B * T_sample / wall, "unit": "tokens/s", "cores": n_proc, "kind": "oracle",
+            "sample": f"layer workload, all {B * H} (b,h) heads, first {T_sample} of 4096 tokens, "
+                      f"fp64 token recurrence, {len(jobs)} slices over {n_proc} processes",
+            "wall_s": round(wall, 3)}
+
+
+# ------------------------------------------------------------------ GPU legs
+
+def bench_layer(torch, kda, inputs, steps, warmup):
+    w = inputs.WORKLOADS["layer"]
+    dev = torch.device("cuda:0")
+    B, T, H, Dk, Dv, C = w.B, w.T, w.H, w.Dk, w.Dv, w.chunk
+    base = inputs.make_workload(w)
+    sets = [{n: base[n].to(dev) for n in ("q", "k", "v", "z", "beta_raw")}]
+    gen = torch.Generator(device=dev)
+    for i in range(1, 4):
+        gen.manual_seed(w.seed * 100 + i)
+        sets.append({n: torch.randn(*base[n].shape, generator=gen, device=dev).to(torch.bfloat16)
+                     for n in ("q", "k", "v", "z", "beta_raw")})
+    A = base["A_log"].to(dev)
+    o = torch.empty(B, T, H, Dv, dtype=torch.bfloat16, device=dev)
+    S = torch.empty(B, H, Dk, Dv, dtype=torch.float32, device=dev)
+    ws_n = kda.workspace_bytes(B, T, H, Dk, Dv, C, torch.bfloat16)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+
+    def step(i, evs=None):
+        s = sets[i % len(sets)]
+        kda.chunk_fwd(s["q"], s["k"], s["v"], s["z"], s["beta_raw"], A, None, chunk=C,
+                      o=o, S_out=S, workspace=ws, events=evs)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        step(i, evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    intra = [e[0].elapsed_time(e[1]) for e in evs]
+    inter = [e[1].elapsed_time(e[2]) for e in evs]
+    return {"B": B, "T": T, "H": H, "Dk": Dk, "Dv": Dv, "C": C, "ws_bytes": ws_n,
+            "ms_per_step": total_ms / steps,
+            "kernel_ms": {"kda_intra": sum(intra) / steps, "kda_inter": sum(inter) / steps}}
+
+
+def bench_decode(torch, kda, inputs, steps, warmup):
+    w = inputs.WORKLOADS["decode"]
+    dev = torch.device("cuda:0")
+    S0, A_log = inputs.make_decode_state(w)
+    S = S0.to(dev)
+    A = A_log.to(dev)
+    pool = [{n: t.to(dev) for n, t in inputs.make_decode_step(w, s).items()} for s in range(8)]
+    o = torch.empty(w.B, w.H, w.Dv, dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        p = pool[i % len(pool)]
+        kda.step(p["q"], p["k"], p["v"], p["z"], p["beta_raw"], A, S, o=o)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        step(i)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    nbytes = decode_bytes(w.B, w.H, w.Dk, w.Dv)
+    return {"workload": "decode: B256 H32 Dk=Dv=128, bf16 q/k/v/z, fp32 state in place",
+            "steps": steps, "us_per_step": round(ms * 1e3, 2), "tokens_per_s": w.B / (ms / 1e3),
+            "hbm_gbs": nbytes / (ms / 1e3) / 1e9,
+            "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
+
+
+def bench_long(torch, kda, inputs, reps):
+    w = inputs.WORKLOADS["long"]
+    dev = torch.device("cuda:0")
+    n, Tseg = w.segments, w.T // w.segments
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    x = {nm: torch.randn(w.B, w.T, w.H, d, generator=gen, device=dev).to(torch.bfloat16)
+         for nm, d in (("q", w.Dk), ("k", w.Dk), ("v", w.Dv), ("z", w.Dk))}
+    x["beta_raw"] = torch.randn(w.B, w.T, w.H, generator=gen, device=dev).to(torch.bfloat16)
+    A = (torch.randn(w.H, generator=gen, device=dev) * w.a_std).float()
+    seg = {k: v.view(n, Tseg, *v.shape[2:]) for k, v in x.items()}
+    o_full = torch.empty_like(x["v"])
+    S_full = torch.empty(w.B, w.H, w.Dk, w.Dv, device=dev)
+    ws = torch.empty(kda.workspace_bytes(w.B, w.T, w.H, w.Dk, w.Dv, w.chunk), dtype=torch.uint8, device=dev)
+    o0 = torch.empty(n, 1, Tseg, w.H, w.Dv, dtype=torch.bfloat16, device=dev)
+    P = torch.empty(n, 1, Tseg, w.H, w.Dk, dtype=torch.bfloat16, device=dev)
+    M = torch.empty(n, 1, w.H, w.Dk, w.Dk, device=dev)
+    St = torch.empty(n, 1, w.H, w.Dk, w.Dv, device=dev)
+    Sp = torch.empty_like(St)
+
+    def full():
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["z"], x["beta_raw"], A, None, o=o_full, S_out=S_full, workspace=ws)
+
+    def segmented():
+        kda.chunk_fwd(seg["q"], seg["k"], seg["v"], seg["z"], seg["beta_raw"], A, None,
+                      want_M=True, want_P=True, o=o0.view(n, Tseg, w.H, w.Dv), S_out=St.view(n, w.H, w.Dk, w.Dv),
+                      M_out=M.view(n, w.H, w.Dk, w.Dk), P_out=P.view(n, Tseg, w.H, w.Dk), workspace=ws)
+        kda.segment_compose(M, St, S_prefix=Sp)
+        kda.segment_fixup(P, Sp, o0)
+
+    res = {}
+    for name, fn in (("full", full), ("segmented", segmented)):
+        fn()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            fn()
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / reps
+        res[name] = {"ms": round(ms, 3), "tokens_per_s": w.T / (ms / 1e3)}
+    diff = float((o0.view(w.B, w.T, w.H, w.Dv).float() - o_full.float()).abs().max())
+    res["max_abs_diff_vs_full"] = diff
+    res["workload"] = "long: B1 T65536 H32 Dk=Dv=128 bf16; segmented = 8 x 8192 fragments + compose + fixup"
+    return res
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-tokens", type=int, default=2048, help="oracle sample length (0 = skip)")
+    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--long-reps", type=int, default=3)
+    ap.add_argument("--only-layer", action="store_true", help="time the layer workload only")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run 3 device copies of 1 GiB (a counter reference of known size)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the KDA heads are independent, so a multi-GPU run "
+              "is B x H sharding with no exchange (see the design notes); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_delta_rule_82_amd import inputs, kda
+
+    kda.load()  # fails loudly if libkda.so is missing
+
+    cpu = None
+    if args.cpu_tokens > 0 and not args.only_layer:
+        log(f"[bench] oracle CPU baseline on {args.cpu_tokens} tokens ...")
+        cpu = cpu_baseline(inputs.make_workload(inputs.WORKLOADS["layer"], T=args.cpu_tokens),
+                           args.cpu_tokens)
+        log(f"[bench] oracle: {cpu['value']:.1f} tokens/s on {cpu['cores']} processes")
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    props = torch.cuda.get_device_properties(0)
+    log(f"[bench] device {props.name}, {props.multi_processor_count} CUs")
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("[bench] copy calibration: 3 x 1 GiB device copies done")
+
+    log("[bench] layer workload ...")
+    L = bench_layer(torch, kda, inputs, args.steps, args.warmup)
+    B, T, H, Dk, Dv, C = L["B"], L["T"], L["H"], L["Dk"], L["Dv"], L["C"]
+    ms = L["ms_per_step"]
+    tok_s = B * T / (ms / 1e3)
+    f_tri, f_full = chunk_flops(B, T, H, Dk, Dv, C)
+    cbytes = chunk_bytes(B, T, H, Dk, Dv)
+    kb = kernel_bytes(B, T, H, Dk, Dv, C, L["ws_bytes"])
+    dom = max(L["kernel_ms"], key=L["kernel_ms"].get)
+    dom_ms = L["kernel_ms"][dom]
+    achieved = kb[dom] / (dom_ms / 1e3) / 1e9
+    traffic = read_traffic(dom)
+    log(f"[bench] layer {ms:.3f} ms/step, {tok_s:.3e} tokens/s; kernels {L['kernel_ms']}")
+
+    extra = {}
+    if not args.only_layer:
+        log("[bench] decode workload ...")
+        extra["decode"] = bench_decode(torch, kda, inputs, args.decode_steps, 10)
+        log(f"[bench] decode {extra['decode']['us_per_step']} us/step")
+        log("[bench] long workload ...")
+        extra["long"] = bench_long(torch, kda, inputs, args.long_reps)
+        log(f"[bench] long {extra['long']}")
+
+    out = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs, A_log ~ N(0,0.5); 4 rotating input sets in HBM)",
+        "config": {"workload": "layer: chunk_kda fwd B4 T4096 H16 Dk=Dv=128 chunk64, bf16 in, fp32 state",
+                   "B": B, "T": T, "H": H, "Dk": Dk, "Dv": Dv, "chunk": C, "g_min": -5.0},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": kb[dom], "kernel_ms": round(dom_ms, 4)},
+        "kernel_ms": {k: round(v, 4) for k, v in L["kernel_ms"].items()},
+        "mfma_frac": {"algorithmic": round(f_tri / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                      "tile_count": round(f_full / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "hbm_frac_compulsory": round(cbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "cpu_baseline": cpu,
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+    }
+    out.update(extra)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

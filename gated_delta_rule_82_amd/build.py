@@ -34,6 +34,8 @@ def common_flags() -> list[str]:
     return [
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # keep matrix-core accumulators in VGPRs (no AGPR copies around the MFMAs)
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-I", CSRC, "-I", INCLUDE, "-Wno-unused-command-line-argument",
     ]
 

@@ -57,12 +57,15 @@ size_t kda_chunk_fwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk, k
     return (size_t)B * (size_t)H * nc * L.bytes;
 }
 
-kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* z,
-                         const void* beta_raw, const float* A_log, const float* S0,
-                         void* o, float* S_out, float* M_out, void* P_out,
-                         int B, int T, int H, int Dk, int Dv, int chunk,
-                         float g_min, unsigned flags, kda_dtype dt,
-                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const void* z,
+                                 const void* beta_raw, const float* A_log, const float* S0,
+                                 void* o, float* S_out, float* M_out, void* P_out,
+                                 int B, int T, int H, int Dk, int Dv, int chunk,
+                                 float g_min, unsigned flags, kda_dtype dt,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                 hipEvent_t* ev) {
     if (!dtype_ok(dt) || !flags_ok(flags)) return KDA_ERR_DTYPE;
     if (chunk == 0) chunk = 64;
     if (B < 0 || T < 0 || H < 0 || !dim_ok(Dk) || !dim_ok(Dv)) return KDA_ERR_SHAPE;
@@ -88,8 +91,32 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
     a.o = o; a.S_out = S_out; a.M_out = M_out; a.P_out = P_out; a.ws = workspace;
     a.B = B; a.T = T; a.H = H; a.Dv = Dv; a.NC = (T + chunk - 1) / chunk;
     a.g_min = g_min; a.flags = flags;
-    return kda::launch_chunk(dt == KDA_BF16 ? 1 : 0, Dk, chunk, a, stream) == hipSuccess ? KDA_OK
-                                                                                         : KDA_ERR_HIP;
+    const hipError_t e = kda::launch_chunk(dt == KDA_BF16 ? 1 : 0, Dk, chunk, a, stream, ev);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+extern "C" {
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* z,
+                         const void* beta_raw, const float* A_log, const float* S0,
+                         void* o, float* S_out, float* M_out, void* P_out,
+                         int B, int T, int H, int Dk, int Dv, int chunk,
+                         float g_min, unsigned flags, kda_dtype dt,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return chunk_fwd_impl(q, k, v, z, beta_raw, A_log, S0, o, S_out, M_out, P_out, B, T, H, Dk, Dv,
+                          chunk, g_min, flags, dt, workspace, workspace_bytes, stream, nullptr);
+}
+
+kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void* z,
+                               const void* beta_raw, const float* A_log, const float* S0,
+                               void* o, float* S_out, float* M_out, void* P_out,
+                               int B, int T, int H, int Dk, int Dv, int chunk,
+                               float g_min, unsigned flags, kda_dtype dt,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream,
+                               hipEvent_t events[3]) {
+    if (!events || !events[0] || !events[1] || !events[2]) return KDA_ERR_NULL;
+    return chunk_fwd_impl(q, k, v, z, beta_raw, A_log, S0, o, S_out, M_out, P_out, B, T, H, Dk, Dv,
+                          chunk, g_min, flags, dt, workspace, workspace_bytes, stream, events);
 }
 
 kda_status kda_step(const void* q, const void* k, const void* v, const void* z,

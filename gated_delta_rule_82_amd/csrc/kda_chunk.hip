@@ -54,21 +54,19 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     constexpr int NV = KSD * 8;
     constexpr int NOFF = NBK > 1 ? NBK - 1 : 1;
     constexpr int NPAIR = NBK > 1 ? NBK * (NBK - 1) / 2 : 1;
-    constexpr int KPS = DK + 4;  // padded row stride of the K' staging tile
 
-    __shared__ float s_tot[NBK][DK];     // block totals of the log2 decay
-    __shared__ float s_eE[NBK][DK];      // exp2(E_I): decay from chunk start to block entry
-    __shared__ float s_eLl[NBK][DK];     // exp2(Ll_I): decay over block I
-    __shared__ float s_eK[NBK][DK];      // exp2(G_C - E_I - Ll_I): block end to chunk end
-    __shared__ float s_pair[NPAIR][DK];  // exp2(E_I - E_{J+1}) <= 1 for J < I - 1
+    __shared__ __align__(16) float s_tot[NBK][DK];    // block totals of the log2 decay
+    __shared__ __align__(16) float s_eE[NBK][DK];     // exp2(E_I): chunk start to block entry
+    __shared__ __align__(16) float s_eLl[NBK][DK];    // exp2(Ll_I): decay over block I
+    __shared__ __align__(16) float s_eK[NBK][DK];     // exp2(G_C - E_I - Ll_I): block end to chunk end
+    __shared__ __align__(16) float s_pair[NPAIR][DK]; // exp2(E_I - E_{J+1}) <= 1 for J < I - 1
     __shared__ float s_beta[C];
-    __shared__ __align__(16) float s_offb[NOFF][KSD][512];
-    __shared__ __align__(16) float s_kp[C][KPS];
-    __shared__ __align__(16) float s_akk[NPAIR][256];
-    __shared__ __align__(16) float s_tdiag[NBK][256];
+    __shared__ __align__(16) T s_offb[NOFF][KSD][512];  // column operands of off-diagonal blocks
+    __shared__ __align__(16) float s_akk[NPAIR][256];   // R layout of A_kk[I][J], J < I
+    __shared__ __align__(16) float s_tdiag[NBK][256];   // R layout of (I + A_kk[I][I])^-1
 
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15;
     const int gq = lane >> 4;
 
@@ -88,6 +86,9 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     float* ws_gamma = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(ws) + L.gamma_byte);
 
     // ------------------------------------------------------------ phase A
+    // Lane (r, gq) of wave I owns token 16 I + r and the channels of its
+    // fragment slots; loads, norms, gate and the block-local scan are all
+    // wave-local.
     float qv[NV], kv[NV], gv[NV];
     float beta = 0.f;
 #pragma unroll
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
             float* dq = &qv[8 * s + 4 * hf];
             float* dk = &kv[8 * s + 4 * hf];
             float* dz = &gv[8 * s + 4 * hf];
-            if (valid && c < DK) {
+            if (valid && (DK >= 32 || hf == 0)) {
                 load4(reinterpret_cast<const T*>(a.q) + row * DK + c, dq);
                 load4(reinterpret_cast<const T*>(a.k) + row * DK + c, dk);
                 load4(reinterpret_cast<const T*>(a.z) + row * DK + c, dz);
@@ -120,20 +121,23 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     const float rq = (a.flags & kQkL2) ? 1.0f / sqrtf(sq + kL2Eps) : 1.0f;
     const float rk = (a.flags & kQkL2) ? 1.0f / sqrtf(sk + kL2Eps) : 1.0f;
     const bool gate = (a.flags & kGateIn) != 0;
-    const float hscale = gate ? expf(a.A_log[h]) : 0.f;
+    const float zscale = gate ? -expf(a.A_log[h]) * kLog2e : 0.f;  // exp2(zscale z) = e^{-e^A z}
     const float gm2 = a.g_min * kLog2e;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
         float g2 = 0.f;  // padding tokens are identity transitions (g = 0, beta = 0)
-        if (valid) g2 = gate ? gm2 * sigmoidf_(hscale * gv[v]) : gv[v] * kLog2e;
+        if (valid) g2 = gate ? gm2 * __builtin_amdgcn_rcpf(1.0f + exp2_fast(zscale * gv[v])) : gv[v] * kLog2e;
         gv[v] = row_scan16(g2);  // block-local inclusive cumulative log2-decay L
     }
     if (active) {
         if (r == 15) {
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                const int c = 32 * (v / 8) + slot_index(gq, v % 8);
-                if (c < DK) s_tot[I][c] = gv[v];
+            for (int s = 0; s < KSD; ++s) {
+                *reinterpret_cast<float4*>(&s_tot[I][32 * s + 4 * gq]) =
+                    make_float4(gv[8 * s], gv[8 * s + 1], gv[8 * s + 2], gv[8 * s + 3]);
+                if (DK >= 32)
+                    *reinterpret_cast<float4*>(&s_tot[I][32 * s + 16 + 4 * gq]) =
+                        make_float4(gv[8 * s + 4], gv[8 * s + 5], gv[8 * s + 6], gv[8 * s + 7]);
             }
         }
         if (gq == 0) s_beta[16 * I + r] = beta;
@@ -141,6 +145,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     __syncthreads();
 
     // ------------------------------------------------------------ phase B
+    // Per (block, channel) decay factors, each computed once.
     for (int e = threadIdx.x; e < NBK * DK; e += 256) {
         const int Ib = e / DK, c = e % DK;
         float E = 0.f, GC = 0.f;
@@ -151,59 +156,91 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
             GC += x;
         }
         const float Ll = s_tot[Ib][c];
-        s_eE[Ib][c] = exp2f(E);
-        s_eLl[Ib][c] = exp2f(Ll);
-        s_eK[Ib][c] = exp2f(GC - E - Ll);
+        s_eE[Ib][c] = exp2_fast(E);
+        s_eLl[Ib][c] = exp2_fast(Ll);
+        s_eK[Ib][c] = exp2_fast(GC - E - Ll);
 #pragma unroll
         for (int J = 0; J + 1 < NBK; ++J) {
             if (J + 1 < Ib) {
-                float gap = 0.f;
+                float gap = 0.f;  // <= 0: decay between the end of block J and the entry of block Ib
 #pragma unroll
                 for (int K = 0; K < NBK; ++K)
                     if (K > J && K < Ib) gap += s_tot[K][c];
-                s_pair[pair_index(Ib, J)][c] = exp2f(gap);  // gap <= 0: decay between the blocks
+                s_pair[pair_index(Ib, J)][c] = exp2_fast(gap);
             }
         }
-        if (Ib == 0) ws_gamma[c] = exp2f(GC);
+        if (Ib == 0) ws_gamma[c] = exp2_fast(GC);
     }
     __syncthreads();
 
     // ------------------------------------------------------------ phase C
+    // Row operands (q, k scaled by exp(L)), diagonal column operand
+    // (k scaled by exp(-L)), the chunk operands Kd, Qp, and K' for KpT.
     Frag<T> rkf[KSD], rqf[KSD], cdf[KSD];
     if (active) {
 #pragma unroll
         for (int s = 0; s < KSD; ++s) {
-            Frag<T> kd, qp;
+            float eE[8], eLl[8], eK[8];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int c = 32 * s + 16 * hf + 4 * gq;
+                if (DK >= 32 || hf == 0) {
+                    const float4 x = *reinterpret_cast<const float4*>(&s_eE[I][c]);
+                    const float4 y = *reinterpret_cast<const float4*>(&s_eLl[I][c]);
+                    const float4 z = *reinterpret_cast<const float4*>(&s_eK[I][c]);
+                    eE[4 * hf] = x.x; eE[4 * hf + 1] = x.y; eE[4 * hf + 2] = x.z; eE[4 * hf + 3] = x.w;
+                    eLl[4 * hf] = y.x; eLl[4 * hf + 1] = y.y; eLl[4 * hf + 2] = y.z; eLl[4 * hf + 3] = y.w;
+                    eK[4 * hf] = z.x; eK[4 * hf + 1] = z.y; eK[4 * hf + 2] = z.z; eK[4 * hf + 3] = z.w;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) { eE[4 * hf + i] = 0.f; eLl[4 * hf + i] = 0.f; eK[4 * hf + i] = 0.f; }
+                }
+            }
+            Frag<T> kd, qp, ob, kp;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int v = 8 * s + j;
-                const int c = 32 * s + slot_index(gq, j);
-                float rsq = 0.f, rsk = 0.f, cdg = 0.f, kdv = 0.f, qpv = 0.f, offv = 0.f, kpv = 0.f;
-                if (c < DK) {
-                    const float Lv = gv[v];
-                    const float e1 = exp2_fast(Lv);
-                    const float einv = exp2_fast(-Lv);
-                    const float qh = qv[v] * rq;
-                    const float kh = kv[v] * rk;
-                    rsq = qh * e1;
-                    rsk = kh * e1;
-                    cdg = kh * einv;
-                    const float eE = s_eE[I][c];
-                    kdv = rsk * eE;
-                    qpv = rsq * eE;
-                    offv = cdg * s_eLl[I][c];
-                    kpv = offv * s_eK[I][c];
-                    s_kp[16 * I + r][c] = kpv;
-                }
+                const float Lv = gv[v];
+                const float e1 = exp2_fast(Lv);
+                const float einv = exp2_fast(-Lv);
+                const float qh = qv[v] * rq;
+                const float kh = kv[v] * rk;
+                const float rsq = qh * e1;
+                const float rsk = kh * e1;
+                const float cdg = kh * einv;
+                const float offv = cdg * eLl[j];   // k exp(Ll - L): decay from the token to its block end
                 rqf[s].set(j, rsq);
                 rkf[s].set(j, rsk);
                 cdf[s].set(j, cdg);
-                kd.set(j, kdv);
-                qp.set(j, qpv);
-                if (NBK > 1 && I < NBK - 1) s_offb[I < NOFF ? I : 0][s][lane * 8 + j] = offv;
+                kd.set(j, rsk * eE[j]);
+                qp.set(j, rsq * eE[j]);
+                ob.set(j, offv);
+                kp.set(j, offv * eK[j]);
             }
             frag_store(kd, ws + L.kd + (size_t)(I * KSD + s) * 512, lane);
             frag_store(qp, ws + L.qp + (size_t)(I * KSD + s) * 512, lane);
+            if (NBK > 1 && I < NBK - 1) frag_store(ob, &s_offb[I < NOFF ? I : 0][s][0], lane);
+            // KpT tiles by an exact identity product: mma(K' rows, E_R) is the
+            // C-layout tile (tokens of block I) x (channels of block R), i.e. one
+            // half of the A fragment of KpT for channel block R.
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int R = 2 * s + hf;
+                if (R < NBD) {
+                    Frag<T> e;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) e.set(j, (slot_index(gq, j) == 16 * hf + r) ? 1.f : 0.f);
+                    floatx4 x = {0.f, 0.f, 0.f, 0.f};
+                    x = mma(kp, e, x);
+                    const float xv[4] = {x[0], x[1], x[2], x[3]};
+                    T* tile = ws + L.kpt + (size_t)(R * KSC + I / 2) * 512;
+                    half_store(tile, lane, I % 2, xv);
+                    if (I % 2 == 0 && I + 1 >= NBK) {
+                        const float zero4[4] = {0.f, 0.f, 0.f, 0.f};
+                        half_store(tile, lane, 1, zero4);
+                    }
+                }
+            }
         }
     }
     __syncthreads();
@@ -218,6 +255,8 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
             aqkR = mma(cdf[s], rqf[s], aqkR);
             akkC = mma(rkf[s], cdf[s], akkC);   // C layout: row 4gq+i, col r
         }
+        const float4 bcol = *reinterpret_cast<const float4*>(&s_beta[16 * I + 4 * gq]);
+        const float bc[4] = {bcol.x, bcol.y, bcol.z, bcol.w};
         float aq[4];
         floatx4 I4;
 #pragma unroll
@@ -225,7 +264,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
             const int cc = 4 * gq + i;
             akkR[i] = (cc < r) ? akkR[i] * beta : 0.f;
             aq[i] = (cc <= r) ? aqkR[i] : 0.f;
-            akkC[i] = (r < cc) ? akkC[i] * s_beta[16 * I + cc] : 0.f;
+            akkC[i] = (r < cc) ? akkC[i] * bc[i] : 0.f;
             I4[i] = (cc == r) ? 1.f : 0.f;
         }
         T* aqk_tile = ws + L.aqk + (size_t)(I * KSC + I / 2) * 512;
@@ -234,7 +273,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
             const float zero4[4] = {0.f, 0.f, 0.f, 0.f};
             half_store(aqk_tile, lane, 1, zero4);
         }
-        // off-diagonal blocks J < I
+        // off-diagonal blocks J < I: entry (i, j) = sum_c rowside_I[i,c] pair[c] offb_J[j,c]
 #pragma unroll
         for (int J = 0; J < NBK - 1; ++J) {
             if (J < I) {
@@ -242,25 +281,29 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
 #pragma unroll
                 for (int s = 0; s < KSD; ++s) {
                     Frag<T> cof;
+                    frag_load(cof, &s_offb[J][s][0], lane);
+                    if (J + 1 < I) {
+                        // rows rescaled by the decay between the blocks (<= 1)
+                        const float* pr = &s_pair[pair_index(I, J)][0];
+                        Frag<T> rk2, rq2;
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int c = 32 * s + slot_index(gq, j);
-                        float x = 0.f;
-                        if (c < DK) {
-                            x = s_offb[J][s][lane * 8 + j];
-                            if (J + 1 < I) x *= s_pair[pair_index(I, J)][c];
+                        for (int j = 0; j < 8; ++j) {
+                            const int c = 32 * s + slot_index(gq, j);
+                            const float sc = (c < DK) ? pr[c] : 0.f;
+                            rk2.set(j, rkf[s].get(j) * sc);
+                            rq2.set(j, rqf[s].get(j) * sc);
                         }
-                        cof.set(j, x);
+                        ak = mma(cof, rk2, ak);
+                        aqo = mma(cof, rq2, aqo);
+                    } else {
+                        ak = mma(cof, rkf[s], ak);
+                        aqo = mma(cof, rqf[s], aqo);
                     }
-                    ak = mma(cof, rkf[s], ak);
-                    aqo = mma(cof, rqf[s], aqo);
                 }
                 float aqv[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    aqv[i] = aqo[i];
-                    s_akk[pair_index(I, J)][lane * 4 + i] = ak[i] * beta;
-                }
+                for (int i = 0; i < 4; ++i) { aqv[i] = aqo[i]; ak[i] *= beta; }
+                *reinterpret_cast<float4*>(&s_akk[pair_index(I, J)][lane * 4]) = make_float4(ak[0], ak[1], ak[2], ak[3]);
                 half_store(ws + L.aqk + (size_t)(I * KSC + J / 2) * 512, lane, J % 2, aqv);
             }
         }
@@ -276,20 +319,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
         const floatx4 P2R = P1R + mm16(P1C, N4R);
         TdC = P2C + mm16(N8R, P2C);
         TdR = P2R + mm16(P2C, N8R);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s_tdiag[I][lane * 4 + i] = TdR[i];
-    }
-    // K'^T tiles (rows = channels, contraction = tokens) from the staged K'
-    for (int tile = w; tile < NBD * KSC; tile += 4) {
-        const int R = tile / KSC, s = tile % KSC;
-        const int c = 16 * R + r;
-        Frag<T> f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int tok = 32 * s + slot_index(gq, j);
-            f.set(j, tok < C ? s_kp[tok][c] : 0.f);
-        }
-        frag_store(f, ws + L.kpt + (size_t)tile * 512, lane);
+        *reinterpret_cast<float4*>(&s_tdiag[I][lane * 4]) = make_float4(TdR[0], TdR[1], TdR[2], TdR[3]);
     }
     __syncthreads();
 
@@ -298,13 +328,9 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     //   T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ,  then writes R(T_IJ) Diag(beta).
     if (active) {
         const int J = w;
-        floatx4 TcolC[NBK];
-#pragma unroll
-        for (int K = 0; K < NBK; ++K) TcolC[K] = TdC;
+        const float4 bj = *reinterpret_cast<const float4*>(&s_beta[16 * J + 4 * gq]);
         auto write_tb = [&](int Ir, const floatx4& TR) {
-            float x[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = TR[i] * s_beta[16 * J + 4 * gq + i];
+            const float x[4] = {TR[0] * bj.x, TR[1] * bj.y, TR[2] * bj.z, TR[3] * bj.w};
             half_store(ws + L.tb + (size_t)(Ir * KSC + J / 2) * 512, lane, J % 2, x);
         };
         write_tb(J, TdR);
@@ -312,6 +338,9 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
             const float zero4[4] = {0.f, 0.f, 0.f, 0.f};
             half_store(ws + L.tb + (size_t)(J * KSC + J / 2) * 512, lane, 1, zero4);
         }
+        floatx4 TcolC[NBK];
+#pragma unroll
+        for (int K = 0; K < NBK; ++K) TcolC[K] = TdC;
 #pragma unroll
         for (int Ir = 1; Ir < NBK; ++Ir) {
             if (Ir > J) {
@@ -319,18 +348,15 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
 #pragma unroll
                 for (int K = 0; K < NBK - 1; ++K) {
                     if (K >= J && K < Ir) {
-                        floatx4 aR;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) aR[i] = s_akk[pair_index(Ir, K)][lane * 4 + i];
+                        const float4 v4 = *reinterpret_cast<const float4*>(&s_akk[pair_index(Ir, K)][lane * 4]);
+                        const floatx4 aR = {v4.x, v4.y, v4.z, v4.w};
                         X += mm16(aR, TcolC[K]);
                     }
                 }
-                floatx4 TiiR;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) TiiR[i] = s_tdiag[Ir][lane * 4 + i];
+                const float4 t4 = *reinterpret_cast<const float4*>(&s_tdiag[Ir][lane * 4]);
+                const floatx4 TiiR = {t4.x, t4.y, t4.z, t4.w};
                 TcolC[Ir] = -mm16(TiiR, X);
-                const floatx4 TR = -mm16(X, TiiR);
-                write_tb(Ir, TR);
+                write_tb(Ir, -mm16(X, TiiR));
             }
         }
     }
@@ -344,19 +370,35 @@ struct InterArgs {
     int n_m, n_strips, n_groups;
 };
 
+constexpr size_t kLdsBudget = 160 * 1024;  // LDS per CU on gfx950
+
+// Start an asynchronous copy of one contiguous chunk block from global memory
+// into LDS (global_load_lds: 16 bytes per lane, 1 KiB per wave instruction).
+// Completion is awaited with s_waitcnt vmcnt(0) followed by a barrier.
+template <int NW>
+__device__ __forceinline__ void block_to_lds_async(const unsigned char* src, unsigned char* dst,
+                                                   int bytes, int w, int lane) {
+    for (int off = w * 1024; off < bytes; off += NW * 1024) {
+        if (off + lane * 16 < bytes)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(src + off + lane * 16),
+                (__attribute__((address_space(3))) void*)(dst + off), 16, 0, 0);
+    }
+}
+
 template <typename T, int DK, int C, int NW>
-__global__ __launch_bounds__(64 * NW) void kda_inter_kernel(const InterArgs a) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void kda_inter_kernel(const InterArgs a) {
     constexpr BlockLayout L = block_layout(sizeof(T), DK, C);
     constexpr int NBK = C / 16;
     constexpr int KSD = (DK + 31) / 32;
     constexpr int NBD = DK / 16;
     constexpr int KSC = (C + 31) / 32;
+    constexpr bool kDouble = 2 * L.bytes <= kLdsBudget;  // double-buffer the chunk blocks
     extern __shared__ __align__(16) unsigned char s_raw[];
-    const T* s_blk = reinterpret_cast<const T*>(s_raw);
-    const float* s_gam = reinterpret_cast<const float*>(s_raw + L.gamma_byte);
 
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15;
     const int gq = lane >> 4;
 
@@ -365,10 +407,11 @@ __global__ __launch_bounds__(64 * NW) void kda_inter_kernel(const InterArgs a) {
     const int bh = bid / a.n_groups;
     const int h = bh % a.H;
     const int b = bh / a.H;
-    const int strip = grp * NW + w;
+    const int strip = grp * NW + w;           // wave-uniform
     const bool live = strip < a.n_strips;
     const bool mstrip = strip < a.n_m;
-    const int col = (mstrip ? strip : strip - a.n_m) * 16 + r;
+    const int col0 = (mstrip ? strip : strip - a.n_m) * 16;
+    const int col = col0 + r;
 
     floatx4 S[NBD];
 #pragma unroll
@@ -385,118 +428,199 @@ __global__ __launch_bounds__(64 * NW) void kda_inter_kernel(const InterArgs a) {
         }
     }
 
-    const size_t blk_elems = L.bytes / sizeof(T);
     const unsigned char* gblk = reinterpret_cast<const unsigned char*>(a.ws) +
                                 (size_t)bh * a.NC * L.bytes;
-    const T* vsrc = reinterpret_cast<const T*>(a.v);
     T* out = mstrip ? reinterpret_cast<T*>(a.P_out) : reinterpret_cast<T*>(a.o);
     const int out_w = mstrip ? DK : a.Dv;
     const bool store_o = live && out != nullptr;
-    (void)blk_elems;
+    const bool load_v = live && !mstrip;
 
-    for (int n = 0; n < a.NC; ++n) {
-        floatx4 V[NBK];
+    // Token-major addressing: a wave-uniform byte base per chunk plus a 32-bit
+    // lane byte offset (token within the chunk times the token stride, plus
+    // the column), so global accesses take the scalar-base form.
+    using Raw = typename RawBits<T>::type;
+    const size_t vstride = (size_t)a.H * a.Dv * sizeof(T);   // bytes per token
+    const size_t ostride = (size_t)a.H * out_w * sizeof(T);
+    const unsigned char* vbase = reinterpret_cast<const unsigned char*>(a.v) +
+                                 (((size_t)b * a.T * a.H + h) * a.Dv + col0) * sizeof(T);
+    unsigned char* obase = store_o ? reinterpret_cast<unsigned char*>(out) +
+                                         (((size_t)b * a.T * a.H + h) * out_w + col0) * sizeof(T)
+                                   : nullptr;
+    uint32_t voff[NBK * 4], ooff[NBK * 4];
 #pragma unroll
-        for (int J = 0; J < NBK; ++J) {
+    for (int J = 0; J < NBK; ++J)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tok = n * C + 16 * J + 4 * gq + i;
-                float x = 0.f;
-                if (live && !mstrip && tok < a.T)
-                    x = to_f<T>(vsrc[(((size_t)b * a.T + tok) * a.H + h) * a.Dv + col]);
-                V[J][i] = x;
+        for (int i = 0; i < 4; ++i) {
+            const int tk = 16 * J + 4 * gq + i;
+            voff[4 * J + i] = (uint32_t)(tk * vstride + r * sizeof(T));
+            ooff[4 * J + i] = (uint32_t)(tk * ostride + r * sizeof(T));
+        }
+
+    // V prefetch: raw element bits, one 32-bit register per element, loaded
+    // unconditionally (in a ragged last chunk, slots past T reread the chunk's
+    // first token and are zeroed when converted), so nothing waits until the
+    // values are consumed one chunk later.
+    auto fetch_v = [&](int n, uint32_t* Vr) {
+        if (!load_v) return;
+        const unsigned char* vp = vbase + (size_t)n * C * vstride;
+        if (n * C + C <= a.T) {
+#pragma unroll
+            for (int k = 0; k < 4 * NBK; ++k) Vr[k] = (uint32_t)*reinterpret_cast<const Raw*>(vp + voff[k]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4 * NBK; ++k) {
+                const int tok = n * C + 16 * (k / 4) + 4 * gq + (k % 4);
+                Vr[k] = (uint32_t)*reinterpret_cast<const Raw*>(vp + (tok < a.T ? voff[k] : (uint32_t)(r * sizeof(T))));
             }
         }
-        __syncthreads();
-        {
-            const uint4* src = reinterpret_cast<const uint4*>(gblk + (size_t)n * L.bytes);
-            uint4* dst = reinterpret_cast<uint4*>(s_raw);
-            for (int i = threadIdx.x; i < (int)(L.bytes / 16); i += 64 * NW) dst[i] = src[i];
+    };
+    auto convert_v = [&](int n, const uint32_t* Vr, floatx4* Vd) {
+        if (!load_v) {
+#pragma unroll
+            for (int J = 0; J < NBK; ++J) Vd[J] = floatx4{0.f, 0.f, 0.f, 0.f};
+        } else if (n * C + C <= a.T) {
+#pragma unroll
+            for (int J = 0; J < NBK; ++J)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Vd[J][i] = RawBits<T>::to_float((Raw)Vr[4 * J + i]);
+        } else {
+#pragma unroll
+            for (int J = 0; J < NBK; ++J)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tok = n * C + 16 * J + 4 * gq + i;
+                    Vd[J][i] = tok < a.T ? RawBits<T>::to_float((Raw)Vr[4 * J + i]) : 0.f;
+                }
         }
-        __syncthreads();
-        if (!live) continue;
+    };
 
+    uint32_t Vr[4 * NBK];
+#pragma unroll
+    for (int k = 0; k < 4 * NBK; ++k) Vr[k] = 0;
+    if (a.NC > 0) {
+        fetch_v(0, Vr);
+        block_to_lds_async<NW>(gblk, s_raw, (int)L.bytes, w, lane);
+    }
+
+    for (int n = 0; n < a.NC; ++n) {
+        unsigned char* cur = s_raw + (kDouble ? (size_t)(n & 1) * L.bytes : 0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();  // block n is in LDS; every wave is done with chunk n - 1
+        const T* s_blk = reinterpret_cast<const T*>(cur);
+        const float* s_gam = reinterpret_cast<const float*>(cur + L.gamma_byte);
+
+        // Operand copy of the incoming state, then S <- Diag(gamma) S in place
+        // (read before the next prefetch is issued into the other buffer).
         Frag<T> Sf[KSD];
 #pragma unroll
         for (int s = 0; s < KSD; ++s)
             Sf[s] = (2 * s + 1 < NBD) ? frag_from_c<T>(S[2 * s], S[2 * s + 1]) : frag_from_c_lo<T>(S[2 * s]);
-
-        // R = V - Kd S
-        floatx4 Rr[NBK];
-#pragma unroll
-        for (int J = 0; J < NBK; ++J) {
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < KSD; ++s) {
-                Frag<T> A;
-                frag_load(A, s_blk + L.kd + (size_t)(J * KSD + s) * 512, lane);
-                acc = mma(A, Sf[s], acc);
-            }
-            Rr[J] = V[J] - acc;
-        }
-        Frag<T> Rf[KSC];
-#pragma unroll
-        for (int s = 0; s < KSC; ++s)
-            Rf[s] = (2 * s + 1 < NBK) ? frag_from_c<T>(Rr[2 * s], Rr[2 * s + 1]) : frag_from_c_lo<T>(Rr[2 * s]);
-        // U = Tb R   (Tb is block lower triangular)
-        floatx4 U[NBK];
-#pragma unroll
-        for (int Ib = 0; Ib < NBK; ++Ib) {
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < KSC; ++s) {
-                if (2 * s <= Ib) {
-                    Frag<T> A;
-                    frag_load(A, s_blk + L.tb + (size_t)(Ib * KSC + s) * 512, lane);
-                    acc = mma(A, Rf[s], acc);
-                }
-            }
-            U[Ib] = acc;
-        }
-        Frag<T> Uf[KSC];
-#pragma unroll
-        for (int s = 0; s < KSC; ++s)
-            Uf[s] = (2 * s + 1 < NBK) ? frag_from_c<T>(U[2 * s], U[2 * s + 1]) : frag_from_c_lo<T>(U[2 * s]);
-        // O = Qp S + Aqk U
-#pragma unroll
-        for (int Ib = 0; Ib < NBK; ++Ib) {
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < KSD; ++s) {
-                Frag<T> A;
-                frag_load(A, s_blk + L.qp + (size_t)(Ib * KSD + s) * 512, lane);
-                acc = mma(A, Sf[s], acc);
-            }
-#pragma unroll
-            for (int s = 0; s < KSC; ++s) {
-                if (2 * s <= Ib) {
-                    Frag<T> A;
-                    frag_load(A, s_blk + L.aqk + (size_t)(Ib * KSC + s) * 512, lane);
-                    acc = mma(A, Uf[s], acc);
-                }
-            }
-            if (store_o) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int tok = n * C + 16 * Ib + 4 * gq + i;
-                    if (tok < a.T)
-                        out[(((size_t)b * a.T + tok) * a.H + h) * out_w + col] = from_f<T>(acc[i]);
-                }
-            }
-        }
-        // S <- Diag(gamma) S + KpT U
 #pragma unroll
         for (int R = 0; R < NBD; ++R) {
-            floatx4 acc = S[R];
+            const float4 g4 = *reinterpret_cast<const float4*>(s_gam + 16 * R + 4 * gq);
+            S[R][0] *= g4.x; S[R][1] *= g4.y; S[R][2] *= g4.z; S[R][3] *= g4.w;
+        }
+        floatx4 V[NBK];
+        convert_v(n, Vr, V);
+        if (kDouble && n + 1 < a.NC) {
+            block_to_lds_async<NW>(gblk + (size_t)(n + 1) * L.bytes, s_raw + (size_t)((n + 1) & 1) * L.bytes,
+                                   (int)L.bytes, w, lane);
+        }
+        if (n + 1 < a.NC) fetch_v(n + 1, Vr);
+
+        if (live) {
+            // R = V - Kd S
+            Frag<T> Ak[NBK][KSD];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] *= s_gam[16 * R + 4 * gq + i];
+            for (int J = 0; J < NBK; ++J)
 #pragma unroll
-            for (int s = 0; s < KSC; ++s) {
-                Frag<T> A;
-                frag_load(A, s_blk + L.kpt + (size_t)(R * KSC + s) * 512, lane);
-                acc = mma(A, Uf[s], acc);
+                for (int s = 0; s < KSD; ++s) frag_load(Ak[J][s], s_blk + L.kd + (size_t)(J * KSD + s) * 512, lane);
+            floatx4 Rr[NBK];
+#pragma unroll
+            for (int J = 0; J < NBK; ++J) {
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KSD; ++s) acc = mma(Ak[J][s], Sf[s], acc);
+                Rr[J] = V[J] - acc;
             }
-            S[R] = acc;
+            // U = Tb R   (Tb is block lower triangular)
+            Frag<T> At[NBK][KSC];
+#pragma unroll
+            for (int Ib = 0; Ib < NBK; ++Ib)
+#pragma unroll
+                for (int s = 0; s < KSC; ++s)
+                    if (2 * s <= Ib) frag_load(At[Ib][s], s_blk + L.tb + (size_t)(Ib * KSC + s) * 512, lane);
+            Frag<T> Rf[KSC];
+#pragma unroll
+            for (int s = 0; s < KSC; ++s)
+                Rf[s] = (2 * s + 1 < NBK) ? frag_from_c<T>(Rr[2 * s], Rr[2 * s + 1]) : frag_from_c_lo<T>(Rr[2 * s]);
+            floatx4 U[NBK];
+#pragma unroll
+            for (int Ib = 0; Ib < NBK; ++Ib) {
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KSC; ++s)
+                    if (2 * s <= Ib) acc = mma(At[Ib][s], Rf[s], acc);
+                U[Ib] = acc;
+            }
+            // O = Qp S + Aqk U
+            Frag<T> Aq[NBK][KSD], Aa[NBK][KSC];
+#pragma unroll
+            for (int Ib = 0; Ib < NBK; ++Ib) {
+#pragma unroll
+                for (int s = 0; s < KSD; ++s) frag_load(Aq[Ib][s], s_blk + L.qp + (size_t)(Ib * KSD + s) * 512, lane);
+#pragma unroll
+                for (int s = 0; s < KSC; ++s)
+                    if (2 * s <= Ib) frag_load(Aa[Ib][s], s_blk + L.aqk + (size_t)(Ib * KSC + s) * 512, lane);
+            }
+            Frag<T> Uf[KSC];
+#pragma unroll
+            for (int s = 0; s < KSC; ++s)
+                Uf[s] = (2 * s + 1 < NBK) ? frag_from_c<T>(U[2 * s], U[2 * s + 1]) : frag_from_c_lo<T>(U[2 * s]);
+            unsigned char* op = store_o ? obase + (size_t)n * C * ostride : nullptr;
+            const bool full = n * C + C <= a.T;
+            floatx4 O[NBK];
+#pragma unroll
+            for (int Ib = 0; Ib < NBK; ++Ib) {
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KSD; ++s) acc = mma(Aq[Ib][s], Sf[s], acc);
+#pragma unroll
+                for (int s = 0; s < KSC; ++s)
+                    if (2 * s <= Ib) acc = mma(Aa[Ib][s], Uf[s], acc);
+                O[Ib] = acc;
+            }
+            if (store_o) {
+                if (full) {
+#pragma unroll
+                    for (int Ib = 0; Ib < NBK; ++Ib)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            *reinterpret_cast<T*>(op + ooff[4 * Ib + i]) = from_f<T>(O[Ib][i]);
+                } else {
+#pragma unroll
+                    for (int Ib = 0; Ib < NBK; ++Ib)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (n * C + 16 * Ib + 4 * gq + i < a.T)
+                                *reinterpret_cast<T*>(op + ooff[4 * Ib + i]) = from_f<T>(O[Ib][i]);
+                }
+            }
+            // S <- Diag(gamma) S + KpT U   (the decay was applied above)
+            Frag<T> Ap[NBD][KSC];
+#pragma unroll
+            for (int R = 0; R < NBD; ++R)
+#pragma unroll
+                for (int s = 0; s < KSC; ++s) frag_load(Ap[R][s], s_blk + L.kpt + (size_t)(R * KSC + s) * 512, lane);
+#pragma unroll
+            for (int R = 0; R < NBD; ++R) {
+#pragma unroll
+                for (int s = 0; s < KSC; ++s) S[R] = mma(Ap[R][s], Uf[s], S[R]);
+            }
+        }
+        if (!kDouble && n + 1 < a.NC) {
+            __syncthreads();  // every wave is done reading the single buffer
+            block_to_lds_async<NW>(gblk + (size_t)(n + 1) * L.bytes, s_raw, (int)L.bytes, w, lane);
         }
     }
 
@@ -517,10 +641,11 @@ __global__ __launch_bounds__(64 * NW) void kda_inter_kernel(const InterArgs a) {
 }
 
 template <typename T, int DK, int C>
-static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t stream) {
+static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t stream, hipEvent_t* ev) {
     constexpr BlockLayout L = block_layout(sizeof(T), DK, C);
     constexpr int NW = 4;
     const int BH = a.B * a.H;
+    if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return hipErrorInvalidValue;
     if (a.NC > 0) {
         IntraArgs ia{a.q, a.k, a.z, a.beta_raw, a.A_log, a.ws, a.T, a.H, a.NC, a.g_min, a.flags};
         hipLaunchKernelGGL((kda_intra_kernel<T, DK, C>), dim3((unsigned)BH * a.NC), dim3(256), 0,
@@ -535,36 +660,41 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t stream) {
     ea.n_strips = ea.n_m + a.Dv / 16;
     ea.n_groups = (ea.n_strips + NW - 1) / NW;
     auto kern = kda_inter_kernel<T, DK, C, NW>;
+    constexpr size_t lds = (2 * L.bytes <= kLdsBudget) ? 2 * L.bytes : L.bytes;
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.bytes);
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(kern, dim3((unsigned)BH * ea.n_groups), dim3(64 * NW), L.bytes, stream, ea);
-    return hipGetLastError();
+    if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kern, dim3((unsigned)BH * ea.n_groups), dim3(64 * NW), lds, stream, ea);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return hipErrorInvalidValue;
+    return hipSuccess;
 }
 
 template <typename T, int DK>
-static hipError_t launch_chunk_c(int C, const ChunkArgs& a, hipStream_t s) {
+static hipError_t launch_chunk_c(int C, const ChunkArgs& a, hipStream_t s, hipEvent_t* ev) {
     switch (C) {
-        case 16: return launch_chunk_t<T, DK, 16>(a, s);
-        case 32: return launch_chunk_t<T, DK, 32>(a, s);
-        case 64: return launch_chunk_t<T, DK, 64>(a, s);
+        case 16: return launch_chunk_t<T, DK, 16>(a, s, ev);
+        case 32: return launch_chunk_t<T, DK, 32>(a, s, ev);
+        case 64: return launch_chunk_t<T, DK, 64>(a, s, ev);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <typename T>
-static hipError_t launch_chunk_d(int DK, int C, const ChunkArgs& a, hipStream_t s) {
+static hipError_t launch_chunk_d(int DK, int C, const ChunkArgs& a, hipStream_t s, hipEvent_t* ev) {
     switch (DK) {
-        case 16: return launch_chunk_c<T, 16>(C, a, s);
-        case 32: return launch_chunk_c<T, 32>(C, a, s);
-        case 64: return launch_chunk_c<T, 64>(C, a, s);
-        case 128: return launch_chunk_c<T, 128>(C, a, s);
+        case 16: return launch_chunk_c<T, 16>(C, a, s, ev);
+        case 32: return launch_chunk_c<T, 32>(C, a, s, ev);
+        case 64: return launch_chunk_c<T, 64>(C, a, s, ev);
+        case 128: return launch_chunk_c<T, 128>(C, a, s, ev);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_chunk(int dt, int DK, int C, const ChunkArgs& a, hipStream_t s) {
-    return dt == 1 ? launch_chunk_d<bf16_t>(DK, C, a, s) : launch_chunk_d<float>(DK, C, a, s);
+hipError_t launch_chunk(int dt, int DK, int C, const ChunkArgs& a, hipStream_t s, hipEvent_t* ev) {
+    return dt == 1 ? launch_chunk_d<bf16_t>(DK, C, a, s, ev) : launch_chunk_d<float>(DK, C, a, s, ev);
 }
 
 }  // namespace kda

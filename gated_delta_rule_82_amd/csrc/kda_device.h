@@ -37,8 +37,9 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float sigmoidf_(float x) {
-    // 1 / (1 + e^-x); exp2 of a large positive argument gives +inf -> 0.
-    return 1.0f / (1.0f + exp2f(-x * kLog2e));
+    // 1 / (1 + e^-x) with the hardware exp2 and reciprocal (about 1 ulp each);
+    // a large negative x gives exp2 = +inf and the reciprocal 0.
+    return __builtin_amdgcn_rcpf(1.0f + exp2_fast(-x * kLog2e));
 }
 
 template <typename T> __device__ __forceinline__ float to_f(T x);
@@ -48,6 +49,17 @@ template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t x) { return (fl
 template <typename T> __device__ __forceinline__ T from_f(float x);
 template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float x) { return (bf16_t)x; }
+
+// Raw element bits, converted to float only when consumed.
+template <typename T> struct RawBits;
+template <> struct RawBits<bf16_t> {
+    typedef uint16_t type;
+    static __device__ __forceinline__ float to_float(uint16_t x) { return bf16_bits_to_float(x); }
+};
+template <> struct RawBits<float> {
+    typedef uint32_t type;
+    static __device__ __forceinline__ float to_float(uint32_t x) { return __uint_as_float(x); }
+};
 
 // Load 4 consecutive elements (8-byte aligned for bf16, 16-byte for fp32).
 __device__ __forceinline__ void load4(const float* p, float out[4]) {
@@ -72,6 +84,7 @@ template <typename T> struct Frag;
 template <> struct Frag<bf16_t> {
     bf16x8 v;
     __device__ __forceinline__ void set(int j, float x) { v[j] = (bf16_t)x; }
+    __device__ __forceinline__ float get(int j) const { return (float)v[j]; }
     __device__ __forceinline__ void zero() {
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = (bf16_t)0.0f;
@@ -80,6 +93,7 @@ template <> struct Frag<bf16_t> {
 template <> struct Frag<float> {
     float v[8];
     __device__ __forceinline__ void set(int j, float x) { v[j] = x; }
+    __device__ __forceinline__ float get(int j) const { return v[j]; }
     __device__ __forceinline__ void zero() {
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = 0.0f;

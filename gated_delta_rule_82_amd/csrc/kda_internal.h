@@ -71,7 +71,9 @@ struct FixupArgs {
 
 // dt: 0 = fp32, 1 = bf16.  Return the launch status (hipSuccess on success).
 hipError_t launch_step(int dt, int DK, int DV, const StepArgs& a, hipStream_t s);
-hipError_t launch_chunk(int dt, int DK, int C, const ChunkArgs& a, hipStream_t s);
+// ev (nullable, 3 events): recorded before the intra kernel, between the two
+// kernels and after the inter kernel, on the same stream.
+hipError_t launch_chunk(int dt, int DK, int C, const ChunkArgs& a, hipStream_t s, hipEvent_t* ev);
 hipError_t launch_compose(int DK, const ComposeArgs& a, hipStream_t s);
 hipError_t launch_fixup(int dt, int DK, const FixupArgs& a, hipStream_t s);
 

@@ -21,7 +21,7 @@ QK_L2NORM, BETA_SIGMOID, GATE_IN_KERNEL = 1, 2, 4
 FLAGS_DEFAULT = 7
 
 EXPORTS = (
-    "kda_safe_chunk_size", "kda_chunk_fwd_workspace", "kda_chunk_fwd", "kda_step",
+    "kda_safe_chunk_size", "kda_chunk_fwd_workspace", "kda_chunk_fwd", "kda_chunk_fwd_timed", "kda_step",
     "kda_segment_compose", "kda_segment_fixup", "kda_status_string",
 )
 
@@ -50,6 +50,8 @@ def load() -> ctypes.CDLL:
     L.kda_chunk_fwd_workspace.restype = S
     L.kda_chunk_fwd.argtypes = [P] * 11 + [I] * 6 + [F, U, I, P, S, P]
     L.kda_chunk_fwd.restype = I
+    L.kda_chunk_fwd_timed.argtypes = [P] * 11 + [I] * 6 + [F, U, I, P, S, P, P]
+    L.kda_chunk_fwd_timed.restype = I
     L.kda_step.argtypes = [P] * 8 + [I] * 4 + [F, U, I, P]
     L.kda_step.restype = I
     L.kda_segment_compose.argtypes = [I, P, P, P, P, I, I, I, I, P]
@@ -101,8 +103,12 @@ def workspace_bytes(B, T, H, Dk, Dv, chunk=64, dtype=torch.bfloat16) -> int:
 
 def chunk_fwd(q, k, v, z, beta_raw, A_log, S0=None, *, chunk=64, g_min=-5.0,
               flags=FLAGS_DEFAULT, want_M=False, want_P=False, o=None, S_out=None,
-              M_out=None, P_out=None, workspace=None):
-    """Chunkwise KDA forward.  Returns (o, S_out) plus M and/or P when asked."""
+              M_out=None, P_out=None, workspace=None, events=None):
+    """Chunkwise KDA forward.  Returns (o, S_out) plus M and/or P when asked.
+
+    `events` (optional): three torch.cuda.Event(enable_timing=True) recorded by
+    the library before, between and after its two kernels (kda_chunk_fwd_timed).
+    """
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
     dt = q.dtype
@@ -118,12 +124,18 @@ def chunk_fwd(q, k, v, z, beta_raw, A_log, S0=None, *, chunk=64, g_min=-5.0,
     need = workspace_bytes(B, T, H, Dk, Dv, chunk, dt)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    st = load().kda_chunk_fwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta_raw), _ptr(A_log), _ptr(S0),
-        _ptr(o), _ptr(S_out), _ptr(M_out), _ptr(P_out),
-        B, T, H, Dk, Dv, chunk, g_min, flags, _dt(dt),
-        _ptr(workspace), workspace.numel(), _stream(dev))
-    _check("kda_chunk_fwd", st)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta_raw), _ptr(A_log), _ptr(S0),
+            _ptr(o), _ptr(S_out), _ptr(M_out), _ptr(P_out),
+            B, T, H, Dk, Dv, chunk, g_min, flags, _dt(dt),
+            _ptr(workspace), workspace.numel(), _stream(dev))
+    if events is None:
+        _check("kda_chunk_fwd", load().kda_chunk_fwd(*args))
+    else:
+        for e in events:
+            if e.cuda_event == 0:  # torch creates the HIP event on its first record
+                e.record()
+        evs = (ctypes.c_void_p * 3)(*[e.cuda_event for e in events])
+        _check("kda_chunk_fwd_timed", load().kda_chunk_fwd_timed(*args, evs))
     out = [o, S_out]
     if want_M:
         out.append(M_out)

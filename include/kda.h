@@ -97,6 +97,19 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
                          float g_min, unsigned flags, kda_dtype dt,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Same computation and validation as kda_chunk_fwd, for measurement: the three
+ * caller-created events are recorded on `stream` before the intra-chunk
+ * kernel, between it and the inter-chunk kernel, and after the latter, so the
+ * caller can time each kernel with hipEventElapsedTime.  KDA_ERR_NULL if any
+ * event is NULL. */
+kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void* z,
+                               const void* beta_raw, const float* A_log, const float* S0,
+                               void* o, float* S_out, float* M_out, void* P_out,
+                               int B, int T, int H, int Dk, int Dv, int chunk,
+                               float g_min, unsigned flags, kda_dtype dt,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream,
+                               hipEvent_t events[3]);
+
 /* One decode step per (b,h), state updated IN PLACE ("KDA 模块交互式演示" §1.7
  * kda_step; "Implémenter KDA" reference step): decay, erase along k, write,
  * then read the updated state.  q, k, z [B,H,Dk]; v [B,H,Dv]; beta_raw [B,H];
