@@ -161,7 +161,8 @@ def bench_layer(torch, kda, inputs, steps, warmup):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    nk = kda.kernel_count(B, T, H, Dk, Dv, C, torch.bfloat16)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
@@ -170,11 +171,13 @@ def bench_layer(torch, kda, inputs, steps, warmup):
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
-    intra = [e[0].elapsed_time(e[1]) for e in evs]
-    inter = [e[1].elapsed_time(e[2]) for e in evs]
+    # kernels alternate intra, inter over the slices of the sequence
+    intra = [sum(e[k].elapsed_time(e[k + 1]) for k in range(0, nk, 2)) for e in evs]
+    inter = [sum(e[k].elapsed_time(e[k + 1]) for k in range(1, nk, 2)) for e in evs]
     return {"B": B, "T": T, "H": H, "Dk": Dk, "Dv": Dv, "C": C, "ws_bytes": ws_n,
             "ms_per_step": total_ms / steps,
-            "kernel_ms": {"kda_intra": sum(intra) / steps, "kda_inter": sum(inter) / steps}}
+            "kernel_ms": {"kda_intra": sum(intra) / steps, "kda_inter": sum(inter) / steps},
+            "launches_per_step": nk}
 
 
 def bench_decode(torch, kda, inputs, steps, warmup):

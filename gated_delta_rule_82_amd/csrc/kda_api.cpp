@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/kda.h"
 #include "kda_internal.h"
 
@@ -39,6 +41,29 @@ kda_status maybe(const void* p) { return (!p || aligned16(p)) ? KDA_OK : KDA_ERR
 
 }  // namespace
 
+namespace kda {
+
+int occupancy_blocks(const void* kernel, int block_threads) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, block_threads, 0) != hipSuccess) return 1;
+    return nb > 0 ? nb : 1;
+}
+
+int device_cu_count() {
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> cache[kMaxDev];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) dev = 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+}  // namespace kda
+
 extern "C" {
 
 int kda_safe_chunk_size(float g_min, kda_dtype dt) {
@@ -53,8 +78,8 @@ size_t kda_chunk_fwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk, k
     if (B < 0 || T < 0 || H < 0 || !dim_ok(Dk) || !dim_ok(Dv) || !dtype_ok(dt)) return 0;
     if (chunk != 16 && chunk != 32 && chunk != 64) return 0;
     const size_t nc = (size_t)(T + chunk - 1) / (size_t)chunk;
-    const kda::BlockLayout L = kda::block_layout(elem_bytes(dt), Dk, chunk);
-    return (size_t)B * (size_t)H * nc * L.bytes;
+    if ((size_t)B * H == 0) return 0;
+    return kda::chunk_workspace_bytes(elem_bytes(dt), Dk, Dv, chunk, (size_t)B * H, nc);
 }
 
 }  // extern "C"
@@ -65,7 +90,7 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
                                  int B, int T, int H, int Dk, int Dv, int chunk,
                                  float g_min, unsigned flags, kda_dtype dt,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream,
-                                 hipEvent_t* ev) {
+                                 hipEvent_t* ev, int n_ev) {
     if (!dtype_ok(dt) || !flags_ok(flags)) return KDA_ERR_DTYPE;
     if (chunk == 0) chunk = 64;
     if (B < 0 || T < 0 || H < 0 || !dim_ok(Dk) || !dim_ok(Dv)) return KDA_ERR_SHAPE;
@@ -91,7 +116,13 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
     a.o = o; a.S_out = S_out; a.M_out = M_out; a.P_out = P_out; a.ws = workspace;
     a.B = B; a.T = T; a.H = H; a.Dv = Dv; a.NC = (T + chunk - 1) / chunk;
     a.g_min = g_min; a.flags = flags;
-    const hipError_t e = kda::launch_chunk(dt == KDA_BF16 ? 1 : 0, Dk, chunk, a, stream, ev);
+    if (ev) {
+        const int need = kda::chunk_kernel_count(elem_bytes(dt), Dk, chunk, B * H, a.NC) + 1;
+        if (n_ev < need) return KDA_ERR_NULL;
+        for (int i = 0; i < need; ++i)
+            if (!ev[i]) return KDA_ERR_NULL;
+    }
+    const hipError_t e = kda::launch_chunk(dt == KDA_BF16 ? 1 : 0, Dk, chunk, a, stream, ev, n_ev);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -104,7 +135,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
                          float g_min, unsigned flags, kda_dtype dt,
                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return chunk_fwd_impl(q, k, v, z, beta_raw, A_log, S0, o, S_out, M_out, P_out, B, T, H, Dk, Dv,
-                          chunk, g_min, flags, dt, workspace, workspace_bytes, stream, nullptr);
+                          chunk, g_min, flags, dt, workspace, workspace_bytes, stream, nullptr, 0);
 }
 
 kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void* z,
@@ -113,10 +144,17 @@ kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, cons
                                int B, int T, int H, int Dk, int Dv, int chunk,
                                float g_min, unsigned flags, kda_dtype dt,
                                void* workspace, size_t workspace_bytes, hipStream_t stream,
-                               hipEvent_t events[3]) {
-    if (!events || !events[0] || !events[1] || !events[2]) return KDA_ERR_NULL;
+                               hipEvent_t* events, int n_events) {
+    if (!events) return KDA_ERR_NULL;
     return chunk_fwd_impl(q, k, v, z, beta_raw, A_log, S0, o, S_out, M_out, P_out, B, T, H, Dk, Dv,
-                          chunk, g_min, flags, dt, workspace, workspace_bytes, stream, events);
+                          chunk, g_min, flags, dt, workspace, workspace_bytes, stream, events, n_events);
+}
+
+int kda_chunk_fwd_kernel_count(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype dt) {
+    if (chunk == 0) chunk = 64;
+    if (B <= 0 || T < 0 || H <= 0 || !dim_ok(Dk) || !dim_ok(Dv) || !dtype_ok(dt)) return 0;
+    if (chunk != 16 && chunk != 32 && chunk != 64) return 0;
+    return kda::chunk_kernel_count(elem_bytes(dt), Dk, chunk, B * H, (T + chunk - 1) / chunk);
 }
 
 kda_status kda_step(const void* q, const void* k, const void* v, const void* z,

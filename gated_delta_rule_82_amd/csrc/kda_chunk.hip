@@ -29,6 +29,8 @@
 // block's entry), exp(G_i - G_j) = exp(L_i) * exp(-L_j) with both factors in
 // [e^-80, e^80].  Across blocks J < I the column factor is taken from the end
 // of block J and the gap between blocks is a per-channel scale <= 1.
+#include <algorithm>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -38,6 +40,7 @@ struct IntraArgs {
     const void* q; const void* k; const void* z; const void* beta_raw;
     const float* A_log; void* ws;
     int T, H, NC;
+    int c0, nc;          // chunks [c0, c0 + nc) of every (b, h) in this launch
     float g_min;
     unsigned flags;
 };
@@ -70,9 +73,9 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     const int r = lane & 15;
     const int gq = lane >> 4;
 
-    const int cid = blockIdx.x;
-    const int n = cid % a.NC;
-    const int bh = cid / a.NC;
+    const int n = a.c0 + (int)blockIdx.x % a.nc;
+    const int bh = (int)blockIdx.x / a.nc;
+    const int cid = bh * a.NC + n;     // workspace block of (b, h, chunk n)
     const int h = bh % a.H;
     const int b = bh / a.H;
 
@@ -142,7 +145,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
         }
         if (gq == 0) s_beta[16 * I + r] = beta;
     }
-    __syncthreads();
+    lds_barrier();
 
     // ------------------------------------------------------------ phase B
     // Per (block, channel) decay factors, each computed once.
@@ -171,7 +174,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
         }
         if (Ib == 0) ws_gamma[c] = exp2_fast(GC);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ------------------------------------------------------------ phase C
     // Row operands (q, k scaled by exp(L)), diagonal column operand
@@ -243,7 +246,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ------------------------------------------------------------ phase D
     floatx4 TdC = {0.f, 0.f, 0.f, 0.f}, TdR = {0.f, 0.f, 0.f, 0.f};
@@ -321,7 +324,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
         TdR = P2R + mm16(P2C, N8R);
         *reinterpret_cast<float4*>(&s_tdiag[I][lane * 4]) = make_float4(TdR[0], TdR[1], TdR[2], TdR[3]);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ------------------------------------------------------------ phase E
     // Wave J builds block column J of T = (I + A_kk)^-1:
@@ -363,22 +366,23 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
 }
 
 struct InterArgs {
-    const void* v; const float* S0;
+    const void* v;
+    const float* S0;     // incoming state of the value strips (NULL: zero)
+    const float* M0;     // incoming transition of the identity strips (NULL: identity)
     void* o; float* S_out; float* M_out; void* P_out;
     const void* ws;
     int T, H, Dv, NC;
+    int c0, nc;          // chunks [c0, c0 + nc) in this launch
     int n_m, n_strips, n_groups;
 };
 
 constexpr size_t kLdsBudget = 160 * 1024;  // LDS per CU on gfx950
 
-// Start an asynchronous copy of one contiguous chunk block from global memory
-// into LDS (global_load_lds: 16 bytes per lane, 1 KiB per wave instruction).
-// Completion is awaited with s_waitcnt vmcnt(0) followed by a barrier.
-template <int NW>
-__device__ __forceinline__ void block_to_lds_async(const unsigned char* src, unsigned char* dst,
-                                                   int bytes, int w, int lane) {
-    for (int off = w * 1024; off < bytes; off += NW * 1024) {
+// Asynchronous copy of one contiguous block into LDS by a single wave
+// (global_load_lds: 16 bytes per lane, 1 KiB per instruction).
+__device__ __forceinline__ void wave_copy_to_lds(const unsigned char* src, unsigned char* dst, int bytes,
+                                                 int lane) {
+    for (int off = 0; off < bytes; off += 1024) {
         if (off + lane * 16 < bytes)
             __builtin_amdgcn_global_load_lds(
                 (const __attribute__((address_space(1))) void*)(src + off + lane * 16),
@@ -386,8 +390,15 @@ __device__ __forceinline__ void block_to_lds_async(const unsigned char* src, uns
     }
 }
 
+// Inter-chunk kernel.  A workgroup serves NW 16-column strips of one (b, h)
+// with NW compute waves plus one copy wave:
+//   * the copy wave streams the next chunk block into the spare LDS buffer,
+//     waiting only on its own loads;
+//   * the compute waves hold their strip of S in fp32 registers, read operands
+//     from LDS and V/o from global memory, and never wait on the copy.
+// One fence-free barrier per chunk hands the buffers over.
 template <typename T, int DK, int C, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * (NW + 1)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void kda_inter_kernel(const InterArgs a) {
     constexpr BlockLayout L = block_layout(sizeof(T), DK, C);
     constexpr int NBK = C / 16;
@@ -407,6 +418,29 @@ void kda_inter_kernel(const InterArgs a) {
     const int bh = bid / a.n_groups;
     const int h = bh % a.H;
     const int b = bh / a.H;
+    const unsigned char* gblk = reinterpret_cast<const unsigned char*>(a.ws) + (size_t)bh * a.NC * L.bytes;
+
+    if (w == NW) {
+        // ------------------------------------------------------ copy wave
+        const int cend = a.c0 + a.nc;
+        if (a.nc > 0) {
+            wave_copy_to_lds(gblk + (size_t)a.c0 * L.bytes, s_raw, (int)L.bytes, lane);
+            wait_vmcnt<0>();
+        }
+        lds_barrier();  // the first block is in LDS
+        for (int n = a.c0; n < cend; ++n) {
+            if (!kDouble) lds_barrier();  // compute waves are done with the single buffer
+            if (n + 1 < cend) {
+                wave_copy_to_lds(gblk + (size_t)(n + 1) * L.bytes,
+                                 s_raw + (kDouble ? (size_t)((n + 1 - a.c0) & 1) * L.bytes : 0), (int)L.bytes, lane);
+                wait_vmcnt<0>();  // block n + 1 is in LDS
+            }
+            lds_barrier();
+        }
+        return;
+    }
+
+    // ------------------------------------------------------------ compute waves
     const int strip = grp * NW + w;           // wave-uniform
     const bool live = strip < a.n_strips;
     const bool mstrip = strip < a.n_m;
@@ -421,15 +455,13 @@ void kda_inter_kernel(const InterArgs a) {
             const int rw = 16 * R + 4 * gq + i;
             float x = 0.f;
             if (live) {
-                if (mstrip) x = (rw == col) ? 1.f : 0.f;
+                if (mstrip) x = a.M0 ? a.M0[((size_t)bh * DK + rw) * DK + col] : ((rw == col) ? 1.f : 0.f);
                 else if (a.S0) x = a.S0[((size_t)bh * DK + rw) * a.Dv + col];
             }
             S[R][i] = x;
         }
     }
 
-    const unsigned char* gblk = reinterpret_cast<const unsigned char*>(a.ws) +
-                                (size_t)bh * a.NC * L.bytes;
     T* out = mstrip ? reinterpret_cast<T*>(a.P_out) : reinterpret_cast<T*>(a.o);
     const int out_w = mstrip ? DK : a.Dv;
     const bool store_o = live && out != nullptr;
@@ -437,7 +469,7 @@ void kda_inter_kernel(const InterArgs a) {
 
     // Token-major addressing: a wave-uniform byte base per chunk plus a 32-bit
     // lane byte offset (token within the chunk times the token stride, plus
-    // the column), so global accesses take the scalar-base form.
+    // the column).
     using Raw = typename RawBits<T>::type;
     const size_t vstride = (size_t)a.H * a.Dv * sizeof(T);   // bytes per token
     const size_t ostride = (size_t)a.H * out_w * sizeof(T);
@@ -456,10 +488,9 @@ void kda_inter_kernel(const InterArgs a) {
             ooff[4 * J + i] = (uint32_t)(tk * ostride + r * sizeof(T));
         }
 
-    // V prefetch: raw element bits, one 32-bit register per element, loaded
-    // unconditionally (in a ragged last chunk, slots past T reread the chunk's
-    // first token and are zeroed when converted), so nothing waits until the
-    // values are consumed one chunk later.
+    // V prefetch one chunk ahead: raw element bits, one 32-bit register per
+    // element (in a ragged last chunk, slots past T reread the chunk's first
+    // token and are zeroed when converted).
     auto fetch_v = [&](int n, uint32_t* Vr) {
         if (!load_v) return;
         const unsigned char* vp = vbase + (size_t)n * C * vstride;
@@ -497,20 +528,16 @@ void kda_inter_kernel(const InterArgs a) {
     uint32_t Vr[4 * NBK];
 #pragma unroll
     for (int k = 0; k < 4 * NBK; ++k) Vr[k] = 0;
-    if (a.NC > 0) {
-        fetch_v(0, Vr);
-        block_to_lds_async<NW>(gblk, s_raw, (int)L.bytes, w, lane);
-    }
+    const int cend = a.c0 + a.nc;
+    if (a.nc > 0) fetch_v(a.c0, Vr);
+    lds_barrier();  // the first block is in LDS
 
-    for (int n = 0; n < a.NC; ++n) {
-        unsigned char* cur = s_raw + (kDouble ? (size_t)(n & 1) * L.bytes : 0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();  // block n is in LDS; every wave is done with chunk n - 1
+    for (int n = a.c0; n < cend; ++n) {
+        const unsigned char* cur = s_raw + (kDouble ? (size_t)((n - a.c0) & 1) * L.bytes : 0);
         const T* s_blk = reinterpret_cast<const T*>(cur);
         const float* s_gam = reinterpret_cast<const float*>(cur + L.gamma_byte);
 
-        // Operand copy of the incoming state, then S <- Diag(gamma) S in place
-        // (read before the next prefetch is issued into the other buffer).
+        // Operand copy of the incoming state, then S <- Diag(gamma) S in place.
         Frag<T> Sf[KSD];
 #pragma unroll
         for (int s = 0; s < KSD; ++s)
@@ -522,11 +549,7 @@ void kda_inter_kernel(const InterArgs a) {
         }
         floatx4 V[NBK];
         convert_v(n, Vr, V);
-        if (kDouble && n + 1 < a.NC) {
-            block_to_lds_async<NW>(gblk + (size_t)(n + 1) * L.bytes, s_raw + (size_t)((n + 1) & 1) * L.bytes,
-                                   (int)L.bytes, w, lane);
-        }
-        if (n + 1 < a.NC) fetch_v(n + 1, Vr);
+        if (n + 1 < cend) fetch_v(n + 1, Vr);
 
         if (live) {
             // R = V - Kd S
@@ -618,10 +641,8 @@ void kda_inter_kernel(const InterArgs a) {
                 for (int s = 0; s < KSC; ++s) S[R] = mma(Ap[R][s], Uf[s], S[R]);
             }
         }
-        if (!kDouble && n + 1 < a.NC) {
-            __syncthreads();  // every wave is done reading the single buffer
-            block_to_lds_async<NW>(gblk + (size_t)(n + 1) * L.bytes, s_raw, (int)L.bytes, w, lane);
-        }
+        if (!kDouble) lds_barrier();  // done reading the single buffer
+        lds_barrier();                // block n + 1 is in LDS
     }
 
     if (live) {
@@ -640,61 +661,102 @@ void kda_inter_kernel(const InterArgs a) {
     }
 }
 
+// Chunks per slice: intra and inter alternate over slices of the sequence of
+// at most kSliceBytes of intermediates each.  Measured on MI355X, smaller
+// slices (64-128 MB, to keep a slice in the 256 MB Infinity Cache) lose more
+// to partial grids and per-launch prologues than they gain, so the budget is
+// large: the layer-sized workloads run as a single slice.
+constexpr size_t kSliceBytes = 1ull << 30;
+
+__host__ inline int slice_chunks(int BH, int NC, size_t block_bytes) {
+    if (NC <= 0) return 0;
+    const size_t per = std::max<size_t>(1, kSliceBytes / std::max<size_t>(1, (size_t)BH * block_bytes));
+    const int nsl = (int)((NC + per - 1) / per);
+    return (NC + nsl - 1) / nsl;
+}
+
 template <typename T, int DK, int C>
-static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t stream, hipEvent_t* ev) {
+static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t stream, hipEvent_t* ev, int n_ev) {
     constexpr BlockLayout L = block_layout(sizeof(T), DK, C);
     constexpr int NW = 4;
     const int BH = a.B * a.H;
-    if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return hipErrorInvalidValue;
-    if (a.NC > 0) {
-        IntraArgs ia{a.q, a.k, a.z, a.beta_raw, a.A_log, a.ws, a.T, a.H, a.NC, a.g_min, a.flags};
-        hipLaunchKernelGGL((kda_intra_kernel<T, DK, C>), dim3((unsigned)BH * a.NC), dim3(256), 0,
-                           stream, ia);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    InterArgs ea{};
-    ea.v = a.v; ea.S0 = a.S0; ea.o = a.o; ea.S_out = a.S_out; ea.M_out = a.M_out; ea.P_out = a.P_out;
-    ea.ws = a.ws; ea.T = a.T; ea.H = a.H; ea.Dv = a.Dv; ea.NC = a.NC;
-    ea.n_m = (a.M_out || a.P_out) ? DK / 16 : 0;
-    ea.n_strips = ea.n_m + a.Dv / 16;
-    ea.n_groups = (ea.n_strips + NW - 1) / NW;
     auto kern = kda_inter_kernel<T, DK, C, NW>;
     constexpr size_t lds = (2 * L.bytes <= kLdsBudget) ? 2 * L.bytes : L.bytes;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
-    if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(kern, dim3((unsigned)BH * ea.n_groups), dim3(64 * NW), lds, stream, ea);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return hipErrorInvalidValue;
+
+    // running state between slices: S then M, after the chunk blocks
+    float* S_scr = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(a.ws) + (size_t)BH * a.NC * L.bytes);
+    float* M_scr = S_scr + (size_t)BH * DK * a.Dv;
+
+    InterArgs ea{};
+    ea.v = a.v; ea.o = a.o; ea.P_out = a.P_out; ea.ws = a.ws;
+    ea.T = a.T; ea.H = a.H; ea.Dv = a.Dv; ea.NC = a.NC;
+    ea.n_m = (a.M_out || a.P_out) ? DK / 16 : 0;
+    ea.n_strips = ea.n_m + a.Dv / 16;
+    ea.n_groups = (ea.n_strips + NW - 1) / NW;
+
+    int k = 0;  // kernels launched so far (event k + 1 is recorded after kernel k)
+    auto mark = [&]() -> bool { return !ev || k + 1 >= n_ev || hipEventRecord(ev[++k], stream) == hipSuccess; };
+    if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return hipErrorInvalidValue;
+
+    const int per = slice_chunks(BH, a.NC, L.bytes);
+    const int nsl = a.NC > 0 ? (a.NC + per - 1) / per : 1;
+    for (int sl = 0; sl < nsl; ++sl) {
+        const int c0 = sl * per;
+        const int nc = std::min(per, a.NC - c0);
+        const bool first = sl == 0, last = sl == nsl - 1;
+        if (nc > 0) {
+            IntraArgs ia{a.q, a.k, a.z, a.beta_raw, a.A_log, a.ws, a.T, a.H, a.NC, c0, nc, a.g_min, a.flags};
+            hipLaunchKernelGGL((kda_intra_kernel<T, DK, C>), dim3((unsigned)(BH * nc)), dim3(256), 0, stream, ia);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            if (!mark()) return hipErrorInvalidValue;
+        }
+        ea.c0 = c0; ea.nc = std::max(nc, 0);
+        ea.S0 = first ? a.S0 : S_scr;
+        ea.M0 = first ? nullptr : M_scr;
+        ea.S_out = last ? a.S_out : S_scr;
+        ea.M_out = last ? a.M_out : M_scr;
+        hipLaunchKernelGGL(kern, dim3((unsigned)BH * ea.n_groups), dim3(64 * (NW + 1)), lds, stream, ea);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        if (!mark()) return hipErrorInvalidValue;
+    }
     return hipSuccess;
 }
 
+int chunk_kernel_count(int elem_bytes, int DK, int C, int BH, int NC) {
+    const BlockLayout L = block_layout(elem_bytes, DK, C);
+    if (NC <= 0) return 1;
+    const int per = slice_chunks(BH, NC, L.bytes);
+    return 2 * ((NC + per - 1) / per);
+}
+
 template <typename T, int DK>
-static hipError_t launch_chunk_c(int C, const ChunkArgs& a, hipStream_t s, hipEvent_t* ev) {
+static hipError_t launch_chunk_c(int C, const ChunkArgs& a, hipStream_t s, hipEvent_t* ev, int n_ev) {
     switch (C) {
-        case 16: return launch_chunk_t<T, DK, 16>(a, s, ev);
-        case 32: return launch_chunk_t<T, DK, 32>(a, s, ev);
-        case 64: return launch_chunk_t<T, DK, 64>(a, s, ev);
+        case 16: return launch_chunk_t<T, DK, 16>(a, s, ev, n_ev);
+        case 32: return launch_chunk_t<T, DK, 32>(a, s, ev, n_ev);
+        case 64: return launch_chunk_t<T, DK, 64>(a, s, ev, n_ev);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <typename T>
-static hipError_t launch_chunk_d(int DK, int C, const ChunkArgs& a, hipStream_t s, hipEvent_t* ev) {
+static hipError_t launch_chunk_d(int DK, int C, const ChunkArgs& a, hipStream_t s, hipEvent_t* ev, int n_ev) {
     switch (DK) {
-        case 16: return launch_chunk_c<T, 16>(C, a, s, ev);
-        case 32: return launch_chunk_c<T, 32>(C, a, s, ev);
-        case 64: return launch_chunk_c<T, 64>(C, a, s, ev);
-        case 128: return launch_chunk_c<T, 128>(C, a, s, ev);
+        case 16: return launch_chunk_c<T, 16>(C, a, s, ev, n_ev);
+        case 32: return launch_chunk_c<T, 32>(C, a, s, ev, n_ev);
+        case 64: return launch_chunk_c<T, 64>(C, a, s, ev, n_ev);
+        case 128: return launch_chunk_c<T, 128>(C, a, s, ev, n_ev);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_chunk(int dt, int DK, int C, const ChunkArgs& a, hipStream_t s, hipEvent_t* ev) {
-    return dt == 1 ? launch_chunk_d<bf16_t>(DK, C, a, s, ev) : launch_chunk_d<float>(DK, C, a, s, ev);
+hipError_t launch_chunk(int dt, int DK, int C, const ChunkArgs& a, hipStream_t s, hipEvent_t* ev, int n_ev) {
+    return dt == 1 ? launch_chunk_d<bf16_t>(DK, C, a, s, ev, n_ev) : launch_chunk_d<float>(DK, C, a, s, ev, n_ev);
 }
 
 }  // namespace kda

@@ -44,6 +44,12 @@ __host__ __device__ constexpr BlockLayout block_layout(int elem_bytes, int DK, i
     return L;
 }
 
+// Workspace: the chunk blocks of every (b, h, chunk), then the running state
+// carried between slices of the sequence (S [BH, Dk, Dv] and M [BH, Dk, Dk]).
+__host__ __device__ constexpr size_t chunk_workspace_bytes(int elem_bytes, int DK, int Dv, int C, size_t BH, size_t NC) {
+    return BH * NC * block_layout(elem_bytes, DK, C).bytes + round_up(BH * (size_t)DK * (DK + Dv) * 4, 256);
+}
+
 struct StepArgs {
     const void* q; const void* k; const void* v; const void* z; const void* beta_raw;
     const float* A_log; float* S; void* o;
@@ -69,11 +75,19 @@ struct FixupArgs {
     int n_seg, B, T_seg, H, Dv;
 };
 
+// Resident workgroups per CU for a kernel at this block size, and the CU
+// count of the current device (queried once and cached).
+int occupancy_blocks(const void* kernel, int block_threads);
+int device_cu_count();
+
 // dt: 0 = fp32, 1 = bf16.  Return the launch status (hipSuccess on success).
 hipError_t launch_step(int dt, int DK, int DV, const StepArgs& a, hipStream_t s);
-// ev (nullable, 3 events): recorded before the intra kernel, between the two
-// kernels and after the inter kernel, on the same stream.
-hipError_t launch_chunk(int dt, int DK, int C, const ChunkArgs& a, hipStream_t s, hipEvent_t* ev);
+// ev (nullable, n_ev events): ev[0] is recorded before the first kernel and
+// ev[k + 1] after kernel k, on the same stream (kernels alternate intra,
+// inter over the slices of the sequence; events past n_ev are skipped).
+hipError_t launch_chunk(int dt, int DK, int C, const ChunkArgs& a, hipStream_t s, hipEvent_t* ev, int n_ev);
+// Kernels one kda_chunk_fwd call launches for these sizes.
+int chunk_kernel_count(int elem_bytes, int DK, int C, int BH, int NC);
 hipError_t launch_compose(int DK, const ComposeArgs& a, hipStream_t s);
 hipError_t launch_fixup(int dt, int DK, const FixupArgs& a, hipStream_t s);
 

@@ -21,7 +21,8 @@ QK_L2NORM, BETA_SIGMOID, GATE_IN_KERNEL = 1, 2, 4
 FLAGS_DEFAULT = 7
 
 EXPORTS = (
-    "kda_safe_chunk_size", "kda_chunk_fwd_workspace", "kda_chunk_fwd", "kda_chunk_fwd_timed", "kda_step",
+    "kda_safe_chunk_size", "kda_chunk_fwd_workspace", "kda_chunk_fwd", "kda_chunk_fwd_timed",
+    "kda_chunk_fwd_kernel_count", "kda_step",
     "kda_segment_compose", "kda_segment_fixup", "kda_status_string",
 )
 
@@ -50,8 +51,10 @@ def load() -> ctypes.CDLL:
     L.kda_chunk_fwd_workspace.restype = S
     L.kda_chunk_fwd.argtypes = [P] * 11 + [I] * 6 + [F, U, I, P, S, P]
     L.kda_chunk_fwd.restype = I
-    L.kda_chunk_fwd_timed.argtypes = [P] * 11 + [I] * 6 + [F, U, I, P, S, P, P]
+    L.kda_chunk_fwd_timed.argtypes = [P] * 11 + [I] * 6 + [F, U, I, P, S, P, P, I]
     L.kda_chunk_fwd_timed.restype = I
+    L.kda_chunk_fwd_kernel_count.argtypes = [I] * 7
+    L.kda_chunk_fwd_kernel_count.restype = I
     L.kda_step.argtypes = [P] * 8 + [I] * 4 + [F, U, I, P]
     L.kda_step.restype = I
     L.kda_segment_compose.argtypes = [I, P, P, P, P, I, I, I, I, P]
@@ -101,13 +104,19 @@ def workspace_bytes(B, T, H, Dk, Dv, chunk=64, dtype=torch.bfloat16) -> int:
     return load().kda_chunk_fwd_workspace(B, T, H, Dk, Dv, chunk, _dt(dtype))
 
 
+def kernel_count(B, T, H, Dk, Dv, chunk=64, dtype=torch.bfloat16) -> int:
+    """Kernels one chunk_fwd call launches (intra and inter alternate over slices)."""
+    return load().kda_chunk_fwd_kernel_count(B, T, H, Dk, Dv, chunk, _dt(dtype))
+
+
 def chunk_fwd(q, k, v, z, beta_raw, A_log, S0=None, *, chunk=64, g_min=-5.0,
               flags=FLAGS_DEFAULT, want_M=False, want_P=False, o=None, S_out=None,
               M_out=None, P_out=None, workspace=None, events=None):
     """Chunkwise KDA forward.  Returns (o, S_out) plus M and/or P when asked.
 
-    `events` (optional): three torch.cuda.Event(enable_timing=True) recorded by
-    the library before, between and after its two kernels (kda_chunk_fwd_timed).
+    `events` (optional): a list of at least kernel_count(...) + 1
+    torch.cuda.Event(enable_timing=True); the library records events[0] before
+    its first kernel and events[k + 1] after kernel k (kda_chunk_fwd_timed).
     """
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
@@ -134,8 +143,8 @@ def chunk_fwd(q, k, v, z, beta_raw, A_log, S0=None, *, chunk=64, g_min=-5.0,
         for e in events:
             if e.cuda_event == 0:  # torch creates the HIP event on its first record
                 e.record()
-        evs = (ctypes.c_void_p * 3)(*[e.cuda_event for e in events])
-        _check("kda_chunk_fwd_timed", load().kda_chunk_fwd_timed(*args, evs))
+        evs = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+        _check("kda_chunk_fwd_timed", load().kda_chunk_fwd_timed(*args, evs, len(events)))
     out = [o, S_out]
     if want_M:
         out.append(M_out)

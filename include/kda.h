@@ -73,7 +73,8 @@ int kda_safe_chunk_size(float g_min, kda_dtype dt);
 
 /* Bytes of device workspace kda_chunk_fwd needs for these sizes (0 for invalid
  * sizes).  The workspace holds the per-chunk intermediates of the chunkwise
- * form; it must be 256-byte aligned.  Host only. */
+ * form and the state carried between slices; it must be 256-byte aligned.
+ * Host only. */
 size_t kda_chunk_fwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk,
                                kda_dtype dt);
 
@@ -97,18 +98,25 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
                          float g_min, unsigned flags, kda_dtype dt,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Same computation and validation as kda_chunk_fwd, for measurement: the three
- * caller-created events are recorded on `stream` before the intra-chunk
- * kernel, between it and the inter-chunk kernel, and after the latter, so the
- * caller can time each kernel with hipEventElapsedTime.  KDA_ERR_NULL if any
- * event is NULL. */
+/* Number of kernels one kda_chunk_fwd call launches for these sizes (0 for
+ * invalid sizes).  The intra-chunk and inter-chunk kernels alternate over
+ * slices of the sequence, so that a slice's intermediates are read back while
+ * they are still in the GPU's last-level cache.  Host only. */
+int kda_chunk_fwd_kernel_count(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype dt);
+
+/* Same computation and validation as kda_chunk_fwd, for measurement: events[0]
+ * is recorded on `stream` before the first kernel and events[k + 1] after
+ * kernel k (kernels alternate intra-chunk, inter-chunk), so the caller can time
+ * each kernel with hipEventElapsedTime.  n_events must be at least
+ * kda_chunk_fwd_kernel_count(...) + 1; KDA_ERR_NULL otherwise or if an event
+ * is NULL. */
 kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void* z,
                                const void* beta_raw, const float* A_log, const float* S0,
                                void* o, float* S_out, float* M_out, void* P_out,
                                int B, int T, int H, int Dk, int Dv, int chunk,
                                float g_min, unsigned flags, kda_dtype dt,
                                void* workspace, size_t workspace_bytes, hipStream_t stream,
-                               hipEvent_t events[3]);
+                               hipEvent_t* events, int n_events);
 
 /* One decode step per (b,h), state updated IN PLACE ("KDA 模块交互式演示" §1.7
  * kda_step; "Implémenter KDA" reference step): decay, erase along k, write,

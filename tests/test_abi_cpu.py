@@ -44,11 +44,16 @@ def test_safe_chunk_size(lib):
 
 
 def test_workspace_sizes(lib):
-    # 64 fragment tiles of 1 KiB + 512 B of fp32 decay per (b, h, chunk) for bf16 D=128 C=64
+    # 64 fragment tiles of 1 KiB + 512 B of fp32 decay per (b, h, chunk) for bf16 D=128 C=64,
+    # plus the fp32 state and transition carried between slices of the sequence
     per = 64 * 1024 + 512
-    assert lib.kda_chunk_fwd_workspace(4, 4096, 16, 128, 128, 64, 1) == 4 * 16 * 64 * per
-    assert lib.kda_chunk_fwd_workspace(1, 65, 1, 128, 128, 64, 1) == 2 * per
-    assert lib.kda_chunk_fwd_workspace(1, 0, 1, 128, 128, 64, 1) == 0
+    carry = lambda bh, dk, dv: bh * dk * (dk + dv) * 4
+    assert lib.kda_chunk_fwd_workspace(4, 4096, 16, 128, 128, 64, 1) == 4 * 16 * 64 * per + carry(64, 128, 128)
+    assert lib.kda_chunk_fwd_workspace(1, 65, 1, 128, 128, 64, 1) == 2 * per + carry(1, 128, 128)
+    assert lib.kda_chunk_fwd_workspace(1, 0, 1, 128, 128, 64, 1) == carry(1, 128, 128)
+    assert lib.kda_chunk_fwd_workspace(0, 64, 1, 128, 128, 64, 1) == 0
+    assert lib.kda_chunk_fwd_kernel_count(4, 4096, 16, 128, 128, 64, 1) % 2 == 0
+    assert lib.kda_chunk_fwd_kernel_count(1, 0, 1, 128, 128, 64, 1) == 1
     assert lib.kda_chunk_fwd_workspace(1, 64, 1, 96, 128, 64, 1) == 0
     assert lib.kda_chunk_fwd_workspace(1, 64, 1, 128, 128, 48, 1) == 0
     # chunk 0 selects 64

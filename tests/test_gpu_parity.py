@@ -312,3 +312,21 @@ def test_long_workload_segmented():
     for h in (0, 31):
         o_ref, _ = oracle_forward(inp, heads=[h], T=2048)
         assert_close(o_full[:, :2048, h:h + 1], o_ref, BF16, f"long prefix h{h}")
+
+
+def test_sliced_sequence_matches_oracle():
+    """Enough heads that the sequence is cut into slices: the state and
+    transition carried between slices must match the oracle."""
+    B, T, H, Dk, Dv = 1, 130, 8192, 128, 128
+    assert kda.kernel_count(B, T, H, Dk, Dv, 64, BF16) == 6   # 3 slices x (intra, inter)
+    inp = inputs.make_inputs(B, T, H, Dk, Dv, "bf16", seed=31, a_std=0.5, s_std=0.2)
+    o, S, M, P = run_chunk(inp, chunk=64, want_M=True, want_P=True)
+    for b, h in ((0, 0), (0, 8191)):
+        sub = {k_: (v_[b:b + 1] if v_ is not None and k_ != "A_log" else v_) for k_, v_ in inp.items()}
+        o_ref, S_ref = oracle_forward(sub, heads=[h])
+        assert_close(o[b:b + 1, :, h:h + 1], o_ref, BF16, f"sliced o b{b} h{h}")
+        assert_close(S[b:b + 1, h:h + 1], S_ref, BF16, f"sliced S b{b} h{h}")
+        qh, kh, g, beta = ora.prepare(*(np64(sub[n][:, :, [h]]) for n in ("q", "k", "z", "beta_raw")),
+                                      np64(inp["A_log"])[[h]])
+        M_ref, _ = ora.segment_fragment(kh, np64(sub["v"][:, :, [h]]), g, beta)
+        assert_close(M[b:b + 1, h:h + 1], M_ref, BF16, f"sliced M b{b} h{h}")
