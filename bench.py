@@ -59,10 +59,15 @@ def chunk_bytes(B, T, H, Dk, Dv, esize=2):
 
 
 def kernel_bytes(B, T, H, Dk, Dv, C, ws_bytes, esize=2):
-    """Algorithmic bytes per launch of each kernel: what it must read and write."""
+    """Algorithmic bytes per launch of each kernel, every byte touched once:
+    intra reads q, k, z, beta_raw and A_log and writes the per-chunk blocks;
+    inter reads the blocks and v and writes o and the final state.  The fp32
+    carry region at the end of the workspace is used only when the sequence is
+    cut into slices, so it is not counted."""
     rows = B * T * H
-    intra = rows * (3 * Dk + 1) * esize + H * 4 + ws_bytes
-    inter = ws_bytes + rows * Dv * esize + rows * Dv * esize + B * H * Dk * Dv * 4
+    blocks = ws_bytes - B * H * Dk * (Dk + Dv) * 4
+    intra = rows * (3 * Dk + 1) * esize + H * 4 + blocks
+    inter = blocks + rows * Dv * esize + rows * Dv * esize + B * H * Dk * Dv * 4
     return {"kda_intra": intra, "kda_inter": inter}
 
 

@@ -6,7 +6,6 @@
 #include <math.h>
 #include <stdint.h>
 
-#include <atomic>
 
 #include "../../include/kda.h"
 #include "kda_internal.h"
@@ -40,29 +39,6 @@ kda_status maybe(const void* p) { return (!p || aligned16(p)) ? KDA_OK : KDA_ERR
     } while (0)
 
 }  // namespace
-
-namespace kda {
-
-int occupancy_blocks(const void* kernel, int block_threads) {
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, block_threads, 0) != hipSuccess) return 1;
-    return nb > 0 ? nb : 1;
-}
-
-int device_cu_count() {
-    constexpr int kMaxDev = 64;
-    static std::atomic<int> cache[kMaxDev];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) dev = 0;
-    int v = cache[dev].load(std::memory_order_relaxed);
-    if (v <= 0) {
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-        cache[dev].store(v, std::memory_order_relaxed);
-    }
-    return v;
-}
-
-}  // namespace kda
 
 extern "C" {
 

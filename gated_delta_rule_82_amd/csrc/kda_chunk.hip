@@ -682,7 +682,8 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t stream, hipEven
     const int BH = a.B * a.H;
     auto kern = kda_inter_kernel<T, DK, C, NW>;
     constexpr size_t lds = (2 * L.bytes <= kLdsBudget) ? 2 * L.bytes : L.bytes;
-    static const hipError_t attr = hipFuncSetAttribute(
+    // set on every call: the attribute is per device, and the call only records a limit
+    const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
 

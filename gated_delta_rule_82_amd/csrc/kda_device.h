@@ -61,27 +61,6 @@ template <> struct RawBits<float> {
     static __device__ __forceinline__ float to_float(uint32_t x) { return __uint_as_float(x); }
 };
 
-// Four consecutive input elements kept as raw bits until converted (lets a
-// load be issued long before its data is needed).
-template <typename T> struct Raw4;
-template <> struct Raw4<bf16_t> {
-    uint2 v;
-    __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
-    __device__ __forceinline__ void to_float(float out[4], bool ok) const {
-        out[0] = ok ? bf16_bits_to_float(v.x & 0xffffu) : 0.f;
-        out[1] = ok ? bf16_bits_to_float(v.x >> 16) : 0.f;
-        out[2] = ok ? bf16_bits_to_float(v.y & 0xffffu) : 0.f;
-        out[3] = ok ? bf16_bits_to_float(v.y >> 16) : 0.f;
-    }
-};
-template <> struct Raw4<float> {
-    float4 v;
-    __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
-    __device__ __forceinline__ void to_float(float out[4], bool ok) const {
-        out[0] = ok ? v.x : 0.f; out[1] = ok ? v.y : 0.f; out[2] = ok ? v.z : 0.f; out[3] = ok ? v.w : 0.f;
-    }
-};
-
 // Load 4 consecutive elements (8-byte aligned for bf16, 16-byte for fp32).
 __device__ __forceinline__ void load4(const float* p, float out[4]) {
     float4 v = *reinterpret_cast<const float4*>(p);

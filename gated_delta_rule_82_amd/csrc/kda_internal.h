@@ -77,8 +77,6 @@ struct FixupArgs {
 
 // Resident workgroups per CU for a kernel at this block size, and the CU
 // count of the current device (queried once and cached).
-int occupancy_blocks(const void* kernel, int block_threads);
-int device_cu_count();
 
 // dt: 0 = fp32, 1 = bf16.  Return the launch status (hipSuccess on success).
 hipError_t launch_step(int dt, int DK, int DV, const StepArgs& a, hipStream_t s);
