@@ -83,7 +83,10 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     const int I = w;
     const int t = n * C + 16 * I + r;
     const bool valid = active && t < a.T;
-    const size_t row = ((size_t)b * a.T + t) * a.H + h;
+    // tokens past the end read the last token (finite values); they are made
+    // identity transitions below (g = 0, beta = 0), so what they hold never
+    // reaches an output
+    const size_t row = ((size_t)b * a.T + (t < a.T ? t : a.T - 1)) * a.H + h;
 
     T* ws = reinterpret_cast<T*>(a.ws) + (size_t)cid * (L.bytes / sizeof(T));
     float* ws_gamma = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(ws) + L.gamma_byte);
@@ -92,45 +95,62 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     // Lane (r, gq) of wave I owns token 16 I + r and the channels of its
     // fragment slots; loads, norms, gate and the block-local scan are all
     // wave-local.
-    float qv[NV], kv[NV], gv[NV];
+    Raw4<T> qr[2 * KSD], kr[2 * KSD];  // q, k as loaded; slot j of step s is element j % 4 of [2 s + j / 4]
+    float gv[NV];
     float beta = 0.f;
 #pragma unroll
     for (int s = 0; s < KSD; ++s) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const int c = 32 * s + 16 * hf + 4 * gq;
-            float* dq = &qv[8 * s + 4 * hf];
-            float* dk = &kv[8 * s + 4 * hf];
             float* dz = &gv[8 * s + 4 * hf];
-            if (valid && (DK >= 32 || hf == 0)) {
-                load4(reinterpret_cast<const T*>(a.q) + row * DK + c, dq);
-                load4(reinterpret_cast<const T*>(a.k) + row * DK + c, dk);
+            if (active && (DK >= 32 || hf == 0)) {
+                qr[2 * s + hf].load(reinterpret_cast<const T*>(a.q) + row * DK + c);
+                kr[2 * s + hf].load(reinterpret_cast<const T*>(a.k) + row * DK + c);
                 load4(reinterpret_cast<const T*>(a.z) + row * DK + c, dz);
             } else {
+                qr[2 * s + hf].zero();
+                kr[2 * s + hf].zero();
 #pragma unroll
-                for (int i = 0; i < 4; ++i) { dq[i] = 0.f; dk[i] = 0.f; dz[i] = 0.f; }
+                for (int i = 0; i < 4; ++i) dz[i] = 0.f;
             }
         }
     }
-    if (valid) {
+    {
         const float braw = to_f<T>(reinterpret_cast<const T*>(a.beta_raw)[row]);
         beta = (a.flags & kBetaSig) ? sigmoidf_(braw) : braw;
+        beta = valid ? beta : 0.f;
     }
     float sq = 0.f, sk = 0.f;
 #pragma unroll
-    for (int v = 0; v < NV; ++v) { sq += qv[v] * qv[v]; sk += kv[v] * kv[v]; }
+    for (int v = 0; v < NV; ++v) {
+        const float x = qr[v / 4].get(v % 4), y = kr[v / 4].get(v % 4);
+        sq += x * x;
+        sk += y * y;
+    }
     sq = group_sum4(sq);
     sk = group_sum4(sk);
-    const float rq = (a.flags & kQkL2) ? 1.0f / sqrtf(sq + kL2Eps) : 1.0f;
-    const float rk = (a.flags & kQkL2) ? 1.0f / sqrtf(sk + kL2Eps) : 1.0f;
-    const bool gate = (a.flags & kGateIn) != 0;
-    const float zscale = gate ? -expf(a.A_log[h]) * kLog2e : 0.f;  // exp2(zscale z) = e^{-e^A z}
-    const float gm2 = a.g_min * kLog2e;
+    const float rq = (a.flags & kQkL2) ? __builtin_amdgcn_rsqf(sq + kL2Eps) : 1.0f;
+    const float rk = (a.flags & kQkL2) ? __builtin_amdgcn_rsqf(sk + kL2Eps) : 1.0f;
+    // log2-decay per element; padding tokens are identity transitions (g = 0, beta = 0)
+    if (a.flags & kGateIn) {
+        const float zscale = -expf(a.A_log[h]) * kLog2e;  // exp2(zscale z) = e^{-e^A z}
+        const float gm2 = a.g_min * kLog2e;
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        float g2 = 0.f;  // padding tokens are identity transitions (g = 0, beta = 0)
-        if (valid) g2 = gate ? gm2 * __builtin_amdgcn_rcpf(1.0f + exp2_fast(zscale * gv[v])) : gv[v] * kLog2e;
-        gv[v] = row_scan16(g2);  // block-local inclusive cumulative log2-decay L
+        for (int v = 0; v < NV; ++v) {
+            const float g2 = gm2 * __builtin_amdgcn_rcpf(1.0f + exp2_fast(zscale * gv[v]));
+            gv[v] = valid ? g2 : 0.f;
+        }
+    } else {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) gv[v] = valid ? gv[v] * kLog2e : 0.f;
+    }
+    // block-local inclusive cumulative log2-decay L, one scan round over all
+    // elements at a time so consecutive DPP operations are independent
+#pragma unroll
+    for (int sh = 0; sh < 4; ++sh) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) gv[v] += row_shift_add(gv[v], sh);
     }
     if (active) {
         if (r == 15) {
@@ -179,7 +199,8 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     // ------------------------------------------------------------ phase C
     // Row operands (q, k scaled by exp(L)), diagonal column operand
     // (k scaled by exp(-L)), the chunk operands Kd, Qp, and K' for KpT.
-    Frag<T> rkf[KSD], rqf[KSD], cdf[KSD];
+    Frag<T> rkf[KSD], rqf[KSD];
+    floatx4 akkR = {0.f, 0.f, 0.f, 0.f}, aqkR = akkR, akkC = akkR;  // diagonal block products
     if (active) {
 #pragma unroll
         for (int s = 0; s < KSD; ++s) {
@@ -199,27 +220,30 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
                     for (int i = 0; i < 4; ++i) { eE[4 * hf + i] = 0.f; eLl[4 * hf + i] = 0.f; eK[4 * hf + i] = 0.f; }
                 }
             }
-            Frag<T> kd, qp, ob, kp;
+            Frag<T> kd, qp, ob, kp, cdf;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int v = 8 * s + j;
                 const float Lv = gv[v];
                 const float e1 = exp2_fast(Lv);
                 const float einv = exp2_fast(-Lv);
-                const float qh = qv[v] * rq;
-                const float kh = kv[v] * rk;
+                const float qh = qr[v / 4].get(v % 4) * rq;
+                const float kh = kr[v / 4].get(v % 4) * rk;
                 const float rsq = qh * e1;
                 const float rsk = kh * e1;
                 const float cdg = kh * einv;
                 const float offv = cdg * eLl[j];   // k exp(Ll - L): decay from the token to its block end
                 rqf[s].set(j, rsq);
                 rkf[s].set(j, rsk);
-                cdf[s].set(j, cdg);
+                cdf.set(j, cdg);
                 kd.set(j, rsk * eE[j]);
                 qp.set(j, rsq * eE[j]);
                 ob.set(j, offv);
                 kp.set(j, offv * eK[j]);
             }
+            akkR = mma(cdf, rkf[s], akkR);   // R layout: row r, col 4gq+i
+            aqkR = mma(cdf, rqf[s], aqkR);
+            akkC = mma(rkf[s], cdf, akkC);   // C layout: row 4gq+i, col r
             frag_store(kd, ws + L.kd + (size_t)(I * KSD + s) * 512, lane);
             frag_store(qp, ws + L.qp + (size_t)(I * KSD + s) * 512, lane);
             if (NBK > 1 && I < NBK - 1) frag_store(ob, &s_offb[I < NOFF ? I : 0][s][0], lane);
@@ -244,6 +268,8 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
                     }
                 }
             }
+            // keep each step's table reads next to their use (bounds live registers)
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     lds_barrier();
@@ -251,13 +277,6 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     // ------------------------------------------------------------ phase D
     floatx4 TdC = {0.f, 0.f, 0.f, 0.f}, TdR = {0.f, 0.f, 0.f, 0.f};
     if (active) {
-        floatx4 akkR = {0.f, 0.f, 0.f, 0.f}, aqkR = akkR, akkC = akkR;
-#pragma unroll
-        for (int s = 0; s < KSD; ++s) {
-            akkR = mma(cdf[s], rkf[s], akkR);   // R layout: row r, col 4gq+i
-            aqkR = mma(cdf[s], rqf[s], aqkR);
-            akkC = mma(rkf[s], cdf[s], akkC);   // C layout: row 4gq+i, col r
-        }
         const float4 bcol = *reinterpret_cast<const float4*>(&s_beta[16 * I + 4 * gq]);
         const float bc[4] = {bcol.x, bcol.y, bcol.z, bcol.w};
         float aq[4];
@@ -286,22 +305,17 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
                     Frag<T> cof;
                     frag_load(cof, &s_offb[J][s][0], lane);
                     if (J + 1 < I) {
-                        // rows rescaled by the decay between the blocks (<= 1)
-                        const float* pr = &s_pair[pair_index(I, J)][0];
-                        Frag<T> rk2, rq2;
+                        // columns rescaled by the decay between the blocks (<= 1)
+                        const float* pr = &s_pair[pair_index(I, J)][32 * s];
+                        const float4 p0 = *reinterpret_cast<const float4*>(pr + 4 * gq);
+                        const float4 p1 = DK >= 32 ? *reinterpret_cast<const float4*>(pr + 16 + 4 * gq)
+                                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+                        const float sc[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            const int c = 32 * s + slot_index(gq, j);
-                            const float sc = (c < DK) ? pr[c] : 0.f;
-                            rk2.set(j, rkf[s].get(j) * sc);
-                            rq2.set(j, rqf[s].get(j) * sc);
-                        }
-                        ak = mma(cof, rk2, ak);
-                        aqo = mma(cof, rq2, aqo);
-                    } else {
-                        ak = mma(cof, rkf[s], ak);
-                        aqo = mma(cof, rqf[s], aqo);
+                        for (int j = 0; j < 8; ++j) cof.set(j, cof.get(j) * sc[j]);
                     }
+                    ak = mma(cof, rkf[s], ak);
+                    aqo = mma(cof, rqf[s], aqo);
                 }
                 float aqv[4];
 #pragma unroll

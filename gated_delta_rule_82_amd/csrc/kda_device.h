@@ -61,6 +61,25 @@ template <> struct RawBits<float> {
     static __device__ __forceinline__ float to_float(uint32_t x) { return __uint_as_float(x); }
 };
 
+// Four consecutive elements kept as loaded (bf16: two packed registers) and
+// widened to float where used, so they occupy half the registers until then.
+template <typename T> struct Raw4;
+template <> struct Raw4<bf16_t> {
+    uint2 v;
+    __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
+    __device__ __forceinline__ void zero() { v = make_uint2(0u, 0u); }
+    __device__ __forceinline__ float get(int i) const {
+        const uint32_t w = i < 2 ? v.x : v.y;
+        return (i & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+    }
+};
+template <> struct Raw4<float> {
+    float4 v;
+    __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
+    __device__ __forceinline__ void zero() { v = make_float4(0.f, 0.f, 0.f, 0.f); }
+    __device__ __forceinline__ float get(int i) const { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
+};
+
 // Load 4 consecutive elements (8-byte aligned for bf16, 16-byte for fp32).
 __device__ __forceinline__ void load4(const float* p, float out[4]) {
     float4 v = *reinterpret_cast<const float4*>(p);
@@ -169,13 +188,16 @@ __device__ __forceinline__ floatx4 mm16(const floatx4& a, const floatx4& b) {
 
 // ---------------------------------------------------------------- lane ops
 
-// Inclusive prefix sum over the 16 lanes of each DPP row (lane % 16 order).
-__device__ __forceinline__ float row_scan16(float x) {
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, true));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, true));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, true));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, true));
-    return x;
+// One round of an inclusive prefix sum over the 16 lanes of each DPP row:
+// x shifted down the row by 2^sh lanes (zero where it runs off the row).
+__device__ __forceinline__ float row_shift_add(float x, int sh) {
+    const int v = __float_as_int(x);
+    switch (sh) {
+        case 0: return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true));
+        case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true));
+        case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true));
+        default: return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true));
+    }
 }
 
 // Sum over the four lane groups that share lane % 16.
