@@ -141,10 +141,11 @@ def cpu_baseline(inp, T_sample):
 
 # ------------------------------------------------------------------ GPU legs
 
-def bench_layer(torch, kda, inputs, steps, warmup):
+def bench_layer(torch, kda, inputs, steps, warmup, chunk=None):
     w = inputs.WORKLOADS["layer"]
     dev = torch.device("cuda:0")
-    B, T, H, Dk, Dv, C = w.B, w.T, w.H, w.Dk, w.Dv, w.chunk
+    B, T, H, Dk, Dv = w.B, w.T, w.H, w.Dk, w.Dv
+    C = chunk or w.chunk
     base = inputs.make_workload(w)
     sets = [{n: base[n].to(dev) for n in ("q", "k", "v", "z", "beta_raw")}]
     gen = torch.Generator(device=dev)
@@ -274,6 +275,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--long-reps", type=int, default=3)
     ap.add_argument("--only-layer", action="store_true", help="time the layer workload only")
+    ap.add_argument("--chunk", type=int, default=0, help="state chunk length (0: the workload's own)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run 3 device copies of 1 GiB (a counter reference of known size)")
     args = ap.parse_args()
@@ -311,7 +313,7 @@ def main():
         log("[bench] copy calibration: 3 x 1 GiB device copies done")
 
     log("[bench] layer workload ...")
-    L = bench_layer(torch, kda, inputs, args.steps, args.warmup)
+    L = bench_layer(torch, kda, inputs, args.steps, args.warmup, args.chunk or None)
     B, T, H, Dk, Dv, C = L["B"], L["T"], L["H"], L["Dk"], L["Dv"], L["C"]
     ms = L["ms_per_step"]
     tok_s = B * T / (ms / 1e3)
@@ -346,7 +348,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) inputs, A_log ~ N(0,0.5); 4 rotating input sets in HBM)",
-        "config": {"workload": "layer: chunk_kda fwd B4 T4096 H16 Dk=Dv=128 chunk64, bf16 in, fp32 state",
+        "config": {"workload": f"layer: chunk_kda fwd B4 T4096 H16 Dk=Dv=128 chunk{C}, bf16 in, fp32 state",
                    "B": B, "T": T, "H": H, "Dk": Dk, "Dv": Dv, "chunk": C, "g_min": -5.0},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

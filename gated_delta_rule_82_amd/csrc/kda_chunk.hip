@@ -57,30 +57,49 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     constexpr int NV = KSD * 8;
     constexpr int NOFF = NBK > 1 ? NBK - 1 : 1;
     constexpr int NPAIR = NBK > 1 ? NBK * (NBK - 1) / 2 : 1;
+    constexpr int KSO = NBK > 1 ? KSD : 1;
+    constexpr int NCH = 64 / C;  // chunks per workgroup: four waves of 16-token blocks
 
-    __shared__ __align__(16) float s_tot[NBK][DK];    // block totals of the log2 decay
-    __shared__ __align__(16) float s_eE[NBK][DK];     // exp2(E_I): chunk start to block entry
-    __shared__ __align__(16) float s_eLl[NBK][DK];    // exp2(Ll_I): decay over block I
-    __shared__ __align__(16) float s_eK[NBK][DK];     // exp2(G_C - E_I - Ll_I): block end to chunk end
-    __shared__ __align__(16) float s_pair[NPAIR][DK]; // exp2(E_I - E_{J+1}) <= 1 for J < I - 1
-    __shared__ float s_beta[C];
-    __shared__ __align__(16) T s_offb[NOFF][KSD][512];  // column operands of off-diagonal blocks
-    __shared__ __align__(16) float s_akk[NPAIR][256];   // R layout of A_kk[I][J], J < I
-    __shared__ __align__(16) float s_tdiag[NBK][256];   // R layout of (I + A_kk[I][I])^-1
+    // per chunk of the workgroup:
+    __shared__ __align__(16) float s_tot_all[NCH][NBK][DK];     // block totals of the log2 decay
+    __shared__ __align__(16) float s_eE_all[NCH][NBK][DK];      // exp2(E_I): chunk start to block entry
+    __shared__ __align__(16) float s_eLl_all[NCH][NBK][DK];     // exp2(Ll_I): decay over block I
+    __shared__ __align__(16) float s_eK_all[NCH][NBK][DK];      // exp2(G_C - E_I - Ll_I): block end to chunk end
+    __shared__ __align__(16) float s_pair_all[NCH][NPAIR][DK];  // exp2(E_I - E_{J+1}) <= 1 for J < I - 1
+    __shared__ float s_beta_all[NCH][C];
+    __shared__ __align__(16) T s_offb_all[NCH][NOFF][KSO][512];  // column operands of off-diagonal blocks
+    __shared__ __align__(16) float s_akk_all[NCH][NPAIR][256];   // R layout of A_kk[I][J], J < I
+    __shared__ __align__(16) float s_tdiag_all[NCH][NBK][256];   // R layout of (I + A_kk[I][I])^-1
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15;
     const int gq = lane >> 4;
 
-    const int n = a.c0 + (int)blockIdx.x % a.nc;
-    const int bh = (int)blockIdx.x / a.nc;
+    // workgroup: chunks [c0 + NCH g, c0 + NCH g + nsub) of (b, h); wave w owns
+    // 16-token block I of chunk sub
+    const int ncg = (a.nc + NCH - 1) / NCH;
+    const int g = (int)blockIdx.x % ncg;
+    const int bh = (int)blockIdx.x / ncg;
+    const int nsub = min(NCH, a.nc - g * NCH);
+    const int sub = w / NBK;
+    const int I = w % NBK;
+    const int n = a.c0 + g * NCH + sub;
     const int cid = bh * a.NC + n;     // workspace block of (b, h, chunk n)
     const int h = bh % a.H;
     const int b = bh / a.H;
 
-    const bool active = w < NBK;
-    const int I = w;
+    float (&s_tot)[NBK][DK] = s_tot_all[sub];
+    float (&s_eE)[NBK][DK] = s_eE_all[sub];
+    float (&s_eLl)[NBK][DK] = s_eLl_all[sub];
+    float (&s_eK)[NBK][DK] = s_eK_all[sub];
+    float (&s_pair)[NPAIR][DK] = s_pair_all[sub];
+    float (&s_beta)[C] = s_beta_all[sub];
+    T (&s_offb)[NOFF][KSO][512] = s_offb_all[sub];
+    float (&s_akk)[NPAIR][256] = s_akk_all[sub];
+    float (&s_tdiag)[NBK][256] = s_tdiag_all[sub];
+
+    const bool active = sub < nsub;  // wave-uniform
     const int t = n * C + 16 * I + r;
     const bool valid = active && t < a.T;
     // tokens past the end read the last token (finite values); they are made
@@ -88,8 +107,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     // reaches an output
     const size_t row = ((size_t)b * a.T + (t < a.T ? t : a.T - 1)) * a.H + h;
 
-    T* ws = reinterpret_cast<T*>(a.ws) + (size_t)cid * (L.bytes / sizeof(T));
-    float* ws_gamma = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(ws) + L.gamma_byte);
+    T* ws = reinterpret_cast<T*>(a.ws) + (size_t)(active ? cid : 0) * (L.bytes / sizeof(T));
 
     // ------------------------------------------------------------ phase A
     // Lane (r, gq) of wave I owns token 16 I + r and the channels of its
@@ -169,30 +187,35 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
 
     // ------------------------------------------------------------ phase B
     // Per (block, channel) decay factors, each computed once.
-    for (int e = threadIdx.x; e < NBK * DK; e += 256) {
-        const int Ib = e / DK, c = e % DK;
+    for (int e = threadIdx.x; e < NCH * NBK * DK; e += 256) {
+        const int sb = e / (NBK * DK), Ib = (e / DK) % NBK, c = e % DK;
+        if (sb >= nsub) continue;
         float E = 0.f, GC = 0.f;
 #pragma unroll
         for (int J = 0; J < NBK; ++J) {
-            const float x = s_tot[J][c];
+            const float x = s_tot_all[sb][J][c];
             if (J < Ib) E += x;
             GC += x;
         }
-        const float Ll = s_tot[Ib][c];
-        s_eE[Ib][c] = exp2_fast(E);
-        s_eLl[Ib][c] = exp2_fast(Ll);
-        s_eK[Ib][c] = exp2_fast(GC - E - Ll);
+        const float Ll = s_tot_all[sb][Ib][c];
+        s_eE_all[sb][Ib][c] = exp2_fast(E);
+        s_eLl_all[sb][Ib][c] = exp2_fast(Ll);
+        s_eK_all[sb][Ib][c] = exp2_fast(GC - E - Ll);
 #pragma unroll
         for (int J = 0; J + 1 < NBK; ++J) {
             if (J + 1 < Ib) {
                 float gap = 0.f;  // <= 0: decay between the end of block J and the entry of block Ib
 #pragma unroll
                 for (int K = 0; K < NBK; ++K)
-                    if (K > J && K < Ib) gap += s_tot[K][c];
-                s_pair[pair_index(Ib, J)][c] = exp2_fast(gap);
+                    if (K > J && K < Ib) gap += s_tot_all[sb][K][c];
+                s_pair_all[sb][pair_index(Ib, J)][c] = exp2_fast(gap);
             }
         }
-        if (Ib == 0) ws_gamma[c] = exp2_fast(GC);
+        if (Ib == 0) {
+            const size_t cb = (size_t)bh * a.NC + a.c0 + g * NCH + sb;  // workspace block of that chunk
+            float* gam = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(a.ws) + cb * L.bytes + L.gamma_byte);
+            gam[c] = exp2_fast(GC);
+        }
     }
     lds_barrier();
 
@@ -246,7 +269,9 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
             akkC = mma(rkf[s], cdf, akkC);   // C layout: row 4gq+i, col r
             frag_store(kd, ws + L.kd + (size_t)(I * KSD + s) * 512, lane);
             frag_store(qp, ws + L.qp + (size_t)(I * KSD + s) * 512, lane);
-            if (NBK > 1 && I < NBK - 1) frag_store(ob, &s_offb[I < NOFF ? I : 0][s][0], lane);
+            if constexpr (NBK > 1) {
+                if (I < NBK - 1) frag_store(ob, &s_offb[I < NOFF ? I : 0][s][0], lane);
+            }
             // KpT tiles by an exact identity product: mma(K' rows, E_R) is the
             // C-layout tile (tokens of block I) x (channels of block R), i.e. one
             // half of the A fragment of KpT for channel block R.
@@ -344,7 +369,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     // Wave J builds block column J of T = (I + A_kk)^-1:
     //   T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ,  then writes R(T_IJ) Diag(beta).
     if (active) {
-        const int J = w;
+        const int J = I;
         const float4 bj = *reinterpret_cast<const float4*>(&s_beta[16 * J + 4 * gq]);
         auto write_tb = [&](int Ir, const floatx4& TR) {
             const float x[4] = {TR[0] * bj.x, TR[1] * bj.y, TR[2] * bj.z, TR[3] * bj.w};
@@ -392,34 +417,62 @@ struct InterArgs {
 
 constexpr size_t kLdsBudget = 160 * 1024;  // LDS per CU on gfx950
 
-// Asynchronous copy of one contiguous block into LDS by a single wave
-// (global_load_lds: 16 bytes per lane, 1 KiB per instruction).
-__device__ __forceinline__ void wave_copy_to_lds(const unsigned char* src, unsigned char* dst, int bytes,
-                                                 int lane) {
-    for (int off = 0; off < bytes; off += 1024) {
-        if (off + lane * 16 < bytes)
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void*)(src + off + lane * 16),
-                (__attribute__((address_space(3))) void*)(dst + off), 16, 0, 0);
+// LDS ring of the inter-chunk kernel.  A slot holds one chunk block followed by
+// the chunk's values for the workgroup's NS = 16-column strips
+// ([C tokens][16 NS]).  Two copy waves fill the slots with global_load_lds,
+// 1 KiB per instruction ("piece"); copy wave c issues the pieces p with
+// p % 2 == c.
+template <typename T, int DK, int C, int NS>
+struct InterRing {
+    static constexpr BlockLayout L = block_layout(sizeof(T), DK, C);
+    static constexpr int kVRow = 16 * NS * (int)sizeof(T);   // bytes of one token's staged values
+    static constexpr size_t kVBytes = round_up((size_t)C * kVRow, 1024);
+    static constexpr size_t kSlot = L.bytes + kVBytes;
+    static constexpr int kSlots = kLdsBudget / kSlot >= 4 ? 4 : (int)(kLdsBudget / kSlot);
+    static constexpr int kBlkPieces = (int)((L.bytes + 1023) / 1024);
+    static constexpr int kVPieces = (int)(kVBytes / 1024);
+    static constexpr int kPieces = kBlkPieces + kVPieces;
+    static constexpr int kPer0 = (kPieces + 1) / 2;  // pieces per chunk of copy wave 0
+    static constexpr int kPer1 = kPieces / 2;        // ... and of copy wave 1
+    static_assert(kSlots >= 1, "a chunk block must fit in LDS");
+    static_assert(kSlots <= 2 || (kSlots - 2) * kPer0 < 64, "vmcnt range");
+    static_assert(kVRow % 16 == 0 && 1024 % kVRow == 0, "value rows tile a piece");
+};
+
+// Wait until at most m chunks of this copy wave's pieces (P per chunk) are in
+// flight; loads complete in issue order.
+template <int P, int MAXM>
+__device__ __forceinline__ void wait_chunks(int m) {
+    if constexpr (MAXM >= 2) {
+        if (m >= 2) { wait_vmcnt<2 * P>(); return; }
     }
+    if constexpr (MAXM >= 1) {
+        if (m >= 1) { wait_vmcnt<P>(); return; }
+    }
+    wait_vmcnt<0>();
 }
 
-// Inter-chunk kernel.  A workgroup serves NW 16-column strips of one (b, h)
-// with NW compute waves plus one copy wave:
-//   * the copy wave streams the next chunk block into the spare LDS buffer,
-//     waiting only on its own loads;
-//   * the compute waves hold their strip of S in fp32 registers, read operands
-//     from LDS and V/o from global memory, and never wait on the copy.
-// One fence-free barrier per chunk hands the buffers over.
-template <typename T, int DK, int C, int NW>
-__global__ __launch_bounds__(64 * (NW + 1)) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// Inter-chunk kernel.  A workgroup serves NS = NW * SPW 16-column strips of one
+// (b, h) with NW compute waves of SPW strips each, plus two copy waves:
+//   * the copy waves keep up to kSlots - 1 chunks ahead in the LDS ring
+//     (block and values), waiting only on their own loads;
+//   * a compute wave holds its strips of S in fp32 registers, reads every
+//     operand fragment from LDS once for all its strips, stores o directly,
+//     and never waits on global loads.
+// One fence-free barrier per chunk hands a slot over.
+template <typename T, int DK, int C, int NW, int SPW>
+__global__ __launch_bounds__(64 * (NW + 2)) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void kda_inter_kernel(const InterArgs a) {
-    constexpr BlockLayout L = block_layout(sizeof(T), DK, C);
+    constexpr int NS = NW * SPW;
+    using Ring = InterRing<T, DK, C, NS>;
+    constexpr BlockLayout L = Ring::L;
+    constexpr int K = Ring::kSlots;
+    constexpr bool kAhead = K >= 3;  // next chunk's operands are read during the current one
+    constexpr bool kPinOrder = C <= 32 && sizeof(T) == 2;
     constexpr int NBK = C / 16;
     constexpr int KSD = (DK + 31) / 32;
     constexpr int NBD = DK / 16;
     constexpr int KSC = (C + 31) / 32;
-    constexpr bool kDouble = 2 * L.bytes <= kLdsBudget;  // double-buffer the chunk blocks
     extern __shared__ __align__(16) unsigned char s_raw[];
 
     const int lane = threadIdx.x & 63;
@@ -432,176 +485,181 @@ void kda_inter_kernel(const InterArgs a) {
     const int bh = bid / a.n_groups;
     const int h = bh % a.H;
     const int b = bh / a.H;
-    const unsigned char* gblk = reinterpret_cast<const unsigned char*>(a.ws) + (size_t)bh * a.NC * L.bytes;
+    const int cend = a.c0 + a.nc;
+    // value columns staged for this workgroup: strips [vs0, vs1) of the value part
+    const int vs0 = max(0, grp * NS - a.n_m);
+    const int vs1 = min(a.Dv / 16, grp * NS + NS - a.n_m);
+    const int vcol0 = 16 * vs0;
+    auto slot_of = [&](int n) -> unsigned char* { return s_raw + (size_t)((n - a.c0) % K) * Ring::kSlot; };
 
-    if (w == NW) {
-        // ------------------------------------------------------ copy wave
-        const int cend = a.c0 + a.nc;
-        if (a.nc > 0) {
-            wave_copy_to_lds(gblk + (size_t)a.c0 * L.bytes, s_raw, (int)L.bytes, lane);
-            wait_vmcnt<0>();
-        }
-        lds_barrier();  // the first block is in LDS
-        for (int n = a.c0; n < cend; ++n) {
-            if (!kDouble) lds_barrier();  // compute waves are done with the single buffer
-            if (n + 1 < cend) {
-                wave_copy_to_lds(gblk + (size_t)(n + 1) * L.bytes,
-                                 s_raw + (kDouble ? (size_t)((n + 1 - a.c0) & 1) * L.bytes : 0), (int)L.bytes, lane);
-                wait_vmcnt<0>();  // block n + 1 is in LDS
+    if (w >= NW) {
+        // ------------------------------------------------------ copy waves
+        const int cw = w - NW;
+        const unsigned char* gblk = reinterpret_cast<const unsigned char*>(a.ws) + (size_t)bh * a.NC * L.bytes;
+        const unsigned char* vsrc = reinterpret_cast<const unsigned char*>(a.v);
+        constexpr int kLanesPerRow = Ring::kVRow / 16;
+        constexpr int kTokPerPiece = 64 / kLanesPerRow;
+        const int vcol = vcol0 + (lane % kLanesPerRow) * (16 / (int)sizeof(T));
+        const int vcol_ld = vcol < 16 * vs1 ? vcol : 0;  // columns outside the range load any valid bytes
+        auto issue = [&](int n) {
+            unsigned char* slot = slot_of(n);
+            const unsigned char* gb = gblk + (size_t)n * L.bytes;
+#pragma unroll
+            for (int p = 0; p < Ring::kPieces; ++p) {
+                if (p % 2 != cw) continue;
+                if (p < Ring::kBlkPieces) {
+                    const int off = p * 1024 + lane * 16;
+                    if (off < (int)L.bytes)
+                        __builtin_amdgcn_global_load_lds(
+                            (const __attribute__((address_space(1))) void*)(gb + off),
+                            (__attribute__((address_space(3))) void*)(slot + p * 1024), 16, 0, 0);
+                } else {
+                    const int j = p - Ring::kBlkPieces;
+                    int tok = n * C + j * kTokPerPiece + lane / kLanesPerRow;
+                    tok = tok < a.T ? tok : a.T - 1;  // rows past the end are zeroed by the compute waves
+                    const size_t e = (((size_t)b * a.T + tok) * a.H + h) * a.Dv + vcol_ld;
+                    __builtin_amdgcn_global_load_lds(
+                        (const __attribute__((address_space(1))) void*)(vsrc + e * sizeof(T)),
+                        (__attribute__((address_space(3))) void*)(slot + L.bytes + j * 1024), 16, 0, 0);
+                }
             }
-            lds_barrier();
+        };
+        auto wait_for = [&](int m) {  // at most m chunks of this wave still in flight
+            if (cw == 0) wait_chunks<Ring::kPer0, (K >= 2 ? K - 2 : 0)>(m);
+            else wait_chunks<Ring::kPer1, (K >= 2 ? K - 2 : 0)>(m);
+        };
+        if (K == 1) {
+            if (a.nc > 0) { issue(a.c0); wait_for(0); }
+            lds_barrier();  // chunk c0 is in LDS
+            for (int n = a.c0; n < cend; ++n) {
+                lds_barrier();  // the compute waves are done with the slot
+                if (n + 1 < cend) { issue(n + 1); wait_for(0); }
+                lds_barrier();
+            }
+        } else {
+            // kAhead: chunks n + 1 and n + 2 are in LDS at the barrier ending
+            // chunk n (the compute waves read chunk n + 1's operands early);
+            // otherwise chunk n + 1.
+            constexpr int D = kAhead ? 2 : 1;
+            int nis = a.c0;  // next chunk to issue
+            for (; nis < cend && nis < a.c0 + K - 1; ++nis) issue(nis);
+            if (a.nc > 0) wait_for(max(0, nis - a.c0 - D));
+            lds_barrier();  // chunks c0 .. c0 + D - 1 are in LDS
+            for (int n = a.c0; n < cend; ++n) {
+                // the slot of chunk n - 1 was released at the previous barrier
+                if (n + K - 1 < cend) issue(n + K - 1);
+                if (n + D < cend) wait_for(min(K - 1 - D, cend - n - 1 - D));  // chunk n + D has landed
+                lds_barrier();
+            }
         }
         return;
     }
 
     // ------------------------------------------------------------ compute waves
-    const int strip = grp * NW + w;           // wave-uniform
-    const bool live = strip < a.n_strips;
-    const bool mstrip = strip < a.n_m;
-    const int col0 = (mstrip ? strip : strip - a.n_m) * 16;
-    const int col = col0 + r;
+    // Strip j of this wave: strip index grp * NS + w * SPW + j (wave-uniform).
+    bool live[SPW], mstrip[SPW];
+    int col0[SPW];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+        const int strip = grp * NS + w * SPW + j;
+        live[j] = strip < a.n_strips;
+        mstrip[j] = strip < a.n_m;
+        col0[j] = (mstrip[j] ? strip : strip - a.n_m) * 16;
+    }
+    bool any_live = false;
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) any_live = any_live || live[j];
 
-    floatx4 S[NBD];
+    // incoming state of each strip: loaded (all loads in flight together), or
+    // identity / zero
+    floatx4 S[SPW][NBD];
 #pragma unroll
-    for (int R = 0; R < NBD; ++R) {
+    for (int j = 0; j < SPW; ++j) {
+        const float* sinit = live[j] ? (mstrip[j] ? a.M0 : a.S0) : nullptr;  // wave-uniform
+        const int sw = mstrip[j] ? DK : a.Dv;
+        const int col = col0[j] + r;
+        if (sinit) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rw = 16 * R + 4 * gq + i;
-            float x = 0.f;
-            if (live) {
-                if (mstrip) x = a.M0 ? a.M0[((size_t)bh * DK + rw) * DK + col] : ((rw == col) ? 1.f : 0.f);
-                else if (a.S0) x = a.S0[((size_t)bh * DK + rw) * a.Dv + col];
-            }
-            S[R][i] = x;
+            for (int R = 0; R < NBD; ++R)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    S[j][R][i] = sinit[((size_t)bh * DK + 16 * R + 4 * gq + i) * sw + col];
+        } else {
+#pragma unroll
+            for (int R = 0; R < NBD; ++R)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    S[j][R][i] = (live[j] && mstrip[j] && 16 * R + 4 * gq + i == col) ? 1.f : 0.f;
         }
     }
 
-    T* out = mstrip ? reinterpret_cast<T*>(a.P_out) : reinterpret_cast<T*>(a.o);
-    const int out_w = mstrip ? DK : a.Dv;
-    const bool store_o = live && out != nullptr;
-    const bool load_v = live && !mstrip;
-
-    // Token-major addressing: a wave-uniform byte base per chunk plus a 32-bit
-    // lane byte offset (token within the chunk times the token stride, plus
-    // the column).
     using Raw = typename RawBits<T>::type;
-    const size_t vstride = (size_t)a.H * a.Dv * sizeof(T);   // bytes per token
-    const size_t ostride = (size_t)a.H * out_w * sizeof(T);
-    const unsigned char* vbase = reinterpret_cast<const unsigned char*>(a.v) +
-                                 (((size_t)b * a.T * a.H + h) * a.Dv + col0) * sizeof(T);
-    unsigned char* obase = store_o ? reinterpret_cast<unsigned char*>(out) +
-                                         (((size_t)b * a.T * a.H + h) * out_w + col0) * sizeof(T)
-                                   : nullptr;
-    uint32_t voff[NBK * 4], ooff[NBK * 4];
+    unsigned char* obase[SPW];
+    size_t ostride[SPW];
+    uint32_t vlane[SPW];
 #pragma unroll
-    for (int J = 0; J < NBK; ++J)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tk = 16 * J + 4 * gq + i;
-            voff[4 * J + i] = (uint32_t)(tk * vstride + r * sizeof(T));
-            ooff[4 * J + i] = (uint32_t)(tk * ostride + r * sizeof(T));
-        }
+    for (int j = 0; j < SPW; ++j) {
+        T* out = mstrip[j] ? reinterpret_cast<T*>(a.P_out) : reinterpret_cast<T*>(a.o);
+        const int out_w = mstrip[j] ? DK : a.Dv;
+        ostride[j] = (size_t)a.H * out_w * sizeof(T);  // bytes per token
+        obase[j] = (live[j] && out) ? reinterpret_cast<unsigned char*>(out) +
+                                          (((size_t)b * a.T * a.H + h) * out_w + col0[j] + r) * sizeof(T)
+                                    : nullptr;
+        // byte offset of this lane's column within a staged value row
+        vlane[j] = (uint32_t)((col0[j] - vcol0 + r) * (int)sizeof(T));
+    }
 
-    // V prefetch one chunk ahead: raw element bits, one 32-bit register per
-    // element (in a ragged last chunk, slots past T reread the chunk's first
-    // token and are zeroed when converted).
-    auto fetch_v = [&](int n, uint32_t* Vr) {
-        if (!load_v) return;
-        const unsigned char* vp = vbase + (size_t)n * C * vstride;
-        if (n * C + C <= a.T) {
-#pragma unroll
-            for (int k = 0; k < 4 * NBK; ++k) Vr[k] = (uint32_t)*reinterpret_cast<const Raw*>(vp + voff[k]);
-        } else {
-#pragma unroll
-            for (int k = 0; k < 4 * NBK; ++k) {
-                const int tok = n * C + 16 * (k / 4) + 4 * gq + (k % 4);
-                Vr[k] = (uint32_t)*reinterpret_cast<const Raw*>(vp + (tok < a.T ? voff[k] : (uint32_t)(r * sizeof(T))));
-            }
-        }
-    };
-    auto convert_v = [&](int n, const uint32_t* Vr, floatx4* Vd) {
-        if (!load_v) {
-#pragma unroll
-            for (int J = 0; J < NBK; ++J) Vd[J] = floatx4{0.f, 0.f, 0.f, 0.f};
-        } else if (n * C + C <= a.T) {
-#pragma unroll
-            for (int J = 0; J < NBK; ++J)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Vd[J][i] = RawBits<T>::to_float((Raw)Vr[4 * J + i]);
-        } else {
-#pragma unroll
-            for (int J = 0; J < NBK; ++J)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int tok = n * C + 16 * J + 4 * gq + i;
-                    Vd[J][i] = tok < a.T ? RawBits<T>::to_float((Raw)Vr[4 * J + i]) : 0.f;
-                }
-        }
-    };
-
-    uint32_t Vr[4 * NBK];
-#pragma unroll
-    for (int k = 0; k < 4 * NBK; ++k) Vr[k] = 0;
-    const int cend = a.c0 + a.nc;
-    if (a.nc > 0) fetch_v(a.c0, Vr);
-    lds_barrier();  // the first block is in LDS
-
-    for (int n = a.c0; n < cend; ++n) {
-        const unsigned char* cur = s_raw + (kDouble ? (size_t)((n - a.c0) & 1) * L.bytes : 0);
+    // Operands on the serial path (Kd, Tb and the values of a chunk) live in
+    // registers from one chunk to the next: with kAhead they are read for
+    // chunk n + 1 while chunk n's output is computed.
+    Frag<T> Ak[NBK][KSD], At[NBK][KSC];
+    uint32_t Vraw[SPW][NBK * 4];
+    auto load_serial = [&](int n) {
+        const unsigned char* cur = slot_of(n);
         const T* s_blk = reinterpret_cast<const T*>(cur);
-        const float* s_gam = reinterpret_cast<const float*>(cur + L.gamma_byte);
-
-        // Operand copy of the incoming state, then S <- Diag(gamma) S in place.
-        Frag<T> Sf[KSD];
+        const unsigned char* s_val = cur + L.bytes;
 #pragma unroll
-        for (int s = 0; s < KSD; ++s)
-            Sf[s] = (2 * s + 1 < NBD) ? frag_from_c<T>(S[2 * s], S[2 * s + 1]) : frag_from_c_lo<T>(S[2 * s]);
+        for (int J = 0; J < NBK; ++J)
 #pragma unroll
-        for (int R = 0; R < NBD; ++R) {
-            const float4 g4 = *reinterpret_cast<const float4*>(s_gam + 16 * R + 4 * gq);
-            S[R][0] *= g4.x; S[R][1] *= g4.y; S[R][2] *= g4.z; S[R][3] *= g4.w;
-        }
-        floatx4 V[NBK];
-        convert_v(n, Vr, V);
-        if (n + 1 < cend) fetch_v(n + 1, Vr);
-
-        if (live) {
-            // R = V - Kd S
-            Frag<T> Ak[NBK][KSD];
+            for (int s = 0; s < KSD; ++s) frag_load(Ak[J][s], s_blk + L.kd + (size_t)(J * KSD + s) * 512, lane);
 #pragma unroll
-            for (int J = 0; J < NBK; ++J)
-#pragma unroll
-                for (int s = 0; s < KSD; ++s) frag_load(Ak[J][s], s_blk + L.kd + (size_t)(J * KSD + s) * 512, lane);
-            floatx4 Rr[NBK];
-#pragma unroll
-            for (int J = 0; J < NBK; ++J) {
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < KSD; ++s) acc = mma(Ak[J][s], Sf[s], acc);
-                Rr[J] = V[J] - acc;
-            }
-            // U = Tb R   (Tb is block lower triangular)
-            Frag<T> At[NBK][KSC];
-#pragma unroll
-            for (int Ib = 0; Ib < NBK; ++Ib)
-#pragma unroll
-                for (int s = 0; s < KSC; ++s)
-                    if (2 * s <= Ib) frag_load(At[Ib][s], s_blk + L.tb + (size_t)(Ib * KSC + s) * 512, lane);
-            Frag<T> Rf[KSC];
+        for (int Ib = 0; Ib < NBK; ++Ib)
 #pragma unroll
             for (int s = 0; s < KSC; ++s)
-                Rf[s] = (2 * s + 1 < NBK) ? frag_from_c<T>(Rr[2 * s], Rr[2 * s + 1]) : frag_from_c_lo<T>(Rr[2 * s]);
-            floatx4 U[NBK];
+                if (2 * s <= Ib) frag_load(At[Ib][s], s_blk + L.tb + (size_t)(Ib * KSC + s) * 512, lane);
 #pragma unroll
-            for (int Ib = 0; Ib < NBK; ++Ib) {
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < SPW; ++j) {
+            const bool use_v = live[j] && !mstrip[j];
 #pragma unroll
-                for (int s = 0; s < KSC; ++s)
-                    if (2 * s <= Ib) acc = mma(At[Ib][s], Rf[s], acc);
-                U[Ib] = acc;
-            }
-            // O = Qp S + Aqk U
-            Frag<T> Aq[NBK][KSD], Aa[NBK][KSC];
+            for (int J = 0; J < NBK; ++J)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    Vraw[j][4 * J + i] = use_v ? (uint32_t)*reinterpret_cast<const Raw*>(
+                                                     s_val + (16 * J + 4 * gq + i) * Ring::kVRow + vlane[j])
+                                               : 0u;
+        }
+    };
+
+    lds_barrier();  // the first chunk(s) are in LDS
+    if (kAhead && any_live && a.nc > 0) load_serial(a.c0);
+
+    for (int n = a.c0; n < cend; ++n) {
+        const unsigned char* cur = slot_of(n);
+        const T* s_blk = reinterpret_cast<const T*>(cur);
+        const float* s_gam = reinterpret_cast<const float*>(cur + L.gamma_byte);
+        const bool full = n * C + C <= a.T;
+
+        if (any_live) {
+            if (!kAhead) load_serial(n);
+            // the rest of chunk n's operands, read now, used after U
+            Frag<T> Ap[NBD][KSC], Aq[NBK][KSD], Aa[NBK][KSC];
+            float4 g4[NBD];
+#pragma unroll
+            for (int R = 0; R < NBD; ++R)
+#pragma unroll
+                for (int s = 0; s < KSC; ++s) frag_load(Ap[R][s], s_blk + L.kpt + (size_t)(R * KSC + s) * 512, lane);
+#pragma unroll
+            for (int R = 0; R < NBD; ++R) g4[R] = *reinterpret_cast<const float4*>(s_gam + 16 * R + 4 * gq);
 #pragma unroll
             for (int Ib = 0; Ib < NBK; ++Ib) {
 #pragma unroll
@@ -610,67 +668,99 @@ void kda_inter_kernel(const InterArgs a) {
                 for (int s = 0; s < KSC; ++s)
                     if (2 * s <= Ib) frag_load(Aa[Ib][s], s_blk + L.aqk + (size_t)(Ib * KSC + s) * 512, lane);
             }
-            Frag<T> Uf[KSC];
+            // keep these reads ahead of the serial products (their latency hides
+            // behind R and U instead of stalling each product that uses them);
+            // larger blocks leave no registers for it
+            if constexpr (kPinOrder) __builtin_amdgcn_sched_barrier(0);
+
+            // Operand copy of the incoming state.
+            Frag<T> Sf[SPW][KSD];
 #pragma unroll
-            for (int s = 0; s < KSC; ++s)
-                Uf[s] = (2 * s + 1 < NBK) ? frag_from_c<T>(U[2 * s], U[2 * s + 1]) : frag_from_c_lo<T>(U[2 * s]);
-            unsigned char* op = store_o ? obase + (size_t)n * C * ostride : nullptr;
-            const bool full = n * C + C <= a.T;
-            floatx4 O[NBK];
+            for (int j = 0; j < SPW; ++j)
 #pragma unroll
-            for (int Ib = 0; Ib < NBK; ++Ib) {
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int s = 0; s < KSD; ++s)
+                    Sf[j][s] = (2 * s + 1 < NBD) ? frag_from_c<T>(S[j][2 * s], S[j][2 * s + 1])
+                                                 : frag_from_c_lo<T>(S[j][2 * s]);
+            // R = V - Kd S,  U = Tb R   (Tb is block lower triangular)
+            Frag<T> Uf[SPW][KSC];
 #pragma unroll
-                for (int s = 0; s < KSD; ++s) acc = mma(Aq[Ib][s], Sf[s], acc);
+            for (int j = 0; j < SPW; ++j) {
+                floatx4 Rr[NBK];
+#pragma unroll
+                for (int J = 0; J < NBK; ++J) {
+                    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < KSD; ++s) acc = mma(Ak[J][s], Sf[j][s], acc);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float x = RawBits<T>::to_float((Raw)Vraw[j][4 * J + i]);
+                        Rr[J][i] = ((full || n * C + 16 * J + 4 * gq + i < a.T) ? x : 0.f) - acc[i];
+                    }
+                }
+                Frag<T> Rf[KSC];
 #pragma unroll
                 for (int s = 0; s < KSC; ++s)
-                    if (2 * s <= Ib) acc = mma(Aa[Ib][s], Uf[s], acc);
-                O[Ib] = acc;
+                    Rf[s] = (2 * s + 1 < NBK) ? frag_from_c<T>(Rr[2 * s], Rr[2 * s + 1]) : frag_from_c_lo<T>(Rr[2 * s]);
+                floatx4 U[NBK];
+#pragma unroll
+                for (int Ib = 0; Ib < NBK; ++Ib) {
+                    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < KSC; ++s)
+                        if (2 * s <= Ib) acc = mma(At[Ib][s], Rf[s], acc);
+                    U[Ib] = acc;
+                }
+#pragma unroll
+                for (int s = 0; s < KSC; ++s)
+                    Uf[j][s] = (2 * s + 1 < NBK) ? frag_from_c<T>(U[2 * s], U[2 * s + 1]) : frag_from_c_lo<T>(U[2 * s]);
             }
-            if (store_o) {
-                if (full) {
+            // S <- Diag(gamma) S + KpT U
 #pragma unroll
-                    for (int Ib = 0; Ib < NBK; ++Ib)
+            for (int j = 0; j < SPW; ++j)
+#pragma unroll
+                for (int R = 0; R < NBD; ++R) {
+                    S[j][R][0] *= g4[R].x; S[j][R][1] *= g4[R].y; S[j][R][2] *= g4[R].z; S[j][R][3] *= g4[R].w;
+#pragma unroll
+                    for (int s = 0; s < KSC; ++s) S[j][R] = mma(Ap[R][s], Uf[j][s], S[j][R]);
+                }
+            // next chunk's serial operands, read while the output is computed
+            if (kAhead && n + 1 < cend) load_serial(n + 1);
+            if constexpr (kPinOrder) __builtin_amdgcn_sched_barrier(0);
+            // O = Qp S + Aqk U, stored
+#pragma unroll
+            for (int j = 0; j < SPW; ++j) {
+#pragma unroll
+                for (int Ib = 0; Ib < NBK; ++Ib) {
+                    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < KSD; ++s) acc = mma(Aq[Ib][s], Sf[j][s], acc);
+#pragma unroll
+                    for (int s = 0; s < KSC; ++s)
+                        if (2 * s <= Ib) acc = mma(Aa[Ib][s], Uf[j][s], acc);
+                    if (obase[j]) {
+                        unsigned char* op = obase[j] + (size_t)(n * C + 16 * Ib + 4 * gq) * ostride[j];
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
-                            *reinterpret_cast<T*>(op + ooff[4 * Ib + i]) = from_f<T>(O[Ib][i]);
-                } else {
-#pragma unroll
-                    for (int Ib = 0; Ib < NBK; ++Ib)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (n * C + 16 * Ib + 4 * gq + i < a.T)
-                                *reinterpret_cast<T*>(op + ooff[4 * Ib + i]) = from_f<T>(O[Ib][i]);
+                            if (full || n * C + 16 * Ib + 4 * gq + i < a.T)
+                                *reinterpret_cast<T*>(op + i * ostride[j]) = from_f<T>(acc[i]);
+                    }
                 }
             }
-            // S <- Diag(gamma) S + KpT U   (the decay was applied above)
-            Frag<T> Ap[NBD][KSC];
+        }
+        if (K == 1) lds_barrier();  // done reading the single slot
+        lds_barrier();              // the next chunk(s) are in LDS
+    }
+
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+        float* dst = mstrip[j] ? a.M_out : a.S_out;
+        const int dw = mstrip[j] ? DK : a.Dv;
+        if (live[j] && dst) {
 #pragma unroll
             for (int R = 0; R < NBD; ++R)
 #pragma unroll
-                for (int s = 0; s < KSC; ++s) frag_load(Ap[R][s], s_blk + L.kpt + (size_t)(R * KSC + s) * 512, lane);
-#pragma unroll
-            for (int R = 0; R < NBD; ++R) {
-#pragma unroll
-                for (int s = 0; s < KSC; ++s) S[R] = mma(Ap[R][s], Uf[s], S[R]);
-            }
-        }
-        if (!kDouble) lds_barrier();  // done reading the single buffer
-        lds_barrier();                // block n + 1 is in LDS
-    }
-
-    if (live) {
-        float* dst = mstrip ? a.M_out : a.S_out;
-        const int dw = mstrip ? DK : a.Dv;
-        if (dst) {
-#pragma unroll
-            for (int R = 0; R < NBD; ++R) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rw = 16 * R + 4 * gq + i;
-                    dst[((size_t)bh * DK + rw) * dw + col] = S[R][i];
-                }
-            }
+                for (int i = 0; i < 4; ++i)
+                    dst[((size_t)bh * DK + 16 * R + 4 * gq + i) * dw + col0[j] + r] = S[j][R][i];
         }
     }
 }
@@ -692,10 +782,14 @@ __host__ inline int slice_chunks(int BH, int NC, size_t block_bytes) {
 template <typename T, int DK, int C>
 static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t stream, hipEvent_t* ev, int n_ev) {
     constexpr BlockLayout L = block_layout(sizeof(T), DK, C);
+    // four compute waves of one 16-column strip each
     constexpr int NW = 4;
+    constexpr int SPW = 1;
+    constexpr int NS = NW * SPW;
     const int BH = a.B * a.H;
-    auto kern = kda_inter_kernel<T, DK, C, NW>;
-    constexpr size_t lds = (2 * L.bytes <= kLdsBudget) ? 2 * L.bytes : L.bytes;
+    auto kern = kda_inter_kernel<T, DK, C, NW, SPW>;
+    using Ring = InterRing<T, DK, C, NS>;
+    constexpr size_t lds = (size_t)Ring::kSlots * Ring::kSlot;
     // set on every call: the attribute is per device, and the call only records a limit
     const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -710,7 +804,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t stream, hipEven
     ea.T = a.T; ea.H = a.H; ea.Dv = a.Dv; ea.NC = a.NC;
     ea.n_m = (a.M_out || a.P_out) ? DK / 16 : 0;
     ea.n_strips = ea.n_m + a.Dv / 16;
-    ea.n_groups = (ea.n_strips + NW - 1) / NW;
+    ea.n_groups = (ea.n_strips + NS - 1) / NS;
 
     int k = 0;  // kernels launched so far (event k + 1 is recorded after kernel k)
     auto mark = [&]() -> bool { return !ev || k + 1 >= n_ev || hipEventRecord(ev[++k], stream) == hipSuccess; };
@@ -724,7 +818,9 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t stream, hipEven
         const bool first = sl == 0, last = sl == nsl - 1;
         if (nc > 0) {
             IntraArgs ia{a.q, a.k, a.z, a.beta_raw, a.A_log, a.ws, a.T, a.H, a.NC, c0, nc, a.g_min, a.flags};
-            hipLaunchKernelGGL((kda_intra_kernel<T, DK, C>), dim3((unsigned)(BH * nc)), dim3(256), 0, stream, ia);
+            constexpr int NCH = 64 / C;  // chunks per intra workgroup
+            hipLaunchKernelGGL((kda_intra_kernel<T, DK, C>), dim3((unsigned)(BH * ((nc + NCH - 1) / NCH))), dim3(256), 0,
+                               stream, ia);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
             if (!mark()) return hipErrorInvalidValue;
@@ -734,7 +830,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t stream, hipEven
         ea.M0 = first ? nullptr : M_scr;
         ea.S_out = last ? a.S_out : S_scr;
         ea.M_out = last ? a.M_out : M_scr;
-        hipLaunchKernelGGL(kern, dim3((unsigned)BH * ea.n_groups), dim3(64 * (NW + 1)), lds, stream, ea);
+        hipLaunchKernelGGL(kern, dim3((unsigned)BH * ea.n_groups), dim3(64 * (NW + 2)), lds, stream, ea);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (!mark()) return hipErrorInvalidValue;
