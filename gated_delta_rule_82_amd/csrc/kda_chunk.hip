@@ -501,9 +501,16 @@ void kda_inter_kernel(const InterArgs a) {
         constexpr int kTokPerPiece = 64 / kLanesPerRow;
         const int vcol = vcol0 + (lane % kLanesPerRow) * (16 / (int)sizeof(T));
         const int vcol_ld = vcol < 16 * vs1 ? vcol : 0;  // columns outside the range load any valid bytes
+        // values: a wave-uniform 64-bit base per chunk plus a 32-bit lane offset
+        const uint32_t tstride = (uint32_t)(a.H * a.Dv * (int)sizeof(T));  // bytes per token
+        const unsigned char* vrow0 = vsrc + (((size_t)b * a.T * a.H + h) * a.Dv) * sizeof(T);
+        const uint32_t vlane_tok = (uint32_t)(lane / kLanesPerRow);
+        const uint32_t vlane_col = (uint32_t)(vcol_ld * (int)sizeof(T));
         auto issue = [&](int n) {
             unsigned char* slot = slot_of(n);
             const unsigned char* gb = gblk + (size_t)n * L.bytes;
+            const unsigned char* vb = vrow0 + (size_t)n * C * tstride;
+            const int left = a.T - n * C;  // tokens of this chunk inside the sequence (>= 1)
 #pragma unroll
             for (int p = 0; p < Ring::kPieces; ++p) {
                 if (p % 2 != cw) continue;
@@ -515,11 +522,10 @@ void kda_inter_kernel(const InterArgs a) {
                             (__attribute__((address_space(3))) void*)(slot + p * 1024), 16, 0, 0);
                 } else {
                     const int j = p - Ring::kBlkPieces;
-                    int tok = n * C + j * kTokPerPiece + lane / kLanesPerRow;
-                    tok = tok < a.T ? tok : a.T - 1;  // rows past the end are zeroed by the compute waves
-                    const size_t e = (((size_t)b * a.T + tok) * a.H + h) * a.Dv + vcol_ld;
+                    uint32_t tok = (uint32_t)(j * kTokPerPiece) + vlane_tok;
+                    if (left < C) tok = tok < (uint32_t)left ? tok : (uint32_t)(left - 1);  // rows past the end are zeroed later
                     __builtin_amdgcn_global_load_lds(
-                        (const __attribute__((address_space(1))) void*)(vsrc + e * sizeof(T)),
+                        (const __attribute__((address_space(1))) void*)(vb + (tok * tstride + vlane_col)),
                         (__attribute__((address_space(3))) void*)(slot + L.bytes + j * 1024), 16, 0, 0);
                 }
             }
@@ -594,16 +600,18 @@ void kda_inter_kernel(const InterArgs a) {
     }
 
     using Raw = typename RawBits<T>::type;
+    // outputs: a wave-uniform 64-bit base per strip and chunk plus 32-bit lane
+    // offsets (token within the chunk times the token stride, plus the column)
     unsigned char* obase[SPW];
-    size_t ostride[SPW];
+    uint32_t ostride[SPW];
     uint32_t vlane[SPW];
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
         T* out = mstrip[j] ? reinterpret_cast<T*>(a.P_out) : reinterpret_cast<T*>(a.o);
         const int out_w = mstrip[j] ? DK : a.Dv;
-        ostride[j] = (size_t)a.H * out_w * sizeof(T);  // bytes per token
+        ostride[j] = (uint32_t)(a.H * out_w * (int)sizeof(T));  // bytes per token
         obase[j] = (live[j] && out) ? reinterpret_cast<unsigned char*>(out) +
-                                          (((size_t)b * a.T * a.H + h) * out_w + col0[j] + r) * sizeof(T)
+                                          (((size_t)b * a.T * a.H + h) * out_w + col0[j]) * sizeof(T)
                                     : nullptr;
         // byte offset of this lane's column within a staged value row
         vlane[j] = (uint32_t)((col0[j] - vcol0 + r) * (int)sizeof(T));
@@ -738,11 +746,18 @@ void kda_inter_kernel(const InterArgs a) {
                     for (int s = 0; s < KSC; ++s)
                         if (2 * s <= Ib) acc = mma(Aa[Ib][s], Uf[j][s], acc);
                     if (obase[j]) {
-                        unsigned char* op = obase[j] + (size_t)(n * C + 16 * Ib + 4 * gq) * ostride[j];
+                        unsigned char* ob = obase[j] + (size_t)n * C * ostride[j];
+                        const uint32_t o0 = (uint32_t)(16 * Ib + 4 * gq) * ostride[j] + (uint32_t)(r * (int)sizeof(T));
+                        if (full) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (full || n * C + 16 * Ib + 4 * gq + i < a.T)
-                                *reinterpret_cast<T*>(op + i * ostride[j]) = from_f<T>(acc[i]);
+                            for (int i = 0; i < 4; ++i)
+                                *reinterpret_cast<T*>(ob + (o0 + (uint32_t)i * ostride[j])) = from_f<T>(acc[i]);
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                if (n * C + 16 * Ib + 4 * gq + i < a.T)
+                                    *reinterpret_cast<T*>(ob + (o0 + (uint32_t)i * ostride[j])) = from_f<T>(acc[i]);
+                        }
                     }
                 }
             }
