@@ -1,15 +1,18 @@
 #!/usr/bin/env python3
 """Benchmark of the KDA hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk 32] [--overlap]
 
-A step is one kda_chunk_fwd call (prep, intra-chunk and inter-chunk kernels)
-over the layer-shaped workload B=4, T=4096, H=16, Dk=Dv=128, chunk 64, bf16
+A step is one chunkwise forward call (prep, intra-chunk and inter-chunk
+kernels) over the layer-shaped workload B=4, T=4096, H=16, Dk=Dv=128, bf16
 inputs and fp32 state, with the inputs already resident in HBM.  Four input
 sets (about 1.1 GB) rotate from step to step so the 256 MB Infinity Cache
-cannot serve them.  The JSON line also reports, measured in the same run:
-  * per-kernel times from HIP events recorded by the library between its
-    kernels, and the roofline of the dominant kernel;
+cannot serve them.  The call is kda_chunk_fwd on one stream (--overlap times
+the two-stream schedule kda_chunk_fwd_overlap instead).  The state chunk is a
+tiling choice of the kernels (results agree to rounding for 16, 32 and 64);
+32 is the fastest here.  The JSON line also reports, measured in the same run:
+  * per-kernel times from HIP events the library records around each of its
+    kernels, and the roofline of the dominant kernel per launch;
   * MFMA % of the whole call under both flop counts, HBM % on compulsory bytes;
   * the decode step (B=256, H=32, D=128, fp32 state) and its HBM %;
   * the long-context segmented flow (B=1, T=65536, H=32, 8 segments);
@@ -58,14 +61,22 @@ def chunk_bytes(B, T, H, Dk, Dv, esize=2):
     return rows * (3 * Dk + Dv + 1) * esize + rows * Dv * esize + B * H * Dk * Dv * 4 + H * 4
 
 
-def kernel_bytes(B, T, H, Dk, Dv, C, ws_bytes, esize=2):
-    """Algorithmic bytes per launch of each kernel, every byte touched once:
-    intra reads q, k, z, beta_raw and A_log and writes the per-chunk blocks;
-    inter reads the blocks and v and writes o and the final state.  The fp32
-    carry region at the end of the workspace is used only when the sequence is
-    cut into slices, so it is not counted."""
+def block_bytes(Dk, C, esize=2):
+    """Bytes of one per-chunk block the intra kernel hands to the inter kernel:
+    Kd, Qp (C x Dk), KpT (Dk x C), Tb, Aqk (C x C) as 512-element operand tiles
+    (contraction padded to 32), the fp32 chunk decay (Dk), rounded to 256."""
+    nbk, ksd, nbd, ksc = C // 16, (Dk + 31) // 32, Dk // 16, (C + 31) // 32
+    tiles = 2 * nbk * ksd + nbd * ksc + 2 * nbk * ksc
+    return (tiles * 512 * esize + Dk * 4 + 255) // 256 * 256
+
+
+def kernel_bytes(B, T, H, Dk, Dv, C, esize=2):
+    """Algorithmic bytes of each kernel over the whole sequence, every byte
+    touched once: intra reads q, k, z, beta_raw and A_log and writes the
+    per-chunk blocks; inter reads the blocks and v and writes o and the final
+    state.  (The fp32 state carried between slices is not counted.)"""
     rows = B * T * H
-    blocks = ws_bytes - B * H * Dk * (Dk + Dv) * 4
+    blocks = B * H * ((T + C - 1) // C) * block_bytes(Dk, C, esize)
     intra = rows * (3 * Dk + 1) * esize + H * 4 + blocks
     inter = blocks + rows * Dv * esize + rows * Dv * esize + B * H * Dk * Dv * 4
     return {"kda_intra": intra, "kda_inter": inter}
@@ -83,9 +94,10 @@ def source_sha():
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel):
+def read_traffic(kernel, chunk, launches):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when the kernel sources changed since the counters were taken."""
+    None when the kernel sources, the chunk or the launch count per step
+    differ from the run the counters were taken on."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
@@ -93,7 +105,9 @@ def read_traffic(kernel):
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_sha") != source_sha():
+    if kv.get("source_sha") != source_sha() or kv.get("chunk") != str(chunk):
+        return None
+    if kv.get(f"{kernel}_launches") != str(launches):
         return None
     val = kv.get(f"{kernel}_hbm_bytes")
     return float(val) if val else None
@@ -141,7 +155,11 @@ def cpu_baseline(inp, T_sample):
 
 # ------------------------------------------------------------------ GPU legs
 
-def bench_layer(torch, kda, inputs, steps, warmup, chunk=None):
+def bench_layer(torch, kda, inputs, steps, warmup, chunk=None, overlap=False):
+    """Time `steps` calls over rotating input sets.  overlap: the two-stream
+    schedule (kda_chunk_fwd_overlap), else one stream (kda_chunk_fwd_timed).
+    Per-kernel launch times come from the events the library records around
+    each of its kernels, on the kernel's own stream."""
     w = inputs.WORKLOADS["layer"]
     dev = torch.device("cuda:0")
     B, T, H, Dk, Dv = w.B, w.T, w.H, w.Dk, w.Dv
@@ -156,19 +174,21 @@ def bench_layer(torch, kda, inputs, steps, warmup, chunk=None):
     A = base["A_log"].to(dev)
     o = torch.empty(B, T, H, Dv, dtype=torch.bfloat16, device=dev)
     S = torch.empty(B, H, Dk, Dv, dtype=torch.float32, device=dev)
-    ws_n = kda.workspace_bytes(B, T, H, Dk, Dv, C, torch.bfloat16)
+    ov = kda.Overlap(dev) if overlap else None
+    ws_n = (kda.overlap_workspace_bytes if overlap else kda.workspace_bytes)(B, T, H, Dk, Dv, C, torch.bfloat16)
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    nk = (kda.overlap_kernel_count if overlap else kda.kernel_count)(B, T, H, Dk, Dv, C, torch.bfloat16)
+    n_ev = 2 * nk if overlap else nk + 1
 
     def step(i, evs=None):
         s = sets[i % len(sets)]
         kda.chunk_fwd(s["q"], s["k"], s["v"], s["z"], s["beta_raw"], A, None, chunk=C,
-                      o=o, S_out=S, workspace=ws, events=evs)
+                      o=o, S_out=S, workspace=ws, events=evs, overlap=ov)
 
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    nk = kda.kernel_count(B, T, H, Dk, Dv, C, torch.bfloat16)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
@@ -177,13 +197,19 @@ def bench_layer(torch, kda, inputs, steps, warmup, chunk=None):
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
-    # kernels alternate intra, inter over the slices of the sequence
-    intra = [sum(e[k].elapsed_time(e[k + 1]) for k in range(0, nk, 2)) for e in evs]
-    inter = [sum(e[k].elapsed_time(e[k + 1]) for k in range(1, nk, 2)) for e in evs]
+    # kernel k: intra for even k, inter for odd k (they alternate over the slices)
+    if overlap:
+        dur = lambda e, k: e[2 * k].elapsed_time(e[2 * k + 1])
+    else:
+        dur = lambda e, k: e[k].elapsed_time(e[k + 1])
+    launches = {"kda_intra": [dur(e, k) for e in evs for k in range(0, nk, 2)],
+                "kda_inter": [dur(e, k) for e in evs for k in range(1, nk, 2)]}
     return {"B": B, "T": T, "H": H, "Dk": Dk, "Dv": Dv, "C": C, "ws_bytes": ws_n,
+            "schedule": "two streams, two slices" if overlap else "one stream",
             "ms_per_step": total_ms / steps,
-            "kernel_ms": {"kda_intra": sum(intra) / steps, "kda_inter": sum(inter) / steps},
-            "launches_per_step": nk}
+            "kernel_ms": {k: sum(v) / steps for k, v in launches.items()},
+            "launch_ms": {k: sum(v) / len(v) for k, v in launches.items()},
+            "launches_per_step": {k: len(v) // steps for k, v in launches.items()}}
 
 
 def bench_decode(torch, kda, inputs, steps, warmup):
@@ -216,7 +242,7 @@ def bench_decode(torch, kda, inputs, steps, warmup):
             "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
 
 
-def bench_long(torch, kda, inputs, reps):
+def bench_long(torch, kda, inputs, reps, chunk):
     w = inputs.WORKLOADS["long"]
     dev = torch.device("cuda:0")
     n, Tseg = w.segments, w.T // w.segments
@@ -229,7 +255,8 @@ def bench_long(torch, kda, inputs, reps):
     seg = {k: v.view(n, Tseg, *v.shape[2:]) for k, v in x.items()}
     o_full = torch.empty_like(x["v"])
     S_full = torch.empty(w.B, w.H, w.Dk, w.Dv, device=dev)
-    ws = torch.empty(kda.workspace_bytes(w.B, w.T, w.H, w.Dk, w.Dv, w.chunk), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(kda.workspace_bytes(w.B, w.T, w.H, w.Dk, w.Dv, chunk),
+                         kda.workspace_bytes(n, Tseg, w.H, w.Dk, w.Dv, chunk)), dtype=torch.uint8, device=dev)
     o0 = torch.empty(n, 1, Tseg, w.H, w.Dv, dtype=torch.bfloat16, device=dev)
     P = torch.empty(n, 1, Tseg, w.H, w.Dk, dtype=torch.bfloat16, device=dev)
     M = torch.empty(n, 1, w.H, w.Dk, w.Dk, device=dev)
@@ -237,10 +264,11 @@ def bench_long(torch, kda, inputs, reps):
     Sp = torch.empty_like(St)
 
     def full():
-        kda.chunk_fwd(x["q"], x["k"], x["v"], x["z"], x["beta_raw"], A, None, o=o_full, S_out=S_full, workspace=ws)
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["z"], x["beta_raw"], A, None, chunk=chunk, o=o_full, S_out=S_full,
+                      workspace=ws)
 
     def segmented():
-        kda.chunk_fwd(seg["q"], seg["k"], seg["v"], seg["z"], seg["beta_raw"], A, None,
+        kda.chunk_fwd(seg["q"], seg["k"], seg["v"], seg["z"], seg["beta_raw"], A, None, chunk=chunk,
                       want_M=True, want_P=True, o=o0.view(n, Tseg, w.H, w.Dv), S_out=St.view(n, w.H, w.Dk, w.Dv),
                       M_out=M.view(n, w.H, w.Dk, w.Dk), P_out=P.view(n, Tseg, w.H, w.Dk), workspace=ws)
         kda.segment_compose(M, St, S_prefix=Sp)
@@ -260,7 +288,8 @@ def bench_long(torch, kda, inputs, reps):
         res[name] = {"ms": round(ms, 3), "tokens_per_s": w.T / (ms / 1e3)}
     diff = float((o0.view(w.B, w.T, w.H, w.Dv).float() - o_full.float()).abs().max())
     res["max_abs_diff_vs_full"] = diff
-    res["workload"] = "long: B1 T65536 H32 Dk=Dv=128 bf16; segmented = 8 x 8192 fragments + compose + fixup"
+    res["workload"] = (f"long: B1 T65536 H32 Dk=Dv=128 bf16, chunk {chunk}; segmented = 8 x 8192 fragments "
+                       "+ compose + fixup")
     return res
 
 
@@ -275,7 +304,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--long-reps", type=int, default=3)
     ap.add_argument("--only-layer", action="store_true", help="time the layer workload only")
-    ap.add_argument("--chunk", type=int, default=0, help="state chunk length (0: the workload's own)")
+    ap.add_argument("--chunk", type=int, default=32, help="state chunk length (16, 32 or 64)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="time the two-stream schedule (kda_chunk_fwd_overlap) instead of the one-stream call")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run 3 device copies of 1 GiB (a counter reference of known size)")
     args = ap.parse_args()
@@ -313,18 +344,21 @@ def main():
         log("[bench] copy calibration: 3 x 1 GiB device copies done")
 
     log("[bench] layer workload ...")
-    L = bench_layer(torch, kda, inputs, args.steps, args.warmup, args.chunk or None)
-    B, T, H, Dk, Dv, C = L["B"], L["T"], L["H"], L["Dk"], L["Dv"], L["C"]
+    C = args.chunk or 32
+    L = bench_layer(torch, kda, inputs, args.steps, args.warmup, C, overlap=args.overlap)
+    B, T, H, Dk, Dv = L["B"], L["T"], L["H"], L["Dk"], L["Dv"]
     ms = L["ms_per_step"]
     tok_s = B * T / (ms / 1e3)
     f_tri, f_full = chunk_flops(B, T, H, Dk, Dv, C)
     cbytes = chunk_bytes(B, T, H, Dk, Dv)
-    kb = kernel_bytes(B, T, H, Dk, Dv, C, L["ws_bytes"])
+    kb = kernel_bytes(B, T, H, Dk, Dv, C)
     dom = max(L["kernel_ms"], key=L["kernel_ms"].get)
-    dom_ms = L["kernel_ms"][dom]
-    achieved = kb[dom] / (dom_ms / 1e3) / 1e9
-    traffic = read_traffic(dom)
-    log(f"[bench] layer {ms:.3f} ms/step, {tok_s:.3e} tokens/s; kernels {L['kernel_ms']}")
+    n_launch = L["launches_per_step"][dom]
+    launch_ms = L["launch_ms"][dom]
+    bytes_per_launch = kb[dom] / n_launch
+    achieved = bytes_per_launch / (launch_ms / 1e3) / 1e9
+    traffic = read_traffic(dom, C, n_launch)
+    log(f"[bench] layer {ms:.3f} ms/step ({L['schedule']}), {tok_s:.3e} tokens/s; kernels {L['kernel_ms']}")
 
     extra = {}
     if not args.only_layer:
@@ -332,7 +366,7 @@ def main():
         extra["decode"] = bench_decode(torch, kda, inputs, args.decode_steps, 10)
         log(f"[bench] decode {extra['decode']['us_per_step']} us/step")
         log("[bench] long workload ...")
-        extra["long"] = bench_long(torch, kda, inputs, args.long_reps)
+        extra["long"] = bench_long(torch, kda, inputs, args.long_reps, C)
         log(f"[bench] long {extra['long']}")
 
     out = {
@@ -348,11 +382,13 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) inputs, A_log ~ N(0,0.5); 4 rotating input sets in HBM)",
-        "config": {"workload": f"layer: chunk_kda fwd B4 T4096 H16 Dk=Dv=128 chunk{C}, bf16 in, fp32 state",
+        "config": {"workload": f"layer: chunk_kda fwd B4 T4096 H16 Dk=Dv=128, bf16 in, fp32 state "
+                               f"(state chunk {C}; {L['schedule']})",
                    "B": B, "T": T, "H": H, "Dk": Dk, "Dv": Dv, "chunk": C, "g_min": -5.0},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes": kb[dom], "kernel_ms": round(dom_ms, 4)},
+                     "traffic": traffic, "algorithmic_bytes": round(bytes_per_launch),
+                     "launch_ms": round(launch_ms, 4), "launches_per_step": n_launch},
         "kernel_ms": {k: round(v, 4) for k, v in L["kernel_ms"].items()},
         "mfma_frac": {"algorithmic": round(f_tri / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                       "tile_count": round(f_full / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)},

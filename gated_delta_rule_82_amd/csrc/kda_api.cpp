@@ -16,6 +16,7 @@ constexpr double kBf16Max = 3.3895313892515355e38;  // (2 - 2^-7) * 2^127
 constexpr double kF32Max = 3.4028234663852886e38;
 constexpr double kHeadroom = 1024.0;
 constexpr int kFactorTile = 16;  // token tile of the factored decay products
+constexpr int kOverlapSyncEvents = 5;  // events kda_chunk_fwd_overlap needs
 
 bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -49,13 +50,23 @@ int kda_safe_chunk_size(float g_min, kda_dtype dt) {
     return v < 0 ? 0 : (int)floor(v);
 }
 
-size_t kda_chunk_fwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype dt) {
+static size_t workspace_bytes_impl(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype dt, bool overlap) {
     if (chunk == 0) chunk = 64;
     if (B < 0 || T < 0 || H < 0 || !dim_ok(Dk) || !dim_ok(Dv) || !dtype_ok(dt)) return 0;
     if (chunk != 16 && chunk != 32 && chunk != 64) return 0;
-    const size_t nc = (size_t)(T + chunk - 1) / (size_t)chunk;
     if ((size_t)B * H == 0) return 0;
-    return kda::chunk_workspace_bytes(elem_bytes(dt), Dk, Dv, chunk, (size_t)B * H, nc);
+    const int BH = B * H, NC = (T + chunk - 1) / chunk;
+    const size_t blk = kda::block_layout(elem_bytes(dt), Dk, chunk).bytes;
+    const int per = overlap ? kda::overlap_slice_chunks(BH, NC, blk) : kda::slice_chunks(BH, NC, blk);
+    return kda::chunk_workspace_bytes(elem_bytes(dt), Dk, Dv, chunk, (size_t)BH, (size_t)per, overlap ? 2 : 1);
+}
+
+size_t kda_chunk_fwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype dt) {
+    return workspace_bytes_impl(B, T, H, Dk, Dv, chunk, dt, false);
+}
+
+size_t kda_chunk_fwd_overlap_workspace(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype dt) {
+    return workspace_bytes_impl(B, T, H, Dk, Dv, chunk, dt, true);
 }
 
 }  // extern "C"
@@ -66,7 +77,8 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
                                  int B, int T, int H, int Dk, int Dv, int chunk,
                                  float g_min, unsigned flags, kda_dtype dt,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream,
-                                 hipEvent_t* ev, int n_ev) {
+                                 hipEvent_t* ev, int n_ev,
+                                 bool overlap = false, hipStream_t aux = nullptr, hipEvent_t* sync = nullptr) {
     if (!dtype_ok(dt) || !flags_ok(flags)) return KDA_ERR_DTYPE;
     if (chunk == 0) chunk = 64;
     if (B < 0 || T < 0 || H < 0 || !dim_ok(Dk) || !dim_ok(Dv)) return KDA_ERR_SHAPE;
@@ -81,7 +93,7 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
         else KDA_TRY(maybe(A_log));
     }
     KDA_TRY(maybe(S0)); KDA_TRY(maybe(S_out)); KDA_TRY(maybe(M_out)); KDA_TRY(maybe(P_out));
-    const size_t ws_need = kda_chunk_fwd_workspace(B, T, H, Dk, Dv, chunk, dt);
+    const size_t ws_need = workspace_bytes_impl(B, T, H, Dk, Dv, chunk, dt, overlap);
     if (ws_need > 0) {
         if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
             workspace_bytes < ws_need)
@@ -89,9 +101,21 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
     }
     kda::ChunkArgs a{};
     a.q = q; a.k = k; a.v = v; a.z = z; a.beta_raw = beta_raw; a.A_log = A_log; a.S0 = S0;
-    a.o = o; a.S_out = S_out; a.M_out = M_out; a.P_out = P_out; a.ws = workspace;
+    a.o = o; a.S_out = S_out; a.M_out = M_out; a.P_out = P_out; a.ws = workspace; a.ws_bytes = workspace_bytes;
     a.B = B; a.T = T; a.H = H; a.Dv = Dv; a.NC = (T + chunk - 1) / chunk;
     a.g_min = g_min; a.flags = flags;
+    if (overlap) {
+        for (int i = 0; i < kOverlapSyncEvents; ++i)
+            if (!sync[i]) return KDA_ERR_NULL;
+        if (ev) {
+            const int need = 2 * kda::chunk_overlap_kernel_count(elem_bytes(dt), Dk, chunk, B * H, a.NC);
+            if (n_ev < need) return KDA_ERR_NULL;
+            for (int i = 0; i < need; ++i)
+                if (!ev[i]) return KDA_ERR_NULL;
+        }
+        const hipError_t e = kda::launch_chunk_overlap(dt == KDA_BF16 ? 1 : 0, Dk, chunk, a, stream, aux, sync, ev, n_ev);
+        return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
     if (ev) {
         const int need = kda::chunk_kernel_count(elem_bytes(dt), Dk, chunk, B * H, a.NC) + 1;
         if (n_ev < need) return KDA_ERR_NULL;
@@ -131,6 +155,29 @@ int kda_chunk_fwd_kernel_count(int B, int T, int H, int Dk, int Dv, int chunk, k
     if (B <= 0 || T < 0 || H <= 0 || !dim_ok(Dk) || !dim_ok(Dv) || !dtype_ok(dt)) return 0;
     if (chunk != 16 && chunk != 32 && chunk != 64) return 0;
     return kda::chunk_kernel_count(elem_bytes(dt), Dk, chunk, B * H, (T + chunk - 1) / chunk);
+}
+
+kda_status kda_chunk_fwd_overlap(const void* q, const void* k, const void* v, const void* z,
+                                 const void* beta_raw, const float* A_log, const float* S0,
+                                 void* o, float* S_out, float* M_out, void* P_out,
+                                 int B, int T, int H, int Dk, int Dv, int chunk,
+                                 float g_min, unsigned flags, kda_dtype dt,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream, hipStream_t aux_stream,
+                                 hipEvent_t* sync_events, int n_sync_events,
+                                 hipEvent_t* timing_events, int n_timing_events) {
+    if (!sync_events || n_sync_events < kOverlapSyncEvents) return KDA_ERR_NULL;
+    if (timing_events == nullptr) n_timing_events = 0;
+    return chunk_fwd_impl(q, k, v, z, beta_raw, A_log, S0, o, S_out, M_out, P_out, B, T, H, Dk, Dv,
+                          chunk, g_min, flags, dt, workspace, workspace_bytes, stream,
+                          timing_events, n_timing_events, true, aux_stream, sync_events);
+}
+
+int kda_chunk_fwd_overlap_kernel_count(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype dt) {
+    if (chunk == 0) chunk = 64;
+    if (B <= 0 || T < 0 || H <= 0 || !dim_ok(Dk) || !dim_ok(Dv) || !dtype_ok(dt)) return 0;
+    if (chunk != 16 && chunk != 32 && chunk != 64) return 0;
+    return kda::chunk_overlap_kernel_count(elem_bytes(dt), Dk, chunk, B * H, (T + chunk - 1) / chunk);
 }
 
 kda_status kda_step(const void* q, const void* k, const void* v, const void* z,

@@ -39,7 +39,8 @@ namespace kda {
 struct IntraArgs {
     const void* q; const void* k; const void* z; const void* beta_raw;
     const float* A_log; void* ws;
-    int T, H, NC;
+    int T, H;
+    int wsNC;            // chunk blocks per (b, h) in the workspace buffer, chunk c0 first
     int c0, nc;          // chunks [c0, c0 + nc) of every (b, h) in this launch
     float g_min;
     unsigned flags;
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     const int sub = w / NBK;
     const int I = w % NBK;
     const int n = a.c0 + g * NCH + sub;
-    const int cid = bh * a.NC + n;     // workspace block of (b, h, chunk n)
+    const int cid = bh * a.wsNC + (n - a.c0);  // workspace block of (b, h, chunk n)
     const int h = bh % a.H;
     const int b = bh / a.H;
 
@@ -212,7 +213,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
             }
         }
         if (Ib == 0) {
-            const size_t cb = (size_t)bh * a.NC + a.c0 + g * NCH + sb;  // workspace block of that chunk
+            const size_t cb = (size_t)bh * a.wsNC + g * NCH + sb;  // workspace block of that chunk
             float* gam = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(a.ws) + cb * L.bytes + L.gamma_byte);
             gam[c] = exp2_fast(GC);
         }
@@ -410,7 +411,8 @@ struct InterArgs {
     const float* M0;     // incoming transition of the identity strips (NULL: identity)
     void* o; float* S_out; float* M_out; void* P_out;
     const void* ws;
-    int T, H, Dv, NC;
+    int T, H, Dv;
+    int wsNC;            // chunk blocks per (b, h) in the workspace buffer, chunk c0 first
     int c0, nc;          // chunks [c0, c0 + nc) in this launch
     int n_m, n_strips, n_groups;
 };
@@ -495,7 +497,7 @@ void kda_inter_kernel(const InterArgs a) {
     if (w >= NW) {
         // ------------------------------------------------------ copy waves
         const int cw = w - NW;
-        const unsigned char* gblk = reinterpret_cast<const unsigned char*>(a.ws) + (size_t)bh * a.NC * L.bytes;
+        const unsigned char* gblk = reinterpret_cast<const unsigned char*>(a.ws) + (size_t)bh * a.wsNC * L.bytes;
         const unsigned char* vsrc = reinterpret_cast<const unsigned char*>(a.v);
         constexpr int kLanesPerRow = Ring::kVRow / 16;
         constexpr int kTokPerPiece = 64 / kLanesPerRow;
@@ -508,7 +510,7 @@ void kda_inter_kernel(const InterArgs a) {
         const uint32_t vlane_col = (uint32_t)(vcol_ld * (int)sizeof(T));
         auto issue = [&](int n) {
             unsigned char* slot = slot_of(n);
-            const unsigned char* gb = gblk + (size_t)n * L.bytes;
+            const unsigned char* gb = gblk + (size_t)(n - a.c0) * L.bytes;
             const unsigned char* vb = vrow0 + (size_t)n * C * tstride;
             const int left = a.T - n * C;  // tokens of this chunk inside the sequence (>= 1)
 #pragma unroll
@@ -780,73 +782,84 @@ void kda_inter_kernel(const InterArgs a) {
     }
 }
 
-// Chunks per slice: intra and inter alternate over slices of the sequence of
-// at most kSliceBytes of intermediates each.  Measured on MI355X, smaller
-// slices (64-128 MB, to keep a slice in the 256 MB Infinity Cache) lose more
-// to partial grids and per-launch prologues than they gain, so the budget is
-// large: the layer-sized workloads run as a single slice.
-constexpr size_t kSliceBytes = 1ull << 30;
+// Launch configuration of the chunk kernels for one (T, DK, C).
+template <typename T, int DK, int C>
+struct ChunkLaunch {
+    static constexpr BlockLayout L = block_layout(sizeof(T), DK, C);
+    static constexpr int NW = 4;   // compute waves of the inter kernel, one 16-column strip each
+    static constexpr int SPW = 1;
+    static constexpr int NS = NW * SPW;
+    using Ring = InterRing<T, DK, C, NS>;
+    static constexpr size_t kLds = (size_t)Ring::kSlots * Ring::kSlot;
+    static constexpr int NCH = 64 / C;  // chunks per intra workgroup
 
-__host__ inline int slice_chunks(int BH, int NC, size_t block_bytes) {
-    if (NC <= 0) return 0;
-    const size_t per = std::max<size_t>(1, kSliceBytes / std::max<size_t>(1, (size_t)BH * block_bytes));
-    const int nsl = (int)((NC + per - 1) / per);
-    return (NC + nsl - 1) / nsl;
-}
+    const ChunkArgs& a;
+    int BH;
+    InterArgs ea{};
+
+    explicit ChunkLaunch(const ChunkArgs& args) : a(args), BH(args.B * args.H) {
+        ea.v = a.v; ea.o = a.o; ea.P_out = a.P_out;
+        ea.T = a.T; ea.H = a.H; ea.Dv = a.Dv;
+        ea.n_m = (a.M_out || a.P_out) ? DK / 16 : 0;
+        ea.n_strips = ea.n_m + a.Dv / 16;
+        ea.n_groups = (ea.n_strips + NS - 1) / NS;
+    }
+    static hipError_t set_attributes() {
+        // set on every call: the attribute is per device, and the call only records a limit
+        return hipFuncSetAttribute(reinterpret_cast<const void*>(kda_inter_kernel<T, DK, C, NW, SPW>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+    }
+    // intra kernel over chunks [c0, c0 + nc) into the buffer `buf` of `per` chunks per (b, h)
+    hipError_t intra(void* buf, int per, int c0, int nc, hipStream_t s) const {
+        IntraArgs ia{a.q, a.k, a.z, a.beta_raw, a.A_log, buf, a.T, a.H, per, c0, nc, a.g_min, a.flags};
+        hipLaunchKernelGGL((kda_intra_kernel<T, DK, C>), dim3((unsigned)(BH * ((nc + NCH - 1) / NCH))), dim3(256), 0,
+                           s, ia);
+        return hipGetLastError();
+    }
+    // inter kernel over the same chunks; the state enters from S0/M0 (first
+    // slice) or the carry region, and leaves to S_out/M_out (last slice) or it
+    hipError_t inter(void* buf, int per, int c0, int nc, bool first, bool last, float* S_scr, float* M_scr,
+                     hipStream_t s) {
+        ea.ws = buf; ea.wsNC = per; ea.c0 = c0; ea.nc = nc;
+        ea.S0 = first ? a.S0 : S_scr;
+        ea.M0 = first ? nullptr : M_scr;
+        ea.S_out = last ? a.S_out : S_scr;
+        ea.M_out = last ? a.M_out : M_scr;
+        hipLaunchKernelGGL((kda_inter_kernel<T, DK, C, NW, SPW>), dim3((unsigned)BH * ea.n_groups),
+                           dim3(64 * (NW + 2)), kLds, s, ea);
+        return hipGetLastError();
+    }
+};
 
 template <typename T, int DK, int C>
 static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t stream, hipEvent_t* ev, int n_ev) {
-    constexpr BlockLayout L = block_layout(sizeof(T), DK, C);
-    // four compute waves of one 16-column strip each
-    constexpr int NW = 4;
-    constexpr int SPW = 1;
-    constexpr int NS = NW * SPW;
-    const int BH = a.B * a.H;
-    auto kern = kda_inter_kernel<T, DK, C, NW, SPW>;
-    using Ring = InterRing<T, DK, C, NS>;
-    constexpr size_t lds = (size_t)Ring::kSlots * Ring::kSlot;
-    // set on every call: the attribute is per device, and the call only records a limit
-    const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    ChunkLaunch<T, DK, C> cl(a);
+    const hipError_t attr = cl.set_attributes();
     if (attr != hipSuccess) return attr;
-
-    // running state between slices: S then M, after the chunk blocks
-    float* S_scr = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(a.ws) + (size_t)BH * a.NC * L.bytes);
+    const int BH = cl.BH;
+    const int per = slice_chunks(BH, a.NC, cl.L.bytes);
+    // the kernels below index the workspace with this `per`: refuse a buffer
+    // sized for anything else rather than write past it
+    if (a.ws_bytes < chunk_workspace_bytes(sizeof(T), DK, a.Dv, C, (size_t)BH, (size_t)per, 1))
+        return hipErrorInvalidValue;
+    // one buffer of `per` chunks, reused by every slice (same stream), then the carry
+    float* S_scr = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(a.ws) + (size_t)BH * per * cl.L.bytes);
     float* M_scr = S_scr + (size_t)BH * DK * a.Dv;
-
-    InterArgs ea{};
-    ea.v = a.v; ea.o = a.o; ea.P_out = a.P_out; ea.ws = a.ws;
-    ea.T = a.T; ea.H = a.H; ea.Dv = a.Dv; ea.NC = a.NC;
-    ea.n_m = (a.M_out || a.P_out) ? DK / 16 : 0;
-    ea.n_strips = ea.n_m + a.Dv / 16;
-    ea.n_groups = (ea.n_strips + NS - 1) / NS;
 
     int k = 0;  // kernels launched so far (event k + 1 is recorded after kernel k)
     auto mark = [&]() -> bool { return !ev || k + 1 >= n_ev || hipEventRecord(ev[++k], stream) == hipSuccess; };
     if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return hipErrorInvalidValue;
 
-    const int per = slice_chunks(BH, a.NC, L.bytes);
     const int nsl = a.NC > 0 ? (a.NC + per - 1) / per : 1;
     for (int sl = 0; sl < nsl; ++sl) {
         const int c0 = sl * per;
-        const int nc = std::min(per, a.NC - c0);
-        const bool first = sl == 0, last = sl == nsl - 1;
+        const int nc = std::max(0, std::min(per, a.NC - c0));
         if (nc > 0) {
-            IntraArgs ia{a.q, a.k, a.z, a.beta_raw, a.A_log, a.ws, a.T, a.H, a.NC, c0, nc, a.g_min, a.flags};
-            constexpr int NCH = 64 / C;  // chunks per intra workgroup
-            hipLaunchKernelGGL((kda_intra_kernel<T, DK, C>), dim3((unsigned)(BH * ((nc + NCH - 1) / NCH))), dim3(256), 0,
-                               stream, ia);
-            const hipError_t e = hipGetLastError();
+            const hipError_t e = cl.intra(a.ws, per, c0, nc, stream);
             if (e != hipSuccess) return e;
             if (!mark()) return hipErrorInvalidValue;
         }
-        ea.c0 = c0; ea.nc = std::max(nc, 0);
-        ea.S0 = first ? a.S0 : S_scr;
-        ea.M0 = first ? nullptr : M_scr;
-        ea.S_out = last ? a.S_out : S_scr;
-        ea.M_out = last ? a.M_out : M_scr;
-        hipLaunchKernelGGL(kern, dim3((unsigned)BH * ea.n_groups), dim3(64 * (NW + 2)), lds, stream, ea);
-        const hipError_t e = hipGetLastError();
+        const hipError_t e = cl.inter(a.ws, per, c0, nc, sl == 0, sl == nsl - 1, S_scr, M_scr, stream);
         if (e != hipSuccess) return e;
         if (!mark()) return hipErrorInvalidValue;
     }
@@ -857,6 +870,68 @@ int chunk_kernel_count(int elem_bytes, int DK, int C, int BH, int NC) {
     const BlockLayout L = block_layout(elem_bytes, DK, C);
     if (NC <= 0) return 1;
     const int per = slice_chunks(BH, NC, L.bytes);
+    return 2 * ((NC + per - 1) / per);
+}
+
+// Overlapped schedule over slices of the sequence: intra(s) on `s_main` writes
+// buffer s % 2; inter(s) on `aux` reads it after intra(s) and carries the state
+// to slice s + 1.  intra(s + 2) reuses the buffer once inter(s) is done.
+// Events: sync[b] = intra into buffer b done, sync[2 + b] = inter of buffer b
+// done, sync[4] = all inter work done (joined back into s_main).
+template <typename T, int DK, int C>
+static hipError_t launch_chunk_overlap_t(const ChunkArgs& a, hipStream_t s_main, hipStream_t aux, hipEvent_t* sync,
+                                         hipEvent_t* tev, int n_tev) {
+    ChunkLaunch<T, DK, C> cl(a);
+    const hipError_t attr = cl.set_attributes();
+    if (attr != hipSuccess) return attr;
+    const int BH = cl.BH;
+    const int per = overlap_slice_chunks(BH, a.NC, cl.L.bytes);
+    if (a.ws_bytes < chunk_workspace_bytes(sizeof(T), DK, a.Dv, C, (size_t)BH, (size_t)per, 2))
+        return hipErrorInvalidValue;
+    const size_t buf_bytes = (size_t)BH * per * cl.L.bytes;
+    unsigned char* ws = reinterpret_cast<unsigned char*>(a.ws);
+    float* S_scr = reinterpret_cast<float*>(ws + 2 * buf_bytes);
+    float* M_scr = S_scr + (size_t)BH * DK * a.Dv;
+    auto rec = [&](int idx, hipStream_t s) -> bool {
+        return !tev || idx >= n_tev || hipEventRecord(tev[idx], s) == hipSuccess;
+    };
+#define KDA_HIP(x) do { const hipError_t e_ = (x); if (e_ != hipSuccess) return e_; } while (0)
+    // the aux stream starts after everything already queued on the main stream
+    KDA_HIP(hipEventRecord(sync[4], s_main));
+    KDA_HIP(hipStreamWaitEvent(aux, sync[4], 0));
+    const int nsl = a.NC > 0 ? (a.NC + per - 1) / per : 1;
+    int k = 0;  // kernel index for the timing events
+    for (int sl = 0; sl < nsl; ++sl) {
+        const int c0 = sl * per;
+        const int nc = std::max(0, std::min(per, a.NC - c0));
+        const int b = sl & 1;
+        void* buf = ws + b * buf_bytes;
+        if (nc > 0) {
+            if (sl >= 2) KDA_HIP(hipStreamWaitEvent(s_main, sync[2 + b], 0));  // inter(sl - 2) has read buffer b
+            if (!rec(2 * k, s_main)) return hipErrorInvalidValue;
+            KDA_HIP(cl.intra(buf, per, c0, nc, s_main));
+            if (!rec(2 * k + 1, s_main)) return hipErrorInvalidValue;
+            ++k;
+            KDA_HIP(hipEventRecord(sync[b], s_main));
+            KDA_HIP(hipStreamWaitEvent(aux, sync[b], 0));
+        }
+        if (!rec(2 * k, aux)) return hipErrorInvalidValue;
+        KDA_HIP(cl.inter(buf, per, c0, nc, sl == 0, sl == nsl - 1, S_scr, M_scr, aux));
+        if (!rec(2 * k + 1, aux)) return hipErrorInvalidValue;
+        ++k;
+        KDA_HIP(hipEventRecord(sync[2 + b], aux));
+    }
+    // the main stream resumes after the last inter kernel
+    KDA_HIP(hipEventRecord(sync[4], aux));
+    KDA_HIP(hipStreamWaitEvent(s_main, sync[4], 0));
+#undef KDA_HIP
+    return hipSuccess;
+}
+
+int chunk_overlap_kernel_count(int elem_bytes, int DK, int C, int BH, int NC) {
+    const BlockLayout L = block_layout(elem_bytes, DK, C);
+    if (NC <= 0) return 1;
+    const int per = overlap_slice_chunks(BH, NC, L.bytes);
     return 2 * ((NC + per - 1) / per);
 }
 
@@ -883,6 +958,35 @@ static hipError_t launch_chunk_d(int DK, int C, const ChunkArgs& a, hipStream_t 
 
 hipError_t launch_chunk(int dt, int DK, int C, const ChunkArgs& a, hipStream_t s, hipEvent_t* ev, int n_ev) {
     return dt == 1 ? launch_chunk_d<bf16_t>(DK, C, a, s, ev, n_ev) : launch_chunk_d<float>(DK, C, a, s, ev, n_ev);
+}
+
+template <typename T, int DK>
+static hipError_t launch_overlap_c(int C, const ChunkArgs& a, hipStream_t s, hipStream_t aux, hipEvent_t* sync,
+                                   hipEvent_t* tev, int n_tev) {
+    switch (C) {
+        case 16: return launch_chunk_overlap_t<T, DK, 16>(a, s, aux, sync, tev, n_tev);
+        case 32: return launch_chunk_overlap_t<T, DK, 32>(a, s, aux, sync, tev, n_tev);
+        case 64: return launch_chunk_overlap_t<T, DK, 64>(a, s, aux, sync, tev, n_tev);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+static hipError_t launch_overlap_d(int DK, int C, const ChunkArgs& a, hipStream_t s, hipStream_t aux,
+                                   hipEvent_t* sync, hipEvent_t* tev, int n_tev) {
+    switch (DK) {
+        case 16: return launch_overlap_c<T, 16>(C, a, s, aux, sync, tev, n_tev);
+        case 32: return launch_overlap_c<T, 32>(C, a, s, aux, sync, tev, n_tev);
+        case 64: return launch_overlap_c<T, 64>(C, a, s, aux, sync, tev, n_tev);
+        case 128: return launch_overlap_c<T, 128>(C, a, s, aux, sync, tev, n_tev);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_chunk_overlap(int dt, int DK, int C, const ChunkArgs& a, hipStream_t s, hipStream_t aux,
+                                hipEvent_t* sync, hipEvent_t* tev, int n_tev) {
+    return dt == 1 ? launch_overlap_d<bf16_t>(DK, C, a, s, aux, sync, tev, n_tev)
+                   : launch_overlap_d<float>(DK, C, a, s, aux, sync, tev, n_tev);
 }
 
 }  // namespace kda

@@ -44,10 +44,38 @@ __host__ __device__ constexpr BlockLayout block_layout(int elem_bytes, int DK, i
     return L;
 }
 
-// Workspace: the chunk blocks of every (b, h, chunk), then the running state
-// carried between slices of the sequence (S [BH, Dk, Dv] and M [BH, Dk, Dk]).
-__host__ __device__ constexpr size_t chunk_workspace_bytes(int elem_bytes, int DK, int Dv, int C, size_t BH, size_t NC) {
-    return BH * NC * block_layout(elem_bytes, DK, C).bytes + round_up(BH * (size_t)DK * (DK + Dv) * 4, 256);
+// Chunks per slice of the sequence: intra and inter kernels alternate over
+// slices whose chunk blocks take at most kSliceBytes.  Measured on MI355X,
+// smaller slices (64-128 MB) lose more to partial grids and per-launch
+// prologues than they gain, so the layer-sized workloads run as one slice.
+constexpr size_t kSliceBytes = 1ull << 30;
+
+inline int slice_chunks(int BH, int NC, size_t block_bytes) {
+    if (NC <= 0) return 0;
+    size_t per = kSliceBytes / ((size_t)(BH > 0 ? BH : 1) * (block_bytes > 0 ? block_bytes : 1));
+    if (per < 1) per = 1;
+    const int nsl = (int)((NC + per - 1) / per);
+    return (NC + nsl - 1) / nsl;
+}
+
+// Slices of the overlapped schedule (intra of slice s + 1 runs beside inter of
+// slice s): two, of at least two chunks, within the slice budget.  Measured on
+// MI355X (layer workload), two slices gain about 9 % over one stream while
+// four or eight lose: every inter launch refills its LDS ring and reloads the
+// state, and the intra kernel only gets the CUs the inter kernel leaves free.
+inline int overlap_slice_chunks(int BH, int NC, size_t block_bytes) {
+    if (NC <= 0) return 0;
+    int per = (NC + 1) / 2;
+    if (per < 2) per = 2;
+    const int cap = slice_chunks(BH, NC, block_bytes);
+    return per < cap ? per : cap;
+}
+
+// Workspace: nbuf buffers of `per` chunk blocks for every (b, h), then the
+// running state carried between slices (S [BH, Dk, Dv] and M [BH, Dk, Dk]).
+__host__ __device__ constexpr size_t chunk_workspace_bytes(int elem_bytes, int DK, int Dv, int C, size_t BH,
+                                                           size_t per, size_t nbuf) {
+    return nbuf * BH * per * block_layout(elem_bytes, DK, C).bytes + round_up(BH * (size_t)DK * (DK + Dv) * 4, 256);
 }
 
 struct StepArgs {
@@ -60,7 +88,7 @@ struct ChunkArgs {
     const void* q; const void* k; const void* v; const void* z; const void* beta_raw;
     const float* A_log; const float* S0;
     void* o; float* S_out; float* M_out; void* P_out;
-    void* ws;
+    void* ws; size_t ws_bytes;
     int B, T, H, Dv, NC;
     float g_min; unsigned flags;
 };
@@ -75,9 +103,6 @@ struct FixupArgs {
     int n_seg, B, T_seg, H, Dv;
 };
 
-// Resident workgroups per CU for a kernel at this block size, and the CU
-// count of the current device (queried once and cached).
-
 // dt: 0 = fp32, 1 = bf16.  Return the launch status (hipSuccess on success).
 hipError_t launch_step(int dt, int DK, int DV, const StepArgs& a, hipStream_t s);
 // ev (nullable, n_ev events): ev[0] is recorded before the first kernel and
@@ -86,6 +111,12 @@ hipError_t launch_step(int dt, int DK, int DV, const StepArgs& a, hipStream_t s)
 hipError_t launch_chunk(int dt, int DK, int C, const ChunkArgs& a, hipStream_t s, hipEvent_t* ev, int n_ev);
 // Kernels one kda_chunk_fwd call launches for these sizes.
 int chunk_kernel_count(int elem_bytes, int DK, int C, int BH, int NC);
+// Overlapped schedule: intra kernels on `s`, inter kernels on `aux`; sync holds
+// 5 events (see kda_chunk_fwd_overlap); tev (nullable, n_tev) gets a start and
+// an end event per kernel k at 2k and 2k + 1, recorded on the kernel's stream.
+hipError_t launch_chunk_overlap(int dt, int DK, int C, const ChunkArgs& a, hipStream_t s, hipStream_t aux,
+                                hipEvent_t* sync, hipEvent_t* tev, int n_tev);
+int chunk_overlap_kernel_count(int elem_bytes, int DK, int C, int BH, int NC);
 hipError_t launch_compose(int DK, const ComposeArgs& a, hipStream_t s);
 hipError_t launch_fixup(int dt, int DK, const FixupArgs& a, hipStream_t s);
 

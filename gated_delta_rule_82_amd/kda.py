@@ -22,9 +22,11 @@ FLAGS_DEFAULT = 7
 
 EXPORTS = (
     "kda_safe_chunk_size", "kda_chunk_fwd_workspace", "kda_chunk_fwd", "kda_chunk_fwd_timed",
-    "kda_chunk_fwd_kernel_count", "kda_step",
+    "kda_chunk_fwd_kernel_count", "kda_chunk_fwd_overlap_workspace", "kda_chunk_fwd_overlap_kernel_count",
+    "kda_chunk_fwd_overlap", "kda_step",
     "kda_segment_compose", "kda_segment_fixup", "kda_status_string",
 )
+OVERLAP_SYNC_EVENTS = 5
 
 _lib = None
 
@@ -55,6 +57,12 @@ def load() -> ctypes.CDLL:
     L.kda_chunk_fwd_timed.restype = I
     L.kda_chunk_fwd_kernel_count.argtypes = [I] * 7
     L.kda_chunk_fwd_kernel_count.restype = I
+    L.kda_chunk_fwd_overlap_workspace.argtypes = [I] * 7
+    L.kda_chunk_fwd_overlap_workspace.restype = S
+    L.kda_chunk_fwd_overlap_kernel_count.argtypes = [I] * 7
+    L.kda_chunk_fwd_overlap_kernel_count.restype = I
+    L.kda_chunk_fwd_overlap.argtypes = [P] * 11 + [I] * 6 + [F, U, I, P, S, P, P, P, I, P, I]
+    L.kda_chunk_fwd_overlap.restype = I
     L.kda_step.argtypes = [P] * 8 + [I] * 4 + [F, U, I, P]
     L.kda_step.restype = I
     L.kda_segment_compose.argtypes = [I, P, P, P, P, I, I, I, I, P]
@@ -109,14 +117,42 @@ def kernel_count(B, T, H, Dk, Dv, chunk=64, dtype=torch.bfloat16) -> int:
     return load().kda_chunk_fwd_kernel_count(B, T, H, Dk, Dv, chunk, _dt(dtype))
 
 
+def overlap_workspace_bytes(B, T, H, Dk, Dv, chunk=64, dtype=torch.bfloat16) -> int:
+    return load().kda_chunk_fwd_overlap_workspace(B, T, H, Dk, Dv, chunk, _dt(dtype))
+
+
+def overlap_kernel_count(B, T, H, Dk, Dv, chunk=64, dtype=torch.bfloat16) -> int:
+    return load().kda_chunk_fwd_overlap_kernel_count(B, T, H, Dk, Dv, chunk, _dt(dtype))
+
+
+def _event_handles(events):
+    for e in events:
+        if e.cuda_event == 0:  # torch creates the HIP event on its first record
+            e.record()
+    return (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+
+
+class Overlap:
+    """The auxiliary stream and the synchronisation events of the overlapped
+    schedule (kda_chunk_fwd_overlap); reuse one per thread of calls."""
+
+    def __init__(self, device=None):
+        self.stream = torch.cuda.Stream(device=device)
+        self.sync = [torch.cuda.Event() for _ in range(OVERLAP_SYNC_EVENTS)]
+
+
 def chunk_fwd(q, k, v, z, beta_raw, A_log, S0=None, *, chunk=64, g_min=-5.0,
               flags=FLAGS_DEFAULT, want_M=False, want_P=False, o=None, S_out=None,
-              M_out=None, P_out=None, workspace=None, events=None):
+              M_out=None, P_out=None, workspace=None, events=None, overlap=None):
     """Chunkwise KDA forward.  Returns (o, S_out) plus M and/or P when asked.
 
-    `events` (optional): a list of at least kernel_count(...) + 1
-    torch.cuda.Event(enable_timing=True); the library records events[0] before
-    its first kernel and events[k + 1] after kernel k (kda_chunk_fwd_timed).
+    `events` (optional): a list of torch.cuda.Event(enable_timing=True).
+    Sequential schedule (kda_chunk_fwd_timed): at least kernel_count(...) + 1;
+    events[0] is recorded before the first kernel and events[k + 1] after
+    kernel k.  Overlapped schedule: at least 2 * overlap_kernel_count(...);
+    events 2k and 2k + 1 bracket kernel k on its own stream.
+    `overlap` (optional): an Overlap; runs kda_chunk_fwd_overlap, the intra
+    kernels of the next slice beside the inter kernel of the current one.
     """
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
@@ -130,20 +166,23 @@ def chunk_fwd(q, k, v, z, beta_raw, A_log, S0=None, *, chunk=64, g_min=-5.0,
         M_out = torch.empty(B, H, Dk, Dk, dtype=torch.float32, device=dev)
     if want_P and P_out is None:
         P_out = torch.empty(B, T, H, Dk, dtype=dt, device=dev)
-    need = workspace_bytes(B, T, H, Dk, Dv, chunk, dt)
+    need = (overlap_workspace_bytes if overlap is not None else workspace_bytes)(B, T, H, Dk, Dv, chunk, dt)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta_raw), _ptr(A_log), _ptr(S0),
             _ptr(o), _ptr(S_out), _ptr(M_out), _ptr(P_out),
             B, T, H, Dk, Dv, chunk, g_min, flags, _dt(dt),
             _ptr(workspace), workspace.numel(), _stream(dev))
-    if events is None:
+    if overlap is not None:
+        sync = _event_handles(overlap.sync)
+        evs = _event_handles(events) if events is not None else None
+        _check("kda_chunk_fwd_overlap",
+               load().kda_chunk_fwd_overlap(*args, overlap.stream.cuda_stream, sync, len(overlap.sync),
+                                            evs, len(events) if events is not None else 0))
+    elif events is None:
         _check("kda_chunk_fwd", load().kda_chunk_fwd(*args))
     else:
-        for e in events:
-            if e.cuda_event == 0:  # torch creates the HIP event on its first record
-                e.record()
-        evs = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+        evs = _event_handles(events)
         _check("kda_chunk_fwd_timed", load().kda_chunk_fwd_timed(*args, evs, len(events)))
     out = [o, S_out]
     if want_M:

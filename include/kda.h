@@ -100,8 +100,8 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
 
 /* Number of kernels one kda_chunk_fwd call launches for these sizes (0 for
  * invalid sizes).  The intra-chunk and inter-chunk kernels alternate over
- * slices of the sequence, so that a slice's intermediates are read back while
- * they are still in the GPU's last-level cache.  Host only. */
+ * slices of the sequence (one slice unless the per-chunk intermediates of
+ * the whole sequence exceed 1 GiB); the workspace holds one slice.  Host only. */
 int kda_chunk_fwd_kernel_count(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype dt);
 
 /* Same computation and validation as kda_chunk_fwd, for measurement: events[0]
@@ -117,6 +117,37 @@ kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, cons
                                float g_min, unsigned flags, kda_dtype dt,
                                void* workspace, size_t workspace_bytes, hipStream_t stream,
                                hipEvent_t* events, int n_events);
+
+/* The same computation as kda_chunk_fwd on two streams: the intra-chunk
+ * kernel of the next slice of the sequence runs on `stream` while the
+ * inter-chunk kernel of the current slice runs on `aux_stream` (the serial
+ * inter-chunk chain leaves most of the GPU idle).  The sequence is cut into
+ * two slices; the workspace holds both
+ * (kda_chunk_fwd_overlap_workspace).  Results equal kda_chunk_fwd's bit for
+ * bit.  Ordering: all work queued on `stream` before the call happens first,
+ * and work queued on `stream` after it sees every output.  `aux_stream` must
+ * not be used by anything else until that point.
+ *   sync_events    5 caller-created events (n_sync_events >= 5), used for the
+ *                  cross-stream dependencies; calls sharing them must not run
+ *                  concurrently.
+ *   timing_events  nullable: events 2k and 2k + 1 are recorded on the stream
+ *                  of kernel k just before and after it (kernels alternate
+ *                  intra, inter over the slices);
+ *                  n_timing_events >= 2 * kda_chunk_fwd_overlap_kernel_count().
+ * Returns KDA_OK, a validation error, or KDA_ERR_NULL for missing events. */
+size_t kda_chunk_fwd_overlap_workspace(int B, int T, int H, int Dk, int Dv, int chunk,
+                                       kda_dtype dt);
+int kda_chunk_fwd_overlap_kernel_count(int B, int T, int H, int Dk, int Dv, int chunk,
+                                       kda_dtype dt);
+kda_status kda_chunk_fwd_overlap(const void* q, const void* k, const void* v, const void* z,
+                                 const void* beta_raw, const float* A_log, const float* S0,
+                                 void* o, float* S_out, float* M_out, void* P_out,
+                                 int B, int T, int H, int Dk, int Dv, int chunk,
+                                 float g_min, unsigned flags, kda_dtype dt,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream, hipStream_t aux_stream,
+                                 hipEvent_t* sync_events, int n_sync_events,
+                                 hipEvent_t* timing_events, int n_timing_events);
 
 /* One decode step per (b,h), state updated IN PLACE ("KDA 模块交互式演示" §1.7
  * kda_step; "Implémenter KDA" reference step): decay, erase along k, write,

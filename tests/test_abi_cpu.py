@@ -123,3 +123,34 @@ def test_compose_and_fixup_validation(lib):
     assert lib.kda_segment_fixup(2, A16, None, None, A16, 1, 64, 1, 64, 64, 1, None) == 1
     assert lib.kda_segment_fixup(2, A16, None, A16, A16, 1, 64, 1, 64, 64, 9, None) == 4
     assert lib.kda_segment_fixup(1, A16, None, None, A16, 1, 0, 1, 64, 64, 1, None) == 0
+
+
+def test_overlap_workspace_and_counts(lib):
+    per = 64 * 1024 + 512   # bf16 D=128 C=64 block
+    carry = lambda bh, dk, dv: bh * dk * (dk + dv) * 4
+    # 64 chunks -> two slices of 32 chunks, two slice buffers
+    assert lib.kda_chunk_fwd_overlap_workspace(4, 4096, 16, 128, 128, 64, 1) == 2 * 64 * 32 * per + carry(64, 128, 128)
+    assert lib.kda_chunk_fwd_overlap_kernel_count(4, 4096, 16, 128, 128, 64, 1) == 4
+    # 3 chunks -> slices of at least 2 chunks
+    assert lib.kda_chunk_fwd_overlap_kernel_count(1, 130, 1, 128, 128, 64, 1) == 4
+    assert lib.kda_chunk_fwd_overlap_kernel_count(1, 0, 1, 128, 128, 64, 1) == 1
+    assert lib.kda_chunk_fwd_overlap_workspace(1, 64, 1, 96, 128, 64, 1) == 0
+    # the one-stream workspace holds one slice: the whole sequence when it fits
+    assert lib.kda_chunk_fwd_workspace(4, 4096, 16, 128, 128, 64, 1) == 64 * 64 * per + carry(64, 128, 128)
+
+
+def test_overlap_validation(lib):
+    sync = (ctypes.c_void_p * 5)(*([A16] * 5))
+    def call(**kw):
+        a = dict(q=A16, k=A16, v=A16, z=A16, beta_raw=A16, A_log=A16, S0=None, o=A16,
+                 S_out=None, M_out=None, P_out=None, B=1, T=64, H=1, Dk=64, Dv=64, chunk=64,
+                 g_min=-5.0, flags=7, dt=1, ws=None, ws_bytes=0, stream=None, aux=None,
+                 sync=sync, n_sync=5, timing=None, n_timing=0)
+        a.update(kw)
+        return lib.kda_chunk_fwd_overlap(*a.values())
+    assert call(sync=None) == 1
+    assert call(n_sync=4) == 1
+    assert call(dt=5) == 4
+    assert call(Dk=48) == 2
+    assert call(ws=None, ws_bytes=1 << 20) == 6
+    assert call(B=0) == 0

@@ -330,3 +330,46 @@ def test_sliced_sequence_matches_oracle():
                                       np64(inp["A_log"])[[h]])
         M_ref, _ = ora.segment_fragment(kh, np64(sub["v"][:, :, [h]]), g, beta)
         assert_close(M[b:b + 1, h:h + 1], M_ref, BF16, f"sliced M b{b} h{h}")
+
+
+# --------------------------------------------------- overlapped schedule
+
+@pytest.mark.parametrize("dtype,Dk,Dv,chunk,T,H,want", [
+    (BF16, 128, 128, 32, 1000, 3, False),
+    (BF16, 128, 128, 64, 700, 2, True),
+    (F32, 64, 64, 16, 333, 2, False),
+    (F32, 32, 128, 32, 64, 2, True),
+    (BF16, 128, 64, 32, 31, 2, False),
+])
+def test_overlap_equals_sequential(dtype, Dk, Dv, chunk, T, H, want):
+    """The two-stream schedule runs the same kernels on slices, carrying the
+    fp32 state exactly: its outputs equal the one-stream call bit for bit."""
+    inp = inputs.make_inputs(2, T, H, Dk, Dv, "bf16" if dtype == BF16 else "f32", seed=T + Dk, a_std=0.5, s_std=0.2)
+    ref = run_chunk(inp, chunk=chunk, want_M=want, want_P=want)
+    ov = kda.Overlap()
+    got = run_chunk(inp, chunk=chunk, want_M=want, want_P=want, overlap=ov)
+    assert kda.overlap_kernel_count(2, T, H, Dk, Dv, chunk, dtype) >= 2
+    for a_, b_ in zip(got, ref):
+        assert torch.equal(a_, b_)
+    o_ref, S_ref = oracle_forward(inp)
+    assert_close(got[0], o_ref, dtype, "overlap o")
+    assert_close(got[1], S_ref, dtype, "overlap S")
+
+
+def test_overlap_layer_workload_and_timing_events():
+    """Layer workload at chunk 32 (two slices): equal to the one-stream call,
+    repeatable with the same events, and the timing events bracket every kernel."""
+    w = inputs.WORKLOADS["layer"]
+    inp = inputs.make_workload(w)
+    d = to_dev(inp)
+    args = (d["q"], d["k"], d["v"], d["z"], d["beta_raw"], d["A_log"], None)
+    o_ref, S_ref = kda.chunk_fwd(*args, chunk=32)
+    ov = kda.Overlap()
+    nk = kda.overlap_kernel_count(w.B, w.T, w.H, w.Dk, w.Dv, 32, BF16)
+    assert nk == 4
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nk)]
+    for _ in range(2):
+        o, S = kda.chunk_fwd(*args, chunk=32, overlap=ov, events=evs)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
+    assert all(evs[2 * k].elapsed_time(evs[2 * k + 1]) > 0 for k in range(nk))
