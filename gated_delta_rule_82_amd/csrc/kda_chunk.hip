@@ -30,6 +30,7 @@
 // [e^-80, e^80].  Across blocks J < I the column factor is taken from the end
 // of block J and the gap between blocks is a per-channel scale <= 1.
 #include <algorithm>
+#include <atomic>
 
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -512,7 +513,10 @@ void kda_inter_kernel(const InterArgs a) {
             unsigned char* slot = slot_of(n);
             const unsigned char* gb = gblk + (size_t)(n - a.c0) * L.bytes;
             const unsigned char* vb = vrow0 + (size_t)n * C * tstride;
-            const int left = a.T - n * C;  // tokens of this chunk inside the sequence (>= 1)
+            // token rows to load: those of this chunk inside the sequence (>= 1);
+            // lanes past them (the chunk's tail, or a piece that spans more
+            // tokens than a chunk holds) reload the last row, zeroed or unused later
+            const uint32_t lim = (uint32_t)min(a.T - n * C, C);
 #pragma unroll
             for (int p = 0; p < Ring::kPieces; ++p) {
                 if (p % 2 != cw) continue;
@@ -525,7 +529,7 @@ void kda_inter_kernel(const InterArgs a) {
                 } else {
                     const int j = p - Ring::kBlkPieces;
                     uint32_t tok = (uint32_t)(j * kTokPerPiece) + vlane_tok;
-                    if (left < C) tok = tok < (uint32_t)left ? tok : (uint32_t)(left - 1);  // rows past the end are zeroed later
+                    tok = tok < lim ? tok : lim - 1;
                     __builtin_amdgcn_global_load_lds(
                         (const __attribute__((address_space(1))) void*)(vb + (tok * tstride + vlane_col)),
                         (__attribute__((address_space(3))) void*)(slot + L.bytes + j * 1024), 16, 0, 0);
@@ -782,19 +786,57 @@ void kda_inter_kernel(const InterArgs a) {
     }
 }
 
+// One instantiation of the inter kernel: NW compute waves of one strip each.
+template <typename T, int DK, int C, int NW>
+struct InterKernel {
+    using Ring = InterRing<T, DK, C, NW>;
+    static constexpr int kThreads = 64 * (NW + 2);
+    static constexpr size_t kLds = (size_t)Ring::kSlots * Ring::kSlot;
+    static const void* fn() { return reinterpret_cast<const void*>(kda_inter_kernel<T, DK, C, NW, 1>); }
+    static hipError_t set_attributes() {
+        // set on every call: the attribute is per device, and the call only records a limit
+        return hipFuncSetAttribute(fn(), hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+    }
+    // workgroups of this kernel resident on device `dev` at once (CUs times
+    // workgroups per CU), asked once per device; 0 when the runtime cannot say
+    static int capacity(int dev) {
+        constexpr int kMaxDev = 64;
+        static std::atomic<int> cache[kMaxDev];
+        if (dev < 0 || dev >= kMaxDev) return 0;
+        int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0) return v;
+        int cus = 0, per_cu = 0;
+        if (set_attributes() != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn(), kThreads, kLds) != hipSuccess)
+            return 0;
+        v = cus * per_cu;
+        cache[dev].store(v, std::memory_order_relaxed);
+        return v;
+    }
+    static hipError_t launch(const InterArgs& ea, int BH, hipStream_t s) {
+        hipLaunchKernelGGL((kda_inter_kernel<T, DK, C, NW, 1>), dim3((unsigned)BH * ea.n_groups), dim3(kThreads),
+                           kLds, s, ea);
+        return hipGetLastError();
+    }
+};
+
 // Launch configuration of the chunk kernels for one (T, DK, C).
+//
+// Compute waves per inter workgroup: the workgroups of one (b, h) all stream
+// the same chunk blocks, and each compute wave reads every block fragment from
+// LDS, so fewer waves per workgroup cost fewer LDS reads per strip but more
+// workgroups.  The launch takes the fewest waves (1, 2 or 4) whose grid is
+// resident on the device in one round; when none is, 4 (or fewer when the
+// strips of a (b, h) fit in fewer).
 template <typename T, int DK, int C>
 struct ChunkLaunch {
     static constexpr BlockLayout L = block_layout(sizeof(T), DK, C);
-    static constexpr int NW = 4;   // compute waves of the inter kernel, one 16-column strip each
-    static constexpr int SPW = 1;
-    static constexpr int NS = NW * SPW;
-    using Ring = InterRing<T, DK, C, NS>;
-    static constexpr size_t kLds = (size_t)Ring::kSlots * Ring::kSlot;
     static constexpr int NCH = 64 / C;  // chunks per intra workgroup
 
     const ChunkArgs& a;
     int BH;
+    int nw = 4;
     InterArgs ea{};
 
     explicit ChunkLaunch(const ChunkArgs& args) : a(args), BH(args.B * args.H) {
@@ -802,12 +844,24 @@ struct ChunkLaunch {
         ea.T = a.T; ea.H = a.H; ea.Dv = a.Dv;
         ea.n_m = (a.M_out || a.P_out) ? DK / 16 : 0;
         ea.n_strips = ea.n_m + a.Dv / 16;
-        ea.n_groups = (ea.n_strips + NS - 1) / NS;
+        int dev = -1;
+        if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+        const int caps[3] = {InterKernel<T, DK, C, 1>::capacity(dev), InterKernel<T, DK, C, 2>::capacity(dev),
+                             InterKernel<T, DK, C, 4>::capacity(dev)};
+        const int groups4 = (ea.n_strips + 3) / 4;
+        nw = 0;
+        for (int i = 0, w = 1; i < 3 && !nw; ++i, w *= 2)
+            if ((long long)BH * ((ea.n_strips + w - 1) / w) <= caps[i]) nw = w;
+        for (int w = 1; !nw; w *= 2)
+            if ((ea.n_strips + w - 1) / w == groups4) nw = w;
+        ea.n_groups = (ea.n_strips + nw - 1) / nw;
     }
-    static hipError_t set_attributes() {
-        // set on every call: the attribute is per device, and the call only records a limit
-        return hipFuncSetAttribute(reinterpret_cast<const void*>(kda_inter_kernel<T, DK, C, NW, SPW>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+    hipError_t set_attributes() const {
+        switch (nw) {
+            case 1: return InterKernel<T, DK, C, 1>::set_attributes();
+            case 2: return InterKernel<T, DK, C, 2>::set_attributes();
+            default: return InterKernel<T, DK, C, 4>::set_attributes();
+        }
     }
     // intra kernel over chunks [c0, c0 + nc) into the buffer `buf` of `per` chunks per (b, h)
     hipError_t intra(void* buf, int per, int c0, int nc, hipStream_t s) const {
@@ -825,9 +879,11 @@ struct ChunkLaunch {
         ea.M0 = first ? nullptr : M_scr;
         ea.S_out = last ? a.S_out : S_scr;
         ea.M_out = last ? a.M_out : M_scr;
-        hipLaunchKernelGGL((kda_inter_kernel<T, DK, C, NW, SPW>), dim3((unsigned)BH * ea.n_groups),
-                           dim3(64 * (NW + 2)), kLds, s, ea);
-        return hipGetLastError();
+        switch (nw) {
+            case 1: return InterKernel<T, DK, C, 1>::launch(ea, BH, s);
+            case 2: return InterKernel<T, DK, C, 2>::launch(ea, BH, s);
+            default: return InterKernel<T, DK, C, 4>::launch(ea, BH, s);
+        }
     }
 };
 

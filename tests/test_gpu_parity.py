@@ -332,6 +332,32 @@ def test_sliced_sequence_matches_oracle():
         assert_close(M[b:b + 1, h:h + 1], M_ref, BF16, f"sliced M b{b} h{h}")
 
 
+@pytest.mark.parametrize("dtype,B,H,want", [
+    (BF16, 2, 20, False), (BF16, 2, 48, False), (BF16, 1, 24, True), (BF16, 3, 16, True),
+    (F32, 2, 20, False), (F32, 2, 48, True),
+])
+def test_inter_wave_counts(dtype, B, H, want):
+    """Head counts spread over the inter kernel's 1, 2 and 4 compute waves per
+    workgroup (the launch takes the fewest waves whose grid is resident at
+    once: on 256 CUs with one workgroup each, 8 value strips per head give 1
+    wave up to 32 heads, 2 up to 64, else 4; the transition strips double the
+    strip count), each against the oracle on every head."""
+    inp = inputs.make_inputs(B, 45, H, 128, 128, "bf16" if dtype == BF16 else "f32", seed=B * H + want,
+                             a_std=0.5, s_std=0.2)
+    o, S, *MP = run_chunk(inp, chunk=32, want_M=want, want_P=want)
+    o_ref, S_ref = oracle_forward(inp)
+    assert_close(o, o_ref, dtype, f"waves B{B} H{H} o")
+    assert_close(S, S_ref, dtype, f"waves B{B} H{H} S")
+    if want:
+        M, P = MP
+        qh, kh, g, beta = ora.prepare(*(np64(inp[n]) for n in ("q", "k", "z", "beta_raw")), np64(inp["A_log"]))
+        M_ref, _ = ora.segment_fragment(kh, np64(inp["v"]), g, beta)
+        assert_close(M, M_ref, dtype, f"waves B{B} H{H} M")
+        o_zero, _ = ora.recurrent(qh, kh, np64(inp["v"]), g, beta, None)
+        o_fix = o_zero + np.einsum("bthk,bhkv->bthv", np64(P), np64(inp["S0"]))
+        assert_close(o_fix, o_ref, dtype, f"waves B{B} H{H} o(0) + P S0")
+
+
 # --------------------------------------------------- overlapped schedule
 
 @pytest.mark.parametrize("dtype,Dk,Dv,chunk,T,H,want", [
