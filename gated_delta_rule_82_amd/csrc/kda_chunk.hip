@@ -442,6 +442,15 @@ struct InterRing {
     static_assert(kVRow % 16 == 0 && 1024 % kVRow == 0, "value rows tile a piece");
 };
 
+// Contraction steps s of the token-block products with row block Ib that
+// touch the causal lower triangle (2 s <= Ib: step s spans blocks 2 s, 2 s + 1).
+constexpr int lower_steps(int nbk, int ksc) {
+    int t = 0;
+    for (int ib = 0; ib < nbk; ++ib)
+        for (int s = 0; s < ksc; ++s) t += (2 * s <= ib) ? 1 : 0;
+    return t;
+}
+
 // Wait until at most m chunks of this copy wave's pieces (P per chunk) are in
 // flight; loads complete in issue order.
 template <int P, int MAXM>
@@ -471,12 +480,19 @@ void kda_inter_kernel(const InterArgs a) {
     constexpr BlockLayout L = Ring::L;
     constexpr int K = Ring::kSlots;
     constexpr bool kAhead = K >= 3;  // next chunk's operands are read during the current one
-    constexpr bool kPinOrder = C <= 32 && sizeof(T) == 2;
+    // small bf16 blocks: the chunk's LDS reads are spread between its
+    // matrix-core products (see the end of the loop body)
+    constexpr bool kInterleave = C <= 32 && sizeof(T) == 2 && SPW == 1;
     constexpr int NBK = C / 16;
     constexpr int KSD = (DK + 31) / 32;
     constexpr int NBD = DK / 16;
     constexpr int KSC = (C + 31) / 32;
     extern __shared__ __align__(16) unsigned char s_raw[];
+    // per chunk and strip: products (R, U, S update, O) and LDS reads
+    // (KpT, gamma, Qp, Aqk, then Kd, Tb and the values of the next chunk)
+    constexpr int kTri = lower_steps(NBK, KSC);
+    constexpr int kMfmaPerChunk = NBK * KSD + kTri + NBD * KSC + NBK * KSD + kTri;
+    constexpr int kDsPerChunk = NBD * KSC + NBD + NBK * KSD + kTri + NBK * KSD + kTri + 4 * NBK;
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -604,13 +620,16 @@ void kda_inter_kernel(const InterArgs a) {
                     S[j][R][i] = (live[j] && mstrip[j] && 16 * R + 4 * gq + i == col) ? 1.f : 0.f;
         }
     }
+    // the state is in registers before the loop: inside it the only vector
+    // memory operations in flight are output stores, never waited for
+    wait_vmcnt<0>();
 
     using Raw = typename RawBits<T>::type;
     // outputs: a wave-uniform 64-bit base per strip and chunk plus 32-bit lane
     // offsets (token within the chunk times the token stride, plus the column)
     unsigned char* obase[SPW];
     uint32_t ostride[SPW];
-    uint32_t vlane[SPW];
+    uint32_t vlane[SPW], vmask[SPW];
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
         T* out = mstrip[j] ? reinterpret_cast<T*>(a.P_out) : reinterpret_cast<T*>(a.o);
@@ -620,7 +639,9 @@ void kda_inter_kernel(const InterArgs a) {
                                           (((size_t)b * a.T * a.H + h) * out_w + col0[j]) * sizeof(T)
                                     : nullptr;
         // byte offset of this lane's column within a staged value row
-        vlane[j] = (uint32_t)((col0[j] - vcol0 + r) * (int)sizeof(T));
+        // (strips without values read row 0 of the staging area and mask it)
+        vlane[j] = (live[j] && !mstrip[j]) ? (uint32_t)((col0[j] - vcol0 + r) * (int)sizeof(T)) : 0u;
+        vmask[j] = (live[j] && !mstrip[j]) ? 0xffffffffu : 0u;
     }
 
     // Operands on the serial path (Kd, Tb and the values of a chunk) live in
@@ -643,14 +664,12 @@ void kda_inter_kernel(const InterArgs a) {
                 if (2 * s <= Ib) frag_load(At[Ib][s], s_blk + L.tb + (size_t)(Ib * KSC + s) * 512, lane);
 #pragma unroll
         for (int j = 0; j < SPW; ++j) {
-            const bool use_v = live[j] && !mstrip[j];
 #pragma unroll
             for (int J = 0; J < NBK; ++J)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    Vraw[j][4 * J + i] = use_v ? (uint32_t)*reinterpret_cast<const Raw*>(
-                                                     s_val + (16 * J + 4 * gq + i) * Ring::kVRow + vlane[j])
-                                               : 0u;
+                    Vraw[j][4 * J + i] =
+                        (uint32_t)*reinterpret_cast<const Raw*>(s_val + (16 * J + 4 * gq + i) * Ring::kVRow + vlane[j]);
         }
     };
 
@@ -682,10 +701,6 @@ void kda_inter_kernel(const InterArgs a) {
                 for (int s = 0; s < KSC; ++s)
                     if (2 * s <= Ib) frag_load(Aa[Ib][s], s_blk + L.aqk + (size_t)(Ib * KSC + s) * 512, lane);
             }
-            // keep these reads ahead of the serial products (their latency hides
-            // behind R and U instead of stalling each product that uses them);
-            // larger blocks leave no registers for it
-            if constexpr (kPinOrder) __builtin_amdgcn_sched_barrier(0);
 
             // Operand copy of the incoming state.
             Frag<T> Sf[SPW][KSD];
@@ -699,18 +714,21 @@ void kda_inter_kernel(const InterArgs a) {
             Frag<T> Uf[SPW][KSC];
 #pragma unroll
             for (int j = 0; j < SPW; ++j) {
+                // the token blocks' product chains interleaved (independent
+                // products between dependent ones).  Rows past the end of the
+                // sequence hold finite copies of the last row: their U rows are
+                // zero (beta = 0 puts zeros in Tb's rows and columns for them)
                 floatx4 Rr[NBK];
 #pragma unroll
-                for (int J = 0; J < NBK; ++J) {
-                    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int J = 0; J < NBK; ++J) Rr[J] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int s = 0; s < KSD; ++s) acc = mma(Ak[J][s], Sf[j][s], acc);
+                for (int s = 0; s < KSD; ++s)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float x = RawBits<T>::to_float((Raw)Vraw[j][4 * J + i]);
-                        Rr[J][i] = ((full || n * C + 16 * J + 4 * gq + i < a.T) ? x : 0.f) - acc[i];
-                    }
-                }
+                    for (int J = 0; J < NBK; ++J) Rr[J] = mma(Ak[J][s], Sf[j][s], Rr[J]);
+#pragma unroll
+                for (int J = 0; J < NBK; ++J)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Rr[J][i] = RawBits<T>::to_float((Raw)(Vraw[j][4 * J + i] & vmask[j])) - Rr[J][i];
                 Frag<T> Rf[KSC];
 #pragma unroll
                 for (int s = 0; s < KSC; ++s)
@@ -738,32 +756,40 @@ void kda_inter_kernel(const InterArgs a) {
                     for (int s = 0; s < KSC; ++s) S[j][R] = mma(Ap[R][s], Uf[j][s], S[j][R]);
                 }
             // next chunk's serial operands, read while the output is computed
-            if (kAhead && n + 1 < cend) load_serial(n + 1);
-            if constexpr (kPinOrder) __builtin_amdgcn_sched_barrier(0);
-            // O = Qp S + Aqk U, stored
+            // (the last chunk reads its own slot again: no branch in the loop body)
+            if (kAhead) load_serial(n + 1 < cend ? n + 1 : n);
+            // O^T = S^T Qp^T + U^T Aqk^T, stored.  A B fragment of S or U is
+            // an A fragment of its transpose, and the A fragments of Qp and Aqk
+            // are B fragments of theirs, so swapping the operands gives O^T:
+            // lane (r, gq) holds value columns 4 gq .. 4 gq + 3 of token
+            // 16 Ib + r, one 4-element store per token block.
 #pragma unroll
             for (int j = 0; j < SPW; ++j) {
+                floatx4 acc[NBK];
 #pragma unroll
-                for (int Ib = 0; Ib < NBK; ++Ib) {
-                    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int Ib = 0; Ib < NBK; ++Ib) acc[Ib] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int s = 0; s < KSD; ++s) acc = mma(Aq[Ib][s], Sf[j][s], acc);
+                for (int s = 0; s < KSD; ++s)
 #pragma unroll
-                    for (int s = 0; s < KSC; ++s)
-                        if (2 * s <= Ib) acc = mma(Aa[Ib][s], Uf[j][s], acc);
-                    if (obase[j]) {
-                        unsigned char* ob = obase[j] + (size_t)n * C * ostride[j];
-                        const uint32_t o0 = (uint32_t)(16 * Ib + 4 * gq) * ostride[j] + (uint32_t)(r * (int)sizeof(T));
-                        if (full) {
+                    for (int Ib = 0; Ib < NBK; ++Ib) acc[Ib] = mma(Sf[j][s], Aq[Ib][s], acc[Ib]);
 #pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                *reinterpret_cast<T*>(ob + (o0 + (uint32_t)i * ostride[j])) = from_f<T>(acc[i]);
-                        } else {
+                for (int s = 0; s < KSC; ++s)
 #pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                if (n * C + 16 * Ib + 4 * gq + i < a.T)
-                                    *reinterpret_cast<T*>(ob + (o0 + (uint32_t)i * ostride[j])) = from_f<T>(acc[i]);
-                        }
+                    for (int Ib = 0; Ib < NBK; ++Ib)
+                        if (2 * s <= Ib) acc[Ib] = mma(Uf[j][s], Aa[Ib][s], acc[Ib]);
+                // one scheduling region from the loop top to here: issue the
+                // chunk's LDS reads (this chunk's S-update and output operands,
+                // then the next chunk's serial operands) between the products,
+                // so the LDS streams while the matrix core works
+                if constexpr (kInterleave) interleave_mfma_ds<kMfmaPerChunk, kDsPerChunk>();
+                if (obase[j]) {
+                    unsigned char* ob = obase[j] + (size_t)n * C * ostride[j];
+#pragma unroll
+                    for (int Ib = 0; Ib < NBK; ++Ib) {
+                        const int tok = 16 * Ib + r;
+                        if (full || n * C + tok < a.T)
+                            store4(reinterpret_cast<T*>(ob + ((uint32_t)tok * ostride[j] + (uint32_t)(4 * gq * (int)sizeof(T)))),
+                                   acc[Ib]);
                     }
                 }
             }

@@ -161,6 +161,16 @@ __device__ __forceinline__ void half_store(float* tile, int lane, int half, cons
     *reinterpret_cast<float4*>(tile + lane * 8 + half * 4) = make_float4(x[0], x[1], x[2], x[3]);
 }
 
+// Store 4 consecutive elements (one 8- or 16-byte store; p aligned to it).
+__device__ __forceinline__ void store4(bf16_t* p, const floatx4& x) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    const bf16x4 v = {(bf16_t)x[0], (bf16_t)x[1], (bf16_t)x[2], (bf16_t)x[3]};
+    *reinterpret_cast<bf16x4*>(p) = v;
+}
+__device__ __forceinline__ void store4(float* p, const floatx4& x) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+}
+
 // B fragment from two C-layout tiles stacked along the contraction axis.
 template <typename T>
 __device__ __forceinline__ Frag<T> frag_from_c(const floatx4& lo, const floatx4& hi) {
@@ -212,6 +222,18 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Scheduling pattern for the rest of the current scheduling region: M
+// matrix-core instructions, each followed by its even share of D LDS reads.
+template <int M, int D, int I = 0>
+__device__ __forceinline__ void interleave_mfma_ds() {
+    if constexpr (I < M) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        constexpr int nr = D * (I + 1) / M - D * I / M;
+        if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);  // nr DS reads
+        interleave_mfma_ds<M, D, I + 1>();
+    }
 }
 
 // Workgroup barrier without a memory fence: this wave's LDS operations are
