@@ -62,16 +62,42 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     constexpr int KSO = NBK > 1 ? KSD : 1;
     constexpr int NCH = 64 / C;  // chunks per workgroup: four waves of 16-token blocks
 
+    // bf16 inputs are staged through LDS: each wave copies its 16 token rows
+    // of q, k and z with whole-row requests (four 256-byte rows per
+    // instruction for DK = 128) instead of reading 32-byte pieces of every row
+    // from each of several register loads
+    constexpr bool kStage = sizeof(T) == 2;
+    constexpr int RB = DK * (int)sizeof(T);          // bytes of one token row of one tensor
+    constexpr int LPR = RB / 16;                     // 16-byte granules (DMA lanes) per row
+    constexpr int kStageWave = 3 * 16 * RB;          // q, k, z rows of one wave
+    constexpr int kStagePieces = (16 * RB + 1023) / 1024;  // 1 KiB copies per tensor and wave
+
     // per chunk of the workgroup:
     __shared__ __align__(16) float s_tot_all[NCH][NBK][DK];     // block totals of the log2 decay
-    __shared__ __align__(16) float s_eE_all[NCH][NBK][DK];      // exp2(E_I): chunk start to block entry
-    __shared__ __align__(16) float s_eLl_all[NCH][NBK][DK];     // exp2(Ll_I): decay over block I
-    __shared__ __align__(16) float s_eK_all[NCH][NBK][DK];      // exp2(G_C - E_I - Ll_I): block end to chunk end
-    __shared__ __align__(16) float s_pair_all[NCH][NPAIR][DK];  // exp2(E_I - E_{J+1}) <= 1 for J < I - 1
     __shared__ float s_beta_all[NCH][C];
-    __shared__ __align__(16) T s_offb_all[NCH][NOFF][KSO][512];  // column operands of off-diagonal blocks
-    __shared__ __align__(16) float s_akk_all[NCH][NPAIR][256];   // R layout of A_kk[I][J], J < I
-    __shared__ __align__(16) float s_tdiag_all[NCH][NBK][256];   // R layout of (I + A_kk[I][I])^-1
+    // phases B to E; the input staging of phase A shares their space (it is
+    // dead once phase A's barrier is passed)
+    struct PhaseArrays {
+        float eE[NCH][NBK][DK];      // exp2(E_I): chunk start to block entry
+        float eLl[NCH][NBK][DK];     // exp2(Ll_I): decay over block I
+        float eK[NCH][NBK][DK];      // exp2(G_C - E_I - Ll_I): block end to chunk end
+        float pair[NCH][NPAIR][DK];  // exp2(E_I - E_{J+1}) <= 1 for J < I - 1
+        T offb[NCH][NOFF][KSO][512]; // column operands of off-diagonal blocks
+        float akk[NCH][NPAIR][256];  // R layout of A_kk[I][J], J < I
+        float tdiag[NCH][NBK][256];  // R layout of (I + A_kk[I][I])^-1
+    };
+    union SharedPhases {
+        PhaseArrays ph;
+        unsigned char stage[kStage ? 4 * kStageWave : 16];
+    };
+    __shared__ __align__(16) SharedPhases sh;
+    auto& s_eE_all = sh.ph.eE;
+    auto& s_eLl_all = sh.ph.eLl;
+    auto& s_eK_all = sh.ph.eK;
+    auto& s_pair_all = sh.ph.pair;
+    auto& s_offb_all = sh.ph.offb;
+    auto& s_akk_all = sh.ph.akk;
+    auto& s_tdiag_all = sh.ph.tdiag;
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -81,8 +107,12 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     // workgroup: chunks [c0 + NCH g, c0 + NCH g + nsub) of (b, h); wave w owns
     // 16-token block I of chunk sub
     const int ncg = (a.nc + NCH - 1) / NCH;
-    const int g = (int)blockIdx.x % ncg;
-    const int bh = (int)blockIdx.x / ncg;
+    // head index fastest: the workgroups that run together read whole token
+    // rows of q, k and z (all heads of the same tokens)
+    const int hh = (int)blockIdx.x % a.H;
+    const int rest = (int)blockIdx.x / a.H;
+    const int g = rest % ncg;
+    const int bh = (rest / ncg) * a.H + hh;
     const int nsub = min(NCH, a.nc - g * NCH);
     const int sub = w / NBK;
     const int I = w % NBK;
@@ -118,6 +148,35 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     Raw4<T> qr[2 * KSD], kr[2 * KSD];  // q, k as loaded; slot j of step s is element j % 4 of [2 s + j / 4]
     float gv[NV];
     float beta = 0.f;
+    // staging of this wave: [tensor q, k, z][row rho][granule position], where
+    // position j of row rho holds granule j ^ (rho % LPR) of the token row (a
+    // swizzle that spreads the 16 rows read by one instruction over the banks)
+    unsigned char* stage = sh.stage + (kStage ? w * kStageWave : 0);
+    if constexpr (kStage) {
+        if (active) {
+            const unsigned char* srcs[3] = {reinterpret_cast<const unsigned char*>(a.q),
+                                            reinterpret_cast<const unsigned char*>(a.k),
+                                            reinterpret_cast<const unsigned char*>(a.z)};
+            const int rho = lane / LPR;       // row within a piece
+            const int jpos = lane % LPR;      // granule position written by this lane
+#pragma unroll
+            for (int p = 0; p < kStagePieces; ++p) {
+                const int rw = p * (1024 / RB) + rho;  // token row within the wave's 16
+                const int tr = n * C + 16 * I + (rw < 16 ? rw : 15);
+                const size_t grow = ((size_t)b * a.T + (tr < a.T ? tr : a.T - 1)) * a.H + h;
+                const uint32_t goff = (uint32_t)((jpos ^ (rw % LPR)) * 16);
+#pragma unroll
+                for (int tn = 0; tn < 3; ++tn) {
+                    if (rw < 16)
+                        __builtin_amdgcn_global_load_lds(
+                            (const __attribute__((address_space(1))) void*)(srcs[tn] + grow * RB + goff),
+                            (__attribute__((address_space(3))) void*)(stage + tn * 16 * RB + p * 1024), 16, 0, 0);
+                }
+            }
+            wait_vmcnt<0>();  // this wave's copies are in LDS (it reads only its own rows)
+            asm volatile("" ::: "memory");
+        }
+    }
 #pragma unroll
     for (int s = 0; s < KSD; ++s) {
 #pragma unroll
@@ -125,9 +184,21 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
             const int c = 32 * s + 16 * hf + 4 * gq;
             float* dz = &gv[8 * s + 4 * hf];
             if (active && (DK >= 32 || hf == 0)) {
-                qr[2 * s + hf].load(reinterpret_cast<const T*>(a.q) + row * DK + c);
-                kr[2 * s + hf].load(reinterpret_cast<const T*>(a.k) + row * DK + c);
-                load4(reinterpret_cast<const T*>(a.z) + row * DK + c, dz);
+                if constexpr (kStage) {
+                    // granule c / 8 of row r, 8 bytes at (c % 8) * 2 within it
+                    const int off = r * RB + (((c / 8) ^ (r % LPR)) * 16) + (c % 8) * 2;
+                    qr[2 * s + hf].v = *reinterpret_cast<const uint2*>(stage + off);
+                    kr[2 * s + hf].v = *reinterpret_cast<const uint2*>(stage + 16 * RB + off);
+                    const uint2 zz = *reinterpret_cast<const uint2*>(stage + 2 * 16 * RB + off);
+                    dz[0] = bf16_bits_to_float(zz.x & 0xffffu);
+                    dz[1] = bf16_bits_to_float(zz.x >> 16);
+                    dz[2] = bf16_bits_to_float(zz.y & 0xffffu);
+                    dz[3] = bf16_bits_to_float(zz.y >> 16);
+                } else {
+                    qr[2 * s + hf].load(reinterpret_cast<const T*>(a.q) + row * DK + c);
+                    kr[2 * s + hf].load(reinterpret_cast<const T*>(a.k) + row * DK + c);
+                    load4(reinterpret_cast<const T*>(a.z) + row * DK + c, dz);
+                }
             } else {
                 qr[2 * s + hf].zero();
                 kr[2 * s + hf].zero();
