@@ -494,20 +494,25 @@ constexpr size_t kLdsBudget = 160 * 1024;  // LDS per CU on gfx950
 // LDS ring of the inter-chunk kernel.  A slot holds one chunk block followed by
 // the chunk's values for the workgroup's NS = 16-column strips
 // ([C tokens][16 NS]).  Two copy waves fill the slots with global_load_lds,
-// 1 KiB per instruction ("piece"); copy wave c issues the pieces p with
-// p % 2 == c.
+// 1 KiB per instruction ("piece"); copy wave 0 issues the first kPer0 pieces
+// of a chunk, copy wave 1 the rest (each streams a contiguous half).
 template <typename T, int DK, int C, int NS>
 struct InterRing {
     static constexpr BlockLayout L = block_layout(sizeof(T), DK, C);
     static constexpr int kVRow = 16 * NS * (int)sizeof(T);   // bytes of one token's staged values
     static constexpr size_t kVBytes = round_up((size_t)C * kVRow, 1024);
     static constexpr size_t kSlot = L.bytes + kVBytes;
-    static constexpr int kSlots = kLdsBudget / kSlot >= 4 ? 4 : (int)(kLdsBudget / kSlot);
     static constexpr int kBlkPieces = (int)((L.bytes + 1023) / 1024);
     static constexpr int kVPieces = (int)(kVBytes / 1024);
     static constexpr int kPieces = kBlkPieces + kVPieces;
     static constexpr int kPer0 = (kPieces + 1) / 2;  // pieces per chunk of copy wave 0
     static constexpr int kPer1 = kPieces / 2;        // ... and of copy wave 1
+    // as many slots as fit, up to 6, with the copies in flight countable by
+    // vmcnt (at most kSlots - 2 chunks of one wave are waited over)
+    static constexpr int kSlotsLds = (int)(kLdsBudget / kSlot);
+    static constexpr int kSlotsVm = 2 + 63 / (kPer0 > 0 ? kPer0 : 1);
+    static constexpr int kSlots = kSlotsLds < 6 ? (kSlotsLds < kSlotsVm ? kSlotsLds : kSlotsVm)
+                                                : (6 < kSlotsVm ? 6 : kSlotsVm);
     static_assert(kSlots >= 1, "a chunk block must fit in LDS");
     static_assert(kSlots <= 2 || (kSlots - 2) * kPer0 < 64, "vmcnt range");
     static_assert(kVRow % 16 == 0 && 1024 % kVRow == 0, "value rows tile a piece");
@@ -526,6 +531,9 @@ constexpr int lower_steps(int nbk, int ksc) {
 // flight; loads complete in issue order.
 template <int P, int MAXM>
 __device__ __forceinline__ void wait_chunks(int m) {
+    if constexpr (MAXM >= 3) {
+        if (m >= 3) { wait_vmcnt<3 * P>(); return; }
+    }
     if constexpr (MAXM >= 2) {
         if (m >= 2) { wait_vmcnt<2 * P>(); return; }
     }
@@ -606,7 +614,7 @@ void kda_inter_kernel(const InterArgs a) {
             const uint32_t lim = (uint32_t)min(a.T - n * C, C);
 #pragma unroll
             for (int p = 0; p < Ring::kPieces; ++p) {
-                if (p % 2 != cw) continue;
+                if ((p < Ring::kPer0) != (cw == 0)) continue;
                 if (p < Ring::kBlkPieces) {
                     const int off = p * 1024 + lane * 16;
                     if (off < (int)L.bytes)
