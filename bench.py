@@ -10,9 +10,12 @@ sets (about 1.1 GB) rotate from step to step so the 256 MB Infinity Cache
 cannot serve them.  The call is kda_chunk_fwd on one stream (--overlap times
 the two-stream schedule kda_chunk_fwd_overlap instead).  The state chunk is a
 tiling choice of the kernels (results agree to rounding for 16, 32 and 64);
-32 is the fastest here.  The JSON line also reports, measured in the same run:
+32 is the fastest here.  The step time (value, ms_per_step) comes from the
+calls alone; the JSON line also reports, measured in the same run:
   * per-kernel times from HIP events the library records around each of its
-    kernels, and the roofline of the dominant kernel per launch;
+    kernels, over a second timed region of the same calls (the records add
+    GPU time between kernels: ms_per_step_with_kernel_events), and the
+    roofline of the dominant kernel per launch;
   * MFMA % of the whole call under both flop counts, HBM % on compulsory bytes;
   * the decode step (B=256, H=32, D=128, fp32 state) and its HBM %;
   * the long-context segmented flow (B=1, T=65536, H=32, 8 segments);
@@ -188,15 +191,26 @@ def bench_layer(torch, kda, inputs, steps, warmup, chunk=None, overlap=False):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
+    # timed region 1: the calls alone (the step time; no per-kernel events,
+    # whose records add GPU time between the kernels)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     start.record()
     for i in range(steps):
-        step(i, evs[i])
+        step(i)
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
+    # timed region 2: the same calls with the library recording an event
+    # around each of its kernels on the kernel's stream (per-launch durations)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
+    start2, end2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start2.record()
+    for i in range(steps):
+        step(i, evs[i])
+    end2.record()
+    torch.cuda.synchronize()
+    timed_ms = start2.elapsed_time(end2)
     # kernel k: intra for even k, inter for odd k (they alternate over the slices)
     if overlap:
         dur = lambda e, k: e[2 * k].elapsed_time(e[2 * k + 1])
@@ -207,6 +221,7 @@ def bench_layer(torch, kda, inputs, steps, warmup, chunk=None, overlap=False):
     return {"B": B, "T": T, "H": H, "Dk": Dk, "Dv": Dv, "C": C, "ws_bytes": ws_n,
             "schedule": "two streams, two slices" if overlap else "one stream",
             "ms_per_step": total_ms / steps,
+            "ms_per_step_with_kernel_events": timed_ms / steps,
             "kernel_ms": {k: sum(v) / steps for k, v in launches.items()},
             "launch_ms": {k: sum(v) / len(v) for k, v in launches.items()},
             "launches_per_step": {k: len(v) // steps for k, v in launches.items()}}
@@ -390,6 +405,7 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": round(bytes_per_launch),
                      "launch_ms": round(launch_ms, 4), "launches_per_step": n_launch},
         "kernel_ms": {k: round(v, 4) for k, v in L["kernel_ms"].items()},
+        "ms_per_step_with_kernel_events": round(L["ms_per_step_with_kernel_events"], 4),
         "mfma_frac": {"algorithmic": round(f_tri / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                       "tile_count": round(f_full / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
         "hbm_frac_compulsory": round(cbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
