@@ -37,6 +37,10 @@
 
 namespace kda {
 
+// cache policy of copies whose data is read once: non-temporal (the nt bit of
+// the gfx950 cache-policy operand)
+constexpr int kCopyNT = 2;
+
 struct IntraArgs {
     const void* q; const void* k; const void* z; const void* beta_raw;
     const float* A_log; void* ws;
@@ -170,7 +174,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
                     if (rw < 16)
                         __builtin_amdgcn_global_load_lds(
                             (const __attribute__((address_space(1))) void*)(srcs[tn] + grow * RB + goff),
-                            (__attribute__((address_space(3))) void*)(stage + tn * 16 * RB + p * 1024), 16, 0, 0);
+                            (__attribute__((address_space(3))) void*)(stage + tn * 16 * RB + p * 1024), 16, 0, kCopyNT);
                 }
             }
             wait_vmcnt<0>();  // this wave's copies are in LDS (it reads only its own rows)
@@ -502,6 +506,11 @@ struct InterRing {
     static constexpr int kVRow = 16 * NS * (int)sizeof(T);   // bytes of one token's staged values
     static constexpr size_t kVBytes = round_up((size_t)C * kVRow, 1024);
     static constexpr size_t kSlot = L.bytes + kVBytes;
+    // output staging: two tiles of [C tokens][16 NS] (chunk parity), so each
+    // output row leaves as one 16 NS-element segment instead of NS strips
+    static constexpr int kORow = 16 * NS * (int)sizeof(T);  // bytes of one token's output row
+    static constexpr size_t kOTile = (size_t)C * kORow;
+    static constexpr size_t kOBytes = 2 * kOTile;
     static constexpr int kBlkPieces = (int)((L.bytes + 1023) / 1024);
     static constexpr int kVPieces = (int)(kVBytes / 1024);
     static constexpr int kPieces = kBlkPieces + kVPieces;
@@ -509,13 +518,16 @@ struct InterRing {
     static constexpr int kPer1 = kPieces / 2;        // ... and of copy wave 1
     // as many slots as fit, up to 6, with the copies in flight countable by
     // vmcnt (at most kSlots - 2 chunks of one wave are waited over)
-    static constexpr int kSlotsLds = (int)(kLdsBudget / kSlot);
+    // (a configuration whose one slot and tiles exceed the LDS is never launched)
+    static constexpr bool kFits = kSlot + kOBytes <= kLdsBudget;
+    static constexpr int kSlotsLds = kFits ? (int)((kLdsBudget - kOBytes) / kSlot) : 1;
     static constexpr int kSlotsVm = 2 + 63 / (kPer0 > 0 ? kPer0 : 1);
     static constexpr int kSlots = kSlotsLds < 6 ? (kSlotsLds < kSlotsVm ? kSlotsLds : kSlotsVm)
                                                 : (6 < kSlotsVm ? 6 : kSlotsVm);
     static_assert(kSlots >= 1, "a chunk block must fit in LDS");
     static_assert(kSlots <= 2 || (kSlots - 2) * kPer0 < 64, "vmcnt range");
     static_assert(kVRow % 16 == 0 && 1024 % kVRow == 0, "value rows tile a piece");
+    static_assert(kORow % 16 == 0, "output rows are whole 16-byte granules");
 };
 
 // Contraction steps s of the token-block products with row block Ib that
@@ -627,7 +639,7 @@ void kda_inter_kernel(const InterArgs a) {
                     tok = tok < lim ? tok : lim - 1;
                     __builtin_amdgcn_global_load_lds(
                         (const __attribute__((address_space(1))) void*)(vb + (tok * tstride + vlane_col)),
-                        (__attribute__((address_space(3))) void*)(slot + L.bytes + j * 1024), 16, 0, 0);
+                        (__attribute__((address_space(3))) void*)(slot + L.bytes + j * 1024), 16, 0, kCopyNT);
                 }
             }
         };
@@ -704,24 +716,58 @@ void kda_inter_kernel(const InterArgs a) {
     wait_vmcnt<0>();
 
     using Raw = typename RawBits<T>::type;
-    // outputs: a wave-uniform 64-bit base per strip and chunk plus 32-bit lane
-    // offsets (token within the chunk times the token stride, plus the column)
-    unsigned char* obase[SPW];
-    uint32_t ostride[SPW];
     uint32_t vlane[SPW], vmask[SPW];
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
-        T* out = mstrip[j] ? reinterpret_cast<T*>(a.P_out) : reinterpret_cast<T*>(a.o);
-        const int out_w = mstrip[j] ? DK : a.Dv;
-        ostride[j] = (uint32_t)(a.H * out_w * (int)sizeof(T));  // bytes per token
-        obase[j] = (live[j] && out) ? reinterpret_cast<unsigned char*>(out) +
-                                          (((size_t)b * a.T * a.H + h) * out_w + col0[j]) * sizeof(T)
-                                    : nullptr;
         // byte offset of this lane's column within a staged value row
         // (strips without values read row 0 of the staging area and mask it)
         vlane[j] = (live[j] && !mstrip[j]) ? (uint32_t)((col0[j] - vcol0 + r) * (int)sizeof(T)) : 0u;
         vmask[j] = (live[j] && !mstrip[j]) ? 0xffffffffu : 0u;
     }
+
+    // Outputs leave through the staging tiles: compute wave w stores tokens
+    // [w C / NW, (w + 1) C / NW) of the previous chunk's tile, one 16-byte
+    // granule per lane and step.  Granule g of the wave's rows covers token
+    // g / kGpr, strip (g % kGpr) / kGps of the group, 16 bytes of it.
+    constexpr int kEpg = 16 / (int)sizeof(T);      // elements per granule
+    constexpr int kGps = 16 / kEpg;                // granules per strip row
+    constexpr int kGpr = NS * kGps;                // granules per token row
+    constexpr int kTpw = C / NW;                   // tokens stored per compute wave
+    constexpr int kOSteps = (kTpw * kGpr + 63) / 64;
+    unsigned char* s_otile = s_raw + (size_t)K * Ring::kSlot;
+    unsigned char* gbase[NS];   // per strip of the group: output row of token 0 (b, h), or null
+    uint32_t gstride[NS];       // bytes per token
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) {
+        const int strip = grp * NS + sl;
+        const bool ms = strip < a.n_m;
+        T* out = ms ? reinterpret_cast<T*>(a.P_out) : reinterpret_cast<T*>(a.o);
+        const int out_w = ms ? DK : a.Dv;
+        const int c0s = (ms ? strip : strip - a.n_m) * 16;
+        gstride[sl] = (uint32_t)(a.H * out_w * (int)sizeof(T));
+        gbase[sl] = (strip < a.n_strips && out)
+                        ? reinterpret_cast<unsigned char*>(out) + (((size_t)b * a.T * a.H + h) * out_w + c0s) * sizeof(T)
+                        : nullptr;
+    }
+    auto store_rows = [&](int m) {  // rows of chunk m's tile owned by this wave
+        const unsigned char* tile = s_otile + (size_t)((m - a.c0) & 1) * Ring::kOTile + (size_t)w * kTpw * Ring::kORow;
+#pragma unroll
+        for (int st = 0; st < kOSteps; ++st) {
+            const int gi = st * 64 + lane;
+            const int tok = w * kTpw + gi / kGpr;
+            const int sl = (gi % kGpr) / kGps;
+            const int part = gi % kGps;
+            unsigned char* base = nullptr;
+            uint32_t stride = 0;
+#pragma unroll
+            for (int t = 0; t < NS; ++t)
+                if (sl == t) { base = gbase[t]; stride = gstride[t]; }
+            if (gi < kTpw * kGpr && base && m * C + tok < a.T) {
+                const uint4 v = *reinterpret_cast<const uint4*>(tile + (size_t)gi * 16);
+                *reinterpret_cast<uint4*>(base + (size_t)m * C * stride + (uint32_t)tok * stride + (uint32_t)(part * 16)) = v;
+            }
+        }
+    };
 
     // Operands on the serial path (Kd, Tb and the values of a chunk) live in
     // registers from one chunk to the next: with kAhead they are read for
@@ -759,7 +805,6 @@ void kda_inter_kernel(const InterArgs a) {
         const unsigned char* cur = slot_of(n);
         const T* s_blk = reinterpret_cast<const T*>(cur);
         const float* s_gam = reinterpret_cast<const float*>(cur + L.gamma_byte);
-        const bool full = n * C + C <= a.T;
 
         if (any_live) {
             if (!kAhead) load_serial(n);
@@ -861,21 +906,20 @@ void kda_inter_kernel(const InterArgs a) {
                 // then the next chunk's serial operands) between the products,
                 // so the LDS streams while the matrix core works
                 if constexpr (kInterleave) interleave_mfma_ds<kMfmaPerChunk, kDsPerChunk>();
-                if (obase[j]) {
-                    unsigned char* ob = obase[j] + (size_t)n * C * ostride[j];
+                unsigned char* tile = s_otile + (size_t)((n - a.c0) & 1) * Ring::kOTile;
 #pragma unroll
-                    for (int Ib = 0; Ib < NBK; ++Ib) {
-                        const int tok = 16 * Ib + r;
-                        if (full || n * C + tok < a.T)
-                            store4(reinterpret_cast<T*>(ob + ((uint32_t)tok * ostride[j] + (uint32_t)(4 * gq * (int)sizeof(T)))),
-                                   acc[Ib]);
-                    }
-                }
+                for (int Ib = 0; Ib < NBK; ++Ib)
+                    store4(reinterpret_cast<T*>(tile + (size_t)(16 * Ib + r) * Ring::kORow +
+                                                (size_t)((w * SPW + j) * 16 + 4 * gq) * sizeof(T)),
+                           acc[Ib]);
             }
         }
+        // the previous chunk's outputs (its tile was completed before the last barrier)
+        if (n > a.c0) store_rows(n - 1);
         if (K == 1) lds_barrier();  // done reading the single slot
         lds_barrier();              // the next chunk(s) are in LDS
     }
+    if (a.nc > 0) store_rows(cend - 1);
 
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
@@ -896,7 +940,7 @@ template <typename T, int DK, int C, int NW>
 struct InterKernel {
     using Ring = InterRing<T, DK, C, NW>;
     static constexpr int kThreads = 64 * (NW + 2);
-    static constexpr size_t kLds = (size_t)Ring::kSlots * Ring::kSlot;
+    static constexpr size_t kLds = (size_t)Ring::kSlots * Ring::kSlot + Ring::kOBytes;
     static const void* fn() { return reinterpret_cast<const void*>(kda_inter_kernel<T, DK, C, NW, 1>); }
     static hipError_t set_attributes() {
         // set on every call: the attribute is per device, and the call only records a limit
@@ -907,7 +951,7 @@ struct InterKernel {
     static int capacity(int dev) {
         constexpr int kMaxDev = 64;
         static std::atomic<int> cache[kMaxDev];
-        if (dev < 0 || dev >= kMaxDev) return 0;
+        if (!Ring::kFits || dev < 0 || dev >= kMaxDev) return 0;
         int v = cache[dev].load(std::memory_order_relaxed);
         if (v > 0) return v;
         int cus = 0, per_cu = 0;
@@ -953,12 +997,18 @@ struct ChunkLaunch {
         if (hipGetDevice(&dev) != hipSuccess) dev = -1;
         const int caps[3] = {InterKernel<T, DK, C, 1>::capacity(dev), InterKernel<T, DK, C, 2>::capacity(dev),
                              InterKernel<T, DK, C, 4>::capacity(dev)};
-        const int groups4 = (ea.n_strips + 3) / 4;
+        const bool fits[3] = {InterKernel<T, DK, C, 1>::Ring::kFits, InterKernel<T, DK, C, 2>::Ring::kFits,
+                              InterKernel<T, DK, C, 4>::Ring::kFits};
         nw = 0;
         for (int i = 0, w = 1; i < 3 && !nw; ++i, w *= 2)
-            if ((long long)BH * ((ea.n_strips + w - 1) / w) <= caps[i]) nw = w;
-        for (int w = 1; !nw; w *= 2)
-            if ((ea.n_strips + w - 1) / w == groups4) nw = w;
+            if (fits[i] && (long long)BH * ((ea.n_strips + w - 1) / w) <= caps[i]) nw = w;
+        if (!nw) {  // no grid resident in one round: the fewest workgroups (fewest waves on a tie)
+            int best_g = 1 << 30;
+            for (int i = 0, w = 1; i < 3; ++i, w *= 2) {
+                const int g = (ea.n_strips + w - 1) / w;
+                if (fits[i] && g < best_g) { best_g = g; nw = w; }
+            }
+        }
         ea.n_groups = (ea.n_strips + nw - 1) / nw;
     }
     hipError_t set_attributes() const {

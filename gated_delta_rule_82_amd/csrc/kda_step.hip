@@ -1,39 +1,47 @@
 // kda_step.hip - single-token KDA decode on gfx950 ("KDA 模块交互式演示" §1.7
 // kda_step; "Implémenter KDA" 'La forme récurrente de référence').
 //
-// One workgroup per (b, h).  The fp32 state is streamed once from HBM into
-// registers and written back once; both reductions over Dk are taken from the
-// same pass, because with S' = Diag(alpha) S and u = beta (v - S'^T k):
+// One workgroup per (b, h) and group of DVW value columns (both reductions
+// run over Dk, column by column, so column groups are independent).  The
+// fp32 state is streamed once from HBM into registers and written back once;
+// both reductions are taken from the same pass, because with
+// S' = Diag(alpha) S and u = beta (v - S'^T k):
 //     S_new = S' + k u^T,     o = S_new^T q = S'^T q + u (k . q).
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, int DVW>
 __global__ __launch_bounds__(256) void kda_step_kernel(const StepArgs a) {
-    constexpr int CG = DV / 4;                         // float4 column groups
+    constexpr int NSPLIT = DV / DVW;                   // workgroups per (b, h)
+    constexpr int CG = DVW / 4;                        // float4 column groups
     constexpr int NT = (CG * DK < 256) ? CG * DK : 256;
     constexpr int RG = NT / CG;                        // row groups
     constexpr int RPT = DK / RG;                       // rows per thread
     constexpr int MC = (DK + 63) / 64;                 // channels per lane in the prep wave
 
     __shared__ float s_q[DK], s_k[DK], s_a[DK];
-    __shared__ __align__(16) float s_red[2][RG][DV];
+    __shared__ __align__(16) float s_red[2][RG][DVW];
     __shared__ float s_misc[2];
 
-    const int bh = blockIdx.x;
+    const int bh = blockIdx.x / NSPLIT;
+    const int col0 = (blockIdx.x % NSPLIT) * DVW;
     const int h = bh % a.H;
     const int tid = threadIdx.x;
     if (tid >= NT) return;  // NT is a multiple of 64; no thread past NT reaches a barrier
     const int cg = tid % CG;
     const int rg = tid / CG;
 
-    float* Sp = a.S + (size_t)bh * DK * DV;
+    float* Sp = a.S + (size_t)bh * DK * DV + col0;
+    // the state is touched once per step: non-temporal loads and stores
+    // (measured: 212 -> 195 us per B256 H32 D128 step, the loads carry it)
     float4 Sr[RPT];
 #pragma unroll
-    for (int m = 0; m < RPT; ++m)
-        Sr[m] = reinterpret_cast<const float4*>(Sp + (size_t)(rg + RG * m) * DV)[cg];
+    for (int m = 0; m < RPT; ++m) {
+        const floatx4 t = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(Sp + (size_t)(rg + RG * m) * DV) + cg);
+        Sr[m] = make_float4(t[0], t[1], t[2], t[3]);
+    }
 
     if (tid < 64) {
         const T* q = reinterpret_cast<const T*>(a.q) + (size_t)bh * DK;
@@ -107,14 +115,14 @@ __global__ __launch_bounds__(256) void kda_step_kernel(const StepArgs a) {
         ss.x += y.x; ss.y += y.y; ss.z += y.z; ss.w += y.w;
     }
     const float beta = s_misc[0], qk = s_misc[1];
-    const T* vp = reinterpret_cast<const T*>(a.v) + (size_t)bh * DV + 4 * cg;
+    const T* vp = reinterpret_cast<const T*>(a.v) + (size_t)bh * DV + col0 + 4 * cg;
     float4 u;
     u.x = beta * (to_f<T>(vp[0]) - rr.x);
     u.y = beta * (to_f<T>(vp[1]) - rr.y);
     u.z = beta * (to_f<T>(vp[2]) - rr.z);
     u.w = beta * (to_f<T>(vp[3]) - rr.w);
     if (rg == 0) {
-        T* op = reinterpret_cast<T*>(a.o) + (size_t)bh * DV + 4 * cg;
+        T* op = reinterpret_cast<T*>(a.o) + (size_t)bh * DV + col0 + 4 * cg;
         op[0] = from_f<T>(ss.x + u.x * qk);
         op[1] = from_f<T>(ss.y + u.y * qk);
         op[2] = from_f<T>(ss.z + u.z * qk);
@@ -126,15 +134,19 @@ __global__ __launch_bounds__(256) void kda_step_kernel(const StepArgs a) {
         const float kr = s_k[rw];
         float4 x = Sr[m];
         x.x += kr * u.x; x.y += kr * u.y; x.z += kr * u.z; x.w += kr * u.w;
-        reinterpret_cast<float4*>(Sp + (size_t)rw * DV)[cg] = x;
+        const floatx4 t = {x.x, x.y, x.z, x.w};
+        __builtin_nontemporal_store(t, reinterpret_cast<floatx4*>(Sp + (size_t)rw * DV) + cg);
     }
 }
 
+// Value columns per workgroup: 64 at most (Dv = 128 takes two workgroups per
+// (b, h): half the registers per thread, twice the workgroups in flight).
 template <typename T, int DK, int DV>
 static hipError_t launch_step_t(const StepArgs& a, hipStream_t s) {
-    constexpr int CG = DV / 4;
+    constexpr int DVW = DV > 64 ? 64 : DV;
+    constexpr int CG = DVW / 4;
     constexpr int NT = (CG * DK < 256) ? CG * DK : 256;
-    hipLaunchKernelGGL((kda_step_kernel<T, DK, DV>), dim3((unsigned)(a.B * a.H)), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((kda_step_kernel<T, DK, DV, DVW>), dim3((unsigned)(a.B * a.H * (DV / DVW))), dim3(NT), 0, s, a);
     return hipGetLastError();
 }
 

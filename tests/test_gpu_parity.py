@@ -332,17 +332,21 @@ def test_sliced_sequence_matches_oracle():
         assert_close(M[b:b + 1, h:h + 1], M_ref, BF16, f"sliced M b{b} h{h}")
 
 
-@pytest.mark.parametrize("dtype,B,H,want", [
-    (BF16, 2, 20, False), (BF16, 2, 48, False), (BF16, 1, 24, True), (BF16, 3, 16, True),
-    (F32, 2, 20, False), (F32, 2, 48, True),
+@pytest.mark.parametrize("dtype,B,H,want,Dk", [
+    (BF16, 2, 20, False, 128), (BF16, 2, 48, False, 128), (BF16, 1, 24, True, 128), (BF16, 3, 16, True, 128),
+    (F32, 2, 20, False, 128), (F32, 2, 48, True, 128), (BF16, 4, 48, True, 16), (F32, 4, 48, True, 16),
 ])
-def test_inter_wave_counts(dtype, B, H, want):
+def test_inter_wave_counts(dtype, B, H, want, Dk):
     """Head counts spread over the inter kernel's 1, 2 and 4 compute waves per
     workgroup (the launch takes the fewest waves whose grid is resident at
     once: on 256 CUs with one workgroup each, 8 value strips per head give 1
     wave up to 32 heads, 2 up to 64, else 4; the transition strips double the
-    strip count), each against the oracle on every head."""
-    inp = inputs.make_inputs(B, 45, H, 128, 128, "bf16" if dtype == BF16 else "f32", seed=B * H + want,
+    strip count), each against the oracle on every head.  With Dk = 16 the one
+    transition strip shares a workgroup's output rows with value strips; its
+    transition M decays to about 1e-4 of the identity over the 45 tokens, so in
+    bf16 (operands rounded to 2^-8 of entries that start near 1) M is held to
+    the bar only in the fp32 case, while o and o(0) + P S0 check the rows."""
+    inp = inputs.make_inputs(B, 45, H, Dk, 128, "bf16" if dtype == BF16 else "f32", seed=B * H + want,
                              a_std=0.5, s_std=0.2)
     o, S, *MP = run_chunk(inp, chunk=32, want_M=want, want_P=want)
     o_ref, S_ref = oracle_forward(inp)
@@ -352,7 +356,8 @@ def test_inter_wave_counts(dtype, B, H, want):
         M, P = MP
         qh, kh, g, beta = ora.prepare(*(np64(inp[n]) for n in ("q", "k", "z", "beta_raw")), np64(inp["A_log"]))
         M_ref, _ = ora.segment_fragment(kh, np64(inp["v"]), g, beta)
-        assert_close(M, M_ref, dtype, f"waves B{B} H{H} M")
+        if not (dtype == BF16 and Dk == 16):
+            assert_close(M, M_ref, dtype, f"waves B{B} H{H} M")
         o_zero, _ = ora.recurrent(qh, kh, np64(inp["v"]), g, beta, None)
         o_fix = o_zero + np.einsum("bthk,bhkv->bthv", np64(P), np64(inp["S0"]))
         assert_close(o_fix, o_ref, dtype, f"waves B{B} H{H} o(0) + P S0")
