@@ -283,3 +283,57 @@ def safe_chunk_size(g_min, dtype_max, headroom=2.0 ** 10):
         raise ValueError("g_min must be finite and negative")
     val = math.log(dtype_max / headroom) / (-g_min)
     return max(0, int(math.floor(val)))
+
+
+# ---------------------------------------------------------------------------
+# Input side of the layer: short convolution and SiLU
+# ([KDA-demo] §1.1 "ShortConv" and §1.7 "KimiDeltaAttention 完整层";
+#  [Impl-KDA] "La paramétrisation")
+# ---------------------------------------------------------------------------
+
+SHORT_CONV_KERNEL = 4  # [Impl-KDA] "La paramétrisation": short_conv(..., kernel=4)
+
+
+def short_conv(x, w, bias=None, state=None):
+    """Causal depthwise convolution over the token axis ([KDA-demo] §1.1):
+    each channel c mixes its own current and K - 1 previous inputs.
+
+    x is [B, T, C]; w is [C, K]; bias is [C] or None.  Tap j of channel c
+    multiplies x[t - (K - 1) + j, c], so tap K - 1 is the current token.  The
+    pages write the sum over lags with w[c, lag] but also state that setting
+    the LAST tap to 1 and the others to 0 makes the layer a no-op; only this
+    indexing (the causal conv1d convention) makes both true, and it is the
+    reading taken here.
+    state is [B, K - 1, C], the K - 1 inputs that precede t = 0 (oldest
+    first), or None for the pages' left zero padding ([KDA-demo] §1.1
+    因果性); it is how a sequence continues across calls and how the decode
+    step keeps its sliding window ([KDA-demo] §1.1 单步 decode).
+    Returns (y [B, T, C], state_out [B, K - 1, C]): state_out holds the last
+    K - 1 inputs of (state, x)."""
+    x = np.asarray(x, dtype=np.float64)
+    B, T, C = x.shape
+    w = np.asarray(w, dtype=np.float64)
+    K = w.shape[1]
+    prev = np.zeros((B, K - 1, C)) if state is None else np.asarray(state, dtype=np.float64)
+    xp = np.concatenate([prev, x], axis=1)  # row i of xp is token i - (K - 1)
+    y = np.zeros((B, T, C))
+    for t in range(T):
+        for j in range(K):
+            y[:, t] += w[:, j] * xp[:, t + j]
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float64)
+    return y, xp[:, T:].copy()
+
+
+def silu(x):
+    """SiLU (Swish) x * sigmoid(x) ([KDA-demo] §1.7; [Impl-KDA] swish)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x * sigmoid(x)
+
+
+def conv_silu(x, w, bias=None, state=None):
+    """SiLU(ShortConv(x)) for one of q, k, v ([KDA-demo] §1.7: the short
+    convolution first, then SiLU; the L2 norm of q and k follows inside the
+    core through its switch).  Returns (y, state_out) as short_conv."""
+    y, st = short_conv(x, w, bias, state)
+    return silu(y), st

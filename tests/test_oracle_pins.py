@@ -382,3 +382,96 @@ class TestSafeChunk:
         for bad in (0.0, 1.0, float("nan"), float("-inf")):
             with pytest.raises(ValueError):
                 ora.safe_chunk_size(bad, F32_MAX)
+
+
+# ---------------------------------------------------------------------------
+# Input side: short convolution and SiLU ([KDA-demo] §1.1, §1.7;
+# [Impl-KDA] "La paramétrisation")
+# ---------------------------------------------------------------------------
+
+class TestShortConv:
+    def test_identity_initialisation_is_a_no_op(self):
+        # [KDA-demo] §1.1: last tap 1, the others 0 -> the layer is a no-op
+        rng = np.random.default_rng(11)
+        x = rng.standard_normal((2, 9, 6))
+        w = np.zeros((6, 4))
+        w[:, -1] = 1.0
+        y, st = ora.short_conv(x, w)
+        assert np.array_equal(y, x)
+        assert np.array_equal(st, x[:, -3:])
+
+    def test_matches_numpy_convolution(self):
+        # causal correlation = full convolution with the reversed kernel,
+        # truncated to T (np.convolve zero-pads the past, as the pages do)
+        rng = np.random.default_rng(12)
+        B, T, C = 2, 13, 5
+        x = rng.standard_normal((B, T, C))
+        w = rng.standard_normal((C, 4))
+        bias = rng.standard_normal(C)
+        y, _ = ora.short_conv(x, w, bias)
+        for b in range(B):
+            for c in range(C):
+                ref = np.convolve(x[b, :, c], w[c, ::-1])[:T] + bias[c]
+                assert np.allclose(y[b, :, c], ref, rtol=0, atol=1e-12)
+
+    def test_shift_kernel_delays_by_three(self):
+        # only the first tap: y[t] = x[t - 3], zero for t < 3 (left zero padding)
+        rng = np.random.default_rng(13)
+        x = rng.standard_normal((1, 8, 3))
+        w = np.zeros((3, 4))
+        w[:, 0] = 1.0
+        y, _ = ora.short_conv(x, w)
+        assert np.array_equal(y[:, 3:], x[:, :-3])
+        assert np.array_equal(y[:, :3], np.zeros((1, 3, 3)))
+
+    @pytest.mark.parametrize("split", [1, 2, 3, 5, 9])
+    def test_state_continues_a_sequence(self, split):
+        # [KDA-demo] §1.1 单步 decode: the K - 1 input window carries the sequence
+        rng = np.random.default_rng(14 + split)
+        x = rng.standard_normal((2, 10, 4))
+        w = rng.standard_normal((4, 4))
+        s0 = rng.standard_normal((2, 3, 4))
+        y_full, st_full = ora.short_conv(x, w, None, s0)
+        y1, st1 = ora.short_conv(x[:, :split], w, None, s0)
+        y2, st2 = ora.short_conv(x[:, split:], w, None, st1)
+        assert np.allclose(np.concatenate([y1, y2], axis=1), y_full, rtol=0, atol=1e-13)
+        assert np.array_equal(st2, st_full)
+        # the window is the last three inputs of (state, x)
+        assert np.array_equal(st_full, np.concatenate([s0, x], axis=1)[:, -3:])
+
+    def test_token_by_token_window_equals_sequence(self):
+        rng = np.random.default_rng(21)
+        x = rng.standard_normal((1, 6, 2))
+        w = rng.standard_normal((2, 4))
+        y_full, _ = ora.short_conv(x, w)
+        st = None
+        for t in range(6):
+            y_t, st = ora.short_conv(x[:, t:t + 1], w, None, st)
+            assert np.allclose(y_t[:, 0], y_full[:, t], rtol=0, atol=1e-13)
+
+
+class TestSilu:
+    def test_odd_part_is_identity(self):
+        # x sigmoid(x) - (-x) sigmoid(-x) = x (sigmoid(x) + sigmoid(-x) = 1)
+        x = np.linspace(-30, 30, 601)
+        assert np.allclose(ora.silu(x) - ora.silu(-x), x, rtol=0, atol=1e-12)
+
+    def test_limits_and_zero(self):
+        assert ora.silu(np.array([0.0]))[0] == 0.0
+        assert abs(ora.silu(np.array([40.0]))[0] - 40.0) < 1e-12
+        assert abs(ora.silu(np.array([-40.0]))[0]) < 1e-15
+        # the minimum of x sigmoid(x) is at x* with x* = -(1 + e^{x*}) (d/dx = 0),
+        # about -1.2785: check against a dense grid
+        xs = np.linspace(-3, 0, 30001)
+        i = int(np.argmin(ora.silu(xs)))
+        assert abs(xs[i] + 1 + math.exp(xs[i])) < 2e-4
+
+    def test_conv_silu_composes_in_the_pages_order(self):
+        # [KDA-demo] §1.7: ShortConv first, then SiLU; with identity taps the
+        # composition is SiLU alone
+        rng = np.random.default_rng(22)
+        x = rng.standard_normal((1, 5, 3))
+        w = np.zeros((3, 4))
+        w[:, -1] = 1.0
+        y, _ = ora.conv_silu(x, w)
+        assert np.allclose(y, x / (1 + np.exp(-x)), rtol=1e-14, atol=0)
