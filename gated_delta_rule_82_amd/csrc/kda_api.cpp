@@ -33,6 +33,12 @@ kda_status need(const void* p) {
 }
 kda_status maybe(const void* p) { return (!p || aligned16(p)) ? KDA_OK : KDA_ERR_ALIGN; }
 
+// Byte ranges [a, a + na) and [b, b + nb) share a byte (both non-empty).
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return na > 0 && nb > 0 && x < y + nb && y < x + na;
+}
+
 #define KDA_TRY(expr)                        \
     do {                                     \
         const kda_status st_ = (expr);       \
@@ -219,6 +225,29 @@ kda_status kda_segment_fixup(int n_seg, const void* P, const float* S_in,
     kda::FixupArgs a{P, S_in, S_prefix, o, n_seg, B, T_seg, H, Dv};
     return kda::launch_fixup(dt == KDA_BF16 ? 1 : 0, Dk, a, stream) == hipSuccess ? KDA_OK
                                                                                   : KDA_ERR_HIP;
+}
+
+kda_status kda_short_conv(const void* x, const float* w, const float* bias,
+                          const void* state_in, void* state_out, void* y,
+                          int B, int T, int C, int silu, kda_dtype dt, hipStream_t stream) {
+    if (!dtype_ok(dt)) return KDA_ERR_DTYPE;
+    if (B < 0 || T < 0 || C < 0 || C % 8 != 0) return KDA_ERR_SHAPE;
+    if (B == 0 || C == 0 || (T == 0 && !state_out)) return KDA_OK;
+    KDA_TRY(need(w));
+    KDA_TRY(maybe(state_in)); KDA_TRY(maybe(state_out));
+    if (T > 0) { KDA_TRY(need(x)); KDA_TRY(need(y)); }
+    const size_t eb = (size_t)elem_bytes(dt);
+    const size_t xb = T > 0 ? (size_t)B * T * C * eb : 0, sb = (size_t)B * 3 * C * eb;
+    // workgroups of different token tiles read x (and the window) while others
+    // write y and the window out: no overlap, except the window updated in
+    // place by a call whose tokens fit one tile
+    if (overlaps(x, xb, y, xb)) return KDA_ERR_SHAPE;
+    if (state_out && (overlaps(state_out, sb, x, xb) || overlaps(state_out, sb, y, xb))) return KDA_ERR_SHAPE;
+    if (state_in && state_out && overlaps(state_in, sb, state_out, sb) &&
+        (state_in != state_out || T > kda::short_conv_tile()))
+        return KDA_ERR_SHAPE;
+    kda::ShortConvArgs a{x, w, bias, state_in, state_out, y, B, T, C, silu ? 1 : 0};
+    return kda::launch_short_conv(dt == KDA_BF16 ? 1 : 0, a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 const char* kda_status_string(kda_status s) {

@@ -120,4 +120,13 @@ int chunk_overlap_kernel_count(int elem_bytes, int DK, int C, int BH, int NC);
 hipError_t launch_compose(int DK, const ComposeArgs& a, hipStream_t s);
 hipError_t launch_fixup(int dt, int DK, const FixupArgs& a, hipStream_t s);
 
+// Input side: causal short convolution (kernel 4) and SiLU over [B, T, C].
+struct ShortConvArgs {
+    const void* x; const float* w; const float* bias;
+    const void* state_in; void* state_out; void* y;
+    int B, T, C, silu;
+};
+int short_conv_tile();  // tokens per thread; an in-place window needs T <= this
+hipError_t launch_short_conv(int dt, const ShortConvArgs& a, hipStream_t s);
+
 }  // namespace kda

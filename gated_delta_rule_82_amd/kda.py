@@ -24,7 +24,7 @@ EXPORTS = (
     "kda_safe_chunk_size", "kda_chunk_fwd_workspace", "kda_chunk_fwd", "kda_chunk_fwd_timed",
     "kda_chunk_fwd_kernel_count", "kda_chunk_fwd_overlap_workspace", "kda_chunk_fwd_overlap_kernel_count",
     "kda_chunk_fwd_overlap", "kda_step",
-    "kda_segment_compose", "kda_segment_fixup", "kda_status_string",
+    "kda_segment_compose", "kda_segment_fixup", "kda_short_conv", "kda_status_string",
 )
 OVERLAP_SYNC_EVENTS = 5
 
@@ -69,6 +69,8 @@ def load() -> ctypes.CDLL:
     L.kda_segment_compose.restype = I
     L.kda_segment_fixup.argtypes = [I, P, P, P, P, I, I, I, I, I, I, P]
     L.kda_segment_fixup.restype = I
+    L.kda_short_conv.argtypes = [P] * 6 + [I] * 5 + [P]
+    L.kda_short_conv.restype = I
     L.kda_status_string.argtypes = [I]
     L.kda_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -224,3 +226,22 @@ def segment_fixup(P, S_prefix, o, S_in=None):
                                   H, Dk, Dv, _dt(P.dtype), _stream(P.device))
     _check("kda_segment_fixup", st)
     return o
+
+
+def short_conv(x, w, bias=None, *, state_in=None, state_out=None, silu=True, y=None):
+    """y = SiLU(ShortConv(x)) (silu=False: the convolution alone) for x [B,T,C]
+    (or [B,T,H,D], flattened to C = H*D); w [C,4] fp32 (tap 3 is the current
+    token), bias [C] fp32 or None.  state_in / state_out [B,3,C] in x's dtype
+    carry the last three inputs between calls (state_out may be state_in when
+    T <= 32).  Returns y shaped like x."""
+    shape = x.shape
+    B, T = shape[0], shape[1]
+    C = 1
+    for d in shape[2:]:
+        C *= d
+    if y is None:
+        y = torch.empty_like(x)
+    st = load().kda_short_conv(_ptr(x), _ptr(w), _ptr(bias), _ptr(state_in), _ptr(state_out), _ptr(y),
+                               B, T, C, 1 if silu else 0, _dt(x.dtype), _stream(x.device))
+    _check("kda_short_conv", st)
+    return y

@@ -179,6 +179,33 @@ kda_status kda_segment_fixup(int n_seg, const void* P, const float* S_in,
                              const float* S_prefix, void* o, int B, int T_seg,
                              int H, int Dk, int Dv, kda_dtype dt, hipStream_t stream);
 
+/* The layer's input side for one of q, k, v ("KDA 模块交互式演示" §1.1
+ * ShortConv and §1.7 完整层; "Implémenter KDA" 'La paramétrisation'): a causal
+ * depthwise convolution of kernel 4 over the token axis, then SiLU when silu
+ * is non-zero:
+ *   y[b,t,c] = act(bias[c] + sum_{j=0..3} w[c,j] * x[b, t-3+j, c]).
+ * Tap 3 multiplies the current token, so w[c] = (0,0,0,1) with no bias is the
+ * identity the pages initialise to.
+ *   x, y       [B,T,C] device, dtype dt, token-major (C = heads * head dim,
+ *              the q/k/v layout above), C a multiple of 8; y must not
+ *              overlap x.
+ *   w          [C,4] fp32 device; bias [C] fp32 device or NULL (zero).
+ *   state_in   [B,3,C] dtype dt device, the three inputs before t = 0, oldest
+ *              first (a previous call's state_out), or NULL (zeros: the
+ *              sequence starts here).
+ *   state_out  [B,3,C] dtype dt device or NULL: receives the last three
+ *              inputs of (state_in, x), the window the next call or the next
+ *              decode token continues from.  It must not overlap x or y, and
+ *              may be state_in itself (updated in place) only when T <= 32;
+ *              otherwise it must not overlap state_in.
+ * T = 0 copies state_in (or zeros) to state_out.  Errors: KDA_ERR_DTYPE,
+ * KDA_ERR_SHAPE (negative size, C % 8, a forbidden overlap), KDA_ERR_NULL /
+ * KDA_ERR_ALIGN (x, y, w, states: present and 16-byte aligned as required),
+ * KDA_ERR_HIP.  Nothing is enqueued when an argument is rejected. */
+kda_status kda_short_conv(const void* x, const float* w, const float* bias,
+                          const void* state_in, void* state_out, void* y,
+                          int B, int T, int C, int silu, kda_dtype dt, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* kda_status_string(kda_status s);
 

@@ -154,3 +154,27 @@ def test_overlap_validation(lib):
     assert call(Dk=48) == 2
     assert call(ws=None, ws_bytes=1 << 20) == 6
     assert call(B=0) == 0
+
+
+def test_short_conv_validation(lib):
+    # fake, never dereferenced device addresses: every call below is rejected
+    # (or is a no-op) before anything is enqueued
+    X, Y, S1, S2, W = 1 << 40, 1 << 41, 1 << 42, 1 << 43, 1 << 44
+
+    def call(**kw):
+        a = dict(x=X, w=W, bias=None, state_in=None, state_out=None, y=Y,
+                 B=2, T=64, C=256, silu=1, dt=1, stream=None)
+        a.update(kw)
+        return lib.kda_short_conv(*a.values())
+    assert call(dt=7) == 4
+    assert call(C=12) == 2                      # C not a multiple of 8
+    assert call(T=-1) == 2
+    assert call(w=None) == 1
+    assert call(x=None) == 1
+    assert call(y=X + 16) == 2                  # y overlaps x
+    assert call(x=X + 8) == 3                   # misaligned
+    assert call(state_in=S1, state_out=S1) == 2                 # in place with T > 32
+    assert call(state_in=S1, state_out=S1 + 16, T=8) == 2       # partial overlap
+    assert call(state_out=X + 64) == 2                          # window over the input
+    assert call(B=0) == 0
+    assert call(T=0, x=None, y=None) == 0       # nothing to write
