@@ -19,6 +19,8 @@ calls alone; the JSON line also reports, measured in the same run:
   * MFMA % of the whole call under both flop counts, HBM % on compulsory bytes;
   * the decode step (B=256, H=32, D=128, fp32 state) and its HBM %;
   * the long-context segmented flow (B=1, T=65536, H=32, 8 segments);
+  * the layer's input side (SiLU of the kernel-4 short convolution of q, k, v)
+    and its HBM %, alone and followed by the core;
   * the fp64 oracle timed on the host cores on a bounded sample.
 Only the JSON line goes to stdout; progress goes to stderr.
 """
@@ -257,6 +259,65 @@ def bench_decode(torch, kda, inputs, steps, warmup):
             "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
 
 
+def bench_input_side(torch, kda, inputs, steps, warmup, chunk):
+    """The layer's input side on the layer workload: SiLU(ShortConv(.)) of q, k
+    and v (kernel 4, [B, T, H*D] bf16 each), then the same call with the core
+    after it.  Algorithmic bytes of one convolution: its input read once and
+    its output written once (the three-row halo of each 32-token tile is not
+    counted)."""
+    w = inputs.WORKLOADS["layer"]
+    dev = torch.device("cuda:0")
+    B, T, H, Dk, Dv = w.B, w.T, w.H, w.Dk, w.Dv
+    base = inputs.make_workload(w)
+    gen = torch.Generator(device=dev)
+    sets = [{n: base[n].to(dev) for n in ("q", "k", "v", "z", "beta_raw")}]
+    for i in range(1, 4):
+        gen.manual_seed(w.seed * 100 + 50 + i)
+        sets.append({n: torch.randn(*base[n].shape, generator=gen, device=dev).to(torch.bfloat16)
+                     for n in ("q", "k", "v", "z", "beta_raw")})
+    A = base["A_log"].to(dev)
+    gen.manual_seed(w.seed * 100 + 99)
+    cw = {n: (torch.randn(H * (Dv if n == "v" else Dk), 4, generator=gen, device=dev) * 0.5).float()
+          for n in ("q", "k", "v")}
+    cb = {n: (torch.randn(cw[n].shape[0], generator=gen, device=dev) * 0.1).float() for n in ("q", "k", "v")}
+    outs = {n: torch.empty_like(sets[0][n]) for n in ("q", "k", "v")}
+    o = torch.empty(B, T, H, Dv, dtype=torch.bfloat16, device=dev)
+    S = torch.empty(B, H, Dk, Dv, dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.workspace_bytes(B, T, H, Dk, Dv, chunk, torch.bfloat16), dtype=torch.uint8, device=dev)
+
+    def convs(i):
+        s = sets[i % len(sets)]
+        for n in ("q", "k", "v"):
+            kda.short_conv(s[n], cw[n], cb[n], silu=True, y=outs[n])
+
+    def full(i):
+        convs(i)
+        s = sets[i % len(sets)]
+        kda.chunk_fwd(outs["q"], outs["k"], outs["v"], s["z"], s["beta_raw"], A, None, chunk=chunk,
+                      o=o, S_out=S, workspace=ws)
+
+    res = {}
+    for name, fn in (("convs", convs), ("input_side_and_core", full)):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / steps
+    conv_bytes = 3 * 2 * B * T * H * Dk * 2
+    return {"workload": "input side of the layer workload: SiLU(ShortConv_4(.)) of q, k, v "
+                        "(B4 T4096, 16 x 128 channels each, bf16), then kda_chunk_fwd (chunk %d)" % chunk,
+            "convs_us": round(res["convs"] * 1e3, 2),
+            "convs_hbm_gbs": round(conv_bytes / (res["convs"] / 1e3) / 1e9, 1),
+            "convs_hbm_frac": round(conv_bytes / (res["convs"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "input_side_and_core_ms": round(res["input_side_and_core"], 4),
+            "input_side_and_core_tokens_per_s": B * T / (res["input_side_and_core"] / 1e3)}
+
+
 def bench_long(torch, kda, inputs, reps, chunk):
     w = inputs.WORKLOADS["long"]
     dev = torch.device("cuda:0")
@@ -383,6 +444,9 @@ def main():
         log("[bench] long workload ...")
         extra["long"] = bench_long(torch, kda, inputs, args.long_reps, C)
         log(f"[bench] long {extra['long']}")
+        log("[bench] input side ...")
+        extra["input_side"] = bench_input_side(torch, kda, inputs, args.steps, args.warmup, C)
+        log(f"[bench] input side {extra['input_side']}")
 
     out = {
         "metric": METRIC,
