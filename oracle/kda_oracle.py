@@ -337,3 +337,30 @@ def conv_silu(x, w, bias=None, state=None):
     core through its switch).  Returns (y, state_out) as short_conv."""
     y, st = short_conv(x, w, bias, state)
     return silu(y), st
+
+
+# ---------------------------------------------------------------------------
+# Output side of the layer: per-head RMS normalisation and sigmoid gate
+# ([KDA-demo] §1.7 "KimiDeltaAttention 完整层" last line; [Impl-KDA] "La porte
+# de sortie de rang plein", kda_output without its final projection)
+# ---------------------------------------------------------------------------
+
+RMS_EPS = 1e-6  # the pages give none; the same epsilon as the L2 norm
+
+
+def head_rms_norm(o, weight=None, eps=RMS_EPS):
+    """o / sqrt(mean(o^2) + eps) over each head's Dv channels (the last axis),
+    times an optional per-channel weight [Dv] shared by the heads
+    ([Impl-KDA] kda_output: RMSNorm par tête)."""
+    o = np.asarray(o, dtype=np.float64)
+    y = o / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    if weight is not None:
+        y = y * np.asarray(weight, dtype=np.float64)
+    return y
+
+
+def output_gate(o, gate, weight=None, eps=RMS_EPS):
+    """sigmoid(gate) * HeadRMSNorm(o): the full-rank output gate applied to the
+    normalised heads, before the output projection ([KDA-demo] §1.7;
+    [Impl-KDA] kda_output).  o and gate are [B, T, H, Dv]."""
+    return sigmoid(gate) * head_rms_norm(o, weight, eps)

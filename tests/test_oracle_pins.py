@@ -475,3 +475,38 @@ class TestSilu:
         w[:, -1] = 1.0
         y, _ = ora.conv_silu(x, w)
         assert np.allclose(y, x / (1 + np.exp(-x)), rtol=1e-14, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# Output side: per-head RMS normalisation and sigmoid gate ([KDA-demo] §1.7;
+# [Impl-KDA] kda_output)
+# ---------------------------------------------------------------------------
+
+class TestOutputGate:
+    def test_rms_of_normalised_head_is_one(self):
+        rng = np.random.default_rng(31)
+        o = rng.standard_normal((2, 5, 3, 64)) * 7.0
+        y = ora.head_rms_norm(o, eps=0.0)
+        assert np.allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, rtol=0, atol=1e-13)
+
+    def test_scale_invariance_and_constant_head(self):
+        rng = np.random.default_rng(32)
+        o = rng.standard_normal((1, 4, 2, 32))
+        assert np.allclose(ora.head_rms_norm(5.0 * o, eps=0.0), ora.head_rms_norm(o, eps=0.0), rtol=0, atol=1e-13)
+        # a head of equal entries c normalises to sign(c) * 1 (eps -> 0)
+        c = np.full((1, 1, 1, 16), -3.0)
+        assert np.allclose(ora.head_rms_norm(c, eps=0.0), -1.0, rtol=0, atol=1e-15)
+        # eps keeps a zero head at zero
+        assert np.array_equal(ora.head_rms_norm(np.zeros((1, 1, 1, 8))), np.zeros((1, 1, 1, 8)))
+
+    def test_gate_limits_and_weight(self):
+        rng = np.random.default_rng(33)
+        o = rng.standard_normal((1, 3, 2, 16))
+        w = rng.standard_normal(16)
+        n = ora.head_rms_norm(o, w, eps=0.0)
+        # gate logit 0 halves, large positive passes, large negative closes
+        assert np.allclose(ora.output_gate(o, np.zeros_like(o), w, eps=0.0), 0.5 * n, rtol=0, atol=1e-14)
+        assert np.allclose(ora.output_gate(o, np.full_like(o, 60.0), w, eps=0.0), n, rtol=0, atol=1e-13)
+        assert np.max(np.abs(ora.output_gate(o, np.full_like(o, -60.0), w, eps=0.0))) < 1e-24
+        # the weight multiplies channels after the normalisation
+        assert np.allclose(n, ora.head_rms_norm(o, eps=0.0) * w, rtol=0, atol=1e-14)
