@@ -250,6 +250,21 @@ kda_status kda_short_conv(const void* x, const float* w, const float* bias,
     return kda::launch_short_conv(dt == KDA_BF16 ? 1 : 0, a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+kda_status kda_output_gate(const void* o, const void* gate, const float* weight, void* y,
+                           int B, int T, int H, int Dv, kda_dtype dt, hipStream_t stream) {
+    if (!dtype_ok(dt)) return KDA_ERR_DTYPE;
+    if (B < 0 || T < 0 || H < 0 || !dim_ok(Dv)) return KDA_ERR_SHAPE;
+    const size_t rows = (size_t)B * T * H;
+    if (rows == 0) return KDA_OK;
+    KDA_TRY(need(o)); KDA_TRY(need(gate)); KDA_TRY(need(y));
+    // each element is read before it is written, so y may be o or gate
+    // itself, but not a shifted view of either
+    const size_t nb = rows * Dv * (size_t)elem_bytes(dt);
+    if ((y != o && overlaps(y, nb, o, nb)) || (y != gate && overlaps(y, nb, gate, nb))) return KDA_ERR_SHAPE;
+    kda::GateArgs a{o, gate, weight, y, rows};
+    return kda::launch_output_gate(dt == KDA_BF16 ? 1 : 0, Dv, a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 const char* kda_status_string(kda_status s) {
     switch (s) {
         case KDA_OK: return "ok";

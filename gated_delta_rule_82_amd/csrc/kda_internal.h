@@ -129,4 +129,11 @@ struct ShortConvArgs {
 int short_conv_tile();  // tokens per thread; an in-place window needs T <= this
 hipError_t launch_short_conv(int dt, const ShortConvArgs& a, hipStream_t s);
 
+// Output side: per-head RMS normalisation under a sigmoid gate, rows of DV.
+struct GateArgs {
+    const void* o; const void* gate; const float* weight; void* y;
+    size_t rows;
+};
+hipError_t launch_output_gate(int dt, int DV, const GateArgs& a, hipStream_t s);
+
 }  // namespace kda

@@ -24,7 +24,7 @@ EXPORTS = (
     "kda_safe_chunk_size", "kda_chunk_fwd_workspace", "kda_chunk_fwd", "kda_chunk_fwd_timed",
     "kda_chunk_fwd_kernel_count", "kda_chunk_fwd_overlap_workspace", "kda_chunk_fwd_overlap_kernel_count",
     "kda_chunk_fwd_overlap", "kda_step",
-    "kda_segment_compose", "kda_segment_fixup", "kda_short_conv", "kda_status_string",
+    "kda_segment_compose", "kda_segment_fixup", "kda_short_conv", "kda_output_gate", "kda_status_string",
 )
 OVERLAP_SYNC_EVENTS = 5
 
@@ -71,6 +71,8 @@ def load() -> ctypes.CDLL:
     L.kda_segment_fixup.restype = I
     L.kda_short_conv.argtypes = [P] * 6 + [I] * 5 + [P]
     L.kda_short_conv.restype = I
+    L.kda_output_gate.argtypes = [P] * 4 + [I] * 5 + [P]
+    L.kda_output_gate.restype = I
     L.kda_status_string.argtypes = [I]
     L.kda_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -244,4 +246,16 @@ def short_conv(x, w, bias=None, *, state_in=None, state_out=None, silu=True, y=N
     st = load().kda_short_conv(_ptr(x), _ptr(w), _ptr(bias), _ptr(state_in), _ptr(state_out), _ptr(y),
                                B, T, C, 1 if silu else 0, _dt(x.dtype), _stream(x.device))
     _check("kda_short_conv", st)
+    return y
+
+
+def output_gate(o, gate, weight=None, *, y=None):
+    """y = sigmoid(gate) * HeadRMSNorm(o) * weight for o, gate [B,T,H,Dv];
+    weight [Dv] fp32 or None.  y may be o or gate (in place)."""
+    B, T, H, Dv = o.shape
+    if y is None:
+        y = torch.empty_like(o)
+    st = load().kda_output_gate(_ptr(o), _ptr(gate), _ptr(weight), _ptr(y), B, T, H, Dv,
+                                _dt(o.dtype), _stream(o.device))
+    _check("kda_output_gate", st)
     return y

@@ -206,6 +206,20 @@ kda_status kda_short_conv(const void* x, const float* w, const float* bias,
                           const void* state_in, void* state_out, void* y,
                           int B, int T, int C, int silu, kda_dtype dt, hipStream_t stream);
 
+/* The layer's output side before its projection ("KDA 模块交互式演示" §1.7
+ * 完整层; "Implémenter KDA" 'La porte de sortie de rang plein', kda_output):
+ * per (b,t,h), over the head's Dv channels,
+ *   y = sigmoid(gate) * o / sqrt(mean(o^2) + 1e-6) * weight[c].
+ *   o, gate, y  [B,T,H,Dv] device, dtype dt; y may be o or gate itself (in
+ *               place) but must not otherwise overlap them.
+ *   weight      [Dv] fp32 device, shared by the heads, or NULL (ones).
+ * Dv in {16,32,64,128}.  Errors: KDA_ERR_DTYPE, KDA_ERR_SHAPE (sizes, a
+ * forbidden overlap), KDA_ERR_NULL / KDA_ERR_ALIGN (o, gate, y present and
+ * 16-byte aligned), KDA_ERR_HIP.  Nothing is enqueued when an argument is
+ * rejected. */
+kda_status kda_output_gate(const void* o, const void* gate, const float* weight, void* y,
+                           int B, int T, int H, int Dv, kda_dtype dt, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* kda_status_string(kda_status s);
 

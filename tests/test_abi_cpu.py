@@ -178,3 +178,19 @@ def test_short_conv_validation(lib):
     assert call(state_out=X + 64) == 2                          # window over the input
     assert call(B=0) == 0
     assert call(T=0, x=None, y=None) == 0       # nothing to write
+
+
+def test_output_gate_validation(lib):
+    O, G, Y = 1 << 40, 1 << 41, 1 << 42
+
+    def call(**kw):
+        a = dict(o=O, gate=G, weight=None, y=Y, B=2, T=8, H=4, Dv=128, dt=1, stream=None)
+        a.update(kw)
+        return lib.kda_output_gate(*a.values())
+    assert call(dt=5) == 4
+    assert call(Dv=48) == 2
+    assert call(H=-1) == 2
+    assert call(gate=None) == 1
+    assert call(y=Y + 8) == 3
+    assert call(y=O + 256) == 2      # a shifted view of o
+    assert call(T=0, o=None, gate=None, y=None) == 0

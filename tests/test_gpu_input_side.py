@@ -139,3 +139,47 @@ def test_input_side_then_core_matches_oracle(dtype):
     o_ref, S_ref = oracle_forward(ref_in)
     assert_close(o, o_ref, dtype, "input side + core o")
     assert_close(S, S_ref, dtype, "input side + core S")
+
+
+# --------------------------------------------------------------- output side
+
+def gate_case(B, T, H, Dv, dtype, seed, weight=True):
+    g = torch.Generator().manual_seed(seed)
+    o = (torch.randn(B, T, H, Dv, generator=g) * 3.0).to(dtype)
+    gate = (torch.randn(B, T, H, Dv, generator=g) * 2.0).to(dtype)
+    w = (torch.rand(Dv, generator=g) + 0.5).float() if weight else None
+    return o, gate, w
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("B,T,H,Dv", [(1, 1, 1, 16), (2, 33, 3, 32), (2, 17, 5, 64), (1, 70, 4, 128), (3, 5, 7, 128)])
+@pytest.mark.parametrize("weight", [True, False])
+def test_output_gate_matches_oracle(dtype, B, T, H, Dv, weight):
+    o, gate, w = gate_case(B, T, H, Dv, dtype, seed=B + 7 * T + 13 * H + Dv, weight=weight)
+    y = kda.output_gate(o.cuda(), gate.cuda(), None if w is None else w.cuda())
+    torch.cuda.synchronize()
+    ref = ora.output_gate(np64(o), np64(gate), np64(w))
+    assert_close(y.cpu(), ref, dtype, f"gate B{B} T{T} H{H} Dv{Dv}")
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_output_gate_in_place(dtype):
+    o, gate, w = gate_case(2, 40, 4, 128, dtype, seed=3)
+    ref = kda.output_gate(o.cuda(), gate.cuda(), w.cuda())
+    buf = o.cuda().clone()
+    kda.output_gate(buf, gate.cuda(), w.cuda(), y=buf)
+    gbuf = gate.cuda().clone()
+    kda.output_gate(o.cuda(), gbuf, w.cuda(), y=gbuf)
+    torch.cuda.synchronize()
+    assert torch.equal(buf, ref) and torch.equal(gbuf, ref)
+
+
+def test_output_gate_zero_head_and_layer_tensor():
+    # a zero head stays zero (the epsilon), and one layer-sized output
+    o, gate, w = gate_case(4, 4096, 16, 128, BF16, seed=5)
+    o[0, 0, 0] = 0
+    y = kda.output_gate(o.cuda(), gate.cuda(), w.cuda())
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y[0, 0, 0]) == 0
+    ref = ora.output_gate(np64(o), np64(gate), np64(w))
+    assert_close(y.cpu(), ref, BF16, "gate layer tensor")
