@@ -19,8 +19,9 @@ calls alone; the JSON line also reports, measured in the same run:
   * MFMA % of the whole call under both flop counts, HBM % on compulsory bytes;
   * the decode step (B=256, H=32, D=128, fp32 state) and its HBM %;
   * the long-context segmented flow (B=1, T=65536, H=32, 8 segments);
-  * the layer's input side (SiLU of the kernel-4 short convolution of q, k, v)
-    and its HBM %, alone and followed by the core;
+  * the layer body around the core: the input side (SiLU of the kernel-4
+    short convolution of q, k, v), the output side (sigmoid gate times per-head
+    RMS norm), each with its HBM %, and input side + core + output side;
   * the fp64 oracle timed on the host cores on a bounded sample.
 Only the JSON line goes to stdout; progress goes to stderr.
 """
@@ -259,12 +260,14 @@ def bench_decode(torch, kda, inputs, steps, warmup):
             "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
 
 
-def bench_input_side(torch, kda, inputs, steps, warmup, chunk):
-    """The layer's input side on the layer workload: SiLU(ShortConv(.)) of q, k
-    and v (kernel 4, [B, T, H*D] bf16 each), then the same call with the core
-    after it.  Algorithmic bytes of one convolution: its input read once and
-    its output written once (the three-row halo of each 32-token tile is not
-    counted)."""
+def bench_layer_body(torch, kda, inputs, steps, warmup, chunk):
+    """The layer's body around the core on the layer workload: SiLU(ShortConv(.))
+    of q, k and v (kernel 4, [B, T, H*D] bf16 each); those then the core; the
+    output side (sigmoid gate times per-head RMS norm) alone; and all three in a
+    row (the layer without its projections).  Algorithmic bytes: each
+    convolution reads its input and writes its output once (the three-row
+    halo of each 32-token tile is not counted); the output side reads o and
+    the gate and writes y once."""
     w = inputs.WORKLOADS["layer"]
     dev = torch.device("cuda:0")
     B, T, H, Dk, Dv = w.B, w.T, w.H, w.Dk, w.Dv
@@ -281,6 +284,9 @@ def bench_input_side(torch, kda, inputs, steps, warmup, chunk):
           for n in ("q", "k", "v")}
     cb = {n: (torch.randn(cw[n].shape[0], generator=gen, device=dev) * 0.1).float() for n in ("q", "k", "v")}
     outs = {n: torch.empty_like(sets[0][n]) for n in ("q", "k", "v")}
+    gates = [torch.randn(B, T, H, Dv, generator=gen, device=dev).to(torch.bfloat16) for _ in range(2)]
+    gw = (torch.rand(Dv, generator=gen, device=dev) + 0.5).float()
+    y = torch.empty(B, T, H, Dv, dtype=torch.bfloat16, device=dev)
     o = torch.empty(B, T, H, Dv, dtype=torch.bfloat16, device=dev)
     S = torch.empty(B, H, Dk, Dv, dtype=torch.float32, device=dev)
     ws = torch.empty(kda.workspace_bytes(B, T, H, Dk, Dv, chunk, torch.bfloat16), dtype=torch.uint8, device=dev)
@@ -296,8 +302,15 @@ def bench_input_side(torch, kda, inputs, steps, warmup, chunk):
         kda.chunk_fwd(outs["q"], outs["k"], outs["v"], s["z"], s["beta_raw"], A, None, chunk=chunk,
                       o=o, S_out=S, workspace=ws)
 
+    def gate(i):
+        kda.output_gate(o, gates[i % 2], gw, y=y)
+
+    def body(i):
+        full(i)
+        gate(i)
+
     res = {}
-    for name, fn in (("convs", convs), ("input_side_and_core", full)):
+    for name, fn in (("convs", convs), ("input_side_and_core", full), ("output_gate", gate), ("body", body)):
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
@@ -309,13 +322,18 @@ def bench_input_side(torch, kda, inputs, steps, warmup, chunk):
         torch.cuda.synchronize()
         res[name] = e0.elapsed_time(e1) / steps
     conv_bytes = 3 * 2 * B * T * H * Dk * 2
-    return {"workload": "input side of the layer workload: SiLU(ShortConv_4(.)) of q, k, v "
-                        "(B4 T4096, 16 x 128 channels each, bf16), then kda_chunk_fwd (chunk %d)" % chunk,
+    gate_bytes = 3 * B * T * H * Dv * 2   # o and the gate read, y written
+    return {"workload": "layer workload body: SiLU(ShortConv_4(.)) of q, k, v (B4 T4096, 16 x 128 channels "
+                        "each, bf16), kda_chunk_fwd (chunk %d), sigmoid(gate) * HeadRMSNorm(o)" % chunk,
             "convs_us": round(res["convs"] * 1e3, 2),
             "convs_hbm_gbs": round(conv_bytes / (res["convs"] / 1e3) / 1e9, 1),
             "convs_hbm_frac": round(conv_bytes / (res["convs"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
             "input_side_and_core_ms": round(res["input_side_and_core"], 4),
-            "input_side_and_core_tokens_per_s": B * T / (res["input_side_and_core"] / 1e3)}
+            "input_side_and_core_tokens_per_s": B * T / (res["input_side_and_core"] / 1e3),
+            "output_gate_us": round(res["output_gate"] * 1e3, 2),
+            "output_gate_hbm_frac": round(gate_bytes / (res["output_gate"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "layer_body_ms": round(res["body"], 4),
+            "layer_body_tokens_per_s": B * T / (res["body"] / 1e3)}
 
 
 def bench_long(torch, kda, inputs, reps, chunk):
@@ -445,8 +463,8 @@ def main():
         extra["long"] = bench_long(torch, kda, inputs, args.long_reps, C)
         log(f"[bench] long {extra['long']}")
         log("[bench] input side ...")
-        extra["input_side"] = bench_input_side(torch, kda, inputs, args.steps, args.warmup, C)
-        log(f"[bench] input side {extra['input_side']}")
+        extra["layer_body"] = bench_layer_body(torch, kda, inputs, args.steps, args.warmup, C)
+        log(f"[bench] layer body {extra['layer_body']}")
 
     out = {
         "metric": METRIC,
