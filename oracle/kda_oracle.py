@@ -364,3 +364,52 @@ def output_gate(o, gate, weight=None, eps=RMS_EPS):
     normalised heads, before the output projection ([KDA-demo] §1.7;
     [Impl-KDA] kda_output).  o and gate are [B, T, H, Dv]."""
     return sigmoid(gate) * head_rms_norm(o, weight, eps)
+
+
+# ---------------------------------------------------------------------------
+# Variants: grouped value heads and a per-dimension gate bias
+# ([KDA-layer] "完整数据流": q, k [B, T, H, K] against v, g, beta [B, T, HV, ...],
+#  A_log [HV] and dt_bias [HV, K] in its parameter table)
+# ---------------------------------------------------------------------------
+
+def group_heads(x, HV):
+    """Give each of the HV value heads its q/k head: value head hv reads head
+    hv // (HV // H) of x [B, T, H, D] (consecutive groups; the pages fix the
+    shapes, not the assignment, and this is the reading taken)."""
+    x = np.asarray(x, dtype=np.float64)
+    H = x.shape[2]
+    if HV % H:
+        raise ValueError("HV must be a multiple of H")
+    return np.repeat(x, HV // H, axis=2)
+
+
+def biased_logit(z, dt_bias):
+    """The gate logit with the per-dimension bias dt_bias [HV, K] added before
+    the bounded gate ([KDA-layer] parameter table: dt_bias, per-dim gate
+    bias)."""
+    z = np.asarray(z, dtype=np.float64)
+    return z if dt_bias is None else z + np.asarray(dt_bias, dtype=np.float64)
+
+
+def forward_grouped(q, k, v, z, beta_raw, A_log, dt_bias=None, S0=None, g_min=G_MIN_DEFAULT,
+                    flags=FLAGS_DEFAULT):
+    """The layer core with HV value heads sharing H q/k heads and an optional
+    gate bias (meaningful only with the gate computed in-kernel).  Shapes:
+    q, k [B, T, H, Dk]; v [B, T, HV, Dv]; z [B, T, HV, Dk]; beta_raw
+    [B, T, HV]; A_log [HV]; dt_bias [HV, Dk] or None."""
+    if dt_bias is not None and not flags & GATE_IN_KERNEL:
+        raise ValueError("dt_bias biases the in-kernel gate")
+    HV = np.asarray(v).shape[2]
+    return forward(group_heads(q, HV), group_heads(k, HV), v, biased_logit(z, dt_bias), beta_raw, A_log,
+                   S0, g_min, flags)
+
+
+def step_grouped(S, q, k, v, z, beta_raw, A_log, dt_bias=None, g_min=G_MIN_DEFAULT, flags=FLAGS_DEFAULT):
+    """One decode step of forward_grouped: q, k [B, H, Dk]; v [B, HV, Dv];
+    z [B, HV, Dk]; beta_raw [B, HV]; S [B, HV, Dk, Dv]."""
+    if dt_bias is not None and not flags & GATE_IN_KERNEL:
+        raise ValueError("dt_bias biases the in-kernel gate")
+    HV = np.asarray(v).shape[1]
+    qg = group_heads(np.asarray(q)[:, None], HV)[:, 0]
+    kg = group_heads(np.asarray(k)[:, None], HV)[:, 0]
+    return step(S, qg, kg, v, biased_logit(z, dt_bias), beta_raw, A_log, g_min, flags)

@@ -510,3 +510,72 @@ class TestOutputGate:
         assert np.max(np.abs(ora.output_gate(o, np.full_like(o, -60.0), w, eps=0.0))) < 1e-24
         # the weight multiplies channels after the normalisation
         assert np.allclose(n, ora.head_rms_norm(o, eps=0.0) * w, rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Variants: grouped value heads and the gate bias ([KDA-layer] 完整数据流 and
+# its parameter table)
+# ---------------------------------------------------------------------------
+
+class TestGroupedHeads:
+    def _problem(self, rng, B=2, T=19, H=2, HV=6, Dk=8, Dv=5):
+        q = rng.standard_normal((B, T, H, Dk))
+        k = rng.standard_normal((B, T, H, Dk))
+        v = rng.standard_normal((B, T, HV, Dv))
+        z = rng.standard_normal((B, T, HV, Dk))
+        br = rng.standard_normal((B, T, HV))
+        A = rng.normal(0, 0.5, HV)
+        S0 = rng.normal(0, 0.3, (B, HV, Dk, Dv))
+        return q, k, v, z, br, A, S0
+
+    def test_equal_head_counts_is_the_plain_core(self):
+        rng = np.random.default_rng(51)
+        q, k, v, z, br, A, S0 = self._problem(rng, H=3, HV=3)
+        o1, S1 = ora.forward_grouped(q, k, v, z, br, A, None, S0)
+        o2, S2 = ora.forward(q, k, v, z, br, A, S0)
+        assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+
+    def test_each_value_head_runs_with_its_groups_qk(self):
+        # a loop over value heads, each an independent plain core on one head
+        rng = np.random.default_rng(52)
+        q, k, v, z, br, A, S0 = self._problem(rng)
+        o, S = ora.forward_grouped(q, k, v, z, br, A, None, S0)
+        G = v.shape[2] // q.shape[2]
+        for hv in range(v.shape[2]):
+            h = hv // G
+            oh, Sh = ora.forward(q[:, :, [h]], k[:, :, [h]], v[:, :, [hv]], z[:, :, [hv]], br[:, :, [hv]],
+                                 A[[hv]], S0[:, [hv]])
+            assert np.allclose(o[:, :, [hv]], oh, rtol=0, atol=1e-12)
+            assert np.allclose(S[:, [hv]], Sh, rtol=0, atol=1e-12)
+
+    def test_gate_bias_limits(self):
+        # with beta = 0 the state only decays: a large positive bias saturates
+        # the gate at g_min (S_T = e^{T g_min} S0), a large negative one opens it
+        # (S_T = S0)
+        rng = np.random.default_rng(53)
+        q, k, v, z, br, A, S0 = self._problem(rng, T=7, H=1, HV=2)
+        beta0 = np.zeros_like(br)
+        flags = ora.QK_L2NORM | ora.GATE_IN_KERNEL  # beta taken as given
+        Dk = z.shape[-1]
+        big = np.full((2, Dk), 80.0)
+        _, S_hi = ora.forward_grouped(q, k, v, z * 0.01, beta0, np.zeros(2), big, S0, flags=flags)
+        assert np.allclose(S_hi, math.exp(7 * ora.G_MIN_DEFAULT) * S0, rtol=1e-12, atol=0)
+        _, S_lo = ora.forward_grouped(q, k, v, z * 0.01, beta0, np.zeros(2), -big, S0, flags=flags)
+        assert np.allclose(S_lo, S0, rtol=1e-12, atol=0)
+
+    def test_gate_bias_needs_the_in_kernel_gate(self):
+        rng = np.random.default_rng(54)
+        q, k, v, z, br, A, S0 = self._problem(rng, H=1, HV=1)
+        with pytest.raises(ValueError):
+            ora.forward_grouped(q, k, v, z, br, A, np.zeros((1, z.shape[-1])), S0, flags=ora.QK_L2NORM)
+
+    def test_grouped_step_follows_the_sequence(self):
+        rng = np.random.default_rng(55)
+        q, k, v, z, br, A, S0 = self._problem(rng, T=5)
+        db = rng.normal(0, 0.5, (v.shape[2], z.shape[-1]))
+        o, S = ora.forward_grouped(q, k, v, z, br, A, db, S0)
+        St = S0.copy()
+        for t in range(5):
+            ot, St = ora.step_grouped(St, q[:, t], k[:, t], v[:, t], z[:, t], br[:, t], A, db)
+            assert np.allclose(ot, o[:, t], rtol=0, atol=1e-12)
+        assert np.allclose(St, S, rtol=0, atol=1e-12)
