@@ -84,8 +84,10 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
                                  float g_min, unsigned flags, kda_dtype dt,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream,
                                  hipEvent_t* ev, int n_ev,
-                                 bool overlap = false, hipStream_t aux = nullptr, hipEvent_t* sync = nullptr) {
+                                 bool overlap = false, hipStream_t aux = nullptr, hipEvent_t* sync = nullptr,
+                                 int G = 1, const float* dt_bias = nullptr) {
     if (!dtype_ok(dt) || !flags_ok(flags)) return KDA_ERR_DTYPE;
+    if (dt_bias && !(flags & KDA_GATE_IN_KERNEL)) return KDA_ERR_DTYPE;  // it biases the in-kernel gate
     if (chunk == 0) chunk = 64;
     if (B < 0 || T < 0 || H < 0 || !dim_ok(Dk) || !dim_ok(Dv)) return KDA_ERR_SHAPE;
     if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_SHAPE;
@@ -99,6 +101,7 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
         else KDA_TRY(maybe(A_log));
     }
     KDA_TRY(maybe(S0)); KDA_TRY(maybe(S_out)); KDA_TRY(maybe(M_out)); KDA_TRY(maybe(P_out));
+    KDA_TRY(maybe(dt_bias));
     const size_t ws_need = workspace_bytes_impl(B, T, H, Dk, Dv, chunk, dt, overlap);
     if (ws_need > 0) {
         if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
@@ -110,6 +113,7 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
     a.o = o; a.S_out = S_out; a.M_out = M_out; a.P_out = P_out; a.ws = workspace; a.ws_bytes = workspace_bytes;
     a.B = B; a.T = T; a.H = H; a.Dv = Dv; a.NC = (T + chunk - 1) / chunk;
     a.g_min = g_min; a.flags = flags;
+    a.G = G; a.dt_bias = dt_bias;
     if (overlap) {
         for (int i = 0; i < kOverlapSyncEvents; ++i)
             if (!sync[i]) return KDA_ERR_NULL;
@@ -186,11 +190,14 @@ int kda_chunk_fwd_overlap_kernel_count(int B, int T, int H, int Dk, int Dv, int 
     return kda::chunk_overlap_kernel_count(elem_bytes(dt), Dk, chunk, B * H, (T + chunk - 1) / chunk);
 }
 
-kda_status kda_step(const void* q, const void* k, const void* v, const void* z,
-                    const void* beta_raw, const float* A_log, float* S, void* o,
-                    int B, int H, int Dk, int Dv, float g_min, unsigned flags,
-                    kda_dtype dt, hipStream_t stream) {
+}  // extern "C"
+
+static kda_status step_impl(const void* q, const void* k, const void* v, const void* z,
+                            const void* beta_raw, const float* A_log, const float* dt_bias, float* S, void* o,
+                            int B, int H, int G, int Dk, int Dv, float g_min, unsigned flags,
+                            kda_dtype dt, hipStream_t stream) {
     if (!dtype_ok(dt) || !flags_ok(flags)) return KDA_ERR_DTYPE;
+    if (dt_bias && !(flags & KDA_GATE_IN_KERNEL)) return KDA_ERR_DTYPE;
     if (B < 0 || H < 0 || !dim_ok(Dk) || !dim_ok(Dv)) return KDA_ERR_SHAPE;
     if (!gmin_ok(g_min)) return KDA_ERR_GATE;
     if (B == 0 || H == 0) return KDA_OK;
@@ -198,9 +205,44 @@ kda_status kda_step(const void* q, const void* k, const void* v, const void* z,
     KDA_TRY(need(beta_raw)); KDA_TRY(need(S)); KDA_TRY(need(o));
     if (flags & KDA_GATE_IN_KERNEL) KDA_TRY(need(A_log));
     else KDA_TRY(maybe(A_log));
+    KDA_TRY(maybe(dt_bias));
     kda::StepArgs a{q, k, v, z, beta_raw, A_log, S, o, B, H, g_min, flags};
+    a.G = G; a.dt_bias = dt_bias;
     return kda::launch_step(dt == KDA_BF16 ? 1 : 0, Dk, Dv, a, stream) == hipSuccess ? KDA_OK
                                                                                      : KDA_ERR_HIP;
+}
+
+extern "C" {
+
+kda_status kda_step(const void* q, const void* k, const void* v, const void* z,
+                    const void* beta_raw, const float* A_log, float* S, void* o,
+                    int B, int H, int Dk, int Dv, float g_min, unsigned flags,
+                    kda_dtype dt, hipStream_t stream) {
+    return step_impl(q, k, v, z, beta_raw, A_log, nullptr, S, o, B, H, 1, Dk, Dv, g_min, flags, dt, stream);
+}
+
+// q/k head count Hk against HV value heads: HV a positive multiple of Hk.
+static bool groups_ok(int Hk, int HV) { return Hk > 0 && HV >= Hk && HV % Hk == 0; }
+
+kda_status kda_step_grouped(const void* q, const void* k, const void* v, const void* z,
+                            const void* beta_raw, const float* A_log, const float* dt_bias,
+                            float* S, void* o, int B, int H, int HV, int Dk, int Dv,
+                            float g_min, unsigned flags, kda_dtype dt, hipStream_t stream) {
+    if (B > 0 && !groups_ok(H, HV)) return KDA_ERR_SHAPE;
+    return step_impl(q, k, v, z, beta_raw, A_log, dt_bias, S, o, B, HV, B > 0 ? HV / H : 1, Dk, Dv,
+                     g_min, flags, dt, stream);
+}
+
+kda_status kda_chunk_fwd_grouped(const void* q, const void* k, const void* v, const void* z,
+                                 const void* beta_raw, const float* A_log, const float* dt_bias,
+                                 const float* S0, void* o, float* S_out, float* M_out, void* P_out,
+                                 int B, int T, int H, int HV, int Dk, int Dv, int chunk,
+                                 float g_min, unsigned flags, kda_dtype dt,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (B > 0 && !groups_ok(H, HV)) return KDA_ERR_SHAPE;
+    return chunk_fwd_impl(q, k, v, z, beta_raw, A_log, S0, o, S_out, M_out, P_out, B, T, HV, Dk, Dv,
+                          chunk, g_min, flags, dt, workspace, workspace_bytes, stream, nullptr, 0,
+                          false, nullptr, nullptr, B > 0 ? HV / H : 1, dt_bias);
 }
 
 kda_status kda_segment_compose(int n_seg, const float* M, const float* S_tilde,

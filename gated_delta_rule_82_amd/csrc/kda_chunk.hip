@@ -44,7 +44,9 @@ constexpr int kCopyNT = 2;
 struct IntraArgs {
     const void* q; const void* k; const void* z; const void* beta_raw;
     const float* A_log; void* ws;
-    int T, H;
+    int T, H;            // H: value heads; q and k have H / G heads
+    int G;               // value heads per q/k head
+    const float* dt_bias;  // [H, DK] gate bias or NULL
     int wsNC;            // chunk blocks per (b, h) in the workspace buffer, chunk c0 first
     int c0, nc;          // chunks [c0, c0 + nc) of every (b, h) in this launch
     float g_min;
@@ -124,6 +126,8 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     const int cid = bh * a.wsNC + (n - a.c0);  // workspace block of (b, h, chunk n)
     const int h = bh % a.H;
     const int b = bh / a.H;
+    const int Hk = a.H / a.G;   // q/k heads; value head h reads q/k head h / G
+    const int hq = h / a.G;
 
     float (&s_tot)[NBK][DK] = s_tot_all[sub];
     float (&s_eE)[NBK][DK] = s_eE_all[sub];
@@ -142,6 +146,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     // identity transitions below (g = 0, beta = 0), so what they hold never
     // reaches an output
     const size_t row = ((size_t)b * a.T + (t < a.T ? t : a.T - 1)) * a.H + h;
+    const size_t row_qk = ((size_t)b * a.T + (t < a.T ? t : a.T - 1)) * Hk + hq;
 
     T* ws = reinterpret_cast<T*>(a.ws) + (size_t)(active ? cid : 0) * (L.bytes / sizeof(T));
 
@@ -167,13 +172,14 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
             for (int p = 0; p < kStagePieces; ++p) {
                 const int rw = p * (1024 / RB) + rho;  // token row within the wave's 16
                 const int tr = n * C + 16 * I + (rw < 16 ? rw : 15);
-                const size_t grow = ((size_t)b * a.T + (tr < a.T ? tr : a.T - 1)) * a.H + h;
+                const size_t tok = (size_t)b * a.T + (tr < a.T ? tr : a.T - 1);
+                const size_t grow_qk = tok * Hk + hq, grow_z = tok * a.H + h;
                 const uint32_t goff = (uint32_t)((jpos ^ (rw % LPR)) * 16);
 #pragma unroll
                 for (int tn = 0; tn < 3; ++tn) {
                     if (rw < 16)
                         __builtin_amdgcn_global_load_lds(
-                            (const __attribute__((address_space(1))) void*)(srcs[tn] + grow * RB + goff),
+                            (const __attribute__((address_space(1))) void*)(srcs[tn] + (tn < 2 ? grow_qk : grow_z) * RB + goff),
                             (__attribute__((address_space(3))) void*)(stage + tn * 16 * RB + p * 1024), 16, 0, kCopyNT);
                 }
             }
@@ -199,8 +205,8 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
                     dz[2] = bf16_bits_to_float(zz.y & 0xffffu);
                     dz[3] = bf16_bits_to_float(zz.y >> 16);
                 } else {
-                    qr[2 * s + hf].load(reinterpret_cast<const T*>(a.q) + row * DK + c);
-                    kr[2 * s + hf].load(reinterpret_cast<const T*>(a.k) + row * DK + c);
+                    qr[2 * s + hf].load(reinterpret_cast<const T*>(a.q) + row_qk * DK + c);
+                    kr[2 * s + hf].load(reinterpret_cast<const T*>(a.k) + row_qk * DK + c);
                     load4(reinterpret_cast<const T*>(a.z) + row * DK + c, dz);
                 }
             } else {
@@ -229,6 +235,18 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     const float rk = (a.flags & kQkL2) ? __builtin_amdgcn_rsqf(sk + kL2Eps) : 1.0f;
     // log2-decay per element; padding tokens are identity transitions (g = 0, beta = 0)
     if (a.flags & kGateIn) {
+        if (a.dt_bias) {  // per-dimension gate bias on the logit
+            const float* db = a.dt_bias + (size_t)h * DK;
+#pragma unroll
+            for (int s = 0; s < KSD; ++s)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+                    if (DK >= 32 || hf == 0) {
+                        const float4 d = *reinterpret_cast<const float4*>(db + 32 * s + 16 * hf + 4 * gq);
+                        gv[8 * s + 4 * hf] += d.x; gv[8 * s + 4 * hf + 1] += d.y;
+                        gv[8 * s + 4 * hf + 2] += d.z; gv[8 * s + 4 * hf + 3] += d.w;
+                    }
+        }
         const float zscale = -expf(a.A_log[h]) * kLog2e;  // exp2(zscale z) = e^{-e^A z}
         const float gm2 = a.g_min * kLog2e;
 #pragma unroll
@@ -1020,7 +1038,7 @@ struct ChunkLaunch {
     }
     // intra kernel over chunks [c0, c0 + nc) into the buffer `buf` of `per` chunks per (b, h)
     hipError_t intra(void* buf, int per, int c0, int nc, hipStream_t s) const {
-        IntraArgs ia{a.q, a.k, a.z, a.beta_raw, a.A_log, buf, a.T, a.H, per, c0, nc, a.g_min, a.flags};
+        IntraArgs ia{a.q, a.k, a.z, a.beta_raw, a.A_log, buf, a.T, a.H, a.G, a.dt_bias, per, c0, nc, a.g_min, a.flags};
         hipLaunchKernelGGL((kda_intra_kernel<T, DK, C>), dim3((unsigned)(BH * ((nc + NCH - 1) / NCH))), dim3(256), 0,
                            s, ia);
         return hipGetLastError();

@@ -81,7 +81,9 @@ __host__ __device__ constexpr size_t chunk_workspace_bytes(int elem_bytes, int D
 struct StepArgs {
     const void* q; const void* k; const void* v; const void* z; const void* beta_raw;
     const float* A_log; float* S; void* o;
-    int B, H; float g_min; unsigned flags;
+    int B, H; float g_min; unsigned flags;   // H: value heads
+    int G = 1;                        // value heads per q/k head
+    const float* dt_bias = nullptr;   // [H, Dk] gate bias
 };
 
 struct ChunkArgs {
@@ -89,8 +91,10 @@ struct ChunkArgs {
     const float* A_log; const float* S0;
     void* o; float* S_out; float* M_out; void* P_out;
     void* ws; size_t ws_bytes;
-    int B, T, H, Dv, NC;
+    int B, T, H, Dv, NC;   // H: value heads
     float g_min; unsigned flags;
+    int G = 1;                        // value heads per q/k head
+    const float* dt_bias = nullptr;   // [H, Dk] gate bias
 };
 
 struct ComposeArgs {

@@ -44,8 +44,10 @@ __global__ __launch_bounds__(256) void kda_step_kernel(const StepArgs a) {
     }
 
     if (tid < 64) {
-        const T* q = reinterpret_cast<const T*>(a.q) + (size_t)bh * DK;
-        const T* k = reinterpret_cast<const T*>(a.k) + (size_t)bh * DK;
+        // value head h reads q/k head h / G of the same batch row
+        const size_t bq = (size_t)(bh / a.H) * (a.H / a.G) + h / a.G;
+        const T* q = reinterpret_cast<const T*>(a.q) + bq * DK;
+        const T* k = reinterpret_cast<const T*>(a.k) + bq * DK;
         const T* z = reinterpret_cast<const T*>(a.z) + (size_t)bh * DK;
         float qv[MC], kv[MC], zv[MC];
         float sq = 0.f, sk = 0.f;
@@ -55,7 +57,7 @@ __global__ __launch_bounds__(256) void kda_step_kernel(const StepArgs a) {
             const bool ok = c < DK;
             qv[m] = ok ? to_f<T>(q[c]) : 0.f;
             kv[m] = ok ? to_f<T>(k[c]) : 0.f;
-            zv[m] = ok ? to_f<T>(z[c]) : 0.f;
+            zv[m] = ok ? to_f<T>(z[c]) + ((a.dt_bias && (a.flags & kGateIn)) ? a.dt_bias[(size_t)h * DK + c] : 0.f) : 0.f;
             sq += qv[m] * qv[m];
             sk += kv[m] * kv[m];
         }

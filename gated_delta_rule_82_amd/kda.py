@@ -23,7 +23,7 @@ FLAGS_DEFAULT = 7
 EXPORTS = (
     "kda_safe_chunk_size", "kda_chunk_fwd_workspace", "kda_chunk_fwd", "kda_chunk_fwd_timed",
     "kda_chunk_fwd_kernel_count", "kda_chunk_fwd_overlap_workspace", "kda_chunk_fwd_overlap_kernel_count",
-    "kda_chunk_fwd_overlap", "kda_step",
+    "kda_chunk_fwd_overlap", "kda_step", "kda_chunk_fwd_grouped", "kda_step_grouped",
     "kda_segment_compose", "kda_segment_fixup", "kda_short_conv", "kda_output_gate", "kda_status_string",
 )
 OVERLAP_SYNC_EVENTS = 5
@@ -73,6 +73,10 @@ def load() -> ctypes.CDLL:
     L.kda_short_conv.restype = I
     L.kda_output_gate.argtypes = [P] * 4 + [I] * 5 + [P]
     L.kda_output_gate.restype = I
+    L.kda_chunk_fwd_grouped.argtypes = [P] * 12 + [I] * 7 + [F, U, I, P, S, P]
+    L.kda_chunk_fwd_grouped.restype = I
+    L.kda_step_grouped.argtypes = [P] * 9 + [I] * 5 + [F, U, I, P]
+    L.kda_step_grouped.restype = I
     L.kda_status_string.argtypes = [I]
     L.kda_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -147,7 +151,7 @@ class Overlap:
 
 def chunk_fwd(q, k, v, z, beta_raw, A_log, S0=None, *, chunk=64, g_min=-5.0,
               flags=FLAGS_DEFAULT, want_M=False, want_P=False, o=None, S_out=None,
-              M_out=None, P_out=None, workspace=None, events=None, overlap=None):
+              M_out=None, P_out=None, workspace=None, events=None, overlap=None, dt_bias=None):
     """Chunkwise KDA forward.  Returns (o, S_out) plus M and/or P when asked.
 
     `events` (optional): a list of torch.cuda.Event(enable_timing=True).
@@ -157,9 +161,15 @@ def chunk_fwd(q, k, v, z, beta_raw, A_log, S0=None, *, chunk=64, g_min=-5.0,
     events 2k and 2k + 1 bracket kernel k on its own stream.
     `overlap` (optional): an Overlap; runs kda_chunk_fwd_overlap, the intra
     kernels of the next slice beside the inter kernel of the current one.
+    Grouped value heads (v, z, beta_raw with HV = a multiple of q's H heads)
+    or a gate bias `dt_bias` [HV, Dk] fp32 run kda_chunk_fwd_grouped.
     """
-    B, T, H, Dk = q.shape
+    B, T, Hq, Dk = q.shape
+    H = v.shape[2]
     Dv = v.shape[-1]
+    grouped = Hq != H or dt_bias is not None
+    if grouped and (events is not None or overlap is not None):
+        raise ValueError("grouped heads / dt_bias run the plain one-stream call only")
     dt = q.dtype
     dev = q.device
     if o is None:
@@ -177,7 +187,13 @@ def chunk_fwd(q, k, v, z, beta_raw, A_log, S0=None, *, chunk=64, g_min=-5.0,
             _ptr(o), _ptr(S_out), _ptr(M_out), _ptr(P_out),
             B, T, H, Dk, Dv, chunk, g_min, flags, _dt(dt),
             _ptr(workspace), workspace.numel(), _stream(dev))
-    if overlap is not None:
+    if grouped:
+        gargs = (_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta_raw), _ptr(A_log), _ptr(dt_bias), _ptr(S0),
+                 _ptr(o), _ptr(S_out), _ptr(M_out), _ptr(P_out),
+                 B, T, Hq, H, Dk, Dv, chunk, g_min, flags, _dt(dt),
+                 _ptr(workspace), workspace.numel(), _stream(dev))
+        _check("kda_chunk_fwd_grouped", load().kda_chunk_fwd_grouped(*gargs))
+    elif overlap is not None:
         sync = _event_handles(overlap.sync)
         evs = _event_handles(events) if events is not None else None
         _check("kda_chunk_fwd_overlap",
@@ -196,12 +212,21 @@ def chunk_fwd(q, k, v, z, beta_raw, A_log, S0=None, *, chunk=64, g_min=-5.0,
     return tuple(out)
 
 
-def step(q, k, v, z, beta_raw, A_log, S, *, g_min=-5.0, flags=FLAGS_DEFAULT, o=None):
-    """One decode step; S [B,H,Dk,Dv] fp32 is updated in place.  Returns o."""
-    B, H, Dk = q.shape
+def step(q, k, v, z, beta_raw, A_log, S, *, g_min=-5.0, flags=FLAGS_DEFAULT, o=None, dt_bias=None):
+    """One decode step; S [B,HV,Dk,Dv] fp32 is updated in place.  Returns o.
+    q, k have H heads, v, z, beta_raw HV (a multiple of H; grouped heads and
+    dt_bias run kda_step_grouped)."""
+    B, Hq, Dk = q.shape
+    H = v.shape[1]
     Dv = v.shape[-1]
     if o is None:
         o = torch.empty(B, H, Dv, dtype=q.dtype, device=q.device)
+    if Hq != H or dt_bias is not None:
+        st = load().kda_step_grouped(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta_raw), _ptr(A_log),
+                                     _ptr(dt_bias), _ptr(S), _ptr(o), B, Hq, H, Dk, Dv, g_min, flags,
+                                     _dt(q.dtype), _stream(q.device))
+        _check("kda_step_grouped", st)
+        return o
     st = load().kda_step(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta_raw), _ptr(A_log),
                          _ptr(S), _ptr(o), B, H, Dk, Dv, g_min, flags, _dt(q.dtype),
                          _stream(q.device))

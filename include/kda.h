@@ -158,6 +158,31 @@ kda_status kda_step(const void* q, const void* k, const void* v, const void* z,
                     int B, int H, int Dk, int Dv, float g_min, unsigned flags,
                     kda_dtype dt, hipStream_t stream);
 
+/* Grouped value heads and the per-dimension gate bias ("KDAAttention 层"
+ * 完整数据流 and its parameter table: q, k [B,T,H,K]; v [B,T,HV,V]; g
+ * [B,T,HV,K]; beta [B,T,HV]; A_log [HV]; dt_bias [HV,K]).  HV is a positive
+ * multiple of H; value head hv reads q/k head hv / (HV / H).  Every other
+ * argument is as in kda_chunk_fwd with H replaced by HV (z, beta_raw, A_log,
+ * S0, o, S_out, M_out, P_out and the workspace, sized by
+ * kda_chunk_fwd_workspace(B, T, HV, ...)).  dt_bias: [HV, Dk] fp32 device,
+ * 16-byte aligned, added to z before the bounded gate, or NULL; it needs
+ * KDA_GATE_IN_KERNEL (KDA_ERR_DTYPE otherwise).  KDA_ERR_SHAPE when HV is
+ * not a positive multiple of H.  H == HV with dt_bias NULL is kda_chunk_fwd. */
+kda_status kda_chunk_fwd_grouped(const void* q, const void* k, const void* v, const void* z,
+                                 const void* beta_raw, const float* A_log, const float* dt_bias,
+                                 const float* S0, void* o, float* S_out, float* M_out, void* P_out,
+                                 int B, int T, int H, int HV, int Dk, int Dv, int chunk,
+                                 float g_min, unsigned flags, kda_dtype dt,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The decode step of kda_chunk_fwd_grouped: q, k [B,H,Dk]; v [B,HV,Dv]; z
+ * [B,HV,Dk]; beta_raw [B,HV]; A_log [HV]; dt_bias [HV,Dk] or NULL; S
+ * [B,HV,Dk,Dv] fp32 updated in place; o [B,HV,Dv]. */
+kda_status kda_step_grouped(const void* q, const void* k, const void* v, const void* z,
+                            const void* beta_raw, const float* A_log, const float* dt_bias,
+                            float* S, void* o, int B, int H, int HV, int Dk, int Dv,
+                            float g_min, unsigned flags, kda_dtype dt, hipStream_t stream);
+
 /* Segment prefix scan ("KDA 模块交互式演示" §1.6 KCP; "Implémenter KDA" Test 3
  * and 'La loi de composition associative'): for s = 0..n_seg-1,
  *   S_prefix[s] = M[s] S_prev + S_tilde[s],  S_prev = (s ? S_prefix[s-1] : S_in).

@@ -194,3 +194,27 @@ def test_output_gate_validation(lib):
     assert call(y=Y + 8) == 3
     assert call(y=O + 256) == 2      # a shifted view of o
     assert call(T=0, o=None, gate=None, y=None) == 0
+
+
+def test_grouped_validation(lib):
+    ws = 1 << 40
+
+    def chunk(**kw):
+        a = dict(q=A16, k=A16, v=A16, z=A16, beta_raw=A16, A_log=A16, dt_bias=None, S0=None, o=A16,
+                 S_out=None, M_out=None, P_out=None, B=2, T=64, H=2, HV=6, Dk=128, Dv=128, chunk=32,
+                 g_min=-5.0, flags=7, dt=1, workspace=ws, workspace_bytes=1 << 40, stream=None)
+        a.update(kw)
+        return lib.kda_chunk_fwd_grouped(*a.values())
+
+    def step(**kw):
+        a = dict(q=A16, k=A16, v=A16, z=A16, beta_raw=A16, A_log=A16, dt_bias=None, S=A16, o=A16,
+                 B=2, H=2, HV=6, Dk=128, Dv=128, g_min=-5.0, flags=7, dt=1, stream=None)
+        a.update(kw)
+        return lib.kda_step_grouped(*a.values())
+    for call in (chunk, step):
+        assert call(HV=5) == 2              # not a multiple of H
+        assert call(H=0) == 2
+        assert call(HV=1) == 2              # fewer value heads than q/k heads
+        assert call(dt_bias=A16, flags=3) == 4   # a gate bias without the in-kernel gate
+        assert call(dt_bias=A16 + 4) == 3
+        assert call(B=0) == 0

@@ -404,3 +404,60 @@ def test_overlap_layer_workload_and_timing_events():
         torch.cuda.synchronize()
         assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
     assert all(evs[2 * k].elapsed_time(evs[2 * k + 1]) > 0 for k in range(nk))
+
+
+# ------------------------------------------------------ grouped value heads
+
+def grouped_case(B, T, H, HV, Dk, Dv, dtype, seed, bias=True):
+    g = torch.Generator().manual_seed(seed)
+    cast = (lambda x: x.to(dtype))
+    q = cast(torch.randn(B, T, H, Dk, generator=g))
+    k = cast(torch.randn(B, T, H, Dk, generator=g))
+    v = cast(torch.randn(B, T, HV, Dv, generator=g))
+    z = cast(torch.randn(B, T, HV, Dk, generator=g))
+    br = cast(torch.randn(B, T, HV, generator=g))
+    A = (torch.randn(HV, generator=g) * 0.5).float()
+    db = (torch.randn(HV, Dk, generator=g) * 0.5).float() if bias else None
+    S0 = (torch.randn(B, HV, Dk, Dv, generator=g) * 0.2).float()
+    return q, k, v, z, br, A, db, S0
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("B,T,H,HV,Dk,Dv,bias", [
+    (2, 77, 2, 6, 64, 64, True), (1, 130, 1, 4, 128, 128, True), (2, 45, 3, 3, 32, 64, True),
+    (1, 33, 2, 8, 128, 64, False),
+])
+def test_grouped_chunk_matches_oracle(dtype, B, T, H, HV, Dk, Dv, bias):
+    q, k, v, z, br, A, db, S0 = grouped_case(B, T, H, HV, Dk, Dv, dtype, seed=T + 10 * HV + Dk)
+    if not bias:
+        db = None
+    o, S = kda.chunk_fwd(*(t.cuda() for t in (q, k, v, z, br, A)), S0.cuda(), chunk=32,
+                         dt_bias=None if db is None else db.cuda())
+    torch.cuda.synchronize()
+    o_ref, S_ref = ora.forward_grouped(np64(q), np64(k), np64(v), np64(z), np64(br), np64(A), np64(db), np64(S0))
+    assert_close(o, o_ref, dtype, f"grouped o H{H} HV{HV}")
+    assert_close(S, S_ref, dtype, f"grouped S H{H} HV{HV}")
+
+
+def test_grouped_with_equal_heads_and_no_bias_is_the_plain_call():
+    q, k, v, z, br, A, _, S0 = grouped_case(2, 70, 3, 3, 64, 64, BF16, seed=3, bias=False)
+    args = [t.cuda() for t in (q, k, v, z, br, A)]
+    o1, S1 = kda.chunk_fwd(*args, S0.cuda(), chunk=32)
+    zero = torch.zeros(3, 64, device="cuda")
+    o2, S2 = kda.chunk_fwd(*args, S0.cuda(), chunk=32, dt_bias=zero)   # grouped entry, zero bias
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_grouped_step_matches_oracle(dtype):
+    B, H, HV, Dk, Dv = 3, 2, 8, 128, 128
+    q, k, v, z, br, A, db, S0 = grouped_case(B, 1, H, HV, Dk, Dv, dtype, seed=17)
+    S = S0.cuda().clone()
+    o = kda.step(q[:, 0].cuda().contiguous(), k[:, 0].cuda().contiguous(), v[:, 0].cuda().contiguous(),
+                 z[:, 0].cuda().contiguous(), br[:, 0].cuda().contiguous(), A.cuda(), S, dt_bias=db.cuda())
+    torch.cuda.synchronize()
+    o_ref, S_ref = ora.step_grouped(np64(S0), np64(q[:, 0]), np64(k[:, 0]), np64(v[:, 0]), np64(z[:, 0]),
+                                    np64(br[:, 0]), np64(A), np64(db))
+    assert_close(o, o_ref, dtype, "grouped step o")
+    assert_close(S, S_ref, F32, "grouped step S")   # the state is fp32 in both paths
