@@ -19,6 +19,7 @@ calls alone; the JSON line also reports, measured in the same run:
   * MFMA % of the whole call under both flop counts, HBM % on compulsory bytes;
   * the decode step (B=256, H=32, D=128, fp32 state) and its HBM %;
   * the long-context segmented flow (B=1, T=65536, H=32, 8 segments);
+  * grouped value heads with the gate bias (4 q/k heads, 16 value heads);
   * the layer body around the core: the input side (SiLU of the kernel-4
     short convolution of q, k, v), the output side (sigmoid gate times per-head
     RMS norm), each with its HBM %, and input side + core + output side;
@@ -336,6 +337,42 @@ def bench_layer_body(torch, kda, inputs, steps, warmup, chunk):
             "layer_body_tokens_per_s": B * T / (res["body"] / 1e3)}
 
 
+def bench_grouped(torch, kda, steps, warmup, chunk):
+    """Grouped value heads with the gate bias at the layer size: B4 T4096, 4
+    q/k heads shared by 16 value heads, D128, bf16 (kda_chunk_fwd_grouped)."""
+    dev = torch.device("cuda:0")
+    B, T, H, HV, D = 4, 4096, 4, 16, 128
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20260)
+    mk = lambda *shape: torch.randn(*shape, generator=gen, device=dev).to(torch.bfloat16)
+    sets = [dict(q=mk(B, T, H, D), k=mk(B, T, H, D), v=mk(B, T, HV, D), z=mk(B, T, HV, D), br=mk(B, T, HV))
+            for _ in range(4)]
+    A = (torch.randn(HV, generator=gen, device=dev) * 0.5).float()
+    db = (torch.randn(HV, D, generator=gen, device=dev) * 0.5).float()
+    o = torch.empty(B, T, HV, D, dtype=torch.bfloat16, device=dev)
+    S = torch.empty(B, HV, D, D, dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.workspace_bytes(B, T, HV, D, D, chunk, torch.bfloat16), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        s = sets[i % 4]
+        kda.chunk_fwd(s["q"], s["k"], s["v"], s["z"], s["br"], A, None, chunk=chunk, o=o, S_out=S,
+                      workspace=ws, dt_bias=db)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"workload": "grouped: kda_chunk_fwd_grouped B4 T4096, 4 q/k heads for 16 value heads, "
+                        "D128 bf16, with dt_bias (chunk %d)" % chunk,
+            "ms": round(ms, 4), "tokens_per_s": B * T / (ms / 1e3)}
+
+
 def bench_long(torch, kda, inputs, reps, chunk):
     w = inputs.WORKLOADS["long"]
     dev = torch.device("cuda:0")
@@ -465,6 +502,8 @@ def main():
         log("[bench] input side ...")
         extra["layer_body"] = bench_layer_body(torch, kda, inputs, args.steps, args.warmup, C)
         log(f"[bench] layer body {extra['layer_body']}")
+        extra["grouped"] = bench_grouped(torch, kda, args.steps, args.warmup, C)
+        log(f"[bench] grouped {extra['grouped']}")
 
     out = {
         "metric": METRIC,
