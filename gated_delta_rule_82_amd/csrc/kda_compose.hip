@@ -70,68 +70,134 @@ __global__ __launch_bounds__(256) void kda_compose_kernel(const ComposeArgs a) {
     }
 }
 
-constexpr int kFixTokens = 256;  // tokens per wave in kda_fixup
+constexpr int kFixTokens = 512;  // tokens per wave in kda_fixup
+constexpr int kFixBlocks = 2;    // 16-token blocks whose reads a fix-up wave has in flight together
 
-template <typename T, int DK>
+// 4 * NST consecutive elements of one o row: the part of a row one fix-up lane
+// owns, kept packed until it is used.
+template <typename T, int NST> struct ORun {
+    static constexpr int W = NST * (int)sizeof(T);  // 32-bit words
+    uint32_t w[W];
+    __device__ __forceinline__ void load(const T* p) {
+        if constexpr (W % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < W / 4; ++i) {
+                const uint4 u = reinterpret_cast<const uint4*>(p)[i];
+                w[4 * i] = u.x; w[4 * i + 1] = u.y; w[4 * i + 2] = u.z; w[4 * i + 3] = u.w;
+            }
+        } else {
+            const uint2 u = *reinterpret_cast<const uint2*>(p);
+            w[0] = u.x; w[1] = u.y;
+        }
+    }
+    __device__ __forceinline__ floatx4 get(int q) const {
+        if constexpr (sizeof(T) == 2)
+            return floatx4{__uint_as_float(w[2 * q] << 16), __uint_as_float(w[2 * q] & 0xffff0000u),
+                           __uint_as_float(w[2 * q + 1] << 16), __uint_as_float(w[2 * q + 1] & 0xffff0000u)};
+        else
+            return floatx4{__uint_as_float(w[4 * q]), __uint_as_float(w[4 * q + 1]),
+                           __uint_as_float(w[4 * q + 2]), __uint_as_float(w[4 * q + 3])};
+    }
+    __device__ __forceinline__ void put(int q, const floatx4& x) {
+        if constexpr (sizeof(T) == 2) {
+            typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+            const bf16x2v lo = {(bf16_t)x[0], (bf16_t)x[1]}, hi = {(bf16_t)x[2], (bf16_t)x[3]};
+            w[2 * q] = __builtin_bit_cast(uint32_t, lo);
+            w[2 * q + 1] = __builtin_bit_cast(uint32_t, hi);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[4 * q + i] = __float_as_uint(x[i]);
+        }
+    }
+    __device__ __forceinline__ void store(T* p) const {
+        if constexpr (W % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < W / 4; ++i)
+                reinterpret_cast<uint4*>(p)[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+        } else {
+            *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+        }
+    }
+};
+
+// One wave per (segment, b, h, 512-token tile, group of NST value strips of
+// 16 columns).  It holds S_prev^T of its group as matrix-core A operands and,
+// per 16-token block, forms O^T = S^T P^T.  Both operands take channel
+// 32 s + 8 gq + j in contraction slot (gq, j) of step s, so each lane reads 16
+// contiguous bytes of a P row.  Row m of strip q's A operand is value column
+// 4 NST (m / 4) + 4 q + m % 4 of the group, which leaves lane (r, gq) of the
+// output with the 4 NST consecutive columns from 4 NST gq on of token r: one
+// contiguous read-modify-write per lane and token.
+template <typename T, int DK, int NST>
 __global__ __launch_bounds__(256) void kda_fixup_kernel(const FixupArgs a) {
     constexpr int KSD = (DK + 31) / 32;
+    constexpr int NB = kFixBlocks;
     const int lane = threadIdx.x & 63;
     const int r = lane & 15;
     const int gq = lane >> 4;
-    const int nstrip = a.Dv / 16;
+    const int ngroup = a.Dv / (16 * NST);
     const int ntile = (a.T_seg + kFixTokens - 1) / kFixTokens;
-    const long long total = (long long)a.n_seg * a.B * a.H * nstrip * ntile;
+    const long long total = (long long)a.n_seg * a.B * a.H * ntile * ngroup;
     const long long wid = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (wid >= total) return;  // no barriers in this kernel
     long long x = wid;
+    const int grp = (int)(x % ngroup); x /= ngroup;
     const int tt = (int)(x % ntile); x /= ntile;
-    const int strip = (int)(x % nstrip); x /= nstrip;
     const int h = (int)(x % a.H); x /= a.H;
     const int b = (int)(x % a.B); x /= a.B;
     const int sg = (int)x;
     const float* Sprev = sg ? a.S_prefix + (((size_t)(sg - 1) * a.B + b) * a.H + h) * DK * a.Dv
                             : (a.S_in ? a.S_in + ((size_t)b * a.H + h) * DK * a.Dv : nullptr);
     if (!Sprev) return;
-    const int col = strip * 16 + r;
+    const int col0 = grp * 16 * NST;
 
-    Frag<T> Sf[KSD];
+    Frag<T> Sf[NST][KSD];
 #pragma unroll
-    for (int s = 0; s < KSD; ++s)
+    for (int q = 0; q < NST; ++q) {
+        const int col = col0 + 4 * NST * (r >> 2) + 4 * q + (r & 3);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int rw = 32 * s + slot_index(gq, j);
-            Sf[s].set(j, rw < DK ? Sprev[(size_t)rw * a.Dv + col] : 0.f);
-        }
+        for (int s = 0; s < KSD; ++s)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int rw = 32 * s + 8 * gq + j;
+                Sf[q][s].set(j, rw < DK ? Sprev[(size_t)rw * a.Dv + col] : 0.f);
+            }
+    }
 
     const T* P = reinterpret_cast<const T*>(a.P);
     T* o = reinterpret_cast<T*>(a.o);
     const size_t seg_row0 = ((size_t)sg * a.B + b) * a.T_seg;
-    for (int tb = 0; tb < kFixTokens / 16; ++tb) {
-        const int tok0 = tt * kFixTokens + 16 * tb;
-        if (tok0 >= a.T_seg) break;
-        const int tr = tok0 + r;
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int tend = min(a.T_seg, (tt + 1) * kFixTokens);
+    for (int tok0 = tt * kFixTokens; tok0 < tend; tok0 += 16 * NB) {
+        // all reads of the NB blocks go out before any product
+        Frag<T> Pf[NB][KSD];
+        ORun<T, NST> run[NB];
 #pragma unroll
-        for (int s = 0; s < KSD; ++s) {
-            Frag<T> A;
-            float tmp[8];
+        for (int u = 0; u < NB; ++u) {
+            const int tok = tok0 + 16 * u + r;
+            if (tok < tend) {
+                const size_t row = (seg_row0 + tok) * a.H + h;
+                const T* prow = P + row * DK;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) tmp[j] = 0.f;
-            if (tr < a.T_seg) {
-                const T* prow = P + ((seg_row0 + tr) * a.H + h) * DK;
-                load4(prow + 32 * s + 4 * gq, &tmp[0]);
-                if (32 * s + 16 < DK) load4(prow + 32 * s + 16 + 4 * gq, &tmp[4]);
+                for (int s = 0; s < KSD; ++s) {
+                    if (32 * s + 8 * gq < DK) frag_load_row8(Pf[u][s], prow + 32 * s + 8 * gq);
+                    else Pf[u][s].zero();
+                }
+                run[u].load(o + row * a.Dv + col0 + 4 * NST * gq);
             }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) A.set(j, tmp[j]);
-            acc = mma(A, Sf[s], acc);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tok = tok0 + 4 * gq + i;
-            if (tok < a.T_seg) {
-                T* dst = o + ((seg_row0 + tok) * a.H + h) * a.Dv + col;
-                *dst = from_f<T>(to_f<T>(*dst) + acc[i]);
+        for (int u = 0; u < NB; ++u) {
+            const int tok = tok0 + 16 * u + r;
+            if (tok0 + 16 * u < tend) {  // wave-uniform: the products need every lane
+#pragma unroll
+                for (int q = 0; q < NST; ++q) {
+                    floatx4 acc = run[u].get(q);
+#pragma unroll
+                    for (int s = 0; s < KSD; ++s) acc = mma(Sf[q][s], Pf[u][s], acc);
+                    run[u].put(q, acc);
+                }
+                if (tok < tend) run[u].store(o + ((seg_row0 + tok) * a.H + h) * a.Dv + col0 + 4 * NST * gq);
             }
         }
     }
@@ -150,19 +216,31 @@ hipError_t launch_compose(int DK, const ComposeArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename T>
-static hipError_t launch_fixup_t(int DK, const FixupArgs& a, hipStream_t s) {
+template <typename T, int NST>
+static hipError_t launch_fixup_n(int DK, const FixupArgs& a, hipStream_t s) {
     const long long ntile = (a.T_seg + kFixTokens - 1) / kFixTokens;
-    const long long waves = (long long)a.n_seg * a.B * a.H * (a.Dv / 16) * ntile;
+    const long long waves = (long long)a.n_seg * a.B * a.H * (a.Dv / (16 * NST)) * ntile;
     const unsigned grid = (unsigned)((waves + 3) / 4);
     switch (DK) {
-        case 16: hipLaunchKernelGGL((kda_fixup_kernel<T, 16>), dim3(grid), dim3(256), 0, s, a); break;
-        case 32: hipLaunchKernelGGL((kda_fixup_kernel<T, 32>), dim3(grid), dim3(256), 0, s, a); break;
-        case 64: hipLaunchKernelGGL((kda_fixup_kernel<T, 64>), dim3(grid), dim3(256), 0, s, a); break;
-        case 128: hipLaunchKernelGGL((kda_fixup_kernel<T, 128>), dim3(grid), dim3(256), 0, s, a); break;
+        case 16: hipLaunchKernelGGL((kda_fixup_kernel<T, 16, NST>), dim3(grid), dim3(256), 0, s, a); break;
+        case 32: hipLaunchKernelGGL((kda_fixup_kernel<T, 32, NST>), dim3(grid), dim3(256), 0, s, a); break;
+        case 64: hipLaunchKernelGGL((kda_fixup_kernel<T, 64, NST>), dim3(grid), dim3(256), 0, s, a); break;
+        case 128: hipLaunchKernelGGL((kda_fixup_kernel<T, 128, NST>), dim3(grid), dim3(256), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+// strips per group: 4 (64 columns) where the value dimension allows, else all of it
+template <typename T>
+static hipError_t launch_fixup_t(int DK, const FixupArgs& a, hipStream_t s) {
+    switch (a.Dv) {
+        case 16: return launch_fixup_n<T, 1>(DK, a, s);
+        case 32: return launch_fixup_n<T, 2>(DK, a, s);
+        case 64:
+        case 128: return launch_fixup_n<T, 4>(DK, a, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_fixup(int dt, int DK, const FixupArgs& a, hipStream_t s) {

@@ -161,6 +161,36 @@ __device__ __forceinline__ void half_store(float* tile, int lane, int half, cons
     *reinterpret_cast<float4*>(tile + lane * 8 + half * 4) = make_float4(x[0], x[1], x[2], x[3]);
 }
 
+// Load 8 consecutive elements into a fragment's slots 0..7 (16 bytes for
+// bf16, 32 for fp32; p aligned to 16 bytes).
+__device__ __forceinline__ void frag_load_row8(Frag<bf16_t>& f, const bf16_t* p) {
+    f.v = *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ void frag_load_row8(Frag<float>& f, const float* p) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+
+// The same with non-temporal loads (data read once).
+__device__ __forceinline__ void frag_load_row8_nt(Frag<bf16_t>& f, const bf16_t* p) {
+    f.v = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p));
+}
+__device__ __forceinline__ void frag_load_row8_nt(Frag<float>& f, const float* p) {
+    const floatx4 a = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p));
+    const floatx4 b = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p) + 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { f.v[i] = a[i]; f.v[4 + i] = b[i]; }
+}
+
+// Load 4 consecutive elements widened to float (p aligned to 8 / 16 bytes).
+__device__ __forceinline__ floatx4 load4v(const bf16_t* p) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return floatx4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                   __uint_as_float(u.y & 0xffff0000u)};
+}
+__device__ __forceinline__ floatx4 load4v(const float* p) { return *reinterpret_cast<const floatx4*>(p); }
+
 // Store 4 consecutive elements (one 8- or 16-byte store; p aligned to it).
 __device__ __forceinline__ void store4(bf16_t* p, const floatx4& x) {
     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));

@@ -214,6 +214,43 @@ def compose_pair(second, first):
     return M2 @ M1, M2 @ S1 + S2
 
 
+def readout_map(q, k, g, beta):
+    """Readout map of one segment: P_t = q_t^T (M_t ... M_1), the row that the
+    state before the segment reaches in o_t.  The recurrence is affine in its
+    initial state ([Impl-KDA] 'Que teste réellement le test 2'), so a segment
+    run from S0 reads o_t(S0) = o_t(0) + P_t S0 -- the output half of the
+    KCP fix-up ([KDA-demo] §1.6).  q, k, g: [B, T, H, Dk]; beta: [B, T, H].
+    Returns P [B, T, H, Dk]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, T, H, Dk = k.shape
+    M = np.broadcast_to(np.eye(Dk), (B, H, Dk, Dk)).copy()
+    P = np.zeros((B, T, H, Dk))
+    for t in range(T):
+        M = transition(k[:, t], beta[:, t], np.exp(np.asarray(g)[:, t])) @ M
+        P[:, t] = np.einsum("bhi,bhij->bhj", q[:, t], M)
+    return P
+
+
+def segment_fixup(o_zero, P, S_prefix, S_in=None):
+    """Outputs of n segments run from their true incoming states: segment s
+    reads o_zero[s] + P[s] S_prev, where S_prev is S_in (zero when None) for
+    the first segment and the composed state after segment s - 1 otherwise.
+    o_zero [n, B, Tseg, H, Dv]; P [n, B, Tseg, H, Dk]; S_prefix
+    [n, B, H, Dk, Dv] (states after each segment, as `compose` returns)."""
+    o_zero = np.asarray(o_zero, dtype=np.float64)
+    out = o_zero.copy()
+    for s in range(o_zero.shape[0]):
+        if s == 0:
+            if S_in is None:
+                continue
+            S_prev = np.asarray(S_in, dtype=np.float64)
+        else:
+            S_prev = np.asarray(S_prefix[s - 1], dtype=np.float64)
+        out[s] += np.einsum("bthk,bhkv->bthv", np.asarray(P[s], dtype=np.float64), S_prev)
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Chunkwise form (model of the chunk algebra; used only to pin recurrent == chunk)
 # ---------------------------------------------------------------------------

@@ -160,6 +160,7 @@ def test_segment_fragment_matches_oracle(dtype):
     o_ref, _ = ora.recurrent(qh, kh, np64(inp["v"]), g, beta, np64(S_in))
     o_fix = np64(o0) + np.einsum("bthk,bhkv->bthv", np64(P), np64(S_in))
     assert_close(o_fix, o_ref, dtype, "o + P S_in")
+    assert_close(P, ora.readout_map(qh, kh, g, beta), dtype, "readout map P")
 
 
 def test_compose_matches_oracle():
@@ -177,6 +178,28 @@ def test_compose_matches_oracle():
     ref0 = ora.compose([(np64(M[s]), np64(St[s])) for s in range(n)], None)
     torch.cuda.synchronize()
     assert max_rel(out0[-1], ref0[-1]) <= RTOL_F32
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("Dk,Dv,Tseg", [(16, 16, 7), (32, 32, 530), (64, 128, 530), (128, 64, 45),
+                                        (128, 128, 530), (16, 128, 100), (128, 16, 530)])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_fixup_matches_oracle(dtype, Dk, Dv, Tseg, with_state):
+    # every strip grouping (Dv 16, 32, 64, 128), tiles of 512 tokens with a
+    # ragged tail, a segment shorter than one 16-token block, with and without
+    # an incoming state for the first segment
+    rng = np.random.default_rng(Dk * 1000 + Dv * 10 + Tseg + with_state)
+    n, B, H = 3, 2, 2
+    P = torch.tensor(rng.normal(0, 0.3, (n, B, Tseg, H, Dk))).to(dtype)
+    o = torch.tensor(rng.standard_normal((n, B, Tseg, H, Dv))).to(dtype)
+    S_pref = torch.tensor(rng.standard_normal((n, B, H, Dk, Dv)), dtype=F32)
+    S_in = torch.tensor(rng.standard_normal((B, H, Dk, Dv)), dtype=F32) if with_state else None
+    ref = ora.segment_fixup(np64(o), np64(P), np64(S_pref), np64(S_in))
+    out = kda.segment_fixup(P.cuda(), S_pref.cuda(), o.cuda(), None if S_in is None else S_in.cuda())
+    torch.cuda.synchronize()
+    assert_close(out, ref, dtype, "fixed-up o")
+    if not with_state:
+        assert torch.equal(out[0].cpu(), o[0]), "the first segment has no incoming state: untouched"
 
 
 @pytest.mark.parametrize("dtype", [F32, BF16])

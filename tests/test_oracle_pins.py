@@ -287,6 +287,43 @@ class TestAffine:
         assert np.max(np.abs(S1 - expect)) < 1e-14
 
 
+    def test_readout_map_is_the_state_part_of_the_output(self):
+        # affine in S0: o(S0) - o(0) = P S0, for any S0 (two random ones)
+        rng = np.random.default_rng(13)
+        q, k, v, g, beta, _ = rand_problem(rng, T=23)
+        P = ora.readout_map(q, k, g, beta)
+        o0, _ = ora.recurrent(q, k, v, g, beta, None)
+        for seed in (1, 2):
+            S0 = np.random.default_rng(seed).standard_normal((q.shape[0], q.shape[2], q.shape[3], v.shape[3]))
+            oS, _ = ora.recurrent(q, k, v, g, beta, S0)
+            assert rel(oS - o0, np.einsum("bthk,bhkv->bthv", P, S0)) < 1e-12
+
+    def test_readout_map_first_token(self):
+        # one token: P_1 = q_1^T M_1 with M_1 from the transition alone
+        rng = np.random.default_rng(14)
+        q, k, _, g, beta, _ = rand_problem(rng, T=1)
+        M = ora.transition(k[:, 0], beta[:, 0], np.exp(g[:, 0]))
+        expect = np.einsum("bhi,bhij->bhj", q[:, 0], M)
+        assert np.max(np.abs(ora.readout_map(q, k, g, beta)[:, 0] - expect)) < 1e-14
+
+    @pytest.mark.parametrize("with_state", [False, True])
+    def test_segment_fixup_rebuilds_the_full_run(self, with_state):
+        # KCP end to end: every segment from a zero state, its fragment and
+        # readout map, the prefix scan, then the fix-up = the full recurrence.
+        n, Tseg = 4, 11
+        rng = np.random.default_rng(15 + with_state)
+        q, k, v, g, beta, S0 = rand_problem(rng, T=n * Tseg, s0=with_state)
+        parts = [slice(s * Tseg, (s + 1) * Tseg) for s in range(n)]
+        o_zero = np.stack([ora.recurrent(q[:, p], k[:, p], v[:, p], g[:, p], beta[:, p], None)[0]
+                           for p in parts])
+        P = np.stack([ora.readout_map(q[:, p], k[:, p], g[:, p], beta[:, p]) for p in parts])
+        S_pref = np.stack(ora.compose([ora.segment_fragment(k[:, p], v[:, p], g[:, p], beta[:, p])
+                                       for p in parts], S0))
+        o = ora.segment_fixup(o_zero, P, S_pref, S0)
+        o_full, _ = ora.recurrent(q, k, v, g, beta, S0)
+        assert rel(np.concatenate(list(o), axis=1), o_full) < 1e-12
+
+
 # ----------------------------------------------------------- chunkwise form
 
 @pytest.mark.parametrize("chunk", [8, 16, 32, 64])
