@@ -1,9 +1,9 @@
 // kda_compose.hip - segment composition (KCP) and output correction on gfx950.
 //
 // kda_compose: the prefix scan of "KDA 模块交互式演示" §1.6 and "Implémenter KDA"
-// Test 3, S_s = M_s S_{s-1} + S_tilde_s, in fp32 on the matrix cores.  One wave
-// per (b, h, 16-column strip); the strip of S stays in accumulators across the
-// segments and feeds the next product as its B operand directly.
+// Test 3, S_s = M_s S_{s-1} + S_tilde_s, in fp32 on the matrix cores.  One
+// workgroup per (b, h, 16-column strip) whose waves split the state's rows and
+// pass the strip to each other through LDS between segments.
 //
 // kda_fixup: o_t += P_t S_in for segments that were run from a zero state.
 // Valid because the recurrence is affine in the incoming state ("Implémenter
@@ -13,59 +13,88 @@
 
 namespace kda {
 
+// Row of the strip state in LDS: 16 floats, plus 16 more every 4 rows so that
+// the four lane groups of a wave (rows 4 apart) fall in different banks.
+__device__ __forceinline__ int strip_at(int row, int c) { return row * 16 + (row >> 2) * 16 + c; }
+
+// One workgroup per (b, h, 16-column strip), one wave per 16-row block R of
+// the state.  Wave R forms rows 16 R .. 16 R + 15 of S_s = M_s S_{s-1} +
+// S_tilde_s from its 16 rows of M_s (read one segment ahead) and the whole
+// strip of S_{s-1}, which the waves exchange through LDS: the new strip goes
+// to buffer s & 1, one barrier, and every wave reads it back as the B operand
+// of the next product.  (Two buffers: a wave writes buffer s & 1 only after
+// the barrier of segment s - 1, which every wave passes after its reads of
+// buffer (s - 2) & 1.)  Contraction slot j of step s is state row 32 s + 4 gq
+// + j (j < 4) or 32 s + 16 + 4 gq + j - 4, in both operands.
 template <int DK>
-__global__ __launch_bounds__(256) void kda_compose_kernel(const ComposeArgs a) {
-    constexpr int NBD = DK / 16;
+__global__ __launch_bounds__(512) void kda_compose_kernel(const ComposeArgs a) {
     constexpr int KSD = (DK + 31) / 32;
+    constexpr int kRowsLds = DK + DK / 4;
+    __shared__ float s_S[2][kRowsLds * 16];
     const int lane = threadIdx.x & 63;
+    const int R = threadIdx.x >> 6;
     const int r = lane & 15;
     const int gq = lane >> 4;
     const int nstrip = a.Dv / 16;
-    const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int strip = blockIdx.x % nstrip;
+    const int bh = blockIdx.x / nstrip;
     const int BH = a.B * a.H;
-    if (wid >= BH * nstrip) return;  // this kernel has no barriers
-    const int strip = wid % nstrip;
-    const int bh = wid / nstrip;
     const int col = strip * 16 + r;
 
-    floatx4 S[NBD];
+    Frag<float> Sf[KSD];
 #pragma unroll
-    for (int R = 0; R < NBD; ++R)
+    for (int s = 0; s < KSD; ++s)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[R][i] = a.S_in ? a.S_in[((size_t)bh * DK + 16 * R + 4 * gq + i) * a.Dv + col] : 0.f;
-
-    for (int sg = 0; sg < a.n_seg; ++sg) {
-        const float* Ms = a.M + ((size_t)sg * BH + bh) * DK * DK;
-        const float* St = a.S_tilde + ((size_t)sg * BH + bh) * DK * a.Dv;
-        float* Sout = a.S_prefix + ((size_t)sg * BH + bh) * DK * a.Dv;
-        Frag<float> Sf[KSD];
-#pragma unroll
-        for (int s = 0; s < KSD; ++s)
-            Sf[s] = (2 * s + 1 < NBD) ? frag_from_c<float>(S[2 * s], S[2 * s + 1])
-                                      : frag_from_c_lo<float>(S[2 * s]);
-        floatx4 Sn[NBD];
-#pragma unroll
-        for (int R = 0; R < NBD; ++R) {
-            floatx4 acc;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = St[(size_t)(16 * R + 4 * gq + i) * a.Dv + col];
-            const float* mrow = Ms + (size_t)(16 * R + r) * DK;
-#pragma unroll
-            for (int s = 0; s < KSD; ++s) {
-                Frag<float> A;
-                load4(mrow + 32 * s + 4 * gq, &A.v[0]);
-                if (32 * s + 16 < DK) load4(mrow + 32 * s + 16 + 4 * gq, &A.v[4]);
-                else { A.v[4] = A.v[5] = A.v[6] = A.v[7] = 0.f; }
-                acc = mma(A, Sf[s], acc);
-            }
-            Sn[R] = acc;
+        for (int j = 0; j < 4; ++j) {
+            const int r0 = 32 * s + 4 * gq + j, r1 = r0 + 16;
+            Sf[s].v[j] = (a.S_in && r0 < DK) ? a.S_in[((size_t)bh * DK + r0) * a.Dv + col] : 0.f;
+            Sf[s].v[4 + j] = (a.S_in && r1 < DK) ? a.S_in[((size_t)bh * DK + r1) * a.Dv + col] : 0.f;
         }
+
+    auto load_segment = [&](int sg, Frag<float> (&A)[KSD], floatx4& acc) {
+        const float* mrow = a.M + (((size_t)sg * BH + bh) * DK + 16 * R + r) * DK;
 #pragma unroll
-        for (int R = 0; R < NBD; ++R) {
-            S[R] = Sn[R];
+        for (int s = 0; s < KSD; ++s) {
+            load4(mrow + 32 * s + 4 * gq, &A[s].v[0]);
+            if (32 * s + 16 < DK) load4(mrow + 32 * s + 16 + 4 * gq, &A[s].v[4]);
+            else A[s].v[4] = A[s].v[5] = A[s].v[6] = A[s].v[7] = 0.f;
+        }
+        const float* St = a.S_tilde + ((size_t)sg * BH + bh) * DK * a.Dv;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Sout[(size_t)(16 * R + 4 * gq + i) * a.Dv + col] = Sn[R][i];
+        for (int i = 0; i < 4; ++i) acc[i] = St[(size_t)(16 * R + 4 * gq + i) * a.Dv + col];
+    };
+
+    Frag<float> A[KSD];
+    floatx4 acc;
+    load_segment(0, A, acc);
+    for (int sg = 0; sg < a.n_seg; ++sg) {
+        Frag<float> nA[KSD];
+        floatx4 nacc;
+        const bool more = sg + 1 < a.n_seg;  // uniform over the workgroup
+        if (more) load_segment(sg + 1, nA, nacc);
+#pragma unroll
+        for (int s = 0; s < KSD; ++s) acc = mma(A[s], Sf[s], acc);
+        float* Sout = a.S_prefix + ((size_t)sg * BH + bh) * DK * a.Dv;
+        float* buf = s_S[sg & 1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * R + 4 * gq + i;
+            Sout[(size_t)row * a.Dv + col] = acc[i];
+            buf[strip_at(row, r)] = acc[i];
+        }
+        __syncthreads();
+        if (more) {
+#pragma unroll
+            for (int s = 0; s < KSD; ++s)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r0 = 32 * s + 4 * gq + j, r1 = r0 + 16;
+                    Sf[s].v[j] = r0 < DK ? buf[strip_at(r0, r)] : 0.f;
+                    Sf[s].v[4 + j] = r1 < DK ? buf[strip_at(r1, r)] : 0.f;
+                }
+#pragma unroll
+            for (int s = 0; s < KSD; ++s) A[s] = nA[s];
+            acc = nacc;
         }
     }
 }
@@ -204,13 +233,13 @@ __global__ __launch_bounds__(256) void kda_fixup_kernel(const FixupArgs a) {
 }
 
 hipError_t launch_compose(int DK, const ComposeArgs& a, hipStream_t s) {
-    const long long waves = (long long)a.B * a.H * (a.Dv / 16);
-    const unsigned grid = (unsigned)((waves + 3) / 4);
+    const unsigned grid = (unsigned)(a.B * a.H * (a.Dv / 16));
+    const dim3 block(64 * (DK / 16));
     switch (DK) {
-        case 16: hipLaunchKernelGGL(kda_compose_kernel<16>, dim3(grid), dim3(256), 0, s, a); break;
-        case 32: hipLaunchKernelGGL(kda_compose_kernel<32>, dim3(grid), dim3(256), 0, s, a); break;
-        case 64: hipLaunchKernelGGL(kda_compose_kernel<64>, dim3(grid), dim3(256), 0, s, a); break;
-        case 128: hipLaunchKernelGGL(kda_compose_kernel<128>, dim3(grid), dim3(256), 0, s, a); break;
+        case 16: hipLaunchKernelGGL(kda_compose_kernel<16>, dim3(grid), block, 0, s, a); break;
+        case 32: hipLaunchKernelGGL(kda_compose_kernel<32>, dim3(grid), block, 0, s, a); break;
+        case 64: hipLaunchKernelGGL(kda_compose_kernel<64>, dim3(grid), block, 0, s, a); break;
+        case 128: hipLaunchKernelGGL(kda_compose_kernel<128>, dim3(grid), block, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

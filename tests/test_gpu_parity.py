@@ -163,9 +163,11 @@ def test_segment_fragment_matches_oracle(dtype):
     assert_close(P, ora.readout_map(qh, kh, g, beta), dtype, "readout map P")
 
 
-def test_compose_matches_oracle():
-    rng = np.random.default_rng(3)
-    n, B, H, Dk, Dv = 5, 2, 3, 128, 64
+@pytest.mark.parametrize("n,Dk,Dv", [(5, 128, 64), (1, 128, 128), (2, 16, 32), (7, 32, 16), (4, 64, 128),
+                                     (9, 128, 16)])
+def test_compose_matches_oracle(n, Dk, Dv):
+    rng = np.random.default_rng(3 + n + Dk + Dv)
+    B, H = 2, 3
     M = torch.tensor(rng.normal(0, 0.15, (n, B, H, Dk, Dk)), dtype=F32)
     St = torch.tensor(rng.standard_normal((n, B, H, Dk, Dv)), dtype=F32)
     S_in = torch.tensor(rng.standard_normal((B, H, Dk, Dv)), dtype=F32)
