@@ -373,6 +373,47 @@ def bench_grouped(torch, kda, steps, warmup, chunk):
             "ms": round(ms, 4), "tokens_per_s": B * T / (ms / 1e3)}
 
 
+def bench_v1_gate(torch, kda, steps, warmup, chunk):
+    """The unbounded KDA v1 gate g = -exp(A_log) softplus(z) at the layer size
+    (B4 T4096 H16 D128 bf16): ordinary logits z ~ N(0, 1), and logits shifted
+    by +8 and spread by 4, where most 16-token blocks decay past the factored
+    range and take the element-by-element diagonal products."""
+    dev = torch.device("cuda:0")
+    B, T, H, D = 4, 4096, 16, 128
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261)
+    mk = lambda *shape: torch.randn(*shape, generator=gen, device=dev)
+    base = [dict(q=mk(B, T, H, D).bfloat16(), k=mk(B, T, H, D).bfloat16(), v=mk(B, T, H, D).bfloat16(),
+                 z=mk(B, T, H, D), br=mk(B, T, H).bfloat16()) for _ in range(4)]
+    A = (torch.randn(H, generator=gen, device=dev) * 0.5).float()
+    o = torch.empty(B, T, H, D, dtype=torch.bfloat16, device=dev)
+    S = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.workspace_bytes(B, T, H, D, D, chunk, torch.bfloat16), dtype=torch.uint8, device=dev)
+    flags = kda.FLAGS_DEFAULT | kda.GATE_SOFTPLUS
+    res = {"workload": "v1 gate: kda_chunk_fwd with -exp(A_log) softplus(z), B4 T4096 H16 D128 bf16 (chunk %d)"
+                       % chunk}
+    for name, shift, scale in (("ordinary", 0.0, 1.0), ("strong_decay", 8.0, 4.0)):
+        zs = [(b["z"] * scale + shift).bfloat16() for b in base]
+
+        def step(i):
+            s = base[i % 4]
+            kda.chunk_fwd(s["q"], s["k"], s["v"], zs[i % 4], s["br"], A, None, chunk=chunk, flags=flags, o=o,
+                          S_out=S, workspace=ws)
+
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        res[name] = {"ms": round(ms, 4), "tokens_per_s": B * T / (ms / 1e3)}
+    return res
+
+
 def bench_long(torch, kda, inputs, reps, chunk):
     w = inputs.WORKLOADS["long"]
     dev = torch.device("cuda:0")
@@ -503,6 +544,7 @@ def main():
         extra["layer_body"] = bench_layer_body(torch, kda, inputs, args.steps, args.warmup, C)
         log(f"[bench] layer body {extra['layer_body']}")
         extra["grouped"] = bench_grouped(torch, kda, args.steps, args.warmup, C)
+        extra["v1_gate"] = bench_v1_gate(torch, kda, args.steps, args.warmup, C)
         log(f"[bench] grouped {extra['grouped']}")
 
     out = {

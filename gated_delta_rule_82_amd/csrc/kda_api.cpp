@@ -21,10 +21,18 @@ constexpr int kOverlapSyncEvents = 5;  // events kda_chunk_fwd_overlap needs
 bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool dtype_ok(kda_dtype dt) { return dt == KDA_F32 || dt == KDA_BF16; }
-bool flags_ok(unsigned f) { return (f & ~7u) == 0; }
+// known bits only; the v1 gate selects the form of the in-kernel gate
+bool flags_ok(unsigned f) {
+    return (f & ~15u) == 0 && (!(f & KDA_GATE_SOFTPLUS) || (f & KDA_GATE_IN_KERNEL));
+}
 int elem_bytes(kda_dtype dt) { return dt == KDA_BF16 ? 2 : 4; }
 
 bool gmin_ok(float g_min) { return isfinite(g_min) && g_min < 0.0f; }
+// the bound g_min is used by the bounded in-kernel gate only
+bool gate_ok(float g_min, unsigned f, kda_dtype dt) {
+    if ((f & KDA_GATE_IN_KERNEL) && (f & KDA_GATE_SOFTPLUS)) return true;
+    return gmin_ok(g_min) && kda_safe_chunk_size(g_min, dt) >= kFactorTile;
+}
 
 // Checks a pointer that must be present; optional ones pass when NULL.
 kda_status need(const void* p) {
@@ -91,7 +99,7 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
     if (chunk == 0) chunk = 64;
     if (B < 0 || T < 0 || H < 0 || !dim_ok(Dk) || !dim_ok(Dv)) return KDA_ERR_SHAPE;
     if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_SHAPE;
-    if (!gmin_ok(g_min) || kda_safe_chunk_size(g_min, dt) < kFactorTile) return KDA_ERR_GATE;
+    if (!gate_ok(g_min, flags, dt)) return KDA_ERR_GATE;
     if ((size_t)B * (size_t)T * (size_t)H * 128u > ((size_t)1 << 46)) return KDA_ERR_SHAPE;
     if (B == 0 || H == 0) return KDA_OK;
     if (T > 0) {
@@ -199,7 +207,7 @@ static kda_status step_impl(const void* q, const void* k, const void* v, const v
     if (!dtype_ok(dt) || !flags_ok(flags)) return KDA_ERR_DTYPE;
     if (dt_bias && !(flags & KDA_GATE_IN_KERNEL)) return KDA_ERR_DTYPE;
     if (B < 0 || H < 0 || !dim_ok(Dk) || !dim_ok(Dv)) return KDA_ERR_SHAPE;
-    if (!gmin_ok(g_min)) return KDA_ERR_GATE;
+    if (!((flags & KDA_GATE_SOFTPLUS) || gmin_ok(g_min))) return KDA_ERR_GATE;
     if (B == 0 || H == 0) return KDA_OK;
     KDA_TRY(need(q)); KDA_TRY(need(k)); KDA_TRY(need(v)); KDA_TRY(need(z));
     KDA_TRY(need(beta_raw)); KDA_TRY(need(S)); KDA_TRY(need(o));

@@ -41,6 +41,13 @@ namespace kda {
 // the gfx950 cache-policy operand)
 constexpr int kCopyNT = 2;
 
+// Largest block-local decay (in log2 units) the factored diagonal product
+// takes: its column factor 2^-L then stays 2^10 below the float maximum, the
+// headroom kda_safe_chunk_size allows, so a bounded gate the library accepts
+// (at most 16 |g_min| / ln 2 = 115.4 over a block at g_min = -5) never
+// exceeds it.
+constexpr float kWideLog2 = 118.f;
+
 struct IntraArgs {
     const void* q; const void* k; const void* z; const void* beta_raw;
     const float* A_log; void* ws;
@@ -55,7 +62,10 @@ struct IntraArgs {
 
 __host__ __device__ constexpr int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }
 
-template <typename T, int DK, int C>
+// GENERAL: the kernel for the unbounded v1 gate and for caller-supplied
+// log-decays (any g <= 0); the bounded in-kernel gate, which the library only
+// accepts when the factored products stay in range, takes the plain kernel.
+template <typename T, int DK, int C, bool GENERAL>
 __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     constexpr BlockLayout L = block_layout(sizeof(T), DK, C);
     constexpr int NBK = C / 16;
@@ -247,12 +257,28 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
                         gv[8 * s + 4 * hf + 2] += d.z; gv[8 * s + 4 * hf + 3] += d.w;
                     }
         }
-        const float zscale = -expf(a.A_log[h]) * kLog2e;  // exp2(zscale z) = e^{-e^A z}
+        const float eA = expf(a.A_log[h]);
+        const float zscale = -eA * kLog2e;  // exp2(zscale z) = e^{-e^A z}
         const float gm2 = a.g_min * kLog2e;
+        if constexpr (GENERAL) {
+            // bounded gate g_min sigmoid(e^A z), or the unbounded v1 gate
+            // -e^A softplus(z) (both evaluated, one kept: no divergent code)
+            const bool softplus = (a.flags & kGateSoftplus) != 0;
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            const float g2 = gm2 * __builtin_amdgcn_rcpf(1.0f + exp2_fast(zscale * gv[v]));
-            gv[v] = valid ? g2 : 0.f;
+            for (int v = 0; v < NV; ++v) {
+                const float x = gv[v];
+                // one exp2: e^{-e^A z} for the bounded gate, e^{-|z|} for softplus
+                const float t = exp2_fast(softplus ? -fabsf(x) * kLog2e : zscale * x);
+                const float gb = gm2 * __builtin_amdgcn_rcpf(1.0f + t);
+                const float gs = -eA * (fmaxf(x, 0.f) * kLog2e + __builtin_amdgcn_logf(1.0f + t));
+                gv[v] = valid ? (softplus ? gs : gb) : 0.f;
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const float g2 = gm2 * __builtin_amdgcn_rcpf(1.0f + exp2_fast(zscale * gv[v]));
+                gv[v] = valid ? g2 : 0.f;
+            }
         }
     } else {
 #pragma unroll
@@ -264,6 +290,19 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     for (int sh = 0; sh < 4; ++sh) {
 #pragma unroll
         for (int v = 0; v < NV; ++v) gv[v] += row_shift_add(gv[v], sh);
+    }
+    // A block whose decay exceeds 2^-kWideLog2 on some channel (an unbounded
+    // gate, or a caller's log-decay) cannot use the factored diagonal product:
+    // its column factor 2^-L would leave the float range.  Such a wave forms
+    // the diagonal products element by element (phase C), the rest of the
+    // chunk algebra only uses factors <= 1.
+    bool wide = false;  // wave-uniform
+    if constexpr (GENERAL) {
+        float lmin = 0.f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+            if (DK >= 32 || v % 8 < 4) lmin = fminf(lmin, gv[v]);  // channels that exist
+        wide = __ballot(lmin < -kWideLog2) != 0;
     }
     if (active) {
         if (r == 15) {
@@ -320,6 +359,58 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     Frag<T> rkf[KSD], rqf[KSD];
     floatx4 akkR = {0.f, 0.f, 0.f, 0.f}, aqkR = akkR, akkC = akkR;  // diagonal block products
     if (active) {
+        if (wide) {
+            // Diagonal block element by element: entry (i, j) = sum_c x_ic k_jc
+            // 2^(L_ic - L_jc), x = k or q, exponent clamped at 0 (positive only
+            // above the diagonal, which phase D masks).  The lanes of group gq
+            // hold the same channels for the block's 16 tokens, so token j's
+            // values come from lane 16 gq + j; each lane sums its own channels,
+            // then the four groups add their partial sums.
+            // two passes of 8 columns bound the live accumulators
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                float pk[8], pq[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) pk[j] = pq[j] = 0.f;
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    const float Lv = gv[v];
+                    const float qh = qr[v / 4].get(v % 4) * rq;
+                    const float kh = kr[v / 4].get(v % 4) * rk;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int src = (lane & 48) | (8 * half + j);
+                        const float kj = __shfl(kh, src, 64), Lj = __shfl(Lv, src, 64);
+                        const float ke = kj * exp2_fast(fminf(Lv - Lj, 0.f));
+                        pk[j] = fmaf(kh, ke, pk[j]);
+                        pq[j] = fmaf(qh, ke, pq[j]);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    pk[j] += __shfl_xor(pk[j], 16, 64);
+                    pk[j] += __shfl_xor(pk[j], 32, 64);
+                    pq[j] += __shfl_xor(pq[j], 16, 64);
+                    pq[j] += __shfl_xor(pq[j], 32, 64);
+                }
+                // every lane of token r now holds row r at columns 8 half + j:
+                // R layout picks columns 4 gq + i, C layout takes row 4 gq + i's
+                // entry at column r
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int col = 8 * half + j;
+                        if (col == 4 * gq + i) {
+                            akkR[i] = pk[j];
+                            aqkR[i] = pq[j];
+                        }
+                        const float tj = __shfl(pk[j], (lane & 48) | (4 * gq + i), 64);
+                        if (col == r) akkC[i] = tj;
+                    }
+                }
+            }
+        }
 #pragma unroll
         for (int s = 0; s < KSD; ++s) {
             float eE[8], eLl[8], eK[8];
@@ -350,7 +441,15 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
                 const float rsq = qh * e1;
                 const float rsk = kh * e1;
                 const float cdg = kh * einv;
-                const float offv = cdg * eLl[j];   // k exp(Ll - L): decay from the token to its block end
+                // k exp(Ll - L): decay from the token to its block end (in one
+                // exponent when 2^-L may overflow)
+                float offv;
+                if (wide) {
+                    const int c = 32 * s + 16 * (j / 4) + 4 * gq + (j % 4);
+                    offv = (DK >= 32 || j < 4) ? kh * exp2_fast(s_tot[I][c] - Lv) : 0.f;
+                } else {
+                    offv = cdg * eLl[j];
+                }
                 rqf[s].set(j, rsq);
                 rkf[s].set(j, rsk);
                 cdf.set(j, cdg);
@@ -359,9 +458,11 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
                 ob.set(j, offv);
                 kp.set(j, offv * eK[j]);
             }
-            akkR = mma(cdf, rkf[s], akkR);   // R layout: row r, col 4gq+i
-            aqkR = mma(cdf, rqf[s], aqkR);
-            akkC = mma(rkf[s], cdf, akkC);   // C layout: row 4gq+i, col r
+            if (!wide) {
+                akkR = mma(cdf, rkf[s], akkR);   // R layout: row r, col 4gq+i
+                aqkR = mma(cdf, rqf[s], aqkR);
+                akkC = mma(rkf[s], cdf, akkC);   // C layout: row 4gq+i, col r
+            }
             frag_store(kd, ws + L.kd + (size_t)(I * KSD + s) * 512, lane);
             frag_store(qp, ws + L.qp + (size_t)(I * KSD + s) * 512, lane);
             if constexpr (NBK > 1) {
@@ -1039,8 +1140,11 @@ struct ChunkLaunch {
     // intra kernel over chunks [c0, c0 + nc) into the buffer `buf` of `per` chunks per (b, h)
     hipError_t intra(void* buf, int per, int c0, int nc, hipStream_t s) const {
         IntraArgs ia{a.q, a.k, a.z, a.beta_raw, a.A_log, buf, a.T, a.H, a.G, a.dt_bias, per, c0, nc, a.g_min, a.flags};
-        hipLaunchKernelGGL((kda_intra_kernel<T, DK, C>), dim3((unsigned)(BH * ((nc + NCH - 1) / NCH))), dim3(256), 0,
-                           s, ia);
+        const dim3 grid((unsigned)(BH * ((nc + NCH - 1) / NCH)));
+        if ((a.flags & kGateSoftplus) || !(a.flags & kGateIn))
+            hipLaunchKernelGGL((kda_intra_kernel<T, DK, C, true>), grid, dim3(256), 0, s, ia);
+        else
+            hipLaunchKernelGGL((kda_intra_kernel<T, DK, C, false>), grid, dim3(256), 0, s, ia);
         return hipGetLastError();
     }
     // inter kernel over the same chunks; the state enters from S0/M0 (first

@@ -7,7 +7,7 @@
 
 namespace kda {
 
-enum : unsigned { kQkL2 = 1u, kBetaSig = 2u, kGateIn = 4u };
+enum : unsigned { kQkL2 = 1u, kBetaSig = 2u, kGateIn = 4u, kGateSoftplus = 8u };
 
 // Per chunk-head block of intermediates written by the intra kernel and read
 // by the inter kernel.  All matrices are stored as fragment-major tiles of

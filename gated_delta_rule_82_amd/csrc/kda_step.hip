@@ -76,7 +76,11 @@ __global__ __launch_bounds__(256) void kda_step_kernel(const StepArgs a) {
             const int c = tid + 64 * m;
             if (c < DK) {
                 const float qh = qv[m] * rq, kh = kv[m] * rk;
-                const float g = gate ? a.g_min * sigmoidf_(hscale * zv[m]) : zv[m];
+                // bounded gate, or the unbounded v1 gate -e^A softplus(z)
+                const float x = zv[m];
+                const float g = !gate ? x
+                              : (a.flags & kGateSoftplus) ? -hscale * (fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))))
+                                                          : a.g_min * sigmoidf_(hscale * x);
                 s_q[c] = qh;
                 s_k[c] = kh;
                 s_a[c] = expf(g);

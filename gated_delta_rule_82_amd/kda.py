@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 KDA_F32, KDA_BF16 = 0, 1
 QK_L2NORM, BETA_SIGMOID, GATE_IN_KERNEL = 1, 2, 4
 FLAGS_DEFAULT = 7
+GATE_SOFTPLUS = 8  # with GATE_IN_KERNEL: the unbounded KDA v1 gate -exp(A_log) softplus(z)
 
 EXPORTS = (
     "kda_safe_chunk_size", "kda_chunk_fwd_workspace", "kda_chunk_fwd", "kda_chunk_fwd_timed",

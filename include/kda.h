@@ -46,7 +46,8 @@ typedef enum {
     KDA_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned                   */
     KDA_ERR_DTYPE = 4,     /* unknown dtype or unknown switch bits               */
     KDA_ERR_GATE = 5,      /* g_min not finite/negative, or the 16-token factor
-                              tile exceeds kda_safe_chunk_size(g_min, dt)        */
+                              tile exceeds kda_safe_chunk_size(g_min, dt)
+                              (bounded gate only)                                */
     KDA_ERR_WORKSPACE = 6, /* workspace NULL, misaligned or too small           */
     KDA_ERR_HIP = 7        /* a kernel launch failed                             */
 } kda_status;
@@ -56,12 +57,21 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 /* Switch bits ("KDAAttention 层", 'three in_kernel switches'; all on by default).
  * With a bit clear the caller supplies the activated value in the same slot:
  * the already-normalised q/k, beta itself in place of beta_raw, or the
- * log-decay g (which must lie in [g_min, 0]) in place of the gate logit z. */
+ * log-decay g (which must lie in [g_min, 0]) in place of the gate logit z.
+ *
+ * KDA_GATE_SOFTPLUS (only together with KDA_GATE_IN_KERNEL, KDA_ERR_DTYPE
+ * otherwise) replaces the bounded gate by the unbounded KDA v1 gate
+ * g = -exp(A_log[h]) * softplus(z) ("Implémenter KDA" 'La décroissance
+ * bornée', the form the bounded gate replaces; "线性注意力交互式演示" Tab 3).
+ * g_min is then not used.  The chunked form stays exact for any decay: a
+ * 16-token block whose decay leaves the range of the factored products is
+ * evaluated element by element in log space. */
 enum {
     KDA_QK_L2NORM = 1u,
     KDA_BETA_SIGMOID = 2u,
     KDA_GATE_IN_KERNEL = 4u,
-    KDA_FLAGS_DEFAULT = 7u
+    KDA_FLAGS_DEFAULT = 7u,
+    KDA_GATE_SOFTPLUS = 8u
 };
 
 /* Largest token tile whose factored inverse retention exp(-g_min * n) stays

@@ -30,6 +30,10 @@ the design notes):
     garbled);
   * L2 normalisation divides by sqrt(sum x^2 + eps) with eps = 1e-6 (the
     pages give no epsilon);
+  * the KDA v1 gate (switch bit 8) is g = -exp(A_log) * softplus(z): the form
+    [Impl-KDA] states and the one whose dalpha/dz minimum (-1/4 at z = 0 for
+    A_log = 0) [KDA-demo] Tab 3 plots; the "Eq. 7" line of [KDA-demo], with
+    exp(A_log) added inside the softplus, would move that minimum to z = -1;
   * with a switch off ([KDA-layer] "三个 in_kernel 开关") the caller supplies
     the activated quantity itself: the normalised q/k, beta in (0, 1), or the
     log-decay g in place of the gate logit z.
@@ -50,6 +54,7 @@ QK_L2NORM = 1
 BETA_SIGMOID = 2
 GATE_IN_KERNEL = 4
 FLAGS_DEFAULT = QK_L2NORM | BETA_SIGMOID | GATE_IN_KERNEL
+GATE_SOFTPLUS = 8  # with GATE_IN_KERNEL: the unbounded KDA v1 gate instead of the bounded one
 
 G_MIN_DEFAULT = -5.0  # gate lower bound, [Impl-KDA] "La décroissance bornée"
 L2_EPS = 1e-6
@@ -89,6 +94,24 @@ def bounded_log_decay(z, A_log, g_min=G_MIN_DEFAULT):
     return g_min * sigmoid(scale * z)
 
 
+def softplus(x):
+    """log(1 + e^x) in float64, written as max(x, 0) + log1p(e^-|x|) so that
+    neither tail overflows."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+
+
+def softplus_log_decay(z, A_log):
+    """The KDA v1 (Kimi Linear) gate g = -exp(A_log[h]) * softplus(z), per Dk
+    channel ([Impl-KDA] "La décroissance bornée", which states the v1 form it
+    replaces; [KDA-demo] Tab 3 plots alpha = exp(-softplus(z)) at A_log = 0).
+    Unbounded below: alpha = exp(g) reaches any value in (0, 1).  z is
+    [..., H, Dk]; A_log is [H]."""
+    z = np.asarray(z, dtype=np.float64)
+    scale = np.exp(np.asarray(A_log, dtype=np.float64))[:, None]  # [H, 1]
+    return -scale * softplus(z)
+
+
 def prepare(q, k, z, beta_raw, A_log, g_min=G_MIN_DEFAULT, flags=FLAGS_DEFAULT):
     """Apply the switched activations of [KDA-layer] "chunk_kda 内部做了什么":
     L2-normalise q and k, squash beta by a sigmoid, and turn the gate logit
@@ -101,7 +124,10 @@ def prepare(q, k, z, beta_raw, A_log, g_min=G_MIN_DEFAULT, flags=FLAGS_DEFAULT):
         q = l2_normalize(q)
         k = l2_normalize(k)
     beta = sigmoid(beta_raw) if flags & BETA_SIGMOID else beta_raw
-    g = bounded_log_decay(z, A_log, g_min) if flags & GATE_IN_KERNEL else z
+    if flags & GATE_IN_KERNEL:
+        g = softplus_log_decay(z, A_log) if flags & GATE_SOFTPLUS else bounded_log_decay(z, A_log, g_min)
+    else:
+        g = z
     return q, k, g, beta
 
 

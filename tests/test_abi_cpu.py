@@ -88,6 +88,11 @@ def test_chunk_fwd_validation(lib):
     assert chunk_call(lib, g_min=0.0) == 5
     assert chunk_call(lib, g_min=-10.0) == 5          # 16-token tile unsafe at g_min = -10
     assert chunk_call(lib, g_min=float("nan")) == 5
+    # the v1 gate bit: only with the in-kernel gate, and it does not use g_min
+    assert chunk_call(lib, flags=16) == 4
+    assert chunk_call(lib, flags=8 | 3) == 4
+    assert chunk_call(lib, flags=15, g_min=float("nan")) == 6   # passes the gate check, no workspace
+    assert chunk_call(lib, flags=15, g_min=-10.0) == 6
     assert chunk_call(lib, q=None) == 1
     assert chunk_call(lib, o=None) == 1
     assert chunk_call(lib, A_log=None) == 1           # gate switch on needs A_log
@@ -110,6 +115,9 @@ def test_step_validation(lib):
     assert call(dt=3) == 4
     assert call(Dk=8) == 2
     assert call(g_min=1.0) == 5
+    assert call(flags=8 | 3) == 4
+    assert call(flags=15, g_min=float("nan"), S=None) == 1   # v1 gate: g_min unused
+    assert call(flags=7, g_min=float("nan"), S=None) == 5
     assert call(S=None) == 1
     assert call(v=A16 + 2) == 3
     assert call(flags=3, A_log=None, B=0) == 0

@@ -1,0 +1,135 @@
+"""GPU parity of the unbounded KDA v1 gate g = -exp(A_log) softplus(z) and of
+decays beyond the range of the factored 16-token products.
+
+The chunked form evaluates a 16-token block whose decay passes 2^-118 on some
+channel element by element in log space; these cases put every block, some
+blocks or no block on that path and compare with the fp64 oracle on the same
+inputs, to the bars of tests/kda_check.py.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_82_amd import inputs, kda
+from oracle import kda_oracle as ora
+from tests.kda_check import RTOL_F32, assert_close, max_rel, np64, oracle_forward, to_dev
+
+pytestmark = pytest.mark.gpu
+
+F32, BF16 = torch.float32, torch.bfloat16
+V1 = kda.FLAGS_DEFAULT | kda.GATE_SOFTPLUS
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    kda.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def v1_inputs(B, T, H, Dk, Dv, dtype, seed, zshift, zscale):
+    inp = inputs.make_inputs(B, T, H, Dk, Dv, "bf16" if dtype == BF16 else "f32", seed=seed,
+                             a_std=0.5, s_std=0.3)
+    # logits moved and spread: softplus(z) ~ z for large z, so the per-token decay reaches -e^A z
+    inp["z"] = (inp["z"].float() * zscale + zshift).to(inp["z"].dtype)
+    return inp
+
+
+def run(inp, chunk, flags, **kw):
+    d = to_dev(inp)
+    o, S = kda.chunk_fwd(d["q"], d["k"], d["v"], d["z"], d["beta_raw"], d["A_log"], d["S0"],
+                         chunk=chunk, flags=flags, **kw)
+    torch.cuda.synchronize()
+    return o, S
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("Dk,Dv,chunk,T,zshift,zscale", [
+    (64, 64, 32, 150, 0.0, 1.0),      # ordinary logits: factored blocks
+    (128, 128, 32, 100, 2.0, 1.0),    # about -3 per token: some blocks element by element
+    (32, 16, 16, 77, 8.0, 4.0),       # strong decay: most blocks element by element
+    (128, 64, 64, 130, 30.0, 10.0),   # every block, with exp(-G) far beyond the float range
+    (16, 32, 64, 90, 8.0, 4.0),
+    (128, 128, 16, 45, 5.0, 6.0),     # mixed, one 16-token chunk per block
+])
+def test_v1_gate_chunk_matches_oracle(dtype, Dk, Dv, chunk, T, zshift, zscale):
+    inp = v1_inputs(2, T, 2, Dk, Dv, dtype, T + Dk + chunk, zshift, zscale)
+    o, S = run(inp, chunk, V1)
+    o_ref, S_ref = oracle_forward(inp, flags=V1)
+    assert_close(o, o_ref, dtype, "v1 o")
+    assert_close(S, S_ref, dtype, "v1 S")
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_v1_gate_ignores_g_min(dtype):
+    inp = v1_inputs(1, 70, 2, 64, 64, dtype, 5, 3.0, 3.0)
+    o1, S1 = run(inp, 32, V1)
+    d = to_dev(inp)
+    o2, S2 = kda.chunk_fwd(d["q"], d["k"], d["v"], d["z"], d["beta_raw"], d["A_log"], d["S0"],
+                           chunk=32, flags=V1, g_min=-50.0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_caller_log_decay_beyond_the_factored_range(dtype):
+    # gate switch off: the caller's log-decay itself, down to -200 per token
+    rng = np.random.default_rng(12)
+    inp = inputs.make_inputs(2, 110, 2, 128, 64, "bf16" if dtype == BF16 else "f32", seed=12, s_std=0.3)
+    g = -np.abs(rng.standard_normal((2, 110, 2, 128))) * rng.choice([0.5, 20.0, 200.0], (2, 110, 2, 1))
+    inp["z"] = torch.tensor(g, dtype=F32).to(inp["z"].dtype)
+    o, S = run(inp, 32, 3)
+    o_ref, S_ref = oracle_forward(inp, flags=3)
+    assert_close(o, o_ref, dtype, "caller g o")
+    assert_close(S, S_ref, dtype, "caller g S")
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("zshift,zscale", [(0.0, 1.0), (20.0, 10.0)])
+def test_v1_gate_step_matches_oracle(dtype, zshift, zscale):
+    inp = v1_inputs(3, 1, 5, 128, 128, dtype, 9, zshift, zscale)
+    d = to_dev(inp)
+    S = d["S0"].clone()
+    o = kda.step(d["q"][:, 0].contiguous(), d["k"][:, 0].contiguous(), d["v"][:, 0].contiguous(),
+                 d["z"][:, 0].contiguous(), d["beta_raw"][:, 0].contiguous(), d["A_log"], S, flags=V1)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_forward(inp, flags=V1)
+    assert_close(o, o_ref[:, 0], dtype, "v1 step o")
+    assert max_rel(S, S_ref) <= RTOL_F32
+
+
+def test_v1_gate_step_loop_matches_chunk():
+    # decode steps and the chunked call agree on a sequence with the v1 gate
+    inp = v1_inputs(2, 40, 3, 64, 64, F32, 21, 4.0, 5.0)
+    o_c, S_c = run(inp, 32, V1)
+    d = to_dev(inp)
+    S = d["S0"].clone()
+    for t in range(40):
+        o_t = kda.step(*(d[n][:, t].contiguous() for n in ("q", "k", "v", "z", "beta_raw")), d["A_log"], S,
+                       flags=V1)
+        assert max_rel(o_t, np64(o_c[:, t])) <= RTOL_F32
+    torch.cuda.synchronize()
+    assert max_rel(S, np64(S_c)) <= RTOL_F32
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_v1_gate_grouped_with_bias(dtype):
+    rng = np.random.default_rng(31)
+    B, T, H, HV, Dk, Dv = 2, 66, 2, 4, 128, 64
+    to = lambda x: torch.tensor(x, dtype=F32).to(dtype)
+    q, k = to(rng.standard_normal((B, T, H, Dk))), to(rng.standard_normal((B, T, H, Dk)))
+    v = to(rng.standard_normal((B, T, HV, Dv)))
+    z = to(rng.standard_normal((B, T, HV, Dk)) * 3.0 + 2.0)
+    br = to(rng.standard_normal((B, T, HV)))
+    A = torch.tensor(rng.normal(0, 0.5, HV), dtype=F32)
+    db = torch.tensor(rng.normal(0, 2.0, (HV, Dk)), dtype=F32)
+    S0 = torch.tensor(rng.normal(0, 0.3, (B, HV, Dk, Dv)), dtype=F32)
+    o, S = kda.chunk_fwd(*(t.cuda() for t in (q, k, v, z, br, A)), S0.cuda(), chunk=32, flags=V1,
+                         dt_bias=db.cuda())
+    torch.cuda.synchronize()
+    o_ref, S_ref = ora.forward_grouped(np64(q), np64(k), np64(v), np64(z), np64(br), np64(A), np64(db),
+                                       np64(S0), flags=V1)
+    assert_close(o, o_ref, dtype, "v1 grouped o")
+    assert_close(S, S_ref, dtype, "v1 grouped S")

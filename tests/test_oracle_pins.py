@@ -96,6 +96,61 @@ class TestGate:
         assert s[3] == 1.0 and s[4] == 0.0
 
 
+class TestSoftplusGate:
+    """The unbounded KDA v1 gate g = -exp(A_log) softplus(z) ([Impl-KDA] 'La
+    décroissance bornée' states it as the form being replaced; [KDA-demo] Tab 3)."""
+
+    def test_closed_values(self):
+        # softplus(0) = ln 2; softplus(ln 3) = ln 4; A_log = ln 2 doubles g
+        z = np.array([0.0, math.log(3.0), -math.log(3.0)]).reshape(1, -1, 1, 1)
+        g = ora.softplus_log_decay(z, np.array([0.0])).ravel()
+        assert abs(g[0] + math.log(2.0)) < 1e-15 and abs(g[1] + math.log(4.0)) < 1e-15
+        assert abs(g[2] + math.log(4.0 / 3.0)) < 1e-15
+        g2 = ora.softplus_log_decay(z, np.array([math.log(2.0)])).ravel()
+        assert np.max(np.abs(g2 - 2 * g)) < 1e-15
+
+    def test_retention_is_logistic_at_unit_scale(self):
+        # A_log = 0: alpha = exp(-softplus(z)) = 1 / (1 + e^z) = sigmoid(-z)
+        z = np.linspace(-30, 30, 601).reshape(1, -1, 1, 1)
+        a = np.exp(ora.softplus_log_decay(z, np.array([0.0])))
+        assert np.max(np.abs(a - 1.0 / (1.0 + np.exp(z)))) < 1e-15
+
+    def test_unbounded_below_and_stable_tails(self):
+        # z -> +inf: g ~ -exp(A) z (no floor, unlike the bounded gate); z -> -inf: g -> 0-
+        z = np.array([800.0, 60.0, -60.0, -800.0]).reshape(1, -1, 1, 1)
+        g = ora.softplus_log_decay(z, np.array([0.5])).ravel()
+        assert np.all(np.isfinite(g)) and np.all(g <= 0.0)
+        assert abs(g[0] + math.exp(0.5) * 800.0) < 1e-9 and abs(g[1] + math.exp(0.5) * 60.0) < 1e-9
+        assert 0 > g[2] > -1e-25 and g[3] <= 0.0 and g[3] > -1e-300
+        assert g[0] < -5.0 * 100  # far below any bounded gate's floor
+
+    def test_gate_derivative_minimum_matches_page(self):
+        # [KDA-demo] Tab 3 (v1 curve): d alpha / dz has its minimum about -0.25 at z = 0
+        gold = GOLD["gate_v1_dalpha_dz_min"]
+        z = np.linspace(-6, 6, 120001)
+        h = 1e-5
+        ap = np.exp(ora.softplus_log_decay((z + h).reshape(1, -1, 1, 1), np.array([gold["A_log"]]))).ravel()
+        am = np.exp(ora.softplus_log_decay((z - h).reshape(1, -1, 1, 1), np.array([gold["A_log"]]))).ravel()
+        d = (ap - am) / (2 * h)
+        i = int(np.argmin(d))
+        assert abs(d[i] - gold["value"]) <= gold["abs_tol"]
+        assert abs(z[i] - gold["at_z"]) <= gold["z_tol"]
+
+    def test_prepare_selects_the_v1_gate(self):
+        rng = np.random.default_rng(41)
+        q, k, z = (rng.standard_normal((1, 5, 2, 4)) for _ in range(3))
+        br = rng.standard_normal((1, 5, 2))
+        A = np.array([0.3, -0.2])
+        _, _, g1, _ = ora.prepare(q, k, z, br, A, flags=ora.FLAGS_DEFAULT | ora.GATE_SOFTPLUS)
+        _, _, g2, _ = ora.prepare(q, k, z, br, A, flags=ora.FLAGS_DEFAULT)
+        assert np.max(np.abs(g1 - ora.softplus_log_decay(z, A))) == 0.0
+        assert np.max(np.abs(g2 - ora.bounded_log_decay(z, A))) == 0.0
+        # the bias of the grouped path is added before either gate
+        _, _, g3, _ = ora.prepare(q, k, ora.biased_logit(z, np.full((2, 4), 1.5)), br, A,
+                                  flags=ora.FLAGS_DEFAULT | ora.GATE_SOFTPLUS)
+        assert np.max(np.abs(g3 - ora.softplus_log_decay(z + 1.5, A))) < 1e-15
+
+
 class TestL2Norm:
     def test_unit_norm_and_scale_invariance(self):
         rng = np.random.default_rng(1)
