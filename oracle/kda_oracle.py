@@ -32,7 +32,7 @@ the design notes):
     pages give no epsilon);
   * the KDA v1 gate (switch bit 8) is g = -exp(A_log) * softplus(z): the form
     [Impl-KDA] states and the one whose dalpha/dz minimum (-1/4 at z = 0 for
-    A_log = 0) [KDA-demo] Tab 3 plots; the "Eq. 7" line of [KDA-demo], with
+    A_log = 0) [LinAttn-demo] Tab 3 plots; Eq. 7 of [LinAttn-demo], with
     exp(A_log) added inside the softplus, would move that minimum to z = -1;
   * with a switch off ([KDA-layer] "三个 in_kernel 开关") the caller supplies
     the activated quantity itself: the normalised q/k, beta in (0, 1), or the
@@ -104,7 +104,8 @@ def softplus(x):
 def softplus_log_decay(z, A_log):
     """The KDA v1 (Kimi Linear) gate g = -exp(A_log[h]) * softplus(z), per Dk
     channel ([Impl-KDA] "La décroissance bornée", which states the v1 form it
-    replaces; [KDA-demo] Tab 3 plots alpha = exp(-softplus(z)) at A_log = 0).
+    replaces; [LinAttn-demo] Tab 3 plots alpha = exp(-softplus(z)) at A_log = 0
+    and its gating paragraph writes g = -softplus(z)).
     Unbounded below: alpha = exp(g) reaches any value in (0, 1).  z is
     [..., H, Dk]; A_log is [H]."""
     z = np.asarray(z, dtype=np.float64)

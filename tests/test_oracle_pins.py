@@ -98,7 +98,7 @@ class TestGate:
 
 class TestSoftplusGate:
     """The unbounded KDA v1 gate g = -exp(A_log) softplus(z) ([Impl-KDA] 'La
-    décroissance bornée' states it as the form being replaced; [KDA-demo] Tab 3)."""
+    décroissance bornée' states it as the form being replaced; [LinAttn-demo] Tab 3)."""
 
     def test_closed_values(self):
         # softplus(0) = ln 2; softplus(ln 3) = ln 4; A_log = ln 2 doubles g
@@ -125,7 +125,7 @@ class TestSoftplusGate:
         assert g[0] < -5.0 * 100  # far below any bounded gate's floor
 
     def test_gate_derivative_minimum_matches_page(self):
-        # [KDA-demo] Tab 3 (v1 curve): d alpha / dz has its minimum about -0.25 at z = 0
+        # [LinAttn-demo] Tab 3 (v1 curve): d alpha / dz has its minimum about -0.25 at z = 0
         gold = GOLD["gate_v1_dalpha_dz_min"]
         z = np.linspace(-6, 6, 120001)
         h = 1e-5
