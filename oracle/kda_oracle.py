@@ -477,3 +477,107 @@ def step_grouped(S, q, k, v, z, beta_raw, A_log, dt_bias=None, g_min=G_MIN_DEFAU
     qg = group_heads(np.asarray(q)[:, None], HV)[:, 0]
     kg = group_heads(np.asarray(k)[:, None], HV)[:, 0]
     return step(S, qg, kg, v, biased_logit(z, dt_bias), beta_raw, A_log, g_min, flags)
+
+
+# ---------------------------------------------------------------------------
+# Backward: the adjoint of the recurrence (the gradient of a scalar loss)
+# ---------------------------------------------------------------------------
+#
+# The pages give no derivation of the backward pass; it is the derivative of
+# the recurrence above, written out token by token in reverse (reverse-mode
+# differentiation of `recurrent` and `prepare`), and pinned by finite
+# differences of the forward.  For a loss L with dL/do_t = do_t and
+# dL/dS_T = dS_T, and per token (P = Diag(alpha) S_prev, r = P^T k,
+# u = beta (v - r), S = P + k u^T, o = S^T q):
+#
+#   Lam   = dS + q do^T                  adjoint of S_t, readout included
+#   dq_hat= S do
+#   w     = Lam^T k                      adjoint of u
+#   dbeta = w . (v - r);   dv = beta w;   dr = -beta w
+#   dP    = Lam + k dr^T
+#   dk_hat= Lam u + P dr
+#   dg    = rowsum(dP * P)               (= d alpha * alpha: d alpha = rowsum(dP * S_prev))
+#   dS    <- Diag(alpha) dP              adjoint of S_{t-1}
+
+def l2_normalize_backward(x, dy, eps=L2_EPS):
+    """Gradient through y = x / sqrt(sum x^2 + eps) over the last axis:
+    dx = dy / n - x (x . dy) / n^3."""
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+    return dy / n - x * np.sum(x * dy, axis=-1, keepdims=True) / n ** 3
+
+
+def backward(q, k, v, z, beta_raw, A_log, do, dS_T=None, S0=None, g_min=G_MIN_DEFAULT,
+             flags=FLAGS_DEFAULT):
+    """Gradients of L = sum(do * o) + sum(dS_T * S_T) for (o, S_T) =
+    forward(q, k, v, z, beta_raw, A_log, S0, g_min, flags).
+
+    Shapes as in `forward`; do is [B, T, H, Dv], dS_T [B, H, Dk, Dv] or None.
+    Returns a dict with dq, dk, dz [B,T,H,Dk], dv [B,T,H,Dv], dbeta_raw
+    [B,T,H], dA_log [H] and dS0 [B,H,Dk,Dv].  With a switch off the gradient
+    is the one of the activated quantity the caller passed in that slot."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    beta_raw = np.asarray(beta_raw, dtype=np.float64)
+    A_log = np.asarray(A_log, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    qh, kh, g, beta = prepare(q, k, z, beta_raw, A_log, g_min, flags)
+    B, T, H, Dk = kh.shape
+    Dv = v.shape[-1]
+
+    # forward again, keeping the state before each token
+    S = np.zeros((B, H, Dk, Dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    S_prev = np.zeros((T, B, H, Dk, Dv))
+    for t in range(T):
+        S_prev[t] = S
+        P = np.exp(g[:, t])[..., None] * S
+        r = np.einsum("bhk,bhkv->bhv", kh[:, t], P)
+        u = beta[:, t][..., None] * (v[:, t] - r)
+        S = P + kh[:, t][..., None] * u[..., None, :]
+
+    dqh = np.zeros_like(qh)
+    dkh = np.zeros_like(kh)
+    dg = np.zeros_like(g)
+    dv = np.zeros_like(v)
+    dbeta = np.zeros_like(beta)
+    dS = np.zeros((B, H, Dk, Dv)) if dS_T is None else np.array(dS_T, dtype=np.float64)
+    for t in reversed(range(T)):
+        alpha = np.exp(g[:, t])
+        P = alpha[..., None] * S_prev[t]
+        kt = kh[:, t]
+        r = np.einsum("bhk,bhkv->bhv", kt, P)
+        e = v[:, t] - r
+        bt = beta[:, t][..., None]
+        u = bt * e
+        S_t = P + kt[..., None] * u[..., None, :]
+        Lam = dS + qh[:, t][..., None] * do[:, t][..., None, :]
+        dqh[:, t] = np.einsum("bhkv,bhv->bhk", S_t, do[:, t])
+        w = np.einsum("bhkv,bhk->bhv", Lam, kt)
+        dbeta[:, t] = np.sum(w * e, axis=-1)
+        dv[:, t] = bt * w
+        dr = -bt * w
+        dP = Lam + kt[..., None] * dr[..., None, :]
+        dkh[:, t] = np.einsum("bhkv,bhv->bhk", Lam, u) + np.einsum("bhkv,bhv->bhk", P, dr)
+        dg[:, t] = np.sum(dP * P, axis=-1)
+        dS = alpha[..., None] * dP
+
+    dq = l2_normalize_backward(q, dqh) if flags & QK_L2NORM else dqh
+    dk = l2_normalize_backward(k, dkh) if flags & QK_L2NORM else dkh
+    dbeta_raw = dbeta * beta * (1.0 - beta) if flags & BETA_SIGMOID else dbeta
+    scale = np.exp(A_log)[:, None]                      # [H, 1]
+    if flags & GATE_IN_KERNEL:
+        if flags & GATE_SOFTPLUS:                        # g = -e^A softplus(z)
+            dz = dg * (-scale * sigmoid(z))
+            dA = np.sum(dg * g, axis=(0, 1, 3))
+        else:                                            # g = g_min sigmoid(e^A z)
+            s = sigmoid(scale * z)
+            dsz = dg * g_min * s * (1.0 - s)             # dL / d(e^A z)
+            dz = dsz * scale
+            dA = np.sum(dsz * scale * z, axis=(0, 1, 3))
+    else:
+        dz = dg
+        dA = np.zeros(H)
+    return {"dq": dq, "dk": dk, "dv": dv, "dz": dz, "dbeta_raw": dbeta_raw, "dA_log": dA, "dS0": dS}

@@ -671,3 +671,79 @@ class TestGroupedHeads:
             ot, St = ora.step_grouped(St, q[:, t], k[:, t], v[:, t], z[:, t], br[:, t], A, db)
             assert np.allclose(ot, o[:, t], rtol=0, atol=1e-12)
         assert np.allclose(St, S, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------ backward
+
+class TestBackward:
+    """The adjoint of the recurrence (oracle.backward): reverse-mode
+    differentiation of `forward`, which the pages do not derive."""
+
+    @staticmethod
+    def problem(rng, flags, B=1, T=6, H=2, Dk=3, Dv=2):
+        q, k, z = (rng.standard_normal((B, T, H, Dk)) for _ in range(3))
+        if not flags & ora.GATE_IN_KERNEL:
+            z = -np.abs(z) * 2.0          # the caller's log-decay itself
+        v = rng.standard_normal((B, T, H, Dv))
+        br = rng.standard_normal((B, T, H))
+        if not flags & ora.BETA_SIGMOID:
+            br = ora.sigmoid(br)
+        A = rng.normal(0, 0.5, H)
+        S0 = rng.normal(0, 0.3, (B, H, Dk, Dv))
+        do = rng.standard_normal((B, T, H, Dv))
+        dST = rng.standard_normal((B, H, Dk, Dv))
+        return dict(q=q, k=k, v=v, z=z, beta_raw=br, A_log=A, S0=S0), do, dST
+
+    @pytest.mark.parametrize("flags", [ora.FLAGS_DEFAULT, ora.FLAGS_DEFAULT | ora.GATE_SOFTPLUS, 0,
+                                       ora.QK_L2NORM | ora.BETA_SIGMOID])
+    def test_matches_central_differences(self, flags):
+        # L = sum(do * o) + sum(dS_T * S_T); every input element perturbed by +-1e-6
+        rng = np.random.default_rng(50 + flags)
+        args, do, dST = self.problem(rng, flags)
+        grads = ora.backward(args["q"], args["k"], args["v"], args["z"], args["beta_raw"], args["A_log"], do,
+                             dST, args["S0"], flags=flags)
+
+        def loss(a):
+            o, S = ora.forward(a["q"], a["k"], a["v"], a["z"], a["beta_raw"], a["A_log"], a["S0"], flags=flags)
+            return float(np.sum(do * o) + np.sum(dST * S))
+
+        names = {"q": "dq", "k": "dk", "v": "dv", "z": "dz", "beta_raw": "dbeta_raw", "A_log": "dA_log",
+                 "S0": "dS0"}
+        h = 1e-6
+        for n, gname in names.items():
+            x = args[n]
+            fd = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                ap, am = dict(args), dict(args)
+                ap[n] = x.copy(); ap[n][idx] += h
+                am[n] = x.copy(); am[n][idx] -= h
+                fd[idx] = (loss(ap) - loss(am)) / (2 * h)
+            if not np.any(fd):
+                assert not np.any(grads[gname]), n       # A_log with the gate switch off
+                continue
+            assert rel(grads[gname], fd) < 1e-6, (n, rel(grads[gname], fd))
+
+    def test_state_gradient_is_the_transposed_linear_map(self):
+        # o_t = o_t(0) + P_t S0 and S_T = S_T(0) + M S0 (readout map, segment
+        # transition), so dS0 = sum_t P_t^T do_t + M^T dS_T exactly
+        rng = np.random.default_rng(60)
+        q, k, v, g, beta, S0 = rand_problem(rng, T=19)
+        do = rng.standard_normal(v.shape)
+        dST = rng.standard_normal(S0.shape)
+        grads = ora.backward(q, k, v, g, beta, np.zeros(q.shape[2]), do, dST, S0, flags=0)
+        P = ora.readout_map(q, k, g, beta)
+        M, _ = ora.segment_fragment(k, v, g, beta)
+        expect = np.einsum("bthk,bthv->bhkv", P, do) + np.einsum("bhjk,bhjv->bhkv", M, dST)
+        assert rel(grads["dS0"], expect) < 1e-12
+
+    def test_value_gradient_of_an_isolated_token(self):
+        # one token from a zero state: o = q^T k beta v, so dv = beta (q . k) do
+        # and dbeta = (q . k) (v . do) (alpha drops out: the state starts empty)
+        rng = np.random.default_rng(61)
+        q, k, v, g, beta, _ = rand_problem(rng, T=1, s0=False)
+        do = rng.standard_normal(v.shape)
+        grads = ora.backward(q, k, v, g, beta, np.zeros(q.shape[2]), do, None, None, flags=0)
+        qk = np.sum(q[:, 0] * k[:, 0], axis=-1)
+        assert rel(grads["dv"][:, 0], (beta[:, 0] * qk)[..., None] * do[:, 0]) < 1e-14
+        assert rel(grads["dbeta_raw"][:, 0], qk * np.sum(v[:, 0] * do[:, 0], axis=-1)) < 1e-14
+        assert np.max(np.abs(grads["dz"])) == 0.0
