@@ -414,6 +414,36 @@ def bench_v1_gate(torch, kda, steps, warmup, chunk):
     return res
 
 
+def bench_backward(torch, kda, inputs, steps, warmup):
+    """The backward (kda_chunk_bwd) at the layer size: B4 T4096 H16 D128 bf16,
+    a random output gradient, no final-state gradient."""
+    w = inputs.WORKLOADS["layer"]
+    dev = torch.device("cuda:0")
+    inp = {k: (None if v is None else v.to(dev)) for k, v in inputs.make_workload(w).items()}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20262)
+    do = torch.randn(w.B, w.T, w.H, w.Dv, generator=gen, device=dev).to(torch.bfloat16)
+    ws = torch.empty(kda.bwd_workspace_bytes(w.B, w.T, w.H, w.Dk, w.Dv), dtype=torch.uint8, device=dev)
+
+    def step():
+        kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["z"], inp["beta_raw"], inp["A_log"], do, inp["S0"],
+                      None, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"workload": "backward: kda_chunk_bwd B4 T4096 H16 D128 bf16 (fp32 arithmetic, 32-token chunks)",
+            "ms": round(ms, 4), "tokens_per_s": w.B * w.T / (ms / 1e3),
+            "workspace_bytes": int(ws.numel())}
+
+
 def bench_long(torch, kda, inputs, reps, chunk):
     w = inputs.WORKLOADS["long"]
     dev = torch.device("cuda:0")
@@ -545,6 +575,7 @@ def main():
         log(f"[bench] layer body {extra['layer_body']}")
         extra["grouped"] = bench_grouped(torch, kda, args.steps, args.warmup, C)
         extra["v1_gate"] = bench_v1_gate(torch, kda, args.steps, args.warmup, C)
+        extra["backward"] = bench_backward(torch, kda, inputs, max(3, args.steps // 4), 2)
         log(f"[bench] grouped {extra['grouped']}")
 
     out = {

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_step.hip", "kda_chunk.hip", "kda_compose.hip", "kda_conv.hip", "kda_gate.hip"]
+SOURCES = ["kda_api.cpp", "kda_step.hip", "kda_chunk.hip", "kda_compose.hip", "kda_conv.hip", "kda_gate.hip", "kda_bwd.hip"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 
 

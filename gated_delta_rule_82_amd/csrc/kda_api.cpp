@@ -263,6 +263,69 @@ kda_status kda_segment_compose(int n_seg, const float* M, const float* S_tilde,
     return kda::launch_compose(Dk, a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+// Backward workspace: operators, chunk-start states, chunk-end adjoints and
+// the per-chunk dA_log parts, each region 256-byte aligned.
+struct BwdWorkspace {
+    size_t ops, states, adj, dA, total;
+};
+static BwdWorkspace bwd_workspace(int B, int T, int H, int Dk, int Dv) {
+    BwdWorkspace w{};
+    const size_t NC = (size_t)(T + kda::kBwdChunk - 1) / kda::kBwdChunk;
+    const size_t BHN = (size_t)B * H * NC;
+    w.ops = 0;
+    w.states = kda::round_up(BHN * kda::bwd_op_floats(Dk) * 4, 256);
+    w.adj = w.states + kda::round_up(BHN * Dk * Dv * 4, 256);
+    w.dA = w.adj + kda::round_up(BHN * Dk * Dv * 4, 256);
+    w.total = w.dA + kda::round_up(BHN * 4, 256);
+    return w;
+}
+
+size_t kda_chunk_bwd_workspace(int B, int T, int H, int Dk, int Dv) {
+    if (B < 0 || T < 0 || H < 0 || !dim_ok(Dk) || !dim_ok(Dv)) return 0;
+    return bwd_workspace(B, T, H, Dk, Dv).total;
+}
+
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* z,
+                         const void* beta_raw, const float* A_log, const float* S0,
+                         const void* dout, const float* dS_T,
+                         void* dq, void* dk, void* dv, void* dz, void* dbeta_raw,
+                         float* dA_log, float* dS0,
+                         int B, int T, int H, int Dk, int Dv, float g_min, unsigned flags,
+                         kda_dtype dt, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+    if (!dtype_ok(dt) || !flags_ok(flags)) return KDA_ERR_DTYPE;
+    if (B < 0 || T < 0 || H < 0 || !dim_ok(Dk) || !dim_ok(Dv)) return KDA_ERR_SHAPE;
+    if ((size_t)B * (size_t)T * (size_t)H * 128u > ((size_t)1 << 46)) return KDA_ERR_SHAPE;
+    if (!gate_ok(g_min, flags, dt)) return KDA_ERR_GATE;
+    if (H == 0) return KDA_OK;
+    KDA_TRY(need(dA_log));
+    if (B > 0 && T > 0) {
+        KDA_TRY(need(q)); KDA_TRY(need(k)); KDA_TRY(need(v)); KDA_TRY(need(z));
+        KDA_TRY(need(beta_raw)); KDA_TRY(need(dout));
+        KDA_TRY(need(dq)); KDA_TRY(need(dk)); KDA_TRY(need(dv)); KDA_TRY(need(dz));
+        KDA_TRY(need(dbeta_raw));
+    }
+    if (flags & KDA_GATE_IN_KERNEL) KDA_TRY(need(A_log));
+    else KDA_TRY(maybe(A_log));
+    KDA_TRY(maybe(S0)); KDA_TRY(maybe(dS_T)); KDA_TRY(maybe(dS0));
+    const BwdWorkspace w = bwd_workspace(B, T, H, Dk, Dv);
+    if (w.total > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+                        workspace_bytes < w.total))
+        return KDA_ERR_WORKSPACE;
+    kda::BwdArgs a{};
+    unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
+    a.q = q; a.k = k; a.v = v; a.z = z; a.beta_raw = beta_raw; a.A_log = A_log; a.S0 = S0;
+    a.dout = dout; a.dS_T = dS_T;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dz = dz; a.dbeta_raw = dbeta_raw; a.dA_log = dA_log; a.dS0 = dS0;
+    a.ops = reinterpret_cast<float*>(ws + w.ops);
+    a.states = reinterpret_cast<float*>(ws + w.states);
+    a.adj = reinterpret_cast<float*>(ws + w.adj);
+    a.dA_part = reinterpret_cast<float*>(ws + w.dA);
+    a.B = B; a.T = T; a.H = H; a.Dv = Dv; a.NC = (T + kda::kBwdChunk - 1) / kda::kBwdChunk;
+    a.g_min = g_min; a.flags = flags;
+    return kda::launch_chunk_bwd(dt == KDA_BF16 ? 1 : 0, Dk, a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 kda_status kda_segment_fixup(int n_seg, const void* P, const float* S_in,
                              const float* S_prefix, void* o, int B, int T_seg,
                              int H, int Dk, int Dv, kda_dtype dt, hipStream_t stream) {

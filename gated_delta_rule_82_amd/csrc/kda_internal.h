@@ -140,4 +140,22 @@ struct GateArgs {
 };
 hipError_t launch_output_gate(int dt, int DV, const GateArgs& a, hipStream_t s);
 
+// Backward of the chunked forward (fp32 arithmetic, kBwdChunk-token chunks).
+constexpr int kBwdChunk = 32;
+struct BwdArgs {
+    const void* q; const void* k; const void* v; const void* z; const void* beta_raw;
+    const float* A_log; const float* S0; const void* dout; const float* dS_T;
+    void* dq; void* dk; void* dv; void* dz; void* dbeta_raw; float* dA_log; float* dS0;
+    float* ops; float* states; float* adj; float* dA_part;  // workspace regions
+    int B, T, H, Dv, NC;
+    float g_min;
+    unsigned flags;
+};
+// fp32 elements of the per-chunk operator block for a key dimension DK
+__host__ __device__ constexpr size_t bwd_op_floats(int DK) {
+    const size_t C = kBwdChunk;
+    return round_up(5 * C * (size_t)DK + 5 * C * C + (size_t)DK + C, 64);
+}
+hipError_t launch_chunk_bwd(int dt, int DK, const BwdArgs& a, hipStream_t s);
+
 }  // namespace kda

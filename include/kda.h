@@ -256,6 +256,33 @@ kda_status kda_output_gate(const void* o, const void* gate, const float* weight,
                            int B, int T, int H, int Dv, kda_dtype dt, hipStream_t stream);
 
 /* Static description of a status code. */
+/* Backward of kda_chunk_fwd (training).  The pages give the forward only; this
+ * is its derivative, for a loss L with dL/do = dout and dL/dS_T = dS_T:
+ *   dq, dk, dz [B,T,H,Dk] and dv [B,T,H,Dv], dbeta_raw [B,T,H]: device, dtype
+ *              dt, the gradients with respect to the raw inputs through the
+ *              switched activations (with a switch off, with respect to the
+ *              activated quantity the caller passed in that slot);
+ *   dA_log     [H] fp32 device: written (summed over batch and tokens; zero
+ *              with the gate switch off);
+ *   dS0        [B,H,Dk,Dv] fp32 device or NULL: the gradient with respect to
+ *              the initial state.
+ * Inputs as for kda_chunk_fwd (HV = H, no gate bias; every switch bit,
+ * KDA_GATE_SOFTPLUS included); dout [B,T,H,Dv] dtype dt; dS_T [B,H,Dk,Dv]
+ * fp32 or NULL (zero).  The arithmetic is fp32 in 32-token chunks, every decay
+ * factor in one exponent (exact for any log-decay).  The workspace
+ * (kda_chunk_bwd_workspace bytes, 256-byte aligned) holds the per-chunk
+ * operators, the state at each chunk start and the state adjoint at each
+ * chunk end.  Outputs must not overlap inputs.  Errors as kda_chunk_fwd. */
+size_t kda_chunk_bwd_workspace(int B, int T, int H, int Dk, int Dv);
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* z,
+                         const void* beta_raw, const float* A_log, const float* S0,
+                         const void* dout, const float* dS_T,
+                         void* dq, void* dk, void* dv, void* dz, void* dbeta_raw,
+                         float* dA_log, float* dS0,
+                         int B, int T, int H, int Dk, int Dv, float g_min, unsigned flags,
+                         kda_dtype dt, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
 const char* kda_status_string(kda_status s);
 
 #ifdef __cplusplus

@@ -226,3 +226,36 @@ def test_grouped_validation(lib):
         assert call(dt_bias=A16, flags=3) == 4   # a gate bias without the in-kernel gate
         assert call(dt_bias=A16 + 4) == 3
         assert call(B=0) == 0
+
+
+def bwd_call(lib, **kw):
+    a = dict(q=A16, k=A16, v=A16, z=A16, beta_raw=A16, A_log=A16, S0=None, dout=A16, dS_T=None,
+             dq=A16, dk=A16, dv=A16, dz=A16, dbeta_raw=A16, dA_log=A16, dS0=None,
+             B=1, T=64, H=2, Dk=64, Dv=64, g_min=-5.0, flags=7, dt=1, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_bwd(*a.values())
+
+
+def test_backward_workspace_and_validation(lib):
+    # operators (32-token chunks), chunk-start states and chunk-end adjoints, dA parts
+    need = lib.kda_chunk_bwd_workspace(1, 64, 2, 64, 64)
+    ops = 2 * 2 * (5 * 32 * 64 + 5 * 32 * 32 + 64 + 32) * 4
+    assert need >= ops + 2 * (2 * 2 * 64 * 64 * 4)
+    assert lib.kda_chunk_bwd_workspace(1, 64, 2, 48, 64) == 0
+    assert lib.kda_chunk_bwd_workspace(1, 0, 2, 64, 64) == 0
+    assert bwd_call(lib, dt=3) == 4
+    assert bwd_call(lib, flags=8) == 4
+    assert bwd_call(lib, Dv=8) == 2
+    assert bwd_call(lib, T=-1) == 2
+    assert bwd_call(lib, g_min=1.0) == 5
+    assert bwd_call(lib, flags=15, g_min=float("nan")) == 6   # v1 gate: g_min unused, then the workspace
+    assert bwd_call(lib, dout=None) == 1
+    assert bwd_call(lib, dz=None) == 1
+    assert bwd_call(lib, dA_log=None) == 1
+    assert bwd_call(lib, A_log=None) == 1
+    assert bwd_call(lib, flags=3, A_log=None) == 6             # no gate: A_log optional
+    assert bwd_call(lib, dq=A16 + 4) == 3
+    assert bwd_call(lib, dS0=A16 + 8) == 3
+    assert bwd_call(lib, ws=A16, ws_bytes=need - 1) == 6
+    assert bwd_call(lib, ws=A16 + 16, ws_bytes=need) == 6
+    assert bwd_call(lib, H=0) == 0
