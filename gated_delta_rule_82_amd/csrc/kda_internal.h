@@ -151,10 +151,24 @@ struct BwdArgs {
     float g_min;
     unsigned flags;
 };
-// fp32 elements of the per-chunk operator block for a key dimension DK
+// fp32 elements of the per-chunk operator block for a key dimension DK: the
+// state pass's region, the adjoint pass's region (operand tiles of 16 rows x
+// 32 contraction slots, 512 floats each, plus gamma and beta; each region a
+// whole number of KiB) and the row-major At.
+__host__ __device__ constexpr size_t bwd_tiles(size_t rows, size_t kext) {
+    return rows / 16 * ((kext + 31) / 32) * 512;
+}
+__host__ __device__ constexpr size_t bwd_op_region_s(int DK) {
+    const size_t C = kBwdChunk;
+    return round_up(bwd_tiles(C, DK) + bwd_tiles(DK, C) + bwd_tiles(C, C) + DK + C, 256);
+}
+__host__ __device__ constexpr size_t bwd_op_region_a(int DK) {
+    const size_t C = kBwdChunk;
+    return round_up(bwd_tiles(C, DK) + 2 * bwd_tiles(DK, C) + 2 * bwd_tiles(C, C) + DK + C, 256);
+}
 __host__ __device__ constexpr size_t bwd_op_floats(int DK) {
     const size_t C = kBwdChunk;
-    return round_up(5 * C * (size_t)DK + 5 * C * C + (size_t)DK + C, 64);
+    return round_up(bwd_op_region_s(DK) + bwd_op_region_a(DK) + C * C, 256);
 }
 hipError_t launch_chunk_bwd(int dt, int DK, const BwdArgs& a, hipStream_t s);
 

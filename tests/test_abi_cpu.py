@@ -239,8 +239,10 @@ def bwd_call(lib, **kw):
 def test_backward_workspace_and_validation(lib):
     # operators (32-token chunks), chunk-start states and chunk-end adjoints, dA parts
     need = lib.kda_chunk_bwd_workspace(1, 64, 2, 64, 64)
-    ops = 2 * 2 * (5 * 32 * 64 + 5 * 32 * 32 + 64 + 32) * 4
+    # per chunk-head: five [C x Dk] operand matrices, four [C x C] ones, gamma and beta
+    ops = 2 * 2 * (5 * 32 * 64 + 4 * 32 * 32 + 64 + 32) * 4
     assert need >= ops + 2 * (2 * 2 * 64 * 64 * 4)
+    assert need <= 2 * (ops + 2 * (2 * 2 * 64 * 64 * 4))
     assert lib.kda_chunk_bwd_workspace(1, 64, 2, 48, 64) == 0
     assert lib.kda_chunk_bwd_workspace(1, 0, 2, 64, 64) == 0
     assert bwd_call(lib, dt=3) == 4
