@@ -136,38 +136,42 @@ __device__ __forceinline__ float gate_of(float zv, float eA, float g_min, unsign
 }
 
 // The switched activations of one chunk into LDS: q_hat, k_hat, cumulative
-// log-decay G (pitch P), beta and the inverse norms.  Tokens past the end are
+// log-decay G in log2 units (pitch P), beta and the inverse norms.  Tokens past the end are
 // zero rows with g = 0 and beta = 0 (identity transitions).
-template <typename T, int DK, int P>
+// Loads of tokens past the end read the last token (a valid address, so no
+// branch and no wait before use) and are replaced by zero afterwards.
+template <typename T, int DK, int P, int NTHR>
 __device__ void prep_chunk(const BwdArgs& a, int b, int h, int t0, float (*sQ)[P], float (*sK)[P], float (*sG)[P],
                            float* sB, float* sRq, float* sRk, float (*sZ)[P] = nullptr) {
-    const int tid = threadIdx.x, nthr = blockDim.x;
-    const int lane = tid & 63, wave = tid >> 6, nw = nthr >> 6;
+    constexpr int NPT = C * DK / NTHR;
+    static_assert(NPT * NTHR == C * DK, "whole rows per thread group");
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6, nw = NTHR >> 6;
     const float eA = (a.flags & kGateIn) ? expf(a.A_log[h]) : 0.f;
-    for (int e = tid; e < C * DK; e += nthr) {
-        const int t = e / DK, d = e % DK;
-        const int tok = t0 + t;
-        float qv = 0.f, kv = 0.f, zv = 0.f, g = 0.f;
-        if (tok < a.T) {
-            const size_t idx = (((size_t)b * a.T + tok) * a.H + h) * DK + d;
-            qv = ldf<T>(a.q, idx);
-            kv = ldf<T>(a.k, idx);
-            zv = ldf<T>(a.z, idx);
-            g = gate_of(zv, eA, a.g_min, a.flags);
-        }
-        sQ[t][d] = qv;
-        sK[t][d] = kv;
-        sG[t][d] = g;
-        if (sZ) sZ[t][d] = zv;
+    float qv[NPT], kv[NPT], zv[NPT];
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) {
+        const int e = tid + u * NTHR, t = e / DK, d = e % DK;
+        const int tok = min(t0 + t, a.T - 1);
+        const size_t idx = (((size_t)b * a.T + tok) * a.H + h) * DK + d;
+        qv[u] = ldf<T>(a.q, idx);
+        kv[u] = ldf<T>(a.k, idx);
+        zv[u] = ldf<T>(a.z, idx);
     }
-    for (int t = tid; t < C; t += nthr) {
-        const int tok = t0 + t;
-        float bt = 0.f;
-        if (tok < a.T) {
-            const float br = ldf<T>(a.beta_raw, ((size_t)b * a.T + tok) * a.H + h);
-            bt = (a.flags & kBetaSig) ? 1.f / (1.f + expf(-br)) : br;
-        }
-        sB[t] = bt;
+    float br = 0.f;
+    if (tid < C) br = ldf<T>(a.beta_raw, ((size_t)b * a.T + min(t0 + tid, a.T - 1)) * a.H + h);
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) {
+        const int e = tid + u * NTHR, t = e / DK, d = e % DK;
+        const bool valid = t0 + t < a.T;
+        sQ[t][d] = valid ? qv[u] : 0.f;
+        sK[t][d] = valid ? kv[u] : 0.f;
+        sG[t][d] = valid ? gate_of(zv[u], eA, a.g_min, a.flags) : 0.f;
+        if (sZ) sZ[t][d] = valid ? zv[u] : 0.f;
+    }
+    if (tid < C) {
+        const float bt = (a.flags & kBetaSig) ? 1.f / (1.f + expf(-br)) : br;
+        sB[tid] = (t0 + tid < a.T) ? bt : 0.f;
     }
     __syncthreads();
     // inverse norms: one wave per token at a time
@@ -188,15 +192,15 @@ __device__ void prep_chunk(const BwdArgs& a, int b, int h, int t0, float (*sQ)[P
         }
     }
     __syncthreads();
-    for (int e = tid; e < C * DK; e += nthr) {
+    for (int e = tid; e < C * DK; e += NTHR) {
         const int t = e / DK, d = e % DK;
         sQ[t][d] *= sRq[t];
         sK[t][d] *= sRk[t];
     }
-    for (int d = tid; d < DK; d += nthr) {
+    for (int d = tid; d < DK; d += NTHR) {
         float acc = 0.f;
         for (int t = 0; t < C; ++t) {
-            acc += sG[t][d];
+            acc += sG[t][d] * kLog2e;  // G in log2 units: every decay factor is one exp2
             sG[t][d] = acc;
         }
     }
@@ -207,59 +211,87 @@ __device__ void prep_chunk(const BwdArgs& a, int b, int h, int t0, float (*sQ)[P
 
 // ------------------------------------------------------------------ 1. ops
 
+// Each operand matrix is assembled in LDS in tile order, then written out as
+// whole 16-byte pieces.
 template <typename T, int DK>
 __global__ __launch_bounds__(256) void kda_bwd_ops_kernel(const BwdArgs a) {
+    using O = Ops<DK>;
     constexpr int P = DK + 1;  // odd pitch: the pair loop reads columns across rows
+    constexpr int KSD = (DK + 31) / 32;
+    constexpr int kStage = (int)(bwd_tiles(C, DK) > 2 * C * C ? bwd_tiles(C, DK) : 2 * C * C);
     __shared__ float sQ[C][P], sK[C][P], sG[C][P];
     __shared__ float sB[C], sRq[C], sRk[C];
     __shared__ float sAt[C][C + 1];
+    __shared__ __align__(16) float sSt[kStage];
     const int n = blockIdx.x % a.NC;
     const int bh = blockIdx.x / a.NC;
     const int b = bh / a.H, h = bh % a.H;
     const int tid = threadIdx.x;
-    prep_chunk<T, DK, P>(a, b, h, n * C, sQ, sK, sG, sB, sRq, sRk);
-
+    prep_chunk<T, DK, P, 256>(a, b, h, n * C, sQ, sK, sG, sB, sRq, sRk);
     float* op = a.ops + ((size_t)bh * a.NC + n) * bwd_op_floats(DK);
-    for (int e = tid; e < C * DK; e += blockDim.x) {
-        const int t = e / DK, d = e % DK;
-        const float G = sG[t][d], GC = sG[C - 1][d];
-        const float kd = sK[t][d] * expf(G);
-        const float qp = sQ[t][d] * expf(G);
-        const float kp = sK[t][d] * expf(GC - G);  // exponent <= 0
-        op[Ops<DK>::Kd + tile_pos(t, d, DK)] = kd;
-        op[Ops<DK>::Kp + tile_pos(t, d, DK)] = kp;
-        op[Ops<DK>::KdT + tile_pos(d, t, C)] = kd;
-        op[Ops<DK>::QpT + tile_pos(d, t, C)] = qp;
-        op[Ops<DK>::KpT + tile_pos(d, t, C)] = kp;
-    }
-    if constexpr (DK < 32) {  // the unused contraction slots of the [C x DK] tiles
-        for (int e = tid; e < C * (32 - DK); e += blockDim.x) {
-            const int t = e / (32 - DK), k = DK + e % (32 - DK);
-            op[Ops<DK>::Kd + tile_pos(t, k, DK)] = 0.f;
-            op[Ops<DK>::Kp + tile_pos(t, k, DK)] = 0.f;
-        }
-    }
-    for (int d = tid; d < DK; d += blockDim.x) op[Ops<DK>::gamS + d] = op[Ops<DK>::gamA + d] = expf(sG[C - 1][d]);
-    for (int t = tid; t < C; t += blockDim.x) op[Ops<DK>::betaS + t] = op[Ops<DK>::betaA + t] = sB[t];
-    // At (strictly lower) and Aqk (lower incl. diagonal), each decay factor in
-    // one exponent exp(G_i - G_j) <= 1
-    for (int e = tid; e < C * C; e += blockDim.x) {
-        const int i = e / C, j = e % C;
-        float akk = 0.f, aqk = 0.f;
-        if (j <= i) {
-            for (int d = 0; d < DK; ++d) {
-                const float x = sK[j][d] * expf(sG[i][d] - sG[j][d]);
-                akk = fmaf(sK[i][d], x, akk);
-                aqk = fmaf(sQ[i][d], x, aqk);
+    auto flush = [&](size_t dst, int count) {  // sSt[0, count) -> op[dst, dst + count)
+        __syncthreads();
+        for (int e = 4 * tid; e < count; e += 4 * 256)
+            *reinterpret_cast<float4*>(op + dst + e) = *reinterpret_cast<const float4*>(sSt + e);
+        __syncthreads();
+    };
+    // [C x DK] operands: Kd = k_hat exp(G), Kp = k_hat exp(G_C - G); slots past DK are zero
+    for (int which = 0; which < 2; ++which) {
+        for (int e = tid; e < C * 32 * KSD; e += 256) {
+            const int t = e / (32 * KSD), k = e % (32 * KSD);
+            float x = 0.f;
+            if (k < DK) {
+                const float G = sG[t][k];
+                x = sK[t][k] * exp2_fast(which == 0 ? G : sG[C - 1][k] - G);  // exponent <= 0
             }
+            sSt[tile_pos(t, k, DK)] = x;
         }
-        if (j >= i) akk = 0.f;
-        sAt[i][j] = akk;
-        op[Ops<DK>::At + i * C + j] = akk;
-        op[Ops<DK>::AqkT + tile_pos(j, i, C)] = aqk;
+        flush(which == 0 ? O::Kd : O::Kp, (int)bwd_tiles(C, DK));
     }
-    __syncthreads();
-    // T = (I + Diag(beta) At)^-1: unit lower triangular, column j by lane j
+    // [DK x C] operands: KpT, QpT, KdT
+    for (int which = 0; which < 3; ++which) {
+        for (int e = tid; e < C * DK; e += 256) {
+            const int d = e / C, t = e % C;
+            const float G = sG[t][d];
+            const float x = which == 0 ? sK[t][d] * exp2_fast(sG[C - 1][d] - G)
+                          : (which == 1 ? sQ[t][d] : sK[t][d]) * exp2_fast(G);
+            sSt[tile_pos(d, t, C)] = x;
+        }
+        flush(which == 0 ? O::KpT : (which == 1 ? O::QpT : O::KdT), (int)bwd_tiles(DK, C));
+    }
+    for (int d = tid; d < DK; d += 256) op[O::gamS + d] = op[O::gamA + d] = exp2_fast(sG[C - 1][d]);
+    for (int t = tid; t < C; t += 256) op[O::betaS + t] = op[O::betaA + t] = sB[t];
+    // At (strictly lower, row-major) and Aqk^T (tiles), each decay factor in one
+    // exponent exp(G_i - G_j) <= 1
+    for (int e = tid; e < C * C; e += 256) {  // zeros above the diagonal
+        const int i = e / C, j = e % C;
+        if (j > i) {
+            sAt[i][j] = 0.f;
+            op[O::At + i * C + j] = 0.f;
+            sSt[tile_pos(j, i, C)] = 0.f;
+        }
+    }
+    // pairs j <= i enumerated densely (no idle lanes): pair p has row i with
+    // i (i + 1) / 2 <= p < (i + 1) (i + 2) / 2
+    for (int p = tid; p < C * (C + 1) / 2; p += 256) {
+        int i = (int)((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
+        if ((i + 1) * (i + 2) / 2 <= p) ++i;
+        if (i * (i + 1) / 2 > p) --i;
+        const int j = p - i * (i + 1) / 2;
+        float akk = 0.f, aqk = 0.f;
+        for (int d = 0; d < DK; ++d) {
+            const float x = sK[j][d] * exp2_fast(sG[i][d] - sG[j][d]);
+            akk = fmaf(sK[i][d], x, akk);
+            aqk = fmaf(sQ[i][d], x, aqk);
+        }
+        if (j == i) akk = 0.f;
+        sAt[i][j] = akk;
+        op[O::At + i * C + j] = akk;
+        sSt[tile_pos(j, i, C)] = aqk;
+    }
+    flush(O::AqkT, C * C);
+    // T = (I + Diag(beta) At)^-1: unit lower triangular, column j by lane j;
+    // T into sSt[0, C^2), T^T into sSt[C^2, 2 C^2)
     if (tid < C) {
         const int j = tid;
         float col[C];
@@ -272,9 +304,14 @@ __global__ __launch_bounds__(256) void kda_bwd_ops_kernel(const BwdArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < C; ++i) {
-            op[Ops<DK>::Tm + tile_pos(i, j, C)] = col[i];
-            op[Ops<DK>::TT + tile_pos(j, i, C)] = col[i];
+            sSt[tile_pos(i, j, C)] = col[i];
+            sSt[C * C + tile_pos(j, i, C)] = col[i];
         }
+    }
+    __syncthreads();
+    for (int e = 4 * tid; e < C * C; e += 4 * 256) {
+        *reinterpret_cast<float4*>(op + O::Tm + e) = *reinterpret_cast<const float4*>(sSt + e);
+        *reinterpret_cast<float4*>(op + O::TT + e) = *reinterpret_cast<const float4*>(sSt + C * C + e);
     }
 }
 
@@ -296,7 +333,7 @@ __device__ __forceinline__ void stage_kib(const unsigned char* src, float* dst, 
 // 16 R + 4 gq + i, column r).  Each chunk's state-pass operators are copied
 // into LDS one chunk ahead.
 template <typename T, int DK, int NSW>
-__global__ __launch_bounds__(64 * NSW) void kda_bwd_states_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_states_kernel(const BwdArgs a) {
     using O = Ops<DK>;
     constexpr int NBD = DK / 16, KSD = (DK + 31) / 32;
     constexpr int kPieces = (int)(O::sizeS / 256);
@@ -307,23 +344,49 @@ __global__ __launch_bounds__(64 * NSW) void kda_bwd_states_kernel(const BwdArgs 
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, gq = lane >> 4;
     const int col = 16 * (grp * NSW + w) + r;
     const unsigned char* blk = reinterpret_cast<const unsigned char*>(a.ops + (size_t)bh * a.NC * bwd_op_floats(DK));
+    // wave NSW only copies operators into LDS (one chunk ahead); the compute
+    // waves never have a copy outstanding, so their LDS reads wait for nothing
+    if (w == NSW) {
+        stage_kib(blk, sOp[0], kPieces, 0, 1);
+        wait_vmcnt<0>();
+        __syncthreads();
+        for (int n = 0; n < a.NC; ++n) {
+            if (n + 1 < a.NC) stage_kib(blk + (size_t)(n + 1) * bwd_op_floats(DK) * 4, sOp[(n + 1) & 1], kPieces, 0, 1);
+            wait_vmcnt<0>();
+            __syncthreads();
+        }
+        return;
+    }
     floatx4 S[NBD];
 #pragma unroll
     for (int R = 0; R < NBD; ++R)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             S[R][i] = a.S0 ? a.S0[((size_t)bh * DK + 16 * R + 4 * gq + i) * a.Dv + col] : 0.f;
-    stage_kib(blk, sOp[0], kPieces, w, NSW);
-    wait_vmcnt<0>();
-    __syncthreads();
-    for (int n = 0; n < a.NC; ++n) {
-        const int buf = n & 1;
-        if (n + 1 < a.NC) stage_kib(blk + (size_t)(n + 1) * bwd_op_floats(DK) * 4, sOp[buf ^ 1], kPieces, w, NSW);
+    // this lane's values of one chunk: tokens 16 tb + 4 gq + i, column col
+    auto load_v = [&](int n, float (&vv)[8]) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int tok = n * C + 16 * (u >> 2) + 4 * gq + (u & 3);
+            const float x = ldf<T>(a.v, (((size_t)b * a.T + min(tok, a.T - 1)) * a.H + h) * a.Dv + col);
+            vv[u] = tok < a.T ? x : 0.f;
+        }
+    };
+    // the state at the start of chunk n (its stores are waited for a chunk later)
+    auto store_state = [&](int n) {
         float* Sn = a.states + ((size_t)bh * a.NC + n) * DK * a.Dv;
 #pragma unroll
         for (int R = 0; R < NBD; ++R)
 #pragma unroll
             for (int i = 0; i < 4; ++i) Sn[(size_t)(16 * R + 4 * gq + i) * a.Dv + col] = S[R][i];
+    };
+    float vcur[8], vnext[8];
+    load_v(0, vcur);
+    if (a.NC > 0) store_state(0);
+    __syncthreads();
+    for (int n = 0; n < a.NC; ++n) {
+        const int buf = n & 1;
+        if (n + 1 < a.NC) load_v(n + 1, vnext);  // the next chunk's values travel during this one
         const float* op = sOp[buf];
         // E = V - Kd S, scaled by beta per token
         floatx4 Eb[2];
@@ -334,9 +397,8 @@ __global__ __launch_bounds__(64 * NSW) void kda_bwd_states_kernel(const BwdArgs 
             for (int s = 0; s < KSD; ++s) acc = mma(frag_tile(op + O::Kd, tb, s, KSD), frag_strip(S, s), acc);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = 16 * tb + 4 * gq + i, tok = n * C + t;
-                const float v = tok < a.T ? ldf<T>(a.v, (((size_t)b * a.T + tok) * a.H + h) * a.Dv + col) : 0.f;
-                Eb[tb][i] = op[O::betaS + t] * (v - acc[i]);
+                const int t = 16 * tb + 4 * gq + i;
+                Eb[tb][i] = op[O::betaS + t] * (vcur[4 * tb + i] - acc[i]);
             }
         }
         // U = T (beta E)
@@ -356,15 +418,17 @@ __global__ __launch_bounds__(64 * NSW) void kda_bwd_states_kernel(const BwdArgs 
             for (int i = 0; i < 4; ++i) acc[i] = op[O::gamS + 16 * R + 4 * gq + i] * S[R][i];
             S[R] = mma(frag_tile(op + O::KpT, R, 0, 1), Uf, acc);
         }
-        wait_vmcnt<0>();   // the next chunk's operators are in LDS
-        __syncthreads();   // ... for every wave, and this chunk's are no longer read
+#pragma unroll
+        for (int u = 0; u < 8; ++u) vcur[u] = vnext[u];
+        __syncthreads();   // the next chunk's operators are in LDS, this chunk's no longer read
+        if (n + 1 < a.NC) store_state(n + 1);
     }
 }
 
 // -------------------------------------------------------------- 3. adjoint
 
 template <typename T, int DK, int NSW>
-__global__ __launch_bounds__(64 * NSW) void kda_bwd_adjoint_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_adjoint_kernel(const BwdArgs a) {
     using O = Ops<DK>;
     constexpr int NBD = DK / 16, KSD = (DK + 31) / 32;
     constexpr int kPieces = (int)(O::sizeA / 256);
@@ -376,31 +440,50 @@ __global__ __launch_bounds__(64 * NSW) void kda_bwd_adjoint_kernel(const BwdArgs
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, gq = lane >> 4;
     const int col = 16 * (grp * NSW + w) + r;
     const unsigned char* blk = reinterpret_cast<const unsigned char*>(a.ops + (size_t)bh * a.NC * bwd_op_floats(DK) + A0);
+    if (w == NSW) {  // the copy wave, one chunk ahead (chunks in reverse order)
+        if (a.NC > 0) stage_kib(blk + (size_t)(a.NC - 1) * bwd_op_floats(DK) * 4, sOp[0], kPieces, 0, 1);
+        wait_vmcnt<0>();
+        __syncthreads();
+        for (int n = a.NC - 1, it = 0; n >= 0; --n, ++it) {
+            if (n > 0) stage_kib(blk + (size_t)(n - 1) * bwd_op_floats(DK) * 4, sOp[(it + 1) & 1], kPieces, 0, 1);
+            wait_vmcnt<0>();
+            __syncthreads();
+        }
+        return;
+    }
     floatx4 dS[NBD];
 #pragma unroll
     for (int R = 0; R < NBD; ++R)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             dS[R][i] = a.dS_T ? a.dS_T[((size_t)bh * DK + 16 * R + 4 * gq + i) * a.Dv + col] : 0.f;
-    if (a.NC > 0) stage_kib(blk + (size_t)(a.NC - 1) * bwd_op_floats(DK) * 4, sOp[0], kPieces, w, NSW);
-    wait_vmcnt<0>();
-    __syncthreads();
-    for (int n = a.NC - 1, it = 0; n >= 0; --n, ++it) {
-        const int buf = it & 1;
-        if (n > 0) stage_kib(blk + (size_t)(n - 1) * bwd_op_floats(DK) * 4, sOp[buf ^ 1], kPieces, w, NSW);
+    // dO of one chunk as the B operand of a product over its tokens
+    auto load_do = [&](int n, Frag<float>& f) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int tok = n * C + slot_index(gq, j);
+            const float x = ldf<T>(a.dout, (((size_t)b * a.T + min(tok, a.T - 1)) * a.H + h) * a.Dv + col);
+            f.v[j] = tok < a.T ? x : 0.f;
+        }
+    };
+    // the adjoint at the end of chunk n (its stores are waited for a chunk later)
+    auto store_adj = [&](int n) {
         float* An = a.adj + ((size_t)bh * a.NC + n) * DK * a.Dv;
 #pragma unroll
         for (int R = 0; R < NBD; ++R)
 #pragma unroll
             for (int i = 0; i < 4; ++i) An[(size_t)(16 * R + 4 * gq + i) * a.Dv + col] = dS[R][i];
+    };
+    Frag<float> dOf, dOnext;
+    if (a.NC > 0) {
+        load_do(a.NC - 1, dOf);
+        store_adj(a.NC - 1);
+    }
+    __syncthreads();
+    for (int n = a.NC - 1, it = 0; n >= 0; --n, ++it) {
+        const int buf = it & 1;
+        if (n > 0) load_do(n - 1, dOnext);  // the previous chunk's dO travels during this one
         const float* op = sOp[buf];
-        // dO as the B operand of a product over the chunk's tokens
-        Frag<float> dOf;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int tok = n * C + slot_index(gq, j);
-            dOf.v[j] = tok < a.T ? ldf<T>(a.dout, (((size_t)b * a.T + tok) * a.H + h) * a.Dv + col) : 0.f;
-        }
         // dU = Aqk^T dO + Kp dS'
         floatx4 dU[2];
 #pragma unroll
@@ -431,8 +514,9 @@ __global__ __launch_bounds__(64 * NSW) void kda_bwd_adjoint_kernel(const BwdArgs
             acc = mma(frag_tile(op + (O::QpT - A0), R, 0, 1), dOf, acc);
             dS[R] = mma(frag_tile(op + (O::KdT - A0), R, 0, 1), Xf, acc);
         }
-        wait_vmcnt<0>();
+        dOf = dOnext;
         __syncthreads();
+        if (n > 0) store_adj(n - 1);
     }
     if (a.dS0) {
 #pragma unroll
@@ -495,7 +579,7 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, r = lane & 15, gq = lane >> 4;
     const int t0 = n * C;
-    prep_chunk<T, DK, DK>(a, b, h, t0, sQ, sK, sG, sB, sRq, sRk, sZ);
+    prep_chunk<T, DK, DK, 512>(a, b, h, t0, sQ, sK, sG, sB, sRq, sRk, sZ);
     const float* op = a.ops + ((size_t)bh * a.NC + n) * bwd_op_floats(DK);
     const float* S0 = a.states + ((size_t)bh * a.NC + n) * DK * DV;
     const float* dSC = a.adj + ((size_t)bh * a.NC + n) * DK * DV;
@@ -503,7 +587,8 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
 
     for (int e = tid; e < C * DV; e += NT) {
         const int t = e / DV, j = e % DV;
-        sdO[t * PV + j] = (t0 + t < a.T) ? ldf<T>(a.dout, row_of(t) * DV + j) : 0.f;
+        const float x = ldf<T>(a.dout, (((size_t)b * a.T + min(t0 + t, a.T - 1)) * a.H + h) * DV + j);
+        sdO[t * PV + j] = (t0 + t < a.T) ? x : 0.f;
     }
     for (int t = tid; t < C; t += NT) sdB[t] = 0.f;
     __syncthreads();
@@ -528,7 +613,8 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * tb + 4 * gq + i;
-                const float vv = (t0 + t < a.T) ? ldf<T>(a.v, row_of(t) * DV + col) : 0.f;
+                const float vx = ldf<T>(a.v, (((size_t)b * a.T + min(t0 + t, a.T - 1)) * a.H + h) * DV + col);
+                const float vv = (t0 + t < a.T) ? vx : 0.f;
                 E[tb][i] = vv - E[tb][i];           // E = V - Kd S
                 Eb[tb][i] = sB[t] * E[tb][i];
                 dO[tb][i] = sdO[t * PV + col];
@@ -612,34 +698,47 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
         const int d = 16 * w + r;
         const float GC = sG[C - 1][d];
         float gcpart = 0.f;
+        float Gt[2][4], dkp[2][4], dkm[2][4];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * tb + 4 * gq + i;
-                const float Gt = sG[t][d];
-                const float et = expf(Gt), ect = expf(GC - Gt);
-                float dq = dQp[tb][i] * et;
-                float dkp = dKd[tb][i] * et;
-                float dkm = dKp[tb][i] * ect;
+                Gt[tb][i] = sG[t][d];
+                const float et = exp2_fast(Gt[tb][i]), ect = exp2_fast(GC - Gt[tb][i]);
+                dqh[tb][i] = dQp[tb][i] * et;
+                dkp[tb][i] = dKd[tb][i] * et;
+                dkm[tb][i] = dKp[tb][i] * ect;
                 gcpart = fmaf(dKp[tb][i], sK[t][d] * ect, gcpart);
-#pragma unroll 2
-                for (int s = 0; s < C; ++s) {
-                    const float Gs = sG[s][d];
-                    const float e = expf(-fabsf(Gt - Gs));  // exp(G_t - G_s) for s <= t, exp(G_s - G_t) for s >= t
-                    if (s <= t) {
-                        dq = fmaf(sdAqk[t][s] * sK[s][d], e, dq);
-                        dkp = fmaf(sdAt[t][s] * sK[s][d], e, dkp);
-                    }
-                    if (s >= t) dkm = fmaf(sdAqk[s][t] * sQ[s][d] + sdAt[s][t] * sK[s][d], e, dkm);
+            }
+        // partner s outermost: its G, k_hat, q_hat are read once for the eight
+        // tokens.  The stored triangles are zero outside their masks (dAqk[t][s]
+        // for s > t, dAt[t][s] for s >= t), so every term is taken, with the
+        // one exponent exp(-|G_t - G_s|) <= 1 for both orders.
+        for (int s = 0; s < C; ++s) {
+            const float Gs = sG[s][d], Ks = sK[s][d], Qs = sQ[s][d];
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 16 * tb + 4 * gq + i;
+                    const float e = exp2_fast(-fabsf(Gt[tb][i] - Gs));
+                    dqh[tb][i] = fmaf(sdAqk[t][s] * Ks, e, dqh[tb][i]);
+                    dkp[tb][i] = fmaf(sdAt[t][s] * Ks, e, dkp[tb][i]);
+                    dkm[tb][i] = fmaf(sdAqk[s][t] * Qs + sdAt[s][t] * Ks, e, dkm[tb][i]);
                 }
-                dqh[tb][i] = dq;
-                dkh[tb][i] = dkp + dkm;
-                dGv[tb][i] = sQ[t][d] * dq + sK[t][d] * (dkp - dkm);
+        }
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * tb + 4 * gq + i;
+                dkh[tb][i] = dkp[tb][i] + dkm[tb][i];
+                dGv[tb][i] = sQ[t][d] * dqh[tb][i] + sK[t][d] * (dkp[tb][i] - dkm[tb][i]);
             }
         gcpart += __shfl_xor(gcpart, 16, 64);
         gcpart += __shfl_xor(gcpart, 32, 64);
-        if (gq == 0) sGC[d] = gcpart + dgam * expf(GC);
+        if (gq == 0) sGC[d] = gcpart + dgam * exp2_fast(GC);
     }
     __syncthreads();  // every read of the value rows is done: reuse their space
     float* fdq = sBig;
@@ -745,10 +844,10 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
     const unsigned serial_groups = heads * (unsigned)(DV / 16 / NSW);
     if (chunk_heads > 0) {
         hipLaunchKernelGGL((kda_bwd_ops_kernel<T, DK>), dim3(chunk_heads), dim3(256), 0, s, a);
-        hipLaunchKernelGGL((kda_bwd_states_kernel<T, DK, NSW>), dim3(serial_groups), dim3(64 * NSW), 0, s, a);
+        hipLaunchKernelGGL((kda_bwd_states_kernel<T, DK, NSW>), dim3(serial_groups), dim3(64 * (NSW + 1)), 0, s, a);
     }
     if (heads > 0)  // with no chunk it passes dS_T (or zero) to dS0
-        hipLaunchKernelGGL((kda_bwd_adjoint_kernel<T, DK, NSW>), dim3(serial_groups), dim3(64 * NSW), 0, s, a);
+        hipLaunchKernelGGL((kda_bwd_adjoint_kernel<T, DK, NSW>), dim3(serial_groups), dim3(64 * (NSW + 1)), 0, s, a);
     if (chunk_heads > 0)
         hipLaunchKernelGGL((kda_bwd_grads_kernel<T, DK, DV>), dim3(chunk_heads), dim3(512), 0, s, a);
     if (a.H > 0)
