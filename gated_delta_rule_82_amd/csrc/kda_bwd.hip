@@ -826,12 +826,18 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
 
 // ------------------------------------------------------------------- 5. dA
 
+// One workgroup per head: the B * NC chunk parts of dA_log[h], summed in a
+// fixed order (deterministic).
 __global__ __launch_bounds__(256) void kda_bwd_dA_kernel(const BwdArgs a) {
-    const int h = blockIdx.x * blockDim.x + threadIdx.x;
-    if (h >= a.H) return;
+    __shared__ float sRed[4];
+    const int h = blockIdx.x;
     float s = 0.f;
-    for (int bn = 0; bn < a.B * a.NC; ++bn) s += a.dA_part[(size_t)bn * a.H + h];
-    a.dA_log[h] = (a.flags & kGateIn) ? s : 0.f;
+    for (int bn = threadIdx.x; bn < a.B * a.NC; bn += 256) s += a.dA_part[(size_t)bn * a.H + h];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+    if ((threadIdx.x & 63) == 0) sRed[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) a.dA_log[h] = (a.flags & kGateIn) ? (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]) : 0.f;
 }
 
 // ---------------------------------------------------------------- launches
@@ -851,7 +857,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
     if (chunk_heads > 0)
         hipLaunchKernelGGL((kda_bwd_grads_kernel<T, DK, DV>), dim3(chunk_heads), dim3(512), 0, s, a);
     if (a.H > 0)
-        hipLaunchKernelGGL(kda_bwd_dA_kernel, dim3((unsigned)((a.H + 255) / 256)), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(kda_bwd_dA_kernel, dim3((unsigned)a.H), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
