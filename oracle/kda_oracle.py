@@ -581,3 +581,26 @@ def backward(q, k, v, z, beta_raw, A_log, do, dS_T=None, S0=None, g_min=G_MIN_DE
         dz = dg
         dA = np.zeros(H)
     return {"dq": dq, "dk": dk, "dv": dv, "dz": dz, "dbeta_raw": dbeta_raw, "dA_log": dA, "dS0": dS}
+
+
+def backward_grouped(q, k, v, z, beta_raw, A_log, do, dt_bias=None, dS_T=None, S0=None,
+                     g_min=G_MIN_DEFAULT, flags=FLAGS_DEFAULT):
+    """Gradients of forward_grouped: q, k [B, T, H, Dk] feed HV = G H value
+    heads (value head hv reads q/k head hv // G) and dt_bias [HV, Dk] is
+    added to the gate logit.  The gradient of a q/k head is the sum over the
+    value heads that read it; the bias gradient is the logit gradient summed
+    over batch and tokens.  Returns the dict of `backward` with dq, dk
+    [B, T, H, Dk] and, with a bias, ddt_bias [HV, Dk]."""
+    if dt_bias is not None and not flags & GATE_IN_KERNEL:
+        raise ValueError("dt_bias biases the in-kernel gate")
+    q = np.asarray(q, dtype=np.float64)
+    B, T, H, Dk = q.shape
+    HV = np.asarray(v).shape[2]
+    g = backward(group_heads(q, HV), group_heads(k, HV), v, biased_logit(z, dt_bias), beta_raw, A_log, do,
+                 dS_T, S0, g_min, flags)
+    G = HV // H
+    g["dq"] = g["dq"].reshape(B, T, H, G, Dk).sum(axis=3)
+    g["dk"] = g["dk"].reshape(B, T, H, G, Dk).sum(axis=3)
+    if dt_bias is not None:
+        g["ddt_bias"] = g["dz"].sum(axis=(0, 1))
+    return g

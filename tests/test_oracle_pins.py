@@ -747,3 +747,46 @@ class TestBackward:
         assert rel(grads["dv"][:, 0], (beta[:, 0] * qk)[..., None] * do[:, 0]) < 1e-14
         assert rel(grads["dbeta_raw"][:, 0], qk * np.sum(v[:, 0] * do[:, 0], axis=-1)) < 1e-14
         assert np.max(np.abs(grads["dz"])) == 0.0
+
+
+class TestBackwardGrouped:
+    def test_matches_central_differences(self):
+        # two q/k heads read by four value heads, with a gate bias
+        rng = np.random.default_rng(70)
+        B, T, H, HV, Dk, Dv = 1, 5, 2, 4, 3, 2
+        q, k = (rng.standard_normal((B, T, H, Dk)) for _ in range(2))
+        v = rng.standard_normal((B, T, HV, Dv))
+        z = rng.standard_normal((B, T, HV, Dk))
+        br = rng.standard_normal((B, T, HV))
+        A = rng.normal(0, 0.5, HV)
+        db = rng.normal(0, 1.0, (HV, Dk))
+        S0 = rng.normal(0, 0.3, (B, HV, Dk, Dv))
+        do = rng.standard_normal((B, T, HV, Dv))
+        dST = rng.standard_normal((B, HV, Dk, Dv))
+        args = dict(q=q, k=k, z=z, dt_bias=db)
+        grads = ora.backward_grouped(q, k, v, z, br, A, do, db, dST, S0)
+
+        def loss(a):
+            o, S = ora.forward_grouped(a["q"], a["k"], v, a["z"], br, A, a["dt_bias"], S0)
+            return float(np.sum(do * o) + np.sum(dST * S))
+
+        h = 1e-6
+        for n, gname in (("q", "dq"), ("k", "dk"), ("z", "dz"), ("dt_bias", "ddt_bias")):
+            x = args[n]
+            fd = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                ap, am = dict(args), dict(args)
+                ap[n] = x.copy(); ap[n][idx] += h
+                am[n] = x.copy(); am[n][idx] -= h
+                fd[idx] = (loss(ap) - loss(am)) / (2 * h)
+            assert rel(grads[gname], fd) < 1e-6, (n, rel(grads[gname], fd))
+
+    def test_equal_heads_without_bias_is_the_plain_backward(self):
+        rng = np.random.default_rng(71)
+        q, k, v, g, beta, S0 = rand_problem(rng, T=11)
+        do = rng.standard_normal(v.shape)
+        a = ora.backward(q, k, v, g, beta, np.zeros(q.shape[2]), do, None, S0, flags=0)
+        b = ora.backward_grouped(q, k, v, g, beta, np.zeros(q.shape[2]), do, None, None, S0, flags=0)
+        for n in ("dq", "dk", "dv", "dz", "dbeta_raw", "dS0"):
+            assert np.array_equal(a[n], b[n]), n
+        assert "ddt_bias" not in b
