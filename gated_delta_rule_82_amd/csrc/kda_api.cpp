@@ -263,42 +263,54 @@ kda_status kda_segment_compose(int n_seg, const float* M, const float* S_tilde,
     return kda::launch_compose(Dk, a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-// Backward workspace: operators, chunk-start states, chunk-end adjoints and
-// the per-chunk dA_log parts, each region 256-byte aligned.
+// Backward workspace: operators, chunk-start states, chunk-end adjoints, the
+// per-chunk dA_log parts and, for grouped heads, the per-value-head q/k
+// gradients and the per-chunk gate-bias parts; each region 256-byte aligned.
 struct BwdWorkspace {
-    size_t ops, states, adj, dA, total;
+    size_t ops, states, adj, dA, dqk, dbias, total;
 };
-static BwdWorkspace bwd_workspace(int B, int T, int H, int Dk, int Dv) {
+static BwdWorkspace bwd_workspace(int B, int T, int HV, int Dk, int Dv, bool grouped, bool bias) {
     BwdWorkspace w{};
     const size_t NC = (size_t)(T + kda::kBwdChunk - 1) / kda::kBwdChunk;
-    const size_t BHN = (size_t)B * H * NC;
+    const size_t BHN = (size_t)B * HV * NC;
     w.ops = 0;
     w.states = kda::round_up(BHN * kda::bwd_op_floats(Dk) * 4, 256);
     w.adj = w.states + kda::round_up(BHN * Dk * Dv * 4, 256);
     w.dA = w.adj + kda::round_up(BHN * Dk * Dv * 4, 256);
-    w.total = w.dA + kda::round_up(BHN * 4, 256);
+    w.dqk = w.dA + kda::round_up(BHN * 4, 256);
+    w.dbias = w.dqk + (grouped ? kda::round_up(2 * (size_t)B * T * HV * Dk * 4, 256) : 0);
+    w.total = w.dbias + (bias ? kda::round_up(BHN * Dk * 4, 256) : 0);
     return w;
 }
 
 size_t kda_chunk_bwd_workspace(int B, int T, int H, int Dk, int Dv) {
     if (B < 0 || T < 0 || H < 0 || !dim_ok(Dk) || !dim_ok(Dv)) return 0;
-    return bwd_workspace(B, T, H, Dk, Dv).total;
+    return bwd_workspace(B, T, H, Dk, Dv, false, false).total;
 }
 
-kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* z,
-                         const void* beta_raw, const float* A_log, const float* S0,
-                         const void* dout, const float* dS_T,
-                         void* dq, void* dk, void* dv, void* dz, void* dbeta_raw,
-                         float* dA_log, float* dS0,
-                         int B, int T, int H, int Dk, int Dv, float g_min, unsigned flags,
-                         kda_dtype dt, void* workspace, size_t workspace_bytes,
-                         hipStream_t stream) {
+size_t kda_chunk_bwd_grouped_workspace(int B, int T, int H, int HV, int Dk, int Dv, int with_bias) {
+    if (B < 0 || T < 0 || H < 0 || HV < 0 || !dim_ok(Dk) || !dim_ok(Dv)) return 0;
+    if (HV > 0 && !groups_ok(H, HV)) return 0;
+    return bwd_workspace(B, T, HV, Dk, Dv, HV > H, with_bias != 0).total;
+}
+
+static kda_status chunk_bwd_impl(const void* q, const void* k, const void* v, const void* z,
+                                 const void* beta_raw, const float* A_log, const float* dt_bias,
+                                 const float* S0, const void* dout, const float* dS_T,
+                                 void* dq, void* dk, void* dv, void* dz, void* dbeta_raw,
+                                 float* dA_log, float* ddt_bias, float* dS0,
+                                 int B, int T, int H, int HV, int Dk, int Dv, float g_min, unsigned flags,
+                                 kda_dtype dt, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!dtype_ok(dt) || !flags_ok(flags)) return KDA_ERR_DTYPE;
-    if (B < 0 || T < 0 || H < 0 || !dim_ok(Dk) || !dim_ok(Dv)) return KDA_ERR_SHAPE;
-    if ((size_t)B * (size_t)T * (size_t)H * 128u > ((size_t)1 << 46)) return KDA_ERR_SHAPE;
+    if (dt_bias && !(flags & KDA_GATE_IN_KERNEL)) return KDA_ERR_DTYPE;  // it biases the in-kernel gate
+    if (B < 0 || T < 0 || H < 0 || HV < 0 || !dim_ok(Dk) || !dim_ok(Dv)) return KDA_ERR_SHAPE;
+    if (HV > 0 && !groups_ok(H, HV)) return KDA_ERR_SHAPE;
+    if ((size_t)B * (size_t)T * (size_t)HV * 128u > ((size_t)1 << 46)) return KDA_ERR_SHAPE;
     if (!gate_ok(g_min, flags, dt)) return KDA_ERR_GATE;
-    if (H == 0) return KDA_OK;
+    if (HV == 0) return KDA_OK;
     KDA_TRY(need(dA_log));
+    if (dt_bias) { KDA_TRY(need(dt_bias)); KDA_TRY(need(ddt_bias)); }
+    else KDA_TRY(maybe(ddt_bias));
     if (B > 0 && T > 0) {
         KDA_TRY(need(q)); KDA_TRY(need(k)); KDA_TRY(need(v)); KDA_TRY(need(z));
         KDA_TRY(need(beta_raw)); KDA_TRY(need(dout));
@@ -308,7 +320,7 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
     if (flags & KDA_GATE_IN_KERNEL) KDA_TRY(need(A_log));
     else KDA_TRY(maybe(A_log));
     KDA_TRY(maybe(S0)); KDA_TRY(maybe(dS_T)); KDA_TRY(maybe(dS0));
-    const BwdWorkspace w = bwd_workspace(B, T, H, Dk, Dv);
+    const BwdWorkspace w = bwd_workspace(B, T, HV, Dk, Dv, HV > H, dt_bias != nullptr);
     if (w.total > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
                         workspace_bytes < w.total))
         return KDA_ERR_WORKSPACE;
@@ -321,9 +333,40 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
     a.states = reinterpret_cast<float*>(ws + w.states);
     a.adj = reinterpret_cast<float*>(ws + w.adj);
     a.dA_part = reinterpret_cast<float*>(ws + w.dA);
-    a.B = B; a.T = T; a.H = H; a.Dv = Dv; a.NC = (T + kda::kBwdChunk - 1) / kda::kBwdChunk;
+    a.B = B; a.T = T; a.H = HV; a.Dv = Dv; a.NC = (T + kda::kBwdChunk - 1) / kda::kBwdChunk;
     a.g_min = g_min; a.flags = flags;
+    a.G = HV / (H > 0 ? H : 1);
+    a.dt_bias = dt_bias;
+    a.ddt_bias = ddt_bias;
+    a.dqk_part = HV > H ? reinterpret_cast<float*>(ws + w.dqk) : nullptr;
+    a.dbias_part = dt_bias ? reinterpret_cast<float*>(ws + w.dbias) : nullptr;
     return kda::launch_chunk_bwd(dt == KDA_BF16 ? 1 : 0, Dk, a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* z,
+                         const void* beta_raw, const float* A_log, const float* S0,
+                         const void* dout, const float* dS_T,
+                         void* dq, void* dk, void* dv, void* dz, void* dbeta_raw,
+                         float* dA_log, float* dS0,
+                         int B, int T, int H, int Dk, int Dv, float g_min, unsigned flags,
+                         kda_dtype dt, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+    return chunk_bwd_impl(q, k, v, z, beta_raw, A_log, nullptr, S0, dout, dS_T, dq, dk, dv, dz, dbeta_raw,
+                          dA_log, nullptr, dS0, B, T, H, H, Dk, Dv, g_min, flags, dt, workspace,
+                          workspace_bytes, stream);
+}
+
+kda_status kda_chunk_bwd_grouped(const void* q, const void* k, const void* v, const void* z,
+                                 const void* beta_raw, const float* A_log, const float* dt_bias,
+                                 const float* S0, const void* dout, const float* dS_T,
+                                 void* dq, void* dk, void* dv, void* dz, void* dbeta_raw,
+                                 float* dA_log, float* ddt_bias, float* dS0,
+                                 int B, int T, int H, int HV, int Dk, int Dv, float g_min, unsigned flags,
+                                 kda_dtype dt, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+    return chunk_bwd_impl(q, k, v, z, beta_raw, A_log, dt_bias, S0, dout, dS_T, dq, dk, dv, dz, dbeta_raw,
+                          dA_log, ddt_bias, dS0, B, T, H, HV, Dk, Dv, g_min, flags, dt, workspace,
+                          workspace_bytes, stream);
 }
 
 kda_status kda_segment_fixup(int n_seg, const void* P, const float* S_in,

@@ -148,15 +148,17 @@ __device__ void prep_chunk(const BwdArgs& a, int b, int h, int t0, float (*sQ)[P
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6, nw = NTHR >> 6;
     const float eA = (a.flags & kGateIn) ? expf(a.A_log[h]) : 0.f;
+    const int Hk = a.H / a.G, hq = h / a.G;  // value head h reads q/k head h / G
     float qv[NPT], kv[NPT], zv[NPT];
 #pragma unroll
     for (int u = 0; u < NPT; ++u) {
         const int e = tid + u * NTHR, t = e / DK, d = e % DK;
         const int tok = min(t0 + t, a.T - 1);
-        const size_t idx = (((size_t)b * a.T + tok) * a.H + h) * DK + d;
-        qv[u] = ldf<T>(a.q, idx);
-        kv[u] = ldf<T>(a.k, idx);
-        zv[u] = ldf<T>(a.z, idx);
+        const size_t idx_qk = (((size_t)b * a.T + tok) * Hk + hq) * DK + d;
+        qv[u] = ldf<T>(a.q, idx_qk);
+        kv[u] = ldf<T>(a.k, idx_qk);
+        zv[u] = ldf<T>(a.z, (((size_t)b * a.T + tok) * a.H + h) * DK + d);
+        if (a.dt_bias) zv[u] += a.dt_bias[(size_t)h * DK + d];  // the biased logit
     }
     float br = 0.f;
     if (tid < C) br = ldf<T>(a.beta_raw, ((size_t)b * a.T + min(t0 + tid, a.T - 1)) * a.H + h);
@@ -763,6 +765,7 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
     const float eA = (a.flags & kGateIn) ? expf(a.A_log[h]) : 0.f;
     for (int dd = tid; dd < DK; dd += NT) {
         float acc = sGC[dd];  // the chunk-end terms enter at the last token
+        float dbias = 0.f;    // the logit gradient summed over the chunk's tokens
         for (int t = C - 1; t >= 0; --t) {
             acc += fdG[t * DK + dd];
             if (t0 + t < a.T) {
@@ -782,8 +785,10 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
                     }
                 }
                 stf<T>(a.dz, idx, dz);
+                dbias += dz;
             }
         }
+        if (a.dbias_part) a.dbias_part[(((size_t)b * a.NC + n) * a.H + h) * DK + dd] = dbias;
     }
     // dq, dk through the L2 norm: dx = r (dx_hat - x_hat (x_hat . dx_hat)); one wave per token
     for (int t = w; t < C; t += NT / 64) {
@@ -803,8 +808,13 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
             const size_t idx = row_of(t) * DK + dd;
             const float gq_ = l2 ? sRq[t] * (fdq[t * DK + dd] - sQ[t][dd] * pq) : fdq[t * DK + dd];
             const float gk_ = l2 ? sRk[t] * (fdk[t * DK + dd] - sK[t][dd] * pk) : fdk[t * DK + dd];
-            stf<T>(a.dq, idx, gq_);
-            stf<T>(a.dk, idx, gk_);
+            if (a.G == 1) {
+                stf<T>(a.dq, idx, gq_);
+                stf<T>(a.dk, idx, gk_);
+            } else {  // this value head's share; the group is summed afterwards
+                a.dqk_part[idx] = gq_;
+                a.dqk_part[(size_t)a.B * a.T * a.H * DK + idx] = gk_;
+            }
         }
         if (lane == 0) {
             const float bt = sB[t];
@@ -840,6 +850,40 @@ __global__ __launch_bounds__(256) void kda_bwd_dA_kernel(const BwdArgs a) {
     if (threadIdx.x == 0) a.dA_log[h] = (a.flags & kGateIn) ? (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]) : 0.f;
 }
 
+// ------------------------------------------------- grouped-head reductions
+
+// dq, dk of q/k head hq: the sum of the G value heads hq G .. hq G + G - 1.
+template <typename T, int DK>
+__global__ __launch_bounds__(256) void kda_bwd_qk_reduce_kernel(const BwdArgs a) {
+    const int Hk = a.H / a.G;
+    const size_t n = (size_t)a.B * a.T * Hk * DK;
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int d = (int)(i % DK);
+    const size_t row = i / DK;  // (b, t, hq)
+    const int hq = (int)(row % Hk);
+    const size_t bt = row / Hk;
+    const size_t half = (size_t)a.B * a.T * a.H * DK;
+    float sq = 0.f, sk = 0.f;
+    for (int j = 0; j < a.G; ++j) {
+        const size_t src = (bt * a.H + (size_t)hq * a.G + j) * DK + d;
+        sq += a.dqk_part[src];
+        sk += a.dqk_part[half + src];
+    }
+    stf<T>(a.dq, i, sq);
+    stf<T>(a.dk, i, sk);
+}
+
+// ddt_bias[h][d]: the per-chunk parts summed over batch and chunks.
+template <int DK>
+__global__ __launch_bounds__(256) void kda_bwd_bias_reduce_kernel(const BwdArgs a) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= a.H * DK) return;
+    float s = 0.f;
+    for (int bn = 0; bn < a.B * a.NC; ++bn) s += a.dbias_part[(size_t)bn * a.H * DK + i];
+    a.ddt_bias[i] = s;
+}
+
 // ---------------------------------------------------------------- launches
 
 template <typename T, int DK, int DV>
@@ -858,6 +902,13 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((kda_bwd_grads_kernel<T, DK, DV>), dim3(chunk_heads), dim3(512), 0, s, a);
     if (a.H > 0)
         hipLaunchKernelGGL(kda_bwd_dA_kernel, dim3((unsigned)a.H), dim3(256), 0, s, a);
+    if (a.G > 1 && chunk_heads > 0) {
+        const size_t nqk = (size_t)a.B * a.T * (a.H / a.G) * DK;
+        hipLaunchKernelGGL((kda_bwd_qk_reduce_kernel<T, DK>), dim3((unsigned)((nqk + 255) / 256)), dim3(256), 0, s, a);
+    }
+    if (a.ddt_bias && a.H > 0)
+        hipLaunchKernelGGL((kda_bwd_bias_reduce_kernel<DK>), dim3((unsigned)((a.H * DK + 255) / 256)), dim3(256), 0,
+                           s, a);
     return hipGetLastError();
 }
 

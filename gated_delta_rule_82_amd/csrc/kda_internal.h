@@ -150,6 +150,14 @@ struct BwdArgs {
     int B, T, H, Dv, NC;
     float g_min;
     unsigned flags;
+    // grouped value heads: H value heads read q/k head h / G of H / G; a gate
+    // bias [H, DK] on the logit; per-value-head q/k gradients (fp32, [2][B,T,H,DK])
+    // summed per group afterwards, and per-chunk bias gradient parts [B NC][H][DK]
+    int G = 1;
+    const float* dt_bias = nullptr;
+    float* ddt_bias = nullptr;
+    float* dqk_part = nullptr;
+    float* dbias_part = nullptr;
 };
 // fp32 elements of the per-chunk operator block for a key dimension DK: the
 // state pass's region, the adjoint pass's region (operand tiles of 16 rows x

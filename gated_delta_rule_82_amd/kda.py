@@ -26,7 +26,8 @@ EXPORTS = (
     "kda_chunk_fwd_kernel_count", "kda_chunk_fwd_overlap_workspace", "kda_chunk_fwd_overlap_kernel_count",
     "kda_chunk_fwd_overlap", "kda_step", "kda_chunk_fwd_grouped", "kda_step_grouped",
     "kda_segment_compose", "kda_segment_fixup", "kda_short_conv", "kda_output_gate",
-    "kda_chunk_bwd_workspace", "kda_chunk_bwd", "kda_status_string",
+    "kda_chunk_bwd_workspace", "kda_chunk_bwd", "kda_chunk_bwd_grouped_workspace", "kda_chunk_bwd_grouped",
+    "kda_status_string",
 )
 OVERLAP_SYNC_EVENTS = 5
 
@@ -83,6 +84,10 @@ def load() -> ctypes.CDLL:
     L.kda_chunk_bwd_workspace.restype = S
     L.kda_chunk_bwd.argtypes = [P] * 16 + [I] * 5 + [F, U, I, P, S, P]
     L.kda_chunk_bwd.restype = I
+    L.kda_chunk_bwd_grouped_workspace.argtypes = [I] * 7
+    L.kda_chunk_bwd_grouped_workspace.restype = S
+    L.kda_chunk_bwd_grouped.argtypes = [P] * 18 + [I] * 6 + [F, U, I, P, S, P]
+    L.kda_chunk_bwd_grouped.restype = I
     L.kda_status_string.argtypes = [I]
     L.kda_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -266,27 +271,44 @@ def bwd_workspace_bytes(B, T, H, Dk, Dv):
 
 
 def chunk_bwd(q, k, v, z, beta_raw, A_log, dout, S0=None, dS_T=None, *, g_min=-5.0, flags=FLAGS_DEFAULT,
-              want_dS0=True, workspace=None):
+              want_dS0=True, workspace=None, dt_bias=None):
     """Backward of chunk_fwd: gradients of L = sum(dout * o) + sum(dS_T * S_T).
     Returns a dict dq, dk, dv, dz, dbeta_raw (input dtype), dA_log [H] and,
-    when asked, dS0 [B,H,Dk,Dv] (fp32)."""
-    B, T, H, Dk = q.shape
+    when asked, dS0 [B,H,Dk,Dv] (fp32).  Grouped value heads (v with more
+    heads than q) or a gate bias `dt_bias` run kda_chunk_bwd_grouped, which
+    adds ddt_bias [HV, Dk] (fp32) when a bias is given."""
+    B, T, Hq, Dk = q.shape
+    H = v.shape[2]
     Dv = v.shape[-1]
     dt = q.dtype
     dev = q.device
+    grouped = Hq != H or dt_bias is not None
     g = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
          "dz": torch.empty_like(z), "dbeta_raw": torch.empty_like(beta_raw),
          "dA_log": torch.empty(H, dtype=torch.float32, device=dev)}
     g["dS0"] = torch.empty(B, H, Dk, Dv, dtype=torch.float32, device=dev) if want_dS0 else None
-    need = bwd_workspace_bytes(B, T, H, Dk, Dv)
+    if dt_bias is not None:
+        g["ddt_bias"] = torch.empty(H, Dk, dtype=torch.float32, device=dev)
+    if grouped:
+        need = load().kda_chunk_bwd_grouped_workspace(B, T, Hq, H, Dk, Dv, 1 if dt_bias is not None else 0)
+    else:
+        need = bwd_workspace_bytes(B, T, H, Dk, Dv)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    st = load().kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta_raw), _ptr(A_log), _ptr(S0),
-                              _ptr(dout), _ptr(dS_T), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dz"]),
-                              _ptr(g["dbeta_raw"]), _ptr(g["dA_log"]), _ptr(g["dS0"]),
-                              B, T, H, Dk, Dv, g_min, flags, _dt(dt), _ptr(workspace), workspace.numel(),
-                              _stream(dev))
-    _check("kda_chunk_bwd", st)
+    if grouped:
+        st = load().kda_chunk_bwd_grouped(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta_raw), _ptr(A_log), _ptr(dt_bias), _ptr(S0), _ptr(dout),
+            _ptr(dS_T), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dz"]), _ptr(g["dbeta_raw"]),
+            _ptr(g["dA_log"]), _ptr(g.get("ddt_bias")), _ptr(g["dS0"]),
+            B, T, Hq, H, Dk, Dv, g_min, flags, _dt(dt), _ptr(workspace), workspace.numel(), _stream(dev))
+        _check("kda_chunk_bwd_grouped", st)
+    else:
+        st = load().kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta_raw), _ptr(A_log), _ptr(S0),
+                                  _ptr(dout), _ptr(dS_T), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dz"]),
+                                  _ptr(g["dbeta_raw"]), _ptr(g["dA_log"]), _ptr(g["dS0"]),
+                                  B, T, H, Dk, Dv, g_min, flags, _dt(dt), _ptr(workspace), workspace.numel(),
+                                  _stream(dev))
+        _check("kda_chunk_bwd", st)
     return g
 
 

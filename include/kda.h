@@ -283,6 +283,25 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
                          kda_dtype dt, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
+/* Backward of kda_chunk_fwd_grouped: q, k [B,T,H,Dk] read by HV = G H value
+ * heads (value head hv reads q/k head hv / G), v, z, beta_raw, A_log, S0 and
+ * dout per value head, dt_bias [HV,Dk] fp32 or NULL (added to the gate logit;
+ * needs KDA_GATE_IN_KERNEL).  dq, dk [B,T,H,Dk] are the sums over the value
+ * heads that read each q/k head; ddt_bias [HV,Dk] fp32 (required with a bias,
+ * ignored without) is the logit gradient summed over batch and tokens; the
+ * other outputs as kda_chunk_bwd, per value head.  Workspace:
+ * kda_chunk_bwd_grouped_workspace(B, T, H, HV, Dk, Dv, dt_bias != NULL)
+ * bytes (0 for invalid sizes).  Errors as kda_chunk_fwd_grouped. */
+size_t kda_chunk_bwd_grouped_workspace(int B, int T, int H, int HV, int Dk, int Dv, int with_bias);
+kda_status kda_chunk_bwd_grouped(const void* q, const void* k, const void* v, const void* z,
+                                 const void* beta_raw, const float* A_log, const float* dt_bias,
+                                 const float* S0, const void* dout, const float* dS_T,
+                                 void* dq, void* dk, void* dv, void* dz, void* dbeta_raw,
+                                 float* dA_log, float* ddt_bias, float* dS0,
+                                 int B, int T, int H, int HV, int Dk, int Dv, float g_min, unsigned flags,
+                                 kda_dtype dt, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
 const char* kda_status_string(kda_status s);
 
 #ifdef __cplusplus

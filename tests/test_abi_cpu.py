@@ -261,3 +261,22 @@ def test_backward_workspace_and_validation(lib):
     assert bwd_call(lib, ws=A16, ws_bytes=need - 1) == 6
     assert bwd_call(lib, ws=A16 + 16, ws_bytes=need) == 6
     assert bwd_call(lib, H=0) == 0
+
+
+def test_backward_grouped_validation(lib):
+    def call(**kw):
+        a = dict(q=A16, k=A16, v=A16, z=A16, beta_raw=A16, A_log=A16, dt_bias=A16, S0=None, dout=A16, dS_T=None,
+                 dq=A16, dk=A16, dv=A16, dz=A16, dbeta_raw=A16, dA_log=A16, ddt_bias=A16, dS0=None,
+                 B=1, T=64, H=2, HV=6, Dk=64, Dv=64, g_min=-5.0, flags=7, dt=1, ws=None, ws_bytes=0, stream=None)
+        a.update(kw)
+        return lib.kda_chunk_bwd_grouped(*a.values())
+    assert lib.kda_chunk_bwd_grouped_workspace(1, 64, 2, 5, 64, 64, 1) == 0     # HV not a multiple of H
+    grouped = lib.kda_chunk_bwd_grouped_workspace(1, 64, 2, 6, 64, 64, 1)
+    plain = lib.kda_chunk_bwd_workspace(1, 64, 6, 64, 64)
+    assert grouped > plain                                                       # q/k and bias parts
+    assert call(HV=5) == 2
+    assert call(flags=3) == 4            # a gate bias without the in-kernel gate
+    assert call(ddt_bias=None) == 1      # a bias needs its gradient
+    assert call(dt_bias=None, ddt_bias=None) == 6   # no bias: valid up to the workspace
+    assert call() == 6
+    assert call(HV=0) == 0

@@ -144,3 +144,31 @@ def test_backward_layer_workload_sampled_heads():
             assert_close(g[n][b:b + 1, :, h:h + 1], ref[n], BF16, f"layer b{b} h{h} {n}")
         assert_close(g["dbeta_raw"][b:b + 1, :, h:h + 1], ref["dbeta_raw"], BF16, f"layer b{b} h{h} dbeta")
         assert_close(g["dS0"][b:b + 1, h:h + 1], ref["dS0"], BF16, f"layer b{b} h{h} dS0")
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("H,HV,bias,T", [(2, 4, True, 70), (1, 4, False, 45), (2, 2, True, 33), (4, 8, True, 96)])
+def test_backward_grouped_matches_oracle(dtype, H, HV, bias, T):
+    # value head hv reads q/k head hv / (HV / H); dq, dk sum over the value heads;
+    # the gate bias gradient sums the logit gradient over batch and tokens
+    rng = np.random.default_rng(H * 100 + HV * 10 + T)
+    B, Dk, Dv = 2, 64, 64
+    to = lambda x: torch.tensor(x, dtype=F32).to(dtype)
+    q, k = to(rng.standard_normal((B, T, H, Dk))), to(rng.standard_normal((B, T, H, Dk)))
+    v = to(rng.standard_normal((B, T, HV, Dv)))
+    z = to(rng.standard_normal((B, T, HV, Dk)))
+    br = to(rng.standard_normal((B, T, HV)))
+    A = torch.tensor(rng.normal(0, 0.5, HV), dtype=F32)
+    db = torch.tensor(rng.normal(0, 0.7, (HV, Dk)), dtype=F32) if bias else None
+    S0 = torch.tensor(rng.normal(0, 0.3, (B, HV, Dk, Dv)), dtype=F32)
+    do = to(rng.standard_normal((B, T, HV, Dv)))
+    dST = torch.tensor(rng.normal(0, 0.5, (B, HV, Dk, Dv)), dtype=F32)
+    g = kda.chunk_bwd(*(t.cuda() for t in (q, k, v, z, br, A, do)), S0.cuda(), dST.cuda(),
+                      dt_bias=None if db is None else db.cuda())
+    torch.cuda.synchronize()
+    ref = ora.backward_grouped(np64(q), np64(k), np64(v), np64(z), np64(br), np64(A), np64(do), np64(db),
+                               np64(dST), np64(S0))
+    names = list(NAMES) + (["ddt_bias"] if bias else [])
+    for n in names:
+        assert_close(g[n], ref[n], F32 if n in ("dA_log", "dS0", "ddt_bias") and dtype == F32 else dtype,
+                     f"grouped H{H} HV{HV} {n}")
