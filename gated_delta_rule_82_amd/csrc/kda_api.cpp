@@ -8,7 +8,7 @@
 
 
 #include "../../include/kda.h"
-#include "kda_internal.h"
+#include "kda_bwd.h"
 
 namespace {
 

@@ -36,7 +36,7 @@
 //  4. kda_bwd_grads:   per chunk-head: every input gradient of the chunk.
 //  5. kda_bwd_dA:      the sum of the per-chunk dA_log parts.
 #include "kda_device.h"
-#include "kda_internal.h"
+#include "kda_bwd.h"
 
 namespace kda {
 
