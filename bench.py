@@ -89,7 +89,6 @@ def kernel_bytes(B, T, H, Dk, Dv, C, esize=2):
     return {"kda_intra": intra, "kda_inter": inter}
 
 
-PEAK_FP32_TFLOPS = 157.3  # MI355X dense fp32 matrix and vector peak
 
 
 def decode_bytes(B, H, Dk, Dv, esize=2):
@@ -442,17 +441,20 @@ def bench_backward(torch, kda, inputs, steps, warmup):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    # algorithmic fp32 flops per chunk-head of the products the backward runs
-    # (state and adjoint passes, gradients, operators):
+    # algorithmic flops per chunk-head of the products the backward runs
+    # (state and adjoint passes, gradients, operators); the bf16 path runs them
+    # on bf16 matrix-core operands with fp32 accumulation, except the operator
+    # triangles (fp32, element by element):
     # 2 C Dk Dv x 10 + 2 C^2 Dv x 8 + 2 C^2 Dk
     C = 32
     nch = w.B * w.H * ((w.T + C - 1) // C)
     flops = nch * (2 * C * w.Dk * w.Dv * 10 + 2 * C * C * w.Dv * 8 + 2 * C * C * w.Dk)
     tflops = flops / (ms * 1e-3) / 1e12
-    return {"workload": "backward: kda_chunk_bwd B4 T4096 H16 D128 bf16 (fp32 arithmetic, 32-token chunks)",
+    return {"workload": "backward: kda_chunk_bwd B4 T4096 H16 D128 bf16 (bf16 matrix-core operands, fp32 accumulation "
+                        "and states, 32-token chunks)",
             "ms": round(ms, 4), "tokens_per_s": w.B * w.T / (ms / 1e3),
             "algorithmic_gflop": round(flops / 1e9, 2), "tflops": round(tflops, 2),
-            "frac_fp32_mfma_peak": round(tflops / PEAK_FP32_TFLOPS, 4),
+            "frac_bf16_mfma_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
             "workspace_bytes": int(ws.numel())}
 
 

@@ -274,7 +274,7 @@ static BwdWorkspace bwd_workspace(int B, int T, int HV, int Dk, int Dv, bool gro
     const size_t NC = (size_t)(T + kda::kBwdChunk - 1) / kda::kBwdChunk;
     const size_t BHN = (size_t)B * HV * NC;
     w.ops = 0;
-    w.states = kda::round_up(BHN * kda::bwd_op_floats(Dk) * 4, 256);
+    w.states = kda::round_up(BHN * kda::bwd_op_bytes(4, Dk), 256);  // fp32 operands: the larger block
     w.adj = w.states + kda::round_up(BHN * Dk * Dv * 4, 256);
     w.dA = w.adj + kda::round_up(BHN * Dk * Dv * 4, 256);
     w.dqk = w.dA + kda::round_up(BHN * 4, 256);
@@ -329,7 +329,7 @@ static kda_status chunk_bwd_impl(const void* q, const void* k, const void* v, co
     a.q = q; a.k = k; a.v = v; a.z = z; a.beta_raw = beta_raw; a.A_log = A_log; a.S0 = S0;
     a.dout = dout; a.dS_T = dS_T;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dz = dz; a.dbeta_raw = dbeta_raw; a.dA_log = dA_log; a.dS0 = dS0;
-    a.ops = reinterpret_cast<float*>(ws + w.ops);
+    a.ops = ws + w.ops;
     a.states = reinterpret_cast<float*>(ws + w.states);
     a.adj = reinterpret_cast<float*>(ws + w.adj);
     a.dA_part = reinterpret_cast<float*>(ws + w.dA);

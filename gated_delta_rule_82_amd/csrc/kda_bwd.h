@@ -7,13 +7,14 @@
 
 namespace kda {
 
-// Backward of the chunked forward (fp32 arithmetic, kBwdChunk-token chunks).
+// Backward of the chunked forward (kBwdChunk-token chunks; fp32 states and
+// accumulation, matrix-core operands in the input precision).
 constexpr int kBwdChunk = 32;
 struct BwdArgs {
     const void* q; const void* k; const void* v; const void* z; const void* beta_raw;
     const float* A_log; const float* S0; const void* dout; const float* dS_T;
     void* dq; void* dk; void* dv; void* dz; void* dbeta_raw; float* dA_log; float* dS0;
-    float* ops; float* states; float* adj; float* dA_part;  // workspace regions
+    unsigned char* ops; float* states; float* adj; float* dA_part;  // workspace regions
     int B, T, H, Dv, NC;
     float g_min;
     unsigned flags;
@@ -26,24 +27,27 @@ struct BwdArgs {
     float* dqk_part = nullptr;
     float* dbias_part = nullptr;
 };
-// fp32 elements of the per-chunk operator block for a key dimension DK: the
-// state pass's region, the adjoint pass's region (operand tiles of 16 rows x
-// 32 contraction slots, 512 floats each, plus gamma and beta; each region a
-// whole number of KiB) and the row-major At.
-__host__ __device__ constexpr size_t bwd_tiles(size_t rows, size_t kext) {
-    return rows / 16 * ((kext + 31) / 32) * 512;
+// Bytes of the per-chunk operator block for operand elements of eb bytes (4
+// for fp32 inputs, 2 for bf16) and key dimension DK: the state pass's region,
+// the adjoint pass's region (operand tiles of 16 rows x 32 contraction slots,
+// 512 elements each, plus gamma and beta in fp32; each region a whole number
+// of KiB) and the row-major fp32 At.
+__host__ __device__ constexpr size_t bwd_tile_bytes(size_t rows, size_t kext, size_t eb) {
+    return rows / 16 * ((kext + 31) / 32) * 512 * eb;
 }
-__host__ __device__ constexpr size_t bwd_op_region_s(int DK) {
+__host__ __device__ constexpr size_t bwd_region_s_bytes(size_t eb, int DK) {
     const size_t C = kBwdChunk;
-    return round_up(bwd_tiles(C, DK) + bwd_tiles(DK, C) + bwd_tiles(C, C) + DK + C, 256);
+    return round_up(bwd_tile_bytes(C, DK, eb) + bwd_tile_bytes(DK, C, eb) + bwd_tile_bytes(C, C, eb) + (DK + C) * 4,
+                    1024);
 }
-__host__ __device__ constexpr size_t bwd_op_region_a(int DK) {
+__host__ __device__ constexpr size_t bwd_region_a_bytes(size_t eb, int DK) {
     const size_t C = kBwdChunk;
-    return round_up(bwd_tiles(C, DK) + 2 * bwd_tiles(DK, C) + 2 * bwd_tiles(C, C) + DK + C, 256);
+    return round_up(bwd_tile_bytes(C, DK, eb) + 2 * bwd_tile_bytes(DK, C, eb) + 2 * bwd_tile_bytes(C, C, eb) +
+                    (DK + C) * 4, 1024);
 }
-__host__ __device__ constexpr size_t bwd_op_floats(int DK) {
+__host__ __device__ constexpr size_t bwd_op_bytes(size_t eb, int DK) {
     const size_t C = kBwdChunk;
-    return round_up(bwd_op_region_s(DK) + bwd_op_region_a(DK) + C * C, 256);
+    return round_up(bwd_region_s_bytes(eb, DK) + bwd_region_a_bytes(eb, DK) + C * C * 4, 1024);
 }
 hipError_t launch_chunk_bwd(int dt, int DK, const BwdArgs& a, hipStream_t s);
 

@@ -44,34 +44,46 @@ namespace {
 
 constexpr int C = kBwdChunk;
 
-// Element offsets of the fp32 operator block of one chunk-head.  Matrices
-// that serve as matrix-core A operands are stored as operand tiles: tile
-// (row block rb, contraction step ks) holds 64 lanes x 8 slots, lane 16 gq + r
-// supplying row 16 rb + r at contraction index 32 ks + slot_index(gq, j), so
-// a lane reads its fragment as 32 contiguous bytes (no LDS bank conflicts,
-// whole global lines).
-template <int DK> struct Ops {
+// Byte offsets of the operator block of one chunk-head, operand tiles in the
+// input precision E (fp32 or bf16).  Matrices that serve as matrix-core A
+// operands are stored as operand tiles: tile (row block rb, contraction step
+// ks) holds 64 lanes x 8 slots, lane 16 gq + r supplying row 16 rb + r at
+// contraction index 32 ks + slot_index(gq, j), so a lane reads its fragment as
+// 8 contiguous elements (no LDS bank conflicts, whole global lines).
+template <typename E, int DK> struct Ops {
+    static constexpr size_t eb = sizeof(E);
     // region S (the state pass)
     static constexpr size_t Kd = 0;                                  // tiles [C x DK]   k_hat exp(G)
-    static constexpr size_t KpT = Kd + bwd_tiles(C, DK);             // tiles [DK x C]   (k_hat exp(G_C - G))^T
-    static constexpr size_t Tm = KpT + bwd_tiles(DK, C);             // tiles [C x C]    (I + Diag(beta) At)^-1
-    static constexpr size_t gamS = Tm + bwd_tiles(C, C);             // [DK]  exp(G_C)
-    static constexpr size_t betaS = gamS + DK;                       // [C]
-    static constexpr size_t sizeS = bwd_op_region_s(DK);
+    static constexpr size_t KpT = Kd + bwd_tile_bytes(C, DK, eb);    // tiles [DK x C]   (k_hat exp(G_C - G))^T
+    static constexpr size_t Tm = KpT + bwd_tile_bytes(DK, C, eb);    // tiles [C x C]    (I + Diag(beta) At)^-1
+    static constexpr size_t gamS = Tm + bwd_tile_bytes(C, C, eb);    // fp32 [DK]  exp(G_C)
+    static constexpr size_t betaS = gamS + DK * 4;                   // fp32 [C]
+    static constexpr size_t sizeS = bwd_region_s_bytes(eb, DK);
     // region A (the adjoint pass), offsets from the block start
     static constexpr size_t A0 = sizeS;
     static constexpr size_t Kp = A0;                                 // tiles [C x DK]
-    static constexpr size_t QpT = Kp + bwd_tiles(C, DK);             // tiles [DK x C]   (q_hat exp(G))^T
-    static constexpr size_t KdT = QpT + bwd_tiles(DK, C);            // tiles [DK x C]
-    static constexpr size_t AqkT = KdT + bwd_tiles(DK, C);           // tiles [C x C]    Aqk^T
-    static constexpr size_t TT = AqkT + bwd_tiles(C, C);             // tiles [C x C]    T^T
-    static constexpr size_t gamA = TT + bwd_tiles(C, C);             // [DK]
-    static constexpr size_t betaA = gamA + DK;                       // [C]
-    static constexpr size_t sizeA = bwd_op_region_a(DK);
-    // row-major At (strictly lower, no beta)
+    static constexpr size_t QpT = Kp + bwd_tile_bytes(C, DK, eb);    // tiles [DK x C]   (q_hat exp(G))^T
+    static constexpr size_t KdT = QpT + bwd_tile_bytes(DK, C, eb);   // tiles [DK x C]
+    static constexpr size_t AqkT = KdT + bwd_tile_bytes(DK, C, eb);  // tiles [C x C]    Aqk^T
+    static constexpr size_t TT = AqkT + bwd_tile_bytes(C, C, eb);    // tiles [C x C]    T^T
+    static constexpr size_t gamA = TT + bwd_tile_bytes(C, C, eb);    // fp32 [DK]
+    static constexpr size_t betaA = gamA + DK * 4;                   // fp32 [C]
+    static constexpr size_t sizeA = bwd_region_a_bytes(eb, DK);
+    // row-major fp32 At (strictly lower, no beta)
     static constexpr size_t At = A0 + sizeA;
-    static_assert(betaS + C <= sizeS && betaA + C <= A0 + sizeA && At + C * C <= bwd_op_floats(DK), "layout");
+    static constexpr size_t bytes = bwd_op_bytes(eb, DK);
+    static_assert(betaS + C * 4 <= sizeS && betaA + C * 4 <= A0 + sizeA && At + C * C * 4 <= bytes, "layout");
+    static_assert(sizeS % 1024 == 0 && sizeA % 1024 == 0 && bytes % 1024 == 0, "whole KiB regions");
+    static __device__ __forceinline__ const E* tiles(const unsigned char* base, size_t off) {
+        return reinterpret_cast<const E*>(base + off);
+    }
+    static __device__ __forceinline__ const float* f32(const unsigned char* base, size_t off) {
+        return reinterpret_cast<const float*>(base + off);
+    }
 };
+
+// Elements of the operand tiles of a [rows x kext] matrix.
+constexpr int tile_elems(int rows, int kext) { return (int)bwd_tile_bytes(rows, kext, 1); }
 
 // Position of element (row, k) in operand tiles with kext contraction indices.
 __device__ __forceinline__ size_t tile_pos(int row, int k, int kext) {
@@ -83,13 +95,32 @@ __device__ __forceinline__ size_t tile_pos(int row, int k, int kext) {
 }
 
 // This lane's fragment of tile (rb, ks) of operand tiles with KS steps.
-__device__ __forceinline__ Frag<float> frag_tile(const float* M, int rb, int ks, int KS) {
-    const float4* p = reinterpret_cast<const float4*>(M + ((size_t)(rb * KS + ks) * 64 + (threadIdx.x & 63)) * 8);
-    const float4 lo = p[0], hi = p[1];
-    Frag<float> f;
-    f.v[0] = lo.x; f.v[1] = lo.y; f.v[2] = lo.z; f.v[3] = lo.w;
-    f.v[4] = hi.x; f.v[5] = hi.y; f.v[6] = hi.z; f.v[7] = hi.w;
+template <typename E>
+__device__ __forceinline__ Frag<E> frag_tile(const E* M, int rb, int ks, int KS) {
+    Frag<E> f;
+    frag_load_row8(f, M + ((size_t)(rb * KS + ks) * 64 + (threadIdx.x & 63)) * 8);
     return f;
+}
+
+// A fragment in the operand precision E (identity for fp32).
+template <typename E>
+__device__ __forceinline__ Frag<E> cvt_frag(const Frag<float>& x) {
+    Frag<E> f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f.set(j, x.v[j]);
+    return f;
+}
+
+// Eight consecutive floats stored as E (32 or 16 bytes, aligned to it).
+__device__ __forceinline__ void store_row8(float* p, const float* x) {
+    reinterpret_cast<float4*>(p)[0] = *reinterpret_cast<const float4*>(x);
+    reinterpret_cast<float4*>(p)[1] = *reinterpret_cast<const float4*>(x + 4);
+}
+__device__ __forceinline__ void store_row8(bf16_t* p, const float* x) {
+    bf16x8 v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (bf16_t)x[j];
+    *reinterpret_cast<bf16x8*>(p) = v;
 }
 
 template <typename T>
@@ -122,10 +153,10 @@ __device__ __forceinline__ Frag<float> frag_rows(const float* M, int ld, int row
 
 // B operand of a 16-row-block strip held as C-layout tiles X[0 .. NB-1] for
 // contraction step s (rows 32 s .. 32 s + 31).
-template <int NB>
-__device__ __forceinline__ Frag<float> frag_strip(const floatx4 (&X)[NB], int s) {
-    if (2 * s + 1 < NB) return frag_from_c<float>(X[2 * s], X[2 * s + 1]);
-    return frag_from_c_lo<float>(X[2 * s]);
+template <typename E, int NB>
+__device__ __forceinline__ Frag<E> frag_strip(const floatx4 (&X)[NB], int s) {
+    if (2 * s + 1 < NB) return frag_from_c<E>(X[2 * s], X[2 * s + 1]);
+    return frag_from_c_lo<E>(X[2 * s]);
 }
 
 // Per-element log-decay of the switched gate (natural log units).
@@ -217,10 +248,10 @@ __device__ void prep_chunk(const BwdArgs& a, int b, int h, int t0, float (*sQ)[P
 // whole 16-byte pieces.
 template <typename T, int DK>
 __global__ __launch_bounds__(256) void kda_bwd_ops_kernel(const BwdArgs a) {
-    using O = Ops<DK>;
+    using O = Ops<T, DK>;
     constexpr int P = DK + 1;  // odd pitch: the pair loop reads columns across rows
     constexpr int KSD = (DK + 31) / 32;
-    constexpr int kStage = (int)(bwd_tiles(C, DK) > 2 * C * C ? bwd_tiles(C, DK) : 2 * C * C);
+    constexpr int kStage = tile_elems(C, DK) > 2 * C * C ? tile_elems(C, DK) : 2 * C * C;
     __shared__ float sQ[C][P], sK[C][P], sG[C][P];
     __shared__ float sB[C], sRq[C], sRk[C];
     __shared__ float sAt[C][C + 1];
@@ -230,11 +261,12 @@ __global__ __launch_bounds__(256) void kda_bwd_ops_kernel(const BwdArgs a) {
     const int b = bh / a.H, h = bh % a.H;
     const int tid = threadIdx.x;
     prep_chunk<T, DK, P, 256>(a, b, h, n * C, sQ, sK, sG, sB, sRq, sRk);
-    float* op = a.ops + ((size_t)bh * a.NC + n) * bwd_op_floats(DK);
-    auto flush = [&](size_t dst, int count) {  // sSt[0, count) -> op[dst, dst + count)
+    unsigned char* op = a.ops + ((size_t)bh * a.NC + n) * O::bytes;
+    float* opf = reinterpret_cast<float*>(op);  // the fp32 parts, in floats
+    auto flush = [&](size_t dst, int count) {   // sSt[0, count) -> elements [0, count) at byte dst, as T
         __syncthreads();
-        for (int e = 4 * tid; e < count; e += 4 * 256)
-            *reinterpret_cast<float4*>(op + dst + e) = *reinterpret_cast<const float4*>(sSt + e);
+        T* out = reinterpret_cast<T*>(op + dst);
+        for (int e = 8 * tid; e < count; e += 8 * 256) store_row8(out + e, sSt + e);
         __syncthreads();
     };
     // [C x DK] operands: Kd = k_hat exp(G), Kp = k_hat exp(G_C - G); slots past DK are zero
@@ -248,7 +280,7 @@ __global__ __launch_bounds__(256) void kda_bwd_ops_kernel(const BwdArgs a) {
             }
             sSt[tile_pos(t, k, DK)] = x;
         }
-        flush(which == 0 ? O::Kd : O::Kp, (int)bwd_tiles(C, DK));
+        flush(which == 0 ? O::Kd : O::Kp, tile_elems(C, DK));
     }
     // [DK x C] operands: KpT, QpT, KdT
     for (int which = 0; which < 3; ++which) {
@@ -259,17 +291,17 @@ __global__ __launch_bounds__(256) void kda_bwd_ops_kernel(const BwdArgs a) {
                           : (which == 1 ? sQ[t][d] : sK[t][d]) * exp2_fast(G);
             sSt[tile_pos(d, t, C)] = x;
         }
-        flush(which == 0 ? O::KpT : (which == 1 ? O::QpT : O::KdT), (int)bwd_tiles(DK, C));
+        flush(which == 0 ? O::KpT : (which == 1 ? O::QpT : O::KdT), tile_elems(DK, C));
     }
-    for (int d = tid; d < DK; d += 256) op[O::gamS + d] = op[O::gamA + d] = exp2_fast(sG[C - 1][d]);
-    for (int t = tid; t < C; t += 256) op[O::betaS + t] = op[O::betaA + t] = sB[t];
+    for (int d = tid; d < DK; d += 256) opf[O::gamS / 4 + d] = opf[O::gamA / 4 + d] = exp2_fast(sG[C - 1][d]);
+    for (int t = tid; t < C; t += 256) opf[O::betaS / 4 + t] = opf[O::betaA / 4 + t] = sB[t];
     // At (strictly lower, row-major) and Aqk^T (tiles), each decay factor in one
     // exponent exp(G_i - G_j) <= 1
     for (int e = tid; e < C * C; e += 256) {  // zeros above the diagonal
         const int i = e / C, j = e % C;
         if (j > i) {
             sAt[i][j] = 0.f;
-            op[O::At + i * C + j] = 0.f;
+            opf[O::At / 4 + i * C + j] = 0.f;
             sSt[tile_pos(j, i, C)] = 0.f;
         }
     }
@@ -288,7 +320,7 @@ __global__ __launch_bounds__(256) void kda_bwd_ops_kernel(const BwdArgs a) {
         }
         if (j == i) akk = 0.f;
         sAt[i][j] = akk;
-        op[O::At + i * C + j] = akk;
+        opf[O::At / 4 + i * C + j] = akk;
         sSt[tile_pos(j, i, C)] = aqk;
     }
     flush(O::AqkT, C * C);
@@ -311,9 +343,9 @@ __global__ __launch_bounds__(256) void kda_bwd_ops_kernel(const BwdArgs a) {
         }
     }
     __syncthreads();
-    for (int e = 4 * tid; e < C * C; e += 4 * 256) {
-        *reinterpret_cast<float4*>(op + O::Tm + e) = *reinterpret_cast<const float4*>(sSt + e);
-        *reinterpret_cast<float4*>(op + O::TT + e) = *reinterpret_cast<const float4*>(sSt + C * C + e);
+    for (int e = 8 * tid; e < C * C; e += 8 * 256) {
+        store_row8(reinterpret_cast<T*>(op + O::Tm) + e, sSt + e);
+        store_row8(reinterpret_cast<T*>(op + O::TT) + e, sSt + C * C + e);
     }
 }
 
@@ -336,16 +368,16 @@ __device__ __forceinline__ void stage_kib(const unsigned char* src, float* dst, 
 // into LDS one chunk ahead.
 template <typename T, int DK, int NSW>
 __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_states_kernel(const BwdArgs a) {
-    using O = Ops<DK>;
+    using O = Ops<T, DK>;
     constexpr int NBD = DK / 16, KSD = (DK + 31) / 32;
-    constexpr int kPieces = (int)(O::sizeS / 256);
-    __shared__ __align__(16) float sOp[2][O::sizeS];
+    constexpr int kPieces = (int)(O::sizeS / 1024);
+    __shared__ __align__(16) float sOp[2][O::sizeS / 4];
     const int ngrp = (a.Dv / 16) / NSW;
     const int bh = blockIdx.x / ngrp, grp = blockIdx.x % ngrp;
     const int b = bh / a.H, h = bh % a.H;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, gq = lane >> 4;
     const int col = 16 * (grp * NSW + w) + r;
-    const unsigned char* blk = reinterpret_cast<const unsigned char*>(a.ops + (size_t)bh * a.NC * bwd_op_floats(DK));
+    const unsigned char* blk = a.ops + (size_t)bh * a.NC * O::bytes;
     // wave NSW only copies operators into LDS (one chunk ahead); the compute
     // waves never have a copy outstanding, so their LDS reads wait for nothing
     if (w == NSW) {
@@ -353,7 +385,7 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_states_kernel(const Bw
         wait_vmcnt<0>();
         __syncthreads();
         for (int n = 0; n < a.NC; ++n) {
-            if (n + 1 < a.NC) stage_kib(blk + (size_t)(n + 1) * bwd_op_floats(DK) * 4, sOp[(n + 1) & 1], kPieces, 0, 1);
+            if (n + 1 < a.NC) stage_kib(blk + (size_t)(n + 1) * O::bytes, sOp[(n + 1) & 1], kPieces, 0, 1);
             wait_vmcnt<0>();
             __syncthreads();
         }
@@ -389,36 +421,38 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_states_kernel(const Bw
     for (int n = 0; n < a.NC; ++n) {
         const int buf = n & 1;
         if (n + 1 < a.NC) load_v(n + 1, vnext);  // the next chunk's values travel during this one
-        const float* op = sOp[buf];
+        const unsigned char* op = reinterpret_cast<const unsigned char*>(sOp[buf]);
+        const float* betaS = O::f32(op, O::betaS);
+        const float* gamS = O::f32(op, O::gamS);
         // E = V - Kd S, scaled by beta per token
         floatx4 Eb[2];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < KSD; ++s) acc = mma(frag_tile(op + O::Kd, tb, s, KSD), frag_strip(S, s), acc);
+            for (int s = 0; s < KSD; ++s) acc = mma(frag_tile(O::tiles(op, O::Kd), tb, s, KSD), frag_strip<T>(S, s), acc);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * tb + 4 * gq + i;
-                Eb[tb][i] = op[O::betaS + t] * (vcur[4 * tb + i] - acc[i]);
+                Eb[tb][i] = betaS[t] * (vcur[4 * tb + i] - acc[i]);
             }
         }
         // U = T (beta E)
         floatx4 U[2];
-        const Frag<float> Ebf = frag_from_c<float>(Eb[0], Eb[1]);
+        const Frag<T> Ebf = frag_from_c<T>(Eb[0], Eb[1]);
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
             const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
-            U[tb] = mma(frag_tile(op + O::Tm, tb, 0, 1), Ebf, z4);
+            U[tb] = mma(frag_tile(O::tiles(op, O::Tm), tb, 0, 1), Ebf, z4);
         }
         // S <- Diag(gamma) S + Kp^T U
-        const Frag<float> Uf = frag_from_c<float>(U[0], U[1]);
+        const Frag<T> Uf = frag_from_c<T>(U[0], U[1]);
 #pragma unroll
         for (int R = 0; R < NBD; ++R) {
             floatx4 acc;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = op[O::gamS + 16 * R + 4 * gq + i] * S[R][i];
-            S[R] = mma(frag_tile(op + O::KpT, R, 0, 1), Uf, acc);
+            for (int i = 0; i < 4; ++i) acc[i] = gamS[16 * R + 4 * gq + i] * S[R][i];
+            S[R] = mma(frag_tile(O::tiles(op, O::KpT), R, 0, 1), Uf, acc);
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) vcur[u] = vnext[u];
@@ -431,23 +465,23 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_states_kernel(const Bw
 
 template <typename T, int DK, int NSW>
 __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_adjoint_kernel(const BwdArgs a) {
-    using O = Ops<DK>;
+    using O = Ops<T, DK>;
     constexpr int NBD = DK / 16, KSD = (DK + 31) / 32;
-    constexpr int kPieces = (int)(O::sizeA / 256);
+    constexpr int kPieces = (int)(O::sizeA / 1024);
     constexpr size_t A0 = O::A0;
-    __shared__ __align__(16) float sOp[2][O::sizeA];
+    __shared__ __align__(16) float sOp[2][O::sizeA / 4];
     const int ngrp = (a.Dv / 16) / NSW;
     const int bh = blockIdx.x / ngrp, grp = blockIdx.x % ngrp;
     const int b = bh / a.H, h = bh % a.H;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, gq = lane >> 4;
     const int col = 16 * (grp * NSW + w) + r;
-    const unsigned char* blk = reinterpret_cast<const unsigned char*>(a.ops + (size_t)bh * a.NC * bwd_op_floats(DK) + A0);
+    const unsigned char* blk = a.ops + (size_t)bh * a.NC * O::bytes + A0;
     if (w == NSW) {  // the copy wave, one chunk ahead (chunks in reverse order)
-        if (a.NC > 0) stage_kib(blk + (size_t)(a.NC - 1) * bwd_op_floats(DK) * 4, sOp[0], kPieces, 0, 1);
+        if (a.NC > 0) stage_kib(blk + (size_t)(a.NC - 1) * O::bytes, sOp[0], kPieces, 0, 1);
         wait_vmcnt<0>();
         __syncthreads();
         for (int n = a.NC - 1, it = 0; n >= 0; --n, ++it) {
-            if (n > 0) stage_kib(blk + (size_t)(n - 1) * bwd_op_floats(DK) * 4, sOp[(it + 1) & 1], kPieces, 0, 1);
+            if (n > 0) stage_kib(blk + (size_t)(n - 1) * O::bytes, sOp[(it + 1) & 1], kPieces, 0, 1);
             wait_vmcnt<0>();
             __syncthreads();
         }
@@ -460,12 +494,12 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_adjoint_kernel(const B
         for (int i = 0; i < 4; ++i)
             dS[R][i] = a.dS_T ? a.dS_T[((size_t)bh * DK + 16 * R + 4 * gq + i) * a.Dv + col] : 0.f;
     // dO of one chunk as the B operand of a product over its tokens
-    auto load_do = [&](int n, Frag<float>& f) {
+    auto load_do = [&](int n, Frag<T>& f) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int tok = n * C + slot_index(gq, j);
             const float x = ldf<T>(a.dout, (((size_t)b * a.T + min(tok, a.T - 1)) * a.H + h) * a.Dv + col);
-            f.v[j] = tok < a.T ? x : 0.f;
+            f.set(j, tok < a.T ? x : 0.f);
         }
     };
     // the adjoint at the end of chunk n (its stores are waited for a chunk later)
@@ -476,7 +510,7 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_adjoint_kernel(const B
 #pragma unroll
             for (int i = 0; i < 4; ++i) An[(size_t)(16 * R + 4 * gq + i) * a.Dv + col] = dS[R][i];
     };
-    Frag<float> dOf, dOnext;
+    Frag<T> dOf, dOnext;
     if (a.NC > 0) {
         load_do(a.NC - 1, dOf);
         store_adj(a.NC - 1);
@@ -485,36 +519,39 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_adjoint_kernel(const B
     for (int n = a.NC - 1, it = 0; n >= 0; --n, ++it) {
         const int buf = it & 1;
         if (n > 0) load_do(n - 1, dOnext);  // the previous chunk's dO travels during this one
-        const float* op = sOp[buf];
+        const unsigned char* op = reinterpret_cast<const unsigned char*>(sOp[buf]);  // region A: offsets - A0
+        const float* betaA = O::f32(op, O::betaA - A0);
+        const float* gamA = O::f32(op, O::gamA - A0);
         // dU = Aqk^T dO + Kp dS'
         floatx4 dU[2];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
             const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
-            floatx4 acc = mma(frag_tile(op + (O::AqkT - A0), tb, 0, 1), dOf, z4);
+            floatx4 acc = mma(frag_tile(O::tiles(op, O::AqkT - A0), tb, 0, 1), dOf, z4);
 #pragma unroll
-            for (int s = 0; s < KSD; ++s) acc = mma(frag_tile(op + (O::Kp - A0), tb, s, KSD), frag_strip(dS, s), acc);
+            for (int s = 0; s < KSD; ++s)
+                acc = mma(frag_tile(O::tiles(op, O::Kp - A0), tb, s, KSD), frag_strip<T>(dS, s), acc);
             dU[tb] = acc;
         }
         // -beta W with W = T^T dU
         floatx4 X[2];
-        const Frag<float> dUf = frag_from_c<float>(dU[0], dU[1]);
+        const Frag<T> dUf = frag_from_c<T>(dU[0], dU[1]);
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
             const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
-            const floatx4 wv = mma(frag_tile(op + (O::TT - A0), tb, 0, 1), dUf, z4);
+            const floatx4 wv = mma(frag_tile(O::tiles(op, O::TT - A0), tb, 0, 1), dUf, z4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) X[tb][i] = -op[O::betaA - A0 + 16 * tb + 4 * gq + i] * wv[i];
+            for (int i = 0; i < 4; ++i) X[tb][i] = -betaA[16 * tb + 4 * gq + i] * wv[i];
         }
         // dS = Diag(gamma) dS' + Qp^T dO - Kd^T (beta W)
-        const Frag<float> Xf = frag_from_c<float>(X[0], X[1]);
+        const Frag<T> Xf = frag_from_c<T>(X[0], X[1]);
 #pragma unroll
         for (int R = 0; R < NBD; ++R) {
             floatx4 acc;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = op[O::gamA - A0 + 16 * R + 4 * gq + i] * dS[R][i];
-            acc = mma(frag_tile(op + (O::QpT - A0), R, 0, 1), dOf, acc);
-            dS[R] = mma(frag_tile(op + (O::KdT - A0), R, 0, 1), Xf, acc);
+            for (int i = 0; i < 4; ++i) acc[i] = gamA[16 * R + 4 * gq + i] * dS[R][i];
+            acc = mma(frag_tile(O::tiles(op, O::QpT - A0), R, 0, 1), dOf, acc);
+            dS[R] = mma(frag_tile(O::tiles(op, O::KdT - A0), R, 0, 1), Xf, acc);
         }
         dOf = dOnext;
         __syncthreads();
@@ -533,13 +570,14 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_adjoint_kernel(const B
 // B operand of a product over rows k0 .. k0 + 31 of a row-major fp32 matrix
 // (leading dimension ld) at column col: lane (r, gq) supplies rows
 // k0 + slot_index(gq, j); rows past klen are zero.
-__device__ __forceinline__ Frag<float> frag_cols(const float* M, int ld, int k0, int col, int klen) {
+template <typename E>
+__device__ __forceinline__ Frag<E> frag_cols(const float* M, int ld, int k0, int col, int klen) {
     const int gq = (threadIdx.x & 63) >> 4;
-    Frag<float> f;
+    Frag<E> f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int k = k0 + slot_index(gq, j);
-        f.v[j] = k < klen ? M[(size_t)k * ld + col] : 0.f;
+        f.set(j, k < klen ? M[(size_t)k * ld + col] : 0.f);
     }
     return f;
 }
@@ -581,8 +619,9 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, r = lane & 15, gq = lane >> 4;
     const int t0 = n * C;
+    using O = Ops<T, DK>;
     prep_chunk<T, DK, DK, 512>(a, b, h, t0, sQ, sK, sG, sB, sRq, sRk, sZ);
-    const float* op = a.ops + ((size_t)bh * a.NC + n) * bwd_op_floats(DK);
+    const unsigned char* op = a.ops + ((size_t)bh * a.NC + n) * O::bytes;
     const float* S0 = a.states + ((size_t)bh * a.NC + n) * DK * DV;
     const float* dSC = a.adj + ((size_t)bh * a.NC + n) * DK * DV;
     auto row_of = [&](int t) { return ((size_t)b * a.T + t0 + t) * a.H + h; };
@@ -601,12 +640,12 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
         floatx4 E[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, dU[2] = {E[0], E[0]};
 #pragma unroll
         for (int s = 0; s < KSD; ++s) {
-            const Frag<float> Sf = frag_cols(S0, DV, 32 * s, col, DK);
-            const Frag<float> Df = frag_cols(dSC, DV, 32 * s, col, DK);
+            const Frag<T> Sf = frag_cols<T>(S0, DV, 32 * s, col, DK);
+            const Frag<T> Df = frag_cols<T>(dSC, DV, 32 * s, col, DK);
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) {
-                E[tb] = mma(frag_tile(op + Ops<DK>::Kd, tb, s, KSD), Sf, E[tb]);
-                dU[tb] = mma(frag_tile(op + Ops<DK>::Kp, tb, s, KSD), Df, dU[tb]);
+                E[tb] = mma(frag_tile(O::tiles(op, O::Kd), tb, s, KSD), Sf, E[tb]);
+                dU[tb] = mma(frag_tile(O::tiles(op, O::Kp), tb, s, KSD), Df, dU[tb]);
             }
         }
         floatx4 dO[2], Eb[2];
@@ -621,19 +660,19 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
                 Eb[tb][i] = sB[t] * E[tb][i];
                 dO[tb][i] = sdO[t * PV + col];
             }
-        const Frag<float> dOf = frag_from_c<float>(dO[0], dO[1]);
-        const Frag<float> Ebf = frag_from_c<float>(Eb[0], Eb[1]);
+        const Frag<T> dOf = frag_from_c<T>(dO[0], dO[1]);
+        const Frag<T> Ebf = frag_from_c<T>(Eb[0], Eb[1]);
         const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
         floatx4 U[2];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
-            dU[tb] = mma(frag_tile(op + Ops<DK>::AqkT, tb, 0, 1), dOf, dU[tb]);  // + Aqk^T dO
-            U[tb] = mma(frag_tile(op + Ops<DK>::Tm, tb, 0, 1), Ebf, z4);         // T (beta E)
+            dU[tb] = mma(frag_tile(O::tiles(op, O::AqkT), tb, 0, 1), dOf, dU[tb]);  // + Aqk^T dO
+            U[tb] = mma(frag_tile(O::tiles(op, O::Tm), tb, 0, 1), Ebf, z4);         // T (beta E)
         }
-        const Frag<float> dUf = frag_from_c<float>(dU[0], dU[1]);
+        const Frag<T> dUf = frag_from_c<T>(dU[0], dU[1]);
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
-            const floatx4 W = mma(frag_tile(op + Ops<DK>::TT, tb, 0, 1), dUf, z4);  // T^T dU
+            const floatx4 W = mma(frag_tile(O::tiles(op, O::TT), tb, 0, 1), dUf, z4);  // T^T dU
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * tb + 4 * gq + i;
@@ -653,14 +692,16 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
         const float* X = kind == 0 ? sW : sdO;
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KSV; ++s) acc = mma(frag_rows(X, PV, 16 * tb, 32 * s, DV), frag_rows(sU, PV, 16 * sb, 32 * s, DV), acc);
+        for (int s = 0; s < KSV; ++s)
+            acc = mma(cvt_frag<T>(frag_rows(X, PV, 16 * tb, 32 * s, DV)), cvt_frag<T>(frag_rows(sU, PV, 16 * sb, 32 * s, DV)),
+                      acc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = 16 * tb + 4 * gq + i, s = 16 * sb + r;
             if (kind == 0) {
                 const float dakk = (s < t) ? -acc[i] : 0.f;
                 sdAt[t][s] = sB[t] * dakk;  // dAt = Diag(beta) dA_kk
-                const float p = row_sum16(dakk * op[Ops<DK>::At + t * C + s]);
+                const float p = row_sum16(dakk * O::f32(op, O::At)[t * C + s]);
                 if (r == 0) atomicAdd(&sdB[t], p);
             } else {
                 sdAqk[t][s] = (s <= t) ? acc[i] : 0.f;
@@ -678,11 +719,12 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
             const Frag<float> dSf = frag_rows(dSC, DV, 16 * w, 32 * s, DV);
 #pragma unroll
             for (int j = 0; j < 8; ++j) dgam = fmaf(S0f.v[j], dSf.v[j], dgam);
+            const Frag<T> S0o = cvt_frag<T>(S0f), dSo = cvt_frag<T>(dSf);
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) {
-                dQp[tb] = mma(frag_rows(sdO, PV, 16 * tb, 32 * s, DV), S0f, dQp[tb]);
-                dKd[tb] = mma(frag_rows(sW, PV, 16 * tb, 32 * s, DV), S0f, dKd[tb]);
-                dKp[tb] = mma(frag_rows(sU, PV, 16 * tb, 32 * s, DV), dSf, dKp[tb]);
+                dQp[tb] = mma(cvt_frag<T>(frag_rows(sdO, PV, 16 * tb, 32 * s, DV)), S0o, dQp[tb]);
+                dKd[tb] = mma(cvt_frag<T>(frag_rows(sW, PV, 16 * tb, 32 * s, DV)), S0o, dKd[tb]);
+                dKp[tb] = mma(cvt_frag<T>(frag_rows(sU, PV, 16 * tb, 32 * s, DV)), dSo, dKp[tb]);
             }
         }
         dgam += __shfl_xor(dgam, 16, 64);
