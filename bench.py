@@ -89,8 +89,6 @@ def kernel_bytes(B, T, H, Dk, Dv, C, esize=2):
     return {"kda_intra": intra, "kda_inter": inter}
 
 
-
-
 def decode_bytes(B, H, Dk, Dv, esize=2):
     return 2 * B * H * Dk * Dv * 4 + B * H * (3 * Dk + Dv + 1) * esize + B * H * Dv * esize + H * 4
 
