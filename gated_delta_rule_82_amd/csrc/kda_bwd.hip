@@ -44,6 +44,13 @@ namespace {
 
 constexpr int C = kBwdChunk;
 
+// A 16-token block whose decay on some channel exceeds 2^-kBwdWideLog2 (log2
+// units) has its decay-weighted gradient sums taken element by element: the
+// factored form's factors reach 2^(kBwdWideLog2 / 2), which leaves 2^48 of the
+// fp32 (and bf16) range for the coefficients and the 32-term sums.  Bounded
+// gates never reach it (a block spans 15 decay steps, 2^-108 at g_min = -5).
+constexpr float kBwdWideLog2 = 160.f;
+
 // Byte offsets of the operator block of one chunk-head, operand tiles in the
 // input precision E (fp32 or bf16).  Matrices that serve as matrix-core A
 // operands are stored as operand tiles: tile (row block rb, contraction step
@@ -742,43 +749,96 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
         const int d = 16 * w + r;
         const float GC = sG[C - 1][d];
         float gcpart = 0.f;
-        float Gt[2][4], dkp[2][4], dkm[2][4];
+        float Gt[2][4], Kt[2][4], Qt[2][4], dkp[2][4], dkm[2][4];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * tb + 4 * gq + i;
                 Gt[tb][i] = sG[t][d];
+                Kt[tb][i] = sK[t][d];
+                Qt[tb][i] = sQ[t][d];
                 const float et = exp2_fast(Gt[tb][i]), ect = exp2_fast(GC - Gt[tb][i]);
                 dqh[tb][i] = dQp[tb][i] * et;
                 dkp[tb][i] = dKd[tb][i] * et;
                 dkm[tb][i] = dKp[tb][i] * ect;
-                gcpart = fmaf(dKp[tb][i], sK[t][d] * ect, gcpart);
+                gcpart = fmaf(dKp[tb][i], Kt[tb][i] * ect, gcpart);
             }
-        // partner s outermost: its G, k_hat, q_hat are read once for the eight
-        // tokens.  The stored triangles are zero outside their masks (dAqk[t][s]
-        // for s > t, dAt[t][s] for s >= t), so every term is taken, with the
-        // one exponent exp(-|G_t - G_s|) <= 1 for both orders.
-        for (int s = 0; s < C; ++s) {
-            const float Gs = sG[s][d], Ks = sK[s][d], Qs = sQ[s][d];
+        // The sums over partners s weigh each term by exp(G_t - G_s).  Factored
+        // about rho, the mean of the first and last G of t's 16-token block, every
+        // factor of a same-block pair lies within 2^(+-span / 2) (span: the
+        // block's decay on this channel) and every cross-block factor is <= 1, so
+        // the sums are products on the matrix cores:
+        //   dqh += e^(G_t - rho) dAqk [K e^(rho - G)]            (s <= t)
+        //   dkp += e^(G_t - rho) dAt  [K e^(rho - G)]            (s < t)
+        //   dkm += e^(rho - G_t) (dAqk^T [Q e^(G - rho)] + dAt^T [K e^(G - rho)])   (s >= t)
+        // A B operand's slot j is this lane's own token slot_index(gq, j); the
+        // slots of the block on the masked side, whose factor could overflow,
+        // are zero.  A wave with a block wider than 2^kBwdWideLog2 sums element
+        // by element instead (one exponent <= 1 per term).
+        float rho[2];
+        bool wide_lane = false;
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
+        for (int tb = 0; tb < 2; ++tb) {
+            const float first = __shfl(Gt[tb][0], r, 64), last = __shfl(Gt[tb][3], 48 + r, 64);
+            rho[tb] = 0.5f * (first + last);
+            wide_lane |= first - last > kBwdWideLog2;
+        }
+        if (__ballot(wide_lane) == 0) {
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+                Frag<float> bK, bQe, bKe, aQK, aT, aQKt, aTt;  // fp32: dG takes differences of these sums
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int sb = j >> 2, si = j & 3;  // the slot's token: 16 sb + 4 gq + si
+                    const float g = Gt[sb][si];
+                    bK.set(j, sb <= tb ? Kt[sb][si] * exp2_fast(rho[tb] - g) : 0.f);
+                    const float eh = sb >= tb ? exp2_fast(g - rho[tb]) : 0.f;
+                    bQe.set(j, Qt[sb][si] * eh);
+                    bKe.set(j, Kt[sb][si] * eh);
+                    const int s = slot_index(gq, j), t = 16 * tb + r;
+                    aQK.set(j, sdAqk[t][s]);
+                    aT.set(j, sdAt[t][s]);
+                    aQKt.set(j, sdAqk[s][t]);
+                    aTt.set(j, sdAt[s][t]);
+                }
+                const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
+                const floatx4 cq = mma(aQK, bK, z4);
+                const floatx4 cp = mma(aT, bK, z4);
+                const floatx4 cm = mma(aTt, bKe, mma(aQKt, bQe, z4));
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * tb + 4 * gq + i;
-                    const float e = exp2_fast(-fabsf(Gt[tb][i] - Gs));
-                    dqh[tb][i] = fmaf(sdAqk[t][s] * Ks, e, dqh[tb][i]);
-                    dkp[tb][i] = fmaf(sdAt[t][s] * Ks, e, dkp[tb][i]);
-                    dkm[tb][i] = fmaf(sdAqk[s][t] * Qs + sdAt[s][t] * Ks, e, dkm[tb][i]);
+                    const float up = exp2_fast(Gt[tb][i] - rho[tb]), dn = exp2_fast(rho[tb] - Gt[tb][i]);
+                    dqh[tb][i] = fmaf(up, cq[i], dqh[tb][i]);
+                    dkp[tb][i] = fmaf(up, cp[i], dkp[tb][i]);
+                    dkm[tb][i] = fmaf(dn, cm[i], dkm[tb][i]);
                 }
+            }
+        } else {
+            // partner s outermost: its G, k_hat, q_hat are read once for the eight
+            // tokens.  The stored triangles are zero outside their masks (dAqk[t][s]
+            // for s > t, dAt[t][s] for s >= t), so every term is taken, with the
+            // one exponent exp(-|G_t - G_s|) <= 1 for both orders.
+            for (int s = 0; s < C; ++s) {
+                const float Gs = sG[s][d], Ks = sK[s][d], Qs = sQ[s][d];
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = 16 * tb + 4 * gq + i;
+                        const float e = exp2_fast(-fabsf(Gt[tb][i] - Gs));
+                        dqh[tb][i] = fmaf(sdAqk[t][s] * Ks, e, dqh[tb][i]);
+                        dkp[tb][i] = fmaf(sdAt[t][s] * Ks, e, dkp[tb][i]);
+                        dkm[tb][i] = fmaf(sdAqk[s][t] * Qs + sdAt[s][t] * Ks, e, dkm[tb][i]);
+                    }
+            }
         }
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = 16 * tb + 4 * gq + i;
                 dkh[tb][i] = dkp[tb][i] + dkm[tb][i];
-                dGv[tb][i] = sQ[t][d] * dqh[tb][i] + sK[t][d] * (dkp[tb][i] - dkm[tb][i]);
+                dGv[tb][i] = Qt[tb][i] * dqh[tb][i] + Kt[tb][i] * (dkp[tb][i] - dkm[tb][i]);
             }
         gcpart += __shfl_xor(gcpart, 16, 64);
         gcpart += __shfl_xor(gcpart, 32, 64);

@@ -75,11 +75,15 @@ def test_backward_optional_states(with_S0, with_dST):
     run_and_compare(inp, do, dST, F32, kda.FLAGS_DEFAULT, f"S0 {with_S0} dS_T {with_dST}")
 
 
-def test_backward_v1_gate_strong_decay():
-    # per-token decays far beyond any bounded gate: every factor in one exponent
-    inp, do, dST = case(1, 70, 2, 128, 64, F32, 11, V1)
-    inp["z"] = (inp["z"] * 6.0 + 8.0)
-    run_and_compare(inp, do, dST, F32, V1, "v1 strong decay")
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("zscale,zshift", [(6.0, 8.0), (4.0, 4.0), (2.0, 2.0)])
+def test_backward_v1_gate_strong_decay(dtype, zscale, zshift):
+    # per-token decays far beyond any bounded gate: 16-token blocks wider than
+    # the factored sums allow (summed element by element) on every channel,
+    # on some channels only, or on none
+    inp, do, dST = case(1, 70, 2, 128, 64, dtype, 11, V1)
+    inp["z"] = (inp["z"].float() * zscale + zshift).to(inp["z"].dtype)
+    run_and_compare(inp, do, dST, dtype, V1, f"v1 strong decay z*{zscale}+{zshift}")
 
 
 @pytest.mark.parametrize("T", [1, 31, 32, 33])
