@@ -180,7 +180,7 @@ __device__ __forceinline__ float gate_of(float zv, float eA, float g_min, unsign
 // branch and no wait before use) and are replaced by zero afterwards.
 template <typename T, int DK, int P, int NTHR>
 __device__ void prep_chunk(const BwdArgs& a, int b, int h, int t0, float (*sQ)[P], float (*sK)[P], float (*sG)[P],
-                           float* sB, float* sRq, float* sRk, float (*sZ)[P] = nullptr) {
+                           float* sB, float* sRq, float* sRk) {
     constexpr int NPT = C * DK / NTHR;
     static_assert(NPT * NTHR == C * DK, "whole rows per thread group");
     const int tid = threadIdx.x;
@@ -207,7 +207,6 @@ __device__ void prep_chunk(const BwdArgs& a, int b, int h, int t0, float (*sQ)[P
         sQ[t][d] = valid ? qv[u] : 0.f;
         sK[t][d] = valid ? kv[u] : 0.f;
         sG[t][d] = valid ? gate_of(zv[u], eA, a.g_min, a.flags) : 0.f;
-        if (sZ) sZ[t][d] = valid ? zv[u] : 0.f;
     }
     if (tid < C) {
         const float bt = (a.flags & kBetaSig) ? 1.f / (1.f + expf(-br)) : br;
@@ -601,19 +600,19 @@ __device__ __forceinline__ float row_sum16(float x) {
 // layout and feed the next product directly), and channel block 16 w ..
 // 16 w + 15 for the products over the value dimension (dQp, dKd, dKp, with
 // the rows of dO, U and W read from LDS and the rows of S and dS' as
-// contiguous global fragments) and for the decay-weighted sums, where lane
-// (r, gq) owns channel 16 w + r and the eight tokens 16 tb + 4 gq + i.
+// contiguous global fragments), and for the decay-weighted sums and the
+// outputs, where lane (r, gq) owns channel 16 w + r and the eight tokens
+// 16 tb + 4 gq + i.
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
     constexpr int NT = 512;
     constexpr int NBV = DV / 16, NBK = DK / 16;
     constexpr int KSD = (DK + 31) / 32, KSV = (DV + 31) / 32;
     constexpr int PV = DV + 4;  // row pitch of the value rows (16-byte rows, spread banks)
-    constexpr int kBig = (3 * C * PV > 3 * C * DK) ? 3 * C * PV : 3 * C * DK;
-    __shared__ float sQ[C][DK], sK[C][DK], sG[C][DK], sZ[C][DK];
+    __shared__ float sQ[C][DK], sK[C][DK], sG[C][DK];
     __shared__ float sB[C], sRq[C], sRk[C], sdB[C];
-    __shared__ float sGC[DK];
-    __shared__ __align__(16) float sBig[kBig];
+    __shared__ float sPq[NBK][C], sPk[NBK][C], sPqT[C], sPkT[C];
+    __shared__ __align__(16) float sBig[3 * C * PV];
     __shared__ float sdAqk[C][C + 1], sdAt[C][C + 1];
     __shared__ float sRed[NT / 64];
     float* sdO = sBig;              // [C][PV]
@@ -627,7 +626,7 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
     const int w = tid >> 6, lane = tid & 63, r = lane & 15, gq = lane >> 4;
     const int t0 = n * C;
     using O = Ops<T, DK>;
-    prep_chunk<T, DK, DK, 512>(a, b, h, t0, sQ, sK, sG, sB, sRq, sRk, sZ);
+    prep_chunk<T, DK, DK, 512>(a, b, h, t0, sQ, sK, sG, sB, sRq, sRk);
     const unsigned char* op = a.ops + ((size_t)bh * a.NC + n) * O::bytes;
     const float* S0 = a.states + ((size_t)bh * a.NC + n) * DK * DV;
     const float* dSC = a.adj + ((size_t)bh * a.NC + n) * DK * DV;
@@ -744,12 +743,23 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
     __syncthreads();
 
     // ---- decay-weighted sums: lane (r, gq) of wave w owns channel 16 w + r
-    float dqh[2][4], dkh[2][4], dGv[2][4];
+    // at tokens 16 tb + 4 gq + i, here and for the outputs
+    float dqh[2][4], dkh[2][4], dGv[2][4], Kt[2][4], Qt[2][4], zl[2][4];
+    float gce = 0.f;  // the chunk-end terms of dg, entering at the last token
     if (w < NBK) {
         const int d = 16 * w + r;
+        // the (biased) gate logits for dz: loaded now, used at the end
+        const float zb = a.dt_bias ? a.dt_bias[(size_t)h * DK + d] : 0.f;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tok = min(t0 + 16 * tb + 4 * gq + i, a.T - 1);
+                zl[tb][i] = ldf<T>(a.z, (((size_t)b * a.T + tok) * a.H + h) * DK + d) + zb;
+            }
         const float GC = sG[C - 1][d];
         float gcpart = 0.f;
-        float Gt[2][4], Kt[2][4], Qt[2][4], dkp[2][4], dkm[2][4];
+        float Gt[2][4], dkp[2][4], dkm[2][4];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
@@ -842,87 +852,118 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
             }
         gcpart += __shfl_xor(gcpart, 16, 64);
         gcpart += __shfl_xor(gcpart, 32, 64);
-        if (gq == 0) sGC[d] = gcpart + dgam * exp2_fast(GC);
+        gce = gcpart + dgam * exp2_fast(GC);
     }
-    __syncthreads();  // every read of the value rows is done: reuse their space
-    float* fdq = sBig;
-    float* fdk = sBig + C * DK;
-    float* fdG = sBig + 2 * C * DK;
+
+    // ---- outputs: dg by a reverse cumulative sum of dG over the chunk (within
+    // the lane, over the four lane groups, then from the second 16-token block
+    // into the first), dz through the gate, and the per-token dot products of
+    // the L2-norm backward (over the 16 lanes of a group, then over the waves)
+    const float eA = (a.flags & kGateIn) ? expf(a.A_log[h]) : 0.f;
+    float dApart = 0.f;
     if (w < NBK) {
         const int d = 16 * w + r;
+        float suf[2][4], base[2];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            suf[tb][3] = dGv[tb][3];
+#pragma unroll
+            for (int i = 2; i >= 0; --i) suf[tb][i] = suf[tb][i + 1] + dGv[tb][i];
+        }
+        float incl[2];  // suffix sums of the lane totals over the lane groups gq .. 3
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            float x = suf[tb][0];
+            float y = __shfl_down(x, 16, 64);
+            x += gq < 3 ? y : 0.f;
+            y = __shfl_down(x, 32, 64);
+            x += gq < 2 ? y : 0.f;
+            incl[tb] = x;
+        }
+        const float block1 = __shfl(incl[1], r, 64);  // all of the second block
+        base[0] = gce + block1 + (incl[0] - suf[0][0]);
+        base[1] = gce + (incl[1] - suf[1][0]);
+        float dbias = 0.f;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * tb + 4 * gq + i;
-                fdq[t * DK + d] = dqh[tb][i];
-                fdk[t * DK + d] = dkh[tb][i];
-                fdG[t * DK + d] = dGv[tb][i];
-            }
-    }
-    __syncthreads();
-
-    // ---- outputs: dg by a reverse cumulative sum, then the activations
-    float dApart = 0.f;
-    const float eA = (a.flags & kGateIn) ? expf(a.A_log[h]) : 0.f;
-    for (int dd = tid; dd < DK; dd += NT) {
-        float acc = sGC[dd];  // the chunk-end terms enter at the last token
-        float dbias = 0.f;    // the logit gradient summed over the chunk's tokens
-        for (int t = C - 1; t >= 0; --t) {
-            acc += fdG[t * DK + dd];
-            if (t0 + t < a.T) {
-                const size_t idx = row_of(t) * DK + dd;
-                float dz = acc;
+                const bool valid = t0 + t < a.T;
+                const float acc = base[tb] + suf[tb][i];
+                float dz = acc, dA = 0.f;
                 if (a.flags & kGateIn) {
-                    const float zv = sZ[t][dd];
+                    const float zv = zl[tb][i];
                     if (a.flags & kGateSoftplus) {
                         const float sg = 1.f / (1.f + expf(-zv));
                         dz = acc * (-eA * sg);
-                        dApart += acc * gate_of(zv, eA, a.g_min, a.flags);
+                        dA = acc * gate_of(zv, eA, a.g_min, a.flags);
                     } else {
                         const float sg = 1.f / (1.f + expf(-eA * zv));
                         const float dx = acc * a.g_min * sg * (1.f - sg);  // d / d(e^A z)
                         dz = dx * eA;
-                        dApart += dx * eA * zv;
+                        dA = dx * eA * zv;
                     }
                 }
-                stf<T>(a.dz, idx, dz);
-                dbias += dz;
+                if (valid) stf<T>(a.dz, row_of(t) * DK + d, dz);
+                dApart += valid ? dA : 0.f;
+                dbias += valid ? dz : 0.f;
             }
-        }
-        if (a.dbias_part) a.dbias_part[(((size_t)b * a.NC + n) * a.H + h) * DK + dd] = dbias;
-    }
-    // dq, dk through the L2 norm: dx = r (dx_hat - x_hat (x_hat . dx_hat)); one wave per token
-    for (int t = w; t < C; t += NT / 64) {
-        if (t0 + t >= a.T) continue;  // wave-uniform
-        float pq = 0.f, pk = 0.f;
-        for (int dd = lane; dd < DK; dd += 64) {
-            pq += sQ[t][dd] * fdq[t * DK + dd];
-            pk += sK[t][dd] * fdk[t * DK + dd];
-        }
+        dbias += __shfl_xor(dbias, 16, 64);
+        dbias += __shfl_xor(dbias, 32, 64);
+        if (a.dbias_part && gq == 0) a.dbias_part[(((size_t)b * a.NC + n) * a.H + h) * DK + d] = dbias;
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            pq += __shfl_xor(pq, off, 64);
-            pk += __shfl_xor(pk, off, 64);
-        }
-        const bool l2 = (a.flags & kQkL2) != 0;
-        for (int dd = lane; dd < DK; dd += 64) {
-            const size_t idx = row_of(t) * DK + dd;
-            const float gq_ = l2 ? sRq[t] * (fdq[t * DK + dd] - sQ[t][dd] * pq) : fdq[t * DK + dd];
-            const float gk_ = l2 ? sRk[t] * (fdk[t * DK + dd] - sK[t][dd] * pk) : fdk[t * DK + dd];
-            if (a.G == 1) {
-                stf<T>(a.dq, idx, gq_);
-                stf<T>(a.dk, idx, gk_);
-            } else {  // this value head's share; the group is summed afterwards
-                a.dqk_part[idx] = gq_;
-                a.dqk_part[(size_t)a.B * a.T * a.H * DK + idx] = gk_;
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * tb + 4 * gq + i;
+                const float pq = row_sum16(Qt[tb][i] * dqh[tb][i]);
+                const float pk = row_sum16(Kt[tb][i] * dkh[tb][i]);
+                if (r == 0) {
+                    sPq[w][t] = pq;
+                    sPk[w][t] = pk;
+                }
             }
+    }
+    __syncthreads();
+    if (tid < C) {  // the per-token dot products over all channels; dbeta
+        const int t = tid;
+        float pq = 0.f, pk = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NBK; ++ww) {
+            pq += sPq[ww][t];
+            pk += sPk[ww][t];
         }
-        if (lane == 0) {
+        sPqT[t] = pq;
+        sPkT[t] = pk;
+        if (t0 + t < a.T) {
             const float bt = sB[t];
             const float db = (a.flags & kBetaSig) ? sdB[t] * bt * (1.f - bt) : sdB[t];
             stf<T>(a.dbeta_raw, row_of(t), db);
         }
+    }
+    __syncthreads();
+    // dq, dk through the L2 norm: dx = r (dx_hat - x_hat (x_hat . dx_hat))
+    if (w < NBK) {
+        const int d = 16 * w + r;
+        const bool l2 = (a.flags & kQkL2) != 0;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * tb + 4 * gq + i;
+                if (t0 + t >= a.T) continue;
+                const size_t idx = row_of(t) * DK + d;
+                const float gq_ = l2 ? sRq[t] * (dqh[tb][i] - Qt[tb][i] * sPqT[t]) : dqh[tb][i];
+                const float gk_ = l2 ? sRk[t] * (dkh[tb][i] - Kt[tb][i] * sPkT[t]) : dkh[tb][i];
+                if (a.G == 1) {
+                    stf<T>(a.dq, idx, gq_);
+                    stf<T>(a.dk, idx, gk_);
+                } else {  // this value head's share; the group is summed afterwards
+                    a.dqk_part[idx] = gq_;
+                    a.dqk_part[(size_t)a.B * a.T * a.H * DK + idx] = gk_;
+                }
+            }
     }
     // the chunk's share of dA_log
 #pragma unroll
