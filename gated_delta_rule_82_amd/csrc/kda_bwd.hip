@@ -139,6 +139,23 @@ __device__ __forceinline__ void stf(void* p, size_t i, float x) {
     reinterpret_cast<T*>(p)[i] = from_f<T>(x);
 }
 
+// A load kept as its raw bits (bf16 zero-extended) until `settle`, an empty
+// asm that needs the register there: the compiler cannot move the conversion,
+// and so the wait for the load, ahead of it.  Loads issued early stay in
+// flight across the work before their use.
+template <typename T> __device__ __forceinline__ uint32_t ldraw(const void* p, size_t i);
+template <> __device__ __forceinline__ uint32_t ldraw<bf16_t>(const void* p, size_t i) {
+    return reinterpret_cast<const uint16_t*>(p)[i];
+}
+template <> __device__ __forceinline__ uint32_t ldraw<float>(const void* p, size_t i) {
+    return reinterpret_cast<const uint32_t*>(p)[i];
+}
+template <typename T> __device__ __forceinline__ float raw_value(uint32_t x) {
+    return sizeof(T) == 2 ? __uint_as_float(x << 16) : __uint_as_float(x);
+}
+__device__ __forceinline__ void settle(uint32_t& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void settle(float& x) { asm volatile("" : "+v"(x)); }
+
 // Fragment of rows row0 .. row0 + 15 of a row-major fp32 matrix (leading
 // dimension ld) at contraction indices k0 + slot_index(gq, j); indices past
 // klen (16 or >= 32) are zero.
@@ -173,52 +190,76 @@ __device__ __forceinline__ float gate_of(float zv, float eA, float g_min, unsign
     return g_min / (1.f + expf(-eA * zv));
 }
 
-// The switched activations of one chunk into LDS: q_hat, k_hat, cumulative
-// log-decay G in log2 units (pitch P), beta and the inverse norms.  Tokens past the end are
-// zero rows with g = 0 and beta = 0 (identity transitions).
-// Loads of tokens past the end read the last token (a valid address, so no
-// branch and no wait before use) and are replaced by zero afterwards.
-template <typename T, int DK, int P, int NTHR>
-__device__ void prep_chunk(const BwdArgs& a, int b, int h, int t0, float (*sQ)[P], float (*sK)[P], float (*sG)[P],
-                           float* sB, float* sRq, float* sRk) {
-    constexpr int NPT = C * DK / NTHR;
-    static_assert(NPT * NTHR == C * DK, "whole rows per thread group");
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6, nw = NTHR >> 6;
-    const float eA = (a.flags & kGateIn) ? expf(a.A_log[h]) : 0.f;
+// The raw inputs of one chunk for one thread: channel d = tid % DK at the NPT
+// consecutive tokens of its thread group tid / DK.  Loaded before any other
+// global operand of the chunk, so that the wait for them does not wait for
+// loads issued later.  Loads of tokens past the end read the last token (a
+// valid address, so no branch and no wait before use) and are replaced by
+// zero afterwards.
+template <int DK, int NTHR>
+struct PrepIn {
+    static constexpr int NG = NTHR / DK, NPT = C / NG;
+    static_assert(NG * DK == NTHR && NG * NPT == C, "whole channel rows per thread group");
+    float q[NPT], k[NPT], z[NPT], br;
+};
+
+template <typename T, int DK, int NTHR>
+__device__ __forceinline__ void prep_load(const BwdArgs& a, int b, int h, int t0, PrepIn<DK, NTHR>& in) {
+    constexpr int NPT = PrepIn<DK, NTHR>::NPT;
+    const int tid = threadIdx.x, d = tid % DK, tg = (tid / DK) * NPT;
     const int Hk = a.H / a.G, hq = h / a.G;  // value head h reads q/k head h / G
-    float qv[NPT], kv[NPT], zv[NPT];
+    // the biased logit; without a bias, a valid address is read and the value dropped
+    // (no branch around a load)
+    const float zbl = *(a.dt_bias ? a.dt_bias + (size_t)h * DK + d : a.A_log + h);
+    const float zb = a.dt_bias ? zbl : 0.f;
 #pragma unroll
     for (int u = 0; u < NPT; ++u) {
-        const int e = tid + u * NTHR, t = e / DK, d = e % DK;
-        const int tok = min(t0 + t, a.T - 1);
+        const int tok = min(t0 + tg + u, a.T - 1);
         const size_t idx_qk = (((size_t)b * a.T + tok) * Hk + hq) * DK + d;
-        qv[u] = ldf<T>(a.q, idx_qk);
-        kv[u] = ldf<T>(a.k, idx_qk);
-        zv[u] = ldf<T>(a.z, (((size_t)b * a.T + tok) * a.H + h) * DK + d);
-        if (a.dt_bias) zv[u] += a.dt_bias[(size_t)h * DK + d];  // the biased logit
+        in.q[u] = ldf<T>(a.q, idx_qk);
+        in.k[u] = ldf<T>(a.k, idx_qk);
+        in.z[u] = ldf<T>(a.z, (((size_t)b * a.T + tok) * a.H + h) * DK + d) + zb;
     }
-    float br = 0.f;
-    if (tid < C) br = ldf<T>(a.beta_raw, ((size_t)b * a.T + min(t0 + tid, a.T - 1)) * a.H + h);
+    in.br = ldf<T>(a.beta_raw, ((size_t)b * a.T + min(t0 + tid % C, a.T - 1)) * a.H + h);  // used by tid < C
+}
+
+// The switched activations of the chunk into LDS: q_hat, k_hat, cumulative
+// log-decay G in log2 units (pitch P), beta and the inverse norms.  Tokens
+// past the end are zero rows with g = 0 and beta = 0 (identity transitions).
+// G is summed over the thread's own tokens in registers, then offset by the
+// totals of the earlier thread groups (sPart: NTHR floats).  The barriers
+// order LDS only: global loads issued before stay in flight.
+template <typename T, int DK, int P, int NTHR>
+__device__ void prep_finish(const BwdArgs& a, int h, int t0, const PrepIn<DK, NTHR>& in, float (*sQ)[P],
+                            float (*sK)[P], float (*sG)[P], float* sB, float* sRq, float* sRk, float* sPart) {
+    constexpr int NPT = PrepIn<DK, NTHR>::NPT;
+    const int tid = threadIdx.x, d = tid % DK, grp = tid / DK, tg = grp * NPT;
+    const int lane = tid & 63, wave = tid >> 6, nw = NTHR >> 6;
+    const float Al = a.A_log[h];
+    const float eA = (a.flags & kGateIn) ? expf(Al) : 0.f;
+    float q[NPT], k[NPT], g[NPT];
 #pragma unroll
     for (int u = 0; u < NPT; ++u) {
-        const int e = tid + u * NTHR, t = e / DK, d = e % DK;
-        const bool valid = t0 + t < a.T;
-        sQ[t][d] = valid ? qv[u] : 0.f;
-        sK[t][d] = valid ? kv[u] : 0.f;
-        sG[t][d] = valid ? gate_of(zv[u], eA, a.g_min, a.flags) : 0.f;
+        const bool valid = t0 + tg + u < a.T;
+        q[u] = valid ? in.q[u] : 0.f;
+        k[u] = valid ? in.k[u] : 0.f;
+        g[u] = (valid ? gate_of(in.z[u], eA, a.g_min, a.flags) : 0.f) * kLog2e;  // log2 units: one exp2 per factor
+        if (u > 0) g[u] += g[u - 1];
+        sQ[tg + u][d] = q[u];
+        sK[tg + u][d] = k[u];
     }
+    sPart[tid] = g[NPT - 1];
     if (tid < C) {
-        const float bt = (a.flags & kBetaSig) ? 1.f / (1.f + expf(-br)) : br;
+        const float bt = (a.flags & kBetaSig) ? 1.f / (1.f + expf(-in.br)) : in.br;
         sB[tid] = (t0 + tid < a.T) ? bt : 0.f;
     }
-    __syncthreads();
+    lds_barrier();
     // inverse norms: one wave per token at a time
     for (int t = wave; t < C; t += nw) {
         float sq = 0.f, sk = 0.f;
-        for (int d = lane; d < DK; d += 64) {
-            sq += sQ[t][d] * sQ[t][d];
-            sk += sK[t][d] * sK[t][d];
+        for (int dd = lane; dd < DK; dd += 64) {
+            sq += sQ[t][dd] * sQ[t][dd];
+            sk += sK[t][dd] * sK[t][dd];
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) {
@@ -230,20 +271,16 @@ __device__ void prep_chunk(const BwdArgs& a, int b, int h, int t0, float (*sQ)[P
             sRk[t] = (a.flags & kQkL2) ? 1.f / sqrtf(sk + kL2Eps) : 1.f;
         }
     }
-    __syncthreads();
-    for (int e = tid; e < C * DK; e += NTHR) {
-        const int t = e / DK, d = e % DK;
-        sQ[t][d] *= sRq[t];
-        sK[t][d] *= sRk[t];
+    float off = 0.f;
+    for (int gg = 0; gg < grp; ++gg) off += sPart[gg * DK + d];
+    lds_barrier();
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) {
+        sQ[tg + u][d] = q[u] * sRq[tg + u];
+        sK[tg + u][d] = k[u] * sRk[tg + u];
+        sG[tg + u][d] = g[u] + off;
     }
-    for (int d = tid; d < DK; d += NTHR) {
-        float acc = 0.f;
-        for (int t = 0; t < C; ++t) {
-            acc += sG[t][d] * kLog2e;  // G in log2 units: every decay factor is one exp2
-            sG[t][d] = acc;
-        }
-    }
-    __syncthreads();
+    lds_barrier();
 }
 
 }  // namespace
@@ -262,11 +299,16 @@ __global__ __launch_bounds__(256) void kda_bwd_ops_kernel(const BwdArgs a) {
     __shared__ float sB[C], sRq[C], sRk[C];
     __shared__ float sAt[C][C + 1];
     __shared__ __align__(16) float sSt[kStage];
+    __shared__ float sPart[256];
     const int n = blockIdx.x % a.NC;
     const int bh = blockIdx.x / a.NC;
     const int b = bh / a.H, h = bh % a.H;
     const int tid = threadIdx.x;
-    prep_chunk<T, DK, P, 256>(a, b, h, n * C, sQ, sK, sG, sB, sRq, sRk);
+    {
+        PrepIn<DK, 256> pin;
+        prep_load<T, DK, 256>(a, b, h, n * C, pin);
+        prep_finish<T, DK, P, 256>(a, h, n * C, pin, sQ, sK, sG, sB, sRq, sRk, sPart);
+    }
     unsigned char* op = a.ops + ((size_t)bh * a.NC + n) * O::bytes;
     float* opf = reinterpret_cast<float*>(op);  // the fp32 parts, in floats
     auto flush = [&](size_t dst, int count) {   // sSt[0, count) -> elements [0, count) at byte dst, as T
@@ -615,6 +657,7 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
     __shared__ __align__(16) float sBig[3 * C * PV];
     __shared__ float sdAqk[C][C + 1], sdAt[C][C + 1];
     __shared__ float sRed[NT / 64];
+    __shared__ float sPart[NT];
     float* sdO = sBig;              // [C][PV]
     float* sU = sBig + C * PV;      // [C][PV]
     float* sW = sBig + 2 * C * PV;  // [C][PV]
@@ -626,32 +669,64 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
     const int w = tid >> 6, lane = tid & 63, r = lane & 15, gq = lane >> 4;
     const int t0 = n * C;
     using O = Ops<T, DK>;
-    prep_chunk<T, DK, DK, 512>(a, b, h, t0, sQ, sK, sG, sB, sRq, sRk);
     const unsigned char* op = a.ops + ((size_t)bh * a.NC + n) * O::bytes;
     const float* S0 = a.states + ((size_t)bh * a.NC + n) * DK * DV;
     const float* dSC = a.adj + ((size_t)bh * a.NC + n) * DK * DV;
     auto row_of = [&](int t) { return ((size_t)b * a.T + t0 + t) * a.H + h; };
+    auto in_row = [&](int t) { return ((size_t)b * a.T + min(t0 + t, a.T - 1)) * a.H + h; };  // clamped
 
-    for (int e = tid; e < C * DV; e += NT) {
-        const int t = e / DV, j = e % DV;
-        const float x = ldf<T>(a.dout, (((size_t)b * a.T + min(t0 + t, a.T - 1)) * a.H + h) * DV + j);
-        sdO[t * PV + j] = (t0 + t < a.T) ? x : 0.f;
+    // Every global operand of the chunk is requested up front, the activations'
+    // inputs first: dO rows, then for the products over tokens this wave's
+    // value column of S, dS' and V.  They arrive while the activations are
+    // prepared in LDS.
+    PrepIn<DK, NT> pin;
+    prep_load<T, DK, NT>(a, b, h, t0, pin);
+    constexpr int NDO = C * DV / NT;
+    static_assert(NDO * NT == C * DV, "whole dO rows per pass");
+    uint32_t dOr[NDO];
+#pragma unroll
+    for (int u = 0; u < NDO; ++u) {
+        const int e = tid + u * NT, t = e / DV, j = e % DV;
+        dOr[u] = ldraw<T>(a.dout, in_row(t) * DV + j);
+    }
+    const int col = 16 * (w % NBV) + r;
+    Frag<float> Sfr[KSD], Dfr[KSD];  // as loaded: converted where used, so nothing waits for them here
+    uint32_t vr[2][4];
+    if (w < NBV) {
+#pragma unroll
+        for (int s = 0; s < KSD; ++s) {
+            Sfr[s] = frag_cols<float>(S0, DV, 32 * s, col, DK);
+            Dfr[s] = frag_cols<float>(dSC, DV, 32 * s, col, DK);
+        }
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vr[tb][i] = ldraw<T>(a.v, in_row(16 * tb + 4 * gq + i) * DV + col);
+    }
+    prep_finish<T, DK, DK, NT>(a, h, t0, pin, sQ, sK, sG, sB, sRq, sRk, sPart);
+#pragma unroll
+    for (int u = 0; u < NDO; ++u) {
+        const int e = tid + u * NT, t = e / DV, j = e % DV;
+        settle(dOr[u]);
+        sdO[t * PV + j] = (t0 + t < a.T) ? raw_value<T>(dOr[u]) : 0.f;
     }
     for (int t = tid; t < C; t += NT) sdB[t] = 0.f;
-    __syncthreads();
+    lds_barrier();
 
     // ---- products over tokens, value column block w
     if (w < NBV) {
-        const int col = 16 * w + r;
         floatx4 E[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, dU[2] = {E[0], E[0]};
 #pragma unroll
         for (int s = 0; s < KSD; ++s) {
-            const Frag<T> Sf = frag_cols<T>(S0, DV, 32 * s, col, DK);
-            const Frag<T> Df = frag_cols<T>(dSC, DV, 32 * s, col, DK);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                settle(Sfr[s].v[j]);
+                settle(Dfr[s].v[j]);
+            }
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) {
-                E[tb] = mma(frag_tile(O::tiles(op, O::Kd), tb, s, KSD), Sf, E[tb]);
-                dU[tb] = mma(frag_tile(O::tiles(op, O::Kp), tb, s, KSD), Df, dU[tb]);
+                E[tb] = mma(frag_tile(O::tiles(op, O::Kd), tb, s, KSD), cvt_frag<T>(Sfr[s]), E[tb]);
+                dU[tb] = mma(frag_tile(O::tiles(op, O::Kp), tb, s, KSD), cvt_frag<T>(Dfr[s]), dU[tb]);
             }
         }
         floatx4 dO[2], Eb[2];
@@ -660,8 +735,8 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * tb + 4 * gq + i;
-                const float vx = ldf<T>(a.v, (((size_t)b * a.T + min(t0 + t, a.T - 1)) * a.H + h) * DV + col);
-                const float vv = (t0 + t < a.T) ? vx : 0.f;
+                settle(vr[tb][i]);
+                const float vv = (t0 + t < a.T) ? raw_value<T>(vr[tb][i]) : 0.f;
                 E[tb][i] = vv - E[tb][i];           // E = V - Kd S
                 Eb[tb][i] = sB[t] * E[tb][i];
                 dO[tb][i] = sdO[t * PV + col];
@@ -859,7 +934,8 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
     // the lane, over the four lane groups, then from the second 16-token block
     // into the first), dz through the gate, and the per-token dot products of
     // the L2-norm backward (over the 16 lanes of a group, then over the waves)
-    const float eA = (a.flags & kGateIn) ? expf(a.A_log[h]) : 0.f;
+    const float Al = a.A_log[h];
+    const float eA = (a.flags & kGateIn) ? expf(Al) : 0.f;
     float dApart = 0.f;
     if (w < NBK) {
         const int d = 16 * w + r;
