@@ -35,6 +35,10 @@
 //                      at each chunk end, and dS0.
 //  4. kda_bwd_grads:   per chunk-head: every input gradient of the chunk.
 //  5. kda_bwd_dA:      the sum of the per-chunk dA_log parts.
+//
+// Workgroups share data through LDS only, so their barriers wait for LDS
+// operations alone (lds_barrier): global stores drain, and global loads issued
+// ahead stay in flight, across them.
 #include "kda_device.h"
 #include "kda_bwd.h"
 
@@ -223,62 +227,95 @@ __device__ __forceinline__ void prep_load(const BwdArgs& a, int b, int h, int t0
     in.br = ldf<T>(a.beta_raw, ((size_t)b * a.T + min(t0 + tid % C, a.T - 1)) * a.H + h);  // used by tid < C
 }
 
+// Sum over the RL lanes (16, 32 or 64, aligned) that share this lane's group,
+// in every lane: row sums with DPP moves (xor 1, xor 2, half-row mirror, row
+// mirror), then the rows' lane 0 read out and added.
+template <int RL>
+__device__ __forceinline__ float group_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));  // row_half_mirror
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));  // row_mirror
+    if constexpr (RL == 16) return x;
+    const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float a2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float a3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    if constexpr (RL == 32) return (threadIdx.x & 32) ? a2 + a3 : a0 + a1;
+    return (a0 + a1) + (a2 + a3);
+}
+
 // The switched activations of the chunk into LDS: q_hat, k_hat, cumulative
 // log-decay G in log2 units (pitch P), beta and the inverse norms.  Tokens
 // past the end are zero rows with g = 0 and beta = 0 (identity transitions).
-// G is summed over the thread's own tokens in registers, then offset by the
-// totals of the earlier thread groups (sPart: NTHR floats).  The barriers
-// order LDS only: global loads issued before stay in flight.
+// Everything a thread needs for its channel's tokens is computed in registers:
+// G summed over its own tokens, then offset by the totals of the earlier
+// thread groups; the squared norms reduced over the wave's lanes of the group
+// for all of its tokens at once, then (DK = 128) with the other wave of the
+// group.  sPart: NTHR floats; sNrm: 2 x (NTHR / 64) x NPT floats.  The
+// barriers order LDS only: global loads issued before stay in flight.
+template <int DK, int NTHR>
+constexpr int prep_norm_floats() { return 2 * (NTHR / 64) * PrepIn<DK, NTHR>::NPT; }
+
 template <typename T, int DK, int P, int NTHR>
 __device__ void prep_finish(const BwdArgs& a, int h, int t0, const PrepIn<DK, NTHR>& in, float (*sQ)[P],
-                            float (*sK)[P], float (*sG)[P], float* sB, float* sRq, float* sRk, float* sPart) {
+                            float (*sK)[P], float (*sG)[P], float* sB, float* sRq, float* sRk, float* sPart,
+                            float* sNrm) {
     constexpr int NPT = PrepIn<DK, NTHR>::NPT;
+    constexpr int NW = NTHR / 64;
+    constexpr int RL = DK < 64 ? DK : 64;  // lanes of one thread group within a wave
     const int tid = threadIdx.x, d = tid % DK, grp = tid / DK, tg = grp * NPT;
-    const int lane = tid & 63, wave = tid >> 6, nw = NTHR >> 6;
+    const int wave = tid >> 6;
     const float Al = a.A_log[h];
     const float eA = (a.flags & kGateIn) ? expf(Al) : 0.f;
-    float q[NPT], k[NPT], g[NPT];
+    const bool l2 = (a.flags & kQkL2) != 0;
+    float q[NPT], k[NPT], g[NPT], nq[NPT], nk[NPT];
 #pragma unroll
     for (int u = 0; u < NPT; ++u) {
         const bool valid = t0 + tg + u < a.T;
         q[u] = valid ? in.q[u] : 0.f;
         k[u] = valid ? in.k[u] : 0.f;
-        g[u] = (valid ? gate_of(in.z[u], eA, a.g_min, a.flags) : 0.f) * kLog2e;  // log2 units: one exp2 per factor
+        const float gl = gate_of(in.z[u], eA, a.g_min, a.flags);  // on a valid logit even past the end
+        g[u] = (valid ? gl : 0.f) * kLog2e;                       // log2 units: one exp2 per factor
         if (u > 0) g[u] += g[u - 1];
-        sQ[tg + u][d] = q[u];
-        sK[tg + u][d] = k[u];
+        nq[u] = q[u] * q[u];
+        nk[u] = k[u] * k[u];
+    }
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) {
+        nq[u] = group_sum<RL>(nq[u]);
+        nk[u] = group_sum<RL>(nk[u]);
     }
     sPart[tid] = g[NPT - 1];
+    if (DK > 64 && (tid & 63) == 0) {
+#pragma unroll
+        for (int u = 0; u < NPT; ++u) {
+            sNrm[wave * NPT + u] = nq[u];
+            sNrm[(NW + wave) * NPT + u] = nk[u];
+        }
+    }
     if (tid < C) {
         const float bt = (a.flags & kBetaSig) ? 1.f / (1.f + expf(-in.br)) : in.br;
         sB[tid] = (t0 + tid < a.T) ? bt : 0.f;
     }
     lds_barrier();
-    // inverse norms: one wave per token at a time
-    for (int t = wave; t < C; t += nw) {
-        float sq = 0.f, sk = 0.f;
-        for (int dd = lane; dd < DK; dd += 64) {
-            sq += sQ[t][dd] * sQ[t][dd];
-            sk += sK[t][dd] * sK[t][dd];
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            sq += __shfl_xor(sq, off, 64);
-            sk += __shfl_xor(sk, off, 64);
-        }
-        if (lane == 0) {
-            sRq[t] = (a.flags & kQkL2) ? 1.f / sqrtf(sq + kL2Eps) : 1.f;
-            sRk[t] = (a.flags & kQkL2) ? 1.f / sqrtf(sk + kL2Eps) : 1.f;
-        }
-    }
     float off = 0.f;
     for (int gg = 0; gg < grp; ++gg) off += sPart[gg * DK + d];
-    lds_barrier();
 #pragma unroll
     for (int u = 0; u < NPT; ++u) {
-        sQ[tg + u][d] = q[u] * sRq[tg + u];
-        sK[tg + u][d] = k[u] * sRk[tg + u];
+        if (DK > 64) {  // the group's other wave
+            nq[u] += sNrm[(wave ^ 1) * NPT + u];
+            nk[u] += sNrm[(NW + (wave ^ 1)) * NPT + u];
+        }
+        const float rq = l2 ? 1.f / sqrtf(nq[u] + kL2Eps) : 1.f;
+        const float rk = l2 ? 1.f / sqrtf(nk[u] + kL2Eps) : 1.f;
+        sQ[tg + u][d] = q[u] * rq;
+        sK[tg + u][d] = k[u] * rk;
         sG[tg + u][d] = g[u] + off;
+        if (d == 0) {
+            sRq[tg + u] = rq;
+            sRk[tg + u] = rk;
+        }
     }
     lds_barrier();
 }
@@ -297,9 +334,9 @@ __global__ __launch_bounds__(256) void kda_bwd_ops_kernel(const BwdArgs a) {
     constexpr int kStage = tile_elems(C, DK) > 2 * C * C ? tile_elems(C, DK) : 2 * C * C;
     __shared__ float sQ[C][P], sK[C][P], sG[C][P];
     __shared__ float sB[C], sRq[C], sRk[C];
-    __shared__ float sAt[C][C + 1];
+    __shared__ float sAt[C][C + 1], sTT[C][C + 1];
     __shared__ __align__(16) float sSt[kStage];
-    __shared__ float sPart[256];
+    __shared__ float sPart[256], sNrm[prep_norm_floats<DK, 256>()];
     const int n = blockIdx.x % a.NC;
     const int bh = blockIdx.x / a.NC;
     const int b = bh / a.H, h = bh % a.H;
@@ -307,15 +344,15 @@ __global__ __launch_bounds__(256) void kda_bwd_ops_kernel(const BwdArgs a) {
     {
         PrepIn<DK, 256> pin;
         prep_load<T, DK, 256>(a, b, h, n * C, pin);
-        prep_finish<T, DK, P, 256>(a, h, n * C, pin, sQ, sK, sG, sB, sRq, sRk, sPart);
+        prep_finish<T, DK, P, 256>(a, h, n * C, pin, sQ, sK, sG, sB, sRq, sRk, sPart, sNrm);
     }
     unsigned char* op = a.ops + ((size_t)bh * a.NC + n) * O::bytes;
     float* opf = reinterpret_cast<float*>(op);  // the fp32 parts, in floats
     auto flush = [&](size_t dst, int count) {   // sSt[0, count) -> elements [0, count) at byte dst, as T
-        __syncthreads();
+        lds_barrier();
         T* out = reinterpret_cast<T*>(op + dst);
         for (int e = 8 * tid; e < count; e += 8 * 256) store_row8(out + e, sSt + e);
-        __syncthreads();
+        lds_barrier();
     };
     // [C x DK] operands: Kd = k_hat exp(G), Kp = k_hat exp(G_C - G); slots past DK are zero
     for (int which = 0; which < 2; ++which) {
@@ -343,54 +380,115 @@ __global__ __launch_bounds__(256) void kda_bwd_ops_kernel(const BwdArgs a) {
     }
     for (int d = tid; d < DK; d += 256) opf[O::gamS / 4 + d] = opf[O::gamA / 4 + d] = exp2_fast(sG[C - 1][d]);
     for (int t = tid; t < C; t += 256) opf[O::betaS / 4 + t] = opf[O::betaA / 4 + t] = sB[t];
-    // At (strictly lower, row-major) and Aqk^T (tiles), each decay factor in one
-    // exponent exp(G_i - G_j) <= 1
-    for (int e = tid; e < C * C; e += 256) {  // zeros above the diagonal
-        const int i = e / C, j = e % C;
-        if (j > i) {
+    // A_kk (strictly lower, no beta) and Aqk (lower) as 16 x 16 blocks on the
+    // matrix cores: wave 0 block (0, 0), wave 1 (1, 1), wave 2 (1, 0), wave 3
+    // the zero block (0, 1).  exp(G_i - G_j) = exp(G_i - rho) exp(rho - G_j)
+    // with rho, per channel, the mean of the first and last G of a diagonal
+    // block (both factors within 2^(+-span / 2)) or G at token 15 for the
+    // off-diagonal block (both factors <= 1).  A diagonal block wider than
+    // 2^kBwdWideLog2 on some channel is summed element by element (one
+    // exponent <= 1 per term).  At goes out row-major, Aqk^T as tiles.
+    const int w = tid >> 6, lane = tid & 63, r = lane & 15, gq = lane >> 4;
+    if (w < 3) {
+        const int bi = w == 0 ? 0 : 1, bj = w == 1 ? 1 : 0;
+        const bool diag = bi == bj;
+        bool wide_lane = false;
+        if (diag)
+            for (int d = lane; d < DK; d += 64) wide_lane |= sG[16 * bi][d] - sG[16 * bi + 15][d] > kBwdWideLog2;
+        floatx4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = akk;
+        if (__ballot(wide_lane) == 0) {
+            const int i = 16 * bi + r, j = 16 * bj + r;  // this lane's A row and B column
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) {
+                Frag<float> fk, fq, fb;
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const int d = 32 * ks + slot_index(gq, jj);
+                    const bool in = d < DK;
+                    const int dc = in ? d : 0;
+                    const float rho = diag ? 0.5f * (sG[16 * bi][dc] + sG[16 * bi + 15][dc]) : sG[15][dc];
+                    const float up = exp2_fast(sG[i][dc] - rho), dn = exp2_fast(rho - sG[j][dc]);
+                    fk.v[jj] = in ? sK[i][dc] * up : 0.f;
+                    fq.v[jj] = in ? sQ[i][dc] * up : 0.f;
+                    fb.v[jj] = in ? sK[j][dc] * dn : 0.f;
+                }
+                akk = mma(fk, fb, akk);
+                aqk = mma(fq, fb, aqk);
+            }
+        } else {  // lane (r, gq) owns the block's entries (4 gq + ii, r)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int i = 16 * bi + 4 * gq + ii, j = 16 * bj + r;
+                if (j > i) continue;
+                for (int d = 0; d < DK; ++d) {
+                    const float x = sK[j][d] * exp2_fast(sG[i][d] - sG[j][d]);
+                    akk[ii] = fmaf(sK[i][d], x, akk[ii]);
+                    aqk[ii] = fmaf(sQ[i][d], x, aqk[ii]);
+                }
+            }
+        }
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {  // C layout: row 16 bi + 4 gq + ii, column 16 bj + r
+            const int i = 16 * bi + 4 * gq + ii, j = 16 * bj + r;
+            const float vkk = j < i ? akk[ii] : 0.f, vqk = j <= i ? aqk[ii] : 0.f;
+            sAt[i][j] = vkk;
+            opf[O::At / 4 + i * C + j] = vkk;
+            sSt[tile_pos(j, i, C)] = vqk;
+        }
+    } else {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int i = 4 * gq + ii, j = 16 + r;
             sAt[i][j] = 0.f;
             opf[O::At / 4 + i * C + j] = 0.f;
             sSt[tile_pos(j, i, C)] = 0.f;
         }
     }
-    // pairs j <= i enumerated densely (no idle lanes): pair p has row i with
-    // i (i + 1) / 2 <= p < (i + 1) (i + 2) / 2
-    for (int p = tid; p < C * (C + 1) / 2; p += 256) {
-        int i = (int)((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
-        if ((i + 1) * (i + 2) / 2 <= p) ++i;
-        if (i * (i + 1) / 2 > p) --i;
-        const int j = p - i * (i + 1) / 2;
-        float akk = 0.f, aqk = 0.f;
-        for (int d = 0; d < DK; ++d) {
-            const float x = sK[j][d] * exp2_fast(sG[i][d] - sG[j][d]);
-            akk = fmaf(sK[i][d], x, akk);
-            aqk = fmaf(sQ[i][d], x, aqk);
-        }
-        if (j == i) akk = 0.f;
-        sAt[i][j] = akk;
-        opf[O::At / 4 + i * C + j] = akk;
-        sSt[tile_pos(j, i, C)] = aqk;
-    }
     flush(O::AqkT, C * C);
-    // T = (I + Diag(beta) At)^-1: unit lower triangular, column j by lane j;
-    // T into sSt[0, C^2), T^T into sSt[C^2, 2 C^2)
-    if (tid < C) {
-        const int j = tid;
-        float col[C];
+    // T = (I + L)^-1 with L = Diag(beta) At (unit lower triangular) by 16 x 16
+    // blocks: the diagonal blocks by forward substitution (lane 16 blk + c:
+    // column c of block blk), then T21 = -T22 (L21 T11) on the matrix cores.
+    if (w == 0) {
+        if (lane < 32) {
+            const int blk = lane >> 4, c = lane & 15, o = 16 * blk;
+            float col[16];
 #pragma unroll
-        for (int i = 0; i < C; ++i) {
-            float s = (i == j) ? 1.f : 0.f;
+            for (int i = 0; i < 16; ++i) {
+                float sacc = (i == c) ? 1.f : 0.f;
+                const float nb = -sB[o + i];
 #pragma unroll
-            for (int m = 0; m < i; ++m) s = fmaf(-sB[i] * sAt[i][m], col[m], s);
-            col[i] = s;
+                for (int m = 0; m < i; ++m) sacc = fmaf(nb * sAt[o + i][o + m], col[m], sacc);
+                col[i] = sacc;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                sTT[o + i][o + c] = col[i];
+                sTT[i][16 + c] = 0.f;  // the zero block above the diagonal
+            }
         }
+        // R layout of L21 (lane: row r, columns 4 gq + i), C layout of T11 and
+        // of the product (lane: rows 4 gq + i, column r)
+        floatx4 l21, t11, t22;
 #pragma unroll
-        for (int i = 0; i < C; ++i) {
-            sSt[tile_pos(i, j, C)] = col[i];
-            sSt[C * C + tile_pos(j, i, C)] = col[i];
+        for (int i = 0; i < 4; ++i) {
+            l21[i] = sB[16 + r] * sAt[16 + r][4 * gq + i];
+            t11[i] = sTT[4 * gq + i][r];
+            t22[i] = sTT[16 + r][16 + 4 * gq + i];
         }
+        const floatx4 pm = mm16(l21, t11);  // L21 T11
+        const floatx4 t21 = mm16(t22, pm);  // T22 (L21 T11)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sTT[16 + 4 * gq + i][r] = -t21[i];
     }
-    __syncthreads();
+    lds_barrier();
+    // T into sSt[0, C^2) and T^T into sSt[C^2, 2 C^2), as tiles
+    for (int e = tid; e < C * C; e += 256) {
+        const int i = e / C, j = e % C;
+        const float x = sTT[i][j];
+        sSt[tile_pos(i, j, C)] = x;
+        sSt[C * C + tile_pos(j, i, C)] = x;
+    }
+    lds_barrier();
     for (int e = 8 * tid; e < C * C; e += 8 * 256) {
         store_row8(reinterpret_cast<T*>(op + O::Tm) + e, sSt + e);
         store_row8(reinterpret_cast<T*>(op + O::TT) + e, sSt + C * C + e);
@@ -431,11 +529,11 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_states_kernel(const Bw
     if (w == NSW) {
         stage_kib(blk, sOp[0], kPieces, 0, 1);
         wait_vmcnt<0>();
-        __syncthreads();
+        lds_barrier();
         for (int n = 0; n < a.NC; ++n) {
             if (n + 1 < a.NC) stage_kib(blk + (size_t)(n + 1) * O::bytes, sOp[(n + 1) & 1], kPieces, 0, 1);
             wait_vmcnt<0>();
-            __syncthreads();
+            lds_barrier();
         }
         return;
     }
@@ -465,7 +563,7 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_states_kernel(const Bw
     float vcur[8], vnext[8];
     load_v(0, vcur);
     if (a.NC > 0) store_state(0);
-    __syncthreads();
+    lds_barrier();
     for (int n = 0; n < a.NC; ++n) {
         const int buf = n & 1;
         if (n + 1 < a.NC) load_v(n + 1, vnext);  // the next chunk's values travel during this one
@@ -504,7 +602,7 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_states_kernel(const Bw
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) vcur[u] = vnext[u];
-        __syncthreads();   // the next chunk's operators are in LDS, this chunk's no longer read
+        lds_barrier();   // the next chunk's operators are in LDS, this chunk's no longer read
         if (n + 1 < a.NC) store_state(n + 1);
     }
 }
@@ -527,11 +625,11 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_adjoint_kernel(const B
     if (w == NSW) {  // the copy wave, one chunk ahead (chunks in reverse order)
         if (a.NC > 0) stage_kib(blk + (size_t)(a.NC - 1) * O::bytes, sOp[0], kPieces, 0, 1);
         wait_vmcnt<0>();
-        __syncthreads();
+        lds_barrier();
         for (int n = a.NC - 1, it = 0; n >= 0; --n, ++it) {
             if (n > 0) stage_kib(blk + (size_t)(n - 1) * O::bytes, sOp[(it + 1) & 1], kPieces, 0, 1);
             wait_vmcnt<0>();
-            __syncthreads();
+            lds_barrier();
         }
         return;
     }
@@ -563,7 +661,7 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_adjoint_kernel(const B
         load_do(a.NC - 1, dOf);
         store_adj(a.NC - 1);
     }
-    __syncthreads();
+    lds_barrier();
     for (int n = a.NC - 1, it = 0; n >= 0; --n, ++it) {
         const int buf = it & 1;
         if (n > 0) load_do(n - 1, dOnext);  // the previous chunk's dO travels during this one
@@ -602,7 +700,7 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_adjoint_kernel(const B
             dS[R] = mma(frag_tile(O::tiles(op, O::KdT - A0), R, 0, 1), Xf, acc);
         }
         dOf = dOnext;
-        __syncthreads();
+        lds_barrier();
         if (n > 0) store_adj(n - 1);
     }
     if (a.dS0) {
@@ -657,7 +755,7 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
     __shared__ __align__(16) float sBig[3 * C * PV];
     __shared__ float sdAqk[C][C + 1], sdAt[C][C + 1];
     __shared__ float sRed[NT / 64];
-    __shared__ float sPart[NT];
+    __shared__ float sPart[NT], sNrm[prep_norm_floats<DK, NT>()];
     float* sdO = sBig;              // [C][PV]
     float* sU = sBig + C * PV;      // [C][PV]
     float* sW = sBig + 2 * C * PV;  // [C][PV]
@@ -703,7 +801,7 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) vr[tb][i] = ldraw<T>(a.v, in_row(16 * tb + 4 * gq + i) * DV + col);
     }
-    prep_finish<T, DK, DK, NT>(a, h, t0, pin, sQ, sK, sG, sB, sRq, sRk, sPart);
+    prep_finish<T, DK, DK, NT>(a, h, t0, pin, sQ, sK, sG, sB, sRq, sRk, sPart, sNrm);
 #pragma unroll
     for (int u = 0; u < NDO; ++u) {
         const int e = tid + u * NT, t = e / DV, j = e % DV;
@@ -765,7 +863,7 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- products over the value dimension
     {   // dA_kk = -W U^T (strictly lower) and dAqk = dO U^T (lower): eight 16x16 tiles
@@ -815,7 +913,7 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) dKd[tb][i] *= -sB[16 * tb + 4 * gq + i];
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- decay-weighted sums: lane (r, gq) of wave w owns channel 16 w + r
     // at tokens 16 tb + 4 gq + i, here and for the outputs
@@ -1001,7 +1099,7 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
                 }
             }
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < C) {  // the per-token dot products over all channels; dbeta
         const int t = tid;
         float pq = 0.f, pk = 0.f;
@@ -1018,7 +1116,7 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
             stf<T>(a.dbeta_raw, row_of(t), db);
         }
     }
-    __syncthreads();
+    lds_barrier();
     // dq, dk through the L2 norm: dx = r (dx_hat - x_hat (x_hat . dx_hat))
     if (w < NBK) {
         const int d = 16 * w + r;
@@ -1045,7 +1143,7 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) dApart += __shfl_xor(dApart, off, 64);
     if (lane == 0) sRed[w] = dApart;
-    __syncthreads();
+    lds_barrier();
     if (tid == 0) {
         float s = 0.f;
         for (int ww = 0; ww < NT / 64; ++ww) s += sRed[ww];
