@@ -191,7 +191,7 @@ __device__ __forceinline__ Frag<E> frag_strip(const floatx4 (&X)[NB], int s) {
 __device__ __forceinline__ float gate_of(float zv, float eA, float g_min, unsigned flags) {
     if (!(flags & kGateIn)) return zv;
     if (flags & kGateSoftplus) return -eA * (fmaxf(zv, 0.f) + log1pf(expf(-fabsf(zv))));
-    return g_min / (1.f + expf(-eA * zv));
+    return g_min * sigmoidf_(eA * zv);
 }
 
 // The raw inputs of one chunk for one thread: channel d = tid % DK at the NPT
@@ -295,7 +295,7 @@ __device__ void prep_finish(const BwdArgs& a, int h, int t0, const PrepIn<DK, NT
         }
     }
     if (tid < C) {
-        const float bt = (a.flags & kBetaSig) ? 1.f / (1.f + expf(-in.br)) : in.br;
+        const float bt = (a.flags & kBetaSig) ? sigmoidf_(in.br) : in.br;
         sB[tid] = (t0 + tid < a.T) ? bt : 0.f;
     }
     lds_barrier();
@@ -307,8 +307,8 @@ __device__ void prep_finish(const BwdArgs& a, int h, int t0, const PrepIn<DK, NT
             nq[u] += sNrm[(wave ^ 1) * NPT + u];
             nk[u] += sNrm[(NW + (wave ^ 1)) * NPT + u];
         }
-        const float rq = l2 ? 1.f / sqrtf(nq[u] + kL2Eps) : 1.f;
-        const float rk = l2 ? 1.f / sqrtf(nk[u] + kL2Eps) : 1.f;
+        const float rq = l2 ? __builtin_amdgcn_rsqf(nq[u] + kL2Eps) : 1.f;  // hardware 1/sqrt (about 1 ulp)
+        const float rk = l2 ? __builtin_amdgcn_rsqf(nk[u] + kL2Eps) : 1.f;
         sQ[tg + u][d] = q[u] * rq;
         sK[tg + u][d] = k[u] * rk;
         sG[tg + u][d] = g[u] + off;
@@ -728,12 +728,8 @@ __device__ __forceinline__ Frag<E> frag_cols(const float* M, int ld, int k0, int
     return f;
 }
 
-// Sum over the 16 lanes that share lane / 16.
-__device__ __forceinline__ float row_sum16(float x) {
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, 16);
-    return x;
-}
+// Sum over the 16 lanes that share lane / 16 (DPP row moves).
+__device__ __forceinline__ float row_sum16(float x) { return group_sum<16>(x); }
 
 // One workgroup (eight waves) per chunk-head.  Wave w owns value columns
 // 16 w .. 16 w + 15 for the products over tokens (E, dU, U, W stay in C
@@ -1069,11 +1065,11 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
                 if (a.flags & kGateIn) {
                     const float zv = zl[tb][i];
                     if (a.flags & kGateSoftplus) {
-                        const float sg = 1.f / (1.f + expf(-zv));
+                        const float sg = sigmoidf_(zv);
                         dz = acc * (-eA * sg);
                         dA = acc * gate_of(zv, eA, a.g_min, a.flags);
                     } else {
-                        const float sg = 1.f / (1.f + expf(-eA * zv));
+                        const float sg = sigmoidf_(eA * zv);
                         const float dx = acc * a.g_min * sg * (1.f - sg);  // d / d(e^A z)
                         dz = dx * eA;
                         dA = dx * eA * zv;
