@@ -39,6 +39,8 @@
 // Workgroups share data through LDS only, so their barriers wait for LDS
 // operations alone (lds_barrier): global stores drain, and global loads issued
 // ahead stay in flight, across them.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_bwd.h"
 
@@ -506,6 +508,73 @@ __device__ __forceinline__ void stage_kib(const unsigned char* src, float* dst, 
                                          (__attribute__((address_space(3))) void*)(dst + p * 256), 16, 0, 0);
 }
 
+// A serial pass's workgroup writes its NSW 16-column strips of a [DK x ld]
+// row-major fp32 matrix through an LDS tile (pitch SW + 4, SW = 16 NSW): each
+// compute wave puts its strip (C layout: lane (r, gq) holds rows 16 R + 4 gq + i
+// at column 16 w + r), and after the next workgroup barrier each wave stores
+// DK / NSW rows as whole SW * 4-byte pieces, 16 bytes a lane.  Row pieces of
+// a full 128-byte line store fast; scattered four-byte or 64-byte pieces make
+// the pass wait on its stores.
+template <int NBD, int NSW>
+__device__ __forceinline__ void put_strip(float* tile, int w, const floatx4 (&X)[NBD]) {
+    constexpr int kP = 16 * NSW + 4;
+    const int lane = threadIdx.x & 63, r = lane & 15, gq = lane >> 4;
+#pragma unroll
+    for (int R = 0; R < NBD; ++R)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tile[(16 * R + 4 * gq + i) * kP + 16 * w + r] = X[R][i];
+}
+template <int NBD, int NSW>
+__device__ __forceinline__ void flush_rows(float* dst, size_t ld, int c0, int w, const float* tile) {
+    constexpr int SW = 16 * NSW, kP = SW + 4, LPR = SW / 4, RPI = 64 / LPR;
+    constexpr int ROWS = 16 * NBD / NSW;  // rows per wave
+    static_assert(ROWS % RPI == 0, "whole instructions");
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int p = 0; p < ROWS / RPI; ++p) {
+        const int row = w * ROWS + p * RPI + lane / LPR, c = 4 * (lane % LPR);
+        const float4 v = *reinterpret_cast<const float4*>(tile + row * kP + c);
+        *reinterpret_cast<float4*>(dst + (size_t)row * ld + c0 + c) = v;
+    }
+}
+
+// LDS ring of the serial passes: slots of one chunk's operator region each;
+// the copy wave keeps up to kSlots - 1 chunks ahead.  bf16 regions are small
+// enough for three slots; fp32 regions take two.
+template <typename T> constexpr int bwd_ring_slots() { return sizeof(T) == 2 ? 3 : 2; }
+
+// Wait until at most m chunks of P pieces each are in flight (m <= MAXM);
+// loads complete in issue order.
+template <int P, int MAXM>
+__device__ __forceinline__ void wait_chunks(int m) {
+    static_assert(MAXM * P < 64, "vmcnt range");
+    if constexpr (MAXM >= 2) {
+        if (m >= 2) { wait_vmcnt<2 * P>(); return; }
+    }
+    if constexpr (MAXM >= 1) {
+        if (m >= 1) { wait_vmcnt<P>(); return; }
+    }
+    wait_vmcnt<0>();
+}
+
+// The copy wave of a serial pass: ring slot i % K receives the operators of
+// chunk chunk_of(i) for i = 0 .. NC - 1; one barrier before the first chunk
+// and one after each (the compute waves' barriers).
+template <int K, int P, typename F>
+__device__ __forceinline__ void ring_copy(int NC, float (*ring)[P * 256], F src_of) {
+    const int pre = NC < K - 1 ? NC : K - 1;
+    for (int i = 0; i < pre; ++i) stage_kib(src_of(i), ring[i % K], P, 0, 1);
+    wait_chunks<P, K - 2>(pre - 1);  // chunk 0 has landed
+    lds_barrier();
+    for (int i = 0; i < NC; ++i) {
+        // the slot of chunk i - 1 is free: every compute wave passed the barrier after it
+        if (i + K - 1 < NC) stage_kib(src_of(i + K - 1), ring[(i + K - 1) % K], P, 0, 1);
+        const int later = (NC - 1) - (i + 1);  // chunks issued after chunk i + 1, at most K - 2
+        wait_chunks<P, K - 2>(later < 0 ? 0 : (later > K - 2 ? K - 2 : later));
+        lds_barrier();
+    }
+}
+
 // --------------------------------------------------------------- 2. states
 
 // One workgroup per (b, h) and group of NSW value strips; wave w holds the
@@ -517,24 +586,19 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_states_kernel(const Bw
     using O = Ops<T, DK>;
     constexpr int NBD = DK / 16, KSD = (DK + 31) / 32;
     constexpr int kPieces = (int)(O::sizeS / 1024);
-    __shared__ __align__(16) float sOp[2][O::sizeS / 4];
+    constexpr int K = bwd_ring_slots<T>();
+    __shared__ __align__(16) float sOp[K][O::sizeS / 4];
+    __shared__ __align__(16) float sTr[2][DK * (16 * NSW + 4)];  // the chunk-start state on its way out
     const int ngrp = (a.Dv / 16) / NSW;
     const int bh = blockIdx.x / ngrp, grp = blockIdx.x % ngrp;
     const int b = bh / a.H, h = bh % a.H;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, gq = lane >> 4;
     const int col = 16 * (grp * NSW + w) + r;
     const unsigned char* blk = a.ops + (size_t)bh * a.NC * O::bytes;
-    // wave NSW only copies operators into LDS (one chunk ahead); the compute
-    // waves never have a copy outstanding, so their LDS reads wait for nothing
+    // wave NSW only copies operators into LDS (up to K - 1 chunks ahead); the
+    // compute waves never have a copy outstanding, so their LDS reads wait for nothing
     if (w == NSW) {
-        stage_kib(blk, sOp[0], kPieces, 0, 1);
-        wait_vmcnt<0>();
-        lds_barrier();
-        for (int n = 0; n < a.NC; ++n) {
-            if (n + 1 < a.NC) stage_kib(blk + (size_t)(n + 1) * O::bytes, sOp[(n + 1) & 1], kPieces, 0, 1);
-            wait_vmcnt<0>();
-            lds_barrier();
-        }
+        ring_copy<K, kPieces>(a.NC, sOp, [&](int i) { return blk + (size_t)i * O::bytes; });
         return;
     }
     floatx4 S[NBD];
@@ -543,31 +607,29 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_states_kernel(const Bw
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             S[R][i] = a.S0 ? a.S0[((size_t)bh * DK + 16 * R + 4 * gq + i) * a.Dv + col] : 0.f;
-    // this lane's values of one chunk: tokens 16 tb + 4 gq + i, column col
-    auto load_v = [&](int n, float (&vv)[8]) {
+    // this lane's values of one chunk (tokens 16 tb + 4 gq + i, column col), raw
+    // until used: the wait for them falls in the chunk that uses them
+    auto load_v = [&](int n, uint32_t (&vr)[8]) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int tok = n * C + 16 * (u >> 2) + 4 * gq + (u & 3);
-            const float x = ldf<T>(a.v, (((size_t)b * a.T + min(tok, a.T - 1)) * a.H + h) * a.Dv + col);
-            vv[u] = tok < a.T ? x : 0.f;
+            vr[u] = ldraw<T>(a.v, (((size_t)b * a.T + min(tok, a.T - 1)) * a.H + h) * a.Dv + col);
         }
     };
     // the state at the start of chunk n (its stores are waited for a chunk later)
-    auto store_state = [&](int n) {
-        float* Sn = a.states + ((size_t)bh * a.NC + n) * DK * a.Dv;
-#pragma unroll
-        for (int R = 0; R < NBD; ++R)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Sn[(size_t)(16 * R + 4 * gq + i) * a.Dv + col] = S[R][i];
+    const int c0 = 16 * grp * NSW;  // the workgroup's first value column
+    auto flush_state = [&](int n) {
+        flush_rows<NBD, NSW>(a.states + ((size_t)bh * a.NC + n) * DK * a.Dv, a.Dv, c0, w, sTr[n & 1]);
     };
-    float vcur[8], vnext[8];
-    load_v(0, vcur);
-    if (a.NC > 0) store_state(0);
-    lds_barrier();
-    for (int n = 0; n < a.NC; ++n) {
-        const int buf = n & 1;
-        if (n + 1 < a.NC) load_v(n + 1, vnext);  // the next chunk's values travel during this one
-        const unsigned char* op = reinterpret_cast<const unsigned char*>(sOp[buf]);
+    // one chunk: its values in vc, the next chunk's requested into vn (two
+    // alternating buffers, so no register copy waits for a load in flight).
+    // Only the last chunk (LAST) skips the request and the store, so every
+    // other chunk's wait for its values counts the loads and stores issued
+    // since exactly, and never waits for a store.
+    auto chunk = [&](int n, uint32_t (&vc)[8], uint32_t (&vn)[8], auto last) {
+        constexpr bool LAST = decltype(last)::value;
+        if constexpr (!LAST) load_v(n + 1, vn);
+        const unsigned char* op = reinterpret_cast<const unsigned char*>(sOp[n % K]);
         const float* betaS = O::f32(op, O::betaS);
         const float* gamS = O::f32(op, O::gamS);
         // E = V - Kd S, scaled by beta per token
@@ -580,7 +642,9 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_states_kernel(const Bw
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * tb + 4 * gq + i;
-                Eb[tb][i] = betaS[t] * (vcur[4 * tb + i] - acc[i]);
+                settle(vc[4 * tb + i]);
+                const float vv = n * C + t < a.T ? raw_value<T>(vc[4 * tb + i]) : 0.f;
+                Eb[tb][i] = betaS[t] * (vv - acc[i]);
             }
         }
         // U = T (beta E)
@@ -600,10 +664,27 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_states_kernel(const Bw
             for (int i = 0; i < 4; ++i) acc[i] = gamS[16 * R + 4 * gq + i] * S[R][i];
             S[R] = mma(frag_tile(O::tiles(op, O::KpT), R, 0, 1), Uf, acc);
         }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) vcur[u] = vnext[u];
+        if constexpr (!LAST) put_strip<NBD, NSW>(sTr[(n + 1) & 1], w, S);
         lds_barrier();   // the next chunk's operators are in LDS, this chunk's no longer read
-        if (n + 1 < a.NC) store_state(n + 1);
+        if constexpr (!LAST) flush_state(n + 1);
+    };
+    const std::integral_constant<bool, false> more;
+    const std::integral_constant<bool, true> last;
+    uint32_t va[8], vb[8];
+    load_v(0, va);
+    if (a.NC > 0) put_strip<NBD, NSW>(sTr[0], w, S);
+    lds_barrier();
+    if (a.NC > 0) flush_state(0);
+    int n = 0;
+    for (; n + 2 < a.NC; n += 2) {
+        chunk(n, va, vb, more);
+        chunk(n + 1, vb, va, more);
+    }
+    if (a.NC - n == 2) {
+        chunk(n, va, vb, more);
+        chunk(n + 1, vb, va, last);
+    } else if (a.NC - n == 1) {
+        chunk(n, va, vb, last);
     }
 }
 
@@ -615,22 +696,17 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_adjoint_kernel(const B
     constexpr int NBD = DK / 16, KSD = (DK + 31) / 32;
     constexpr int kPieces = (int)(O::sizeA / 1024);
     constexpr size_t A0 = O::A0;
-    __shared__ __align__(16) float sOp[2][O::sizeA / 4];
+    constexpr int K = bwd_ring_slots<T>();
+    __shared__ __align__(16) float sOp[K][O::sizeA / 4];
+    __shared__ __align__(16) float sTr[2][DK * (16 * NSW + 4)];  // the chunk-end adjoint on its way out
     const int ngrp = (a.Dv / 16) / NSW;
     const int bh = blockIdx.x / ngrp, grp = blockIdx.x % ngrp;
     const int b = bh / a.H, h = bh % a.H;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, gq = lane >> 4;
     const int col = 16 * (grp * NSW + w) + r;
     const unsigned char* blk = a.ops + (size_t)bh * a.NC * O::bytes + A0;
-    if (w == NSW) {  // the copy wave, one chunk ahead (chunks in reverse order)
-        if (a.NC > 0) stage_kib(blk + (size_t)(a.NC - 1) * O::bytes, sOp[0], kPieces, 0, 1);
-        wait_vmcnt<0>();
-        lds_barrier();
-        for (int n = a.NC - 1, it = 0; n >= 0; --n, ++it) {
-            if (n > 0) stage_kib(blk + (size_t)(n - 1) * O::bytes, sOp[(it + 1) & 1], kPieces, 0, 1);
-            wait_vmcnt<0>();
-            lds_barrier();
-        }
+    if (w == NSW) {  // the copy wave (chunks in reverse order)
+        ring_copy<K, kPieces>(a.NC, sOp, [&](int i) { return blk + (size_t)(a.NC - 1 - i) * O::bytes; });
         return;
     }
     floatx4 dS[NBD];
@@ -639,33 +715,34 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_adjoint_kernel(const B
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             dS[R][i] = a.dS_T ? a.dS_T[((size_t)bh * DK + 16 * R + 4 * gq + i) * a.Dv + col] : 0.f;
-    // dO of one chunk as the B operand of a product over its tokens
-    auto load_do = [&](int n, Frag<T>& f) {
+    // dO of one chunk (this lane's tokens slot_index(gq, j), column col), raw
+    // until used as the B operand of a product over its tokens
+    auto load_do = [&](int n, uint32_t (&dr)[8]) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int tok = n * C + slot_index(gq, j);
-            const float x = ldf<T>(a.dout, (((size_t)b * a.T + min(tok, a.T - 1)) * a.H + h) * a.Dv + col);
-            f.set(j, tok < a.T ? x : 0.f);
+            dr[j] = ldraw<T>(a.dout, (((size_t)b * a.T + min(tok, a.T - 1)) * a.H + h) * a.Dv + col);
         }
     };
     // the adjoint at the end of chunk n (its stores are waited for a chunk later)
-    auto store_adj = [&](int n) {
-        float* An = a.adj + ((size_t)bh * a.NC + n) * DK * a.Dv;
-#pragma unroll
-        for (int R = 0; R < NBD; ++R)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) An[(size_t)(16 * R + 4 * gq + i) * a.Dv + col] = dS[R][i];
+    const int c0 = 16 * grp * NSW;  // the workgroup's first value column
+    auto flush_adj = [&](int n, int slot) {
+        flush_rows<NBD, NSW>(a.adj + ((size_t)bh * a.NC + n) * DK * a.Dv, a.Dv, c0, w, sTr[slot]);
     };
-    Frag<T> dOf, dOnext;
-    if (a.NC > 0) {
-        load_do(a.NC - 1, dOf);
-        store_adj(a.NC - 1);
-    }
-    lds_barrier();
-    for (int n = a.NC - 1, it = 0; n >= 0; --n, ++it) {
-        const int buf = it & 1;
-        if (n > 0) load_do(n - 1, dOnext);  // the previous chunk's dO travels during this one
-        const unsigned char* op = reinterpret_cast<const unsigned char*>(sOp[buf]);  // region A: offsets - A0
+    // one chunk (it-th from the end): its dO in dc, the previous chunk's
+    // requested into dn (two alternating buffers: no register copy waits for a
+    // load in flight)
+    // (LAST: the first chunk, which requests and stores nothing more; see the state pass)
+    auto chunk = [&](int n, int it, uint32_t (&dc)[8], uint32_t (&dn)[8], auto last) {
+        constexpr bool LAST = decltype(last)::value;
+        if constexpr (!LAST) load_do(n - 1, dn);
+        Frag<T> dOf;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            settle(dc[j]);
+            dOf.set(j, n * C + slot_index(gq, j) < a.T ? raw_value<T>(dc[j]) : 0.f);
+        }
+        const unsigned char* op = reinterpret_cast<const unsigned char*>(sOp[it % K]);  // region A: offsets - A0
         const float* betaA = O::f32(op, O::betaA - A0);
         const float* gamA = O::f32(op, O::gamA - A0);
         // dU = Aqk^T dO + Kp dS'
@@ -699,9 +776,29 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_adjoint_kernel(const B
             acc = mma(frag_tile(O::tiles(op, O::QpT - A0), R, 0, 1), dOf, acc);
             dS[R] = mma(frag_tile(O::tiles(op, O::KdT - A0), R, 0, 1), Xf, acc);
         }
-        dOf = dOnext;
+        if constexpr (!LAST) put_strip<NBD, NSW>(sTr[(it + 1) & 1], w, dS);
         lds_barrier();
-        if (n > 0) store_adj(n - 1);
+        if constexpr (!LAST) flush_adj(n - 1, (it + 1) & 1);
+    };
+    const std::integral_constant<bool, false> more;
+    const std::integral_constant<bool, true> last;
+    uint32_t da[8], db[8];
+    if (a.NC > 0) {
+        load_do(a.NC - 1, da);
+        put_strip<NBD, NSW>(sTr[0], w, dS);
+    }
+    lds_barrier();
+    if (a.NC > 0) flush_adj(a.NC - 1, 0);
+    int it = 0;
+    for (; it + 2 < a.NC; it += 2) {
+        chunk(a.NC - 1 - it, it, da, db, more);
+        chunk(a.NC - 2 - it, it + 1, db, da, more);
+    }
+    if (a.NC - it == 2) {
+        chunk(1, it, da, db, more);
+        chunk(0, it + 1, db, da, last);
+    } else if (a.NC - it == 1) {
+        chunk(0, it, da, db, last);
     }
     if (a.dS0) {
 #pragma unroll
