@@ -267,7 +267,7 @@ kda_status kda_segment_compose(int n_seg, const float* M, const float* S_tilde,
 // per-chunk dA_log parts and, for grouped heads, the per-value-head q/k
 // gradients and the per-chunk gate-bias parts; each region 256-byte aligned.
 struct BwdWorkspace {
-    size_t ops, states, adj, dA, dqk, dbias, total;
+    size_t ops, states, adj, eu, w, dA, dqk, dbias, total;
 };
 static BwdWorkspace bwd_workspace(int B, int T, int HV, int Dk, int Dv, bool grouped, bool bias) {
     BwdWorkspace w{};
@@ -276,7 +276,9 @@ static BwdWorkspace bwd_workspace(int B, int T, int HV, int Dk, int Dv, bool gro
     w.ops = 0;
     w.states = kda::round_up(BHN * kda::bwd_op_bytes(4, Dk), 256);  // fp32 operands: the larger block
     w.adj = w.states + kda::round_up(BHN * Dk * Dv * 4, 256);
-    w.dA = w.adj + kda::round_up(BHN * Dk * Dv * 4, 256);
+    w.eu = w.adj + kda::round_up(BHN * Dk * Dv * 4, 256);
+    w.w = w.eu + kda::round_up(BHN * 2 * kda::kBwdChunk * Dv * 4, 256);
+    w.dA = w.w + kda::round_up(BHN * kda::kBwdChunk * Dv * 4, 256);
     w.dqk = w.dA + kda::round_up(BHN * 4, 256);
     w.dbias = w.dqk + (grouped ? kda::round_up(2 * (size_t)B * T * HV * Dk * 4, 256) : 0);
     w.total = w.dbias + (bias ? kda::round_up(BHN * Dk * 4, 256) : 0);
@@ -332,6 +334,11 @@ static kda_status chunk_bwd_impl(const void* q, const void* k, const void* v, co
     a.ops = ws + w.ops;
     a.states = reinterpret_cast<float*>(ws + w.states);
     a.adj = reinterpret_cast<float*>(ws + w.adj);
+    a.eu = reinterpret_cast<float*>(ws + w.eu);
+    a.w = reinterpret_cast<float*>(ws + w.w);
+    // without the gate A_log may be NULL: the kernels still read a value (and
+    // drop it) from a valid address, the workspace's
+    if (!A_log) a.A_log = reinterpret_cast<const float*>(ws);
     a.dA_part = reinterpret_cast<float*>(ws + w.dA);
     a.B = B; a.T = T; a.H = HV; a.Dv = Dv; a.NC = (T + kda::kBwdChunk - 1) / kda::kBwdChunk;
     a.g_min = g_min; a.flags = flags;

@@ -15,6 +15,11 @@ struct BwdArgs {
     const float* A_log; const float* S0; const void* dout; const float* dS_T;
     void* dq; void* dk; void* dv; void* dz; void* dbeta_raw; float* dA_log; float* dS0;
     unsigned char* ops; float* states; float* adj; float* dA_part;  // workspace regions
+    // per chunk-head, from the serial passes to the gradient kernel: E = V - Kd S and
+    // U (eu, two [C x Dv] matrices), W = T^T dU (w, one), in fragment order:
+    // element ((strip * 2 + tb) * 64 + lane) * 4 + i is row 16 tb + 4 (lane / 16) + i,
+    // column 16 strip + lane % 16
+    float* eu; float* w;
     int B, T, H, Dv, NC;
     float g_min;
     unsigned flags;

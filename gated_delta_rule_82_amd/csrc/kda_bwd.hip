@@ -557,18 +557,45 @@ __device__ __forceinline__ void wait_chunks(int m) {
     wait_vmcnt<0>();
 }
 
-// The copy wave of a serial pass: ring slot i % K receives the operators of
-// chunk chunk_of(i) for i = 0 .. NC - 1; one barrier before the first chunk
-// and one after each (the compute waves' barriers).
-template <int K, int P, typename F>
-__device__ __forceinline__ void ring_copy(int NC, float (*ring)[P * 256], F src_of) {
+// Value rows of one chunk for a serial pass's workgroup: token rows of its
+// NSW * 16 columns (RB bytes each, from column c0 of the [B, T, H, Dv] tensor
+// x), as whole KiB pieces of 16-byte lane copies into LDS.  Tokens past the
+// end read the last token; the compute waves zero them.
+template <typename T, int NSW>
+struct ValueRows {
+    static constexpr int RB = NSW * 16 * (int)sizeof(T);  // bytes of one token's row
+    static constexpr int LPT = RB / 16;                    // lanes per token
+    static constexpr int TPP = 64 / LPT;                   // tokens per piece
+    static constexpr int PIECES = C / TPP;
+    static_assert(LPT * 16 == RB && TPP * LPT == 64 && PIECES * TPP == C, "whole pieces");
+    static __device__ __forceinline__ void stage(const void* x, const BwdArgs& a, int b, int h, int c0, int n,
+                                                 float* dst) {
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int p = 0; p < PIECES; ++p) {
+            const int tok = min(n * C + p * TPP + lane / LPT, a.T - 1);
+            const unsigned char* src = reinterpret_cast<const unsigned char*>(x) +
+                                       ((((size_t)b * a.T + tok) * a.H + h) * a.Dv + c0) * sizeof(T) + (lane % LPT) * 16;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                             (__attribute__((address_space(3))) void*)(dst + p * 256), 16, 0, 0);
+        }
+    }
+};
+
+// The copy wave of a serial pass: ring slot i % K receives chunk i's P pieces
+// (stage(i, slot) issues them) for i = 0 .. NC - 1; one barrier before the
+// first chunk and one after each (the compute waves' barriers).  The compute
+// waves load nothing from global memory, so none of their waits counts a
+// store.
+template <int K, int P, int SLOT, typename F>
+__device__ __forceinline__ void ring_copy(int NC, float (*ring)[SLOT], F stage) {
     const int pre = NC < K - 1 ? NC : K - 1;
-    for (int i = 0; i < pre; ++i) stage_kib(src_of(i), ring[i % K], P, 0, 1);
+    for (int i = 0; i < pre; ++i) stage(i, ring[i % K]);
     wait_chunks<P, K - 2>(pre - 1);  // chunk 0 has landed
     lds_barrier();
     for (int i = 0; i < NC; ++i) {
         // the slot of chunk i - 1 is free: every compute wave passed the barrier after it
-        if (i + K - 1 < NC) stage_kib(src_of(i + K - 1), ring[(i + K - 1) % K], P, 0, 1);
+        if (i + K - 1 < NC) stage(i + K - 1, ring[(i + K - 1) % K]);
         const int later = (NC - 1) - (i + 1);  // chunks issued after chunk i + 1, at most K - 2
         wait_chunks<P, K - 2>(later < 0 ? 0 : (later > K - 2 ? K - 2 : later));
         lds_barrier();
@@ -579,26 +606,32 @@ __device__ __forceinline__ void ring_copy(int NC, float (*ring)[P * 256], F src_
 
 // One workgroup per (b, h) and group of NSW value strips; wave w holds the
 // fp32 strip of value columns 16 st .. 16 st + 15 of S in C layout (rows
-// 16 R + 4 gq + i, column r).  Each chunk's state-pass operators are copied
-// into LDS one chunk ahead.
+// 16 R + 4 gq + i, column r).  Each chunk's state-pass operators and value
+// rows are copied into an LDS ring ahead of use by a copy wave.
 template <typename T, int DK, int NSW>
 __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_states_kernel(const BwdArgs a) {
     using O = Ops<T, DK>;
+    using VR = ValueRows<T, NSW>;
     constexpr int NBD = DK / 16, KSD = (DK + 31) / 32;
     constexpr int kPieces = (int)(O::sizeS / 1024);
+    constexpr int P = kPieces + VR::PIECES;  // KiB per ring slot: operators, then value rows
     constexpr int K = bwd_ring_slots<T>();
-    __shared__ __align__(16) float sOp[K][O::sizeS / 4];
+    __shared__ __align__(16) float sOp[K][P * 256];
     __shared__ __align__(16) float sTr[2][DK * (16 * NSW + 4)];  // the chunk-start state on its way out
     const int ngrp = (a.Dv / 16) / NSW;
     const int bh = blockIdx.x / ngrp, grp = blockIdx.x % ngrp;
     const int b = bh / a.H, h = bh % a.H;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, gq = lane >> 4;
-    const int col = 16 * (grp * NSW + w) + r;
+    const int c0 = 16 * grp * NSW;  // the workgroup's first value column
+    const int col = c0 + 16 * w + r;
     const unsigned char* blk = a.ops + (size_t)bh * a.NC * O::bytes;
-    // wave NSW only copies operators into LDS (up to K - 1 chunks ahead); the
-    // compute waves never have a copy outstanding, so their LDS reads wait for nothing
+    // wave NSW only copies each chunk's operators and value rows into LDS (up to
+    // K - 1 chunks ahead); the compute waves never load from global memory
     if (w == NSW) {
-        ring_copy<K, kPieces>(a.NC, sOp, [&](int i) { return blk + (size_t)i * O::bytes; });
+        ring_copy<K, P>(a.NC, sOp, [&](int i, float* slot) {
+            stage_kib(blk + (size_t)i * O::bytes, slot, kPieces, 0, 1);
+            VR::stage(a.v, a, b, h, c0, i, slot + kPieces * 256);
+        });
         return;
     }
     floatx4 S[NBD];
@@ -607,33 +640,21 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_states_kernel(const Bw
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             S[R][i] = a.S0 ? a.S0[((size_t)bh * DK + 16 * R + 4 * gq + i) * a.Dv + col] : 0.f;
-    // this lane's values of one chunk (tokens 16 tb + 4 gq + i, column col), raw
-    // until used: the wait for them falls in the chunk that uses them
-    auto load_v = [&](int n, uint32_t (&vr)[8]) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int tok = n * C + 16 * (u >> 2) + 4 * gq + (u & 3);
-            vr[u] = ldraw<T>(a.v, (((size_t)b * a.T + min(tok, a.T - 1)) * a.H + h) * a.Dv + col);
-        }
-    };
-    // the state at the start of chunk n (its stores are waited for a chunk later)
-    const int c0 = 16 * grp * NSW;  // the workgroup's first value column
+    // the state at the start of chunk n, stored through the LDS tile
     auto flush_state = [&](int n) {
         flush_rows<NBD, NSW>(a.states + ((size_t)bh * a.NC + n) * DK * a.Dv, a.Dv, c0, w, sTr[n & 1]);
     };
-    // one chunk: its values in vc, the next chunk's requested into vn (two
-    // alternating buffers, so no register copy waits for a load in flight).
-    // Only the last chunk (LAST) skips the request and the store, so every
-    // other chunk's wait for its values counts the loads and stores issued
-    // since exactly, and never waits for a store.
-    auto chunk = [&](int n, uint32_t (&vc)[8], uint32_t (&vn)[8], auto last) {
-        constexpr bool LAST = decltype(last)::value;
-        if constexpr (!LAST) load_v(n + 1, vn);
-        const unsigned char* op = reinterpret_cast<const unsigned char*>(sOp[n % K]);
+    if (a.NC > 0) put_strip<NBD, NSW>(sTr[0], w, S);
+    lds_barrier();
+    if (a.NC > 0) flush_state(0);
+    for (int n = 0; n < a.NC; ++n) {
+        const float* slot = sOp[n % K];
+        const unsigned char* op = reinterpret_cast<const unsigned char*>(slot);
+        const T* vrow = reinterpret_cast<const T*>(slot + kPieces * 256);  // [C][16 NSW] value rows
         const float* betaS = O::f32(op, O::betaS);
         const float* gamS = O::f32(op, O::gamS);
         // E = V - Kd S, scaled by beta per token
-        floatx4 Eb[2];
+        floatx4 E[2], Eb[2];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -642,9 +663,9 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_states_kernel(const Bw
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * tb + 4 * gq + i;
-                settle(vc[4 * tb + i]);
-                const float vv = n * C + t < a.T ? raw_value<T>(vc[4 * tb + i]) : 0.f;
-                Eb[tb][i] = betaS[t] * (vv - acc[i]);
+                const float vv = n * C + t < a.T ? to_f<T>(vrow[t * (16 * NSW) + col - c0]) : 0.f;
+                E[tb][i] = vv - acc[i];
+                Eb[tb][i] = betaS[t] * E[tb][i];
             }
         }
         // U = T (beta E)
@@ -664,27 +685,16 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_states_kernel(const Bw
             for (int i = 0; i < 4; ++i) acc[i] = gamS[16 * R + 4 * gq + i] * S[R][i];
             S[R] = mma(frag_tile(O::tiles(op, O::KpT), R, 0, 1), Uf, acc);
         }
-        if constexpr (!LAST) put_strip<NBD, NSW>(sTr[(n + 1) & 1], w, S);
-        lds_barrier();   // the next chunk's operators are in LDS, this chunk's no longer read
-        if constexpr (!LAST) flush_state(n + 1);
-    };
-    const std::integral_constant<bool, false> more;
-    const std::integral_constant<bool, true> last;
-    uint32_t va[8], vb[8];
-    load_v(0, va);
-    if (a.NC > 0) put_strip<NBD, NSW>(sTr[0], w, S);
-    lds_barrier();
-    if (a.NC > 0) flush_state(0);
-    int n = 0;
-    for (; n + 2 < a.NC; n += 2) {
-        chunk(n, va, vb, more);
-        chunk(n + 1, vb, va, more);
-    }
-    if (a.NC - n == 2) {
-        chunk(n, va, vb, more);
-        chunk(n + 1, vb, va, last);
-    } else if (a.NC - n == 1) {
-        chunk(n, va, vb, last);
+        // this chunk's E and U for the gradient kernel, in fragment order
+        float4* eu = reinterpret_cast<float4*>(a.eu + ((size_t)bh * a.NC + n) * 2 * C * a.Dv);
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            eu[((col >> 4) * 2 + tb) * 64 + lane] = make_float4(E[tb][0], E[tb][1], E[tb][2], E[tb][3]);
+            eu[(C * a.Dv) / 4 + ((col >> 4) * 2 + tb) * 64 + lane] = make_float4(U[tb][0], U[tb][1], U[tb][2], U[tb][3]);
+        }
+        if (n + 1 < a.NC) put_strip<NBD, NSW>(sTr[(n + 1) & 1], w, S);
+        lds_barrier();   // the next chunk is in LDS, this chunk's slot no longer read
+        if (n + 1 < a.NC) flush_state(n + 1);
     }
 }
 
@@ -693,20 +703,26 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_states_kernel(const Bw
 template <typename T, int DK, int NSW>
 __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_adjoint_kernel(const BwdArgs a) {
     using O = Ops<T, DK>;
+    using VR = ValueRows<T, NSW>;
     constexpr int NBD = DK / 16, KSD = (DK + 31) / 32;
     constexpr int kPieces = (int)(O::sizeA / 1024);
+    constexpr int P = kPieces + VR::PIECES;  // KiB per ring slot: operators, then dO rows
     constexpr size_t A0 = O::A0;
     constexpr int K = bwd_ring_slots<T>();
-    __shared__ __align__(16) float sOp[K][O::sizeA / 4];
+    __shared__ __align__(16) float sOp[K][P * 256];
     __shared__ __align__(16) float sTr[2][DK * (16 * NSW + 4)];  // the chunk-end adjoint on its way out
     const int ngrp = (a.Dv / 16) / NSW;
     const int bh = blockIdx.x / ngrp, grp = blockIdx.x % ngrp;
     const int b = bh / a.H, h = bh % a.H;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, gq = lane >> 4;
-    const int col = 16 * (grp * NSW + w) + r;
+    const int c0 = 16 * grp * NSW;  // the workgroup's first value column
+    const int col = c0 + 16 * w + r;
     const unsigned char* blk = a.ops + (size_t)bh * a.NC * O::bytes + A0;
-    if (w == NSW) {  // the copy wave (chunks in reverse order)
-        ring_copy<K, kPieces>(a.NC, sOp, [&](int i) { return blk + (size_t)(a.NC - 1 - i) * O::bytes; });
+    if (w == NSW) {  // the copy wave: chunks in reverse order, operators then dO rows
+        ring_copy<K, P>(a.NC, sOp, [&](int i, float* slot) {
+            stage_kib(blk + (size_t)(a.NC - 1 - i) * O::bytes, slot, kPieces, 0, 1);
+            VR::stage(a.dout, a, b, h, c0, a.NC - 1 - i, slot + kPieces * 256);
+        });
         return;
     }
     floatx4 dS[NBD];
@@ -715,36 +731,27 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_adjoint_kernel(const B
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             dS[R][i] = a.dS_T ? a.dS_T[((size_t)bh * DK + 16 * R + 4 * gq + i) * a.Dv + col] : 0.f;
-    // dO of one chunk (this lane's tokens slot_index(gq, j), column col), raw
-    // until used as the B operand of a product over its tokens
-    auto load_do = [&](int n, uint32_t (&dr)[8]) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int tok = n * C + slot_index(gq, j);
-            dr[j] = ldraw<T>(a.dout, (((size_t)b * a.T + min(tok, a.T - 1)) * a.H + h) * a.Dv + col);
-        }
-    };
-    // the adjoint at the end of chunk n (its stores are waited for a chunk later)
-    const int c0 = 16 * grp * NSW;  // the workgroup's first value column
+    // the adjoint at the end of chunk n, stored through the LDS tile
     auto flush_adj = [&](int n, int slot) {
         flush_rows<NBD, NSW>(a.adj + ((size_t)bh * a.NC + n) * DK * a.Dv, a.Dv, c0, w, sTr[slot]);
     };
-    // one chunk (it-th from the end): its dO in dc, the previous chunk's
-    // requested into dn (two alternating buffers: no register copy waits for a
-    // load in flight)
-    // (LAST: the first chunk, which requests and stores nothing more; see the state pass)
-    auto chunk = [&](int n, int it, uint32_t (&dc)[8], uint32_t (&dn)[8], auto last) {
-        constexpr bool LAST = decltype(last)::value;
-        if constexpr (!LAST) load_do(n - 1, dn);
+    if (a.NC > 0) put_strip<NBD, NSW>(sTr[0], w, dS);
+    lds_barrier();
+    if (a.NC > 0) flush_adj(a.NC - 1, 0);
+    for (int it = 0; it < a.NC; ++it) {
+        const int n = a.NC - 1 - it;
+        const float* slot = sOp[it % K];
+        const unsigned char* op = reinterpret_cast<const unsigned char*>(slot);  // region A: offsets - A0
+        const T* drow = reinterpret_cast<const T*>(slot + kPieces * 256);      // [C][16 NSW] dO rows
+        const float* betaA = O::f32(op, O::betaA - A0);
+        const float* gamA = O::f32(op, O::gamA - A0);
+        // dO as the B operand of products over the chunk's tokens
         Frag<T> dOf;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            settle(dc[j]);
-            dOf.set(j, n * C + slot_index(gq, j) < a.T ? raw_value<T>(dc[j]) : 0.f);
+            const int t = slot_index(gq, j);
+            dOf.set(j, n * C + t < a.T ? to_f<T>(drow[t * (16 * NSW) + col - c0]) : 0.f);
         }
-        const unsigned char* op = reinterpret_cast<const unsigned char*>(sOp[it % K]);  // region A: offsets - A0
-        const float* betaA = O::f32(op, O::betaA - A0);
-        const float* gamA = O::f32(op, O::gamA - A0);
         // dU = Aqk^T dO + Kp dS'
         floatx4 dU[2];
 #pragma unroll
@@ -765,6 +772,9 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_adjoint_kernel(const B
             const floatx4 wv = mma(frag_tile(O::tiles(op, O::TT - A0), tb, 0, 1), dUf, z4);
 #pragma unroll
             for (int i = 0; i < 4; ++i) X[tb][i] = -betaA[16 * tb + 4 * gq + i] * wv[i];
+            // this chunk's W for the gradient kernel, in fragment order
+            reinterpret_cast<float4*>(a.w + ((size_t)bh * a.NC + n) * C * a.Dv)[((col >> 4) * 2 + tb) * 64 + lane] =
+                make_float4(wv[0], wv[1], wv[2], wv[3]);
         }
         // dS = Diag(gamma) dS' + Qp^T dO - Kd^T (beta W)
         const Frag<T> Xf = frag_from_c<T>(X[0], X[1]);
@@ -776,29 +786,9 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_adjoint_kernel(const B
             acc = mma(frag_tile(O::tiles(op, O::QpT - A0), R, 0, 1), dOf, acc);
             dS[R] = mma(frag_tile(O::tiles(op, O::KdT - A0), R, 0, 1), Xf, acc);
         }
-        if constexpr (!LAST) put_strip<NBD, NSW>(sTr[(it + 1) & 1], w, dS);
+        if (n > 0) put_strip<NBD, NSW>(sTr[(it + 1) & 1], w, dS);
         lds_barrier();
-        if constexpr (!LAST) flush_adj(n - 1, (it + 1) & 1);
-    };
-    const std::integral_constant<bool, false> more;
-    const std::integral_constant<bool, true> last;
-    uint32_t da[8], db[8];
-    if (a.NC > 0) {
-        load_do(a.NC - 1, da);
-        put_strip<NBD, NSW>(sTr[0], w, dS);
-    }
-    lds_barrier();
-    if (a.NC > 0) flush_adj(a.NC - 1, 0);
-    int it = 0;
-    for (; it + 2 < a.NC; it += 2) {
-        chunk(a.NC - 1 - it, it, da, db, more);
-        chunk(a.NC - 2 - it, it + 1, db, da, more);
-    }
-    if (a.NC - it == 2) {
-        chunk(1, it, da, db, more);
-        chunk(0, it + 1, db, da, last);
-    } else if (a.NC - it == 1) {
-        chunk(0, it, da, db, last);
+        if (n > 0) flush_adj(n - 1, (it + 1) & 1);
     }
     if (a.dS0) {
 #pragma unroll
@@ -810,27 +800,12 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_adjoint_kernel(const B
 
 // ---------------------------------------------------------------- 4. grads
 
-// B operand of a product over rows k0 .. k0 + 31 of a row-major fp32 matrix
-// (leading dimension ld) at column col: lane (r, gq) supplies rows
-// k0 + slot_index(gq, j); rows past klen are zero.
-template <typename E>
-__device__ __forceinline__ Frag<E> frag_cols(const float* M, int ld, int k0, int col, int klen) {
-    const int gq = (threadIdx.x & 63) >> 4;
-    Frag<E> f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int k = k0 + slot_index(gq, j);
-        f.set(j, k < klen ? M[(size_t)k * ld + col] : 0.f);
-    }
-    return f;
-}
-
 // Sum over the 16 lanes that share lane / 16 (DPP row moves).
 __device__ __forceinline__ float row_sum16(float x) { return group_sum<16>(x); }
 
 // One workgroup (eight waves) per chunk-head.  Wave w owns value columns
-// 16 w .. 16 w + 15 for the products over tokens (E, dU, U, W stay in C
-// layout and feed the next product directly), and channel block 16 w ..
+// 16 w .. 16 w + 15 for the per-token terms (E, U and W of the chunk, handed
+// over by the serial passes in C layout), and channel block 16 w ..
 // 16 w + 15 for the products over the value dimension (dQp, dKd, dKp, with
 // the rows of dO, U and W read from LDS and the rows of S and dS' as
 // contiguous global fragments), and for the decay-weighted sums and the
@@ -881,18 +856,16 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
         dOr[u] = ldraw<T>(a.dout, in_row(t) * DV + j);
     }
     const int col = 16 * (w % NBV) + r;
-    Frag<float> Sfr[KSD], Dfr[KSD];  // as loaded: converted where used, so nothing waits for them here
-    uint32_t vr[2][4];
+    floatx4 Ef[2], Uf[2], Wf[2];  // this wave's strip of E, U and W, settled where used
     if (w < NBV) {
+        const floatx4* eu = reinterpret_cast<const floatx4*>(a.eu + ((size_t)bh * a.NC + n) * 2 * C * DV);
+        const floatx4* wf = reinterpret_cast<const floatx4*>(a.w + ((size_t)bh * a.NC + n) * C * DV);
 #pragma unroll
-        for (int s = 0; s < KSD; ++s) {
-            Sfr[s] = frag_cols<float>(S0, DV, 32 * s, col, DK);
-            Dfr[s] = frag_cols<float>(dSC, DV, 32 * s, col, DK);
+        for (int tb = 0; tb < 2; ++tb) {
+            Ef[tb] = eu[(w * 2 + tb) * 64 + lane];
+            Uf[tb] = eu[(C * DV) / 4 + (w * 2 + tb) * 64 + lane];
+            Wf[tb] = wf[(w * 2 + tb) * 64 + lane];
         }
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) vr[tb][i] = ldraw<T>(a.v, in_row(16 * tb + 4 * gq + i) * DV + col);
     }
     prep_finish<T, DK, DK, NT>(a, h, t0, pin, sQ, sK, sG, sB, sRq, sRk, sPart, sNrm);
 #pragma unroll
@@ -904,57 +877,24 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
     for (int t = tid; t < C; t += NT) sdB[t] = 0.f;
     lds_barrier();
 
-    // ---- products over tokens, value column block w
+    // ---- per token, value column block w: dV = Diag(beta) W, the E.W part of
+    // dbeta, and the rows of U and W for the products over the value dimension
     if (w < NBV) {
-        floatx4 E[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, dU[2] = {E[0], E[0]};
-#pragma unroll
-        for (int s = 0; s < KSD; ++s) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                settle(Sfr[s].v[j]);
-                settle(Dfr[s].v[j]);
-            }
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-                E[tb] = mma(frag_tile(O::tiles(op, O::Kd), tb, s, KSD), cvt_frag<T>(Sfr[s]), E[tb]);
-                dU[tb] = mma(frag_tile(O::tiles(op, O::Kp), tb, s, KSD), cvt_frag<T>(Dfr[s]), dU[tb]);
-            }
-        }
-        floatx4 dO[2], Eb[2];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
+                float E = Ef[tb][i], U = Uf[tb][i], W = Wf[tb][i];
+                settle(E);
+                settle(U);
+                settle(W);
                 const int t = 16 * tb + 4 * gq + i;
-                settle(vr[tb][i]);
-                const float vv = (t0 + t < a.T) ? raw_value<T>(vr[tb][i]) : 0.f;
-                E[tb][i] = vv - E[tb][i];           // E = V - Kd S
-                Eb[tb][i] = sB[t] * E[tb][i];
-                dO[tb][i] = sdO[t * PV + col];
-            }
-        const Frag<T> dOf = frag_from_c<T>(dO[0], dO[1]);
-        const Frag<T> Ebf = frag_from_c<T>(Eb[0], Eb[1]);
-        const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
-        floatx4 U[2];
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            dU[tb] = mma(frag_tile(O::tiles(op, O::AqkT), tb, 0, 1), dOf, dU[tb]);  // + Aqk^T dO
-            U[tb] = mma(frag_tile(O::tiles(op, O::Tm), tb, 0, 1), Ebf, z4);         // T (beta E)
-        }
-        const Frag<T> dUf = frag_from_c<T>(dU[0], dU[1]);
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            const floatx4 W = mma(frag_tile(O::tiles(op, O::TT), tb, 0, 1), dUf, z4);  // T^T dU
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * tb + 4 * gq + i;
-                if (t0 + t < a.T) stf<T>(a.dv, row_of(t) * DV + col, sB[t] * W[i]);
-                const float p = row_sum16(W[i] * E[tb][i]);
+                if (t0 + t < a.T) stf<T>(a.dv, row_of(t) * DV + col, sB[t] * W);
+                const float p = row_sum16(W * E);
                 if (r == 0) atomicAdd(&sdB[t], p);
-                sU[t * PV + col] = U[tb][i];
-                sW[t * PV + col] = W[i];
+                sU[t * PV + col] = U;
+                sW[t * PV + col] = W;
             }
-        }
     }
     lds_barrier();
 
