@@ -69,6 +69,18 @@ def test_backward_switches(flags):
     run_and_compare(inp, do, dST, F32, flags, f"flags {flags}")
 
 
+def test_backward_without_gate_needs_no_A_log():
+    # the gate switch off: A_log may be NULL and every gradient is the same
+    inp, do, dST = case(2, 45, 2, 64, 64, F32, 9, 3)
+    d = {k_: v_.cuda().contiguous() for k_, v_ in inp.items()}
+    g1 = kda.chunk_bwd(d["q"], d["k"], d["v"], d["z"], d["beta_raw"], d["A_log"], do.cuda(), d["S0"], dST.cuda(),
+                       flags=3)
+    g2 = kda.chunk_bwd(d["q"], d["k"], d["v"], d["z"], d["beta_raw"], None, do.cuda(), d["S0"], dST.cuda(), flags=3)
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert torch.equal(g1[n], g2[n]), n
+
+
 @pytest.mark.parametrize("with_S0,with_dST", [(False, False), (True, False), (False, True)])
 def test_backward_optional_states(with_S0, with_dST):
     inp, do, dST = case(1, 40, 3, 64, 64, F32, 7, kda.FLAGS_DEFAULT, with_S0, with_dST)
