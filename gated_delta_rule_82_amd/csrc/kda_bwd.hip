@@ -818,7 +818,8 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
     constexpr int KSD = (DK + 31) / 32, KSV = (DV + 31) / 32;
     constexpr int PV = DV + 4;  // row pitch of the value rows (16-byte rows, spread banks)
     __shared__ float sQ[C][DK], sK[C][DK], sG[C][DK];
-    __shared__ float sB[C], sRq[C], sRk[C], sdB[C];
+    __shared__ float sB[C], sRq[C], sRk[C];
+    __shared__ float sdBp[2][NT / 64][C];  // dbeta parts per wave (E.W, then dA_kk.At), summed in a fixed order
     __shared__ float sPq[NBK][C], sPk[NBK][C], sPqT[C], sPkT[C];
     __shared__ __align__(16) float sBig[3 * C * PV];
     __shared__ float sdAqk[C][C + 1], sdAt[C][C + 1];
@@ -874,7 +875,7 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
         settle(dOr[u]);
         sdO[t * PV + j] = (t0 + t < a.T) ? raw_value<T>(dOr[u]) : 0.f;
     }
-    for (int t = tid; t < C; t += NT) sdB[t] = 0.f;
+    for (int e = tid; e < (NT / 64) * C; e += NT) sdBp[1][e / C][e % C] = 0.f;  // dA_kk waves fill half their rows
     lds_barrier();
 
     // ---- per token, value column block w: dV = Diag(beta) W, the E.W part of
@@ -891,7 +892,7 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
                 const int t = 16 * tb + 4 * gq + i;
                 if (t0 + t < a.T) stf<T>(a.dv, row_of(t) * DV + col, sB[t] * W);
                 const float p = row_sum16(W * E);
-                if (r == 0) atomicAdd(&sdB[t], p);
+                if (r == 0) sdBp[0][w][t] = p;
                 sU[t * PV + col] = U;
                 sW[t * PV + col] = W;
             }
@@ -914,7 +915,7 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
                 const float dakk = (s < t) ? -acc[i] : 0.f;
                 sdAt[t][s] = sB[t] * dakk;  // dAt = Diag(beta) dA_kk
                 const float p = row_sum16(dakk * O::f32(op, O::At)[t * C + s]);
-                if (r == 0) atomicAdd(&sdB[t], p);
+                if (r == 0) sdBp[1][w][t] = p;
             } else {
                 sdAqk[t][s] = (s <= t) ? acc[i] : 0.f;
             }
@@ -1145,7 +1146,12 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
         sPkT[t] = pk;
         if (t0 + t < a.T) {
             const float bt = sB[t];
-            const float db = (a.flags & kBetaSig) ? sdB[t] * bt * (1.f - bt) : sdB[t];
+            float dbs = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < NBV; ++ww) dbs += sdBp[0][ww][t];
+#pragma unroll
+            for (int ww = 0; ww < 4; ++ww) dbs += sdBp[1][ww][t];
+            const float db = (a.flags & kBetaSig) ? dbs * bt * (1.f - bt) : dbs;
             stf<T>(a.dbeta_raw, row_of(t), db);
         }
     }
