@@ -95,9 +95,6 @@ template <typename E, int DK> struct Ops {
     }
 };
 
-// Elements of the operand tiles of a [rows x kext] matrix.
-constexpr int tile_elems(int rows, int kext) { return (int)bwd_tile_bytes(rows, kext, 1); }
-
 // Position of element (row, k) in operand tiles with kext contraction indices.
 __device__ __forceinline__ size_t tile_pos(int row, int k, int kext) {
     const int ks = k >> 5, kk = k & 31;
@@ -326,14 +323,14 @@ __device__ void prep_finish(const BwdArgs& a, int h, int t0, const PrepIn<DK, NT
 
 // ------------------------------------------------------------------ 1. ops
 
-// Each operand matrix is assembled in LDS in tile order, then written out as
-// whole 16-byte pieces.
+// The operand tiles of K_d, K_p and the transposes are written fragment by
+// fragment; Aqk^T, T and T^T are assembled in LDS in tile order first.
 template <typename T, int DK>
 __global__ __launch_bounds__(256) void kda_bwd_ops_kernel(const BwdArgs a) {
     using O = Ops<T, DK>;
     constexpr int P = DK + 1;  // odd pitch: the pair loop reads columns across rows
     constexpr int KSD = (DK + 31) / 32;
-    constexpr int kStage = tile_elems(C, DK) > 2 * C * C ? tile_elems(C, DK) : 2 * C * C;
+    constexpr int kStage = 2 * C * C;  // Aqk^T, then T and T^T, in tile order
     __shared__ float sQ[C][P], sK[C][P], sG[C][P];
     __shared__ float sB[C], sRq[C], sRk[C];
     __shared__ float sAt[C][C + 1], sTT[C][C + 1];
@@ -356,29 +353,46 @@ __global__ __launch_bounds__(256) void kda_bwd_ops_kernel(const BwdArgs a) {
         for (int e = 8 * tid; e < count; e += 8 * 256) store_row8(out + e, sSt + e);
         lds_barrier();
     };
-    // [C x DK] operands: Kd = k_hat exp(G), Kp = k_hat exp(G_C - G); slots past DK are zero
-    for (int which = 0; which < 2; ++which) {
-        for (int e = tid; e < C * 32 * KSD; e += 256) {
-            const int t = e / (32 * KSD), k = e % (32 * KSD);
-            float x = 0.f;
-            if (k < DK) {
-                const float G = sG[t][k];
-                x = sK[t][k] * exp2_fast(which == 0 ? G : sG[C - 1][k] - G);  // exponent <= 0
-            }
-            sSt[tile_pos(t, k, DK)] = x;
+    // The operand tiles of K_d, K_p and the transposes, fragment by fragment:
+    // item (tile, lane) is the lane's 8 slots of the tile, computed and stored
+    // (16 or 32 bytes) by one thread, so a wave writes 64 consecutive items.
+    auto put8 = [&](size_t off, int item, const float (&x)[8]) {
+        store_row8(reinterpret_cast<T*>(op + off) + (size_t)item * 8, x);
+    };
+    // [C x DK]: Kd = k_hat exp(G), Kp = k_hat exp(G_C - G); slots past DK are zero
+    for (int it = tid; it < (C / 16) * KSD * 64; it += 256) {
+        const int ln = it & 63, tile = it >> 6, rb = tile / KSD, ks = tile % KSD;
+        const int t = 16 * rb + (ln & 15), g4 = ln >> 4;
+        float xd[8], xp[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int k = 32 * ks + slot_index(g4, j);
+            const bool in = k < DK;
+            const int kc = in ? k : 0;
+            const float G = sG[t][kc], Kv = sK[t][kc];
+            xd[j] = in ? Kv * exp2_fast(G) : 0.f;                   // exponent <= 0
+            xp[j] = in ? Kv * exp2_fast(sG[C - 1][kc] - G) : 0.f;
         }
-        flush(which == 0 ? O::Kd : O::Kp, tile_elems(C, DK));
+        put8(O::Kd, it, xd);
+        put8(O::Kp, it, xp);
     }
-    // [DK x C] operands: KpT, QpT, KdT
-    for (int which = 0; which < 3; ++which) {
-        for (int e = tid; e < C * DK; e += 256) {
-            const int d = e / C, t = e % C;
-            const float G = sG[t][d];
-            const float x = which == 0 ? sK[t][d] * exp2_fast(sG[C - 1][d] - G)
-                          : (which == 1 ? sQ[t][d] : sK[t][d]) * exp2_fast(G);
-            sSt[tile_pos(d, t, C)] = x;
+    // [DK x C]: KpT, QpT = (q_hat exp(G))^T, KdT
+    for (int it = tid; it < (DK / 16) * 64; it += 256) {
+        const int ln = it & 63, rb = it >> 6;
+        const int d = 16 * rb + (ln & 15), g4 = ln >> 4;
+        const float GC = sG[C - 1][d];
+        float xkp[8], xq[8], xkd[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int t = slot_index(g4, j);
+            const float G = sG[t][d], Kv = sK[t][d], e = exp2_fast(G);
+            xkp[j] = Kv * exp2_fast(GC - G);
+            xq[j] = sQ[t][d] * e;
+            xkd[j] = Kv * e;
         }
-        flush(which == 0 ? O::KpT : (which == 1 ? O::QpT : O::KdT), tile_elems(DK, C));
+        put8(O::KpT, it, xkp);
+        put8(O::QpT, it, xq);
+        put8(O::KdT, it, xkd);
     }
     for (int d = tid; d < DK; d += 256) opf[O::gamS / 4 + d] = opf[O::gamA / 4 + d] = exp2_fast(sG[C - 1][d]);
     for (int t = tid; t < C; t += 256) opf[O::betaS / 4 + t] = opf[O::betaA / 4 + t] = sB[t];
