@@ -269,13 +269,24 @@ __device__ void prep_finish(const BwdArgs& a, int h, int t0, const PrepIn<DK, NT
     const float eA = (a.flags & kGateIn) ? expf(Al) : 0.f;
     const bool l2 = (a.flags & kQkL2) != 0;
     float q[NPT], k[NPT], g[NPT], nq[NPT], nk[NPT];
+    // the per-token log-decay (the gate chosen once, not per element), on a
+    // valid logit even past the end
+    if (!(a.flags & kGateIn)) {
+#pragma unroll
+        for (int u = 0; u < NPT; ++u) g[u] = in.z[u];
+    } else if (a.flags & kGateSoftplus) {
+#pragma unroll
+        for (int u = 0; u < NPT; ++u) g[u] = -eA * (fmaxf(in.z[u], 0.f) + log1pf(expf(-fabsf(in.z[u]))));
+    } else {
+#pragma unroll
+        for (int u = 0; u < NPT; ++u) g[u] = a.g_min * sigmoidf_(eA * in.z[u]);
+    }
 #pragma unroll
     for (int u = 0; u < NPT; ++u) {
         const bool valid = t0 + tg + u < a.T;
         q[u] = valid ? in.q[u] : 0.f;
         k[u] = valid ? in.k[u] : 0.f;
-        const float gl = gate_of(in.z[u], eA, a.g_min, a.flags);  // on a valid logit even past the end
-        g[u] = (valid ? gl : 0.f) * kLog2e;                       // log2 units: one exp2 per factor
+        g[u] = (valid ? g[u] : 0.f) * kLog2e;  // log2 units: one exp2 per factor
         if (u > 0) g[u] += g[u - 1];
         nq[u] = q[u] * q[u];
         nk[u] = k[u] * k[u];
@@ -965,18 +976,20 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
 
     // ---- decay-weighted sums: lane (r, gq) of wave w owns channel 16 w + r
     // at tokens 16 tb + 4 gq + i, here and for the outputs
-    float dqh[2][4], dkh[2][4], dGv[2][4], Kt[2][4], Qt[2][4], zl[2][4];
+    float dqh[2][4], dkh[2][4], dGv[2][4], Kt[2][4], Qt[2][4];
+    uint32_t zr[2][4];  // gate logits, raw until dz (their wait then falls after the decay sums)
+    float zb = 0.f;
     float gce = 0.f;  // the chunk-end terms of dg, entering at the last token
     if (w < NBK) {
         const int d = 16 * w + r;
-        // the (biased) gate logits for dz: loaded now, used at the end
-        const float zb = a.dt_bias ? a.dt_bias[(size_t)h * DK + d] : 0.f;
+        // the (biased) gate logits for dz: requested now, used at the end
+        zb = a.dt_bias ? a.dt_bias[(size_t)h * DK + d] : 0.f;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int tok = min(t0 + 16 * tb + 4 * gq + i, a.T - 1);
-                zl[tb][i] = ldf<T>(a.z, (((size_t)b * a.T + tok) * a.H + h) * DK + d) + zb;
+                zr[tb][i] = ldraw<T>(a.z, (((size_t)b * a.T + tok) * a.H + h) * DK + d);
             }
         const float GC = sG[C - 1][d];
         float gcpart = 0.f;
@@ -1115,7 +1128,8 @@ __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
                 const float acc = base[tb] + suf[tb][i];
                 float dz = acc, dA = 0.f;
                 if (a.flags & kGateIn) {
-                    const float zv = zl[tb][i];
+                    settle(zr[tb][i]);
+                    const float zv = raw_value<T>(zr[tb][i]) + zb;
                     if (a.flags & kGateSoftplus) {
                         const float sg = sigmoidf_(zv);
                         dz = acc * (-eA * sg);
