@@ -24,15 +24,16 @@
 // -x dx), G to the per-token log-decay by a reverse cumulative sum, and the
 // switched activations (L2 norm, sigmoid beta, gate) to the raw inputs.
 //
-// Five kernels:
-//  1. kda_bwd_ops:     per chunk-head, the chunk operators in fp32 (Aqk and
-//                      At element by element in log space, T by forward
-//                      substitution; Kd, Qp, Kp and the transposes the
-//                      matrix cores read).
-//  2. kda_bwd_states:  per (b, h), serial over chunks: the state at each
-//                      chunk start (fp32 MFMA, one wave per 16 value columns).
-//  3. kda_bwd_adjoint: per (b, h), serial over chunks in reverse: the adjoint
-//                      at each chunk end, and dS0.
+// Five kernels (matrix-core operands in the input precision, fp32 states and
+// accumulation):
+//  1. kda_bwd_ops:     per chunk-head, the chunk operators: Aqk and At as
+//                      16 x 16 blocks with the decay factored per block, T by
+//                      blocked substitution, Kd, Qp, Kp and the transposes as
+//                      operand tiles.
+//  2. kda_bwd_states:  per (b, h) and 32 value columns, serial over chunks:
+//                      the state at each chunk start, and each chunk's E, U.
+//  3. kda_bwd_adjoint: the same in reverse: the adjoint at each chunk end,
+//                      each chunk's W, and dS0.
 //  4. kda_bwd_grads:   per chunk-head: every input gradient of the chunk.
 //  5. kda_bwd_dA:      the sum of the per-chunk dA_log parts.
 //
