@@ -694,6 +694,9 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_states_kernel(const Bw
                 Eb[tb][i] = betaS[t] * E[tb][i];
             }
         }
+        // the state at the start of this chunk, put into the LDS tile before the
+        // last barrier, goes out here, behind the products just issued
+        if (n > 0) flush_state(n);
         // U = T (beta E)
         floatx4 U[2];
         const Frag<T> Ebf = frag_from_c<T>(Eb[0], Eb[1]);
@@ -720,7 +723,6 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_states_kernel(const Bw
         }
         if (n + 1 < a.NC) put_strip<NBD, NSW>(sTr[(n + 1) & 1], w, S);
         lds_barrier();   // the next chunk is in LDS, this chunk's slot no longer read
-        if (n + 1 < a.NC) flush_state(n + 1);
     }
 }
 
@@ -789,6 +791,9 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_adjoint_kernel(const B
                 acc = mma(frag_tile(O::tiles(op, O::Kp - A0), tb, s, KSD), frag_strip<T>(dS, s), acc);
             dU[tb] = acc;
         }
+        // the adjoint at the end of this chunk, put into the LDS tile before the
+        // last barrier, goes out here, behind the products just issued
+        if (it > 0) flush_adj(n, it & 1);
         // -beta W with W = T^T dU
         floatx4 X[2];
         const Frag<T> dUf = frag_from_c<T>(dU[0], dU[1]);
@@ -814,7 +819,6 @@ __global__ __launch_bounds__(64 * (NSW + 1)) void kda_bwd_adjoint_kernel(const B
         }
         if (n > 0) put_strip<NBD, NSW>(sTr[(it + 1) & 1], w, dS);
         lds_barrier();
-        if (n > 0) flush_adj(n - 1, (it + 1) & 1);
     }
     if (a.dS0) {
 #pragma unroll
