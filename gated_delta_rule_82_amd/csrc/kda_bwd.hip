@@ -845,7 +845,7 @@ template <typename T, int DK, int DV>
 __global__ __launch_bounds__(512) void kda_bwd_grads_kernel(const BwdArgs a) {
     constexpr int NT = 512;
     constexpr int NBV = DV / 16, NBK = DK / 16;
-    constexpr int KSD = (DK + 31) / 32, KSV = (DV + 31) / 32;
+    constexpr int KSV = (DV + 31) / 32;
     constexpr int PV = DV + 4;  // row pitch of the value rows (16-byte rows, spread banks)
     __shared__ float sQ[C][DK], sK[C][DK], sG[C][DK];
     __shared__ float sB[C], sRq[C], sRk[C];
