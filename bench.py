@@ -1,14 +1,13 @@
 #!/usr/bin/env python3
 """Benchmark of the KDA hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk 32] [--overlap]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk 32]
 
 A step is one chunkwise forward call (prep, intra-chunk and inter-chunk
 kernels) over the layer-shaped workload B=4, T=4096, H=16, Dk=Dv=128, bf16
 inputs and fp32 state, with the inputs already resident in HBM.  Four input
 sets (about 1.1 GB) rotate from step to step so the 256 MB Infinity Cache
-cannot serve them.  The call is kda_chunk_fwd on one stream (--overlap times
-the two-stream schedule kda_chunk_fwd_overlap instead).  The state chunk is a
+cannot serve them.  The call is kda_chunk_fwd on one stream.  The state chunk is a
 tiling choice of the kernels (results agree to rounding for 16, 32 and 64);
 32 is the fastest here.  The step time (value, ms_per_step) comes from the
 calls alone; the JSON line also reports, measured in the same run:
@@ -47,6 +46,26 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_layer.txt")
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def percentile(sorted_vals, p):
+    """Linear-interpolated percentile of an ascending list."""
+    if not sorted_vals:
+        return None
+    x = (len(sorted_vals) - 1) * p / 100.0
+    lo = int(x)
+    hi = min(lo + 1, len(sorted_vals) - 1)
+    return sorted_vals[lo] + (sorted_vals[hi] - sorted_vals[lo]) * (x - lo)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # ------------------------------------------------------------------ work model
@@ -131,9 +150,10 @@ def _oracle_slice(args):
     return True
 
 
-def cpu_baseline(inp, T_sample):
+def cpu_baseline(inp, T_sample, T_full):
     """Time the fp64 oracle on all heads of the layer workload, first T_sample
-    tokens, split over (b, head group) across worker processes."""
+    tokens (all of them by default), split over (b, head group) across worker
+    processes."""
     import multiprocessing as mp
 
     import numpy as np
@@ -155,18 +175,18 @@ def cpu_baseline(inp, T_sample):
         pool.map(_oracle_slice, jobs)
     wall = time.perf_counter() - t0
     return {"value": B * T_sample / wall, "unit": "tokens/s", "cores": n_proc, "kind": "oracle",
-            "sample": f"layer workload, all {B * H} (b,h) heads, first {T_sample} of 4096 tokens, "
+            "cpu_model": cpu_model(), "host_cpus_visible": len(os.sched_getaffinity(0)),
+            "sample": f"layer workload, all {B * H} (b,h) heads, first {T_sample} of {T_full} tokens, "
                       f"fp64 token recurrence, {len(jobs)} slices over {n_proc} processes",
             "wall_s": round(wall, 3)}
 
 
 # ------------------------------------------------------------------ GPU legs
 
-def bench_layer(torch, kda, inputs, steps, warmup, chunk=None, overlap=False):
-    """Time `steps` calls over rotating input sets.  overlap: the two-stream
-    schedule (kda_chunk_fwd_overlap), else one stream (kda_chunk_fwd_timed).
-    Per-kernel launch times come from the events the library records around
-    each of its kernels, on the kernel's own stream."""
+def bench_layer(torch, kda, inputs, steps, warmup, chunk=None):
+    """Time `steps` calls over rotating input sets (one stream).  Per-kernel
+    launch times come from the events the library records around each of its
+    kernels on the launch stream (kda_chunk_fwd_timed)."""
     w = inputs.WORKLOADS["layer"]
     dev = torch.device("cuda:0")
     B, T, H, Dk, Dv = w.B, w.T, w.H, w.Dk, w.Dv
@@ -181,22 +201,21 @@ def bench_layer(torch, kda, inputs, steps, warmup, chunk=None, overlap=False):
     A = base["A_log"].to(dev)
     o = torch.empty(B, T, H, Dv, dtype=torch.bfloat16, device=dev)
     S = torch.empty(B, H, Dk, Dv, dtype=torch.float32, device=dev)
-    ov = kda.Overlap(dev) if overlap else None
-    ws_n = (kda.overlap_workspace_bytes if overlap else kda.workspace_bytes)(B, T, H, Dk, Dv, C, torch.bfloat16)
+    ws_n = kda.workspace_bytes(B, T, H, Dk, Dv, C, torch.bfloat16)
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
-    nk = (kda.overlap_kernel_count if overlap else kda.kernel_count)(B, T, H, Dk, Dv, C, torch.bfloat16)
-    n_ev = 2 * nk if overlap else nk + 1
+    nk = kda.kernel_count(B, T, H, Dk, Dv, C, torch.bfloat16)
+    n_ev = nk + 1
 
     def step(i, evs=None):
         s = sets[i % len(sets)]
         kda.chunk_fwd(s["q"], s["k"], s["v"], s["z"], s["beta_raw"], A, None, chunk=C,
-                      o=o, S_out=S, workspace=ws, events=evs, overlap=ov)
+                      o=o, S_out=S, workspace=ws, events=evs)
 
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    # timed region 1: the calls alone (the step time; no per-kernel events,
-    # whose records add GPU time between the kernels)
+    # timed region 1: the calls alone, back to back (the step time; no
+    # per-kernel events, whose records add GPU time between the kernels)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(steps):
@@ -204,6 +223,15 @@ def bench_layer(torch, kda, inputs, steps, warmup, chunk=None, overlap=False):
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
+    # timed region 1b: the same calls, each bracketed by its own pair of
+    # events on the launch stream (distribution of the call time)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        pairs[i][0].record()
+        step(i)
+        pairs[i][1].record()
+    torch.cuda.synchronize()
+    call_ms = sorted(a.elapsed_time(b) for a, b in pairs)
     # timed region 2: the same calls with the library recording an event
     # around each of its kernels on the kernel's stream (per-launch durations)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
@@ -216,15 +244,14 @@ def bench_layer(torch, kda, inputs, steps, warmup, chunk=None, overlap=False):
     torch.cuda.synchronize()
     timed_ms = start2.elapsed_time(end2)
     # kernel k: intra for even k, inter for odd k (they alternate over the slices)
-    if overlap:
-        dur = lambda e, k: e[2 * k].elapsed_time(e[2 * k + 1])
-    else:
-        dur = lambda e, k: e[k].elapsed_time(e[k + 1])
+    dur = lambda e, k: e[k].elapsed_time(e[k + 1])
     launches = {"kda_intra": [dur(e, k) for e in evs for k in range(0, nk, 2)],
                 "kda_inter": [dur(e, k) for e in evs for k in range(1, nk, 2)]}
     return {"B": B, "T": T, "H": H, "Dk": Dk, "Dv": Dv, "C": C, "ws_bytes": ws_n,
-            "schedule": "two streams, two slices" if overlap else "one stream",
+            "schedule": "one stream",
             "ms_per_step": total_ms / steps,
+            "call_ms": {"median": percentile(call_ms, 50), "p10": percentile(call_ms, 10),
+                        "p90": percentile(call_ms, 90), "mean": sum(call_ms) / len(call_ms), "n": len(call_ms)},
             "ms_per_step_with_kernel_events": timed_ms / steps,
             "kernel_ms": {k: sum(v) / steps for k, v in launches.items()},
             "launch_ms": {k: sum(v) / len(v) for k, v in launches.items()},
@@ -512,15 +539,13 @@ def bench_long(torch, kda, inputs, reps, chunk):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-tokens", type=int, default=2048, help="oracle sample length (0 = skip)")
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-tokens", type=int, default=4096, help="oracle sample length (0 = skip)")
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--long-reps", type=int, default=3)
     ap.add_argument("--only-layer", action="store_true", help="time the layer workload only")
     ap.add_argument("--chunk", type=int, default=32, help="state chunk length (16, 32 or 64)")
-    ap.add_argument("--overlap", action="store_true",
-                    help="time the two-stream schedule (kda_chunk_fwd_overlap) instead of the one-stream call")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run 3 device copies of 1 GiB (a counter reference of known size)")
     args = ap.parse_args()
@@ -540,8 +565,8 @@ def main():
     cpu = None
     if args.cpu_tokens > 0 and not args.only_layer:
         log(f"[bench] oracle CPU baseline on {args.cpu_tokens} tokens ...")
-        cpu = cpu_baseline(inputs.make_workload(inputs.WORKLOADS["layer"], T=args.cpu_tokens),
-                           args.cpu_tokens)
+        wl = inputs.WORKLOADS["layer"]
+        cpu = cpu_baseline(inputs.make_workload(wl, T=args.cpu_tokens), args.cpu_tokens, wl.T)
         log(f"[bench] oracle: {cpu['value']:.1f} tokens/s on {cpu['cores']} processes")
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -559,19 +584,27 @@ def main():
 
     log("[bench] layer workload ...")
     C = args.chunk or 32
-    L = bench_layer(torch, kda, inputs, args.steps, args.warmup, C, overlap=args.overlap)
+    L = bench_layer(torch, kda, inputs, args.steps, args.warmup, C)
     B, T, H, Dk, Dv = L["B"], L["T"], L["H"], L["Dk"], L["Dv"]
     ms = L["ms_per_step"]
     tok_s = B * T / (ms / 1e3)
     f_tri, f_full = chunk_flops(B, T, H, Dk, Dv, C)
+    f_tri64, f_full64 = chunk_flops(B, T, H, Dk, Dv, 64)
     cbytes = chunk_bytes(B, T, H, Dk, Dv)
     kb = kernel_bytes(B, T, H, Dk, Dv, C)
     dom = max(L["kernel_ms"], key=L["kernel_ms"].get)
     n_launch = L["launches_per_step"][dom]
     launch_ms = L["launch_ms"][dom]
     bytes_per_launch = kb[dom] / n_launch
-    achieved = bytes_per_launch / (launch_ms / 1e3) / 1e9
-    traffic = read_traffic(dom, C, n_launch)
+    dom_rate = bytes_per_launch / (launch_ms / 1e3) / 1e9
+    # the roofline of the whole call: its compulsory bytes (q, k, v, z,
+    # beta_raw read once; o and the final state written once) over the step
+    # time; the counted traffic is the sum over the call's kernels
+    achieved = cbytes / (ms / 1e3) / 1e9
+    traffic = None
+    per_kernel_traffic = {kn: read_traffic(kn, C, L["launches_per_step"][kn]) for kn in L["launches_per_step"]}
+    if per_kernel_traffic and all(v is not None for v in per_kernel_traffic.values()):
+        traffic = sum(v * L["launches_per_step"][kn] for kn, v in per_kernel_traffic.items())
     log(f"[bench] layer {ms:.3f} ms/step ({L['schedule']}), {tok_s:.3e} tokens/s; kernels {L['kernel_ms']}")
 
     extra = {}
@@ -606,14 +639,24 @@ def main():
         "config": {"workload": f"layer: chunk_kda fwd B4 T4096 H16 Dk=Dv=128, bf16 in, fp32 state "
                                f"(state chunk {C}; {L['schedule']})",
                    "B": B, "T": T, "H": H, "Dk": Dk, "Dv": Dv, "chunk": C, "g_min": -5.0},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes": round(bytes_per_launch),
-                     "launch_ms": round(launch_ms, 4), "launches_per_step": n_launch},
+        "roofline": {"bound": "hbm", "kernel": "kda_chunk_fwd call (all kernels)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes": cbytes, "launch_ms": round(ms, 4), "launches_per_step": 1,
+                     "basis": "compulsory bytes of the call / ms_per_step"},
+        "call_ms": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in L["call_ms"].items()},
+        "dominant_kernel": {"kernel": dom, "launch_ms": round(launch_ms, 4), "launches_per_step": n_launch,
+                            "own_bytes_per_launch": round(bytes_per_launch),
+                            "own_bytes_rate_gbs": round(dom_rate, 1),
+                            "own_bytes_frac": round(dom_rate / HBM_PEAK_GBS, 4),
+                            "own_bytes": "the kernel's own algorithmic reads and writes, workspace blocks included"},
         "kernel_ms": {k: round(v, 4) for k, v in L["kernel_ms"].items()},
         "ms_per_step_with_kernel_events": round(L["ms_per_step_with_kernel_events"], 4),
-        "mfma_frac": {"algorithmic": round(f_tri / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                      "tile_count": round(f_full / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "mfma_frac": {"algorithmic": round(f_tri64 / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                      "tile_count": round(f_full64 / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                      "flop_basis": "C = 64 counts of the chunk form whatever chunk runs: triangles exact with the C^3/3 solve (36.9 GFLOP), full C x C tiles (47.2 GFLOP)",
+                      "algorithmic_at_run_chunk": round(f_tri / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                      "tile_count_at_run_chunk": round(f_full / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
         "hbm_frac_compulsory": round(cbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count},

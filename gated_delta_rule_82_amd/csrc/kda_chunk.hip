@@ -31,6 +31,7 @@
 // of block J and the gap between blocks is a per-channel scale <= 1.
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -1141,7 +1142,7 @@ struct ChunkLaunch {
     hipError_t intra(void* buf, int per, int c0, int nc, hipStream_t s) const {
         IntraArgs ia{a.q, a.k, a.z, a.beta_raw, a.A_log, buf, a.T, a.H, a.G, a.dt_bias, per, c0, nc, a.g_min, a.flags};
         const dim3 grid((unsigned)(BH * ((nc + NCH - 1) / NCH)));
-        if ((a.flags & kGateSoftplus) || !(a.flags & kGateIn))
+        if (a.wide_decay)
             hipLaunchKernelGGL((kda_intra_kernel<T, DK, C, true>), grid, dim3(256), 0, s, ia);
         else
             hipLaunchKernelGGL((kda_intra_kernel<T, DK, C, false>), grid, dim3(256), 0, s, ia);
@@ -1170,7 +1171,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t stream, hipEven
     const hipError_t attr = cl.set_attributes();
     if (attr != hipSuccess) return attr;
     const int BH = cl.BH;
-    const int per = slice_chunks(BH, a.NC, cl.L.bytes);
+    const int per = slice_chunks(BH, a.NC, cl.L.bytes, a.slice_budget);
     // the kernels below index the workspace with this `per`: refuse a buffer
     // sized for anything else rather than write past it
     if (a.ws_bytes < chunk_workspace_bytes(sizeof(T), DK, a.Dv, C, (size_t)BH, (size_t)per, 1))
@@ -1206,68 +1207,6 @@ int chunk_kernel_count(int elem_bytes, int DK, int C, int BH, int NC) {
     return 2 * ((NC + per - 1) / per);
 }
 
-// Overlapped schedule over slices of the sequence: intra(s) on `s_main` writes
-// buffer s % 2; inter(s) on `aux` reads it after intra(s) and carries the state
-// to slice s + 1.  intra(s + 2) reuses the buffer once inter(s) is done.
-// Events: sync[b] = intra into buffer b done, sync[2 + b] = inter of buffer b
-// done, sync[4] = all inter work done (joined back into s_main).
-template <typename T, int DK, int C>
-static hipError_t launch_chunk_overlap_t(const ChunkArgs& a, hipStream_t s_main, hipStream_t aux, hipEvent_t* sync,
-                                         hipEvent_t* tev, int n_tev) {
-    ChunkLaunch<T, DK, C> cl(a);
-    const hipError_t attr = cl.set_attributes();
-    if (attr != hipSuccess) return attr;
-    const int BH = cl.BH;
-    const int per = overlap_slice_chunks(BH, a.NC, cl.L.bytes);
-    if (a.ws_bytes < chunk_workspace_bytes(sizeof(T), DK, a.Dv, C, (size_t)BH, (size_t)per, 2))
-        return hipErrorInvalidValue;
-    const size_t buf_bytes = (size_t)BH * per * cl.L.bytes;
-    unsigned char* ws = reinterpret_cast<unsigned char*>(a.ws);
-    float* S_scr = reinterpret_cast<float*>(ws + 2 * buf_bytes);
-    float* M_scr = S_scr + (size_t)BH * DK * a.Dv;
-    auto rec = [&](int idx, hipStream_t s) -> bool {
-        return !tev || idx >= n_tev || hipEventRecord(tev[idx], s) == hipSuccess;
-    };
-#define KDA_HIP(x) do { const hipError_t e_ = (x); if (e_ != hipSuccess) return e_; } while (0)
-    // the aux stream starts after everything already queued on the main stream
-    KDA_HIP(hipEventRecord(sync[4], s_main));
-    KDA_HIP(hipStreamWaitEvent(aux, sync[4], 0));
-    const int nsl = a.NC > 0 ? (a.NC + per - 1) / per : 1;
-    int k = 0;  // kernel index for the timing events
-    for (int sl = 0; sl < nsl; ++sl) {
-        const int c0 = sl * per;
-        const int nc = std::max(0, std::min(per, a.NC - c0));
-        const int b = sl & 1;
-        void* buf = ws + b * buf_bytes;
-        if (nc > 0) {
-            if (sl >= 2) KDA_HIP(hipStreamWaitEvent(s_main, sync[2 + b], 0));  // inter(sl - 2) has read buffer b
-            if (!rec(2 * k, s_main)) return hipErrorInvalidValue;
-            KDA_HIP(cl.intra(buf, per, c0, nc, s_main));
-            if (!rec(2 * k + 1, s_main)) return hipErrorInvalidValue;
-            ++k;
-            KDA_HIP(hipEventRecord(sync[b], s_main));
-            KDA_HIP(hipStreamWaitEvent(aux, sync[b], 0));
-        }
-        if (!rec(2 * k, aux)) return hipErrorInvalidValue;
-        KDA_HIP(cl.inter(buf, per, c0, nc, sl == 0, sl == nsl - 1, S_scr, M_scr, aux));
-        if (!rec(2 * k + 1, aux)) return hipErrorInvalidValue;
-        ++k;
-        KDA_HIP(hipEventRecord(sync[2 + b], aux));
-    }
-    // the main stream resumes after the last inter kernel
-    KDA_HIP(hipEventRecord(sync[4], aux));
-    KDA_HIP(hipStreamWaitEvent(s_main, sync[4], 0));
-#undef KDA_HIP
-    return hipSuccess;
-}
-
-int chunk_overlap_kernel_count(int elem_bytes, int DK, int C, int BH, int NC) {
-    const BlockLayout L = block_layout(elem_bytes, DK, C);
-    if (NC <= 0) return 1;
-    const int per = overlap_slice_chunks(BH, NC, L.bytes);
-    return 2 * ((NC + per - 1) / per);
-}
-
 template <typename T, int DK>
 static hipError_t launch_chunk_c(int C, const ChunkArgs& a, hipStream_t s, hipEvent_t* ev, int n_ev) {
     switch (C) {
@@ -1293,33 +1232,31 @@ hipError_t launch_chunk(int dt, int DK, int C, const ChunkArgs& a, hipStream_t s
     return dt == 1 ? launch_chunk_d<bf16_t>(DK, C, a, s, ev, n_ev) : launch_chunk_d<float>(DK, C, a, s, ev, n_ev);
 }
 
-template <typename T, int DK>
-static hipError_t launch_overlap_c(int C, const ChunkArgs& a, hipStream_t s, hipStream_t aux, hipEvent_t* sync,
-                                   hipEvent_t* tev, int n_tev) {
-    switch (C) {
-        case 16: return launch_chunk_overlap_t<T, DK, 16>(a, s, aux, sync, tev, n_tev);
-        case 32: return launch_chunk_overlap_t<T, DK, 32>(a, s, aux, sync, tev, n_tev);
-        case 64: return launch_chunk_overlap_t<T, DK, 64>(a, s, aux, sync, tev, n_tev);
-        default: return hipErrorInvalidValue;
-    }
-}
+// ------------------------------------------------------------ built-in scratch
+// The per-chunk blocks of one slice and the carried state of the
+// allocation-free entry point.  In host code `scratch` names a host-side
+// stand-in, never the device memory: kernels and copies take the address
+// hipGetSymbolAddress returns for the current device, cached per device.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
-template <typename T>
-static hipError_t launch_overlap_d(int DK, int C, const ChunkArgs& a, hipStream_t s, hipStream_t aux,
-                                   hipEvent_t* sync, hipEvent_t* tev, int n_tev) {
-    switch (DK) {
-        case 16: return launch_overlap_c<T, 16>(C, a, s, aux, sync, tev, n_tev);
-        case 32: return launch_overlap_c<T, 32>(C, a, s, aux, sync, tev, n_tev);
-        case 64: return launch_overlap_c<T, 64>(C, a, s, aux, sync, tev, n_tev);
-        case 128: return launch_overlap_c<T, 128>(C, a, s, aux, sync, tev, n_tev);
-        default: return hipErrorInvalidValue;
+hipError_t scratch_pointer(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* cache[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!cache[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        cache[dev] = p;
     }
-}
-
-hipError_t launch_chunk_overlap(int dt, int DK, int C, const ChunkArgs& a, hipStream_t s, hipStream_t aux,
-                                hipEvent_t* sync, hipEvent_t* tev, int n_tev) {
-    return dt == 1 ? launch_overlap_d<bf16_t>(DK, C, a, s, aux, sync, tev, n_tev)
-                   : launch_overlap_d<float>(DK, C, a, s, aux, sync, tev, n_tev);
+    *ptr = cache[dev];
+    return hipSuccess;
 }
 
 }  // namespace kda

@@ -50,25 +50,12 @@ __host__ __device__ constexpr BlockLayout block_layout(int elem_bytes, int DK, i
 // prologues than they gain, so the layer-sized workloads run as one slice.
 constexpr size_t kSliceBytes = 1ull << 30;
 
-inline int slice_chunks(int BH, int NC, size_t block_bytes) {
+inline int slice_chunks(int BH, int NC, size_t block_bytes, size_t budget = kSliceBytes) {
     if (NC <= 0) return 0;
-    size_t per = kSliceBytes / ((size_t)(BH > 0 ? BH : 1) * (block_bytes > 0 ? block_bytes : 1));
+    size_t per = budget / ((size_t)(BH > 0 ? BH : 1) * (block_bytes > 0 ? block_bytes : 1));
     if (per < 1) per = 1;
     const int nsl = (int)((NC + per - 1) / per);
     return (NC + nsl - 1) / nsl;
-}
-
-// Slices of the overlapped schedule (intra of slice s + 1 runs beside inter of
-// slice s): two, of at least two chunks, within the slice budget.  Measured on
-// MI355X (layer workload), two slices gain about 9 % over one stream while
-// four or eight lose: every inter launch refills its LDS ring and reloads the
-// state, and the intra kernel only gets the CUs the inter kernel leaves free.
-inline int overlap_slice_chunks(int BH, int NC, size_t block_bytes) {
-    if (NC <= 0) return 0;
-    int per = (NC + 1) / 2;
-    if (per < 2) per = 2;
-    const int cap = slice_chunks(BH, NC, block_bytes);
-    return per < cap ? per : cap;
 }
 
 // Workspace: nbuf buffers of `per` chunk blocks for every (b, h), then the
@@ -95,7 +82,15 @@ struct ChunkArgs {
     float g_min; unsigned flags;
     int G = 1;                        // value heads per q/k head
     const float* dt_bias = nullptr;   // [H, Dk] gate bias
+    bool wide_decay = false;          // decays may leave the factored range: the GENERAL intra kernel
+    size_t slice_budget = kSliceBytes;  // bytes of chunk blocks per slice of the sequence
 };
+
+// Built-in device scratch of the allocation-free chunk entry point (one copy
+// per GPU, held until the process ends).
+constexpr size_t kScratchBytes = 64ull << 20;
+// Device address of the current device's scratch (looked up once per device).
+hipError_t scratch_pointer(void** ptr);
 
 struct ComposeArgs {
     const float* M; const float* S_tilde; const float* S_in; float* S_prefix;
@@ -115,12 +110,6 @@ hipError_t launch_step(int dt, int DK, int DV, const StepArgs& a, hipStream_t s)
 hipError_t launch_chunk(int dt, int DK, int C, const ChunkArgs& a, hipStream_t s, hipEvent_t* ev, int n_ev);
 // Kernels one kda_chunk_fwd call launches for these sizes.
 int chunk_kernel_count(int elem_bytes, int DK, int C, int BH, int NC);
-// Overlapped schedule: intra kernels on `s`, inter kernels on `aux`; sync holds
-// 5 events (see kda_chunk_fwd_overlap); tev (nullable, n_tev) gets a start and
-// an end event per kernel k at 2k and 2k + 1, recorded on the kernel's stream.
-hipError_t launch_chunk_overlap(int dt, int DK, int C, const ChunkArgs& a, hipStream_t s, hipStream_t aux,
-                                hipEvent_t* sync, hipEvent_t* tev, int n_tev);
-int chunk_overlap_kernel_count(int elem_bytes, int DK, int C, int BH, int NC);
 hipError_t launch_compose(int DK, const ComposeArgs& a, hipStream_t s);
 hipError_t launch_fixup(int dt, int DK, const FixupArgs& a, hipStream_t s);
 

@@ -23,13 +23,11 @@ GATE_SOFTPLUS = 8  # with GATE_IN_KERNEL: the unbounded KDA v1 gate -exp(A_log) 
 
 EXPORTS = (
     "kda_safe_chunk_size", "kda_chunk_fwd_workspace", "kda_chunk_fwd", "kda_chunk_fwd_timed",
-    "kda_chunk_fwd_kernel_count", "kda_chunk_fwd_overlap_workspace", "kda_chunk_fwd_overlap_kernel_count",
-    "kda_chunk_fwd_overlap", "kda_step", "kda_chunk_fwd_grouped", "kda_step_grouped",
+    "kda_chunk_fwd_kernel_count", "kda_chunk_fwd_noalloc", "kda_step", "kda_chunk_fwd_grouped", "kda_step_grouped",
     "kda_segment_compose", "kda_segment_fixup", "kda_short_conv", "kda_output_gate",
     "kda_chunk_bwd_workspace", "kda_chunk_bwd", "kda_chunk_bwd_grouped_workspace", "kda_chunk_bwd_grouped",
     "kda_status_string",
 )
-OVERLAP_SYNC_EVENTS = 5
 
 _lib = None
 
@@ -60,12 +58,8 @@ def load() -> ctypes.CDLL:
     L.kda_chunk_fwd_timed.restype = I
     L.kda_chunk_fwd_kernel_count.argtypes = [I] * 7
     L.kda_chunk_fwd_kernel_count.restype = I
-    L.kda_chunk_fwd_overlap_workspace.argtypes = [I] * 7
-    L.kda_chunk_fwd_overlap_workspace.restype = S
-    L.kda_chunk_fwd_overlap_kernel_count.argtypes = [I] * 7
-    L.kda_chunk_fwd_overlap_kernel_count.restype = I
-    L.kda_chunk_fwd_overlap.argtypes = [P] * 11 + [I] * 6 + [F, U, I, P, S, P, P, P, I, P, I]
-    L.kda_chunk_fwd_overlap.restype = I
+    L.kda_chunk_fwd_noalloc.argtypes = [P] * 11 + [I] * 6 + [F, U, I, P]
+    L.kda_chunk_fwd_noalloc.restype = I
     L.kda_step.argtypes = [P] * 8 + [I] * 4 + [F, U, I, P]
     L.kda_step.restype = I
     L.kda_segment_compose.argtypes = [I, P, P, P, P, I, I, I, I, P]
@@ -136,14 +130,6 @@ def kernel_count(B, T, H, Dk, Dv, chunk=64, dtype=torch.bfloat16) -> int:
     return load().kda_chunk_fwd_kernel_count(B, T, H, Dk, Dv, chunk, _dt(dtype))
 
 
-def overlap_workspace_bytes(B, T, H, Dk, Dv, chunk=64, dtype=torch.bfloat16) -> int:
-    return load().kda_chunk_fwd_overlap_workspace(B, T, H, Dk, Dv, chunk, _dt(dtype))
-
-
-def overlap_kernel_count(B, T, H, Dk, Dv, chunk=64, dtype=torch.bfloat16) -> int:
-    return load().kda_chunk_fwd_overlap_kernel_count(B, T, H, Dk, Dv, chunk, _dt(dtype))
-
-
 def _event_handles(events):
     for e in events:
         if e.cuda_event == 0:  # torch creates the HIP event on its first record
@@ -151,27 +137,14 @@ def _event_handles(events):
     return (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
 
 
-class Overlap:
-    """The auxiliary stream and the synchronisation events of the overlapped
-    schedule (kda_chunk_fwd_overlap); reuse one per thread of calls."""
-
-    def __init__(self, device=None):
-        self.stream = torch.cuda.Stream(device=device)
-        self.sync = [torch.cuda.Event() for _ in range(OVERLAP_SYNC_EVENTS)]
-
-
 def chunk_fwd(q, k, v, z, beta_raw, A_log, S0=None, *, chunk=64, g_min=-5.0,
               flags=FLAGS_DEFAULT, want_M=False, want_P=False, o=None, S_out=None,
-              M_out=None, P_out=None, workspace=None, events=None, overlap=None, dt_bias=None):
+              M_out=None, P_out=None, workspace=None, events=None, dt_bias=None):
     """Chunkwise KDA forward.  Returns (o, S_out) plus M and/or P when asked.
 
-    `events` (optional): a list of torch.cuda.Event(enable_timing=True).
-    Sequential schedule (kda_chunk_fwd_timed): at least kernel_count(...) + 1;
-    events[0] is recorded before the first kernel and events[k + 1] after
-    kernel k.  Overlapped schedule: at least 2 * overlap_kernel_count(...);
-    events 2k and 2k + 1 bracket kernel k on its own stream.
-    `overlap` (optional): an Overlap; runs kda_chunk_fwd_overlap, the intra
-    kernels of the next slice beside the inter kernel of the current one.
+    `events` (optional): a list of torch.cuda.Event(enable_timing=True), at
+    least kernel_count(...) + 1 (kda_chunk_fwd_timed): events[0] is recorded
+    before the first kernel and events[k + 1] after kernel k.
     Grouped value heads (v, z, beta_raw with HV = a multiple of q's H heads)
     or a gate bias `dt_bias` [HV, Dk] fp32 run kda_chunk_fwd_grouped.
     """
@@ -179,8 +152,8 @@ def chunk_fwd(q, k, v, z, beta_raw, A_log, S0=None, *, chunk=64, g_min=-5.0,
     H = v.shape[2]
     Dv = v.shape[-1]
     grouped = Hq != H or dt_bias is not None
-    if grouped and (events is not None or overlap is not None):
-        raise ValueError("grouped heads / dt_bias run the plain one-stream call only")
+    if grouped and events is not None:
+        raise ValueError("grouped heads / dt_bias run the plain call only")
     dt = q.dtype
     dev = q.device
     if o is None:
@@ -191,7 +164,7 @@ def chunk_fwd(q, k, v, z, beta_raw, A_log, S0=None, *, chunk=64, g_min=-5.0,
         M_out = torch.empty(B, H, Dk, Dk, dtype=torch.float32, device=dev)
     if want_P and P_out is None:
         P_out = torch.empty(B, T, H, Dk, dtype=dt, device=dev)
-    need = (overlap_workspace_bytes if overlap is not None else workspace_bytes)(B, T, H, Dk, Dv, chunk, dt)
+    need = workspace_bytes(B, T, H, Dk, Dv, chunk, dt)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta_raw), _ptr(A_log), _ptr(S0),
@@ -204,17 +177,41 @@ def chunk_fwd(q, k, v, z, beta_raw, A_log, S0=None, *, chunk=64, g_min=-5.0,
                  B, T, Hq, H, Dk, Dv, chunk, g_min, flags, _dt(dt),
                  _ptr(workspace), workspace.numel(), _stream(dev))
         _check("kda_chunk_fwd_grouped", load().kda_chunk_fwd_grouped(*gargs))
-    elif overlap is not None:
-        sync = _event_handles(overlap.sync)
-        evs = _event_handles(events) if events is not None else None
-        _check("kda_chunk_fwd_overlap",
-               load().kda_chunk_fwd_overlap(*args, overlap.stream.cuda_stream, sync, len(overlap.sync),
-                                            evs, len(events) if events is not None else 0))
     elif events is None:
         _check("kda_chunk_fwd", load().kda_chunk_fwd(*args))
     else:
         evs = _event_handles(events)
         _check("kda_chunk_fwd_timed", load().kda_chunk_fwd_timed(*args, evs, len(events)))
+    out = [o, S_out]
+    if want_M:
+        out.append(M_out)
+    if want_P:
+        out.append(P_out)
+    return tuple(out)
+
+
+def chunk_fwd_noalloc(q, k, v, z, beta_raw, A_log, S0=None, *, chunk=64, g_min=-5.0,
+                      flags=FLAGS_DEFAULT, want_M=False, want_P=False, o=None, S_out=None,
+                      M_out=None, P_out=None):
+    """kda_chunk_fwd_noalloc: chunk_fwd without a workspace (the library's
+    built-in device scratch; calls on one GPU must not overlap in time).
+    Outputs not passed are allocated here by torch, before the call."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    dev = q.device
+    if o is None:
+        o = torch.empty(B, T, H, Dv, dtype=dt, device=dev)
+    if S_out is None:
+        S_out = torch.empty(B, H, Dk, Dv, dtype=torch.float32, device=dev)
+    if want_M and M_out is None:
+        M_out = torch.empty(B, H, Dk, Dk, dtype=torch.float32, device=dev)
+    if want_P and P_out is None:
+        P_out = torch.empty(B, T, H, Dk, dtype=dt, device=dev)
+    _check("kda_chunk_fwd_noalloc",
+           load().kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta_raw), _ptr(A_log), _ptr(S0),
+                                        _ptr(o), _ptr(S_out), _ptr(M_out), _ptr(P_out),
+                                        B, T, H, Dk, Dv, chunk, g_min, flags, _dt(dt), _stream(dev)))
     out = [o, S_out]
     if want_M:
         out.append(M_out)

@@ -45,11 +45,10 @@ typedef enum {
     KDA_ERR_SHAPE = 2,     /* unsupported or negative size, or bad chunk         */
     KDA_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned                   */
     KDA_ERR_DTYPE = 4,     /* unknown dtype or unknown switch bits               */
-    KDA_ERR_GATE = 5,      /* g_min not finite/negative, or the 16-token factor
-                              tile exceeds kda_safe_chunk_size(g_min, dt)
-                              (bounded gate only)                                */
+    KDA_ERR_GATE = 5,      /* g_min not finite or not negative (bounded gate)  */
     KDA_ERR_WORKSPACE = 6, /* workspace NULL, misaligned or too small           */
-    KDA_ERR_HIP = 7        /* a kernel launch failed                             */
+    KDA_ERR_HIP = 7,       /* a kernel launch failed                             */
+    KDA_ERR_SCRATCH = 8    /* kda_chunk_fwd_noalloc: sizes beyond its scratch   */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -78,7 +77,11 @@ enum {
  * below dtype_max / 2^10: floor(ln(dtype_max / 2^10) / -g_min)
  * ("KDA 模块交互式演示" §1.4 safe_chunk_size; Tab 9).  Returns 16 for g_min = -5
  * with either dtype, 8 for g_min = -10, and -1 for a non-finite or
- * non-negative g_min or an unknown dtype.  Host only; no HIP call. */
+ * non-negative g_min or an unknown dtype.  Host only; no HIP call.
+ * kda_chunk_fwd factors the decay of 16-token tiles; when this returns less
+ * than 16 for the call's bounded gate it evaluates every tile whose decay
+ * leaves the factored range element by element (the path the unbounded v1
+ * gate takes), so any finite negative g_min is accepted. */
 int kda_safe_chunk_size(float g_min, kda_dtype dt);
 
 /* Bytes of device workspace kda_chunk_fwd needs for these sizes (0 for invalid
@@ -128,36 +131,29 @@ kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, cons
                                void* workspace, size_t workspace_bytes, hipStream_t stream,
                                hipEvent_t* events, int n_events);
 
-/* The same computation as kda_chunk_fwd on two streams: the intra-chunk
- * kernel of the next slice of the sequence runs on `stream` while the
- * inter-chunk kernel of the current slice runs on `aux_stream` (the serial
- * inter-chunk chain leaves most of the GPU idle).  The sequence is cut into
- * two slices; the workspace holds both
- * (kda_chunk_fwd_overlap_workspace).  Results equal kda_chunk_fwd's bit for
- * bit.  Ordering: all work queued on `stream` before the call happens first,
- * and work queued on `stream` after it sees every output.  `aux_stream` must
- * not be used by anything else until that point.
- *   sync_events    5 caller-created events (n_sync_events >= 5), used for the
- *                  cross-stream dependencies; calls sharing them must not run
- *                  concurrently.
- *   timing_events  nullable: events 2k and 2k + 1 are recorded on the stream
- *                  of kernel k just before and after it (kernels alternate
- *                  intra, inter over the slices);
- *                  n_timing_events >= 2 * kda_chunk_fwd_overlap_kernel_count().
- * Returns KDA_OK, a validation error, or KDA_ERR_NULL for missing events. */
-size_t kda_chunk_fwd_overlap_workspace(int B, int T, int H, int Dk, int Dv, int chunk,
-                                       kda_dtype dt);
-int kda_chunk_fwd_overlap_kernel_count(int B, int T, int H, int Dk, int Dv, int chunk,
-                                       kda_dtype dt);
-kda_status kda_chunk_fwd_overlap(const void* q, const void* k, const void* v, const void* z,
+/* kda_chunk_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, computation, validation and results as kda_chunk_fwd
+ * without the workspace.  The per-chunk blocks and the state carried between
+ * slices of the sequence live in a built-in device buffer of 64 MiB that every
+ * GPU the library runs on holds until the process ends; the sequence is cut
+ * into as many slices as that buffer requires.  The call allocates nothing
+ * and calls no allocating routine; its first call on a device looks up that
+ * device's buffer address.
+ *   Limit: B * H * (blk + Dk * (Dk + Dv) * 4) <= 64 MiB, with blk the bytes
+ *   of one chunk block (29 184 for bf16, Dk = 128, chunk 32; 66 048 at chunk
+ *   64; 57 856 for fp32 at chunk 32), rounded as in kda_chunk_fwd_workspace;
+ *   e.g. B * H <= 418 at Dk = Dv = 128, chunk 32, bf16.  Larger sizes return
+ *   KDA_ERR_SCRATCH and enqueue nothing.
+ *   Every call on a GPU uses that GPU's one buffer: calls that can overlap in
+ *   time on one GPU (different streams, or host threads sharing a stream
+ *   without ordering) race and give wrong results.  Calls issued in order on
+ *   one stream are safe; nothing in the buffer needs to start at zero. */
+kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* z,
                                  const void* beta_raw, const float* A_log, const float* S0,
                                  void* o, float* S_out, float* M_out, void* P_out,
                                  int B, int T, int H, int Dk, int Dv, int chunk,
-                                 float g_min, unsigned flags, kda_dtype dt,
-                                 void* workspace, size_t workspace_bytes,
-                                 hipStream_t stream, hipStream_t aux_stream,
-                                 hipEvent_t* sync_events, int n_sync_events,
-                                 hipEvent_t* timing_events, int n_timing_events);
+                                 float g_min, unsigned flags, kda_dtype dt, hipStream_t stream);
 
 /* One decode step per (b,h), state updated IN PLACE ("KDA 模块交互式演示" §1.7
  * kda_step; "Implémenter KDA" reference step): decay, erase along k, write,
@@ -198,7 +194,7 @@ kda_status kda_step_grouped(const void* q, const void* k, const void* v, const v
  *   S_prefix[s] = M[s] S_prev + S_tilde[s],  S_prev = (s ? S_prefix[s-1] : S_in).
  *   M [n_seg,B,H,Dk,Dk], S_tilde and S_prefix [n_seg,B,H,Dk,Dv], all fp32;
  *   S_in nullable [B,H,Dk,Dv] (NULL = zero).  S_prefix must not overlap the
- *   inputs. */
+ *   inputs (KDA_ERR_SHAPE). */
 kda_status kda_segment_compose(int n_seg, const float* M, const float* S_tilde,
                                const float* S_in, float* S_prefix,
                                int B, int H, int Dk, int Dv, hipStream_t stream);
@@ -255,7 +251,6 @@ kda_status kda_short_conv(const void* x, const float* w, const float* bias,
 kda_status kda_output_gate(const void* o, const void* gate, const float* weight, void* y,
                            int B, int T, int H, int Dv, kda_dtype dt, hipStream_t stream);
 
-/* Static description of a status code. */
 /* Backward of kda_chunk_fwd (training).  The pages give the forward only; this
  * is its derivative, for a loss L with dL/do = dout and dL/dS_T = dS_T:
  *   dq, dk, dz [B,T,H,Dk] and dv [B,T,H,Dv], dbeta_raw [B,T,H]: device, dtype
@@ -272,7 +267,8 @@ kda_status kda_output_gate(const void* o, const void* gate, const float* weight,
  * factor in one exponent (exact for any log-decay).  The workspace
  * (kda_chunk_bwd_workspace bytes, 256-byte aligned) holds the per-chunk
  * operators, the state at each chunk start and the state adjoint at each
- * chunk end.  Outputs must not overlap inputs.  Errors as kda_chunk_fwd. */
+ * chunk end.  Outputs may overlap neither an input, another output nor the
+ * workspace (KDA_ERR_SHAPE).  Errors otherwise as kda_chunk_fwd. */
 size_t kda_chunk_bwd_workspace(int B, int T, int H, int Dk, int Dv);
 kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* z,
                          const void* beta_raw, const float* A_log, const float* S0,
@@ -302,6 +298,7 @@ kda_status kda_chunk_bwd_grouped(const void* q, const void* k, const void* v, co
                                  kda_dtype dt, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream);
 
+/* Static description of a status code (never NULL). */
 const char* kda_status_string(kda_status s);
 
 #ifdef __cplusplus

@@ -61,12 +61,17 @@ def test_workspace_sizes(lib):
 
 
 def test_status_strings(lib):
-    for s in range(8):
+    for s in range(9):
         assert len(kda.status_string(s)) > 0
     assert kda.status_string(99) == "unknown status"
 
 
 A16 = 0x10000  # an aligned fake device address; never dereferenced (validation fails first)
+
+
+def addr(i):
+    """Distinct aligned fake device addresses, 4 GiB apart (no two buffers overlap)."""
+    return A16 + (i << 32)
 
 
 def chunk_call(lib, **kw):
@@ -86,7 +91,7 @@ def test_chunk_fwd_validation(lib):
     assert chunk_call(lib, chunk=128) == 2
     assert chunk_call(lib, T=-1) == 2
     assert chunk_call(lib, g_min=0.0) == 5
-    assert chunk_call(lib, g_min=-10.0) == 5          # 16-token tile unsafe at g_min = -10
+    assert chunk_call(lib, g_min=-10.0) == 6          # accepted (element-wise tiles), then the workspace
     assert chunk_call(lib, g_min=float("nan")) == 5
     # the v1 gate bit: only with the in-kernel gate, and it does not use g_min
     assert chunk_call(lib, flags=16) == 4
@@ -128,40 +133,15 @@ def test_compose_and_fixup_validation(lib):
     assert lib.kda_segment_compose(2, None, A16, None, A16, 1, 1, 64, 64, None) == 1
     assert lib.kda_segment_compose(2, A16, A16, A16 + 4, A16, 1, 1, 64, 64, None) == 3
     assert lib.kda_segment_compose(0, None, None, None, None, 1, 1, 64, 64, None) == 0
+    # S_prefix may not overlap M, S_tilde or S_in
+    M, St, Sin = addr(1), addr(2), addr(3)
+    seg_bytes = 2 * 64 * 64 * 4
+    assert lib.kda_segment_compose(2, M, St, Sin, M + seg_bytes - 256, 1, 1, 64, 64, None) == 2
+    assert lib.kda_segment_compose(2, M, St, Sin, St, 1, 1, 64, 64, None) == 2
+    assert lib.kda_segment_compose(2, M, St, Sin, Sin - 1024, 1, 1, 64, 64, None) == 2
     assert lib.kda_segment_fixup(2, A16, None, None, A16, 1, 64, 1, 64, 64, 1, None) == 1
     assert lib.kda_segment_fixup(2, A16, None, A16, A16, 1, 64, 1, 64, 64, 9, None) == 4
     assert lib.kda_segment_fixup(1, A16, None, None, A16, 1, 0, 1, 64, 64, 1, None) == 0
-
-
-def test_overlap_workspace_and_counts(lib):
-    per = 64 * 1024 + 512   # bf16 D=128 C=64 block
-    carry = lambda bh, dk, dv: bh * dk * (dk + dv) * 4
-    # 64 chunks -> two slices of 32 chunks, two slice buffers
-    assert lib.kda_chunk_fwd_overlap_workspace(4, 4096, 16, 128, 128, 64, 1) == 2 * 64 * 32 * per + carry(64, 128, 128)
-    assert lib.kda_chunk_fwd_overlap_kernel_count(4, 4096, 16, 128, 128, 64, 1) == 4
-    # 3 chunks -> slices of at least 2 chunks
-    assert lib.kda_chunk_fwd_overlap_kernel_count(1, 130, 1, 128, 128, 64, 1) == 4
-    assert lib.kda_chunk_fwd_overlap_kernel_count(1, 0, 1, 128, 128, 64, 1) == 1
-    assert lib.kda_chunk_fwd_overlap_workspace(1, 64, 1, 96, 128, 64, 1) == 0
-    # the one-stream workspace holds one slice: the whole sequence when it fits
-    assert lib.kda_chunk_fwd_workspace(4, 4096, 16, 128, 128, 64, 1) == 64 * 64 * per + carry(64, 128, 128)
-
-
-def test_overlap_validation(lib):
-    sync = (ctypes.c_void_p * 5)(*([A16] * 5))
-    def call(**kw):
-        a = dict(q=A16, k=A16, v=A16, z=A16, beta_raw=A16, A_log=A16, S0=None, o=A16,
-                 S_out=None, M_out=None, P_out=None, B=1, T=64, H=1, Dk=64, Dv=64, chunk=64,
-                 g_min=-5.0, flags=7, dt=1, ws=None, ws_bytes=0, stream=None, aux=None,
-                 sync=sync, n_sync=5, timing=None, n_timing=0)
-        a.update(kw)
-        return lib.kda_chunk_fwd_overlap(*a.values())
-    assert call(sync=None) == 1
-    assert call(n_sync=4) == 1
-    assert call(dt=5) == 4
-    assert call(Dk=48) == 2
-    assert call(ws=None, ws_bytes=1 << 20) == 6
-    assert call(B=0) == 0
 
 
 def test_short_conv_validation(lib):
@@ -229,8 +209,9 @@ def test_grouped_validation(lib):
 
 
 def bwd_call(lib, **kw):
-    a = dict(q=A16, k=A16, v=A16, z=A16, beta_raw=A16, A_log=A16, S0=None, dout=A16, dS_T=None,
-             dq=A16, dk=A16, dv=A16, dz=A16, dbeta_raw=A16, dA_log=A16, dS0=None,
+    a = dict(q=addr(1), k=addr(2), v=addr(3), z=addr(4), beta_raw=addr(5), A_log=addr(6), S0=None, dout=addr(7),
+             dS_T=None, dq=addr(8), dk=addr(9), dv=addr(10), dz=addr(11), dbeta_raw=addr(12), dA_log=addr(13),
+             dS0=None,
              B=1, T=64, H=2, Dk=64, Dv=64, g_min=-5.0, flags=7, dt=1, ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return lib.kda_chunk_bwd(*a.values())
@@ -256,17 +237,25 @@ def test_backward_workspace_and_validation(lib):
     assert bwd_call(lib, dA_log=None) == 1
     assert bwd_call(lib, A_log=None) == 1
     assert bwd_call(lib, flags=3, A_log=None) == 6             # no gate: A_log optional
-    assert bwd_call(lib, dq=A16 + 4) == 3
-    assert bwd_call(lib, dS0=A16 + 8) == 3
-    assert bwd_call(lib, ws=A16, ws_bytes=need - 1) == 6
-    assert bwd_call(lib, ws=A16 + 16, ws_bytes=need) == 6
+    assert bwd_call(lib, dq=addr(8) + 4) == 3
+    assert bwd_call(lib, dS0=addr(14) + 8) == 3
+    # outputs overlapping an input, another output or the workspace
+    assert bwd_call(lib, dq=addr(1)) == 2
+    assert bwd_call(lib, dv=addr(7) + 16) == 2
+    assert bwd_call(lib, dz=addr(8)) == 2
+    assert bwd_call(lib, dS0=addr(20), S0=addr(20) + 4096) == 2
+    assert bwd_call(lib, dA_log=addr(30), ws=addr(30) - 256, ws_bytes=need) == 2
+    assert bwd_call(lib, dS0=addr(14), S0=addr(15)) == 6
+    assert bwd_call(lib, ws=addr(40), ws_bytes=need - 1) == 6
+    assert bwd_call(lib, ws=addr(40) + 16, ws_bytes=need) == 6
     assert bwd_call(lib, H=0) == 0
 
 
 def test_backward_grouped_validation(lib):
     def call(**kw):
-        a = dict(q=A16, k=A16, v=A16, z=A16, beta_raw=A16, A_log=A16, dt_bias=A16, S0=None, dout=A16, dS_T=None,
-                 dq=A16, dk=A16, dv=A16, dz=A16, dbeta_raw=A16, dA_log=A16, ddt_bias=A16, dS0=None,
+        a = dict(q=addr(1), k=addr(2), v=addr(3), z=addr(4), beta_raw=addr(5), A_log=addr(6), dt_bias=addr(7),
+                 S0=None, dout=addr(8), dS_T=None, dq=addr(9), dk=addr(10), dv=addr(11), dz=addr(12),
+                 dbeta_raw=addr(13), dA_log=addr(14), ddt_bias=addr(15), dS0=None,
                  B=1, T=64, H=2, HV=6, Dk=64, Dv=64, g_min=-5.0, flags=7, dt=1, ws=None, ws_bytes=0, stream=None)
         a.update(kw)
         return lib.kda_chunk_bwd_grouped(*a.values())
@@ -279,4 +268,5 @@ def test_backward_grouped_validation(lib):
     assert call(ddt_bias=None) == 1      # a bias needs its gradient
     assert call(dt_bias=None, ddt_bias=None) == 6   # no bias: valid up to the workspace
     assert call() == 6
+    assert call(ddt_bias=addr(7)) == 2   # the bias gradient over the bias
     assert call(HV=0) == 0

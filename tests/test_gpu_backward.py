@@ -188,3 +188,21 @@ def test_backward_grouped_matches_oracle(dtype, H, HV, bias, T):
     for n in names:
         assert_close(g[n], ref[n], F32 if n in ("dA_log", "dS0", "ddt_bias") and dtype == F32 else dtype,
                      f"grouped H{H} HV{HV} {n}")
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_backward_strong_bounded_gate(dtype):
+    """g_min = -10: the 16-token factored tile is unsafe (kda_safe_chunk_size
+    returns 8); the backward takes every decay factor in one exponent and is
+    accepted and exact for it."""
+    flags = kda.FLAGS_DEFAULT
+    inp, do, dST = case(2, 90, 2, 64, 64, dtype, 4242, flags)
+    inp["z"] = (inp["z"].float() * 2.0 + 3.0).to(inp["z"].dtype)
+    dev = {k_: (None if v_ is None else v_.cuda().contiguous()) for k_, v_ in inp.items()}
+    g = kda.chunk_bwd(dev["q"], dev["k"], dev["v"], dev["z"], dev["beta_raw"], dev["A_log"], do.cuda(),
+                      dev["S0"], dST.cuda(), flags=flags, g_min=-10.0)
+    torch.cuda.synchronize()
+    ref = ora.backward(*(np64(inp[n]) for n in ("q", "k", "v", "z", "beta_raw", "A_log")), np64(do),
+                       np64(dST), np64(inp["S0"]), g_min=-10.0, flags=flags)
+    for n in NAMES:
+        assert_close(g[n], ref[n], F32 if n in ("dA_log", "dS0") and dtype == F32 else dtype, f"g_min -10 {n}")

@@ -133,3 +133,28 @@ def test_v1_gate_grouped_with_bias(dtype):
                                        np64(S0), flags=V1)
     assert_close(o, o_ref, dtype, "v1 grouped o")
     assert_close(S, S_ref, dtype, "v1 grouped S")
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("g_min,Dk,Dv,chunk,T", [
+    (-10.0, 64, 64, 32, 150),
+    (-10.0, 128, 128, 64, 130),
+    (-20.0, 32, 16, 16, 77),
+    (-5.5, 128, 64, 32, 100),
+])
+def test_strong_bounded_gate_matches_oracle(dtype, g_min, Dk, Dv, chunk, T):
+    """A bounded gate whose 16-token factored tile is unsafe
+    (kda_safe_chunk_size(g_min) < 16, "KDA 模块交互式演示" §1.4) is accepted:
+    tiles that leave the factored range are evaluated element by element.
+    Logits shifted up so that most tokens decay close to g_min."""
+    inp = inputs.make_inputs(2, T, 2, Dk, Dv, "bf16" if dtype == BF16 else "f32", seed=T + Dk + int(-g_min),
+                             a_std=0.5, s_std=0.3)
+    inp["z"] = (inp["z"].float() * 2.0 + 3.0).to(inp["z"].dtype)
+    assert kda.safe_chunk_size(g_min, dtype) < 16
+    d = to_dev(inp)
+    o, S = kda.chunk_fwd(d["q"], d["k"], d["v"], d["z"], d["beta_raw"], d["A_log"], d["S0"], chunk=chunk,
+                         g_min=g_min)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_forward(inp, g_min=g_min)
+    assert_close(o, o_ref, dtype, f"g_min {g_min} o")
+    assert_close(S, S_ref, dtype, f"g_min {g_min} S")
