@@ -42,6 +42,10 @@ __global__ __launch_bounds__(256) void kda_step_kernel(const StepArgs a) {
         const floatx4 t = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(Sp + (size_t)(rg + RG * m) * DV) + cg);
         Sr[m] = make_float4(t[0], t[1], t[2], t[3]);
     }
+    // this thread's four values, requested with the state so that no global
+    // load waits after the reductions (the workgroup lives one memory latency)
+    float vv[4];
+    load4(reinterpret_cast<const T*>(a.v) + (size_t)bh * DV + col0 + 4 * cg, vv);
 
     if (tid < 64) {
         // value head h reads q/k head h / G of the same batch row
@@ -121,12 +125,11 @@ __global__ __launch_bounds__(256) void kda_step_kernel(const StepArgs a) {
         ss.x += y.x; ss.y += y.y; ss.z += y.z; ss.w += y.w;
     }
     const float beta = s_misc[0], qk = s_misc[1];
-    const T* vp = reinterpret_cast<const T*>(a.v) + (size_t)bh * DV + col0 + 4 * cg;
     float4 u;
-    u.x = beta * (to_f<T>(vp[0]) - rr.x);
-    u.y = beta * (to_f<T>(vp[1]) - rr.y);
-    u.z = beta * (to_f<T>(vp[2]) - rr.z);
-    u.w = beta * (to_f<T>(vp[3]) - rr.w);
+    u.x = beta * (vv[0] - rr.x);
+    u.y = beta * (vv[1] - rr.y);
+    u.z = beta * (vv[2] - rr.z);
+    u.w = beta * (vv[3] - rr.w);
     if (rg == 0) {
         T* op = reinterpret_cast<T*>(a.o) + (size_t)bh * DV + col0 + 4 * cg;
         op[0] = from_f<T>(ss.x + u.x * qk);
