@@ -337,8 +337,21 @@ def bench_layer_body(torch, kda, inputs, steps, warmup, chunk):
         full(i)
         gate(i)
 
+    cw_all = torch.cat([cw["q"], cw["k"], cw["v"]]).contiguous()
+    cb_all = torch.cat([cb["q"], cb["k"], cb["v"]]).contiguous()
+
+    def fused_core(i):
+        s = sets[i % len(sets)]
+        kda.chunk_fwd_conv(s["q"], s["k"], s["v"], s["z"], s["beta_raw"], A, cw_all, cb_all, None, None,
+                           chunk=chunk, o=o, S_out=S, workspace=ws)
+
+    def fused_body(i):
+        fused_core(i)
+        gate(i)
+
     res = {}
-    for name, fn in (("convs", convs), ("input_side_and_core", full), ("output_gate", gate), ("body", body)):
+    for name, fn in (("convs", convs), ("input_side_and_core", full), ("output_gate", gate), ("body", body),
+                     ("fused_input_side_and_core", fused_core), ("fused_body", fused_body)):
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
@@ -361,7 +374,11 @@ def bench_layer_body(torch, kda, inputs, steps, warmup, chunk):
             "output_gate_us": round(res["output_gate"] * 1e3, 2),
             "output_gate_hbm_frac": round(gate_bytes / (res["output_gate"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
             "layer_body_ms": round(res["body"], 4),
-            "layer_body_tokens_per_s": B * T / (res["body"] / 1e3)}
+            "layer_body_tokens_per_s": B * T / (res["body"] / 1e3),
+            "fused_input_side_and_core_ms": round(res["fused_input_side_and_core"], 4),
+            "fused_layer_body_ms": round(res["fused_body"], 4),
+            "fused_layer_body_tokens_per_s": B * T / (res["fused_body"] / 1e3),
+            "fused": "kda_chunk_fwd_conv: the short convolutions and SiLU inside the chunk kernels, then the output side"}
 
 
 def bench_grouped(torch, kda, steps, warmup, chunk):

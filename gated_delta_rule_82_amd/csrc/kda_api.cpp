@@ -105,7 +105,9 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
                                  float g_min, unsigned flags, kda_dtype dt,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream,
                                  hipEvent_t* ev, int n_ev,
-                                 int G = 1, const float* dt_bias = nullptr, bool noalloc = false) {
+                                 int G = 1, const float* dt_bias = nullptr, bool noalloc = false,
+                                 const float* conv_w = nullptr, const float* conv_b = nullptr,
+                                 const void* conv_state = nullptr) {
     if (!dtype_ok(dt) || !flags_ok(flags)) return KDA_ERR_DTYPE;
     if (dt_bias && !(flags & KDA_GATE_IN_KERNEL)) return KDA_ERR_DTYPE;  // it biases the in-kernel gate
     if (chunk == 0) chunk = 64;
@@ -122,6 +124,7 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
     }
     KDA_TRY(maybe(S0)); KDA_TRY(maybe(S_out)); KDA_TRY(maybe(M_out)); KDA_TRY(maybe(P_out));
     KDA_TRY(maybe(dt_bias));
+    if (conv_w) { KDA_TRY(maybe(conv_b)); KDA_TRY(maybe(conv_state)); }
     size_t slice_budget = kda::kSliceBytes;
     if (noalloc) {
         // one chunk block of every (b, h) and the carried state must fit the
@@ -147,6 +150,7 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
     a.G = G; a.dt_bias = dt_bias;
     a.wide_decay = wide_decay(g_min, flags, dt);
     a.slice_budget = slice_budget;
+    a.conv_w = conv_w; a.conv_b = conv_b; a.conv_state = conv_state;
     if (ev) {
         const int need = kda::chunk_kernel_count(elem_bytes(dt), Dk, chunk, B * H, a.NC) + 1;
         if (n_ev < need) return KDA_ERR_NULL;
@@ -179,6 +183,18 @@ kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, cons
     if (!events) return KDA_ERR_NULL;
     return chunk_fwd_impl(q, k, v, z, beta_raw, A_log, S0, o, S_out, M_out, P_out, B, T, H, Dk, Dv,
                           chunk, g_min, flags, dt, workspace, workspace_bytes, stream, events, n_events);
+}
+
+kda_status kda_chunk_fwd_conv(const void* q, const void* k, const void* v, const void* z,
+                              const void* beta_raw, const float* A_log, const float* S0,
+                              const float* conv_w, const float* conv_b, const void* conv_state,
+                              void* o, float* S_out, int B, int T, int H, int Dk, int Dv, int chunk,
+                              float g_min, unsigned flags, kda_dtype dt,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (B > 0 && H > 0) KDA_TRY(need(conv_w));
+    return chunk_fwd_impl(q, k, v, z, beta_raw, A_log, S0, o, S_out, nullptr, nullptr, B, T, H, Dk, Dv,
+                          chunk, g_min, flags, dt, workspace, workspace_bytes, stream, nullptr, 0, 1, nullptr, false,
+                          conv_w, conv_b, conv_state);
 }
 
 kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* z,

@@ -59,6 +59,12 @@ struct IntraArgs {
     int c0, nc;          // chunks [c0, c0 + nc) of every (b, h) in this launch
     float g_min;
     unsigned flags;
+    // fused input-side convolution (CONV instantiations): kernel-4 taps and
+    // biases of the q and k channels ([Hk DK][4] / [Hk DK], biases nullable)
+    // and the carried window [B][3][cstride] (nullable: zeros) whose rows hold
+    // the q channels at offset 0 and the k channels at offset qk_off
+    const float* cw_q; const float* cw_k; const float* cb_q; const float* cb_k;
+    const void* cstate; int cstride, qk_off;
 };
 
 __host__ __device__ constexpr int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }
@@ -66,7 +72,9 @@ __host__ __device__ constexpr int pair_index(int I, int J) { return I * (I - 1) 
 // GENERAL: the kernel for the unbounded v1 gate and for caller-supplied
 // log-decays (any g <= 0); the bounded in-kernel gate, which the library only
 // accepts when the factored products stay in range, takes the plain kernel.
-template <typename T, int DK, int C, bool GENERAL>
+// CONV: q and k are the raw inputs of the layer's short convolution; the
+// kernel forms SiLU(ShortConv_4(.)) of each before everything else.
+template <typename T, int DK, int C, bool GENERAL, bool CONV = false>
 __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     constexpr BlockLayout L = block_layout(sizeof(T), DK, C);
     constexpr int NBK = C / 16;
@@ -92,6 +100,8 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     // per chunk of the workgroup:
     __shared__ __align__(16) float s_tot_all[NCH][NBK][DK];     // block totals of the log2 decay
     __shared__ float s_beta_all[NCH][C];
+    __shared__ __align__(16) float4 s_cw[CONV ? 2 : 1][CONV ? DK : 1];  // conv taps of q, k channels
+    __shared__ float s_cb[CONV ? 2 : 1][CONV ? DK : 1];
     // phases B to E; the input staging of phase A shares their space (it is
     // dead once phase A's barrier is passed)
     struct PhaseArrays {
@@ -194,9 +204,27 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
                             (__attribute__((address_space(3))) void*)(stage + tn * 16 * RB + p * 1024), 16, 0, kCopyNT);
                 }
             }
-            wait_vmcnt<0>();  // this wave's copies are in LDS (it reads only its own rows)
-            asm volatile("" ::: "memory");
+            if constexpr (!CONV) {
+                wait_vmcnt<0>();  // this wave's copies are in LDS (it reads only its own rows)
+                asm volatile("" ::: "memory");
+            }
         }
+    }
+    if constexpr (CONV) {
+        // taps and biases of the head's q and k channels into LDS; every wave
+        // waits for its copies, then a barrier makes all staged rows (the
+        // previous block's rows are this block's window) and the taps visible
+        if (threadIdx.x < 2 * DK) {
+            const int tt = threadIdx.x / DK, c = threadIdx.x % DK;
+            const float* cw = tt ? a.cw_k : a.cw_q;
+            const float* cb = tt ? a.cb_k : a.cb_q;
+            const float4 wv = reinterpret_cast<const float4*>(cw)[(size_t)hq * DK + c];
+            const float bv = cb ? cb[(size_t)hq * DK + c] : 0.f;
+            s_cw[tt][c] = wv;
+            s_cb[tt][c] = bv;
+        }
+        wait_vmcnt<0>();
+        lds_barrier();
     }
 #pragma unroll
     for (int s = 0; s < KSD; ++s) {
@@ -227,6 +255,75 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
                 for (int i = 0; i < 4; ++i) dz[i] = 0.f;
             }
         }
+    }
+    if constexpr (CONV) {
+        // SiLU(ShortConv_4(x)) of q and k at this lane's token t = 16 I + r and
+        // channels.  x[t - 3] comes from this wave's staged row r - 3, the
+        // previous wave's row 13 + r, or (the workgroup's first three tokens,
+        // and the fp32 path) global memory, the carried window or zero for
+        // t - 3 < 0; x[t - 1] and x[t - 2] are the neighbouring lanes' x, or
+        // their x[t - 3] where the row runs out.  Values are rounded to the
+        // input type as if the convolution had been stored.
+        const int tok0 = n * C + 16 * I;           // token of row 0 of this block
+        const int tm3 = tok0 + r - 3;              // this lane's x[t - 3]
+        Raw4<T> yq[2 * KSD], yk[2 * KSD];
+#pragma unroll
+        for (int s2 = 0; s2 < KSD; ++s2) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int c = 32 * s2 + 16 * hf + 4 * gq;
+                const int e = 2 * s2 + hf;
+                yq[e].zero();
+                yk[e].zero();
+                if (!active || !(DK >= 32 || hf == 0)) continue;
+                bool done = false;
+                if constexpr (kStage) {
+                    const int rw = r >= 3 ? r - 3 : 13 + r;
+                    const unsigned char* st = r >= 3 ? stage : (w > 0 ? sh.stage + (w - 1) * kStageWave : nullptr);
+                    if (st) {
+                        const int off = rw * RB + (((c / 8) ^ (rw % LPR)) * 16) + (c % 8) * 2;
+                        yq[e].v = *reinterpret_cast<const uint2*>(st + off);
+                        yk[e].v = *reinterpret_cast<const uint2*>(st + 16 * RB + off);
+                        done = true;
+                    }
+                }
+                if (!done) {
+                    if (tm3 >= 0) {
+                        const size_t rr = ((size_t)b * a.T + (tm3 < a.T ? tm3 : a.T - 1)) * Hk + hq;
+                        yq[e].load(reinterpret_cast<const T*>(a.q) + rr * DK + c);
+                        yk[e].load(reinterpret_cast<const T*>(a.k) + rr * DK + c);
+                    } else if (a.cstate) {
+                        const T* srow = reinterpret_cast<const T*>(a.cstate) + ((size_t)b * 3 + 3 + tm3) * a.cstride;
+                        yq[e].load(srow + (size_t)hq * DK + c);
+                        yk[e].load(srow + a.qk_off + (size_t)hq * DK + c);
+                    }
+                }
+            }
+        }
+        auto conv_tensor = [&](Raw4<T> (&x)[2 * KSD], const Raw4<T> (&y)[2 * KSD], int tt) {
+#pragma unroll
+            for (int e = 0; e < 2 * KSD; ++e) {
+                if (!(DK >= 32 || e % 2 == 0)) continue;  // channels that exist (the rest stay zero)
+                Raw4<T> x1, x2;  // x[t - 1], x[t - 2]
+#pragma unroll
+                for (int wd = 0; wd < Raw4<T>::kWords; ++wd) {
+                    const uint32_t xw = x[e].word(wd), yw = y[e].word(wd);
+                    const uint32_t a1 = row_shr_word(xw, 1), b1 = row_shl_word(yw, 2);
+                    const uint32_t a2 = row_shr_word(xw, 2), b2 = row_shl_word(yw, 1);
+                    x1.set_word(wd, r >= 1 ? a1 : b1);
+                    x2.set_word(wd, r >= 2 ? a2 : b2);
+                }
+                const int c = 32 * (e / 2) + 16 * (e % 2) + 4 * gq;
+                float out[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    out[i] = silu_(conv4(s_cw[tt][c + i], s_cb[tt][c + i], y[e].get(i), x2.get(i), x1.get(i), x[e].get(i)));
+                }
+                x[e].set4(out);
+            }
+        };
+        conv_tensor(qr, yq, 0);
+        conv_tensor(kr, yk, 1);
     }
     {
         const float braw = to_f<T>(reinterpret_cast<const T*>(a.beta_raw)[row]);
@@ -611,6 +708,10 @@ struct InterArgs {
     int wsNC;            // chunk blocks per (b, h) in the workspace buffer, chunk c0 first
     int c0, nc;          // chunks [c0, c0 + nc) in this launch
     int n_m, n_strips, n_groups;
+    // fused input-side convolution of v (CONV instantiations): taps [H Dv][4],
+    // biases [H Dv] or NULL, carried window [B][3][cstride] or NULL with the
+    // v channels at offset v_off of each row
+    const float* cw_v; const float* cb_v; const void* cstate; int cstride, v_off;
 };
 
 constexpr size_t kLdsBudget = 160 * 1024;  // LDS per CU on gfx950
@@ -683,7 +784,7 @@ __device__ __forceinline__ void wait_chunks(int m) {
 //     operand fragment from LDS once for all its strips, stores o directly,
 //     and never waits on global loads.
 // One fence-free barrier per chunk hands a slot over.
-template <typename T, int DK, int C, int NW, int SPW>
+template <typename T, int DK, int C, int NW, int SPW, bool CONV = false>
 __global__ __launch_bounds__(64 * (NW + 2)) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void kda_inter_kernel(const InterArgs a) {
     constexpr int NS = NW * SPW;
@@ -894,6 +995,32 @@ void kda_inter_kernel(const InterArgs a) {
     // chunk n + 1 while chunk n's output is computed.
     Frag<T> Ak[NBK][KSD], At[NBK][KSC];
     uint32_t Vraw[SPW][NBK * 4];
+    // fused convolution of v: this lane's column's taps and bias per strip, and
+    // the raw values of the three tokens before the chunk being read
+    float4 cvw[SPW];
+    float cvb[SPW];
+    uint32_t vprev[SPW][3];
+    if constexpr (CONV) {
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) {
+            const int col = (live[j] && !mstrip[j]) ? col0[j] + r : 0;
+            const size_t ch = (size_t)h * a.Dv + col;
+            cvw[j] = reinterpret_cast<const float4*>(a.cw_v)[ch];
+            cvb[j] = a.cb_v ? a.cb_v[ch] : 0.f;
+#pragma unroll
+            for (int p = 0; p < 3; ++p) {
+                const int tt = a.c0 * C - 3 + p;
+                Raw x = 0;
+                if (tt >= 0)
+                    x = *reinterpret_cast<const Raw*>(reinterpret_cast<const T*>(a.v) +
+                                                      (((size_t)b * a.T + tt) * a.H + h) * a.Dv + col);
+                else if (a.cstate)
+                    x = *reinterpret_cast<const Raw*>(reinterpret_cast<const T*>(a.cstate) +
+                                                      ((size_t)b * 3 + 3 + tt) * a.cstride + a.v_off + ch);
+                vprev[j][p] = (uint32_t)x;
+            }
+        }
+    }
     auto load_serial = [&](int n) {
         const unsigned char* cur = slot_of(n);
         const T* s_blk = reinterpret_cast<const T*>(cur);
@@ -909,12 +1036,38 @@ void kda_inter_kernel(const InterArgs a) {
                 if (2 * s <= Ib) frag_load(At[Ib][s], s_blk + L.tb + (size_t)(Ib * KSC + s) * 512, lane);
 #pragma unroll
         for (int j = 0; j < SPW; ++j) {
+            if constexpr (CONV) {
+                // SiLU(ShortConv_4(v)) of tokens 16 J + 4 gq + i: the window
+                // reaches three tokens back, into the previous chunk (vprev)
+                // for the first rows; rounded to the input type as if stored
 #pragma unroll
-            for (int J = 0; J < NBK; ++J)
+                for (int J = 0; J < NBK; ++J) {
+                    float x[7];
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    Vraw[j][4 * J + i] =
-                        (uint32_t)*reinterpret_cast<const Raw*>(s_val + (16 * J + 4 * gq + i) * Ring::kVRow + vlane[j]);
+                    for (int p = 0; p < 7; ++p) {
+                        const int tt = 16 * J + 4 * gq + p - 3;
+                        const int tr = tt >= 0 ? tt : 0;
+                        const uint32_t raw = (uint32_t)*reinterpret_cast<const Raw*>(s_val + tr * Ring::kVRow + vlane[j]);
+                        const uint32_t pv = tt == -3 ? vprev[j][0] : tt == -2 ? vprev[j][1] : vprev[j][2];
+                        x[p] = RawBits<T>::to_float((Raw)(tt >= 0 ? raw : pv));
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const T yv = (T)silu_(conv4(cvw[j], cvb[j], x[i], x[i + 1], x[i + 2], x[i + 3]));
+                        Vraw[j][4 * J + i] = (uint32_t)__builtin_bit_cast(Raw, yv);
+                    }
+                }
+#pragma unroll
+                for (int p = 0; p < 3; ++p)
+                    vprev[j][p] = (uint32_t)*reinterpret_cast<const Raw*>(s_val + (C - 3 + p) * Ring::kVRow + vlane[j]);
+            } else {
+#pragma unroll
+                for (int J = 0; J < NBK; ++J)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        Vraw[j][4 * J + i] =
+                            (uint32_t)*reinterpret_cast<const Raw*>(s_val + (16 * J + 4 * gq + i) * Ring::kVRow + vlane[j]);
+            }
         }
     };
 
@@ -1055,13 +1208,14 @@ void kda_inter_kernel(const InterArgs a) {
     }
 }
 
-// One instantiation of the inter kernel: NW compute waves of one strip each.
-template <typename T, int DK, int C, int NW>
+// One instantiation of the inter kernel: NW compute waves of one strip each
+// (CONV: with the fused convolution of v).
+template <typename T, int DK, int C, int NW, bool CONV = false>
 struct InterKernel {
     using Ring = InterRing<T, DK, C, NW>;
     static constexpr int kThreads = 64 * (NW + 2);
     static constexpr size_t kLds = (size_t)Ring::kSlots * Ring::kSlot + Ring::kOBytes;
-    static const void* fn() { return reinterpret_cast<const void*>(kda_inter_kernel<T, DK, C, NW, 1>); }
+    static const void* fn() { return reinterpret_cast<const void*>(kda_inter_kernel<T, DK, C, NW, 1, CONV>); }
     static hipError_t set_attributes() {
         // set on every call: the attribute is per device, and the call only records a limit
         return hipFuncSetAttribute(fn(), hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
@@ -1084,7 +1238,7 @@ struct InterKernel {
         return v;
     }
     static hipError_t launch(const InterArgs& ea, int BH, hipStream_t s) {
-        hipLaunchKernelGGL((kda_inter_kernel<T, DK, C, NW, 1>), dim3((unsigned)BH * ea.n_groups), dim3(kThreads),
+        hipLaunchKernelGGL((kda_inter_kernel<T, DK, C, NW, 1, CONV>), dim3((unsigned)BH * ea.n_groups), dim3(kThreads),
                            kLds, s, ea);
         return hipGetLastError();
     }
@@ -1130,8 +1284,23 @@ struct ChunkLaunch {
             }
         }
         ea.n_groups = (ea.n_strips + nw - 1) / nw;
+        if (a.conv_w) {
+            const int Hk = a.H / a.G;
+            ea.cw_v = a.conv_w + (size_t)2 * Hk * DK * 4;
+            ea.cb_v = a.conv_b ? a.conv_b + (size_t)2 * Hk * DK : nullptr;
+            ea.cstate = a.conv_state;
+            ea.cstride = 2 * Hk * DK + a.H * a.Dv;
+            ea.v_off = 2 * Hk * DK;
+        }
     }
     hipError_t set_attributes() const {
+        if (a.conv_w) {
+            switch (nw) {
+                case 1: return InterKernel<T, DK, C, 1, true>::set_attributes();
+                case 2: return InterKernel<T, DK, C, 2, true>::set_attributes();
+                default: return InterKernel<T, DK, C, 4, true>::set_attributes();
+            }
+        }
         switch (nw) {
             case 1: return InterKernel<T, DK, C, 1>::set_attributes();
             case 2: return InterKernel<T, DK, C, 2>::set_attributes();
@@ -1142,10 +1311,24 @@ struct ChunkLaunch {
     hipError_t intra(void* buf, int per, int c0, int nc, hipStream_t s) const {
         IntraArgs ia{a.q, a.k, a.z, a.beta_raw, a.A_log, buf, a.T, a.H, a.G, a.dt_bias, per, c0, nc, a.g_min, a.flags};
         const dim3 grid((unsigned)(BH * ((nc + NCH - 1) / NCH)));
-        if (a.wide_decay)
+        if (a.conv_w) {
+            const int Hk = a.H / a.G;
+            ia.cw_q = a.conv_w;
+            ia.cw_k = a.conv_w + (size_t)Hk * DK * 4;
+            ia.cb_q = a.conv_b;
+            ia.cb_k = a.conv_b ? a.conv_b + (size_t)Hk * DK : nullptr;
+            ia.cstate = a.conv_state;
+            ia.cstride = 2 * Hk * DK + a.H * a.Dv;
+            ia.qk_off = Hk * DK;
+            if (a.wide_decay)
+                hipLaunchKernelGGL((kda_intra_kernel<T, DK, C, true, true>), grid, dim3(256), 0, s, ia);
+            else
+                hipLaunchKernelGGL((kda_intra_kernel<T, DK, C, false, true>), grid, dim3(256), 0, s, ia);
+        } else if (a.wide_decay) {
             hipLaunchKernelGGL((kda_intra_kernel<T, DK, C, true>), grid, dim3(256), 0, s, ia);
-        else
+        } else {
             hipLaunchKernelGGL((kda_intra_kernel<T, DK, C, false>), grid, dim3(256), 0, s, ia);
+        }
         return hipGetLastError();
     }
     // inter kernel over the same chunks; the state enters from S0/M0 (first
@@ -1157,6 +1340,13 @@ struct ChunkLaunch {
         ea.M0 = first ? nullptr : M_scr;
         ea.S_out = last ? a.S_out : S_scr;
         ea.M_out = last ? a.M_out : M_scr;
+        if (a.conv_w) {
+            switch (nw) {
+                case 1: return InterKernel<T, DK, C, 1, true>::launch(ea, BH, s);
+                case 2: return InterKernel<T, DK, C, 2, true>::launch(ea, BH, s);
+                default: return InterKernel<T, DK, C, 4, true>::launch(ea, BH, s);
+            }
+        }
         switch (nw) {
             case 1: return InterKernel<T, DK, C, 1>::launch(ea, BH, s);
             case 2: return InterKernel<T, DK, C, 2>::launch(ea, BH, s);

@@ -116,12 +116,9 @@ __global__ __launch_bounds__(kThreads) void kda_short_conv_kernel(const ShortCon
 #pragma unroll
                 for (int i = 0; i < kChan; ++i) {
                     const float cur = rows[u].get(i);
-                    float s = bias[i];
-                    s = fmaf(w[i][0], win[0][i], s);
-                    s = fmaf(w[i][1], win[1][i], s);
-                    s = fmaf(w[i][2], win[2][i], s);
-                    s = fmaf(w[i][3], cur, s);
-                    out[i] = a.silu ? s * sigmoidf_(s) : s;
+                    const float s = conv4(make_float4(w[i][0], w[i][1], w[i][2], w[i][3]), bias[i], win[0][i],
+                                          win[1][i], win[2][i], cur);
+                    out[i] = a.silu ? silu_(s) : s;
                     win[0][i] = win[1][i];
                     win[1][i] = win[2][i];
                     win[2][i] = cur;

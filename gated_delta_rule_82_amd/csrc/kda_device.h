@@ -50,6 +50,31 @@ template <typename T> __device__ __forceinline__ T from_f(float x);
 template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float x) { return (bf16_t)x; }
 
+// Causal kernel-4 short convolution of one channel: bias + w.x x[t-3] +
+// w.y x[t-2] + w.z x[t-1] + w.w x[t], summed in this order with fused
+// multiply-adds (the standalone input-side kernel and the convolution fused
+// into the chunk kernels share it, so they produce the same values).
+__device__ __forceinline__ float conv4(const float4 w, float bias, float x3, float x2, float x1, float x0) {
+    float s = bias;
+    s = fmaf(w.x, x3, s);
+    s = fmaf(w.y, x2, s);
+    s = fmaf(w.z, x1, s);
+    s = fmaf(w.w, x0, s);
+    return s;
+}
+__device__ __forceinline__ float silu_(float s) { return s * sigmoidf_(s); }
+
+// 32-bit word of lane (row position r - d) within each 16-lane DPP row, for
+// d in {1, 2} (zero where it runs off the row), and of lane r + d.
+__device__ __forceinline__ uint32_t row_shr_word(uint32_t x, int d) {
+    return d == 1 ? (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true)
+                  : (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t row_shl_word(uint32_t x, int d) {
+    return d == 1 ? (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x101, 0xF, 0xF, true)
+                  : (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x102, 0xF, 0xF, true);
+}
+
 // Raw element bits, converted to float only when consumed.
 template <typename T> struct RawBits;
 template <> struct RawBits<bf16_t> {
@@ -65,6 +90,7 @@ template <> struct RawBits<float> {
 // widened to float where used, so they occupy half the registers until then.
 template <typename T> struct Raw4;
 template <> struct Raw4<bf16_t> {
+    static constexpr int kWords = 2;
     uint2 v;
     __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
     __device__ __forceinline__ void zero() { v = make_uint2(0u, 0u); }
@@ -72,12 +98,26 @@ template <> struct Raw4<bf16_t> {
         const uint32_t w = i < 2 ? v.x : v.y;
         return (i & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
     }
+    __device__ __forceinline__ uint32_t word(int i) const { return i ? v.y : v.x; }
+    __device__ __forceinline__ void set_word(int i, uint32_t x) { if (i) v.y = x; else v.x = x; }
+    // four values rounded to bf16 (round to nearest even)
+    __device__ __forceinline__ void set4(const float (&x)[4]) {
+        v.x = (uint32_t)__builtin_bit_cast(uint16_t, (bf16_t)x[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, (bf16_t)x[1]) << 16);
+        v.y = (uint32_t)__builtin_bit_cast(uint16_t, (bf16_t)x[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, (bf16_t)x[3]) << 16);
+    }
 };
 template <> struct Raw4<float> {
+    static constexpr int kWords = 4;
     float4 v;
     __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
     __device__ __forceinline__ void zero() { v = make_float4(0.f, 0.f, 0.f, 0.f); }
     __device__ __forceinline__ float get(int i) const { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
+    __device__ __forceinline__ uint32_t word(int i) const { return __float_as_uint(get(i)); }
+    __device__ __forceinline__ void set_word(int i, uint32_t x) {
+        const float f = __uint_as_float(x);
+        if (i == 0) v.x = f; else if (i == 1) v.y = f; else if (i == 2) v.z = f; else v.w = f;
+    }
+    __device__ __forceinline__ void set4(const float (&x)[4]) { v = make_float4(x[0], x[1], x[2], x[3]); }
 };
 
 // Load 4 consecutive elements (8-byte aligned for bf16, 16-byte for fp32).

@@ -84,6 +84,13 @@ struct ChunkArgs {
     const float* dt_bias = nullptr;   // [H, Dk] gate bias
     bool wide_decay = false;          // decays may leave the factored range: the GENERAL intra kernel
     size_t slice_budget = kSliceBytes;  // bytes of chunk blocks per slice of the sequence
+    // fused input-side convolution: q, k and v are the raw inputs of
+    // SiLU(ShortConv_4(.)); taps [Hk Dk + Hk Dk + H Dv][4] fp32 in the order q,
+    // k, v channels, biases of the same channels (nullable), carried window
+    // [B][3][channels] in the input type (nullable: zeros).  conv_w NULL: none.
+    const float* conv_w = nullptr;
+    const float* conv_b = nullptr;
+    const void* conv_state = nullptr;
 };
 
 // Built-in device scratch of the allocation-free chunk entry point (one copy

@@ -23,7 +23,7 @@ GATE_SOFTPLUS = 8  # with GATE_IN_KERNEL: the unbounded KDA v1 gate -exp(A_log) 
 
 EXPORTS = (
     "kda_safe_chunk_size", "kda_chunk_fwd_workspace", "kda_chunk_fwd", "kda_chunk_fwd_timed",
-    "kda_chunk_fwd_kernel_count", "kda_chunk_fwd_noalloc", "kda_step", "kda_chunk_fwd_grouped", "kda_step_grouped",
+    "kda_chunk_fwd_kernel_count", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_conv", "kda_step", "kda_chunk_fwd_grouped", "kda_step_grouped",
     "kda_segment_compose", "kda_segment_fixup", "kda_short_conv", "kda_output_gate",
     "kda_chunk_bwd_workspace", "kda_chunk_bwd", "kda_chunk_bwd_grouped_workspace", "kda_chunk_bwd_grouped",
     "kda_status_string",
@@ -60,6 +60,8 @@ def load() -> ctypes.CDLL:
     L.kda_chunk_fwd_kernel_count.restype = I
     L.kda_chunk_fwd_noalloc.argtypes = [P] * 11 + [I] * 6 + [F, U, I, P]
     L.kda_chunk_fwd_noalloc.restype = I
+    L.kda_chunk_fwd_conv.argtypes = [P] * 12 + [I] * 6 + [F, U, I, P, S, P]
+    L.kda_chunk_fwd_conv.restype = I
     L.kda_step.argtypes = [P] * 8 + [I] * 4 + [F, U, I, P]
     L.kda_step.restype = I
     L.kda_segment_compose.argtypes = [I, P, P, P, P, I, I, I, I, P]
@@ -188,6 +190,31 @@ def chunk_fwd(q, k, v, z, beta_raw, A_log, S0=None, *, chunk=64, g_min=-5.0,
     if want_P:
         out.append(P_out)
     return tuple(out)
+
+
+def chunk_fwd_conv(q, k, v, z, beta_raw, A_log, conv_w, conv_b=None, conv_state=None, S0=None, *, chunk=64,
+                   g_min=-5.0, flags=FLAGS_DEFAULT, o=None, S_out=None, workspace=None):
+    """kda_chunk_fwd_conv: the core on SiLU(ShortConv_4(.)) of the raw q, k, v.
+    conv_w [H*(2 Dk + Dv), 4] fp32 (q channels, then k, then v), conv_b the
+    same channels or None, conv_state [B, 3, H*(2 Dk + Dv)] in the input
+    dtype or None.  Returns (o, S_out)."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    dev = q.device
+    if o is None:
+        o = torch.empty(B, T, H, Dv, dtype=dt, device=dev)
+    if S_out is None:
+        S_out = torch.empty(B, H, Dk, Dv, dtype=torch.float32, device=dev)
+    need = workspace_bytes(B, T, H, Dk, Dv, chunk, dt)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check("kda_chunk_fwd_conv",
+           load().kda_chunk_fwd_conv(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta_raw), _ptr(A_log), _ptr(S0),
+                                     _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(o), _ptr(S_out),
+                                     B, T, H, Dk, Dv, chunk, g_min, flags, _dt(dt),
+                                     _ptr(workspace), workspace.numel(), _stream(dev)))
+    return o, S_out
 
 
 def chunk_fwd_noalloc(q, k, v, z, beta_raw, A_log, S0=None, *, chunk=64, g_min=-5.0,

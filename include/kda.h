@@ -131,6 +131,33 @@ kda_status kda_chunk_fwd_timed(const void* q, const void* k, const void* v, cons
                                void* workspace, size_t workspace_bytes, hipStream_t stream,
                                hipEvent_t* events, int n_events);
 
+/* kda_chunk_fwd with the layer's input-side short convolution fused into it
+ * ("KDA 模块交互式演示" §1.1 ShortConv and §1.7 完整层; "Implémenter KDA"
+ * 'La paramétrisation'): q, k and v are the raw inputs of the convolution and
+ * the core runs on
+ *   x'[b,t,c] = SiLU(bias[c] + sum_{j=0..3} w[c,j] * x[b, t-3+j, c])
+ * for each of q, k, v, with the values rounded to dt as if stored (so the
+ * call equals kda_short_conv of each followed by kda_chunk_fwd, bit for bit).
+ * The L2 norm of q', k' and every other switch act as in kda_chunk_fwd.
+ *   conv_w      [H*Dk + H*Dk + H*Dv, 4] fp32 device: the taps of the q
+ *               channels (head-major, [H][Dk]), then of the k channels, then
+ *               of the v channels; tap 3 multiplies the current token.
+ *   conv_b      [H*Dk + H*Dk + H*Dv] fp32 device (same channel order) or NULL.
+ *   conv_state  [B, 3, H*Dk + H*Dk + H*Dv] dtype dt device or NULL (zeros):
+ *               the three raw inputs before t = 0, oldest first (the window
+ *               kda_short_conv hands on).  The window after the call is the
+ *               last three raw inputs of (conv_state, x); the call does not
+ *               write it.
+ * Everything else as in kda_chunk_fwd without M_out and P_out (the same
+ * workspace).  KDA_ERR_NULL without conv_w, KDA_ERR_ALIGN when conv_w,
+ * conv_b or conv_state is not 16-byte aligned. */
+kda_status kda_chunk_fwd_conv(const void* q, const void* k, const void* v, const void* z,
+                              const void* beta_raw, const float* A_log, const float* S0,
+                              const float* conv_w, const float* conv_b, const void* conv_state,
+                              void* o, float* S_out, int B, int T, int H, int Dk, int Dv, int chunk,
+                              float g_min, unsigned flags, kda_dtype dt,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* kda_chunk_fwd for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Same arguments, computation, validation and results as kda_chunk_fwd

@@ -114,6 +114,29 @@ int main() {
                                  C, -5.f, 7, KDA_BF16, ws, wsn, nullptr),
            KDA_ERR_SHAPE, 0);
 
+    // ---- the fused input-side convolution: taps required, all 16-byte aligned
+    float* cw = (float*)buf((size_t)H * (2 * Dk + Dv) * 16);
+    float* cb = (float*)buf((size_t)H * (2 * Dk + Dv) * 4);
+    void* cs = buf((size_t)B * 3 * H * (2 * Dk + Dv) * 2);
+    EXPECT(kda_chunk_fwd_conv(q, k, v, z, br, A, nullptr, cw, cb, cs, o, S, B, T, H, Dk, Dv, C, -5.f, 7, KDA_BF16,
+                              ws, wsn, nullptr),
+           KDA_OK, 1);
+    EXPECT(kda_chunk_fwd_conv(q, k, v, z, br, A, nullptr, cw, nullptr, nullptr, o, S, B, T, H, Dk, Dv, C, -5.f, 7,
+                              KDA_BF16, ws, wsn, nullptr),
+           KDA_OK, 1);
+    EXPECT(kda_chunk_fwd_conv(q, k, v, z, br, A, nullptr, nullptr, cb, cs, o, S, B, T, H, Dk, Dv, C, -5.f, 7,
+                              KDA_BF16, ws, wsn, nullptr),
+           KDA_ERR_NULL, 0);
+    EXPECT(kda_chunk_fwd_conv(q, k, v, z, br, A, nullptr, cw + 1, cb, cs, o, S, B, T, H, Dk, Dv, C, -5.f, 7,
+                              KDA_BF16, ws, wsn, nullptr),
+           KDA_ERR_ALIGN, 0);
+    EXPECT(kda_chunk_fwd_conv(q, k, v, z, br, A, nullptr, cw, cb + 1, cs, o, S, B, T, H, Dk, Dv, C, -5.f, 7,
+                              KDA_BF16, ws, wsn, nullptr),
+           KDA_ERR_ALIGN, 0);
+    EXPECT(kda_chunk_fwd_conv(q, k, v, z, br, A, nullptr, cw, cb, (char*)cs + 2, o, S, B, T, H, Dk, Dv, C, -5.f, 7,
+                              KDA_BF16, ws, wsn, nullptr),
+           KDA_ERR_ALIGN, 0);
+
     // ---- the allocation-free entry point: its own size limit, no workspace
     EXPECT(kda_chunk_fwd_noalloc(q, k, v, z, br, A, nullptr, o, S, nullptr, nullptr, B, T, H, Dk, Dv, C, -5.f, 7,
                                  KDA_BF16, nullptr),

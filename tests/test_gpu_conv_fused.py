@@ -1,0 +1,177 @@
+"""GPU parity of the core with the layer's input-side convolution fused into
+it (kda_chunk_fwd_conv): SiLU(ShortConv_4(.)) of the raw q, k and v
+("KDA 模块交互式演示" §1.1 and §1.7; "Implémenter KDA" 'La paramétrisation')
+formed inside the chunk kernels.
+
+Two checks per case:
+  * bit for bit against the unfused pipeline through the C ABI
+    (kda_short_conv of q, k and v, then kda_chunk_fwd), since the fused path
+    rounds each convolved value to the input type as if it had been stored;
+  * against the fp64 oracle: ora.conv_silu of each input, rounded to the input
+    type the same way, then ora.forward, to the bars of tests/kda_check.py.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_82_amd import inputs, kda
+from oracle import kda_oracle as ora
+from tests.kda_check import assert_close, np64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+F32, BF16 = torch.float32, torch.bfloat16
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    kda.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def conv_params(B, H, Dk, Dv, dtype, seed, bias=True, state=True):
+    g = torch.Generator().manual_seed(seed)
+    Cc = H * (2 * Dk + Dv)
+    w = (torch.randn(Cc, 4, generator=g) * 0.5).float()
+    b = (torch.randn(Cc, generator=g) * 0.1).float() if bias else None
+    st = torch.randn(B, 3, Cc, generator=g).to(dtype) if state else None
+    return w, b, st
+
+
+def split(B, H, Dk, Dv, w, b, st):
+    """Per-tensor taps, biases and windows of the concatenated q | k | v channels."""
+    o1, o2 = H * Dk, 2 * H * Dk
+    ws = (w[:o1], w[o1:o2], w[o2:])
+    bs = (None, None, None) if b is None else (b[:o1], b[o1:o2], b[o2:])
+    ss = (None, None, None) if st is None else (st[:, :, :o1], st[:, :, o1:o2], st[:, :, o2:])
+    return ws, bs, ss
+
+
+def fused(d, w, b, st, chunk, flags=7, g_min=-5.0):
+    o, S = kda.chunk_fwd_conv(d["q"], d["k"], d["v"], d["z"], d["beta_raw"], d["A_log"], w.cuda(),
+                              None if b is None else b.cuda(), None if st is None else st.cuda(), d["S0"],
+                              chunk=chunk, flags=flags, g_min=g_min)
+    torch.cuda.synchronize()
+    return o, S
+
+
+def unfused(d, w, b, st, chunk, flags=7, g_min=-5.0):
+    B, T, H, Dk = d["q"].shape
+    Dv = d["v"].shape[-1]
+    ws, bs, ss = split(B, H, Dk, Dv, w, b, st)
+    xs = []
+    for x, wi, bi, si in zip((d["q"], d["k"], d["v"]), ws, bs, ss):
+        C = x.shape[2] * x.shape[3]
+        y = kda.short_conv(x.reshape(B, T, C), wi.contiguous().cuda(), None if bi is None else bi.contiguous().cuda(),
+                           state_in=None if si is None else si.contiguous().cuda(), silu=True)
+        xs.append(y.reshape(x.shape))
+    o, S = kda.chunk_fwd(xs[0], xs[1], xs[2], d["z"], d["beta_raw"], d["A_log"], d["S0"], chunk=chunk, flags=flags,
+                         g_min=g_min)
+    torch.cuda.synchronize()
+    return o, S
+
+
+def oracle(inp, w, b, st, dtype, flags=7, g_min=-5.0, heads=None, T=None, batch=None):
+    B, Tt, H, Dk = inp["q"].shape
+    Dv = inp["v"].shape[-1]
+    ws, bs, ss = split(B, H, Dk, Dv, w, b, st)
+    conv = []
+    for name, wi, bi, si in zip(("q", "k", "v"), ws, bs, ss):
+        x = inp[name]
+        D = x.shape[-1]
+        y, _ = ora.conv_silu(np64(x).reshape(B, Tt, H * D), np64(wi), np64(bi), np64(si))
+        # rounded to the input type, as the fused path stores it
+        y = torch.tensor(y).to(dtype).double().numpy().reshape(B, Tt, H, D)
+        conv.append(y)
+    q, k, v = conv
+    z, br, A, S0 = np64(inp["z"]), np64(inp["beta_raw"]), np64(inp["A_log"]), np64(inp["S0"])
+    if T is not None:
+        q, k, v, z, br = q[:, :T], k[:, :T], v[:, :T], z[:, :T], br[:, :T]
+    if batch is not None:
+        q, k, v, z, br = q[batch], k[batch], v[batch], z[batch], br[batch]
+        S0 = None if S0 is None else S0[batch]
+    if heads is not None:
+        q, k, v, z, br = q[:, :, heads], k[:, :, heads], v[:, :, heads], z[:, :, heads], br[:, :, heads]
+        A = A[heads]
+        S0 = None if S0 is None else S0[:, heads]
+    return ora.forward(q, k, v, z, br, A, S0, g_min, flags)
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("Dk,Dv,chunk,T,bias,state", [
+    (128, 128, 32, 200, True, True), (64, 64, 64, 130, True, False), (32, 64, 16, 77, False, True),
+    (16, 16, 16, 2, True, True), (128, 32, 32, 1, True, False), (64, 128, 64, 67, False, False),
+    (16, 128, 32, 33, True, True), (128, 16, 64, 100, True, True),
+])
+def test_fused_conv_equals_unfused_and_oracle(dtype, Dk, Dv, chunk, T, bias, state):
+    B, H = 2, 3
+    inp = inputs.make_inputs(B, T, H, Dk, Dv, "bf16" if dtype == BF16 else "f32", seed=T * 7 + Dk + Dv + chunk,
+                             a_std=0.5, s_std=0.2)
+    w, b, st = conv_params(B, H, Dk, Dv, dtype, seed=T + Dk, bias=bias, state=state)
+    d = to_dev(inp)
+    o_f, S_f = fused(d, w, b, st, chunk)
+    o_u, S_u = unfused(d, w, b, st, chunk)
+    assert torch.equal(o_f, o_u), "fused o differs from short_conv + chunk_fwd"
+    assert torch.equal(S_f, S_u), "fused S differs from short_conv + chunk_fwd"
+    o_ref, S_ref = oracle(inp, w, b, st, dtype)
+    assert_close(o_f, o_ref, dtype, f"fused o Dk{Dk} Dv{Dv} C{chunk} T{T}")
+    assert_close(S_f, S_ref, dtype, f"fused S Dk{Dk} Dv{Dv} C{chunk} T{T}")
+
+
+@pytest.mark.parametrize("flags", [3, 5, 15])
+def test_fused_conv_switches_and_v1_gate(flags):
+    """The beta and gate switches off (beta and the log-decay passed through)
+    and the unbounded v1 gate, which takes the element-wise intra kernel."""
+    B, T, H, D = 1, 90, 2, 64
+    inp = inputs.make_inputs(B, T, H, D, D, "f32", seed=500 + flags, a_std=0.5, s_std=0.2)
+    if not flags & kda.GATE_IN_KERNEL:
+        inp["z"] = -inp["z"].abs() * 0.5
+    if not flags & kda.BETA_SIGMOID:
+        inp["beta_raw"] = torch.sigmoid(inp["beta_raw"])
+    w, b, st = conv_params(B, H, D, D, F32, seed=flags)
+    d = to_dev(inp)
+    o_f, S_f = fused(d, w, b, st, 32, flags=flags)
+    o_u, S_u = unfused(d, w, b, st, 32, flags=flags)
+    assert torch.equal(o_f, o_u) and torch.equal(S_f, S_u)
+    o_ref, S_ref = oracle(inp, w, b, st, F32, flags=flags)
+    assert_close(o_f, o_ref, F32, f"fused flags {flags} o")
+    assert_close(S_f, S_ref, F32, f"fused flags {flags} S")
+
+
+def test_fused_conv_identity_taps_are_the_plain_core():
+    """Identity taps (last tap 1, no bias, "KDA 模块交互式演示" §1.1 恒等初始化)
+    make the convolution a no-op: SiLU of the inputs themselves."""
+    B, T, H, D = 2, 70, 2, 64
+    inp = inputs.make_inputs(B, T, H, D, D, "bf16", seed=9, a_std=0.5, s_std=0.2)
+    w = torch.zeros(H * 3 * D, 4)
+    w[:, 3] = 1.0
+    d = to_dev(inp)
+    o_f, S_f = fused(d, w, None, None, 32)
+    silu = lambda x: torch.nn.functional.silu(x.float()).to(x.dtype)
+    o_p, S_p = kda.chunk_fwd(silu(d["q"]), silu(d["k"]), silu(d["v"]), d["z"], d["beta_raw"], d["A_log"], d["S0"],
+                             chunk=32)
+    torch.cuda.synchronize()
+    # torch's SiLU and the kernel's may differ in the last bf16 bit; the bar
+    o_ref, S_ref = oracle(inp, w, None, None, BF16)
+    assert_close(o_f, o_ref, BF16, "identity taps o")
+    assert_close(o_p, o_ref, BF16, "identity taps o (plain core)")
+
+
+def test_fused_conv_layer_workload():
+    """B4 T4096 H16 D128 bf16 at the benchmarked chunk: equal to the unfused
+    pipeline bit for bit over the whole call, and the oracle on three (b, h)
+    pairs over all tokens."""
+    w_ = inputs.WORKLOADS["layer"]
+    inp = inputs.make_workload(w_)
+    w, b, st = conv_params(w_.B, w_.H, w_.Dk, w_.Dv, BF16, seed=4242)
+    d = to_dev(inp)
+    o_f, S_f = fused(d, w, b, st, 32)
+    o_u, S_u = unfused(d, w, b, st, 32)
+    assert torch.equal(o_f, o_u) and torch.equal(S_f, S_u)
+    for bb, h in ((0, 0), (2, 9), (3, 15)):
+        o_ref, S_ref = oracle(inp, w, b, st, BF16, heads=[h], batch=slice(bb, bb + 1))
+        assert_close(o_f[bb:bb + 1, :, h:h + 1], o_ref, BF16, f"fused layer o b{bb} h{h}")
+        assert_close(S_f[bb:bb + 1, h:h + 1], S_ref, BF16, f"fused layer S b{bb} h{h}")
