@@ -732,6 +732,29 @@ struct InterRing {
     static constexpr int kORow = 16 * NS * (int)sizeof(T);  // bytes of one token's output row
     static constexpr size_t kOTile = (size_t)C * kORow;
     static constexpr size_t kOBytes = 2 * kOTile;
+    // Bank-spread layouts.  A compute wave reads the values of tokens
+    // 4 gq + i (i fixed per instruction) and writes output rows r, so rows
+    // four apart must not share banks.  Values: a 1 KiB piece holds kVTok
+    // token rows of kVGran 16-byte granules; granule g of row u of the piece
+    // sits at granule position (u % 4) 16 + (u / 4) kVGran + g, so the rows
+    // 4 gq + i of one read fall on distinct banks.  Outputs: the tile is cut
+    // into 16-row blocks stored granule-column-major (granule og of row t at
+    // position og 16 + t % 16), so the 16 rows one write touches are distinct
+    // banks.
+    static constexpr int kVGran = kVRow / 16;  // granules per staged value row
+    static constexpr int kVTok = 64 / kVGran;  // value rows per piece
+    static constexpr int kOGran = kORow / 16;  // granules per output row
+    static_assert(kVTok % 4 == 0, "pieces hold whole groups of four rows");
+    // LDS offset (from the values of the slot) of byte lb of value row t
+    static __host__ __device__ constexpr uint32_t voff(int t, uint32_t lb) {
+        return (uint32_t)((t / kVTok) * 1024 +
+                          ((((t % kVTok) & 3) * 16 + ((t % kVTok) >> 2) * kVGran + (int)(lb >> 4)) << 4)) +
+               (lb & 15u);
+    }
+    // LDS offset (from the tile) of byte ob of output row t
+    static __host__ __device__ constexpr uint32_t ooff(int t, uint32_t ob) {
+        return (uint32_t)((t >> 4) * 16 * kORow + (((int)(ob >> 4) * 16 + (t & 15)) << 4)) + (ob & 15u);
+    }
     static constexpr int kBlkPieces = (int)((L.bytes + 1023) / 1024);
     static constexpr int kVPieces = (int)(kVBytes / 1024);
     static constexpr int kPieces = kBlkPieces + kVPieces;
@@ -828,15 +851,16 @@ void kda_inter_kernel(const InterArgs a) {
         const int cw = w - NW;
         const unsigned char* gblk = reinterpret_cast<const unsigned char*>(a.ws) + (size_t)bh * a.wsNC * L.bytes;
         const unsigned char* vsrc = reinterpret_cast<const unsigned char*>(a.v);
-        constexpr int kLanesPerRow = Ring::kVRow / 16;
-        constexpr int kTokPerPiece = 64 / kLanesPerRow;
-        const int vcol = vcol0 + (lane % kLanesPerRow) * (16 / (int)sizeof(T));
-        const int vcol_ld = vcol < 16 * vs1 ? vcol : 0;  // columns outside the range load any valid bytes
+        constexpr int kTokPerPiece = Ring::kVTok;
+        // lane L writes granule position L of a piece: row 4 ((L % 16) /
+        // kVGran) + L / 16 of the piece, granule (L % 16) % kVGran of the row
+        // (the inverse of Ring::voff)
+        const int vcol = vcol0 + ((lane % 16) % Ring::kVGran) * (16 / (int)sizeof(T));
+        const uint32_t vcol_b = (uint32_t)((vcol < 16 * vs1 ? vcol : 0) * (int)sizeof(T));  // columns outside the range load any valid bytes
         // values: a wave-uniform 64-bit base per chunk plus a 32-bit lane offset
         const uint32_t tstride = (uint32_t)(a.H * a.Dv * (int)sizeof(T));  // bytes per token
         const unsigned char* vrow0 = vsrc + (((size_t)b * a.T * a.H + h) * a.Dv) * sizeof(T);
-        const uint32_t vlane_tok = (uint32_t)(lane / kLanesPerRow);
-        const uint32_t vlane_col = (uint32_t)(vcol_ld * (int)sizeof(T));
+        const uint32_t vlane_tok = (uint32_t)(4 * ((lane % 16) / Ring::kVGran) + lane / 16);
         auto issue = [&](int n) {
             unsigned char* slot = slot_of(n);
             const unsigned char* gb = gblk + (size_t)(n - a.c0) * L.bytes;
@@ -859,7 +883,7 @@ void kda_inter_kernel(const InterArgs a) {
                     uint32_t tok = (uint32_t)(j * kTokPerPiece) + vlane_tok;
                     tok = tok < lim ? tok : lim - 1;
                     __builtin_amdgcn_global_load_lds(
-                        (const __attribute__((address_space(1))) void*)(vb + (tok * tstride + vlane_col)),
+                        (const __attribute__((address_space(1))) void*)(vb + (tok * tstride + vcol_b)),
                         (__attribute__((address_space(3))) void*)(slot + L.bytes + j * 1024), 16, 0, kCopyNT);
                 }
             }
@@ -945,11 +969,16 @@ void kda_inter_kernel(const InterArgs a) {
         vlane[j] = (live[j] && !mstrip[j]) ? (uint32_t)((col0[j] - vcol0 + r) * (int)sizeof(T)) : 0u;
         vmask[j] = (live[j] && !mstrip[j]) ? 0xffffffffu : 0u;
     }
+    // offset of row 16 J + 4 gq + i: voff(4 gq, lb) + voff(16 J, 0) + 256 i
+    uint32_t vlane_q[SPW];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) vlane_q[j] = Ring::voff(4 * gq, vlane[j]);
 
     // Outputs leave through the staging tiles: compute wave w stores tokens
     // [w C / NW, (w + 1) C / NW) of the previous chunk's tile, one 16-byte
-    // granule per lane and step.  Granule g of the wave's rows covers token
-    // g / kGpr, strip (g % kGpr) / kGps of the group, 16 bytes of it.
+    // granule per lane and step: step st, lane l takes granule og = g / kTpw
+    // of row g % kTpw of the wave's rows (g = 64 st + l), i.e. strip og / kGps
+    // of the group, 16 bytes of it.
     constexpr int kEpg = 16 / (int)sizeof(T);      // elements per granule
     constexpr int kGps = 16 / kEpg;                // granules per strip row
     constexpr int kGpr = NS * kGps;                // granules per token row
@@ -971,20 +1000,21 @@ void kda_inter_kernel(const InterArgs a) {
                         : nullptr;
     }
     auto store_rows = [&](int m) {  // rows of chunk m's tile owned by this wave
-        const unsigned char* tile = s_otile + (size_t)((m - a.c0) & 1) * Ring::kOTile + (size_t)w * kTpw * Ring::kORow;
+        const unsigned char* tile = s_otile + (size_t)((m - a.c0) & 1) * Ring::kOTile;
 #pragma unroll
         for (int st = 0; st < kOSteps; ++st) {
             const int gi = st * 64 + lane;
-            const int tok = w * kTpw + gi / kGpr;
-            const int sl = (gi % kGpr) / kGps;
-            const int part = gi % kGps;
+            const int tok = w * kTpw + gi % kTpw;
+            const int og = gi / kTpw;
+            const int sl = og / kGps;
+            const int part = og % kGps;
             unsigned char* base = nullptr;
             uint32_t stride = 0;
 #pragma unroll
             for (int t = 0; t < NS; ++t)
                 if (sl == t) { base = gbase[t]; stride = gstride[t]; }
             if (gi < kTpw * kGpr && base && m * C + tok < a.T) {
-                const uint4 v = *reinterpret_cast<const uint4*>(tile + (size_t)gi * 16);
+                const uint4 v = *reinterpret_cast<const uint4*>(tile + Ring::ooff(tok, (uint32_t)og * 16));
                 *reinterpret_cast<uint4*>(base + (size_t)m * C * stride + (uint32_t)tok * stride + (uint32_t)(part * 16)) = v;
             }
         }
@@ -1047,7 +1077,7 @@ void kda_inter_kernel(const InterArgs a) {
                     for (int p = 0; p < 7; ++p) {
                         const int tt = 16 * J + 4 * gq + p - 3;
                         const int tr = tt >= 0 ? tt : 0;
-                        const uint32_t raw = (uint32_t)*reinterpret_cast<const Raw*>(s_val + tr * Ring::kVRow + vlane[j]);
+                        const uint32_t raw = (uint32_t)*reinterpret_cast<const Raw*>(s_val + Ring::voff(tr, vlane[j]));
                         const uint32_t pv = tt == -3 ? vprev[j][0] : tt == -2 ? vprev[j][1] : vprev[j][2];
                         x[p] = RawBits<T>::to_float((Raw)(tt >= 0 ? raw : pv));
                     }
@@ -1059,14 +1089,14 @@ void kda_inter_kernel(const InterArgs a) {
                 }
 #pragma unroll
                 for (int p = 0; p < 3; ++p)
-                    vprev[j][p] = (uint32_t)*reinterpret_cast<const Raw*>(s_val + (C - 3 + p) * Ring::kVRow + vlane[j]);
+                    vprev[j][p] = (uint32_t)*reinterpret_cast<const Raw*>(s_val + Ring::voff(C - 3 + p, vlane[j]));
             } else {
 #pragma unroll
                 for (int J = 0; J < NBK; ++J)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         Vraw[j][4 * J + i] =
-                            (uint32_t)*reinterpret_cast<const Raw*>(s_val + (16 * J + 4 * gq + i) * Ring::kVRow + vlane[j]);
+                            (uint32_t)*reinterpret_cast<const Raw*>(s_val + Ring::voff(16 * J, 0) + 256 * i + vlane_q[j]);
             }
         }
     };
@@ -1180,11 +1210,10 @@ void kda_inter_kernel(const InterArgs a) {
                 // so the LDS streams while the matrix core works
                 if constexpr (kInterleave) interleave_mfma_ds<kMfmaPerChunk, kDsPerChunk>();
                 unsigned char* tile = s_otile + (size_t)((n - a.c0) & 1) * Ring::kOTile;
+                const uint32_t opos = Ring::ooff(r, (uint32_t)(((w * SPW + j) * 16 + 4 * gq) * (int)sizeof(T)));
 #pragma unroll
                 for (int Ib = 0; Ib < NBK; ++Ib)
-                    store4(reinterpret_cast<T*>(tile + (size_t)(16 * Ib + r) * Ring::kORow +
-                                                (size_t)((w * SPW + j) * 16 + 4 * gq) * sizeof(T)),
-                           acc[Ib]);
+                    store4(reinterpret_cast<T*>(tile + Ring::ooff(16 * Ib, 0) + opos), acc[Ib]);
             }
         }
         // the previous chunk's outputs (its tile was completed before the last barrier)
