@@ -740,7 +740,8 @@ struct InterRing {
     // 4 gq + i of one read fall on distinct banks.  Outputs: the tile is cut
     // into 16-row blocks stored granule-column-major (granule og of row t at
     // position og 16 + t % 16), so the 16 rows one write touches are distinct
-    // banks.
+    // banks; with 8-byte writes (bf16) rows 8-15 of a block also swap the two
+    // halves of their granules, so rows eight apart differ in bank too.
     static constexpr int kVGran = kVRow / 16;  // granules per staged value row
     static constexpr int kVTok = 64 / kVGran;  // value rows per piece
     static constexpr int kOGran = kORow / 16;  // granules per output row
@@ -752,8 +753,10 @@ struct InterRing {
                (lb & 15u);
     }
     // LDS offset (from the tile) of byte ob of output row t
+    static constexpr uint32_t kOHalf = sizeof(T) == 2 ? 8u : 0u;
     static __host__ __device__ constexpr uint32_t ooff(int t, uint32_t ob) {
-        return (uint32_t)((t >> 4) * 16 * kORow + (((int)(ob >> 4) * 16 + (t & 15)) << 4)) + (ob & 15u);
+        return (uint32_t)((t >> 4) * 16 * kORow + (((int)(ob >> 4) * 16 + (t & 15)) << 4)) +
+               ((ob & 15u) ^ (((t >> 3) & 1) ? kOHalf : 0u));
     }
     static constexpr int kBlkPieces = (int)((L.bytes + 1023) / 1024);
     static constexpr int kVPieces = (int)(kVBytes / 1024);
@@ -1014,7 +1017,8 @@ void kda_inter_kernel(const InterArgs a) {
             for (int t = 0; t < NS; ++t)
                 if (sl == t) { base = gbase[t]; stride = gstride[t]; }
             if (gi < kTpw * kGpr && base && m * C + tok < a.T) {
-                const uint4 v = *reinterpret_cast<const uint4*>(tile + Ring::ooff(tok, (uint32_t)og * 16));
+                uint4 v = *reinterpret_cast<const uint4*>(tile + (Ring::ooff(tok, (uint32_t)og * 16) & ~15u));
+                if (Ring::kOHalf && ((tok >> 3) & 1)) v = make_uint4(v.z, v.w, v.x, v.y);  // halves swapped in LDS
                 *reinterpret_cast<uint4*>(base + (size_t)m * C * stride + (uint32_t)tok * stride + (uint32_t)(part * 16)) = v;
             }
         }
