@@ -12,11 +12,11 @@
 
 namespace kda {
 
-template <typename T, int DK, int DV, int DVW>
-__global__ __launch_bounds__(256) void kda_step_kernel(const StepArgs a) {
+template <typename T, int DK, int DV, int DVW, int NTH>
+__global__ __launch_bounds__(NTH) void kda_step_kernel(const StepArgs a) {
     constexpr int NSPLIT = DV / DVW;                   // workgroups per (b, h)
     constexpr int CG = DVW / 4;                        // float4 column groups
-    constexpr int NT = (CG * DK < 256) ? CG * DK : 256;
+    constexpr int NT = (CG * DK < NTH) ? CG * DK : NTH;
     constexpr int RG = NT / CG;                        // row groups
     constexpr int RPT = DK / RG;                       // rows per thread
     constexpr int MC = (DK + 63) / 64;                 // channels per lane in the prep wave
@@ -148,15 +148,25 @@ __global__ __launch_bounds__(256) void kda_step_kernel(const StepArgs a) {
     }
 }
 
-// Value columns per workgroup: 64 at most (Dv = 128 takes two workgroups per
-// (b, h): half the registers per thread, twice the workgroups in flight).
+template <typename T, int DK, int DV, int DVW, int NTH>
+static hipError_t launch_step_x(const StepArgs& a, hipStream_t s) {
+    constexpr int CG = DVW / 4;
+    constexpr int NT = (CG * DK < NTH) ? CG * DK : NTH;
+    hipLaunchKernelGGL((kda_step_kernel<T, DK, DV, DVW, NTH>), dim3((unsigned)(a.B * a.H * (DV / DVW))), dim3(NT), 0, s, a);
+    return hipGetLastError();
+}
+
+// Dv = 128: one workgroup of 512 threads per (b, h), so each wave reads two
+// whole 512-byte state rows per instruction and the workgroup one contiguous
+// 64 KiB state (measured at B256 H32 D128: 189 us per step against 195 us
+// with two 64-column workgroups per (b, h), 197 us with 256 threads, 194-199
+// us for forms that keep three workgroups per CU resident instead of two).
+// Smaller Dv: 64 columns at most per workgroup of 256 threads.
 template <typename T, int DK, int DV>
 static hipError_t launch_step_t(const StepArgs& a, hipStream_t s) {
+    if constexpr (DV == 128) return launch_step_x<T, DK, DV, 128, 512>(a, s);
     constexpr int DVW = DV > 64 ? 64 : DV;
-    constexpr int CG = DVW / 4;
-    constexpr int NT = (CG * DK < 256) ? CG * DK : 256;
-    hipLaunchKernelGGL((kda_step_kernel<T, DK, DV, DVW>), dim3((unsigned)(a.B * a.H * (DV / DVW))), dim3(NT), 0, s, a);
-    return hipGetLastError();
+    return launch_step_x<T, DK, DV, DVW, 256>(a, s);
 }
 
 template <typename T, int DK>
