@@ -99,7 +99,7 @@ __global__ __launch_bounds__(512) void kda_compose_kernel(const ComposeArgs a) {
     }
 }
 
-constexpr int kFixTokens = 512;  // tokens per wave in kda_fixup
+constexpr int kFixTokens = 512;  // tokens per workgroup in kda_fixup
 constexpr int kFixBlocks = 2;    // 16-token blocks whose reads a fix-up wave has in flight together
 
 // 4 * NST consecutive elements of one o row: the part of a row one fix-up lane
@@ -149,55 +149,75 @@ template <typename T, int NST> struct ORun {
     }
 };
 
-// One wave per (segment, b, h, 512-token tile, group of NST value strips of
-// 16 columns).  It holds S_prev^T of its group as matrix-core A operands and,
-// per 16-token block, forms O^T = S^T P^T.  Both operands take channel
-// 32 s + 8 gq + j in contraction slot (gq, j) of step s, so each lane reads 16
-// contiguous bytes of a P row.  Row m of strip q's A operand is value column
-// 4 NST (m / 4) + 4 q + m % 4 of the group, which leaves lane (r, gq) of the
-// output with the 4 NST consecutive columns from 4 NST gq on of token r: one
-// contiguous read-modify-write per lane and token.
-template <typename T, int DK, int NST>
+// One workgroup per (segment, b, h, 512-token tile): four waves, NG groups
+// of NST value strips of 16 columns times 4 / NG token sub-tiles.  The
+// workgroup first copies S_prev of its (segment, b, h) into LDS transposed
+// (one row of DK channels per value column, coalesced 16-byte reads of the
+// fp32 state), then every wave takes S_prev^T of its group as matrix-core A
+// operands and, per 16-token block, forms O^T = S^T P^T.  Both operands take
+// channel 32 s + 8 gq + j in contraction slot (gq, j) of step s, so each lane
+// reads 16 contiguous bytes of a P row (and of an LDS column).  Row m of
+// strip q's A operand is value column 4 NST (m / 4) + 4 q + m % 4 of the
+// group, which leaves lane (r, gq) of the output with the 4 NST consecutive
+// columns from 4 NST gq on of token r: one contiguous read-modify-write per
+// lane and token.
+template <typename T, int DK, int NST, int NG>
 __global__ __launch_bounds__(256) void kda_fixup_kernel(const FixupArgs a) {
     constexpr int KSD = (DK + 31) / 32;
     constexpr int NB = kFixBlocks;
+    constexpr int SUB = 4 / NG;           // token sub-tiles per workgroup
+    constexpr int DV = 16 * NST * NG;     // value columns
+    constexpr int LD = DK + 8;            // elements per LDS column (16-byte aligned rows)
+    extern __shared__ __align__(16) unsigned char fix_raw[];
+    T* s_St = reinterpret_cast<T*>(fix_raw);
     const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
     const int r = lane & 15;
     const int gq = lane >> 4;
-    const int ngroup = a.Dv / (16 * NST);
     const int ntile = (a.T_seg + kFixTokens - 1) / kFixTokens;
-    const long long total = (long long)a.n_seg * a.B * a.H * ntile * ngroup;
-    const long long wid = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (wid >= total) return;  // no barriers in this kernel
-    long long x = wid;
-    const int grp = (int)(x % ngroup); x /= ngroup;
-    const int tt = (int)(x % ntile); x /= ntile;
+    // head index fastest: the workgroups that run together read and write
+    // whole token rows of P and o (all heads of the same tokens)
+    long long x = blockIdx.x;
     const int h = (int)(x % a.H); x /= a.H;
+    const int tt = (int)(x % ntile); x /= ntile;
     const int b = (int)(x % a.B); x /= a.B;
     const int sg = (int)x;
-    const float* Sprev = sg ? a.S_prefix + (((size_t)(sg - 1) * a.B + b) * a.H + h) * DK * a.Dv
-                            : (a.S_in ? a.S_in + ((size_t)b * a.H + h) * DK * a.Dv : nullptr);
-    if (!Sprev) return;
-    const int col0 = grp * 16 * NST;
+    const float* Sprev = sg ? a.S_prefix + (((size_t)(sg - 1) * a.B + b) * a.H + h) * DK * DV
+                            : (a.S_in ? a.S_in + ((size_t)b * a.H + h) * DK * DV : nullptr);
+    if (!Sprev) return;  // uniform over the workgroup, before its only barrier
 
+    // S_prev^T into LDS: element (row, col) of the state at s_St[col LD + row]
+    for (int i = threadIdx.x; i < DK * DV / 4; i += 256) {
+        const int row = i / (DV / 4), c4 = 4 * (i % (DV / 4));
+        const float4 v = reinterpret_cast<const float4*>(Sprev + (size_t)row * DV)[c4 / 4];
+        s_St[(c4 + 0) * LD + row] = (T)v.x;
+        s_St[(c4 + 1) * LD + row] = (T)v.y;
+        s_St[(c4 + 2) * LD + row] = (T)v.z;
+        s_St[(c4 + 3) * LD + row] = (T)v.w;
+    }
+    __syncthreads();
+
+    const int grp = w % NG;
+    const int sub = w / NG;
+    const int col0 = grp * 16 * NST;
     Frag<T> Sf[NST][KSD];
 #pragma unroll
     for (int q = 0; q < NST; ++q) {
         const int col = col0 + 4 * NST * (r >> 2) + 4 * q + (r & 3);
 #pragma unroll
-        for (int s = 0; s < KSD; ++s)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int rw = 32 * s + 8 * gq + j;
-                Sf[q][s].set(j, rw < DK ? Sprev[(size_t)rw * a.Dv + col] : 0.f);
-            }
+        for (int s = 0; s < KSD; ++s) {
+            if (32 * s + 8 * gq < DK) frag_load_row8(Sf[q][s], s_St + col * LD + 32 * s + 8 * gq);
+            else Sf[q][s].zero();
+        }
     }
 
     const T* P = reinterpret_cast<const T*>(a.P);
     T* o = reinterpret_cast<T*>(a.o);
     const size_t seg_row0 = ((size_t)sg * a.B + b) * a.T_seg;
-    const int tend = min(a.T_seg, (tt + 1) * kFixTokens);
-    for (int tok0 = tt * kFixTokens; tok0 < tend; tok0 += 16 * NB) {
+    constexpr int kSubTokens = kFixTokens / SUB;
+    const int tbeg = tt * kFixTokens + sub * kSubTokens;
+    const int tend = min(a.T_seg, tbeg + kSubTokens);
+    for (int tok0 = tbeg; tok0 < tend; tok0 += 16 * NB) {
         // all reads of the NB blocks go out before any product
         Frag<T> Pf[NB][KSD];
         ORun<T, NST> run[NB];
@@ -212,7 +232,7 @@ __global__ __launch_bounds__(256) void kda_fixup_kernel(const FixupArgs a) {
                     if (32 * s + 8 * gq < DK) frag_load_row8(Pf[u][s], prow + 32 * s + 8 * gq);
                     else Pf[u][s].zero();
                 }
-                run[u].load(o + row * a.Dv + col0 + 4 * NST * gq);
+                run[u].load(o + row * DV + col0 + 4 * NST * gq);
             }
         }
 #pragma unroll
@@ -226,7 +246,7 @@ __global__ __launch_bounds__(256) void kda_fixup_kernel(const FixupArgs a) {
                     for (int s = 0; s < KSD; ++s) acc = mma(Sf[q][s], Pf[u][s], acc);
                     run[u].put(q, acc);
                 }
-                if (tok < tend) run[u].store(o + ((seg_row0 + tok) * a.H + h) * a.Dv + col0 + 4 * NST * gq);
+                if (tok < tend) run[u].store(o + ((seg_row0 + tok) * a.H + h) * DV + col0 + 4 * NST * gq);
             }
         }
     }
@@ -245,29 +265,39 @@ hipError_t launch_compose(int DK, const ComposeArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename T, int NST>
-static hipError_t launch_fixup_n(int DK, const FixupArgs& a, hipStream_t s) {
+template <typename T, int DK, int NST, int NG>
+static hipError_t launch_fixup_g(const FixupArgs& a, hipStream_t s) {
+    constexpr size_t kLds = (size_t)16 * NST * NG * (DK + 8) * sizeof(T);
+    const auto fn = kda_fixup_kernel<T, DK, NST, NG>;
+    // set on every call: the attribute is per device, and the call only records a limit
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+    if (e != hipSuccess) return e;
     const long long ntile = (a.T_seg + kFixTokens - 1) / kFixTokens;
-    const long long waves = (long long)a.n_seg * a.B * a.H * (a.Dv / (16 * NST)) * ntile;
-    const unsigned grid = (unsigned)((waves + 3) / 4);
-    switch (DK) {
-        case 16: hipLaunchKernelGGL((kda_fixup_kernel<T, 16, NST>), dim3(grid), dim3(256), 0, s, a); break;
-        case 32: hipLaunchKernelGGL((kda_fixup_kernel<T, 32, NST>), dim3(grid), dim3(256), 0, s, a); break;
-        case 64: hipLaunchKernelGGL((kda_fixup_kernel<T, 64, NST>), dim3(grid), dim3(256), 0, s, a); break;
-        case 128: hipLaunchKernelGGL((kda_fixup_kernel<T, 128, NST>), dim3(grid), dim3(256), 0, s, a); break;
-        default: return hipErrorInvalidValue;
-    }
+    const unsigned grid = (unsigned)((long long)a.n_seg * a.B * a.H * ntile);
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(256), kLds, s, a);
     return hipGetLastError();
 }
 
-// strips per group: 4 (64 columns) where the value dimension allows, else all of it
+template <typename T, int DK>
+static hipError_t launch_fixup_v(const FixupArgs& a, hipStream_t s) {
+    // strips per group: 4 (64 columns) where the value dimension allows, else all of it
+    switch (a.Dv) {
+        case 16: return launch_fixup_g<T, DK, 1, 1>(a, s);
+        case 32: return launch_fixup_g<T, DK, 2, 1>(a, s);
+        case 64: return launch_fixup_g<T, DK, 4, 1>(a, s);
+        case 128: return launch_fixup_g<T, DK, 4, 2>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <typename T>
 static hipError_t launch_fixup_t(int DK, const FixupArgs& a, hipStream_t s) {
-    switch (a.Dv) {
-        case 16: return launch_fixup_n<T, 1>(DK, a, s);
-        case 32: return launch_fixup_n<T, 2>(DK, a, s);
-        case 64:
-        case 128: return launch_fixup_n<T, 4>(DK, a, s);
+    switch (DK) {
+        case 16: return launch_fixup_v<T, 16>(a, s);
+        case 32: return launch_fixup_v<T, 32>(a, s);
+        case 64: return launch_fixup_v<T, 64>(a, s);
+        case 128: return launch_fixup_v<T, 128>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
