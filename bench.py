@@ -11,10 +11,12 @@ cannot serve them.  The call is kda_chunk_fwd on one stream.  The state chunk is
 tiling choice of the kernels (results agree to rounding for 16, 32 and 64);
 32 is the fastest here.  The step time (value, ms_per_step) comes from the
 calls alone; the JSON line also reports, measured in the same run:
+  * per-call times (median, p10, p90) from an event pair around each call;
   * per-kernel times from HIP events the library records around each of its
-    kernels, over a second timed region of the same calls (the records add
-    GPU time between kernels: ms_per_step_with_kernel_events), and the
-    roofline of the dominant kernel per launch;
+    kernels, over a third timed region of the same calls (the records add
+    GPU time between kernels: ms_per_step_with_kernel_events);
+  * the roofline of the whole call (its compulsory bytes over the step time)
+    and the dominant kernel's own-byte rate per launch;
   * MFMA % of the whole call under both flop counts, HBM % on compulsory bytes;
   * the decode step (B=256, H=32, D=128, fp32 state) and its HBM %;
   * the long-context segmented flow (B=1, T=65536, H=32, 8 segments);
@@ -22,7 +24,8 @@ calls alone; the JSON line also reports, measured in the same run:
   * the layer body around the core: the input side (SiLU of the kernel-4
     short convolution of q, k, v), the output side (sigmoid gate times per-head
     RMS norm), each with its HBM %, and input side + core + output side;
-  * the fp64 oracle timed on the host cores on a bounded sample.
+  * the fp64 oracle timed on the host cores: the whole layer workload, the
+    first 2048 tokens of the long workload and 8 full decode steps.
 Only the JSON line goes to stdout; progress goes to stderr.
 """
 
@@ -148,6 +151,74 @@ def _oracle_slice(args):
     with threadpool_limits(1):
         ora.forward(q, k, v, z, br, A, None)
     return True
+
+
+def _oracle_decode_slice(args):
+    from threadpoolctl import threadpool_limits
+    from oracle import kda_oracle as ora
+    S, steps, A = args
+    with threadpool_limits(1):
+        for q, k, v, z, br in steps:
+            _, S = ora.step(S, q, k, v, z, br, A)
+    return True
+
+
+def _pool_run(fn, jobs):
+    import multiprocessing as mp
+    n_proc = min(max(1, min(16, len(os.sched_getaffinity(0)))), len(jobs))
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(n_proc) as pool:
+        pool.map(fn, jobs)
+    return time.perf_counter() - t0, n_proc
+
+
+def cpu_baseline_long(inputs, T_sample=2048):
+    """The fp64 oracle on the first T_sample tokens of the long workload (B1
+    H32 D128), one process per head group."""
+    w = inputs.WORKLOADS["long"]
+    inp = inputs.make_workload(w, T=T_sample)
+    f = lambda n: inp[n].double().numpy()
+    q, k, v, z, br = (f(n) for n in ("q", "k", "v", "z", "beta_raw"))
+    A = inp["A_log"].double().numpy()
+    H = q.shape[2]
+    hg = max(1, H // 16)
+    jobs = [(q[:, :, h:h + hg], k[:, :, h:h + hg], v[:, :, h:h + hg], z[:, :, h:h + hg], br[:, :, h:h + hg],
+             A[h:h + hg]) for h in range(0, H, hg)]
+    wall, n_proc = _pool_run(_oracle_slice, jobs)
+    return {"value": w.B * T_sample / wall, "unit": "tokens/s", "cores": n_proc,
+            "sample": f"long workload, all {w.B * H} heads, first {T_sample} of {w.T} tokens", "wall_s": round(wall, 3)}
+
+
+def cpu_baseline_decode(inputs, n_steps=8):
+    """n_steps full-size decode steps (B256 H32 D128) of the fp64 oracle, one
+    process per group of batch rows; per-step time."""
+    w = inputs.WORKLOADS["decode"]
+    S0, A_log = inputs.make_decode_state(w)
+    S = S0.double().numpy()
+    A = A_log.double().numpy()
+    steps = [inputs.make_decode_step(w, s) for s in range(n_steps)]
+    per = max(1, w.B // 16)
+    jobs = [(S[b:b + per], [tuple(st[n][b:b + per].double().numpy() for n in ("q", "k", "v", "z", "beta_raw"))
+                            for st in steps], A) for b in range(0, w.B, per)]
+    wall, n_proc = _pool_run(_oracle_decode_slice, jobs)
+    return {"us_per_step": round(wall / n_steps * 1e6, 1), "tokens_per_s": w.B * n_steps / wall, "cores": n_proc,
+            "sample": f"decode workload, {n_steps} full steps of B{w.B} H{w.H} D{w.Dk}", "wall_s": round(wall, 3)}
+
+
+def device_clocks(dev_index=0):
+    """Peak shader and memory clocks (MHz) and the CU count from the HIP runtime."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return {}
+    out = {}
+    # hipDeviceAttribute_t values of hip_runtime_api.h
+    for key, attr in (("clock_mhz", 5), ("mem_clock_mhz", 60), ("cus", 63)):
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, dev_index) == 0:
+            out[key] = v.value // 1000 if key.endswith("mhz") else v.value
+    return out
 
 
 def cpu_baseline(inp, T_sample, T_full):
@@ -281,9 +352,20 @@ def bench_decode(torch, kda, inputs, steps, warmup):
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
+    # each step timed on its own (event pair per launch)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        step(i)
+        b.record()
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
     nbytes = decode_bytes(w.B, w.H, w.Dk, w.Dv)
     return {"workload": "decode: B256 H32 Dk=Dv=128, bf16 q/k/v/z, fp32 state in place",
-            "steps": steps, "us_per_step": round(ms * 1e3, 2), "tokens_per_s": w.B / (ms / 1e3),
+            "steps": steps, "us_per_step": round(ms * 1e3, 2),
+            "us_per_step_each": {"median": round(percentile(per, 50), 2), "p10": round(percentile(per, 10), 2),
+                                 "p90": round(percentile(per, 90), 2)},
+            "tokens_per_s": w.B / (ms / 1e3),
             "hbm_gbs": nbytes / (ms / 1e3) / 1e9,
             "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
 
@@ -585,6 +667,9 @@ def main():
         wl = inputs.WORKLOADS["layer"]
         cpu = cpu_baseline(inputs.make_workload(wl, T=args.cpu_tokens), args.cpu_tokens, wl.T)
         log(f"[bench] oracle: {cpu['value']:.1f} tokens/s on {cpu['cores']} processes")
+        cpu["long_sample"] = cpu_baseline_long(inputs)
+        cpu["decode_sample"] = cpu_baseline_decode(inputs)
+        log(f"[bench] oracle long {cpu['long_sample']}, decode {cpu['decode_sample']}")
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     props = torch.cuda.get_device_properties(0)
@@ -676,7 +761,8 @@ def main():
                       "tile_count_at_run_chunk": round(f_full / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
         "hbm_frac_compulsory": round(cbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "cpu_baseline": cpu,
-        "device": {"name": props.name, "cus": props.multi_processor_count},
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+                   "cus": props.multi_processor_count, **{f"hip_{k}": v for k, v in device_clocks().items()}},
     }
     out.update(extra)
     print(json.dumps(out), flush=True)
