@@ -93,10 +93,15 @@ def chunk_bytes(B, T, H, Dk, Dv, esize=2):
 def block_bytes(Dk, C, esize=2):
     """Bytes of one per-chunk block the intra kernel hands to the inter kernel:
     Kd, Qp (C x Dk), KpT (Dk x C), Tb, Aqk (C x C) as 512-element operand tiles
-    (contraction padded to 32), the fp32 chunk decay (Dk), rounded to 256."""
+    (contraction steps of 32 tokens), of which tiles that are zero by
+    construction are not stored (Tb and Aqk: steps above the diagonal; the
+    diagonal step of an even row block, and a KpT step with no second 16
+    tokens, as half tiles), then the fp32 chunk decay (Dk), rounded to 256."""
     nbk, ksd, nbd, ksc = C // 16, (Dk + 31) // 32, Dk // 16, (C + 31) // 32
-    tiles = 2 * nbk * ksd + nbd * ksc + 2 * nbk * ksc
-    return (tiles * 512 * esize + Dk * 4 + 255) // 256 * 256
+    tri = sum((256 if 2 * s == ib else 512) for ib in range(nbk) for s in range(ksc) if 2 * s <= ib)
+    kpt = nbd * sum((256 if 2 * s + 1 >= nbk else 512) for s in range(ksc))
+    elems = 2 * nbk * ksd * 512 + kpt + 2 * tri
+    return (elems * esize + Dk * 4 + 255) // 256 * 256
 
 
 def kernel_bytes(B, T, H, Dk, Dv, C, esize=2):

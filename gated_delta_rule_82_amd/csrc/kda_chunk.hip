@@ -579,12 +579,9 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
                     floatx4 x = {0.f, 0.f, 0.f, 0.f};
                     x = mma(kp, e, x);
                     const float xv[4] = {x[0], x[1], x[2], x[3]};
-                    T* tile = ws + L.kpt + (size_t)(R * KSC + I / 2) * 512;
-                    half_store(tile, lane, I % 2, xv);
-                    if (I % 2 == 0 && I + 1 >= NBK) {
-                        const float zero4[4] = {0.f, 0.f, 0.f, 0.f};
-                        half_store(tile, lane, 1, zero4);
-                    }
+                    T* tile = ws + L.kpt + kpt_offset(R, I / 2, KSC, NBK);
+                    if (kpt_half(I / 2, NBK)) quarter_store(tile, lane, xv);  // no block I + 1: a half tile
+                    else half_store(tile, lane, I % 2, xv);
                 }
             }
             // keep each step's table reads next to their use (bounds live registers)
@@ -608,12 +605,11 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
             akkC[i] = (r < cc) ? akkC[i] * bc[i] : 0.f;
             I4[i] = (cc == r) ? 1.f : 0.f;
         }
-        T* aqk_tile = ws + L.aqk + (size_t)(I * KSC + I / 2) * 512;
-        half_store(aqk_tile, lane, I % 2, aq);
-        if (I % 2 == 0) {
-            const float zero4[4] = {0.f, 0.f, 0.f, 0.f};
-            half_store(aqk_tile, lane, 1, zero4);
-        }
+        // diagonal block: a half tile for even I (block I + 1 of the step lies
+        // above the diagonal), the second half of a full tile for odd I
+        T* aqk_tile = ws + L.aqk + tri_offset(I, I / 2, KSC);
+        if (I % 2 == 0) quarter_store(aqk_tile, lane, aq);
+        else half_store(aqk_tile, lane, 1, aq);
         // off-diagonal blocks J < I: entry (i, j) = sum_c rowside_I[i,c] pair[c] offb_J[j,c]
 #pragma unroll
         for (int J = 0; J < NBK - 1; ++J) {
@@ -640,7 +636,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) { aqv[i] = aqo[i]; ak[i] *= beta; }
                 *reinterpret_cast<float4*>(&s_akk[pair_index(I, J)][lane * 4]) = make_float4(ak[0], ak[1], ak[2], ak[3]);
-                half_store(ws + L.aqk + (size_t)(I * KSC + J / 2) * 512, lane, J % 2, aqv);
+                half_store(ws + L.aqk + tri_offset(I, J / 2, KSC), lane, J % 2, aqv);
             }
         }
         // (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) for the strictly lower 16x16 N
@@ -667,13 +663,11 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
         const float4 bj = *reinterpret_cast<const float4*>(&s_beta[16 * J + 4 * gq]);
         auto write_tb = [&](int Ir, const floatx4& TR) {
             const float x[4] = {TR[0] * bj.x, TR[1] * bj.y, TR[2] * bj.z, TR[3] * bj.w};
-            half_store(ws + L.tb + (size_t)(Ir * KSC + J / 2) * 512, lane, J % 2, x);
+            T* tile = ws + L.tb + tri_offset(Ir, J / 2, KSC);
+            if (tri_half(Ir, J / 2)) quarter_store(tile, lane, x);  // diagonal block of an even row block
+            else half_store(tile, lane, J % 2, x);
         };
         write_tb(J, TdR);
-        if (J % 2 == 0) {
-            const float zero4[4] = {0.f, 0.f, 0.f, 0.f};
-            half_store(ws + L.tb + (size_t)(J * KSC + J / 2) * 512, lane, 1, zero4);
-        }
         floatx4 TcolC[NBK];
 #pragma unroll
         for (int K = 0; K < NBK; ++K) TcolC[K] = TdC;
@@ -1067,7 +1061,10 @@ void kda_inter_kernel(const InterArgs a) {
         for (int Ib = 0; Ib < NBK; ++Ib)
 #pragma unroll
             for (int s = 0; s < KSC; ++s)
-                if (2 * s <= Ib) frag_load(At[Ib][s], s_blk + L.tb + (size_t)(Ib * KSC + s) * 512, lane);
+                if (2 * s <= Ib) {
+                    if (tri_half(Ib, s)) frag_load_half(At[Ib][s], s_blk + L.tb + tri_offset(Ib, s, KSC), lane);
+                    else frag_load(At[Ib][s], s_blk + L.tb + tri_offset(Ib, s, KSC), lane);
+                }
 #pragma unroll
         for (int j = 0; j < SPW; ++j) {
             if constexpr (CONV) {
@@ -1121,7 +1118,10 @@ void kda_inter_kernel(const InterArgs a) {
 #pragma unroll
             for (int R = 0; R < NBD; ++R)
 #pragma unroll
-                for (int s = 0; s < KSC; ++s) frag_load(Ap[R][s], s_blk + L.kpt + (size_t)(R * KSC + s) * 512, lane);
+                for (int s = 0; s < KSC; ++s) {
+                    if (kpt_half(s, NBK)) frag_load_half(Ap[R][s], s_blk + L.kpt + kpt_offset(R, s, KSC, NBK), lane);
+                    else frag_load(Ap[R][s], s_blk + L.kpt + kpt_offset(R, s, KSC, NBK), lane);
+                }
 #pragma unroll
             for (int R = 0; R < NBD; ++R) g4[R] = *reinterpret_cast<const float4*>(s_gam + 16 * R + 4 * gq);
 #pragma unroll
@@ -1130,7 +1130,10 @@ void kda_inter_kernel(const InterArgs a) {
                 for (int s = 0; s < KSD; ++s) frag_load(Aq[Ib][s], s_blk + L.qp + (size_t)(Ib * KSD + s) * 512, lane);
 #pragma unroll
                 for (int s = 0; s < KSC; ++s)
-                    if (2 * s <= Ib) frag_load(Aa[Ib][s], s_blk + L.aqk + (size_t)(Ib * KSC + s) * 512, lane);
+                    if (2 * s <= Ib) {
+                        if (tri_half(Ib, s)) frag_load_half(Aa[Ib][s], s_blk + L.aqk + tri_offset(Ib, s, KSC), lane);
+                        else frag_load(Aa[Ib][s], s_blk + L.aqk + tri_offset(Ib, s, KSC), lane);
+                    }
             }
 
             // Operand copy of the incoming state.

@@ -201,6 +201,27 @@ __device__ __forceinline__ void half_store(float* tile, int lane, int half, cons
     *reinterpret_cast<float4*>(tile + lane * 8 + half * 4) = make_float4(x[0], x[1], x[2], x[3]);
 }
 
+// Half tiles (64 lanes x 4 elements): a lane's slots 0..3, the other four zero.
+__device__ __forceinline__ void quarter_store(bf16_t* tile, int lane, const float x[4]) {
+    typedef __bf16 bf16x4q __attribute__((ext_vector_type(4)));
+    const bf16x4q v = {(bf16_t)x[0], (bf16_t)x[1], (bf16_t)x[2], (bf16_t)x[3]};
+    *reinterpret_cast<bf16x4q*>(tile + lane * 4) = v;
+}
+__device__ __forceinline__ void quarter_store(float* tile, int lane, const float x[4]) {
+    *reinterpret_cast<float4*>(tile + lane * 4) = make_float4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void frag_load_half(Frag<bf16_t>& f, const bf16_t* tile, int lane) {
+    typedef __bf16 bf16x4q __attribute__((ext_vector_type(4)));
+    const bf16x4q h = *reinterpret_cast<const bf16x4q*>(tile + lane * 4);
+    const bf16_t z = (bf16_t)0.f;
+    f.v = bf16x8{h[0], h[1], h[2], h[3], z, z, z, z};
+}
+__device__ __forceinline__ void frag_load_half(Frag<float>& f, const float* tile, int lane) {
+    const float4 h = *reinterpret_cast<const float4*>(tile + lane * 4);
+    f.v[0] = h.x; f.v[1] = h.y; f.v[2] = h.z; f.v[3] = h.w;
+    f.v[4] = f.v[5] = f.v[6] = f.v[7] = 0.f;
+}
+
 // Load 8 consecutive elements into a fragment's slots 0..7 (16 bytes for
 // bf16, 32 for fp32; p aligned to 16 bytes).
 __device__ __forceinline__ void frag_load_row8(Frag<bf16_t>& f, const bf16_t* p) {

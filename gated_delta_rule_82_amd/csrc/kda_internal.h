@@ -17,7 +17,32 @@ enum : unsigned { kQkL2 = 1u, kBetaSig = 2u, kGateIn = 4u, kGateSoftplus = 8u };
 //   KpT = (K_hat * exp(G_C - G))^T [Dk x C]   tiles (channel block, token step)
 //   Tb  = (I + A_kk)^-1 Diag(beta) [C x C]    tiles (token block, token step)
 //   Aqk = tril(Q K^T with decay)   [C x C]    tiles (token block, token step)
-// followed by gamma = exp(G_C) [Dk] in fp32.
+// followed by gamma = exp(G_C) [Dk] in fp32.  No tile that is zero by
+// construction is stored: of Tb and Aqk only the steps s with 2 s <= Ib, and
+// the step 2 s == Ib (whose second 16 tokens lie above the diagonal) as a
+// half tile of 64 lanes x 4 elements (the fragment's slots 0..3); of KpT a
+// step whose second 16 tokens lie past the chunk (C = 16) as a half tile.
+__host__ __device__ constexpr bool tri_half(int Ib, int s) { return 2 * s == Ib; }
+// element offset of stored tile (Ib, s), 2 s <= Ib, of a Tb / Aqk area
+__host__ __device__ constexpr size_t tri_offset(int Ib, int s, int ksc) {
+    size_t off = 0;
+    for (int i = 0; i < Ib; ++i)
+        for (int t = 0; t < ksc; ++t)
+            if (2 * t <= i) off += (2 * t == i) ? 256 : 512;
+    for (int t = 0; t < s; ++t)
+        if (2 * t <= Ib) off += (2 * t == Ib) ? 256 : 512;
+    return off;
+}
+__host__ __device__ constexpr bool kpt_half(int s, int nbk) { return 2 * s + 1 >= nbk; }
+// element offset of KpT tile (R, s)
+__host__ __device__ constexpr size_t kpt_offset(int R, int s, int ksc, int nbk) {
+    size_t row = 0;
+    for (int t = 0; t < ksc; ++t) row += kpt_half(t, nbk) ? 256 : 512;
+    size_t off = (size_t)R * row;
+    for (int t = 0; t < s; ++t) off += kpt_half(t, nbk) ? 256 : 512;
+    return off;
+}
+
 struct BlockLayout {
     int nbk, ksd, nbd, ksc;
     size_t kd, qp, kpt, tb, aqk, end;   // element offsets
@@ -36,9 +61,9 @@ __host__ __device__ constexpr BlockLayout block_layout(int elem_bytes, int DK, i
     L.kd = 0;
     L.qp = L.kd + (size_t)L.nbk * L.ksd * tile;
     L.kpt = L.qp + (size_t)L.nbk * L.ksd * tile;
-    L.tb = L.kpt + (size_t)L.nbd * L.ksc * tile;
-    L.aqk = L.tb + (size_t)L.nbk * L.ksc * tile;
-    L.end = L.aqk + (size_t)L.nbk * L.ksc * tile;
+    L.tb = L.kpt + kpt_offset(L.nbd, 0, L.ksc, L.nbk);
+    L.aqk = L.tb + tri_offset(L.nbk, 0, L.ksc);
+    L.end = L.aqk + tri_offset(L.nbk, 0, L.ksc);
     L.gamma_byte = L.end * (size_t)elem_bytes;
     L.bytes = round_up(L.gamma_byte + (size_t)DK * 4, 256);
     return L;

@@ -168,9 +168,9 @@ kda_status kda_chunk_fwd_conv(const void* q, const void* k, const void* v, const
  * and calls no allocating routine; its first call on a device looks up that
  * device's buffer address.
  *   Limit: B * H * (blk + Dk * (Dk + Dv) * 4) <= 64 MiB, with blk the bytes
- *   of one chunk block (29 184 for bf16, Dk = 128, chunk 32; 66 048 at chunk
- *   64; 57 856 for fp32 at chunk 32), rounded as in kda_chunk_fwd_workspace;
- *   e.g. B * H <= 418 at Dk = Dv = 128, chunk 32, bf16.  Larger sizes return
+ *   of one chunk block (28 160 for bf16, Dk = 128, chunk 32; 59 904 at chunk
+ *   64; 55 808 for fp32 at chunk 32), rounded as in kda_chunk_fwd_workspace;
+ *   e.g. B * H <= 421 at Dk = Dv = 128, chunk 32, bf16.  Larger sizes return
  *   KDA_ERR_SCRATCH and enqueue nothing.
  *   Every call on a GPU uses that GPU's one buffer: calls that can overlap in
  *   time on one GPU (different streams, or host threads sharing a stream

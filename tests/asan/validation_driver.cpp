@@ -141,10 +141,10 @@ int main() {
     EXPECT(kda_chunk_fwd_noalloc(q, k, v, z, br, A, nullptr, o, S, nullptr, nullptr, B, T, H, Dk, Dv, C, -5.f, 7,
                                  KDA_BF16, nullptr),
            KDA_OK, 1);
-    EXPECT(kda_chunk_fwd_noalloc(q, k, v, z, br, A, nullptr, o, S, nullptr, nullptr, 1, T, 418, 128, 128, 32, -5.f, 7,
+    EXPECT(kda_chunk_fwd_noalloc(q, k, v, z, br, A, nullptr, o, S, nullptr, nullptr, 1, T, 421, 128, 128, 32, -5.f, 7,
                                  KDA_BF16, nullptr),
            KDA_OK, 1);
-    EXPECT(kda_chunk_fwd_noalloc(q, k, v, z, br, A, nullptr, o, S, nullptr, nullptr, 1, T, 419, 128, 128, 32, -5.f, 7,
+    EXPECT(kda_chunk_fwd_noalloc(q, k, v, z, br, A, nullptr, o, S, nullptr, nullptr, 1, T, 422, 128, 128, 32, -5.f, 7,
                                  KDA_BF16, nullptr),
            KDA_ERR_SCRATCH, 0);
     EXPECT(kda_chunk_fwd_noalloc(nullptr, k, v, z, br, A, nullptr, o, S, nullptr, nullptr, B, T, H, Dk, Dv, C, -5.f,

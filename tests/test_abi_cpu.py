@@ -44,9 +44,10 @@ def test_safe_chunk_size(lib):
 
 
 def test_workspace_sizes(lib):
-    # 64 fragment tiles of 1 KiB + 512 B of fp32 decay per (b, h, chunk) for bf16 D=128 C=64,
-    # plus the fp32 state and transition carried between slices of the sequence
-    per = 64 * 1024 + 512
+    # per (b, h, chunk) for bf16 D=128 C=64: Kd, Qp, KpT 16 fragment tiles of 1 KiB each; Tb and Aqk
+    # the 6 tiles on or below the diagonal, two of them half tiles (5 KiB each); 512 B of fp32
+    # decay; plus the fp32 state and transition carried between slices of the sequence
+    per = (3 * 16 + 2 * 5) * 1024 + 512
     carry = lambda bh, dk, dv: bh * dk * (dk + dv) * 4
     assert lib.kda_chunk_fwd_workspace(4, 4096, 16, 128, 128, 64, 1) == 4 * 16 * 64 * per + carry(64, 128, 128)
     assert lib.kda_chunk_fwd_workspace(1, 65, 1, 128, 128, 64, 1) == 2 * per + carry(1, 128, 128)
