@@ -715,7 +715,7 @@ constexpr size_t kLdsBudget = 160 * 1024;  // LDS per CU on gfx950
 // ([C tokens][16 NS]).  Two copy waves fill the slots with global_load_lds,
 // 1 KiB per instruction ("piece"); copy wave 0 issues the first kPer0 pieces
 // of a chunk, copy wave 1 the rest (each streams a contiguous half).
-template <typename T, int DK, int C, int NS>
+template <typename T, int DK, int C, int NS, bool VSPREAD = true>
 struct InterRing {
     static constexpr BlockLayout L = block_layout(sizeof(T), DK, C);
     static constexpr int kVRow = 16 * NS * (int)sizeof(T);   // bytes of one token's staged values
@@ -728,10 +728,13 @@ struct InterRing {
     static constexpr size_t kOBytes = 2 * kOTile;
     // Bank-spread layouts.  A compute wave reads the values of tokens
     // 4 gq + i (i fixed per instruction) and writes output rows r, so rows
-    // four apart must not share banks.  Values: a 1 KiB piece holds kVTok
-    // token rows of kVGran 16-byte granules; granule g of row u of the piece
-    // sits at granule position (u % 4) 16 + (u / 4) kVGran + g, so the rows
-    // 4 gq + i of one read fall on distinct banks.  Outputs: the tile is cut
+    // four apart must not share banks.  Values (VSPREAD): a 1 KiB piece holds
+    // kVTok token rows of kVGran 16-byte granules; granule g of row u of the
+    // piece sits at granule position (u % 4) 16 + (u / 4) kVGran + g, so the
+    // rows 4 gq + i of one read fall on distinct banks (without VSPREAD the
+    // rows follow each other: the fused convolution reads seven rows per
+    // token block at lane-dependent offsets, for which the plain layout
+    // measured faster).  Outputs: the tile is cut
     // into 16-row blocks stored granule-column-major (granule og of row t at
     // position og 16 + t % 16), so the 16 rows one write touches are distinct
     // banks; with 8-byte writes (bf16) rows 8-15 of a block also swap the two
@@ -742,13 +745,21 @@ struct InterRing {
     static_assert(kVTok % 4 == 0, "pieces hold whole groups of four rows");
     // LDS offset (from the values of the slot) of byte lb of value row t
     static __host__ __device__ constexpr uint32_t voff(int t, uint32_t lb) {
+        if (!VSPREAD) return (uint32_t)(t * kVRow) + lb;
         return (uint32_t)((t / kVTok) * 1024 +
                           ((((t % kVTok) & 3) * 16 + ((t % kVTok) >> 2) * kVGran + (int)(lb >> 4)) << 4)) +
                (lb & 15u);
     }
+    // the row and granule that DMA lane L writes in its piece (the inverse of voff)
+    static __device__ __forceinline__ int dma_row(int L) {
+        return VSPREAD ? 4 * ((L % 16) / kVGran) + L / 16 : L / kVGran;
+    }
+    static __device__ __forceinline__ int dma_granule(int L) { return VSPREAD ? (L % 16) % kVGran : L % kVGran; }
     // LDS offset (from the tile) of byte ob of output row t
-    static constexpr uint32_t kOHalf = sizeof(T) == 2 ? 8u : 0u;
+    static constexpr bool kSpread = VSPREAD;
+    static constexpr uint32_t kOHalf = (sizeof(T) == 2 && VSPREAD) ? 8u : 0u;
     static __host__ __device__ constexpr uint32_t ooff(int t, uint32_t ob) {
+        if (!VSPREAD) return (uint32_t)(t * kORow) + ob;
         return (uint32_t)((t >> 4) * 16 * kORow + (((int)(ob >> 4) * 16 + (t & 15)) << 4)) +
                ((ob & 15u) ^ (((t >> 3) & 1) ? kOHalf : 0u));
     }
@@ -808,7 +819,7 @@ template <typename T, int DK, int C, int NW, int SPW, bool CONV = false>
 __global__ __launch_bounds__(64 * (NW + 2)) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void kda_inter_kernel(const InterArgs a) {
     constexpr int NS = NW * SPW;
-    using Ring = InterRing<T, DK, C, NS>;
+    using Ring = InterRing<T, DK, C, NS, !CONV>;
     constexpr BlockLayout L = Ring::L;
     constexpr int K = Ring::kSlots;
     constexpr bool kAhead = K >= 3;  // next chunk's operands are read during the current one
@@ -849,15 +860,14 @@ void kda_inter_kernel(const InterArgs a) {
         const unsigned char* gblk = reinterpret_cast<const unsigned char*>(a.ws) + (size_t)bh * a.wsNC * L.bytes;
         const unsigned char* vsrc = reinterpret_cast<const unsigned char*>(a.v);
         constexpr int kTokPerPiece = Ring::kVTok;
-        // lane L writes granule position L of a piece: row 4 ((L % 16) /
-        // kVGran) + L / 16 of the piece, granule (L % 16) % kVGran of the row
-        // (the inverse of Ring::voff)
-        const int vcol = vcol0 + ((lane % 16) % Ring::kVGran) * (16 / (int)sizeof(T));
+        // lane L writes granule position L of a piece: row Ring::dma_row(L)
+        // of the piece, granule Ring::dma_granule(L) of the row
+        const int vcol = vcol0 + Ring::dma_granule(lane) * (16 / (int)sizeof(T));
         const uint32_t vcol_b = (uint32_t)((vcol < 16 * vs1 ? vcol : 0) * (int)sizeof(T));  // columns outside the range load any valid bytes
         // values: a wave-uniform 64-bit base per chunk plus a 32-bit lane offset
         const uint32_t tstride = (uint32_t)(a.H * a.Dv * (int)sizeof(T));  // bytes per token
         const unsigned char* vrow0 = vsrc + (((size_t)b * a.T * a.H + h) * a.Dv) * sizeof(T);
-        const uint32_t vlane_tok = (uint32_t)(4 * ((lane % 16) / Ring::kVGran) + lane / 16);
+        const uint32_t vlane_tok = (uint32_t)Ring::dma_row(lane);
         auto issue = [&](int n) {
             unsigned char* slot = slot_of(n);
             const unsigned char* gb = gblk + (size_t)(n - a.c0) * L.bytes;
@@ -974,8 +984,9 @@ void kda_inter_kernel(const InterArgs a) {
     // Outputs leave through the staging tiles: compute wave w stores tokens
     // [w C / NW, (w + 1) C / NW) of the previous chunk's tile, one 16-byte
     // granule per lane and step: step st, lane l takes granule og = g / kTpw
-    // of row g % kTpw of the wave's rows (g = 64 st + l), i.e. strip og / kGps
-    // of the group, 16 bytes of it.
+    // of row g % kTpw of the wave's rows (g = 64 st + l; with the plain tile
+    // granule g % kGpr of row g / kGpr), i.e. strip og / kGps of the group,
+    // 16 bytes of it.
     constexpr int kEpg = 16 / (int)sizeof(T);      // elements per granule
     constexpr int kGps = 16 / kEpg;                // granules per strip row
     constexpr int kGpr = NS * kGps;                // granules per token row
@@ -1001,8 +1012,10 @@ void kda_inter_kernel(const InterArgs a) {
 #pragma unroll
         for (int st = 0; st < kOSteps; ++st) {
             const int gi = st * 64 + lane;
-            const int tok = w * kTpw + gi % kTpw;
-            const int og = gi / kTpw;
+            // (bank-spread tile: a granule column of the wave's rows per 16
+            // lanes; plain tile: whole rows one after the other)
+            const int tok = w * kTpw + (Ring::kSpread ? gi % kTpw : gi / kGpr);
+            const int og = Ring::kSpread ? gi / kTpw : gi % kGpr;
             const int sl = og / kGps;
             const int part = og % kGps;
             unsigned char* base = nullptr;
@@ -1049,6 +1062,18 @@ void kda_inter_kernel(const InterArgs a) {
             }
         }
     }
+    // fused convolution: staging offsets of the rows 4 gq + p - 3 (p < 7)
+    // relative to their 16-row block, and whether a row lies in the block before
+    uint32_t crow[CONV ? 7 : 1];
+    bool cprev[CONV ? 7 : 1];
+    if constexpr (CONV) {
+#pragma unroll
+        for (int p = 0; p < 7; ++p) {
+            const int x = 4 * gq + p - 3;
+            cprev[p] = x < 0;
+            crow[p] = Ring::voff(x < 0 ? 16 + x : x, 0);
+        }
+    }
     auto load_serial = [&](int n) {
         const unsigned char* cur = slot_of(n);
         const T* s_blk = reinterpret_cast<const T*>(cur);
@@ -1076,11 +1101,12 @@ void kda_inter_kernel(const InterArgs a) {
                     float x[7];
 #pragma unroll
                     for (int p = 0; p < 7; ++p) {
-                        const int tt = 16 * J + 4 * gq + p - 3;
-                        const int tr = tt >= 0 ? tt : 0;
-                        const uint32_t raw = (uint32_t)*reinterpret_cast<const Raw*>(s_val + Ring::voff(tr, vlane[j]));
-                        const uint32_t pv = tt == -3 ? vprev[j][0] : tt == -2 ? vprev[j][1] : vprev[j][2];
-                        x[p] = RawBits<T>::to_float((Raw)(tt >= 0 ? raw : pv));
+                        // row 16 J + 4 gq + p - 3: in block J, or (cprev[p]) at
+                        // the end of block J - 1, or before the chunk (J = 0)
+                        const uint32_t base = cprev[p] ? (J > 0 ? Ring::voff(16 * (J - 1), 0) : 0u) : Ring::voff(16 * J, 0);
+                        const uint32_t raw = (uint32_t)*reinterpret_cast<const Raw*>(s_val + base + crow[p] + vlane[j]);
+                        const uint32_t pv = vprev[j][p < 3 ? p : 2];
+                        x[p] = RawBits<T>::to_float((Raw)((J == 0 && cprev[p]) ? pv : raw));
                     }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -1090,7 +1116,7 @@ void kda_inter_kernel(const InterArgs a) {
                 }
 #pragma unroll
                 for (int p = 0; p < 3; ++p)
-                    vprev[j][p] = (uint32_t)*reinterpret_cast<const Raw*>(s_val + Ring::voff(C - 3 + p, vlane[j]));
+                    vprev[j][p] = (uint32_t)*reinterpret_cast<const Raw*>(s_val + Ring::voff(C - 3 + p, 0) + vlane[j]);
             } else {
 #pragma unroll
                 for (int J = 0; J < NBK; ++J)
@@ -1248,7 +1274,7 @@ void kda_inter_kernel(const InterArgs a) {
 // (CONV: with the fused convolution of v).
 template <typename T, int DK, int C, int NW, bool CONV = false>
 struct InterKernel {
-    using Ring = InterRing<T, DK, C, NW>;
+    using Ring = InterRing<T, DK, C, NW, !CONV>;
     static constexpr int kThreads = 64 * (NW + 2);
     static constexpr size_t kLds = (size_t)Ring::kSlots * Ring::kSlot + Ring::kOBytes;
     static const void* fn() { return reinterpret_cast<const void*>(kda_inter_kernel<T, DK, C, NW, 1, CONV>); }
