@@ -36,8 +36,11 @@ __global__ __launch_bounds__(512) void kda_compose_kernel(const ComposeArgs a) {
     const int r = lane & 15;
     const int gq = lane >> 4;
     const int nstrip = a.Dv / 16;
-    const int strip = blockIdx.x % nstrip;
-    const int bh = blockIdx.x / nstrip;
+    // the strips of one (b, h) on one XCD: they read the same M rows, which
+    // that XCD's L2 then serves after the first
+    const int bid = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+    const int strip = bid % nstrip;
+    const int bh = bid / nstrip;
     const int BH = a.B * a.H;
     const int col = strip * 16 + r;
 
