@@ -715,7 +715,7 @@ constexpr size_t kLdsBudget = 160 * 1024;  // LDS per CU on gfx950
 // ([C tokens][16 NS]).  Two copy waves fill the slots with global_load_lds,
 // 1 KiB per instruction ("piece"); copy wave 0 issues the first kPer0 pieces
 // of a chunk, copy wave 1 the rest (each streams a contiguous half).
-template <typename T, int DK, int C, int NS, bool VSPREAD = true>
+template <typename T, int DK, int C, int NS, bool SPREAD = true>
 struct InterRing {
     static constexpr BlockLayout L = block_layout(sizeof(T), DK, C);
     static constexpr int kVRow = 16 * NS * (int)sizeof(T);   // bytes of one token's staged values
@@ -726,40 +726,40 @@ struct InterRing {
     static constexpr int kORow = 16 * NS * (int)sizeof(T);  // bytes of one token's output row
     static constexpr size_t kOTile = (size_t)C * kORow;
     static constexpr size_t kOBytes = 2 * kOTile;
-    // Bank-spread layouts.  A compute wave reads the values of tokens
-    // 4 gq + i (i fixed per instruction) and writes output rows r, so rows
-    // four apart must not share banks.  Values (VSPREAD): a 1 KiB piece holds
+    // Bank-spread layouts (SPREAD).  A compute wave reads the values of
+    // tokens 4 gq + i (i fixed per instruction) and writes output rows r, so
+    // rows four apart must not share banks.  Values: a 1 KiB piece holds
     // kVTok token rows of kVGran 16-byte granules; granule g of row u of the
     // piece sits at granule position (u % 4) 16 + (u / 4) kVGran + g, so the
-    // rows 4 gq + i of one read fall on distinct banks (without VSPREAD the
-    // rows follow each other: the fused convolution reads seven rows per
-    // token block at lane-dependent offsets, for which the plain layout
-    // measured faster).  Outputs: the tile is cut
-    // into 16-row blocks stored granule-column-major (granule og of row t at
-    // position og 16 + t % 16), so the 16 rows one write touches are distinct
-    // banks; with 8-byte writes (bf16) rows 8-15 of a block also swap the two
-    // halves of their granules, so rows eight apart differ in bank too.
+    // rows 4 gq + i of one read fall on distinct banks.  Outputs: the tile is
+    // cut into 16-row blocks stored granule-column-major (granule og of row t
+    // at position og 16 + t % 16), so the 16 rows one write touches are
+    // distinct banks; with 8-byte writes (bf16) rows 8-15 of a block also
+    // swap the two halves of their granules, so rows eight apart differ in
+    // bank too.  Without SPREAD both keep plain row-major order: the fused
+    // convolution reads seven value rows per token block at lane-dependent
+    // offsets, and for it the plain layouts measured faster.
     static constexpr int kVGran = kVRow / 16;  // granules per staged value row
     static constexpr int kVTok = 64 / kVGran;  // value rows per piece
     static constexpr int kOGran = kORow / 16;  // granules per output row
     static_assert(kVTok % 4 == 0, "pieces hold whole groups of four rows");
     // LDS offset (from the values of the slot) of byte lb of value row t
     static __host__ __device__ constexpr uint32_t voff(int t, uint32_t lb) {
-        if (!VSPREAD) return (uint32_t)(t * kVRow) + lb;
+        if (!SPREAD) return (uint32_t)(t * kVRow) + lb;
         return (uint32_t)((t / kVTok) * 1024 +
                           ((((t % kVTok) & 3) * 16 + ((t % kVTok) >> 2) * kVGran + (int)(lb >> 4)) << 4)) +
                (lb & 15u);
     }
     // the row and granule that DMA lane L writes in its piece (the inverse of voff)
     static __device__ __forceinline__ int dma_row(int L) {
-        return VSPREAD ? 4 * ((L % 16) / kVGran) + L / 16 : L / kVGran;
+        return SPREAD ? 4 * ((L % 16) / kVGran) + L / 16 : L / kVGran;
     }
-    static __device__ __forceinline__ int dma_granule(int L) { return VSPREAD ? (L % 16) % kVGran : L % kVGran; }
+    static __device__ __forceinline__ int dma_granule(int L) { return SPREAD ? (L % 16) % kVGran : L % kVGran; }
     // LDS offset (from the tile) of byte ob of output row t
-    static constexpr bool kSpread = VSPREAD;
-    static constexpr uint32_t kOHalf = (sizeof(T) == 2 && VSPREAD) ? 8u : 0u;
+    static constexpr bool kSpread = SPREAD;
+    static constexpr uint32_t kOHalf = (sizeof(T) == 2 && SPREAD) ? 8u : 0u;
     static __host__ __device__ constexpr uint32_t ooff(int t, uint32_t ob) {
-        if (!VSPREAD) return (uint32_t)(t * kORow) + ob;
+        if (!SPREAD) return (uint32_t)(t * kORow) + ob;
         return (uint32_t)((t >> 4) * 16 * kORow + (((int)(ob >> 4) * 16 + (t & 15)) << 4)) +
                ((ob & 15u) ^ (((t >> 3) & 1) ? kOHalf : 0u));
     }
