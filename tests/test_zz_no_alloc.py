@@ -31,7 +31,7 @@ def both(inp, chunk, want):
 
 
 def test_noalloc_equals_workspace_call_twice():
-    # 1) the layer workload at the benchmarked chunk: 239 MB of blocks, so the
+    # 1) the layer workload at the benchmarked chunk: 231 MB of blocks, so the
     #    64 MiB scratch cuts the sequence into slices
     w = inputs.WORKLOADS["layer"]
     print("noalloc: layer workload B4 T4096 H16 D128 bf16 chunk 32", flush=True)
