@@ -61,6 +61,19 @@ def test_workspace_sizes(lib):
     assert lib.kda_chunk_fwd_workspace(2, 100, 3, 64, 32, 0, 0) == lib.kda_chunk_fwd_workspace(2, 100, 3, 64, 32, 64, 0)
 
 
+def test_benchmark_block_model_matches_the_library(lib):
+    # bench.py prices the hand-off with its own model of the per-chunk block;
+    # it must agree with the workspace the library asks for (one chunk per
+    # (b, h), so the workspace is one block plus the fp32 carry)
+    import bench
+    carry = lambda dk, dv: dk * (dk + dv) * 4
+    for dt, esize in ((0, 4), (1, 2)):
+        for Dk in (16, 32, 64, 128):
+            for C in (16, 32, 64):
+                got = lib.kda_chunk_fwd_workspace(1, C, 1, Dk, 128, C, dt) - carry(Dk, 128)
+                assert got == bench.block_bytes(Dk, C, esize), (dt, Dk, C)
+
+
 def test_status_strings(lib):
     for s in range(9):
         assert len(kda.status_string(s)) > 0
