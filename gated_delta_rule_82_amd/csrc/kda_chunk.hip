@@ -97,6 +97,15 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     constexpr int kStageWave = 3 * 16 * RB;          // q, k, z rows of one wave
     constexpr int kStagePieces = (16 * RB + 1023) / 1024;  // 1 KiB copies per tensor and wave
 
+    // The tail of each chunk block (KpT, Tb, Aqk, gamma: the tiles that
+    // different waves write in halves) is assembled in LDS and leaves at the
+    // end as whole 16-byte lane stores, so every line of the block is written
+    // once and in full (bf16, chunks of at most 32 tokens, where the image
+    // fits beside the phase arrays in the space of the input staging).
+    constexpr bool kImg = kStage && C <= 32;
+    constexpr size_t kImgBytes = L.bytes - L.kpt * sizeof(T);  // block bytes from KpT on
+    static_assert(kImgBytes % 16 == 0, "whole 16-byte pieces");
+
     // per chunk of the workgroup:
     __shared__ __align__(16) float s_tot_all[NCH][NBK][DK];     // block totals of the log2 decay
     __shared__ float s_beta_all[NCH][C];
@@ -112,6 +121,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
         T offb[NCH][NOFF][KSO][512]; // column operands of off-diagonal blocks
         float akk[NCH][NPAIR][256];  // R layout of A_kk[I][J], J < I
         float tdiag[NCH][NBK][256];  // R layout of (I + A_kk[I][I])^-1
+        __align__(16) unsigned char img[kImg ? NCH : 1][kImg ? kImgBytes : 16];  // block tails (kImg)
     };
     union SharedPhases {
         PhaseArrays ph;
@@ -170,6 +180,9 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
     const size_t row_qk = ((size_t)b * a.T + (t < a.T ? t : a.T - 1)) * Hk + hq;
 
     T* ws = reinterpret_cast<T*>(a.ws) + (size_t)(active ? cid : 0) * (L.bytes / sizeof(T));
+    // where this wave's block tail (from KpT on) is written: the LDS image
+    // (kImg) or the workspace block itself
+    T* tl = kImg ? reinterpret_cast<T*>(sh.ph.img[kImg ? sub : 0]) : ws + L.kpt;
 
     // ------------------------------------------------------------ phase A
     // Lane (r, gq) of wave I owns token 16 I + r and the channels of its
@@ -445,7 +458,8 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
         }
         if (Ib == 0) {
             const size_t cb = (size_t)bh * a.wsNC + g * NCH + sb;  // workspace block of that chunk
-            float* gam = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(a.ws) + cb * L.bytes + L.gamma_byte);
+            float* gam = kImg ? reinterpret_cast<float*>(sh.ph.img[kImg ? sb : 0] + (L.gamma_byte - L.kpt * sizeof(T)))
+                              : reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(a.ws) + cb * L.bytes + L.gamma_byte);
             gam[c] = exp2_fast(GC);
         }
     }
@@ -579,7 +593,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
                     floatx4 x = {0.f, 0.f, 0.f, 0.f};
                     x = mma(kp, e, x);
                     const float xv[4] = {x[0], x[1], x[2], x[3]};
-                    T* tile = ws + L.kpt + kpt_offset(R, I / 2, KSC, NBK);
+                    T* tile = tl + kpt_offset(R, I / 2, KSC, NBK);
                     if (kpt_half(I / 2, NBK)) quarter_store(tile, lane, xv);  // no block I + 1: a half tile
                     else half_store(tile, lane, I % 2, xv);
                 }
@@ -607,7 +621,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
         }
         // diagonal block: a half tile for even I (block I + 1 of the step lies
         // above the diagonal), the second half of a full tile for odd I
-        T* aqk_tile = ws + L.aqk + tri_offset(I, I / 2, KSC);
+        T* aqk_tile = tl + (L.aqk - L.kpt) + tri_offset(I, I / 2, KSC);
         if (I % 2 == 0) quarter_store(aqk_tile, lane, aq);
         else half_store(aqk_tile, lane, 1, aq);
         // off-diagonal blocks J < I: entry (i, j) = sum_c rowside_I[i,c] pair[c] offb_J[j,c]
@@ -636,7 +650,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) { aqv[i] = aqo[i]; ak[i] *= beta; }
                 *reinterpret_cast<float4*>(&s_akk[pair_index(I, J)][lane * 4]) = make_float4(ak[0], ak[1], ak[2], ak[3]);
-                half_store(ws + L.aqk + tri_offset(I, J / 2, KSC), lane, J % 2, aqv);
+                half_store(tl + (L.aqk - L.kpt) + tri_offset(I, J / 2, KSC), lane, J % 2, aqv);
             }
         }
         // (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) for the strictly lower 16x16 N
@@ -663,7 +677,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
         const float4 bj = *reinterpret_cast<const float4*>(&s_beta[16 * J + 4 * gq]);
         auto write_tb = [&](int Ir, const floatx4& TR) {
             const float x[4] = {TR[0] * bj.x, TR[1] * bj.y, TR[2] * bj.z, TR[3] * bj.w};
-            T* tile = ws + L.tb + tri_offset(Ir, J / 2, KSC);
+            T* tile = tl + (L.tb - L.kpt) + tri_offset(Ir, J / 2, KSC);
             if (tri_half(Ir, J / 2)) quarter_store(tile, lane, x);  // diagonal block of an even row block
             else half_store(tile, lane, J % 2, x);
         };
@@ -688,6 +702,16 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(const IntraArgs a) {
                 TcolC[Ir] = -mm16(TiiR, X);
                 write_tb(Ir, -mm16(X, TiiR));
             }
+        }
+    }
+    if constexpr (kImg) {
+        // the assembled block tails leave as whole 16-byte pieces
+        lds_barrier();
+        for (int sb = 0; sb < nsub; ++sb) {
+            unsigned char* dst = reinterpret_cast<unsigned char*>(a.ws) +
+                                 ((size_t)bh * a.wsNC + g * NCH + sb) * L.bytes + L.kpt * sizeof(T);
+            for (int e = threadIdx.x; e < (int)(kImgBytes / 16); e += 256)
+                *reinterpret_cast<uint4*>(dst + (size_t)e * 16) = *reinterpret_cast<const uint4*>(sh.ph.img[sb] + e * 16);
         }
     }
 }
