@@ -458,3 +458,24 @@ def test_grouped_step_matches_oracle(dtype):
                                     np64(br[:, 0]), np64(A), np64(db))
     assert_close(o, o_ref, dtype, "grouped step o")
     assert_close(S, S_ref, F32, "grouped step S")   # the state is fp32 in both paths
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("B,H,HV", [(7, 45, 45), (5, 120, 120), (40, 2, 8)])
+def test_step_heads_beyond_one_round(dtype, B, H, HV):
+    """Dk = Dv = 128 decode with more (b, h) heads than one resident round of
+    workgroups (315, 600 and 320 heads), so that workgroups carry two or three
+    heads each in uneven numbers: three steps in a row, every head against
+    the oracle (grouped heads with a gate bias in the last case)."""
+    q, k, v, z, br, A, db, S0 = grouped_case(B, 3, H, HV, 128, 128, dtype, seed=B * 1000 + HV, bias=HV != H)
+    print(f"step: B{B} H{H} HV{HV} D128 {dtype}", flush=True)
+    S = S0.cuda().clone()
+    S_ref = np64(S0)
+    for t in range(3):
+        args = [x[:, t].cuda().contiguous() for x in (q, k, v, z, br)]
+        o = kda.step(*args, A.cuda(), S, dt_bias=None if db is None else db.cuda())
+        torch.cuda.synchronize()
+        o_ref, S_ref = ora.step_grouped(S_ref, *(np64(x[:, t]) for x in (q, k, v, z, br)), np64(A),
+                                        None if db is None else np64(db))
+        assert_close(o, o_ref, dtype, f"step {t} o")
+    assert_close(S, S_ref, F32, "state after three steps")
