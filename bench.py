@@ -646,7 +646,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-tokens", type=int, default=4096, help="oracle sample length (0 = skip)")
-    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--decode-steps", type=int, default=1024)  # the decode workload: 1024 successive steps
     ap.add_argument("--long-reps", type=int, default=3)
     ap.add_argument("--only-layer", action="store_true", help="time the layer workload only")
     ap.add_argument("--chunk", type=int, default=32, help="state chunk length (16, 32 or 64)")
