@@ -54,10 +54,11 @@ def test_step_matches_oracle(dtype, Dk, Dv):
     assert max_rel(S, S_ref) <= RTOL_F32
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("flags", [0, 1, 2, 4, 6])
-def test_step_switches(flags):
+def test_step_switches(flags, D):
     rng = np.random.default_rng(flags)
-    B, H, Dk, Dv = 2, 3, 64, 64
+    B, H, Dk, Dv = 2, 3, D, D
     q = torch.tensor(ora.l2_normalize(rng.standard_normal((B, 1, H, Dk))), dtype=F32)
     k = torch.tensor(ora.l2_normalize(rng.standard_normal((B, 1, H, Dk))), dtype=F32)
     z = torch.tensor(rng.uniform(-4.9, -0.1, (B, 1, H, Dk)) if not flags & 4 else rng.standard_normal((B, 1, H, Dk)), dtype=F32)
