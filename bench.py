@@ -436,9 +436,30 @@ def bench_layer_body(torch, kda, inputs, steps, warmup, chunk):
         fused_core(i)
         gate(i)
 
+    lws = torch.empty(kda.layer_workspace_bytes(B, T, H, Dk, Dv, chunk, torch.bfloat16), dtype=torch.uint8,
+                      device=dev)
+
+    def layer_call(i):
+        s = sets[i % len(sets)]
+        kda.layer_fwd(s["q"], s["k"], s["v"], s["z"], s["beta_raw"], A, gates[i % 2], gw, None, conv_w=cw_all,
+                      conv_b=cb_all, chunk=chunk, y=y, S_out=S, workspace=lws)
+
+    def layer_call_noconv(i):
+        s = sets[i % len(sets)]
+        kda.layer_fwd(s["q"], s["k"], s["v"], s["z"], s["beta_raw"], A, gates[i % 2], gw, None, chunk=chunk,
+                      y=y, S_out=S, workspace=lws)
+
+    def core_then_gate(i):
+        s = sets[i % len(sets)]
+        kda.chunk_fwd(s["q"], s["k"], s["v"], s["z"], s["beta_raw"], A, None, chunk=chunk, o=o, S_out=S,
+                      workspace=ws)
+        gate(i)
+
     res = {}
     for name, fn in (("convs", convs), ("input_side_and_core", full), ("output_gate", gate), ("body", body),
-                     ("fused_input_side_and_core", fused_core), ("fused_body", fused_body)):
+                     ("fused_input_side_and_core", fused_core), ("fused_body", fused_body),
+                     ("layer_fwd", layer_call), ("layer_fwd_noconv", layer_call_noconv),
+                     ("core_then_gate", core_then_gate)):
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
@@ -465,7 +486,14 @@ def bench_layer_body(torch, kda, inputs, steps, warmup, chunk):
             "fused_input_side_and_core_ms": round(res["fused_input_side_and_core"], 4),
             "fused_layer_body_ms": round(res["fused_body"], 4),
             "fused_layer_body_tokens_per_s": B * T / (res["fused_body"] / 1e3),
-            "fused": "kda_chunk_fwd_conv: the short convolutions and SiLU inside the chunk kernels, then the output side"}
+            "fused": "kda_chunk_fwd_conv: the short convolutions and SiLU inside the chunk kernels, then the output side",
+            "layer_fwd_ms": round(res["layer_fwd"], 4),
+            "layer_fwd_tokens_per_s": B * T / (res["layer_fwd"] / 1e3),
+            "layer_fwd_noconv_ms": round(res["layer_fwd_noconv"], 4),
+            "core_then_output_gate_ms": round(res["core_then_gate"], 4),
+            "layer_fwd": "kda_layer_fwd: the convolutions in the chunk kernels and the output side in the inter "
+                         "kernel's output stores (one call, o never stored); _noconv: the output side only, "
+                         "against kda_chunk_fwd then kda_output_gate"}
 
 
 def bench_grouped(torch, kda, steps, warmup, chunk):

@@ -96,6 +96,19 @@ size_t kda_chunk_fwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk, k
     return workspace_bytes_impl(B, T, H, Dk, Dv, chunk, dt);
 }
 
+static size_t layer_workspace_impl(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype dt) {
+    if (workspace_bytes_impl(B, T, H, Dk, Dv, chunk, dt) == 0) return 0;
+    if (chunk == 0) chunk = 64;
+    const int BH = B * H, NC = chunks_of(T, chunk);
+    const size_t blk = kda::block_layout(elem_bytes(dt), Dk, chunk).bytes;
+    const int per = kda::slice_chunks(BH, NC, blk);
+    return kda::layer_workspace_bytes(elem_bytes(dt), Dk, Dv, chunk, (size_t)BH, (size_t)per);
+}
+
+size_t kda_layer_fwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype dt) {
+    return layer_workspace_impl(B, T, H, Dk, Dv, chunk, dt);
+}
+
 }  // extern "C"
 
 static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const void* z,
@@ -107,7 +120,8 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
                                  hipEvent_t* ev, int n_ev,
                                  int G = 1, const float* dt_bias = nullptr, bool noalloc = false,
                                  const float* conv_w = nullptr, const float* conv_b = nullptr,
-                                 const void* conv_state = nullptr) {
+                                 const void* conv_state = nullptr,
+                                 const void* gate = nullptr, const float* gate_w = nullptr) {
     if (!dtype_ok(dt) || !flags_ok(flags)) return KDA_ERR_DTYPE;
     if (dt_bias && !(flags & KDA_GATE_IN_KERNEL)) return KDA_ERR_DTYPE;  // it biases the in-kernel gate
     if (chunk == 0) chunk = 64;
@@ -125,6 +139,21 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
     KDA_TRY(maybe(S0)); KDA_TRY(maybe(S_out)); KDA_TRY(maybe(M_out)); KDA_TRY(maybe(P_out));
     KDA_TRY(maybe(dt_bias));
     if (conv_w) { KDA_TRY(maybe(conv_b)); KDA_TRY(maybe(conv_state)); }
+    if (gate) {
+        // the layer body: y (in the o slot) is written while other workgroups
+        // still read the inputs, so it may share no byte with any of them
+        KDA_TRY(maybe(gate_w));
+        const size_t eb = (size_t)elem_bytes(dt);
+        const size_t rows = (size_t)B * T * H;
+        const size_t ny = rows * Dv * eb;
+        const struct { const void* p; size_t n; } ins[] = {
+            {q, rows * Dk * eb}, {k, rows * Dk * eb}, {v, ny}, {z, rows * Dk * eb}, {beta_raw, rows * eb},
+            {gate, ny}, {gate_w, gate_w ? (size_t)Dv * 4 : 0}, {A_log, A_log ? (size_t)H * 4 : 0},
+            {S0, S0 ? (size_t)B * H * Dk * Dv * 4 : 0}, {S_out, S_out ? (size_t)B * H * Dk * Dv * 4 : 0},
+            {workspace, workspace_bytes}};
+        for (const auto& in : ins)
+            if (in.p && overlaps(o, ny, in.p, in.n)) return KDA_ERR_SHAPE;
+    }
     size_t slice_budget = kda::kSliceBytes;
     if (noalloc) {
         // one chunk block of every (b, h) and the carried state must fit the
@@ -136,7 +165,9 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
         workspace_bytes = kda::kScratchBytes;
         slice_budget = kda::kScratchBytes - carry;
     }
-    const size_t ws_need = noalloc ? 0 : workspace_bytes_impl(B, T, H, Dk, Dv, chunk, dt);
+    const size_t ws_need = noalloc ? 0
+                           : gate ? layer_workspace_impl(B, T, H, Dk, Dv, chunk, dt)
+                                  : workspace_bytes_impl(B, T, H, Dk, Dv, chunk, dt);
     if (ws_need > 0) {
         if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
             workspace_bytes < ws_need)
@@ -151,6 +182,11 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
     a.wide_decay = wide_decay(g_min, flags, dt);
     a.slice_budget = slice_budget;
     a.conv_w = conv_w; a.conv_b = conv_b; a.conv_state = conv_state;
+    a.gate = gate; a.gate_w = gate_w;
+    if (gate) {
+        const hipError_t e = kda::launch_layer(dt == KDA_BF16 ? 1 : 0, Dk, chunk, a, stream);
+        return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
     if (ev) {
         const int need = kda::chunk_kernel_count(elem_bytes(dt), Dk, chunk, B * H, a.NC) + 1;
         if (n_ev < need) return KDA_ERR_NULL;
@@ -195,6 +231,21 @@ kda_status kda_chunk_fwd_conv(const void* q, const void* k, const void* v, const
     return chunk_fwd_impl(q, k, v, z, beta_raw, A_log, S0, o, S_out, nullptr, nullptr, B, T, H, Dk, Dv,
                           chunk, g_min, flags, dt, workspace, workspace_bytes, stream, nullptr, 0, 1, nullptr, false,
                           conv_w, conv_b, conv_state);
+}
+
+kda_status kda_layer_fwd(const void* q, const void* k, const void* v, const void* z,
+                         const void* beta_raw, const float* A_log, const float* S0,
+                         const float* conv_w, const float* conv_b, const void* conv_state,
+                         const void* gate, const float* gate_weight,
+                         void* y, float* S_out, int B, int T, int H, int Dk, int Dv, int chunk,
+                         float g_min, unsigned flags, kda_dtype dt,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (B > 0 && H > 0 && T > 0) KDA_TRY(need(gate));
+    // with T = 0 nothing reads the gate: y stands in for it so that the call
+    // still takes the layer path (its workspace and validation)
+    return chunk_fwd_impl(q, k, v, z, beta_raw, A_log, S0, y, S_out, nullptr, nullptr, B, T, H, Dk, Dv,
+                          chunk, g_min, flags, dt, workspace, workspace_bytes, stream, nullptr, 0, 1, nullptr, false,
+                          conv_w, conv_b, conv_state, gate ? gate : (const void*)y, gate_weight);
 }
 
 kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* z,

@@ -86,6 +86,34 @@ template <> struct RawBits<float> {
     static __device__ __forceinline__ float to_float(uint32_t x) { return __uint_as_float(x); }
 };
 
+// One 16-byte granule of consecutive elements: element i widened to float,
+// and N floats packed back (round to nearest even for bf16).
+template <typename T> struct Gran16;
+template <> struct Gran16<bf16_t> {
+    static constexpr int N = 8;
+    static __device__ __forceinline__ float get(const uint4& g, int i) {
+        const uint32_t wd = i < 2 ? g.x : i < 4 ? g.y : i < 6 ? g.z : g.w;
+        return (i & 1) ? __uint_as_float(wd & 0xffff0000u) : __uint_as_float(wd << 16);
+    }
+    static __device__ __forceinline__ uint4 pack(const float (&x)[8]) {
+        uint32_t wd[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            wd[k] = (uint32_t)__builtin_bit_cast(uint16_t, (bf16_t)x[2 * k]) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, (bf16_t)x[2 * k + 1]) << 16);
+        return make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    }
+};
+template <> struct Gran16<float> {
+    static constexpr int N = 4;
+    static __device__ __forceinline__ float get(const uint4& g, int i) {
+        return __uint_as_float(i == 0 ? g.x : i == 1 ? g.y : i == 2 ? g.z : g.w);
+    }
+    static __device__ __forceinline__ uint4 pack(const float (&x)[4]) {
+        return make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3]));
+    }
+};
+
 // Four consecutive elements kept as loaded (bf16: two packed registers) and
 // widened to float where used, so they occupy half the registers until then.
 template <typename T> struct Raw4;

@@ -90,6 +90,16 @@ __host__ __device__ constexpr size_t chunk_workspace_bytes(int elem_bytes, int D
     return nbuf * BH * per * block_layout(elem_bytes, DK, C).bytes + round_up(BH * (size_t)DK * (DK + Dv) * 4, 256);
 }
 
+// Workspace of the layer body: that of the chunk call, then the output side's
+// exchange area, Dv / 16 x C floats per chunk-head of a slice.
+__host__ __device__ constexpr size_t layer_gss_offset(int elem_bytes, int DK, int Dv, int C, size_t BH, size_t per) {
+    return chunk_workspace_bytes(elem_bytes, DK, Dv, C, BH, per, 1);
+}
+__host__ __device__ constexpr size_t layer_workspace_bytes(int elem_bytes, int DK, int Dv, int C, size_t BH,
+                                                           size_t per) {
+    return layer_gss_offset(elem_bytes, DK, Dv, C, BH, per) + round_up(BH * per * (size_t)(Dv / 16) * C * 4, 256);
+}
+
 struct StepArgs {
     const void* q; const void* k; const void* v; const void* z; const void* beta_raw;
     const float* A_log; float* S; void* o;
@@ -116,6 +126,15 @@ struct ChunkArgs {
     const float* conv_w = nullptr;
     const float* conv_b = nullptr;
     const void* conv_state = nullptr;
+    // fused output side (launch_layer): o receives
+    // sigmoid(gate) * o / sqrt(mean o^2 + 1e-6) * gate_w per head row; gate
+    // [B,T,H,Dv] in the input type, gate_w [Dv] fp32 or NULL (ones); gss the
+    // exchange area of its per-token partial sums (gss_n floats per
+    // chunk-head of a slice), set by the launch
+    const void* gate = nullptr;
+    const float* gate_w = nullptr;
+    float* gss = nullptr;
+    int gss_n = 0;
 };
 
 // Built-in device scratch of the allocation-free chunk entry point (one copy
@@ -142,6 +161,13 @@ hipError_t launch_step(int dt, int DK, int DV, const StepArgs& a, hipStream_t s)
 hipError_t launch_chunk(int dt, int DK, int C, const ChunkArgs& a, hipStream_t s, hipEvent_t* ev, int n_ev);
 // Kernels one kda_chunk_fwd call launches for these sizes.
 int chunk_kernel_count(int elem_bytes, int DK, int C, int BH, int NC);
+// The intra-chunk kernel alone, over chunks [c0, c0 + nc) into `buf` of `per`
+// chunk blocks per (b, h) (with the exchange area marks of a.gss, if set).
+hipError_t launch_chunk_intra(int dt, int DK, int C, const ChunkArgs& a, void* buf, int per, int c0, int nc,
+                              hipStream_t s);
+// The layer body: the chunk kernels with the output side applied to o (a.gate
+// set; a.o receives y).  The workspace is layer_workspace_bytes.
+hipError_t launch_layer(int dt, int DK, int C, const ChunkArgs& a, hipStream_t s);
 hipError_t launch_compose(int DK, const ComposeArgs& a, hipStream_t s);
 hipError_t launch_fixup(int dt, int DK, const FixupArgs& a, hipStream_t s);
 

@@ -23,7 +23,8 @@ GATE_SOFTPLUS = 8  # with GATE_IN_KERNEL: the unbounded KDA v1 gate -exp(A_log) 
 
 EXPORTS = (
     "kda_safe_chunk_size", "kda_chunk_fwd_workspace", "kda_chunk_fwd", "kda_chunk_fwd_timed",
-    "kda_chunk_fwd_kernel_count", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_conv", "kda_step", "kda_chunk_fwd_grouped", "kda_step_grouped",
+    "kda_chunk_fwd_kernel_count", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_conv", "kda_layer_fwd_workspace",
+    "kda_layer_fwd", "kda_step", "kda_chunk_fwd_grouped", "kda_step_grouped",
     "kda_segment_compose", "kda_segment_fixup", "kda_short_conv", "kda_output_gate",
     "kda_chunk_bwd_workspace", "kda_chunk_bwd", "kda_chunk_bwd_grouped_workspace", "kda_chunk_bwd_grouped",
     "kda_status_string",
@@ -62,6 +63,10 @@ def load() -> ctypes.CDLL:
     L.kda_chunk_fwd_noalloc.restype = I
     L.kda_chunk_fwd_conv.argtypes = [P] * 12 + [I] * 6 + [F, U, I, P, S, P]
     L.kda_chunk_fwd_conv.restype = I
+    L.kda_layer_fwd_workspace.argtypes = [I, I, I, I, I, I, I]
+    L.kda_layer_fwd_workspace.restype = S
+    L.kda_layer_fwd.argtypes = [P] * 14 + [I] * 6 + [F, U, I, P, S, P]
+    L.kda_layer_fwd.restype = I
     L.kda_step.argtypes = [P] * 8 + [I] * 4 + [F, U, I, P]
     L.kda_step.restype = I
     L.kda_segment_compose.argtypes = [I, P, P, P, P, I, I, I, I, P]
@@ -215,6 +220,36 @@ def chunk_fwd_conv(q, k, v, z, beta_raw, A_log, conv_w, conv_b=None, conv_state=
                                      B, T, H, Dk, Dv, chunk, g_min, flags, _dt(dt),
                                      _ptr(workspace), workspace.numel(), _stream(dev)))
     return o, S_out
+
+
+def layer_workspace_bytes(B, T, H, Dk, Dv, chunk=64, dtype=torch.bfloat16) -> int:
+    return int(load().kda_layer_fwd_workspace(B, T, H, Dk, Dv, chunk, _dt(dtype)))
+
+
+def layer_fwd(q, k, v, z, beta_raw, A_log, gate, gate_weight=None, S0=None, *, conv_w=None, conv_b=None,
+              conv_state=None, chunk=64, g_min=-5.0, flags=FLAGS_DEFAULT, y=None, S_out=None, workspace=None):
+    """kda_layer_fwd: the layer body without its projections, with the output
+    side sigmoid(gate) * HeadRMSNorm(o) * gate_weight applied inside the core's
+    output stores (and the input-side convolution when conv_w is given, as in
+    chunk_fwd_conv).  gate [B,T,H,Dv] in the input dtype, gate_weight [Dv] fp32
+    or None.  Returns (y, S_out)."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    dev = q.device
+    if y is None:
+        y = torch.empty(B, T, H, Dv, dtype=dt, device=dev)
+    if S_out is None:
+        S_out = torch.empty(B, H, Dk, Dv, dtype=torch.float32, device=dev)
+    need = layer_workspace_bytes(B, T, H, Dk, Dv, chunk, dt)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check("kda_layer_fwd",
+           load().kda_layer_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta_raw), _ptr(A_log), _ptr(S0),
+                                _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(gate), _ptr(gate_weight),
+                                _ptr(y), _ptr(S_out), B, T, H, Dk, Dv, chunk, g_min, flags, _dt(dt),
+                                _ptr(workspace), workspace.numel(), _stream(dev)))
+    return y, S_out
 
 
 def chunk_fwd_noalloc(q, k, v, z, beta_raw, A_log, S0=None, *, chunk=64, g_min=-5.0,

@@ -158,6 +158,39 @@ kda_status kda_chunk_fwd_conv(const void* q, const void* k, const void* v, const
                               float g_min, unsigned flags, kda_dtype dt,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The layer body without its projections ("KDA 模块交互式演示" §1.7
+ * KimiDeltaAttention 完整层; "Implémenter KDA" 'La paramétrisation' and 'La
+ * porte de sortie de rang plein'): the optional input-side convolution of
+ * kda_chunk_fwd_conv, the chunkwise core of kda_chunk_fwd, and the output side
+ * applied to each row of the core's output o before it is stored:
+ *   y[b,t,h,c] = sigmoid(gate[b,t,h,c]) * o[b,t,h,c] * gate_weight[c]
+ *                / sqrt(mean_c' o[b,t,h,c']^2 + 1e-6)
+ * with o rounded to dt first (as kda_output_gate reads a stored o), so the
+ * call equals kda_chunk_fwd(_conv) followed by kda_output_gate up to the
+ * summation order of the norm.  o itself is never written to memory.
+ *   conv_w, conv_b, conv_state  as in kda_chunk_fwd_conv; conv_w NULL: no
+ *               convolution (q, k, v go to the core as given).
+ *   gate        [B,T,H,Dv] dtype dt device (required when T > 0).
+ *   gate_weight [Dv] fp32 device or NULL (ones), shared by the heads.
+ *   y           [B,T,H,Dv] dtype dt device; it may overlap no input, S_out or
+ *               the workspace (KDA_ERR_SHAPE).
+ *   workspace   kda_layer_fwd_workspace bytes, 256-byte aligned: the chunk
+ *               call's workspace plus an exchange area of Dv/16 x chunk
+ *               floats per chunk-head.
+ * The workgroups that share a head's Dv channels exchange per-token partial
+ * sums of squares through the workspace; when the device cannot hold all of
+ * them at once the call runs the core into y and the output side over y in
+ * place instead (same results).  Everything else as kda_chunk_fwd without
+ * M_out and P_out. */
+size_t kda_layer_fwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype dt);
+kda_status kda_layer_fwd(const void* q, const void* k, const void* v, const void* z,
+                         const void* beta_raw, const float* A_log, const float* S0,
+                         const float* conv_w, const float* conv_b, const void* conv_state,
+                         const void* gate, const float* gate_weight,
+                         void* y, float* S_out, int B, int T, int H, int Dk, int Dv, int chunk,
+                         float g_min, unsigned flags, kda_dtype dt,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* kda_chunk_fwd for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Same arguments, computation, validation and results as kda_chunk_fwd

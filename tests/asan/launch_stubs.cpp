@@ -15,6 +15,7 @@ hipError_t launch_chunk(int, int, int, const ChunkArgs&, hipStream_t, hipEvent_t
     return hipSuccess;
 }
 int chunk_kernel_count(int, int, int, int, int NC) { return NC > 0 ? 2 : 1; }
+hipError_t launch_layer(int, int, int, const ChunkArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_compose(int, const ComposeArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_fixup(int, int, const FixupArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
 int short_conv_tile() { return 32; }

@@ -137,6 +137,33 @@ int main() {
                               KDA_BF16, ws, wsn, nullptr),
            KDA_ERR_ALIGN, 0);
 
+    // ---- the layer body with the fused output side: the gate required, y
+    // apart from every input, the larger workspace
+    {
+        void* gate = buf(rows * Dv * 2);
+        float* gw = (float*)buf(Dv * 4);
+        void* y = buf(rows * Dv * 2);
+        const size_t lwn = kda_layer_fwd_workspace(B, T, H, Dk, Dv, C, KDA_BF16);
+        void* lws = buf(lwn);
+        auto layer = [&](const void* gate_, const float* gw_, void* y_, const float* cw_, void* ws_, size_t wsb) {
+            return kda_layer_fwd(q, k, v, z, br, A, nullptr, cw_, nullptr, nullptr, gate_, gw_, y_, S, B, T, H, Dk,
+                                 Dv, C, -5.f, 7, KDA_BF16, ws_, wsb, nullptr);
+        };
+        EXPECT(layer(gate, gw, y, nullptr, lws, lwn), KDA_OK, 1);
+        EXPECT(layer(gate, nullptr, y, cw, lws, lwn), KDA_OK, 1);
+        EXPECT(layer(nullptr, gw, y, nullptr, lws, lwn), KDA_ERR_NULL, 0);
+        EXPECT(layer((char*)gate + 2, gw, y, nullptr, lws, lwn), KDA_ERR_ALIGN, 0);
+        EXPECT(layer(gate, gw + 1, y, nullptr, lws, lwn), KDA_ERR_ALIGN, 0);
+        EXPECT(layer(gate, gw, gate, nullptr, lws, lwn), KDA_ERR_SHAPE, 0);
+        EXPECT(layer(gate, gw, v, nullptr, lws, lwn), KDA_ERR_SHAPE, 0);
+        EXPECT(layer(gate, gw, y, nullptr, lws, lwn - 1), KDA_ERR_WORKSPACE, 0);
+        EXPECT(layer(gate, gw, y, nullptr, lws, wsn), wsn < lwn ? KDA_ERR_WORKSPACE : KDA_OK, wsn < lwn ? 0 : 1);
+        EXPECT(kda_layer_fwd(q, k, v, z, br, A, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, y, S, B, 0, H,
+                             Dk, Dv, C, -5.f, 7, KDA_BF16, lws, lwn, nullptr),
+               KDA_OK, 1);
+        free(gate); free(gw); free(y); free(lws);
+    }
+
     // ---- the allocation-free entry point: its own size limit, no workspace
     EXPECT(kda_chunk_fwd_noalloc(q, k, v, z, br, A, nullptr, o, S, nullptr, nullptr, B, T, H, Dk, Dv, C, -5.f, 7,
                                  KDA_BF16, nullptr),

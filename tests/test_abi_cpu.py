@@ -125,6 +125,37 @@ def test_chunk_fwd_validation(lib):
     assert chunk_call(lib, H=0) == 0
 
 
+def test_layer_fwd_workspace_and_validation(lib):
+    # the chunk call's workspace plus Dv / 16 x chunk floats per chunk-head
+    for B, T, H, Dk, Dv, C, dt in ((4, 4096, 16, 128, 128, 32, 1), (1, 65, 2, 64, 32, 16, 0), (1, 0, 1, 16, 16, 64, 1)):
+        base = lib.kda_chunk_fwd_workspace(B, T, H, Dk, Dv, C, dt)
+        nc = -(-T // C)
+        extra = -(-(B * H * nc * (Dv // 16) * C * 4) // 256) * 256
+        assert lib.kda_layer_fwd_workspace(B, T, H, Dk, Dv, C, dt) == base + extra
+    assert lib.kda_layer_fwd_workspace(1, 64, 1, 96, 64, 64, 1) == 0
+    Q, K, V, Z, BR, G, Y, WS = (addr(i) for i in range(1, 9))
+    need = lib.kda_layer_fwd_workspace(2, 64, 2, 64, 64, 32, 1)
+
+    def call(**kw):
+        a = dict(q=Q, k=K, v=V, z=Z, beta_raw=BR, A_log=A16, S0=None, conv_w=None, conv_b=None, conv_state=None,
+                 gate=G, gate_weight=None, y=Y, S_out=None, B=2, T=64, H=2, Dk=64, Dv=64, chunk=32,
+                 g_min=-5.0, flags=7, dt=1, ws=WS, ws_bytes=need, stream=None)
+        a.update(kw)
+        return lib.kda_layer_fwd(*a.values())
+    assert call(gate=None) == 1
+    assert call(gate=G + 8) == 3
+    assert call(gate_weight=A16 + 4) == 3
+    assert call(conv_w=A16, conv_b=A16 + 4) == 3
+    assert call(y=G) == 2                     # y is the gate
+    assert call(y=V + 128) == 2               # y overlaps v
+    assert call(y=WS + 256) == 2              # y inside the workspace
+    assert call(ws_bytes=need - 1) == 6
+    assert call(ws_bytes=lib.kda_chunk_fwd_workspace(2, 64, 2, 64, 64, 32, 1)) == 6   # the chunk call's is too small
+    assert call(Dv=48) == 2
+    assert call(g_min=0.0) == 5
+    assert call(B=0) == 0
+
+
 def test_step_validation(lib):
     def call(**kw):
         a = dict(q=A16, k=A16, v=A16, z=A16, beta_raw=A16, A_log=A16, S=A16, o=A16,
