@@ -122,7 +122,7 @@ def decode_bytes(B, H, Dk, Dv, esize=2):
 
 def source_sha():
     h = hashlib.sha256()
-    for f in ("kda_chunk.hip", "kda_device.h", "kda_internal.h"):
+    for f in ("kda_chunk.hip", "kda_chunk_kernels.h", "kda_device.h", "kda_internal.h"):
         with open(os.path.join(ROOT, "gated_delta_rule_82_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

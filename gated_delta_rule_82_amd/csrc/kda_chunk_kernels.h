@@ -45,6 +45,9 @@ namespace kda {
 // cache policy of copies whose data is read once: non-temporal (the nt bit of
 // the gfx950 cache-policy operand)
 constexpr int kCopyNT = 2;
+// cache policy of copies of data other workgroups write during the kernel:
+// the sc1 bit, as the agent-scope atomic loads of the same data take it
+constexpr int kCopyCoherent = 16;
 
 // Largest block-local decay (in log2 units) the factored diagonal product
 // takes: its column factor 2^-L then stays 2^10 below the float maximum, the
@@ -765,21 +768,27 @@ constexpr int kGateSpinLimit = 1 << 20;
 // ([C tokens][16 NS]).  Two copy waves fill the slots with global_load_lds,
 // 1 KiB per instruction ("piece"); copy wave 0 issues the first kPer0 pieces
 // of a chunk, copy wave 1 the rest (each streams a contiguous half).
-template <typename T, int DK, int C, int NS, bool SPREAD = true, int NOT = 2>
+// GATE (the fused output side): the slot of chunk n also carries the gate
+// tile of chunk n - kGateLag (laid out as the values) and the exchange area of
+// that chunk (partial sums of squares [C][kGateGroups] fp32, read past the
+// caches), so the compute waves that store chunk n - kGateLag's rows during
+// chunk n find both in LDS.
+template <typename T, int DK, int C, int NS, bool SPREAD = true, bool GATE = false>
 struct InterRing {
     static constexpr BlockLayout L = block_layout(sizeof(T), DK, C);
     static constexpr int kVRow = 16 * NS * (int)sizeof(T);   // bytes of one token's staged values
     static constexpr size_t kVBytes = round_up((size_t)C * kVRow, 1024);
-    static constexpr size_t kSlot = L.bytes + kVBytes;
-    // output staging: NOT tiles of [C tokens][16 NS] (a ring over chunks), so
-    // each output row leaves as one 16 NS-element segment instead of NS
-    // strips; with more than two tiles (the fused output side) they are
-    // followed by two sets (chunk parity) of NS per-token partial sums of
-    // squares [NS][C] fp32
+    static constexpr size_t kGBytes = GATE ? kVBytes : 0;                          // gate tile
+    static constexpr size_t kPBytes = GATE ? round_up((size_t)kGateGroups * C * 4, 1024) : 0;  // exchange area
+    static constexpr size_t kSlot = L.bytes + kVBytes + kGBytes + kPBytes;
+    // output staging: tiles of [C tokens][16 NS] (a ring over chunks), so each
+    // output row leaves as one 16 NS-element segment instead of NS strips:
+    // two (a chunk's rows leave during the next chunk), or with GATE
+    // kSlots + 4 (they leave kGateLag = kSlots + 3 chunks later) followed by
+    // two sets (chunk parity) of NS per-token partial sums of squares [NS][C]
     static constexpr int kORow = 16 * NS * (int)sizeof(T);  // bytes of one token's output row
     static constexpr size_t kOTile = (size_t)C * kORow;
-    static constexpr size_t kSsBytes = NOT > 2 ? 2 * (size_t)NS * C * 4 : 0;
-    static constexpr size_t kOBytes = NOT * kOTile + kSsBytes;
+    static constexpr size_t kSsBytes = GATE ? 2 * (size_t)NS * C * 4 : 0;
     // Bank-spread layouts (SPREAD).  A compute wave reads the values of
     // tokens 4 gq + i (i fixed per instruction) and writes output rows r, so
     // rows four apart must not share banks.  Values: a 1 KiB piece holds
@@ -819,17 +828,32 @@ struct InterRing {
     }
     static constexpr int kBlkPieces = (int)((L.bytes + 1023) / 1024);
     static constexpr int kVPieces = (int)(kVBytes / 1024);
-    static constexpr int kPieces = kBlkPieces + kVPieces;
+    static constexpr int kPPieces = (int)(kPBytes / 1024);
+    static constexpr int kPieces = kBlkPieces + kVPieces + (GATE ? kVPieces + kPPieces : 0);
     static constexpr int kPer0 = (kPieces + 1) / 2;  // pieces per chunk of copy wave 0
     static constexpr int kPer1 = kPieces / 2;        // ... and of copy wave 1
     // as many slots as fit, up to 6, with the copies in flight countable by
-    // vmcnt (at most kSlots - 2 chunks of one wave are waited over)
+    // vmcnt (at most kSlots - 2 chunks of one wave are waited over); with
+    // GATE every slot brings one more output tile
     // (a configuration whose one slot and tiles exceed the LDS is never launched)
-    static constexpr bool kFits = kSlot + kOBytes <= kLdsBudget;
-    static constexpr int kSlotsLds = kFits ? (int)((kLdsBudget - kOBytes) / kSlot) : 1;
+    static constexpr size_t kFixed = (GATE ? 4 : 2) * kOTile + kSsBytes;
+    static constexpr size_t kPerSlot = kSlot + (GATE ? kOTile : 0);
+    static constexpr bool kFitsOne = kPerSlot + kFixed <= kLdsBudget;
+    static constexpr int kSlotsLds = kFitsOne ? (int)((kLdsBudget - kFixed) / kPerSlot) : 1;
     static constexpr int kSlotsVm = 2 + 63 / (kPer0 > 0 ? kPer0 : 1);
     static constexpr int kSlots = kSlotsLds < 6 ? (kSlotsLds < kSlotsVm ? kSlotsLds : kSlotsVm)
                                                 : (6 < kSlotsVm ? 6 : kSlotsVm);
+    // GATE takes at least two slots (with one, the fused output side is not
+    // offered and the call takes the separate output-side kernel)
+    static constexpr bool kFits = kFitsOne && (!GATE || kSlots >= 2);
+    // GATE: chunks between a chunk's products and its store.  The slot of
+    // chunk n is copied from the start of chunk n - kSlots + 1 (the ring's
+    // depth), so the partials of chunk n - kGateLag it carries were published
+    // three chunks before: a group up to that far behind the others costs
+    // them no read of the exchange area.
+    static constexpr int kGateLag = kSlots + 3;
+    static constexpr int kOT = GATE ? kGateLag + 1 : 2;  // output tiles
+    static constexpr size_t kOBytes = kOT * kOTile + kSsBytes;
     static_assert(kSlots >= 1, "a chunk block must fit in LDS");
     static_assert(kSlots <= 2 || (kSlots - 2) * kPer0 < 64, "vmcnt range");
     static_assert(kVRow % 16 == 0 && 1024 % kVRow == 0, "value rows tile a piece");
@@ -874,22 +898,28 @@ __device__ __forceinline__ void wait_chunks(int m) {
 // stored ("KDA 模块交互式演示" §1.7 完整层; "Implémenter KDA" 'La porte de
 // sortie de rang plein'): y = sigmoid(gate) * o / sqrt(mean o^2 + 1e-6) * gw
 // over the head's Dv channels, which the n_groups workgroups of a (b, h)
-// share.  Each workgroup publishes, per chunk, the partial sum of squares of
-// its columns for every token (o rounded to the output type first, as a
-// stored o would be) to the exchange area, one chunk after the chunk's
-// products; it stores a chunk's rows three chunks after them, once every
-// group's partial for the chunk is there.  A group waits only for partials
-// of chunks at least two behind its own, which the others publish without
-// waiting on anything later, so the wait ends whenever all workgroups of the
-// (b, h) are resident together (the launch only takes this path when the
-// whole grid is).  Each wait is also bounded: past the bound the row is
-// written as NaN rather than hang.
+// share.  Each workgroup publishes, at the start of chunk n + 1, the partial
+// sums of squares of its columns for every token of chunk n (o rounded to
+// the output type first, as a stored o would be) to the exchange area.  The
+// copy waves bring chunk m's gate tile and every group's partials for it into
+// the slot of chunk m + D (D = kGateLag, three more than the ring's depth, so
+// the copy starts well after the partials were published), and the compute waves
+// store chunk m's rows during chunk m + D from the tile kept since.  A
+// partial not yet published when it was copied (a group more than a chunk
+// behind) is read again from the exchange area until it is there.  A group
+// waits only for partials of chunks well behind its own, which the others
+// publish without waiting on anything later, so the wait ends whenever all
+// workgroups of the (b, h) are resident together (the launch only takes
+// this path when the whole grid is).  Each wait is also bounded: past the
+// bound the row is written as NaN rather than hang.
 template <typename T, int DK, int C, int NW, int SPW, bool CONV = false, bool GATE = false>
 __global__ __launch_bounds__(64 * (NW + 2)) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void kda_inter_kernel(const InterArgs a) {
     constexpr int NS = NW * SPW;
-    constexpr int kOT = GATE ? 4 : 2;  // output tiles: a chunk is stored 3 (GATE) or 1 chunk later
-    using Ring = InterRing<T, DK, C, NS, !CONV, kOT>;
+    using Ring = InterRing<T, DK, C, NS, !CONV, GATE>;
+    constexpr int kOT = Ring::kOT;       // output tiles: a chunk's rows leave 1 or (GATE) D chunks later
+    constexpr int D = Ring::kGateLag;
+    if constexpr (GATE && !Ring::kFits) return;  // never launched
     constexpr BlockLayout L = Ring::L;
     constexpr int K = Ring::kSlots;
     constexpr bool kAhead = K >= 3;  // next chunk's operands are read during the current one
@@ -938,6 +968,8 @@ void kda_inter_kernel(const InterArgs a) {
         const uint32_t tstride = (uint32_t)(a.H * a.Dv * (int)sizeof(T));  // bytes per token
         const unsigned char* vrow0 = vsrc + (((size_t)b * a.T * a.H + h) * a.Dv) * sizeof(T);
         const uint32_t vlane_tok = (uint32_t)Ring::dma_row(lane);
+        // gate rows of (b, h) (GATE), addressed like the values
+        const unsigned char* grow0 = GATE ? reinterpret_cast<const unsigned char*>(a.gate) + (vrow0 - vsrc) : nullptr;
         auto issue = [&](int n) {
             unsigned char* slot = slot_of(n);
             const unsigned char* gb = gblk + (size_t)(n - a.c0) * L.bytes;
@@ -955,13 +987,41 @@ void kda_inter_kernel(const InterArgs a) {
                         __builtin_amdgcn_global_load_lds(
                             (const __attribute__((address_space(1))) void*)(gb + off),
                             (__attribute__((address_space(3))) void*)(slot + p * 1024), 16, 0, 0);
-                } else {
+                } else if (p < Ring::kBlkPieces + Ring::kVPieces) {
                     const int j = p - Ring::kBlkPieces;
                     uint32_t tok = (uint32_t)(j * kTokPerPiece) + vlane_tok;
                     tok = tok < lim ? tok : lim - 1;
                     __builtin_amdgcn_global_load_lds(
                         (const __attribute__((address_space(1))) void*)(vb + (tok * tstride + vcol_b)),
                         (__attribute__((address_space(3))) void*)(slot + L.bytes + j * 1024), 16, 0, kCopyNT);
+                } else if constexpr (GATE) {
+                    // chunk mg = n - D (chunk c0 before the first D chunks: loaded, unused)
+                    const int mg = max(n - D, a.c0);
+                    if (p < Ring::kBlkPieces + 2 * Ring::kVPieces) {
+                        // its gate tile, staged like the values
+                        const int j = p - Ring::kBlkPieces - Ring::kVPieces;
+                        const uint32_t glim = (uint32_t)min(a.T - mg * C, C);
+                        uint32_t tok = (uint32_t)(j * kTokPerPiece) + vlane_tok;
+                        tok = tok < glim ? tok : glim - 1;
+                        const unsigned char* gtb = grow0 + (size_t)mg * C * tstride;
+                        __builtin_amdgcn_global_load_lds(
+                            (const __attribute__((address_space(1))) void*)(gtb + (tok * tstride + vcol_b)),
+                            (__attribute__((address_space(3))) void*)(slot + L.bytes + Ring::kVBytes + j * 1024), 16,
+                            0, kCopyNT);
+                    } else {
+                        // every group's partials of it, past the caches (as the
+                        // exchange area's coherent loads and stores go)
+                        const int j = p - Ring::kBlkPieces - 2 * Ring::kVPieces;
+                        const int off = j * 1024 + lane * 16;
+                        if (off < kGateGroups * C * 4)
+                            __builtin_amdgcn_global_load_lds(
+                                (const __attribute__((address_space(1))) void*)(
+                                    reinterpret_cast<const unsigned char*>(
+                                        a.gss + ((size_t)bh * a.wsNC + (size_t)(mg - a.c0)) * (kGateGroups * C)) +
+                                    off),
+                                (__attribute__((address_space(3))) void*)(slot + L.bytes + 2 * Ring::kVBytes + j * 1024),
+                                16, 0, kCopyCoherent);
+                    }
                 }
             }
         };
@@ -1078,7 +1138,7 @@ void kda_inter_kernel(const InterArgs a) {
                         : nullptr;
     }
     auto store_rows = [&](int m) {  // rows of chunk m's tile owned by this wave
-        const unsigned char* tile = s_otile + (size_t)((m - a.c0) & (kOT - 1)) * Ring::kOTile;
+        const unsigned char* tile = s_otile + (size_t)((unsigned)(m - a.c0) % (unsigned)kOT) * Ring::kOTile;
 #pragma unroll
         for (int st = 0; st < kOSteps; ++st) {
             const int gi = st * 64 + lane;
@@ -1101,19 +1161,15 @@ void kda_inter_kernel(const InterArgs a) {
         }
     };
 
-    // Fused output side (GATE).  Exchange area of chunk m: n_groups x C
-    // partial sums of squares, group-major.  This lane's granules of a stored
-    // chunk keep their gate values, the groups' partials of their tokens and
-    // the output weights of their columns in registers.
-    constexpr int kGMax = 8;  // workgroups per (b, h): Dv / 16 strips at most
+    // Fused output side (GATE).  Exchange area of chunk m: the partial sums of
+    // squares of its C tokens, token-major with room for kGateGroups groups
+    // (one workgroup per 16 NS value columns of the head: at most Dv / 16 = 8).
+    constexpr int kGMax = kGateGroups;
     float* s_ss = reinterpret_cast<float*>(s_otile + (size_t)kOT * Ring::kOTile);  // [2][NW][C]
     auto gss_at = [&](int m, int grp_, int tok) -> float* {
-        return a.gss + (((size_t)bh * a.wsNC + (size_t)(m - a.c0)) * a.n_groups + grp_) * C + tok;
+        return a.gss + (((size_t)bh * a.wsNC + (size_t)(m - a.c0)) * C + tok) * kGMax + grp_;
     };
     bool gate_expired = false;  // a wait of this lane ran out (its rows are then NaN)
-    uint4 gpre[GATE ? kOSteps : 1];
-    float ppre[GATE ? kOSteps : 1][GATE ? kGMax : 1];
-    float wv[GATE ? kOSteps : 1][GATE ? kEpg : 1];
     // where granule st of this lane goes: token row, strip of the group, part of it
     auto granule = [&](int st, int& tok, int& sl, int& part) -> bool {
         const int gi = st * 64 + lane;
@@ -1123,6 +1179,7 @@ void kda_inter_kernel(const InterArgs a) {
         part = og % kGps;
         return gi < kTpw * kGpr && grp * NS + sl < a.n_strips;
     };
+    float wv[GATE ? kOSteps : 1][GATE ? kEpg : 1];  // output weights of this lane's granules
     if constexpr (GATE) {
 #pragma unroll
         for (int st = 0; st < kOSteps; ++st) {
@@ -1133,8 +1190,8 @@ void kda_inter_kernel(const InterArgs a) {
             for (int e = 0; e < kEpg; ++e) wv[st][e] = a.gw ? a.gw[col + e] : 1.f;
         }
     }
-    // rank this workgroup's partials of chunk m (the tile's rows, summed over the
-    // compute waves in a fixed order) in the exchange area
+    // put this workgroup's partials of chunk m (the tile's rows, summed over
+    // the compute waves in a fixed order) in the exchange area
     auto publish = [&](int m) {
         if (w == 0 && lane < C) {
             const float* ss = s_ss + (size_t)((m - a.c0) & 1) * NW * C;
@@ -1144,71 +1201,113 @@ void kda_inter_kernel(const InterArgs a) {
             __hip_atomic_store(gss_at(m, grp, lane), p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     };
-    // request chunk m's gate granules and every group's partials of their tokens
-    auto prefetch_gate = [&](int m) {
+    // partial p of group g for token tok of chunk m as copied; read again from
+    // the exchange area while it is unpublished (-1; a NaN partial passes)
+    auto settle = [&](float p, int m, int g, int tok) -> float {
+        for (int it = 0; p < 0.f; ++it) {
+            if (gate_expired || it >= kGateSpinLimit) {
+                gate_expired = true;
+                return __builtin_nanf("");
+            }
+            __builtin_amdgcn_s_sleep(2);
+            p = __hip_atomic_load(gss_at(m, g, tok), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        return p;
+    };
+    // chunk m's rows of this wave: o from its tile, normalised and gated
+    auto emit_gated = [&](int m, int st, int tok, int sl, int part, const uint4& gt, float tot) {
+        const unsigned char* tile = s_otile + (size_t)((unsigned)(m - a.c0) % (unsigned)kOT) * Ring::kOTile;
+        unsigned char* base = nullptr;
+        uint32_t stride = 0;
+#pragma unroll
+        for (int t = 0; t < NS; ++t)
+            if (sl == t) { base = gbase[t]; stride = gstride[t]; }
+        const int og = sl * kGps + part;
+        uint4 v = *reinterpret_cast<const uint4*>(tile + (Ring::ooff(tok, (uint32_t)og * 16) & ~15u));
+        if (Ring::kOHalf && ((tok >> 3) & 1)) v = make_uint4(v.z, v.w, v.x, v.y);  // halves swapped in LDS
+        const float inv = __builtin_amdgcn_rsqf(tot * (1.f / (float)a.Dv) + kGateRmsEps);
+        float y[kEpg];
+#pragma unroll
+        for (int e = 0; e < kEpg; ++e)
+            y[e] = sigmoidf_(Gran16<T>::get(gt, e)) * Gran16<T>::get(v, e) * inv * wv[st][e];
+        *reinterpret_cast<uint4*>(base + (size_t)m * C * stride + (uint32_t)tok * stride + (uint32_t)(part * 16)) =
+            Gran16<T>::pack(y);
+    };
+    // chunk m = n - D during chunk n: gate and partials from the slot of chunk n.
+    // All LDS reads go out together; the partials are summed without a branch
+    // and read again from the exchange area only if one of them was copied
+    // before its group published it.
+    auto store_gated_lds = [&](int m, const unsigned char* slot) {
+        const unsigned char* gtile = slot + L.bytes + Ring::kVBytes;
+        const float* part_s = reinterpret_cast<const float*>(slot + L.bytes + 2 * Ring::kVBytes);
 #pragma unroll
         for (int st = 0; st < kOSteps; ++st) {
             int tok, sl, part;
             if (granule(st, tok, sl, part) && m * C + tok < a.T) {
-                unsigned char* base = nullptr;
-                uint32_t stride = 0;
+                const int og = sl * kGps + part;
+                const uint4 gt = *reinterpret_cast<const uint4*>(gtile + Ring::voff(tok, (uint32_t)og * 16));
+                const float4 p0 = *reinterpret_cast<const float4*>(part_s + tok * kGMax);
+                const float4 p1 = *reinterpret_cast<const float4*>(part_s + tok * kGMax + 4);
+                const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+                float tot = 0.f, lo = 0.f;
 #pragma unroll
-                for (int t = 0; t < NS; ++t)
-                    if (sl == t) { base = gbase[t]; stride = gstride[t]; }
-                const size_t off = (size_t)(base - reinterpret_cast<unsigned char*>(a.o)) + (size_t)m * C * stride +
-                                   (uint32_t)tok * stride + (uint32_t)(part * 16);
-                typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-                const u32x4 gv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                    reinterpret_cast<const unsigned char*>(a.gate) + off));
-                gpre[st] = make_uint4(gv[0], gv[1], gv[2], gv[3]);
+                for (int g = 0; g < kGMax; ++g) {
+                    const float x = g < a.n_groups ? pv[g] : 0.f;
+                    tot += x;
+                    lo = fminf(lo, x);
+                }
+                if (lo < 0.f) {  // copied before publication: wait for the late ones
+                    tot = 0.f;
 #pragma unroll
-                for (int g = 0; g < kGMax; ++g)
-                    if (g < a.n_groups)
-                        ppre[st][g] = __hip_atomic_load(gss_at(m, g, tok), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    for (int g = 0; g < kGMax; ++g)
+                        if (g < a.n_groups) tot += settle(pv[g], m, g, tok);
+                }
+                emit_gated(m, st, tok, sl, part, gt, tot);
             }
         }
     };
-    // chunk m's rows of this wave, gated and normalised, from the tile
-    auto store_gated = [&](int m) {
-        const unsigned char* tile = s_otile + (size_t)((m - a.c0) & (kOT - 1)) * Ring::kOTile;
+    // the last D chunks after the loop: their gates and partials are read
+    // straight from memory, all requests in flight together
+    constexpr int kDB = D;
+    auto drain_gated = [&](int m0, int m1) {
+        uint4 gpre[GATE ? kDB : 1][GATE ? kOSteps : 1];
+        float ppre[GATE ? kDB : 1][GATE ? kOSteps : 1][GATE ? kGMax : 1];
 #pragma unroll
-        for (int st = 0; st < kOSteps; ++st) {
-            int tok, sl, part;
-            if (granule(st, tok, sl, part) && m * C + tok < a.T) {
-                unsigned char* base = nullptr;
-                uint32_t stride = 0;
+        for (int i = 0; i < kDB; ++i) {
+            const int m = m0 + i;
 #pragma unroll
-                for (int t = 0; t < NS; ++t)
-                    if (sl == t) { base = gbase[t]; stride = gstride[t]; }
-                const int og = sl * kGps + part;
-                uint4 v = *reinterpret_cast<const uint4*>(tile + (Ring::ooff(tok, (uint32_t)og * 16) & ~15u));
-                if (Ring::kOHalf && ((tok >> 3) & 1)) v = make_uint4(v.z, v.w, v.x, v.y);  // halves swapped in LDS
-                float tot = 0.f;
+            for (int st = 0; st < kOSteps; ++st) {
+                int tok, sl, part;
+                if (m < m1 && granule(st, tok, sl, part) && m * C + tok < a.T) {
+                    unsigned char* base = nullptr;
+                    uint32_t stride = 0;
 #pragma unroll
-                for (int g = 0; g < kGMax; ++g) {
-                    if (g < a.n_groups) {
-                        float p = ppre[st][g];
-                        // -1: not yet published; a NaN partial (NaN outputs) passes.
-                        // After one expired wait the lane waits no more.
-                        for (int it = 0; p < 0.f; ++it) {
-                            if (gate_expired || it >= kGateSpinLimit) {
-                                gate_expired = true;
-                                p = __builtin_nanf("");
-                                break;
-                            }
-                            __builtin_amdgcn_s_sleep(2);
-                            p = __hip_atomic_load(gss_at(m, g, tok), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        }
-                        tot += p;
-                    }
+                    for (int t = 0; t < NS; ++t)
+                        if (sl == t) { base = gbase[t]; stride = gstride[t]; }
+                    const size_t off = (size_t)(base - reinterpret_cast<unsigned char*>(a.o)) + (size_t)m * C * stride +
+                                       (uint32_t)tok * stride + (uint32_t)(part * 16);
+                    gpre[i][st] = *reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(a.gate) + off);
+#pragma unroll
+                    for (int g = 0; g < kGMax; ++g)
+                        if (g < a.n_groups)
+                            ppre[i][st][g] =
+                                __hip_atomic_load(gss_at(m, g, tok), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
-                const float inv = __builtin_amdgcn_rsqf(tot * (1.f / (float)a.Dv) + kGateRmsEps);
-                float y[kEpg];
+            }
+        }
 #pragma unroll
-                for (int e = 0; e < kEpg; ++e)
-                    y[e] = sigmoidf_(Gran16<T>::get(gpre[st], e)) * Gran16<T>::get(v, e) * inv * wv[st][e];
-                *reinterpret_cast<uint4*>(base + (size_t)m * C * stride + (uint32_t)tok * stride + (uint32_t)(part * 16)) =
-                    Gran16<T>::pack(y);
+        for (int i = 0; i < kDB; ++i) {
+            const int m = m0 + i;
+#pragma unroll
+            for (int st = 0; st < kOSteps; ++st) {
+                int tok, sl, part;
+                if (m < m1 && granule(st, tok, sl, part) && m * C + tok < a.T) {
+                    float tot = 0.f;
+#pragma unroll
+                    for (int g = 0; g < kGMax; ++g)
+                        if (g < a.n_groups) tot += settle(ppre[i][st][g], m, g, tok);
+                    emit_gated(m, st, tok, sl, part, gpre[i][st], tot);
+                }
             }
         }
     };
@@ -1430,7 +1529,7 @@ void kda_inter_kernel(const InterArgs a) {
                 // then the next chunk's serial operands) between the products,
                 // so the LDS streams while the matrix core works
                 if constexpr (kInterleave) interleave_mfma_ds<kMfmaPerChunk, kDsPerChunk>();
-                unsigned char* tile = s_otile + (size_t)((n - a.c0) & (kOT - 1)) * Ring::kOTile;
+                unsigned char* tile = s_otile + (size_t)((unsigned)(n - a.c0) % (unsigned)kOT) * Ring::kOTile;
                 const uint32_t opos = Ring::ooff(r, (uint32_t)(((w * SPW + j) * 16 + 4 * gq) * (int)sizeof(T)));
 #pragma unroll
                 for (int Ib = 0; Ib < NBK; ++Ib)
@@ -1459,10 +1558,7 @@ void kda_inter_kernel(const InterArgs a) {
             if (lane < C) ss[lane] = 0.f;
         }
         if constexpr (GATE) {
-            // chunk n - 3 leaves (every group published it by its chunk n - 2);
-            // chunk n - 2's gate and partials are requested for the next round
-            if (n - 3 >= a.c0) store_gated(n - 3);
-            if (n - 2 >= a.c0) prefetch_gate(n - 2);
+            if (n - D >= a.c0) store_gated_lds(n - D, cur);  // its gate and partials came with this chunk's slot
         } else if (n > a.c0) {
             store_rows(n - 1);  // the previous chunk's tile was completed before the last barrier
         }
@@ -1472,10 +1568,7 @@ void kda_inter_kernel(const InterArgs a) {
     if constexpr (GATE) {
         if (a.nc > 0) {
             publish(cend - 1);
-            for (int m = max(a.c0, cend - 3); m < cend; ++m) {
-                if (m != cend - 3) prefetch_gate(m);  // chunk cend - 3 was requested in the loop
-                store_gated(m);
-            }
+            drain_gated(max(a.c0, cend - D), cend);
         }
     } else if (a.nc > 0) {
         store_rows(cend - 1);
@@ -1499,7 +1592,7 @@ void kda_inter_kernel(const InterArgs a) {
 // (CONV: with the fused convolution of v; GATE: with the fused output side).
 template <typename T, int DK, int C, int NW, bool CONV = false, bool GATE = false>
 struct InterKernel {
-    using Ring = InterRing<T, DK, C, NW, !CONV, GATE ? 4 : 2>;
+    using Ring = InterRing<T, DK, C, NW, !CONV, GATE>;
     static constexpr int kThreads = 64 * (NW + 2);
     static constexpr size_t kLds = (size_t)Ring::kSlots * Ring::kSlot + Ring::kOBytes;
     static const void* fn() { return reinterpret_cast<const void*>(kda_inter_kernel<T, DK, C, NW, 1, CONV, GATE>); }
@@ -1585,6 +1678,7 @@ struct ChunkLaunch {
                 if (fits[i] && g < best_g) { best_g = g; nw = w; }
             }
         }
+        if (!nw) nw = 4;  // no instantiation fits (GATE only: the caller takes the separate path)
         ea.n_groups = (ea.n_strips + nw - 1) / nw;
         if (a.conv_w) {
             const int Hk = a.H / a.G;
@@ -1597,7 +1691,7 @@ struct ChunkLaunch {
         ea.gate = a.gate; ea.gw = a.gate_w; ea.gss = a.gss;
     }
     // floats of the output side's exchange area per chunk-head
-    int gss_per_chunk() const { return ea.n_groups * C; }
+    int gss_per_chunk() const { return kGateGroups * C; }
 
     template <bool CONV>
     hipError_t set_attributes_c() const {

@@ -90,14 +90,17 @@ __host__ __device__ constexpr size_t chunk_workspace_bytes(int elem_bytes, int D
     return nbuf * BH * per * block_layout(elem_bytes, DK, C).bytes + round_up(BH * (size_t)DK * (DK + Dv) * 4, 256);
 }
 
+// Workgroups that can share a head's value columns in the fused output side
+// (one per 16 value columns or more, Dv <= 128).
+constexpr int kGateGroups = 8;
 // Workspace of the layer body: that of the chunk call, then the output side's
-// exchange area, Dv / 16 x C floats per chunk-head of a slice.
+// exchange area, kGateGroups x C floats per chunk-head of a slice.
 __host__ __device__ constexpr size_t layer_gss_offset(int elem_bytes, int DK, int Dv, int C, size_t BH, size_t per) {
     return chunk_workspace_bytes(elem_bytes, DK, Dv, C, BH, per, 1);
 }
 __host__ __device__ constexpr size_t layer_workspace_bytes(int elem_bytes, int DK, int Dv, int C, size_t BH,
                                                            size_t per) {
-    return layer_gss_offset(elem_bytes, DK, Dv, C, BH, per) + round_up(BH * per * (size_t)(Dv / 16) * C * 4, 256);
+    return layer_gss_offset(elem_bytes, DK, Dv, C, BH, per) + round_up(BH * per * (size_t)kGateGroups * C * 4, 256);
 }
 
 struct StepArgs {

@@ -175,7 +175,7 @@ kda_status kda_chunk_fwd_conv(const void* q, const void* k, const void* v, const
  *   y           [B,T,H,Dv] dtype dt device; it may overlap no input, S_out or
  *               the workspace (KDA_ERR_SHAPE).
  *   workspace   kda_layer_fwd_workspace bytes, 256-byte aligned: the chunk
- *               call's workspace plus an exchange area of Dv/16 x chunk
+ *               call's workspace plus an exchange area of 8 x chunk
  *               floats per chunk-head.
  * The workgroups that share a head's Dv channels exchange per-token partial
  * sums of squares through the workspace; when the device cannot hold all of

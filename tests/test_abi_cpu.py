@@ -126,11 +126,11 @@ def test_chunk_fwd_validation(lib):
 
 
 def test_layer_fwd_workspace_and_validation(lib):
-    # the chunk call's workspace plus Dv / 16 x chunk floats per chunk-head
+    # the chunk call's workspace plus 8 x chunk floats per chunk-head
     for B, T, H, Dk, Dv, C, dt in ((4, 4096, 16, 128, 128, 32, 1), (1, 65, 2, 64, 32, 16, 0), (1, 0, 1, 16, 16, 64, 1)):
         base = lib.kda_chunk_fwd_workspace(B, T, H, Dk, Dv, C, dt)
         nc = -(-T // C)
-        extra = -(-(B * H * nc * (Dv // 16) * C * 4) // 256) * 256
+        extra = -(-(B * H * nc * 8 * C * 4) // 256) * 256
         assert lib.kda_layer_fwd_workspace(B, T, H, Dk, Dv, C, dt) == base + extra
     assert lib.kda_layer_fwd_workspace(1, 64, 1, 96, 64, 64, 1) == 0
     Q, K, V, Z, BR, G, Y, WS = (addr(i) for i in range(1, 9))
