@@ -180,8 +180,12 @@ kda_status kda_chunk_fwd_conv(const void* q, const void* k, const void* v, const
  * The workgroups that share a head's Dv channels exchange per-token partial
  * sums of squares through the workspace; when the device cannot hold all of
  * them at once the call runs the core into y and the output side over y in
- * place instead (same results).  Everything else as kda_chunk_fwd without
- * M_out and P_out. */
+ * place instead (same results).  The exchange counts on the device holding
+ * the call's whole grid: calls of this entry point running at the same time
+ * on one device (different streams) can share out its capacity so that
+ * neither grid is whole, and their waits then run out after about a second
+ * and write NaN rows; issue them in order on one stream.  Everything else as
+ * kda_chunk_fwd without M_out and P_out. */
 size_t kda_layer_fwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype dt);
 kda_status kda_layer_fwd(const void* q, const void* k, const void* v, const void* z,
                          const void* beta_raw, const float* A_log, const float* S0,

@@ -1,6 +1,6 @@
 """HIP graph capture of the C-ABI calls a serving loop captures: the
-allocation-free chunk call, the chunk call on a caller workspace and the
-decode step.  The library launches kernels on the caller's stream and never
+allocation-free chunk call, the chunk call on a caller workspace, the layer
+call with the fused output side and the decode step.  The library launches kernels on the caller's stream and never
 allocates, synchronises or clears memory with a memset, so a call records
 into a graph as it is.  Each graph is replayed three times on new inputs
 copied into its static tensors, with eager work and synchronisations between
@@ -69,6 +69,40 @@ def test_chunk_call_replays_equal_eager(entry):
         o_e, S_e = kda.chunk_fwd(*(inp[n] for n in NAMES), chunk=C)  # eager, its own outputs and workspace
         torch.cuda.synchronize()
         assert torch.equal(o_g, o_e), f"replay {i}: o differs from the eager call"
+        assert torch.equal(S_g, S_e), f"replay {i}: S differs from the eager call"
+
+
+def test_layer_call_replays_equal_eager():
+    """kda_layer_fwd: its intra kernel marks the output side's exchange area
+    unwritten on every call, so every replay of the graph (and the eager call
+    on another workspace between replays) exchanges afresh."""
+    B, T, H, D, C = 2, 300, 4, 128, 32
+    sets = [to_dev(inputs.make_inputs(B, T, H, D, D, "bf16", seed=950 + i, a_std=0.5, s_std=0.1))
+            for i in range(3)]
+    g_gen = torch.Generator().manual_seed(951)
+    gates = [torch.randn(B, T, H, D, generator=g_gen).to(torch.bfloat16).cuda() for _ in range(3)]
+    gw = (torch.rand(D, generator=g_gen) + 0.5).float().cuda()
+    st = {n: sets[0][n].clone() for n in NAMES}
+    gate = gates[0].clone()
+    y = torch.empty(B, T, H, D, dtype=torch.bfloat16, device="cuda")
+    S = torch.empty(B, H, D, D, dtype=torch.float32, device="cuda")
+    ws = torch.empty(kda.layer_workspace_bytes(B, T, H, D, D, C, torch.bfloat16), dtype=torch.uint8, device="cuda")
+
+    def call():
+        kda.layer_fwd(*(st[n] for n in NAMES[:6]), gate, gw, st["S0"], chunk=C, y=y, S_out=S, workspace=ws)
+
+    print(f"graph: layer call B{B} T{T} H{H} D{D} bf16 chunk {C}", flush=True)
+    g = capture(call)
+    for i, inp in enumerate(sets):
+        for n in NAMES:
+            st[n].copy_(inp[n])
+        gate.copy_(gates[i])
+        g.replay()
+        torch.cuda.synchronize()
+        y_g, S_g = y.clone(), S.clone()
+        y_e, S_e = kda.layer_fwd(*(inp[n] for n in NAMES[:6]), gates[i], gw, inp["S0"], chunk=C)
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, y_e), f"replay {i}: y differs from the eager call"
         assert torch.equal(S_g, S_e), f"replay {i}: S differs from the eager call"
 
 
