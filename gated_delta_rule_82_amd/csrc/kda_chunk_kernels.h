@@ -771,7 +771,7 @@ constexpr int kGateSpinLimit = 1 << 20;
 // GATE (the fused output side): the slot of chunk n also carries the gate
 // tile of chunk n - kGateLag (laid out as the values) and the exchange area of
 // that chunk (partial sums of squares [C][kGateGroups] fp32, read past the
-// caches), so the compute waves that store chunk n - kGateLag's rows during
+// caches), so the store waves that store chunk n - kGateLag's rows during
 // chunk n find both in LDS.
 template <typename T, int DK, int C, int NS, bool SPREAD = true, bool GATE = false>
 struct InterRing {
@@ -785,10 +785,11 @@ struct InterRing {
     // output row leaves as one 16 NS-element segment instead of NS strips:
     // two (a chunk's rows leave during the next chunk), or with GATE
     // kSlots + 4 (they leave kGateLag = kSlots + 3 chunks later) followed by
-    // two sets (chunk parity) of NS per-token partial sums of squares [NS][C]
+    // two sets (chunk parity) of the compute waves' per-lane partial sums of
+    // squares [C tokens][NS strips x 4 lane groups]
     static constexpr int kORow = 16 * NS * (int)sizeof(T);  // bytes of one token's output row
     static constexpr size_t kOTile = (size_t)C * kORow;
-    static constexpr size_t kSsBytes = GATE ? 2 * (size_t)NS * C * 4 : 0;
+    static constexpr size_t kSsBytes = GATE ? 2 * (size_t)C * NS * 4 * 4 : 0;
     // Bank-spread layouts (SPREAD).  A compute wave reads the values of
     // tokens 4 gq + i (i fixed per instruction) and writes output rows r, so
     // rows four apart must not share banks.  Values: a 1 KiB piece holds
@@ -903,8 +904,10 @@ __device__ __forceinline__ void wait_chunks(int m) {
 // the output type first, as a stored o would be) to the exchange area.  The
 // copy waves bring chunk m's gate tile and every group's partials for it into
 // the slot of chunk m + D (D = kGateLag, three more than the ring's depth, so
-// the copy starts well after the partials were published), and the compute waves
-// store chunk m's rows during chunk m + D from the tile kept since.  A
+// the copy starts well after the partials were published), and NW store waves
+// (beside the compute and copy waves) publish the partials and store chunk m's
+// rows during chunk m + D from the tile kept since, off the compute waves'
+// serial chunk step.  A
 // partial not yet published when it was copied (a group more than a chunk
 // behind) is read again from the exchange area until it is there.  A group
 // waits only for partials of chunks well behind its own, which the others
@@ -913,7 +916,7 @@ __device__ __forceinline__ void wait_chunks(int m) {
 // this path when the whole grid is).  Each wait is also bounded: past the
 // bound the row is written as NaN rather than hang.
 template <typename T, int DK, int C, int NW, int SPW, bool CONV = false, bool GATE = false>
-__global__ __launch_bounds__(64 * (NW + 2)) __attribute__((amdgpu_waves_per_eu(1, 2)))
+__global__ __launch_bounds__(64 * (NW + 2 + (GATE ? NW : 0))) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void kda_inter_kernel(const InterArgs a) {
     constexpr int NS = NW * SPW;
     using Ring = InterRing<T, DK, C, NS, !CONV, GATE>;
@@ -953,6 +956,235 @@ void kda_inter_kernel(const InterArgs a) {
     const int vs1 = min(a.Dv / 16, grp * NS + NS - a.n_m);
     const int vcol0 = 16 * vs0;
     auto slot_of = [&](int n) -> unsigned char* { return s_raw + (size_t)((n - a.c0) % K) * Ring::kSlot; };
+
+    // Outputs leave through the staging tiles: output wave ow (compute wave
+    // ow, or with GATE store wave ow) stores tokens [ow C / NW, (ow + 1) C / NW)
+    // of a chunk's tile, one 16-byte
+    // granule per lane and step: step st, lane l takes granule og = g / kTpw
+    // of row g % kTpw of the wave's rows (g = 64 st + l; with the plain tile
+    // granule g % kGpr of row g / kGpr), i.e. strip og / kGps of the group,
+    // 16 bytes of it.
+    constexpr int kEpg = 16 / (int)sizeof(T);      // elements per granule
+    constexpr int kGps = 16 / kEpg;                // granules per strip row
+    constexpr int kGpr = NS * kGps;                // granules per token row
+    constexpr int kTpw = C / NW;                   // tokens stored per output wave
+    const int ow = GATE ? w - NW - 2 : w;          // this wave's index among the output waves
+    constexpr int kOSteps = (kTpw * kGpr + 63) / 64;
+    unsigned char* s_otile = s_raw + (size_t)K * Ring::kSlot;
+    unsigned char* gbase[NS];   // per strip of the group: output row of token 0 (b, h), or null
+    uint32_t gstride[NS];       // bytes per token
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) {
+        const int strip = grp * NS + sl;
+        const bool ms = strip < a.n_m;
+        T* out = ms ? reinterpret_cast<T*>(a.P_out) : reinterpret_cast<T*>(a.o);
+        const int out_w = ms ? DK : a.Dv;
+        const int c0s = (ms ? strip : strip - a.n_m) * 16;
+        gstride[sl] = (uint32_t)(a.H * out_w * (int)sizeof(T));
+        gbase[sl] = (strip < a.n_strips && out)
+                        ? reinterpret_cast<unsigned char*>(out) + (((size_t)b * a.T * a.H + h) * out_w + c0s) * sizeof(T)
+                        : nullptr;
+    }
+    auto store_rows = [&](int m) {  // rows of chunk m's tile owned by this wave
+        const unsigned char* tile = s_otile + (size_t)((unsigned)(m - a.c0) % (unsigned)kOT) * Ring::kOTile;
+#pragma unroll
+        for (int st = 0; st < kOSteps; ++st) {
+            const int gi = st * 64 + lane;
+            // (bank-spread tile: a granule column of the wave's rows per 16
+            // lanes; plain tile: whole rows one after the other)
+            const int tok = ow * kTpw + (Ring::kSpread ? gi % kTpw : gi / kGpr);
+            const int og = Ring::kSpread ? gi / kTpw : gi % kGpr;
+            const int sl = og / kGps;
+            const int part = og % kGps;
+            unsigned char* base = nullptr;
+            uint32_t stride = 0;
+#pragma unroll
+            for (int t = 0; t < NS; ++t)
+                if (sl == t) { base = gbase[t]; stride = gstride[t]; }
+            if (gi < kTpw * kGpr && base && m * C + tok < a.T) {
+                uint4 v = *reinterpret_cast<const uint4*>(tile + (Ring::ooff(tok, (uint32_t)og * 16) & ~15u));
+                if (Ring::kOHalf && ((tok >> 3) & 1)) v = make_uint4(v.z, v.w, v.x, v.y);  // halves swapped in LDS
+                *reinterpret_cast<uint4*>(base + (size_t)m * C * stride + (uint32_t)tok * stride + (uint32_t)(part * 16)) = v;
+            }
+        }
+    };
+
+    // Fused output side (GATE).  Exchange area of chunk m: the partial sums of
+    // squares of its C tokens, token-major with room for kGateGroups groups
+    // (one workgroup per 16 NS value columns of the head: at most Dv / 16 = 8).
+    constexpr int kGMax = kGateGroups;
+    // per-lane partials of the compute waves: [2 (chunk parity)][C tokens][NW waves x 4 lane groups]
+    float* s_ss = reinterpret_cast<float*>(s_otile + (size_t)kOT * Ring::kOTile);
+    auto gss_at = [&](int m, int grp_, int tok) -> float* {
+        return a.gss + (((size_t)bh * a.wsNC + (size_t)(m - a.c0)) * C + tok) * kGMax + grp_;
+    };
+    bool gate_expired = false;  // a wait of this lane ran out (its rows are then NaN)
+    // where granule st of this lane goes: token row, strip of the group, part of it
+    auto granule = [&](int st, int& tok, int& sl, int& part) -> bool {
+        const int gi = st * 64 + lane;
+        tok = ow * kTpw + (Ring::kSpread ? gi % kTpw : gi / kGpr);
+        const int og = Ring::kSpread ? gi / kTpw : gi % kGpr;
+        sl = og / kGps;
+        part = og % kGps;
+        return gi < kTpw * kGpr && grp * NS + sl < a.n_strips;
+    };
+    float wv[GATE ? kOSteps : 1][GATE ? kEpg : 1];  // output weights of this lane's granules
+    if constexpr (GATE) {
+#pragma unroll
+        for (int st = 0; st < kOSteps; ++st) {
+            int tok, sl, part;
+            const bool ok = granule(st, tok, sl, part);
+            const int col = ok ? (grp * NS + sl) * 16 + part * kEpg : 0;
+#pragma unroll
+            for (int e = 0; e < kEpg; ++e) wv[st][e] = a.gw ? a.gw[col + e] : 1.f;
+        }
+    }
+    // put this workgroup's partials of chunk m (the tile's rows, summed over
+    // the compute waves' lanes in a fixed order) in the exchange area
+    auto publish = [&](int m) {
+        if (ow == 0 && lane < C) {
+            const float4* ss = reinterpret_cast<const float4*>(s_ss + ((size_t)((m - a.c0) & 1) * C + lane) * NW * 4);
+            float p = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) {
+                const float4 x = ss[ww];
+                p += (x.x + x.y) + (x.z + x.w);
+            }
+            __hip_atomic_store(gss_at(m, grp, lane), p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
+    // partial p of group g for token tok of chunk m as copied; read again from
+    // the exchange area while it is unpublished (-1; a NaN partial passes)
+    auto settle = [&](float p, int m, int g, int tok) -> float {
+        for (int it = 0; p < 0.f; ++it) {
+            if (gate_expired || it >= kGateSpinLimit) {
+                gate_expired = true;
+                return __builtin_nanf("");
+            }
+            __builtin_amdgcn_s_sleep(2);
+            p = __hip_atomic_load(gss_at(m, g, tok), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        return p;
+    };
+    // chunk m's rows of this wave: o from its tile, normalised and gated
+    auto emit_gated = [&](int m, int st, int tok, int sl, int part, const uint4& gt, float tot) {
+        const unsigned char* tile = s_otile + (size_t)((unsigned)(m - a.c0) % (unsigned)kOT) * Ring::kOTile;
+        unsigned char* base = nullptr;
+        uint32_t stride = 0;
+#pragma unroll
+        for (int t = 0; t < NS; ++t)
+            if (sl == t) { base = gbase[t]; stride = gstride[t]; }
+        const int og = sl * kGps + part;
+        uint4 v = *reinterpret_cast<const uint4*>(tile + (Ring::ooff(tok, (uint32_t)og * 16) & ~15u));
+        if (Ring::kOHalf && ((tok >> 3) & 1)) v = make_uint4(v.z, v.w, v.x, v.y);  // halves swapped in LDS
+        const float inv = __builtin_amdgcn_rsqf(tot * (1.f / (float)a.Dv) + kGateRmsEps);
+        float y[kEpg];
+#pragma unroll
+        for (int e = 0; e < kEpg; ++e)
+            y[e] = sigmoidf_(Gran16<T>::get(gt, e)) * Gran16<T>::get(v, e) * inv * wv[st][e];
+        *reinterpret_cast<uint4*>(base + (size_t)m * C * stride + (uint32_t)tok * stride + (uint32_t)(part * 16)) =
+            Gran16<T>::pack(y);
+    };
+    // chunk m = n - D during chunk n: gate and partials from the slot of chunk n.
+    // All LDS reads go out together; the partials are summed without a branch
+    // and read again from the exchange area only if one of them was copied
+    // before its group published it.
+    auto store_gated_lds = [&](int m, const unsigned char* slot) {
+        const unsigned char* gtile = slot + L.bytes + Ring::kVBytes;
+        const float* part_s = reinterpret_cast<const float*>(slot + L.bytes + 2 * Ring::kVBytes);
+#pragma unroll
+        for (int st = 0; st < kOSteps; ++st) {
+            int tok, sl, part;
+            if (granule(st, tok, sl, part) && m * C + tok < a.T) {
+                const int og = sl * kGps + part;
+                const uint4 gt = *reinterpret_cast<const uint4*>(gtile + Ring::voff(tok, (uint32_t)og * 16));
+                const float4 p0 = *reinterpret_cast<const float4*>(part_s + tok * kGMax);
+                const float4 p1 = *reinterpret_cast<const float4*>(part_s + tok * kGMax + 4);
+                const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+                float tot = 0.f, lo = 0.f;
+#pragma unroll
+                for (int g = 0; g < kGMax; ++g) {
+                    const float x = g < a.n_groups ? pv[g] : 0.f;
+                    tot += x;
+                    lo = fminf(lo, x);
+                }
+                if (lo < 0.f) {  // copied before publication: wait for the late ones
+                    tot = 0.f;
+#pragma unroll
+                    for (int g = 0; g < kGMax; ++g)
+                        if (g < a.n_groups) tot += settle(pv[g], m, g, tok);
+                }
+                emit_gated(m, st, tok, sl, part, gt, tot);
+            }
+        }
+    };
+    // the last D chunks after the loop: their gates and partials are read
+    // straight from memory, all requests in flight together
+    constexpr int kDB = D;
+    auto drain_gated = [&](int m0, int m1) {
+        uint4 gpre[GATE ? kDB : 1][GATE ? kOSteps : 1];
+        float ppre[GATE ? kDB : 1][GATE ? kOSteps : 1][GATE ? kGMax : 1];
+#pragma unroll
+        for (int i = 0; i < kDB; ++i) {
+            const int m = m0 + i;
+#pragma unroll
+            for (int st = 0; st < kOSteps; ++st) {
+                int tok, sl, part;
+                if (m < m1 && granule(st, tok, sl, part) && m * C + tok < a.T) {
+                    unsigned char* base = nullptr;
+                    uint32_t stride = 0;
+#pragma unroll
+                    for (int t = 0; t < NS; ++t)
+                        if (sl == t) { base = gbase[t]; stride = gstride[t]; }
+                    const size_t off = (size_t)(base - reinterpret_cast<unsigned char*>(a.o)) + (size_t)m * C * stride +
+                                       (uint32_t)tok * stride + (uint32_t)(part * 16);
+                    gpre[i][st] = *reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(a.gate) + off);
+#pragma unroll
+                    for (int g = 0; g < kGMax; ++g)
+                        if (g < a.n_groups)
+                            ppre[i][st][g] =
+                                __hip_atomic_load(gss_at(m, g, tok), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kDB; ++i) {
+            const int m = m0 + i;
+#pragma unroll
+            for (int st = 0; st < kOSteps; ++st) {
+                int tok, sl, part;
+                if (m < m1 && granule(st, tok, sl, part) && m * C + tok < a.T) {
+                    float tot = 0.f;
+#pragma unroll
+                    for (int g = 0; g < kGMax; ++g)
+                        if (g < a.n_groups) tot += settle(ppre[i][st][g], m, g, tok);
+                    emit_gated(m, st, tok, sl, part, gpre[i][st], tot);
+                }
+            }
+        }
+    };
+
+    if constexpr (GATE) {
+        if (w >= NW + 2) {
+            // ------------------------------------------------- store waves
+            // During chunk n: publish chunk n - 1's partials (completed
+            // before the last barrier) and store chunk n - D's rows with the
+            // gate tile and partials that came in chunk n's slot; after the
+            // loop, the last chunks.  The same barriers as the other waves.
+            lds_barrier();  // the first chunk(s) are in LDS
+            for (int n = a.c0; n < cend; ++n) {
+                if (n > a.c0) publish(n - 1);
+                if (n - D >= a.c0) store_gated_lds(n - D, slot_of(n));
+                if (K == 1) lds_barrier();
+                lds_barrier();
+            }
+            if (a.nc > 0) {
+                publish(cend - 1);
+                drain_gated(max(a.c0, cend - D), cend);
+            }
+            return;
+        }
+    }
 
     if (w >= NW) {
         // ------------------------------------------------------ copy waves
@@ -1111,207 +1343,6 @@ void kda_inter_kernel(const InterArgs a) {
 #pragma unroll
     for (int j = 0; j < SPW; ++j) vlane_q[j] = Ring::voff(4 * gq, vlane[j]);
 
-    // Outputs leave through the staging tiles: compute wave w stores tokens
-    // [w C / NW, (w + 1) C / NW) of the previous chunk's tile, one 16-byte
-    // granule per lane and step: step st, lane l takes granule og = g / kTpw
-    // of row g % kTpw of the wave's rows (g = 64 st + l; with the plain tile
-    // granule g % kGpr of row g / kGpr), i.e. strip og / kGps of the group,
-    // 16 bytes of it.
-    constexpr int kEpg = 16 / (int)sizeof(T);      // elements per granule
-    constexpr int kGps = 16 / kEpg;                // granules per strip row
-    constexpr int kGpr = NS * kGps;                // granules per token row
-    constexpr int kTpw = C / NW;                   // tokens stored per compute wave
-    constexpr int kOSteps = (kTpw * kGpr + 63) / 64;
-    unsigned char* s_otile = s_raw + (size_t)K * Ring::kSlot;
-    unsigned char* gbase[NS];   // per strip of the group: output row of token 0 (b, h), or null
-    uint32_t gstride[NS];       // bytes per token
-#pragma unroll
-    for (int sl = 0; sl < NS; ++sl) {
-        const int strip = grp * NS + sl;
-        const bool ms = strip < a.n_m;
-        T* out = ms ? reinterpret_cast<T*>(a.P_out) : reinterpret_cast<T*>(a.o);
-        const int out_w = ms ? DK : a.Dv;
-        const int c0s = (ms ? strip : strip - a.n_m) * 16;
-        gstride[sl] = (uint32_t)(a.H * out_w * (int)sizeof(T));
-        gbase[sl] = (strip < a.n_strips && out)
-                        ? reinterpret_cast<unsigned char*>(out) + (((size_t)b * a.T * a.H + h) * out_w + c0s) * sizeof(T)
-                        : nullptr;
-    }
-    auto store_rows = [&](int m) {  // rows of chunk m's tile owned by this wave
-        const unsigned char* tile = s_otile + (size_t)((unsigned)(m - a.c0) % (unsigned)kOT) * Ring::kOTile;
-#pragma unroll
-        for (int st = 0; st < kOSteps; ++st) {
-            const int gi = st * 64 + lane;
-            // (bank-spread tile: a granule column of the wave's rows per 16
-            // lanes; plain tile: whole rows one after the other)
-            const int tok = w * kTpw + (Ring::kSpread ? gi % kTpw : gi / kGpr);
-            const int og = Ring::kSpread ? gi / kTpw : gi % kGpr;
-            const int sl = og / kGps;
-            const int part = og % kGps;
-            unsigned char* base = nullptr;
-            uint32_t stride = 0;
-#pragma unroll
-            for (int t = 0; t < NS; ++t)
-                if (sl == t) { base = gbase[t]; stride = gstride[t]; }
-            if (gi < kTpw * kGpr && base && m * C + tok < a.T) {
-                uint4 v = *reinterpret_cast<const uint4*>(tile + (Ring::ooff(tok, (uint32_t)og * 16) & ~15u));
-                if (Ring::kOHalf && ((tok >> 3) & 1)) v = make_uint4(v.z, v.w, v.x, v.y);  // halves swapped in LDS
-                *reinterpret_cast<uint4*>(base + (size_t)m * C * stride + (uint32_t)tok * stride + (uint32_t)(part * 16)) = v;
-            }
-        }
-    };
-
-    // Fused output side (GATE).  Exchange area of chunk m: the partial sums of
-    // squares of its C tokens, token-major with room for kGateGroups groups
-    // (one workgroup per 16 NS value columns of the head: at most Dv / 16 = 8).
-    constexpr int kGMax = kGateGroups;
-    float* s_ss = reinterpret_cast<float*>(s_otile + (size_t)kOT * Ring::kOTile);  // [2][NW][C]
-    auto gss_at = [&](int m, int grp_, int tok) -> float* {
-        return a.gss + (((size_t)bh * a.wsNC + (size_t)(m - a.c0)) * C + tok) * kGMax + grp_;
-    };
-    bool gate_expired = false;  // a wait of this lane ran out (its rows are then NaN)
-    // where granule st of this lane goes: token row, strip of the group, part of it
-    auto granule = [&](int st, int& tok, int& sl, int& part) -> bool {
-        const int gi = st * 64 + lane;
-        tok = w * kTpw + (Ring::kSpread ? gi % kTpw : gi / kGpr);
-        const int og = Ring::kSpread ? gi / kTpw : gi % kGpr;
-        sl = og / kGps;
-        part = og % kGps;
-        return gi < kTpw * kGpr && grp * NS + sl < a.n_strips;
-    };
-    float wv[GATE ? kOSteps : 1][GATE ? kEpg : 1];  // output weights of this lane's granules
-    if constexpr (GATE) {
-#pragma unroll
-        for (int st = 0; st < kOSteps; ++st) {
-            int tok, sl, part;
-            const bool ok = granule(st, tok, sl, part);
-            const int col = ok ? (grp * NS + sl) * 16 + part * kEpg : 0;
-#pragma unroll
-            for (int e = 0; e < kEpg; ++e) wv[st][e] = a.gw ? a.gw[col + e] : 1.f;
-        }
-    }
-    // put this workgroup's partials of chunk m (the tile's rows, summed over
-    // the compute waves in a fixed order) in the exchange area
-    auto publish = [&](int m) {
-        if (w == 0 && lane < C) {
-            const float* ss = s_ss + (size_t)((m - a.c0) & 1) * NW * C;
-            float p = 0.f;
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) p += ss[ww * C + lane];
-            __hip_atomic_store(gss_at(m, grp, lane), p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    };
-    // partial p of group g for token tok of chunk m as copied; read again from
-    // the exchange area while it is unpublished (-1; a NaN partial passes)
-    auto settle = [&](float p, int m, int g, int tok) -> float {
-        for (int it = 0; p < 0.f; ++it) {
-            if (gate_expired || it >= kGateSpinLimit) {
-                gate_expired = true;
-                return __builtin_nanf("");
-            }
-            __builtin_amdgcn_s_sleep(2);
-            p = __hip_atomic_load(gss_at(m, g, tok), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        return p;
-    };
-    // chunk m's rows of this wave: o from its tile, normalised and gated
-    auto emit_gated = [&](int m, int st, int tok, int sl, int part, const uint4& gt, float tot) {
-        const unsigned char* tile = s_otile + (size_t)((unsigned)(m - a.c0) % (unsigned)kOT) * Ring::kOTile;
-        unsigned char* base = nullptr;
-        uint32_t stride = 0;
-#pragma unroll
-        for (int t = 0; t < NS; ++t)
-            if (sl == t) { base = gbase[t]; stride = gstride[t]; }
-        const int og = sl * kGps + part;
-        uint4 v = *reinterpret_cast<const uint4*>(tile + (Ring::ooff(tok, (uint32_t)og * 16) & ~15u));
-        if (Ring::kOHalf && ((tok >> 3) & 1)) v = make_uint4(v.z, v.w, v.x, v.y);  // halves swapped in LDS
-        const float inv = __builtin_amdgcn_rsqf(tot * (1.f / (float)a.Dv) + kGateRmsEps);
-        float y[kEpg];
-#pragma unroll
-        for (int e = 0; e < kEpg; ++e)
-            y[e] = sigmoidf_(Gran16<T>::get(gt, e)) * Gran16<T>::get(v, e) * inv * wv[st][e];
-        *reinterpret_cast<uint4*>(base + (size_t)m * C * stride + (uint32_t)tok * stride + (uint32_t)(part * 16)) =
-            Gran16<T>::pack(y);
-    };
-    // chunk m = n - D during chunk n: gate and partials from the slot of chunk n.
-    // All LDS reads go out together; the partials are summed without a branch
-    // and read again from the exchange area only if one of them was copied
-    // before its group published it.
-    auto store_gated_lds = [&](int m, const unsigned char* slot) {
-        const unsigned char* gtile = slot + L.bytes + Ring::kVBytes;
-        const float* part_s = reinterpret_cast<const float*>(slot + L.bytes + 2 * Ring::kVBytes);
-#pragma unroll
-        for (int st = 0; st < kOSteps; ++st) {
-            int tok, sl, part;
-            if (granule(st, tok, sl, part) && m * C + tok < a.T) {
-                const int og = sl * kGps + part;
-                const uint4 gt = *reinterpret_cast<const uint4*>(gtile + Ring::voff(tok, (uint32_t)og * 16));
-                const float4 p0 = *reinterpret_cast<const float4*>(part_s + tok * kGMax);
-                const float4 p1 = *reinterpret_cast<const float4*>(part_s + tok * kGMax + 4);
-                const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-                float tot = 0.f, lo = 0.f;
-#pragma unroll
-                for (int g = 0; g < kGMax; ++g) {
-                    const float x = g < a.n_groups ? pv[g] : 0.f;
-                    tot += x;
-                    lo = fminf(lo, x);
-                }
-                if (lo < 0.f) {  // copied before publication: wait for the late ones
-                    tot = 0.f;
-#pragma unroll
-                    for (int g = 0; g < kGMax; ++g)
-                        if (g < a.n_groups) tot += settle(pv[g], m, g, tok);
-                }
-                emit_gated(m, st, tok, sl, part, gt, tot);
-            }
-        }
-    };
-    // the last D chunks after the loop: their gates and partials are read
-    // straight from memory, all requests in flight together
-    constexpr int kDB = D;
-    auto drain_gated = [&](int m0, int m1) {
-        uint4 gpre[GATE ? kDB : 1][GATE ? kOSteps : 1];
-        float ppre[GATE ? kDB : 1][GATE ? kOSteps : 1][GATE ? kGMax : 1];
-#pragma unroll
-        for (int i = 0; i < kDB; ++i) {
-            const int m = m0 + i;
-#pragma unroll
-            for (int st = 0; st < kOSteps; ++st) {
-                int tok, sl, part;
-                if (m < m1 && granule(st, tok, sl, part) && m * C + tok < a.T) {
-                    unsigned char* base = nullptr;
-                    uint32_t stride = 0;
-#pragma unroll
-                    for (int t = 0; t < NS; ++t)
-                        if (sl == t) { base = gbase[t]; stride = gstride[t]; }
-                    const size_t off = (size_t)(base - reinterpret_cast<unsigned char*>(a.o)) + (size_t)m * C * stride +
-                                       (uint32_t)tok * stride + (uint32_t)(part * 16);
-                    gpre[i][st] = *reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(a.gate) + off);
-#pragma unroll
-                    for (int g = 0; g < kGMax; ++g)
-                        if (g < a.n_groups)
-                            ppre[i][st][g] =
-                                __hip_atomic_load(gss_at(m, g, tok), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < kDB; ++i) {
-            const int m = m0 + i;
-#pragma unroll
-            for (int st = 0; st < kOSteps; ++st) {
-                int tok, sl, part;
-                if (m < m1 && granule(st, tok, sl, part) && m * C + tok < a.T) {
-                    float tot = 0.f;
-#pragma unroll
-                    for (int g = 0; g < kGMax; ++g)
-                        if (g < a.n_groups) tot += settle(ppre[i][st][g], m, g, tok);
-                    emit_gated(m, st, tok, sl, part, gpre[i][st], tot);
-                }
-            }
-        }
-    };
-
     // Operands on the serial path (Kd, Tb and the values of a chunk) live in
     // registers from one chunk to the next: with kAhead they are read for
     // chunk n + 1 while chunk n's output is computed.
@@ -1416,9 +1447,6 @@ void kda_inter_kernel(const InterArgs a) {
         const unsigned char* cur = slot_of(n);
         const T* s_blk = reinterpret_cast<const T*>(cur);
         const float* s_gam = reinterpret_cast<const float*>(cur + L.gamma_byte);
-        if constexpr (GATE) {
-            if (n > a.c0) publish(n - 1);  // its partials were completed before the last barrier
-        }
 
         if (any_live) {
             if (!kAhead) load_serial(n);
@@ -1546,33 +1574,23 @@ void kda_inter_kernel(const InterArgs a) {
             }
             if constexpr (GATE) {
                 // lane (r, gq) holds columns 4 gq .. 4 gq + 3 of token 16 Ib + r
-                float* ss = s_ss + (size_t)((n - a.c0) & 1) * NW * C + w * C;
+                float* ss = s_ss + (size_t)((n - a.c0) & 1) * C * NW * 4 + w * 4 + gq;
 #pragma unroll
-                for (int Ib = 0; Ib < NBK; ++Ib) {
-                    const float x = group_sum4(ssw[Ib]);
-                    if (gq == 0) ss[16 * Ib + r] = x;
-                }
+                for (int Ib = 0; Ib < NBK; ++Ib) ss[(16 * Ib + r) * NW * 4] = ssw[Ib];
             }
         } else if constexpr (GATE) {
-            float* ss = s_ss + (size_t)((n - a.c0) & 1) * NW * C + w * C;
-            if (lane < C) ss[lane] = 0.f;
+            float* ss = s_ss + (size_t)((n - a.c0) & 1) * C * NW * 4 + w * 4 + gq;
+#pragma unroll
+            for (int Ib = 0; Ib < NBK; ++Ib) ss[(16 * Ib + r) * NW * 4] = 0.f;
         }
-        if constexpr (GATE) {
-            if (n - D >= a.c0) store_gated_lds(n - D, cur);  // its gate and partials came with this chunk's slot
-        } else if (n > a.c0) {
-            store_rows(n - 1);  // the previous chunk's tile was completed before the last barrier
+        if constexpr (!GATE) {
+            // the previous chunk's tile was completed before the last barrier
+            if (n > a.c0) store_rows(n - 1);
         }
         if (K == 1) lds_barrier();  // done reading the single slot
         lds_barrier();              // the next chunk(s) are in LDS
     }
-    if constexpr (GATE) {
-        if (a.nc > 0) {
-            publish(cend - 1);
-            drain_gated(max(a.c0, cend - D), cend);
-        }
-    } else if (a.nc > 0) {
-        store_rows(cend - 1);
-    }
+    if (!GATE && a.nc > 0) store_rows(cend - 1);  // (GATE: the store waves store)
 
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
@@ -1593,7 +1611,7 @@ void kda_inter_kernel(const InterArgs a) {
 template <typename T, int DK, int C, int NW, bool CONV = false, bool GATE = false>
 struct InterKernel {
     using Ring = InterRing<T, DK, C, NW, !CONV, GATE>;
-    static constexpr int kThreads = 64 * (NW + 2);
+    static constexpr int kThreads = 64 * (NW + 2 + (GATE ? NW : 0));  // GATE: NW store waves
     static constexpr size_t kLds = (size_t)Ring::kSlots * Ring::kSlot + Ring::kOBytes;
     static const void* fn() { return reinterpret_cast<const void*>(kda_inter_kernel<T, DK, C, NW, 1, CONV, GATE>); }
     static hipError_t set_attributes() {
