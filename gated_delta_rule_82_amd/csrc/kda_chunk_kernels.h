@@ -968,7 +968,12 @@ void kda_inter_kernel(const InterArgs a) {
     constexpr int kGps = 16 / kEpg;                // granules per strip row
     constexpr int kGpr = NS * kGps;                // granules per token row
     constexpr int kTpw = C / NW;                   // tokens stored per output wave
-    const int ow = GATE ? w - NW - 2 : w;          // this wave's index among the output waves
+    // wave roles: compute waves [0, NW), with GATE store waves [NW, 2 NW),
+    // then the two copy waves (so that, with waves dealt to the four SIMDs in
+    // order, the store waves' arithmetic does not share a SIMD with a compute
+    // wave at NW = 2)
+    constexpr int kCopy0 = GATE ? 2 * NW : NW;
+    const int ow = GATE ? w - NW : w;              // this wave's index among the output waves
     constexpr int kOSteps = (kTpw * kGpr + 63) / 64;
     unsigned char* s_otile = s_raw + (size_t)K * Ring::kSlot;
     unsigned char* gbase[NS];   // per strip of the group: output row of token 0 (b, h), or null
@@ -1165,7 +1170,7 @@ void kda_inter_kernel(const InterArgs a) {
     };
 
     if constexpr (GATE) {
-        if (w >= NW + 2) {
+        if (w >= NW && w < kCopy0) {
             // ------------------------------------------------- store waves
             // During chunk n: publish chunk n - 1's partials (completed
             // before the last barrier) and store chunk n - D's rows with the
@@ -1186,9 +1191,9 @@ void kda_inter_kernel(const InterArgs a) {
         }
     }
 
-    if (w >= NW) {
+    if (w >= kCopy0) {
         // ------------------------------------------------------ copy waves
-        const int cw = w - NW;
+        const int cw = w - kCopy0;
         const unsigned char* gblk = reinterpret_cast<const unsigned char*>(a.ws) + (size_t)bh * a.wsNC * L.bytes;
         const unsigned char* vsrc = reinterpret_cast<const unsigned char*>(a.v);
         constexpr int kTokPerPiece = Ring::kVTok;
