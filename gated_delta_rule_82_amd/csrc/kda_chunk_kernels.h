@@ -1169,28 +1169,6 @@ void kda_inter_kernel(const InterArgs a) {
         }
     };
 
-    if constexpr (GATE) {
-        if (w >= NW && w < kCopy0) {
-            // ------------------------------------------------- store waves
-            // During chunk n: publish chunk n - 1's partials (completed
-            // before the last barrier) and store chunk n - D's rows with the
-            // gate tile and partials that came in chunk n's slot; after the
-            // loop, the last chunks.  The same barriers as the other waves.
-            lds_barrier();  // the first chunk(s) are in LDS
-            for (int n = a.c0; n < cend; ++n) {
-                if (n > a.c0) publish(n - 1);
-                if (n - D >= a.c0) store_gated_lds(n - D, slot_of(n));
-                if (K == 1) lds_barrier();
-                lds_barrier();
-            }
-            if (a.nc > 0) {
-                publish(cend - 1);
-                drain_gated(max(a.c0, cend - D), cend);
-            }
-            return;
-        }
-    }
-
     if (w >= kCopy0) {
         // ------------------------------------------------------ copy waves
         const int cw = w - kCopy0;
@@ -1291,6 +1269,31 @@ void kda_inter_kernel(const InterArgs a) {
             }
         }
         return;
+    }
+
+    if constexpr (GATE) {
+        if (w >= NW && w < kCopy0) {
+            // ------------------------------------------------- store waves
+            // During chunk n: publish chunk n - 1's partials (completed
+            // before the last barrier) and store chunk n - D's rows with the
+            // gate tile and partials that came in chunk n's slot; after the
+            // loop, the last chunks.  The same barriers as the other waves.
+            // (Placed after the copy waves' code: placed before it, the
+            // compiler made every LDS read here wait for this wave's own
+            // output stores, a full store latency per chunk.)
+            lds_barrier();  // the first chunk(s) are in LDS
+            for (int n = a.c0; n < cend; ++n) {
+                if (n > a.c0) publish(n - 1);
+                if (n - D >= a.c0) store_gated_lds(n - D, slot_of(n));
+                if (K == 1) lds_barrier();
+                lds_barrier();
+            }
+            if (a.nc > 0) {
+                publish(cend - 1);
+                drain_gated(max(a.c0, cend - D), cend);
+            }
+            return;
+        }
     }
 
     // ------------------------------------------------------------ compute waves
