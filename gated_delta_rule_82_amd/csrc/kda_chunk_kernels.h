@@ -1043,6 +1043,7 @@ void kda_inter_kernel(const InterArgs a) {
 #pragma unroll
             for (int e = 0; e < kEpg; ++e) wv[st][e] = a.gw ? a.gw[col + e] : 1.f;
         }
+        wait_vmcnt<0>();  // landed before the store waves' loop (see the convolution's taps)
     }
     // put this workgroup's partials of chunk m (the tile's rows, summed over
     // the compute waves' lanes in a fixed order) in the exchange area
@@ -1381,6 +1382,9 @@ void kda_inter_kernel(const InterArgs a) {
                 vprev[j][p] = (uint32_t)x;
             }
         }
+        // these loads land before the loop too (a first use inside it would
+        // put a wait on every chunk, behind that chunk's output stores)
+        wait_vmcnt<0>();
     }
     // fused convolution: staging offsets of the rows 4 gq + p - 3 (p < 7)
     // relative to their 16-row block, and whether a row lies in the block before
