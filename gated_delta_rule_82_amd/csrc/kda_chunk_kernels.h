@@ -899,22 +899,22 @@ __device__ __forceinline__ void wait_chunks(int m) {
 // stored ("KDA 模块交互式演示" §1.7 完整层; "Implémenter KDA" 'La porte de
 // sortie de rang plein'): y = sigmoid(gate) * o / sqrt(mean o^2 + 1e-6) * gw
 // over the head's Dv channels, which the n_groups workgroups of a (b, h)
-// share.  Each workgroup publishes, at the start of chunk n + 1, the partial
-// sums of squares of its columns for every token of chunk n (o rounded to
-// the output type first, as a stored o would be) to the exchange area.  The
-// copy waves bring chunk m's gate tile and every group's partials for it into
-// the slot of chunk m + D (D = kGateLag, three more than the ring's depth, so
-// the copy starts well after the partials were published), and NW store waves
-// (beside the compute and copy waves) publish the partials and store chunk m's
+// share.  NW store waves join the compute and copy waves.  Every compute lane
+// writes the sum of squares of its four columns of each token of chunk n to
+// LDS (o rounded to the output type first, as a stored o would be); during
+// chunk n + 1 store wave 0 adds them up and publishes the workgroup's partial
+// of each token to the exchange area.  The copy waves bring chunk m's gate
+// tile and every group's partials for it into the slot of chunk m + D
+// (D = kGateLag, three more than the ring's depth, so the copy starts well
+// after the partials were published), and the store waves store chunk m's
 // rows during chunk m + D from the tile kept since, off the compute waves'
-// serial chunk step.  A
-// partial not yet published when it was copied (a group more than a chunk
-// behind) is read again from the exchange area until it is there.  A group
-// waits only for partials of chunks well behind its own, which the others
-// publish without waiting on anything later, so the wait ends whenever all
-// workgroups of the (b, h) are resident together (the launch only takes
-// this path when the whole grid is).  Each wait is also bounded: past the
-// bound the row is written as NaN rather than hang.
+// serial chunk step.  A partial not yet published when it was copied (a group
+// more than three chunks behind) is read again from the exchange area until
+// it is there.  A group waits only for partials of chunks well behind its
+// own, which the others publish without waiting on anything later, so the
+// wait ends whenever all workgroups of the (b, h) are resident together (the
+// launch only takes this path when the whole grid is).  Each wait is also
+// bounded: past the bound the row is written as NaN rather than hang.
 template <typename T, int DK, int C, int NW, int SPW, bool CONV = false, bool GATE = false>
 __global__ __launch_bounds__(64 * (NW + 2 + (GATE ? NW : 0))) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void kda_inter_kernel(const InterArgs a) {
