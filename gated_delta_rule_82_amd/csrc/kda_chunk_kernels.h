@@ -1659,9 +1659,11 @@ struct InterKernel {
 // Compute waves per inter workgroup: the workgroups of one (b, h) all stream
 // the same chunk blocks, and each compute wave reads every block fragment from
 // LDS, so fewer waves per workgroup cost fewer LDS reads per strip but more
-// workgroups.  The launch takes the fewest waves (1, 2 or 4) whose grid is
-// resident on the device in one round; when none is, 4 (or fewer when the
-// strips of a (b, h) fit in fewer).  GATE (the fused output side) needs the
+// workgroups.  The launch takes the fewest waves (1, 2, 4, or for 2-byte
+// elements without the fused output side 8) whose grid is resident on the
+// device in one round; when none is, the most (or fewer when the strips of a
+// (b, h) fit in fewer): every workgroup streams the whole block of each
+// chunk, so fewer workgroups copy less.  GATE (the fused output side) needs the
 // workgroups of a (b, h) resident together: `resident` says whether a grid
 // of the exact instantiation fits in one round, and the caller takes another
 // path when it does not.
@@ -1675,14 +1677,24 @@ struct ChunkLaunch {
     int nw = 4;
     bool resident = false;
     InterArgs ea{};
+    // eight compute waves: 2-byte elements only (four-byte value rows of
+    // eight strips do not tile the ring's bank-spread pieces) and not with the
+    // fused output side (its store waves would pass 1024 threads)
+    static constexpr bool kNW8 = sizeof(T) == 2 && !GATE;
 
     template <int NW>
     static int capacity(int dev, bool conv) {
+        if constexpr (NW == 8 && !kNW8) return 0;
         // the plain path sizes every launch by the instantiation without the
         // convolution (same LDS, one workgroup per CU at the sizes that fill
         // the device); the gated path asks the exact one
-        if (GATE && conv) return InterKernel<T, DK, C, NW, true, GATE>::capacity(dev);
-        return InterKernel<T, DK, C, NW, false, GATE>::capacity(dev);
+        else if (GATE && conv) return InterKernel<T, DK, C, NW, true, GATE>::capacity(dev);
+        else return InterKernel<T, DK, C, NW, false, GATE>::capacity(dev);
+    }
+    template <int NW>
+    static constexpr bool fits() {
+        if constexpr (NW == 8 && !kNW8) return false;
+        else return InterKernel<T, DK, C, NW, false, GATE>::Ring::kFits;
     }
 
     explicit ChunkLaunch(const ChunkArgs& args) : a(args), BH(args.B * args.H) {
@@ -1693,17 +1705,17 @@ struct ChunkLaunch {
         int dev = -1;
         if (hipGetDevice(&dev) != hipSuccess) dev = -1;
         const bool conv = a.conv_w != nullptr;
-        const int caps[3] = {capacity<1>(dev, conv), capacity<2>(dev, conv), capacity<4>(dev, conv)};
-        const bool fits[3] = {InterKernel<T, DK, C, 1, false, GATE>::Ring::kFits,
-                              InterKernel<T, DK, C, 2, false, GATE>::Ring::kFits,
-                              InterKernel<T, DK, C, 4, false, GATE>::Ring::kFits};
+        const int caps[4] = {capacity<1>(dev, conv), capacity<2>(dev, conv), capacity<4>(dev, conv),
+                             capacity<8>(dev, conv)};
+        const bool fits[4] = {ChunkLaunch::fits<1>(), ChunkLaunch::fits<2>(), ChunkLaunch::fits<4>(),
+                              ChunkLaunch::fits<8>()};
         nw = 0;
-        for (int i = 0, w = 1; i < 3 && !nw; ++i, w *= 2)
+        for (int i = 0, w = 1; i < 4 && !nw; ++i, w *= 2)
             if (fits[i] && (long long)BH * ((ea.n_strips + w - 1) / w) <= caps[i]) nw = w;
         resident = nw != 0;
         if (!nw) {  // no grid resident in one round: the fewest workgroups (fewest waves on a tie)
             int best_g = 1 << 30;
-            for (int i = 0, w = 1; i < 3; ++i, w *= 2) {
+            for (int i = 0, w = 1; i < 4; ++i, w *= 2) {
                 const int g = (ea.n_strips + w - 1) / w;
                 if (fits[i] && g < best_g) { best_g = g; nw = w; }
             }
@@ -1728,6 +1740,9 @@ struct ChunkLaunch {
         switch (nw) {
             case 1: return InterKernel<T, DK, C, 1, CONV, GATE>::set_attributes();
             case 2: return InterKernel<T, DK, C, 2, CONV, GATE>::set_attributes();
+            case 8:
+                if constexpr (kNW8) return InterKernel<T, DK, C, 8, CONV, GATE>::set_attributes();
+                else return hipErrorInvalidValue;
             default: return InterKernel<T, DK, C, 4, CONV, GATE>::set_attributes();
         }
     }
@@ -1765,6 +1780,9 @@ struct ChunkLaunch {
         switch (nw) {
             case 1: return InterKernel<T, DK, C, 1, CONV, GATE>::launch(ea, BH, s);
             case 2: return InterKernel<T, DK, C, 2, CONV, GATE>::launch(ea, BH, s);
+            case 8:
+                if constexpr (kNW8) return InterKernel<T, DK, C, 8, CONV, GATE>::launch(ea, BH, s);
+                else return hipErrorInvalidValue;
             default: return InterKernel<T, DK, C, 4, CONV, GATE>::launch(ea, BH, s);
         }
     }

@@ -376,13 +376,15 @@ def test_sliced_sequence_matches_oracle():
 @pytest.mark.parametrize("dtype,B,H,want,Dk", [
     (BF16, 2, 20, False, 128), (BF16, 2, 48, False, 128), (BF16, 1, 24, True, 128), (BF16, 3, 16, True, 128),
     (F32, 2, 20, False, 128), (F32, 2, 48, True, 128), (BF16, 4, 48, True, 16), (F32, 4, 48, True, 16),
+    (BF16, 4, 64, False, 128), (BF16, 2, 64, True, 128), (BF16, 8, 64, True, 128),
 ])
 def test_inter_wave_counts(dtype, B, H, want, Dk):
-    """Head counts spread over the inter kernel's 1, 2 and 4 compute waves per
-    workgroup (the launch takes the fewest waves whose grid is resident at
+    """Head counts spread over the inter kernel's 1, 2, 4 and 8 compute waves
+    per workgroup (the launch takes the fewest waves whose grid is resident at
     once: on 256 CUs with one workgroup each, 8 value strips per head give 1
-    wave up to 32 heads, 2 up to 64, else 4; the transition strips double the
-    strip count), each against the oracle on every head.  With Dk = 16 the one
+    wave up to 32 heads, 2 up to 64, 4 up to 128, then 8 for bf16 up to 256;
+    the transition strips double the strip count; a grid that is not resident
+    takes the most waves), each against the oracle on every head.  With Dk = 16 the one
     transition strip shares a workgroup's output rows with value strips; its
     transition M decays to about 1e-4 of the identity over the 45 tokens, so in
     bf16 (operands rounded to 2^-8 of entries that start near 1) M is held to
