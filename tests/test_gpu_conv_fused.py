@@ -121,6 +121,23 @@ def test_fused_conv_equals_unfused_and_oracle(dtype, Dk, Dv, chunk, T, bias, sta
     assert_close(S_f, S_ref, dtype, f"fused S Dk{Dk} Dv{Dv} C{chunk} T{T}")
 
 
+def test_fused_conv_eight_wave_launch():
+    """256 (b, h) pairs of eight 16-column value strips in bf16: the inter
+    kernel's grid is resident in one round only with eight compute waves per
+    workgroup, so both the fused and the unfused pipeline take that launch.
+    Four chunks with a ragged tail; every head against the oracle."""
+    B, T, H, D = 4, 100, 64, 128
+    inp = inputs.make_inputs(B, T, H, D, D, "bf16", seed=808, a_std=0.5, s_std=0.2)
+    w, b, st = conv_params(B, H, D, D, BF16, seed=809)
+    d = to_dev(inp)
+    o_f, S_f = fused(d, w, b, st, 32)
+    o_u, S_u = unfused(d, w, b, st, 32)
+    assert torch.equal(o_f, o_u) and torch.equal(S_f, S_u)
+    o_ref, S_ref = oracle(inp, w, b, st, BF16)
+    assert_close(o_f, o_ref, BF16, "eight-wave fused o")
+    assert_close(S_f, S_ref, BF16, "eight-wave fused S")
+
+
 @pytest.mark.parametrize("flags", [3, 5, 15])
 def test_fused_conv_switches_and_v1_gate(flags):
     """The beta and gate switches off (beta and the log-decay passed through)
