@@ -189,14 +189,21 @@ __global__ __launch_bounds__(256) void kda_fixup_kernel(const FixupArgs a) {
                             : (a.S_in ? a.S_in + ((size_t)b * a.H + h) * DK * DV : nullptr);
     if (!Sprev) return;  // uniform over the workgroup, before its only barrier
 
-    // S_prev^T into LDS: element (row, col) of the state at s_St[col LD + row]
+    // S_prev^T into LDS: element (row, col) of the state at
+    // s_St[col LD + (row ^ swz(col))].  The swizzle permutes the 8-row
+    // granules of a column (so a granule stays 16 contiguous bytes), with a
+    // different permutation for each group of four columns: the columns four
+    // apart that one staging write touches, and the lanes of a fragment read
+    // four columns apart, then fall on different banks.
+    const auto swz = [](int col) { return 8 * ((col >> 2) % (DK / 8)); };
     for (int i = threadIdx.x; i < DK * DV / 4; i += 256) {
         const int row = i / (DV / 4), c4 = 4 * (i % (DV / 4));
         const float4 v = reinterpret_cast<const float4*>(Sprev + (size_t)row * DV)[c4 / 4];
-        s_St[(c4 + 0) * LD + row] = (T)v.x;
-        s_St[(c4 + 1) * LD + row] = (T)v.y;
-        s_St[(c4 + 2) * LD + row] = (T)v.z;
-        s_St[(c4 + 3) * LD + row] = (T)v.w;
+        const int rs = row ^ swz(c4);  // the same for the four columns c4 .. c4 + 3
+        s_St[(c4 + 0) * LD + rs] = (T)v.x;
+        s_St[(c4 + 1) * LD + rs] = (T)v.y;
+        s_St[(c4 + 2) * LD + rs] = (T)v.z;
+        s_St[(c4 + 3) * LD + rs] = (T)v.w;
     }
     __syncthreads();
 
@@ -209,7 +216,7 @@ __global__ __launch_bounds__(256) void kda_fixup_kernel(const FixupArgs a) {
         const int col = col0 + 4 * NST * (r >> 2) + 4 * q + (r & 3);
 #pragma unroll
         for (int s = 0; s < KSD; ++s) {
-            if (32 * s + 8 * gq < DK) frag_load_row8(Sf[q][s], s_St + col * LD + 32 * s + 8 * gq);
+            if (32 * s + 8 * gq < DK) frag_load_row8(Sf[q][s], s_St + col * LD + ((32 * s + 8 * gq) ^ swz(col)));
             else Sf[q][s].zero();
         }
     }
